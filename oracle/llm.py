@@ -1,0 +1,53 @@
+"""Pre-norm transformer block and the VLM backbone prefill (oracle side).
+
+Page "AI Infra如何优化VLA - 模型推理性能提升技术拆解":
+  * section 整体方案: the LLM is a 36-layer decoder with GQA (32 query / 8 KV
+    heads) and a SwiGLU MLP with intermediate size 9728, run as a pure
+    prefill (no autoregressive decode);
+  * section 算子开发: RMSNorm is the pre-norm of each sublayer (72 pre-norm
+    calls over 36 layers); RoPE rotates halves of Q and K in every layer;
+  * section 算子融合: fused QKV (one projection producing Q, K and V) and the
+    SwiGLU MLP;
+  * section CUDA Graph: the LLM pass runs its layers and ends in a final
+    RMSNorm.
+Block (no biases, consistent with the decoder family the page names):
+  h   = x + Attn(RoPE(Q), RoPE(K), V) W_o^T,   [Q|K|V] = RMSNorm(x, g1) W_qkv^T
+  out = h + (SiLU(n W_g^T) * (n W_u^T)) W_d^T,  n = RMSNorm(h, g2)
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import ops
+
+
+def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
+    """One pre-norm block on x [S, H]; ``pos0`` is the position of row 0."""
+    x = np.asarray(x, dtype=np.float64)
+    S, H = x.shape
+    Hq, Hkv, D = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    n = ops.rmsnorm(x, W[prefix + "attn_norm"], shape.eps)
+    q = ops.linear(n, W[prefix + "wq"]).reshape(S, Hq, D)
+    k = ops.linear(n, W[prefix + "wk"]).reshape(S, Hkv, D)
+    v = ops.linear(n, W[prefix + "wv"]).reshape(S, Hkv, D)
+    pos = np.arange(S) + pos0
+    q = ops.rope(q, pos, shape.rope_base)
+    k = ops.rope(k, pos, shape.rope_base)
+    o = ops.attention(q, k, v, causal=True).reshape(S, Hq * D)
+    h = x + ops.linear(o, W[prefix + "wo"])
+    n2 = ops.rmsnorm(h, W[prefix + "mlp_norm"], shape.eps)
+    a = ops.silu(ops.linear(n2, W[prefix + "wg"])) * ops.linear(n2, W[prefix + "wu"])
+    return h + ops.linear(a, W[prefix + "wd"])
+
+
+def backbone(E: np.ndarray, W, cfg, layers=None) -> np.ndarray:
+    """The layer stack over embeddings E [S, H], then the final RMSNorm when
+    the config has one. Positions are 0..S-1 for every row (1-D RoPE)."""
+    x = np.asarray(E, dtype=np.float64)
+    n_layers = cfg.layers if layers is None else layers
+    for l in range(n_layers):
+        x = block(x, W, f"llm.{l}.", cfg.block)
+    if cfg.final_norm:
+        x = ops.rmsnorm(x, W["llm.final_norm"], cfg.block.eps)
+    return x

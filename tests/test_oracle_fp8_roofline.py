@@ -1,0 +1,89 @@
+"""Pins of the fp8 decoder (OCP E4M3FN specification values), of the seeded
+fp8 storage encoder, and of the roofline latency model (VLA-Perf section 2.3
+formula, the RTX 4090 ridge printed on the XPU characterisation page)."""
+
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle.fp8 import decode_e4m3fn, dequantize_rows
+from synth.fp8 import encode_e4m3fn, quantize_rows
+from synth.gen import f32_to_bf16_bits, bf16_bits_to_f32
+from synth import small_config, get_config
+from vla_robot_policy_amd import roofline
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_e4m3fn_spec_values():
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+             0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in table.items():
+        assert decode_e4m3fn(np.array([c]))[0] == v, hex(c)
+    assert np.isnan(decode_e4m3fn(np.array([0x7F, 0xFF]))).all()
+    assert math.copysign(1.0, decode_e4m3fn(np.array([0x80]))[0]) == -1.0
+    vals = decode_e4m3fn(np.arange(256))
+    assert np.isfinite(vals).sum() == 254
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)                          # codes 0..0x7E ascend
+    np.testing.assert_array_equal(vals[0x80:0xFF], -vals[:0x7F])
+
+
+def test_e4m3_values_are_exact_in_bf16():
+    v = decode_e4m3fn(np.arange(256))
+    f = v[np.isfinite(v)].astype(np.float32)
+    np.testing.assert_array_equal(bf16_bits_to_f32(f32_to_bf16_bits(f)), f)
+
+
+def test_encoder_nearest_even_and_saturating(rng):
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)])
+    np.testing.assert_array_equal(encode_e4m3fn(decode_e4m3fn(codes)), codes)
+    x = rng.standard_normal(20000) * 100
+    q = decode_e4m3fn(encode_e4m3fn(x))
+    finite = decode_e4m3fn(np.arange(0x7F))
+    allv = np.concatenate([finite, -finite])
+    best = np.min(np.abs(allv[None, :] - np.clip(x, -448, 448)[:, None]), axis=1)
+    np.testing.assert_array_equal(np.abs(q - np.clip(x, -448, 448)), best)
+    # ties go to the even code: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39)
+    assert encode_e4m3fn(np.array([1.0625]))[0] == 0x38
+    assert encode_e4m3fn(np.array([1.1875]))[0] == 0x3A     # between 0x39 and 0x3A -> even
+    assert encode_e4m3fn(np.array([1e6, -1e6])).tolist() == [0x7E, 0xFE]
+
+
+def test_row_quantisation_bounds(rng):
+    w = (rng.standard_normal((33, 70)) * 0.02).astype(np.float32)
+    q, s = quantize_rows(w)
+    assert q.dtype == np.uint8 and s.dtype == np.float32 and s.shape == (33,)
+    d = decode_e4m3fn(q)
+    assert np.nanmax(np.abs(d)) <= 448.0
+    assert np.all(np.abs(d).max(axis=1) >= 400)              # each row uses the top of the range
+    wt = dequantize_rows(q, s)
+    rel = np.linalg.norm(wt - w) / np.linalg.norm(w)
+    assert rel < 0.04                                          # 3 mantissa bits: ~2^-4 / sqrt(3)
+
+
+def test_roofline_formula_and_golden_ridge():
+    g = json.load(open(os.path.join(GOLDEN, "roofline_rtx4090.json")))
+    assert roofline.ridge(g["implied_peak_flops"], g["hbm_bytes_per_s"]) == g["ridge_flop_per_byte"]
+    # T_o = max(FLOPs / peak, Bytes / BW)
+    assert roofline.op_time(10.0, 1.0, 5.0, 1.0) == 2.0
+    assert roofline.op_time(1.0, 10.0, 5.0, 1.0) == 10.0
+    # a GEMM: F = 2MNK; B = weights + activations in + out
+    op = roofline.linear_op("g", "p", 16, 128, 64, "bf16")
+    assert op.flops == 2 * 16 * 128 * 64
+    assert op.bytes == 2 * 128 * 64 + 2 * 16 * 64 + 2 * 16 * 128
+    fp8 = roofline.linear_op("g", "p", 16, 128, 64, "fp8")
+    assert fp8.bytes == 128 * 64 + 4 * 128 + 2 * 16 * 64 + 2 * 16 * 128
+
+
+def test_roofline_bounds_of_named_workloads():
+    b2 = roofline.bound(get_config(2))
+    # weights of the 36-layer backbone: 36 * (6144 + 4096... ) -> dominated by 7.25e9 bytes
+    w = 36 * 2 * 2560 * (6144 + 4096 + 2 * 9728 + 9728)
+    assert b2.bytes > w and b2.bytes < w * 1.2
+    assert 0.9e-3 < b2.seconds < 1.2e-3
+    b4 = roofline.bound(get_config(4))
+    assert 1.8e-3 < b4.seconds < 2.4e-3
+    assert set(b4.per_phase) == {"vit", "backbone", "projector", "dit_once", "dit_step"}
