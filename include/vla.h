@@ -1,0 +1,266 @@
+/*
+ * libvla — batch-1 forward pass of a Vision-Language-Action policy on one
+ * AMD Instinct MI355X (gfx950): ViT encoder + 2x2 merger -> pre-norm GQA
+ * decoder backbone (prefill) -> projector -> DiT action expert inside a
+ * K-step flow-matching Euler loop, optionally captured as one hipGraph.
+ *
+ * Sources (pages, by title and section):
+ *   [R]  "AI Infra如何优化VLA - 模型推理性能提升技术拆解" (StarVLA on RTX 4090):
+ *        整体方案 (model structure, the ten operator types), 自研推理框架
+ *        (weights handed over directly as tensors), CUDA Graph (three graphs,
+ *        static I/O buffers refreshed by copy before replay), 算子开发 (RMSNorm
+ *        chain, half-split RoPE), 算子融合 (fused GELU / SwiGLU MLP, fused QKV).
+ *   [A]  "开源 APXInf 把 VLA 推理压到 26 毫秒": capture the whole inference
+ *        graph on the first call and replay it every control cycle; FP8
+ *        weights.
+ *
+ * Conventions for every entry point
+ *   - Activations are row-major [rows, features] (token-major). A Linear
+ *     weight is row-major [N_out, K_in] (PyTorch convention, y = x W^T + b).
+ *     bf16 tensors are raw bfloat16 bit patterns (uint16); fp8 tensors are
+ *     OCP E4M3FN codes (uint8) with one float32 scale per output row; norm
+ *     gains, biases, positional tables and modulation vectors are float32.
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned, owned by the
+ *     caller. The library never allocates device memory in a run, capture or
+ *     replay call; scratch space is the caller's workspace (ws, ws_bytes),
+ *     whose required size the matching *_workspace_bytes() returns. The
+ *     workspace content need not be initialised.
+ *   - Calls are asynchronous on the given stream (0 = the null stream);
+ *     results are valid once the caller has synchronised that stream.
+ *   - Errors: a negative vla_status; vla_last_error() returns a message
+ *     for the calling thread. Nothing is launched when argument validation
+ *     fails. VLA_ERR_HIP wraps a HIP runtime error (launch or graph API).
+ */
+#ifndef VLA_H
+#define VLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VLA_ABI_VERSION 1
+
+typedef enum {
+  VLA_OK = 0,
+  VLA_ERR_INVALID_ARG = -1, /* null pointer, bad enum, misaligned buffer   */
+  VLA_ERR_SHAPE = -2,       /* shape outside the supported set            */
+  VLA_ERR_UNSUPPORTED = -3, /* valid but not implemented combination      */
+  VLA_ERR_WORKSPACE = -4,   /* ws_bytes below the required size           */
+  VLA_ERR_HIP = -5,         /* HIP runtime error                          */
+  VLA_ERR_STATE = -6        /* plan used out of order / already captured  */
+} vla_status;
+
+typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2 } vla_dtype;
+
+/* ------------------------------------------------------------------ block
+ * One pre-norm decoder block ([R] 整体方案, 算子开发, 算子融合):
+ *   [Q|K|V] = RMSNorm(x, attn_norm) W_qkv^T, RoPE (half-split, base
+ *   rope_base, positions 0..seq-1) on Q and K, causal GQA attention (query
+ *   head h reads KV head h / (n_q_heads / n_kv_heads)), h = x + O W_o^T,
+ *   out = h + (SiLU(n W_gate^T) * (n W_up^T)) W_down^T with n = RMSNorm(h,
+ *   mlp_norm). RMSNorm(x, g) = x / sqrt(mean(x^2) + eps) * g. No biases.
+ * Supported: head_dim in {64, 128}; hidden, intermediate multiples of 8;
+ * n_q_heads % n_kv_heads == 0; wdtype F32 with adtype F32, or wdtype
+ * BF16 / FP8_E4M3 with adtype BF16.
+ */
+typedef struct {
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, intermediate;
+  float rope_base, eps;
+  int32_t wdtype;  /* vla_dtype of the Linear weights                  */
+  int32_t adtype;  /* vla_dtype of x_in / x_out / embeddings: F32, BF16 */
+  int32_t flags;   /* must be 0                                        */
+} vla_block_cfg;
+
+typedef struct {
+  const float* attn_norm; /* [hidden]                                             */
+  const void* w_qkv;      /* [(Hq + 2 Hkv) head_dim, hidden]: rows of W_q, W_k, W_v */
+  const float* s_qkv;     /* fp8 only: [(Hq + 2 Hkv) head_dim]                     */
+  const void* w_o;        /* [hidden, Hq head_dim]                                 */
+  const float* s_o;
+  const float* mlp_norm;  /* [hidden]                                             */
+  const void* w_gate_up;  /* [2 intermediate, hidden]: rows of W_gate, then W_up   */
+  const float* s_gate_up;
+  const void* w_down;     /* [hidden, intermediate]                                */
+  const float* s_down;
+} vla_block_weights;
+
+/* x_in, x_out: [seq, hidden] in cfg->adtype (may alias). */
+vla_status vla_block_forward(const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
+                             int32_t seq, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t vla_block_workspace_bytes(const vla_block_cfg* cfg, int32_t seq);
+
+/* ------------------------------------------------------------------ backbone
+ * The decoder prefill ([R] 整体方案; CUDA Graph: "36 layers to the final
+ * RMSNorm"): n_layers blocks over the embeddings, then RMSNorm(final_norm)
+ * when final_norm is not NULL. `layers` is a HOST array of n_layers weight
+ * records (device pointers inside); it is read during the call only.
+ */
+typedef struct {
+  vla_block_cfg cfg;
+  int32_t n_layers;
+  const vla_block_weights* layers; /* host array [n_layers]      */
+  const float* final_norm;         /* [hidden] or NULL           */
+} vla_backbone;
+
+/* embeds, hidden_out: [seq, hidden] in cfg.adtype. 1 <= seq <= 4096. */
+vla_status vla_backbone_prefill(const vla_backbone* bb, const void* embeds, int32_t seq, void* hidden_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+size_t vla_backbone_workspace_bytes(const vla_backbone* bb, int32_t seq);
+
+/* ------------------------------------------------------------------ DiT + Euler
+ * The action expert ([R] 整体方案: flow-matching Euler denoising from noise).
+ * With t_k = k/K and a_0 = x0:  a_{k+1} = a_k + v(a_k, t_k, ctx) / K; the
+ * output is a_K. The velocity v:
+ *   x = a W_in^T + b_in;  phi(t) = [cos(time_scale t w_i), sin(time_scale t
+ *   w_i)], w_i = freq_base^(-i/(tdim/2)); c = W_t2 SiLU(W_t1 phi + b_t1) +
+ *   b_t2;  per layer m = W_ada SiLU(c) + b_ada = 9 vectors [shift, scale,
+ *   gate] x [self-attn, cross-attn, MLP]; each sublayer adds
+ *   gate * f(LN(x)(1 + scale) + shift) (LN without affine, eps); self-attn
+ *   is full multi-head attention over the action rows; cross-attn reads
+ *   K/V = ctx W^T + b of every context row; MLP is Linear-GELU(erf)-Linear;
+ *   finally v = (LN(x)(1 + scale_f) + shift_f) W_out^T + b_out with
+ *   [shift_f, scale_f] = W_f SiLU(c) + b_f. Every Linear has a bias.
+ * Supported: head_dim 80 or 64 (hidden = heads * head_dim); widths
+ * multiples of 8; 1 <= chunk <= 64; 1 <= K <= 64; 1 <= ctx_len <= 4096.
+ */
+typedef struct {
+  int32_t hidden, heads, head_dim, mlp, layers, tdim, ctx_dim;
+  float eps, time_scale, freq_base;
+  int32_t wdtype; /* F32, BF16 or FP8_E4M3 */
+  int32_t flags;  /* must be 0             */
+} vla_dit_cfg;
+
+typedef struct {
+  const void* w_qkv; const float* s_qkv; const float* b_qkv; /* self-attn [3 hidden, hidden]: W_q, W_k, W_v rows */
+  const void* w_o; const float* s_o; const float* b_o;       /* [hidden, hidden]                                */
+  const void* w_cq; const float* s_cq; const float* b_cq;    /* cross-attn query [hidden, hidden]               */
+  const void* w_co; const float* s_co; const float* b_co;    /* cross-attn out   [hidden, hidden]               */
+  const void* w_up; const float* s_up; const float* b_up;    /* [mlp, hidden]                                   */
+  const void* w_down; const float* s_down; const float* b_down; /* [hidden, mlp]                                */
+} vla_dit_layer;
+
+typedef struct {
+  vla_dit_cfg cfg;
+  const vla_dit_layer* layers;  /* host array [cfg.layers]                                            */
+  /* per-layer tensors stacked over layers so each is one launch per policy step:              */
+  const void* w_ada; const float* s_ada; const float* b_ada; /* [layers*9*hidden, hidden]                 */
+  const void* w_ckv; const float* s_ckv; const float* b_ckv; /* [layers*2*hidden, ctx_dim]: per layer W_k then W_v */
+  const void* w_t1; const float* s_t1; const float* b_t1;    /* [hidden, tdim]                            */
+  const void* w_t2; const float* s_t2; const float* b_t2;    /* [hidden, hidden]                          */
+  const void* w_f; const float* s_f; const float* b_f;       /* [2 hidden, hidden]: shift rows, scale rows */
+  const void* w_in; const float* s_in; const float* b_in;    /* [hidden, action_dim]                      */
+  const void* w_out; const float* s_out; const float* b_out; /* [action_dim, hidden]                      */
+} vla_dit;
+
+/* ctx: [ctx_len, ctx_dim] bf16 (F32 for an F32 DiT); x0, actions_out:
+ * float32 [chunk, action_dim] (may alias); velocities_out: optional float32
+ * [K, chunk, action_dim] record of every v (NULL to skip). */
+vla_status vla_flow_euler_sample(const vla_dit* dit, const void* ctx, int32_t ctx_len, const float* x0, int32_t chunk,
+                                 int32_t action_dim, int32_t K, float* actions_out, float* velocities_out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+size_t vla_dit_workspace_bytes(const vla_dit* dit, int32_t ctx_len, int32_t chunk, int32_t action_dim, int32_t K);
+
+/* ------------------------------------------------------------------ vision
+ * ViT + merger ([R] CUDA Graph: PatchEmbed -> ViT blocks -> Merger; 算子融合:
+ * GELU MLPs). Patch (r, c) of image i is token i*grid^2 + r*grid + c with
+ * features in (channel, row, column) order; z = P W_pe^T + b_pe + pos; each
+ * layer: z += MHA(LN(z)) W_o^T + b_o (non-causal, biased q/k/v), z += W_2
+ * GELU(W_1 LN(z) + b_1) + b_2. Merger: u = LN(z; mln); merged token (R, C)
+ * concatenates u of patches (2R+dy, 2C+dx) for (dy, dx) in raster order;
+ * out = GELU(u W_m1^T + b_m1) W_m2^T + b_m2.
+ * w_pe rows have a pitch of round_up(channels*patch^2, 8) elements; the pad
+ * columns must be zero.
+ */
+typedef struct {
+  int32_t image, patch, channels, hidden, heads, head_dim, mlp, layers, merge, out_dim;
+  float eps;
+  int32_t wdtype; /* BF16 */
+  int32_t flags;  /* must be 0 */
+} vla_vit_cfg;
+
+typedef struct {
+  const float* ln1_g; const float* ln1_b;
+  const void* w_qkv; const float* b_qkv;  /* [3 hidden, hidden]: W_q, W_k, W_v rows */
+  const void* w_o; const float* b_o;      /* [hidden, hidden]                      */
+  const float* ln2_g; const float* ln2_b;
+  const void* w_up; const float* b_up;    /* [mlp, hidden]                         */
+  const void* w_down; const float* b_down;/* [hidden, mlp]                         */
+} vla_vit_layer;
+
+typedef struct {
+  vla_vit_cfg cfg;
+  const vla_vit_layer* layers;            /* host array [cfg.layers]                  */
+  const void* w_pe; const float* b_pe;    /* [hidden, pitch] (see above), [hidden]    */
+  const float* pos;                       /* [grid^2, hidden]                         */
+  const float* mln_g; const float* mln_b; /* [hidden]                                 */
+  const void* w_m1; const float* b_m1;    /* [4 hidden, 4 hidden] (merge 2)           */
+  const void* w_m2; const float* b_m2;    /* [out_dim, 4 hidden]                      */
+} vla_vit;
+
+/* images: bf16 [n_images, channels, image, image]; tokens_out: float32
+ * [n_images * grid^2 / merge^2, out_dim]; vit_out: optional float32
+ * [n_images * grid^2, hidden] (the encoder output before the merger). */
+vla_status vla_vit_encode(const vla_vit* vit, const void* images, int32_t n_images, float* tokens_out, float* vit_out,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+size_t vla_vit_workspace_bytes(const vla_vit* vit, int32_t n_images);
+
+/* ------------------------------------------------------------------ whole step
+ * The full policy step ([R] 整体方案: vision -> LLM (with projection layers)
+ * -> action head; [A]: capture once, replay per control cycle): sequence =
+ * [visual tokens of each image; text embeddings], backbone with final norm,
+ * ctx = hidden W_proj^T + b_proj (all rows), then the Euler sampler.
+ * A plan binds the model and the caller's static I/O buffers; the caller
+ * refreshes the inputs in place (device copies) before each replay ([R]
+ * CUDA Graph). Every pointer handed to the plan must stay valid at the same
+ * address until vla_step_plan_destroy.
+ */
+typedef struct {
+  const vla_vit* vit;           /* NULL: no vision encoder (all tokens given as text) */
+  const vla_backbone* backbone; /* final_norm required                               */
+  const void* w_proj; const float* s_proj; const float* b_proj; /* [ctx_dim, hidden], bias [ctx_dim] */
+  const vla_dit* dit;
+} vla_model;
+
+typedef struct {
+  int32_t n_images, n_text, chunk, action_dim, steps;
+} vla_step_shape;
+
+typedef struct {
+  const void* images;   /* bf16 [n_images, C, image, image] or NULL when n_images == 0 */
+  const void* text;     /* [n_text, hidden] in the backbone's adtype                  */
+  const float* noise;   /* [chunk, action_dim]                                        */
+  float* actions;       /* [chunk, action_dim]                                        */
+  void* hidden_out;     /* optional [seq, hidden] copy of the backbone output (adtype) */
+  float* velocities;    /* optional [steps, chunk, action_dim]                        */
+} vla_step_io;
+
+typedef struct vla_step_plan vla_step_plan;
+
+size_t vla_step_workspace_bytes(const vla_model* model, const vla_step_shape* shape);
+/* Validates, copies the host-side descriptors, and binds io and ws. Host
+ * memory only; nothing is launched. */
+vla_status vla_step_plan_create(const vla_model* model, const vla_step_shape* shape, const vla_step_io* io, void* ws,
+                                size_t ws_bytes, vla_step_plan** out);
+/* One eager pass of the step (kernel launches on `stream`). */
+vla_status vla_step_run(vla_step_plan* plan, hipStream_t stream);
+/* Capture one pass into a hipGraph and instantiate it (one eager warm-up
+ * pass is launched first). VLA_ERR_STATE if already captured. */
+vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream);
+/* Replay the captured graph (VLA_ERR_STATE if not captured). */
+vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream);
+/* Kernel nodes in the captured graph (0 before capture). */
+int32_t vla_step_graph_nodes(const vla_step_plan* plan);
+void vla_step_plan_destroy(vla_step_plan* plan);
+
+/* ------------------------------------------------------------------ misc */
+const char* vla_last_error(void);
+int32_t vla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VLA_H */

@@ -1,0 +1,79 @@
+"""The C-ABI library loads, exports every entry point include/vla.h
+declares, and validates arguments on the host (no GPU needed: every case
+here fails validation before any HIP call, or only sizes a workspace)."""
+
+import ctypes as C
+
+import pytest
+
+from vla_robot_policy_amd import lib
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib.load()
+    syms = lib.header_symbols()
+    assert len(syms) >= 17
+    for s in syms:
+        assert hasattr(L, s), s
+    assert lib.vla_abi_version() == 1
+
+
+def llm_cfg(**kw):
+    base = dict(hidden=2560, n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=9728, rope_base=1e6, eps=1e-6,
+                wdtype=lib.VLA_BF16, adtype=lib.VLA_BF16, flags=0)
+    base.update(kw)
+    return lib.BlockCfg(**base)
+
+
+def test_workspace_sizes_scale_with_shape():
+    a = lib.vla_block_workspace_bytes(llm_cfg(), 104)
+    b = lib.vla_block_workspace_bytes(llm_cfg(), 256)
+    assert 0 < a < b
+    bb = lib.Backbone(cfg=llm_cfg(), n_layers=36, layers=None, final_norm=None)
+    assert lib.vla_backbone_workspace_bytes(bb, 256) >= b
+    assert lib.vla_block_workspace_bytes(llm_cfg(head_dim=96), 64) == 0       # unsupported -> 0
+    assert lib.vla_block_workspace_bytes(llm_cfg(), 0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), lib.VLA_ERR_SHAPE),
+    (dict(n_kv_heads=5), lib.VLA_ERR_SHAPE),
+    (dict(hidden=2561), lib.VLA_ERR_SHAPE),
+    (dict(flags=1), lib.VLA_ERR_UNSUPPORTED),
+    (dict(wdtype=7), lib.VLA_ERR_INVALID_ARG),
+    (dict(wdtype=lib.VLA_F32), lib.VLA_ERR_UNSUPPORTED),
+])
+def test_block_cfg_validation(kw, code):
+    w = lib.BlockWeights()
+    st = lib.vla_block_forward(llm_cfg(**kw), w, 16, 16, 8, 256, 1 << 30)
+    assert st == code, lib.vla_last_error()
+    assert lib.vla_last_error()
+
+
+def test_null_weights_and_buffers_are_rejected():
+    w = lib.BlockWeights()
+    assert lib.vla_block_forward(llm_cfg(), w, 16, 16, 8, 256, 1 << 30) == lib.VLA_ERR_INVALID_ARG
+    fake = 1 << 20
+    for f in w._fields_:
+        setattr(w, f[0], fake)
+    assert lib.vla_block_forward(llm_cfg(), w, None, fake, 8, fake, 1 << 30) == lib.VLA_ERR_INVALID_ARG
+    assert lib.vla_block_forward(llm_cfg(), w, fake, fake, 0, fake, 1 << 30) == lib.VLA_ERR_SHAPE
+    # workspace: too small, then misaligned (checked before anything is launched)
+    assert lib.vla_block_forward(llm_cfg(), w, fake, fake, 8, fake, 1024) == lib.VLA_ERR_WORKSPACE
+    assert lib.vla_block_forward(llm_cfg(), w, fake, fake, 8, fake + 16, 1 << 30) == lib.VLA_ERR_INVALID_ARG
+
+
+def test_dit_and_step_validation():
+    dc = lib.DitCfg(hidden=1280, heads=16, head_dim=80, mlp=5120, layers=2, tdim=256, ctx_dim=1280, eps=1e-6,
+                    time_scale=1000.0, freq_base=10000.0, wdtype=lib.VLA_BF16, flags=0)
+    d = lib.Dit(cfg=dc, layers=None)
+    assert lib.vla_dit_workspace_bytes(d, 256, 16, 7, 4) > 0
+    assert lib.vla_dit_workspace_bytes(d, 256, 65, 7, 4) == 0                  # chunk > 64
+    assert lib.vla_flow_euler_sample(d, 16, 256, 16, 16, 7, 4, 16, None, 256, 1 << 30) == lib.VLA_ERR_INVALID_ARG
+    d.cfg.head_dim = 96
+    assert lib.vla_flow_euler_sample(d, 16, 256, 16, 16, 7, 4, 16, None, 256, 1 << 30) == lib.VLA_ERR_SHAPE
+    # step plan: null model / out pointers
+    st, plan = lib.vla_step_plan_create(lib.Model(), lib.StepShape(), lib.StepIO(), None, 0)
+    assert st == lib.VLA_ERR_INVALID_ARG and plan is None
+    assert lib.vla_step_replay(None) == lib.VLA_ERR_INVALID_ARG
+    assert lib.vla_step_graph_nodes(None) == 0

@@ -1,0 +1,967 @@
+// libvla host runtime: argument validation, workspace planning, kernel
+// selection and launch, and the captured whole-step graph (C ABI in vla.h).
+//
+// Every entry point is written once as a "schedule" over a Ctx. The schedule
+// runs twice: in plan mode (no device pointers, nothing launched) it sizes
+// the workspace — fixed buffers by bump allocation and the shared split-K
+// scratch as the maximum over all GEMMs — and in launch mode it enqueues the
+// kernels on the caller's stream. Both passes allocate in the same order, so
+// the buffers land at the same offsets.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "../../include/vla.h"
+#include "gemm.h"
+#include "attention.h"
+#include "kernels.h"
+#include "tail.h"
+
+using namespace vla;
+
+namespace {
+
+thread_local std::string g_err;
+
+vla_status fail(vla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define VLA_TRY(expr)                    \
+  do {                                   \
+    vla_status _s = (expr);              \
+    if (_s != VLA_OK) return _s;         \
+  } while (0)
+
+#define VLA_HIP(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t _e = (expr);                                                                   \
+    if (_e != hipSuccess) return fail(VLA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(_e));  \
+  } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Ctx {
+  bool plan;               // plan mode: size buffers, launch nothing
+  char* base;              // workspace base (launch mode)
+  size_t cap;
+  size_t off = 0;
+  hipStream_t st = nullptr;
+  // shared GEMM scratch (requirements gathered in plan mode)
+  size_t need_part = 0, need_tiles = 0, need_sp = 0;
+  float* part = nullptr;
+  unsigned* cnt_tile = nullptr;
+  unsigned* cnt_all = nullptr;
+  float2* stats_part = nullptr;
+  int kernels = 0;         // launches issued (or that would be issued)
+
+  template <typename T>
+  T* take(size_t n) {
+    off = align_up(off, 256);
+    T* p = plan ? nullptr : reinterpret_cast<T*>(base + off);
+    off += n * sizeof(T);
+    return p;
+  }
+  // Lay out the split-K scratch after the fixed buffers.
+  void take_scratch(size_t part_f, size_t tiles, size_t sp) {
+    part = take<float>(std::max<size_t>(part_f, 1));
+    cnt_tile = take<unsigned>(tiles + 1);
+    cnt_all = cnt_tile + tiles;
+    stats_part = take<float2>(std::max<size_t>(sp, 1));
+  }
+};
+
+vla_status launch(Ctx& c, const void* fn, dim3 grid, dim3 block, size_t smem, void** args) {
+  c.kernels++;
+  if (c.plan) return VLA_OK;
+  VLA_HIP(hipLaunchKernel(fn, grid, block, args, smem, c.st));
+  return VLA_OK;
+}
+
+vla_status zero_counters(Ctx& c) {
+  if (c.plan) return VLA_OK;
+  unsigned* p = c.cnt_tile;
+  unsigned v = 0;
+  int n = (int)(c.need_tiles + 1);
+  void* args[] = {&p, &v, &n};
+  return launch(c, k_fill_ref(), dim3((n + 255) / 256), dim3(256), 0, args);
+}
+
+// Kernels that need more than 64 KiB of dynamic LDS are opted in once.
+vla_status allow_smem(const KernelRef& k) {
+  static std::mutex mu;
+  static std::set<const void*> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count(k.fn)) return VLA_OK;
+  VLA_HIP(hipFuncSetAttribute(k.fn, hipFuncAttributeMaxDynamicSharedMemorySize, k.smem));
+  done.insert(k.fn);
+  return VLA_OK;
+}
+
+// ------------------------------------------------------------------ GEMM launcher
+struct GemmOp {
+  int wdtype;   // vla_dtype of W
+  int am, em;
+};
+
+void pick_tile(int M, int em, int& mb, int& wn, int& nbw) {
+  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : 16;
+  bool wide = em == E_ROPE || em == E_SWIGLU;
+  if (wide) { wn = 4; nbw = 2; }
+  else if (mb == 1) { wn = 1; nbw = 1; }
+  else { wn = 4; nbw = 1; }
+}
+
+vla_status gemm(Ctx& c, GemmArgs a, GemmOp op) {
+  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return fail(VLA_ERR_SHAPE, "gemm: empty shape %d x %d x %d", a.M, a.N, a.K);
+  int mb, wn, nbw;
+  pick_tile(a.M, op.em, mb, wn, nbw);
+  const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * (4 / wn) * 2;
+  const int bn_out = op.em == E_SWIGLU ? BN / 2 : BN;
+  a.n_tiles_n = (a.N + bn_out - 1) / bn_out;
+  a.n_tiles_m = (a.M + BM - 1) / BM;
+  const int tiles = a.n_tiles_n * a.n_tiles_m;
+  int split = 1;
+  if (tiles < 200) {
+    int max_split = std::max(1, (a.K + BK - 1) / BK);
+    split = std::min(max_split, (320 + tiles - 1) / tiles);
+  }
+  int ksplit = (int)align_up((size_t)((a.K + split - 1) / split), (size_t)BK);
+  split = (a.K + ksplit - 1) / ksplit;
+  a.split = split;
+  a.ksplit = ksplit;
+  // weight-type / alignment requirements of the 8-element fragment loads
+  if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
+  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM) && (a.lda % 4 != 0 || a.K % 4 != 0))
+    return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of 4", a.lda, a.K);
+  size_t part_f = split > 1 ? (size_t)split * tiles * BM * BN : 0;
+  size_t sp = op.em == E_RESID ? (size_t)a.n_tiles_n * a.M : 0;
+  c.need_part = std::max(c.need_part, part_f);
+  c.need_tiles = std::max(c.need_tiles, (size_t)tiles);
+  c.need_sp = std::max(c.need_sp, sp);
+  KernelRef k{};
+  bool found = false;
+  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, nbw, &k);
+  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, nbw, &k);
+  else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, nbw, &k);
+  if (!found) return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d", op.wdtype, op.am, op.em, mb, wn, nbw);
+  if (c.plan) { c.kernels++; return VLA_OK; }
+  a.part = c.part;
+  a.cnt_tile = c.cnt_tile;
+  a.cnt_all = c.cnt_all;
+  if (op.em == E_RESID) a.stats_part = c.stats_part;
+  if (k.smem > 64 * 1024) VLA_TRY(allow_smem(k));
+  void* args[] = {&a};
+  return launch(c, k.fn, dim3(tiles * split), dim3(256), (size_t)k.smem, args);
+}
+
+GemmArgs gargs() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.split = 1;
+  return a;
+}
+
+// ------------------------------------------------------------------ attention
+vla_status attention(Ctx& c, AttnArgs a, bool f32) {
+  if (a.Hkv <= 0 || a.Hq % a.Hkv != 0) return fail(VLA_ERR_SHAPE, "attention: %d query heads not a multiple of %d kv heads", a.Hq, a.Hkv);
+  int dp = a.D <= 64 ? 64 : a.D <= 96 ? 96 : a.D <= 128 ? 128 : 0;
+  if (dp == 0 || a.D % 8 != 0) return fail(VLA_ERR_SHAPE, "attention: head_dim %d unsupported", a.D);
+  int group = a.Hq / a.Hkv;
+  int hpw = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  KernelRef k{};
+  if (!attn_lookup(f32 ? 1 : 0, dp, hpw, &k)) return fail(VLA_ERR_UNSUPPORTED, "attention: no kernel for D %d", a.D);
+  int rb = 4 / hpw;
+  int nrb = (a.Sq + 16 * rb - 1) / (16 * rb);
+  int grid = a.Hkv * (group / hpw) * nrb;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)a.D));
+  void* args[] = {&a};
+  return launch(c, k.fn, dim3(grid), dim3(256), 0, args);
+}
+
+vla_status stage_rows(Ctx& c, float* x, int ldx, int M, int N, const void* src, int src_f32, int ld_src, int r0, int r1,
+                      float2* stats) {
+  void* args[] = {&x, &ldx, &M, &N, &src, &src_f32, &ld_src, &r0, &r1, &stats};
+  return launch(c, k_stage_rows_ref(), dim3((M + 3) / 4), dim3(256), 0, args);
+}
+
+vla_status rmsnorm_out(Ctx& c, const float* x, int ldx, int M, int N, const float2* stats, const float* gain, float eps,
+                       void* out, int ldo, int out_f32) {
+  void* args[] = {&x, &ldx, &M, &N, &stats, &gain, &eps, &out, &ldo, &out_f32};
+  return launch(c, k_rmsnorm_out_ref(), dim3((M + 3) / 4), dim3(256), 0, args);
+}
+
+vla_status convert_rows(Ctx& c, const float* x, int ldx, int M, int N, void* out, int ldo, int out_f32) {
+  void* args[] = {&x, &ldx, &M, &N, &out, &ldo, &out_f32};
+  return launch(c, k_convert_rows_ref(), dim3((M + 3) / 4), dim3(256), 0, args);
+}
+
+bool dtype_ok(int t) { return t == VLA_F32 || t == VLA_BF16 || t == VLA_FP8_E4M3; }
+
+// ------------------------------------------------------------------ backbone
+vla_status check_block_cfg(const vla_block_cfg* cfg) {
+  if (!cfg) return fail(VLA_ERR_INVALID_ARG, "null block cfg");
+  if (cfg->flags != 0) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags must be 0");
+  if (!dtype_ok(cfg->wdtype) || (cfg->adtype != VLA_F32 && cfg->adtype != VLA_BF16))
+    return fail(VLA_ERR_INVALID_ARG, "block cfg: bad dtype (w %d, act %d)", cfg->wdtype, cfg->adtype);
+  if ((cfg->wdtype == VLA_F32) != (cfg->adtype == VLA_F32))
+    return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp32 weights need fp32 activations and vice versa");
+  if (cfg->hidden <= 0 || cfg->hidden % 8 || cfg->intermediate <= 0 || cfg->intermediate % 8)
+    return fail(VLA_ERR_SHAPE, "block cfg: hidden %d / intermediate %d must be positive multiples of 8", cfg->hidden, cfg->intermediate);
+  if (cfg->n_kv_heads <= 0 || cfg->n_q_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads)
+    return fail(VLA_ERR_SHAPE, "block cfg: n_q_heads %d not a multiple of n_kv_heads %d", cfg->n_q_heads, cfg->n_kv_heads);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return fail(VLA_ERR_SHAPE, "block cfg: head_dim %d not in {64, 128}", cfg->head_dim);
+  if (!(cfg->eps >= 0.f) || !(cfg->rope_base > 1.f)) return fail(VLA_ERR_INVALID_ARG, "block cfg: bad eps / rope_base");
+  return VLA_OK;
+}
+
+vla_status check_block_weights(const vla_block_cfg* cfg, const vla_block_weights* w) {
+  if (!w) return fail(VLA_ERR_INVALID_ARG, "null block weights");
+  if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
+    return fail(VLA_ERR_INVALID_ARG, "block weights: null tensor pointer");
+  if (cfg->wdtype == VLA_FP8_E4M3 && (!w->s_qkv || !w->s_o || !w->s_gate_up || !w->s_down))
+    return fail(VLA_ERR_INVALID_ARG, "block weights: fp8 weights need scales");
+  return VLA_OK;
+}
+
+struct BackboneBufs {
+  float* x;        // [S, H] residual
+  float2* stats;   // [S]
+  void* qkv;       // [S, Nqkv]
+  void* ao;        // [S, q_dim]
+  void* act;       // [S, I]
+};
+
+BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
+  size_t es = cfg.adtype == VLA_F32 ? 4 : 2;
+  int nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim;
+  BackboneBufs b;
+  b.x = c.take<float>((size_t)S * cfg.hidden);
+  b.stats = c.take<float2>(S);
+  b.qkv = c.take<char>((size_t)S * nqkv * es);
+  b.ao = c.take<char>((size_t)S * cfg.n_q_heads * cfg.head_dim * es);
+  b.act = c.take<char>((size_t)S * cfg.intermediate * es);
+  return b;
+}
+
+vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weights* layers, int n_layers, const BackboneBufs& b,
+                        int S) {
+  const int H = cfg.hidden, D = cfg.head_dim, qd = cfg.n_q_heads * D, kd = cfg.n_kv_heads * D;
+  const int nqkv = qd + 2 * kd, I = cfg.intermediate;
+  const bool f32 = cfg.adtype == VLA_F32;
+  const int wt = cfg.wdtype;
+  const size_t es = f32 ? 4 : 2;
+  for (int l = 0; l < n_layers; l++) {
+    const vla_block_weights& w = layers[l];
+    {  // RMSNorm -> fused QKV -> RoPE
+      GemmArgs a = gargs();
+      a.M = S; a.N = nqkv; a.K = H;
+      a.a = b.x; a.lda = H; a.stats = b.stats; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm;
+      a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
+      a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32;
+      a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_base = cfg.rope_base;
+      VLA_TRY(gemm(c, a, {wt, A_NORM, E_ROPE}));
+    }
+    {  // causal GQA attention
+      AttnArgs a{};
+      a.q = b.qkv; a.ldq = nqkv;
+      a.k = b.qkv ? (const char*)b.qkv + qd * es : nullptr; a.ldk = nqkv;
+      a.v = b.qkv ? (const char*)b.qkv + (qd + kd) * es : nullptr; a.ldv = nqkv;
+      a.o = b.ao; a.ldo = qd;
+      a.Sq = S; a.Sk = S; a.Hq = cfg.n_q_heads; a.Hkv = cfg.n_kv_heads; a.D = D; a.causal = 1;
+      VLA_TRY(attention(c, a, f32));
+    }
+    {  // O-proj + residual (+ row statistics)
+      GemmArgs a = gargs();
+      a.M = S; a.N = H; a.K = qd;
+      a.a = b.ao; a.lda = qd;
+      a.w = w.w_o; a.ldw = qd; a.wscale = w.s_o;
+      a.x = b.x; a.ldx = H; a.stats_out = b.stats;
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}));
+    }
+    {  // RMSNorm -> gate/up -> SiLU(gate) * up
+      GemmArgs a = gargs();
+      a.M = S; a.N = I; a.K = H;
+      a.a = b.x; a.lda = H; a.stats = b.stats; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm;
+      a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
+      a.c = b.act; a.ldc = I; a.c_f32 = f32;
+      VLA_TRY(gemm(c, a, {wt, A_NORM, E_SWIGLU}));
+    }
+    {  // down + residual (+ row statistics)
+      GemmArgs a = gargs();
+      a.M = S; a.N = H; a.K = I;
+      a.a = b.act; a.lda = I;
+      a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
+      a.x = b.x; a.ldx = H; a.stats_out = b.stats;
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}));
+    }
+  }
+  return VLA_OK;
+}
+
+// The scratch is laid out after the fixed buffers; plan mode sizes it from
+// what the GEMMs asked for (a schedule is run once to learn the maxima).
+template <typename Sched>
+vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out, Sched sched) {
+  // pass 0: learn scratch maxima
+  Ctx p0;
+  p0.plan = true;
+  VLA_TRY(sched(p0));
+  size_t fixed = p0.off;
+  Ctx p1;
+  p1.plan = true;
+  p1.off = fixed;
+  p1.take_scratch(p0.need_part, p0.need_tiles, p0.need_sp);
+  size_t need = p1.off;
+  if (need_out) { *need_out = need; return VLA_OK; }
+  if (!ws) return fail(VLA_ERR_INVALID_ARG, "null workspace");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(VLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  Ctx c;
+  c.plan = false; c.base = (char*)ws; c.cap = ws_bytes; c.st = st;
+  c.off = fixed;
+  c.need_part = p0.need_part; c.need_tiles = p0.need_tiles; c.need_sp = p0.need_sp;
+  c.take_scratch(p0.need_part, p0.need_tiles, p0.need_sp);
+  c.off = 0;   // fixed buffers are taken again by the schedule from offset 0
+  VLA_TRY(zero_counters(c));
+  return sched(c);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// ------------------------------------------------------------------ DiT
+vla_status check_dit(const vla_dit* d) {
+  if (!d) return fail(VLA_ERR_INVALID_ARG, "null dit");
+  const vla_dit_cfg& c = d->cfg;
+  if (c.flags != 0) return fail(VLA_ERR_UNSUPPORTED, "dit cfg flags must be 0");
+  if (c.wdtype != VLA_BF16 && c.wdtype != VLA_FP8_E4M3) return fail(VLA_ERR_UNSUPPORTED, "dit: weights must be bf16 or fp8");
+  if (c.head_dim != 80 && c.head_dim != 64) return fail(VLA_ERR_SHAPE, "dit: head_dim %d not in {64, 80}", c.head_dim);
+  if (c.heads <= 0 || c.hidden != c.heads * c.head_dim) return fail(VLA_ERR_SHAPE, "dit: hidden %d != heads*head_dim", c.hidden);
+  if (c.hidden % 8 || c.mlp % 8 || c.tdim % 8 || c.ctx_dim % 8 || c.layers <= 0 || c.mlp <= 0)
+    return fail(VLA_ERR_SHAPE, "dit: widths must be positive multiples of 8");
+  if (!d->layers || !d->w_ada || !d->b_ada || !d->w_ckv || !d->b_ckv || !d->w_t1 || !d->b_t1 || !d->w_t2 || !d->b_t2 ||
+      !d->w_f || !d->b_f || !d->w_in || !d->b_in || !d->w_out || !d->b_out)
+    return fail(VLA_ERR_INVALID_ARG, "dit: null tensor pointer");
+  for (int l = 0; l < c.layers; l++) {
+    const vla_dit_layer& L = d->layers[l];
+    if (!L.w_qkv || !L.b_qkv || !L.w_o || !L.b_o || !L.w_cq || !L.b_cq || !L.w_co || !L.b_co || !L.w_up || !L.b_up ||
+        !L.w_down || !L.b_down)
+      return fail(VLA_ERR_INVALID_ARG, "dit layer %d: null tensor pointer", l);
+    if (c.wdtype == VLA_FP8_E4M3 && (!L.s_qkv || !L.s_o || !L.s_cq || !L.s_co || !L.s_up || !L.s_down))
+      return fail(VLA_ERR_INVALID_ARG, "dit layer %d: fp8 weights need scales", l);
+  }
+  if (c.wdtype == VLA_FP8_E4M3 && (!d->s_ada || !d->s_ckv || !d->s_t1 || !d->s_t2 || !d->s_f || !d->s_in || !d->s_out))
+    return fail(VLA_ERR_INVALID_ARG, "dit: fp8 weights need scales");
+  return VLA_OK;
+}
+
+struct DitIO {
+  const void* ctx; int ctx_len;
+  const float* x0; int n, A, K;
+  float* actions; float* velocities;
+};
+
+vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
+  const vla_dit_cfg& cf = d.cfg;
+  const int D = cf.hidden, L = cf.layers, K = io.K, n = io.n, A = io.A, C = io.ctx_len;
+  const int wt = cf.wdtype;
+  const int mod_w = L * 9 * D;
+  uint16_t* t1 = c.take<uint16_t>((size_t)K * D);
+  uint16_t* sc = c.take<uint16_t>((size_t)K * D);
+  float* mod = c.take<float>((size_t)K * mod_w);
+  float* fmod = c.take<float>((size_t)K * 2 * D);
+  uint16_t* ckv = c.take<uint16_t>((size_t)C * L * 2 * D);
+  float* x = c.take<float>((size_t)n * D);
+  float2* stats = c.take<float2>(n);
+  uint16_t* qkv = c.take<uint16_t>((size_t)n * 3 * D);
+  uint16_t* ao = c.take<uint16_t>((size_t)n * D);
+  uint16_t* q = c.take<uint16_t>((size_t)n * D);
+  uint16_t* h = c.take<uint16_t>((size_t)n * cf.mlp);
+
+  {  // phi(t_k) -> Linear -> SiLU
+    GemmArgs a = gargs();
+    a.M = K; a.N = D; a.K = cf.tdim;
+    a.tsteps = K; a.time_scale = cf.time_scale; a.freq_base = cf.freq_base; a.half = cf.tdim / 2;
+    a.w = d.w_t1; a.ldw = cf.tdim; a.wscale = d.s_t1; a.bias = d.b_t1; a.act = ACT_SILU;
+    a.c = t1; a.ldc = D;
+    VLA_TRY(gemm(c, a, {wt, A_TIME, E_STORE}));
+  }
+  {  // Linear -> SiLU: SiLU(c_k) for every step
+    GemmArgs a = gargs();
+    a.M = K; a.N = D; a.K = D;
+    a.a = t1; a.lda = D;
+    a.w = d.w_t2; a.ldw = D; a.wscale = d.s_t2; a.bias = d.b_t2; a.act = ACT_SILU;
+    a.c = sc; a.ldc = D;
+    VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
+  }
+  {  // adaLN modulations of every layer for every step (one launch)
+    GemmArgs a = gargs();
+    a.M = K; a.N = mod_w; a.K = D;
+    a.a = sc; a.lda = D;
+    a.w = d.w_ada; a.ldw = D; a.wscale = d.s_ada; a.bias = d.b_ada;
+    a.c = mod; a.ldc = mod_w; a.c_f32 = 1;
+    VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
+  }
+  {  // final-layer modulation
+    GemmArgs a = gargs();
+    a.M = K; a.N = 2 * D; a.K = D;
+    a.a = sc; a.lda = D;
+    a.w = d.w_f; a.ldw = D; a.wscale = d.s_f; a.bias = d.b_f;
+    a.c = fmod; a.ldc = 2 * D; a.c_f32 = 1;
+    VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
+  }
+  {  // cross-attention K/V of every layer from the fixed context (one launch)
+    GemmArgs a = gargs();
+    a.M = C; a.N = L * 2 * D; a.K = cf.ctx_dim;
+    a.a = io.ctx; a.lda = cf.ctx_dim;
+    a.w = d.w_ckv; a.ldw = cf.ctx_dim; a.wscale = d.s_ckv; a.bias = d.b_ckv;
+    a.c = ckv; a.ldc = L * 2 * D;
+    VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
+  }
+  KernelRef tail{};
+  euler_tail_lookup(wt, &tail);
+  const size_t tail_smem = (size_t)(D + A) * sizeof(float);
+  {  // a_0 = x0 -> x = a_0 W_in^T + b_in (+ row statistics)
+    TailArgs t{};
+    t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
+    t.a_in = io.x0; t.a_out = io.actions;
+    t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.stats_out = stats;
+    void* args[] = {&t};
+    VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, args));
+  }
+  for (int k = 0; k < K; k++) {
+    for (int l = 0; l < L; l++) {
+      const vla_dit_layer& w = d.layers[l];
+      const float* m = mod ? mod + (size_t)k * mod_w + (size_t)l * 9 * D : nullptr;
+      auto mv = [&](int j) { return m ? m + (size_t)j * D : nullptr; };
+      {  // adaLN(LN) -> self-attn QKV
+        GemmArgs a = gargs();
+        a.M = n; a.N = 3 * D; a.K = D;
+        a.a = x; a.lda = D; a.stats = stats; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(1); a.g_plus_one = 1; a.bsh = mv(0);
+        a.w = w.w_qkv; a.ldw = D; a.wscale = w.s_qkv; a.bias = w.b_qkv;
+        a.c = qkv; a.ldc = 3 * D;
+        VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
+      }
+      {
+        AttnArgs a{};
+        a.q = qkv; a.ldq = 3 * D;
+        a.k = qkv ? qkv + D : nullptr; a.ldk = 3 * D;
+        a.v = qkv ? qkv + 2 * D : nullptr; a.ldv = 3 * D;
+        a.o = ao; a.ldo = D;
+        a.Sq = n; a.Sk = n; a.Hq = cf.heads; a.Hkv = cf.heads; a.D = cf.head_dim; a.causal = 0;
+        VLA_TRY(attention(c, a, false));
+      }
+      {  // O-proj, gated residual
+        GemmArgs a = gargs();
+        a.M = n; a.N = D; a.K = D;
+        a.a = ao; a.lda = D;
+        a.w = w.w_o; a.ldw = D; a.wscale = w.s_o; a.bias = w.b_o; a.gate = mv(2);
+        a.x = x; a.ldx = D; a.stats_out = stats;
+        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}));
+      }
+      {  // adaLN(LN) -> cross-attn query
+        GemmArgs a = gargs();
+        a.M = n; a.N = D; a.K = D;
+        a.a = x; a.lda = D; a.stats = stats; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(4); a.g_plus_one = 1; a.bsh = mv(3);
+        a.w = w.w_cq; a.ldw = D; a.wscale = w.s_cq; a.bias = w.b_cq;
+        a.c = q; a.ldc = D;
+        VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
+      }
+      {
+        AttnArgs a{};
+        a.q = q; a.ldq = D;
+        a.k = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.ldk = L * 2 * D;
+        a.v = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldv = L * 2 * D;
+        a.o = ao; a.ldo = D;
+        a.Sq = n; a.Sk = C; a.Hq = cf.heads; a.Hkv = cf.heads; a.D = cf.head_dim; a.causal = 0;
+        VLA_TRY(attention(c, a, false));
+      }
+      {  // cross-attn out, gated residual
+        GemmArgs a = gargs();
+        a.M = n; a.N = D; a.K = D;
+        a.a = ao; a.lda = D;
+        a.w = w.w_co; a.ldw = D; a.wscale = w.s_co; a.bias = w.b_co; a.gate = mv(5);
+        a.x = x; a.ldx = D; a.stats_out = stats;
+        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}));
+      }
+      {  // adaLN(LN) -> MLP up -> GELU
+        GemmArgs a = gargs();
+        a.M = n; a.N = cf.mlp; a.K = D;
+        a.a = x; a.lda = D; a.stats = stats; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(7); a.g_plus_one = 1; a.bsh = mv(6);
+        a.w = w.w_up; a.ldw = D; a.wscale = w.s_up; a.bias = w.b_up; a.act = ACT_GELU;
+        a.c = h; a.ldc = cf.mlp;
+        VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
+      }
+      {  // MLP down, gated residual
+        GemmArgs a = gargs();
+        a.M = n; a.N = D; a.K = cf.mlp;
+        a.a = h; a.lda = cf.mlp;
+        a.w = w.w_down; a.ldw = cf.mlp; a.wscale = w.s_down; a.bias = w.b_down; a.gate = mv(8);
+        a.x = x; a.ldx = D; a.stats_out = stats;
+        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}));
+      }
+    }
+    {  // velocity head + Euler update (+ input projection for the next step)
+      TailArgs t{};
+      t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
+      t.x = x; t.stats = stats;
+      t.shift = fmod ? fmod + (size_t)k * 2 * D : nullptr;
+      t.scale = fmod ? fmod + (size_t)k * 2 * D + D : nullptr;
+      t.w_out = d.w_out; t.s_out = d.s_out; t.b_out = d.b_out;
+      t.a_in = io.actions; t.a_out = io.actions;
+      t.v_out = io.velocities ? io.velocities + (size_t)k * n * A : nullptr;
+      if (k + 1 < K) { t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.stats_out = stats; }
+      void* args[] = {&t};
+      VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, args));
+    }
+  }
+  return VLA_OK;
+}
+
+// ------------------------------------------------------------------ ViT
+vla_status check_vit(const vla_vit* v) {
+  if (!v) return fail(VLA_ERR_INVALID_ARG, "null vit");
+  const vla_vit_cfg& c = v->cfg;
+  if (c.flags != 0) return fail(VLA_ERR_UNSUPPORTED, "vit cfg flags must be 0");
+  if (c.wdtype != VLA_BF16) return fail(VLA_ERR_UNSUPPORTED, "vit: weights must be bf16");
+  if (c.patch <= 0 || c.image % c.patch || c.merge <= 0 || (c.image / c.patch) % c.merge)
+    return fail(VLA_ERR_SHAPE, "vit: image %d / patch %d / merge %d do not tile", c.image, c.patch, c.merge);
+  if (c.head_dim != 64 || c.hidden != c.heads * c.head_dim) return fail(VLA_ERR_SHAPE, "vit: head_dim must be 64 and hidden = heads*64");
+  if (c.hidden % 8 || c.mlp % 8 || c.out_dim % 8) return fail(VLA_ERR_SHAPE, "vit: widths must be multiples of 8");
+  if (!v->layers || !v->w_pe || !v->b_pe || !v->pos || !v->mln_g || !v->mln_b || !v->w_m1 || !v->b_m1 || !v->w_m2 || !v->b_m2)
+    return fail(VLA_ERR_INVALID_ARG, "vit: null tensor pointer");
+  for (int l = 0; l < c.layers; l++) {
+    const vla_vit_layer& L = v->layers[l];
+    if (!L.ln1_g || !L.ln1_b || !L.w_qkv || !L.b_qkv || !L.w_o || !L.b_o || !L.ln2_g || !L.ln2_b || !L.w_up || !L.b_up ||
+        !L.w_down || !L.b_down)
+      return fail(VLA_ERR_INVALID_ARG, "vit layer %d: null tensor pointer", l);
+  }
+  return VLA_OK;
+}
+
+// Writes the merged tokens (fp32) to out rows [0, n_img * n_merged) with pitch ldo.
+vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, float* out, int ldo, float* vit_out) {
+  const vla_vit_cfg& cf = v.cfg;
+  const int grid = cf.image / cf.patch, np = grid * grid, S = n_img * np, D = cf.hidden;
+  const int pdim = cf.channels * cf.patch * cf.patch, pitch = (int)align_up(pdim, 8);
+  const int nm = np / (cf.merge * cf.merge), Mm = n_img * nm, MD = D * cf.merge * cf.merge;
+  float* z = c.take<float>((size_t)S * D);
+  float2* zs = c.take<float2>(S);
+  uint16_t* qkv = c.take<uint16_t>((size_t)S * 3 * D);
+  uint16_t* ao = c.take<uint16_t>((size_t)S * D);
+  uint16_t* h = c.take<uint16_t>((size_t)S * cf.mlp);
+  uint16_t* m1 = c.take<uint16_t>((size_t)Mm * MD);
+  {  // patchify -> Linear + bias + position table (+ row statistics)
+    GemmArgs a = gargs();
+    a.M = S; a.N = D; a.K = pdim;
+    a.a = images; a.img = cf.image; a.patch = cf.patch; a.chans = cf.channels; a.vgrid = grid; a.n_patches = np;
+    a.w = v.w_pe; a.ldw = pitch; a.bias = v.b_pe;
+    a.x = z; a.ldx = D; a.x_init = 1; a.addrow = v.pos; a.addrow_rows = np; a.stats_out = zs;
+    VLA_TRY(gemm(c, a, {VLA_BF16, A_PATCH, E_RESID}));
+  }
+  for (int l = 0; l < cf.layers; l++) {
+    const vla_vit_layer& w = v.layers[l];
+    {
+      GemmArgs a = gargs();
+      a.M = S; a.N = 3 * D; a.K = D;
+      a.a = z; a.lda = D; a.stats = zs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln1_g; a.bsh = w.ln1_b;
+      a.w = w.w_qkv; a.ldw = D; a.bias = w.b_qkv;
+      a.c = qkv; a.ldc = 3 * D;
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_NORM, E_STORE}));
+    }
+    {
+      AttnArgs a{};
+      a.q = qkv; a.ldq = 3 * D;
+      a.k = qkv ? qkv + D : nullptr; a.ldk = 3 * D;
+      a.v = qkv ? qkv + 2 * D : nullptr; a.ldv = 3 * D;
+      a.o = ao; a.ldo = D;
+      // images are independent sequences: one attention call per image
+      for (int i = 0; i < n_img; i++) {
+        AttnArgs ai = a;
+        if (qkv) {
+          ai.q = qkv + (size_t)i * np * 3 * D;
+          ai.k = qkv + (size_t)i * np * 3 * D + D;
+          ai.v = qkv + (size_t)i * np * 3 * D + 2 * D;
+          ai.o = ao + (size_t)i * np * D;
+        }
+        ai.Sq = np; ai.Sk = np; ai.Hq = cf.heads; ai.Hkv = cf.heads; ai.D = cf.head_dim; ai.causal = 0;
+        VLA_TRY(attention(c, ai, false));
+      }
+    }
+    {
+      GemmArgs a = gargs();
+      a.M = S; a.N = D; a.K = D;
+      a.a = ao; a.lda = D;
+      a.w = w.w_o; a.ldw = D; a.bias = w.b_o;
+      a.x = z; a.ldx = D; a.stats_out = zs;
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}));
+    }
+    {
+      GemmArgs a = gargs();
+      a.M = S; a.N = cf.mlp; a.K = D;
+      a.a = z; a.lda = D; a.stats = zs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln2_g; a.bsh = w.ln2_b;
+      a.w = w.w_up; a.ldw = D; a.bias = w.b_up; a.act = ACT_GELU;
+      a.c = h; a.ldc = cf.mlp;
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_NORM, E_STORE}));
+    }
+    {
+      GemmArgs a = gargs();
+      a.M = S; a.N = D; a.K = cf.mlp;
+      a.a = h; a.lda = cf.mlp;
+      a.w = w.w_down; a.ldw = cf.mlp; a.bias = w.b_down;
+      a.x = z; a.ldx = D; a.stats_out = zs;
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}));
+    }
+  }
+  if (vit_out) VLA_TRY(convert_rows(c, z, D, S, D, vit_out, D, 1));
+  {  // LN -> 2x2 concat -> Linear -> GELU
+    GemmArgs a = gargs();
+    a.M = Mm; a.N = MD; a.K = MD;
+    a.a = z; a.lda = D; a.stats = zs; a.norm_rms = 0; a.eps = cf.eps; a.g = v.mln_g; a.bsh = v.mln_b;
+    a.vgrid = grid; a.n_patches = np; a.merge = cf.merge; a.n_merged = nm;
+    a.w = v.w_m1; a.ldw = MD; a.bias = v.b_m1; a.act = ACT_GELU;
+    a.c = m1; a.ldc = MD;
+    VLA_TRY(gemm(c, a, {VLA_BF16, A_MERGE, E_STORE}));
+  }
+  {  // Linear -> visual tokens (fp32)
+    GemmArgs a = gargs();
+    a.M = Mm; a.N = cf.out_dim; a.K = MD;
+    a.a = m1; a.lda = MD;
+    a.w = v.w_m2; a.ldw = MD; a.bias = v.b_m2;
+    a.c = out; a.ldc = ldo; a.c_f32 = 1;
+    VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE}));
+  }
+  return VLA_OK;
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+const char* vla_last_error(void) { return g_err.c_str(); }
+int32_t vla_abi_version(void) { return VLA_ABI_VERSION; }
+
+static vla_status block_sched(Ctx& c, const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
+                              int seq) {
+  BackboneBufs b = take_backbone_bufs(c, *cfg, seq);
+  const int f32 = cfg->adtype == VLA_F32;
+  VLA_TRY(stage_rows(c, b.x, cfg->hidden, seq, cfg->hidden, x_in, f32, cfg->hidden, 0, seq, b.stats));
+  VLA_TRY(sched_layers(c, *cfg, w, 1, b, seq));
+  return convert_rows(c, b.x, cfg->hidden, seq, cfg->hidden, x_out, cfg->hidden, f32);
+}
+
+vla_status vla_block_forward(const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
+                             int32_t seq, void* ws, size_t ws_bytes, hipStream_t stream) {
+  VLA_TRY(check_block_cfg(cfg));
+  VLA_TRY(check_block_weights(cfg, w));
+  if (!x_in || !x_out) return fail(VLA_ERR_INVALID_ARG, "null input/output");
+  if (seq < 1 || seq > 4096) return fail(VLA_ERR_SHAPE, "seq %d outside [1, 4096]", seq);
+  return two_pass(ws, ws_bytes, stream, nullptr, [&](Ctx& c) { return block_sched(c, cfg, w, x_in, x_out, seq); });
+}
+
+size_t vla_block_workspace_bytes(const vla_block_cfg* cfg, int32_t seq) {
+  if (check_block_cfg(cfg) != VLA_OK || seq < 1 || seq > 4096) return 0;
+  vla_block_weights dummy{};
+  size_t need = 0;
+  if (two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return block_sched(c, cfg, &dummy, nullptr, nullptr, seq); }) != VLA_OK)
+    return 0;
+  return need;
+}
+
+static vla_status check_backbone(const vla_backbone* bb) {
+  if (!bb) return fail(VLA_ERR_INVALID_ARG, "null backbone");
+  VLA_TRY(check_block_cfg(&bb->cfg));
+  if (bb->n_layers < 1 || !bb->layers) return fail(VLA_ERR_INVALID_ARG, "backbone: no layers");
+  for (int l = 0; l < bb->n_layers; l++) VLA_TRY(check_block_weights(&bb->cfg, &bb->layers[l]));
+  return VLA_OK;
+}
+
+static vla_status backbone_sched(Ctx& c, const vla_backbone* bb, const void* embeds, int seq, void* out) {
+  const vla_block_cfg& cfg = bb->cfg;
+  BackboneBufs b = take_backbone_bufs(c, cfg, seq);
+  const int f32 = cfg.adtype == VLA_F32;
+  VLA_TRY(stage_rows(c, b.x, cfg.hidden, seq, cfg.hidden, embeds, f32, cfg.hidden, 0, seq, b.stats));
+  VLA_TRY(sched_layers(c, cfg, bb->layers, bb->n_layers, b, seq));
+  if (bb->final_norm) return rmsnorm_out(c, b.x, cfg.hidden, seq, cfg.hidden, b.stats, bb->final_norm, cfg.eps, out, cfg.hidden, f32);
+  return convert_rows(c, b.x, cfg.hidden, seq, cfg.hidden, out, cfg.hidden, f32);
+}
+
+vla_status vla_backbone_prefill(const vla_backbone* bb, const void* embeds, int32_t seq, void* hidden_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  VLA_TRY(check_backbone(bb));
+  if (!embeds || !hidden_out) return fail(VLA_ERR_INVALID_ARG, "null input/output");
+  if (seq < 1 || seq > 4096) return fail(VLA_ERR_SHAPE, "seq %d outside [1, 4096]", seq);
+  return two_pass(ws, ws_bytes, stream, nullptr, [&](Ctx& c) { return backbone_sched(c, bb, embeds, seq, hidden_out); });
+}
+
+size_t vla_backbone_workspace_bytes(const vla_backbone* bb, int32_t seq) {
+  if (!bb || check_block_cfg(&bb->cfg) != VLA_OK || seq < 1 || seq > 4096 || bb->n_layers < 1) return 0;
+  std::vector<vla_block_weights> dummy(bb->n_layers);
+  vla_backbone b2 = *bb;
+  b2.layers = dummy.data();
+  size_t need = 0;
+  if (two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return backbone_sched(c, &b2, nullptr, seq, nullptr); }) != VLA_OK)
+    return 0;
+  return need;
+}
+
+static vla_status check_dit_call(const vla_dit* d, int ctx_len, int chunk, int A, int K) {
+  if (ctx_len < 1 || ctx_len > 4096) return fail(VLA_ERR_SHAPE, "ctx_len %d outside [1, 4096]", ctx_len);
+  if (chunk < 1 || chunk > 64) return fail(VLA_ERR_SHAPE, "chunk %d outside [1, 64]", chunk);
+  if (A < 1 || A > 256) return fail(VLA_ERR_SHAPE, "action_dim %d outside [1, 256]", A);
+  if (K < 1 || K > 64) return fail(VLA_ERR_SHAPE, "K %d outside [1, 64]", K);
+  (void)d;
+  return VLA_OK;
+}
+
+vla_status vla_flow_euler_sample(const vla_dit* dit, const void* ctx, int32_t ctx_len, const float* x0, int32_t chunk,
+                                 int32_t action_dim, int32_t K, float* actions_out, float* velocities_out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  VLA_TRY(check_dit(dit));
+  VLA_TRY(check_dit_call(dit, ctx_len, chunk, action_dim, K));
+  if (!ctx || !x0 || !actions_out) return fail(VLA_ERR_INVALID_ARG, "null input/output");
+  DitIO io{ctx, ctx_len, x0, chunk, action_dim, K, actions_out, velocities_out};
+  return two_pass(ws, ws_bytes, stream, nullptr, [&](Ctx& c) { return sched_dit(c, *dit, io); });
+}
+
+size_t vla_dit_workspace_bytes(const vla_dit* dit, int32_t ctx_len, int32_t chunk, int32_t action_dim, int32_t K) {
+  if (!dit || check_dit_call(dit, ctx_len, chunk, action_dim, K) != VLA_OK) return 0;
+  std::vector<vla_dit_layer> dummy(dit->cfg.layers > 0 ? dit->cfg.layers : 1);
+  vla_dit d2 = *dit;
+  d2.layers = dummy.data();
+  DitIO io{nullptr, ctx_len, nullptr, chunk, action_dim, K, nullptr, nullptr};
+  size_t need = 0;
+  if (two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return sched_dit(c, d2, io); }) != VLA_OK) return 0;
+  return need;
+}
+
+vla_status vla_vit_encode(const vla_vit* vit, const void* images, int32_t n_images, float* tokens_out, float* vit_out,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  VLA_TRY(check_vit(vit));
+  if (!images || !tokens_out) return fail(VLA_ERR_INVALID_ARG, "null input/output");
+  if (n_images < 1 || n_images > 16) return fail(VLA_ERR_SHAPE, "n_images %d outside [1, 16]", n_images);
+  return two_pass(ws, ws_bytes, stream, nullptr,
+                  [&](Ctx& c) { return sched_vit(c, *vit, images, n_images, tokens_out, vit->cfg.out_dim, vit_out); });
+}
+
+size_t vla_vit_workspace_bytes(const vla_vit* vit, int32_t n_images) {
+  if (!vit || n_images < 1 || n_images > 16) return 0;
+  std::vector<vla_vit_layer> dummy(vit->cfg.layers > 0 ? vit->cfg.layers : 1);
+  vla_vit v2 = *vit;
+  v2.layers = dummy.data();
+  size_t need = 0;
+  if (two_pass(nullptr, 0, nullptr, &need,
+               [&](Ctx& c) { return sched_vit(c, v2, nullptr, n_images, nullptr, v2.cfg.out_dim, nullptr); }) != VLA_OK)
+    return 0;
+  return need;
+}
+
+}  // extern "C"
+
+// ================================================================== step plan
+struct vla_step_plan {
+  // deep copies of the host-side descriptors
+  vla_vit vit{};
+  bool has_vit = false;
+  std::vector<vla_vit_layer> vit_layers;
+  vla_backbone bb{};
+  std::vector<vla_block_weights> bb_layers;
+  vla_dit dit{};
+  std::vector<vla_dit_layer> dit_layers;
+  const void* w_proj = nullptr; const float* s_proj = nullptr; const float* b_proj = nullptr;
+  vla_step_shape shape{};
+  vla_step_io io{};
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int nodes = 0;
+};
+
+namespace {
+
+vla_status step_sched(Ctx& c, const vla_step_plan& P) {
+  const vla_block_cfg& cfg = P.bb.cfg;
+  const int H = cfg.hidden;
+  int n_vis = 0;
+  if (P.has_vit) {
+    const int grid = P.vit.cfg.image / P.vit.cfg.patch;
+    n_vis = P.shape.n_images * (grid * grid) / (P.vit.cfg.merge * P.vit.cfg.merge);
+  }
+  const int S = n_vis + P.shape.n_text;
+  BackboneBufs b = take_backbone_bufs(c, cfg, S);
+  uint16_t* hid = c.take<uint16_t>((size_t)S * H);
+  uint16_t* ctx = c.take<uint16_t>((size_t)S * P.dit.cfg.ctx_dim);
+  if (P.has_vit) VLA_TRY(sched_vit(c, P.vit, P.io.images, P.shape.n_images, b.x, H, nullptr));
+  VLA_TRY(stage_rows(c, b.x, H, S, H, P.io.text, 0, H, n_vis, S, b.stats));
+  VLA_TRY(sched_layers(c, cfg, P.bb.layers, P.bb.n_layers, b, S));
+  VLA_TRY(rmsnorm_out(c, b.x, H, S, H, b.stats, P.bb.final_norm, cfg.eps, hid, H, 0));
+  if (P.io.hidden_out) VLA_TRY(rmsnorm_out(c, b.x, H, S, H, b.stats, P.bb.final_norm, cfg.eps, P.io.hidden_out, H, 0));
+  {  // projector to the action expert's context width
+    GemmArgs a = gargs();
+    a.M = S; a.N = P.dit.cfg.ctx_dim; a.K = H;
+    a.a = hid; a.lda = H;
+    a.w = P.w_proj; a.ldw = H; a.wscale = P.s_proj; a.bias = P.b_proj;
+    a.c = ctx; a.ldc = P.dit.cfg.ctx_dim;
+    VLA_TRY(gemm(c, a, {cfg.wdtype, A_BF16, E_STORE}));
+  }
+  DitIO io{ctx, S, P.io.noise, P.shape.chunk, P.shape.action_dim, P.shape.steps, P.io.actions, P.io.velocities};
+  return sched_dit(c, P.dit, io);
+}
+
+vla_status check_step(const vla_model* m, const vla_step_shape* s) {
+  if (!m || !s) return fail(VLA_ERR_INVALID_ARG, "null model/shape");
+  VLA_TRY(check_backbone(m->backbone));
+  if (m->backbone->cfg.adtype != VLA_BF16) return fail(VLA_ERR_UNSUPPORTED, "step: backbone activations must be bf16");
+  if (!m->backbone->final_norm) return fail(VLA_ERR_INVALID_ARG, "step: backbone final_norm required");
+  VLA_TRY(check_dit(m->dit));
+  if (m->dit->cfg.wdtype != m->backbone->cfg.wdtype) return fail(VLA_ERR_UNSUPPORTED, "step: backbone and DiT weight dtypes differ");
+  if (!m->w_proj || !m->b_proj) return fail(VLA_ERR_INVALID_ARG, "step: null projector");
+  if (m->backbone->cfg.wdtype == VLA_FP8_E4M3 && !m->s_proj) return fail(VLA_ERR_INVALID_ARG, "step: fp8 projector needs scales");
+  if (s->n_images < 0 || s->n_text < 0) return fail(VLA_ERR_SHAPE, "step: negative token counts");
+  if (s->n_images > 0) {
+    VLA_TRY(check_vit(m->vit));
+    if (m->vit->cfg.out_dim != m->backbone->cfg.hidden) return fail(VLA_ERR_SHAPE, "step: vit out_dim != backbone hidden");
+    if (s->n_images > 16) return fail(VLA_ERR_SHAPE, "step: n_images %d > 16", s->n_images);
+  }
+  int n_vis = 0;
+  if (s->n_images > 0) {
+    int g = m->vit->cfg.image / m->vit->cfg.patch;
+    n_vis = s->n_images * g * g / (m->vit->cfg.merge * m->vit->cfg.merge);
+  }
+  int S = n_vis + s->n_text;
+  if (S < 1 || S > 4096) return fail(VLA_ERR_SHAPE, "step: sequence %d outside [1, 4096]", S);
+  VLA_TRY(check_dit_call(m->dit, S, s->chunk, s->action_dim, s->steps));
+  return VLA_OK;
+}
+
+void fill_plan(vla_step_plan& P, const vla_model* m, const vla_step_shape* s) {
+  P.shape = *s;
+  P.has_vit = s->n_images > 0;
+  if (P.has_vit) {
+    P.vit = *m->vit;
+    P.vit_layers.assign(m->vit->layers, m->vit->layers + m->vit->cfg.layers);
+    P.vit.layers = P.vit_layers.data();
+  }
+  P.bb = *m->backbone;
+  P.bb_layers.assign(m->backbone->layers, m->backbone->layers + m->backbone->n_layers);
+  P.bb.layers = P.bb_layers.data();
+  P.dit = *m->dit;
+  P.dit_layers.assign(m->dit->layers, m->dit->layers + m->dit->cfg.layers);
+  P.dit.layers = P.dit_layers.data();
+  P.w_proj = m->w_proj; P.s_proj = m->s_proj; P.b_proj = m->b_proj;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vla_step_workspace_bytes(const vla_model* model, const vla_step_shape* shape) {
+  if (check_step(model, shape) != VLA_OK) return 0;
+  vla_step_plan P;
+  fill_plan(P, model, shape);
+  size_t need = 0;
+  if (two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, P); }) != VLA_OK) return 0;
+  return need;
+}
+
+vla_status vla_step_plan_create(const vla_model* model, const vla_step_shape* shape, const vla_step_io* io, void* ws,
+                                size_t ws_bytes, vla_step_plan** out) {
+  if (!out) return fail(VLA_ERR_INVALID_ARG, "null plan out pointer");
+  *out = nullptr;
+  VLA_TRY(check_step(model, shape));
+  if (!io || !io->text || !io->noise || !io->actions || (shape->n_images > 0 && !io->images))
+    return fail(VLA_ERR_INVALID_ARG, "step io: null buffer");
+  vla_step_plan* P = new vla_step_plan();
+  fill_plan(*P, model, shape);
+  P->io = *io;
+  size_t need = 0;
+  vla_status s = two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, *P); });
+  if (s != VLA_OK) { delete P; return s; }
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) { delete P; return fail(VLA_ERR_INVALID_ARG, "workspace null or not 256-byte aligned"); }
+  if (ws_bytes < need) { delete P; return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need); }
+  P->ws = ws;
+  P->ws_bytes = ws_bytes;
+  *out = P;
+  return VLA_OK;
+}
+
+vla_status vla_step_run(vla_step_plan* plan, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  return two_pass(plan->ws, plan->ws_bytes, stream, nullptr, [&](Ctx& c) { return step_sched(c, *plan); });
+}
+
+vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  if (plan->exec) return fail(VLA_ERR_STATE, "plan already captured");
+  // warm-up pass (also clears the self-resetting split-K counters)
+  VLA_TRY(vla_step_run(plan, stream));
+  hipStream_t cs = nullptr;
+  VLA_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  VLA_HIP(hipStreamSynchronize(stream));
+  vla_status s = VLA_OK;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) { (void)hipStreamDestroy(cs); return fail(VLA_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)); }
+  {
+    // The counters are already zero after the warm-up pass and every kernel
+    // leaves them zero, so the captured pass launches no clearing node.
+    Ctx p0;
+    p0.plan = true;
+    s = step_sched(p0, *plan);
+    if (s == VLA_OK) {
+      size_t fixed = p0.off;
+      Ctx c;
+      c.plan = false; c.base = (char*)plan->ws; c.cap = plan->ws_bytes; c.st = cs;
+      c.off = fixed;
+      c.need_part = p0.need_part; c.need_tiles = p0.need_tiles; c.need_sp = p0.need_sp;
+      c.take_scratch(p0.need_part, p0.need_tiles, p0.need_sp);
+      c.off = 0;
+      s = step_sched(c, *plan);
+      plan->nodes = c.kernels;
+    }
+  }
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (s != VLA_OK) { if (g) (void)hipGraphDestroy(g); return s; }
+  if (e != hipSuccess) return fail(VLA_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) { (void)hipGraphDestroy(g); return fail(VLA_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e)); }
+  plan->graph = g;
+  plan->exec = ex;
+  return VLA_OK;
+}
+
+vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  if (!plan->exec) return fail(VLA_ERR_STATE, "plan not captured");
+  VLA_HIP(hipGraphLaunch(plan->exec, stream));
+  return VLA_OK;
+}
+
+int32_t vla_step_graph_nodes(const vla_step_plan* plan) { return plan && plan->exec ? plan->nodes : 0; }
+
+void vla_step_plan_destroy(vla_step_plan* plan) {
+  if (!plan) return;
+  if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
+  if (plan->graph) (void)hipGraphDestroy(plan->graph);
+  delete plan;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device-side building blocks shared by the kernels of libvla (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vla {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- scalar conversion
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// ---------------------------------------------------------------- 8-wide fragments
+// A fragment is the 8 contraction-dimension values one lane contributes to a
+// 16x16x32 MFMA step. For bf16 it is one bf16x8 register quad; for fp32 it is
+// 8 floats fed to 8 consecutive 16x16x4 fp32 MFMAs. Lane group g = lane/16
+// owns contraction indices 8g..8g+7 of each 32-wide step in both cases (for
+// fp32, MFMA j pairs index 8g+j of A with 8g+j of B), so any operand loaded
+// with that convention on both sides contracts correctly.
+struct FragBF16 {
+  bf16x8 v;
+};
+struct FragF32 {
+  f32x4 lo, hi;
+};
+
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { using type = FragBF16; };
+template <> struct Frag<float> { using type = FragF32; };
+
+__device__ __forceinline__ void mma32(f32x4& acc, const FragBF16& a, const FragBF16& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma32(f32x4& acc, const FragF32& a, const FragF32& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ FragBF16 zero_frag(FragBF16) {
+  FragBF16 f;
+  f.v = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  return f;
+}
+__device__ __forceinline__ FragF32 zero_frag(FragF32) {
+  FragF32 f;
+  f.lo = (f32x4){0, 0, 0, 0};
+  f.hi = (f32x4){0, 0, 0, 0};
+  return f;
+}
+
+// Build a fragment from 8 floats (rounding to bf16 when needed).
+__device__ __forceinline__ void frag_from_floats(FragBF16& f, const float* x) {
+  uint4 u;
+  u.x = pack_bf2(x[0], x[1]);
+  u.y = pack_bf2(x[2], x[3]);
+  u.z = pack_bf2(x[4], x[5]);
+  u.w = pack_bf2(x[6], x[7]);
+  f.v = __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void frag_from_floats(FragF32& f, const float* x) {
+  f.lo = (f32x4){x[0], x[1], x[2], x[3]};
+  f.hi = (f32x4){x[4], x[5], x[6], x[7]};
+}
+
+// ---------------------------------------------------------------- fp8 (OCP E4M3FN, gfx950 native)
+// 8 codes (two dwords) -> bf16 fragment. Every E4M3FN value is exact in bf16.
+__device__ __forceinline__ FragBF16 fp8x8_to_frag(uint2 codes) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, 1.0f, false);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, 1.0f, true);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, 1.0f, false);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, 1.0f, true);
+  FragBF16 f;
+  f.v = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return f;
+}
+
+__device__ __forceinline__ float fp8_to_f32(uint8_t c) {
+  f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+  return v[0];
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Exact GELU z * Phi(z) and SiLU z / (1 + e^-z), with the device math library.
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Chan et al. pairwise merge of (count, mean, M2) partial moments.
+__device__ __forceinline__ void moments_merge(float& n, float& mean, float& m2, float nb, float meanb, float m2b) {
+  if (nb <= 0.f) return;
+  float nn = n + nb;
+  float d = meanb - mean;
+  mean += d * (nb / nn);
+  m2 += m2b + d * d * (n * nb / nn);
+  n = nn;
+}
+
+}  // namespace vla

@@ -1,0 +1,17 @@
+// GEMM instantiations for fp8 (OCP E4M3FN) weights with per-row scales:
+// codes are widened to bf16 in registers (exact), bf16 MFMA, fp32 accumulate,
+// scale applied per output column in the epilogue.
+#include "gemm_inst.h"
+
+namespace vla {
+bool gemm_lookup_fp8(int am, int em, int mb, int wn, int nbw, KernelRef* out) {
+  VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_STORE)
+  VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_RESID)
+  VLA_GEMM_NARROW(uint8_t, __bf16, A_NORM, E_STORE)
+  VLA_GEMM_WIDE(uint8_t, __bf16, A_NORM, E_ROPE)
+  VLA_GEMM_WIDE(uint8_t, __bf16, A_NORM, E_SWIGLU)
+  VLA_GEMM_CASE(uint8_t, __bf16, A_TIME, E_STORE, 1, 1, 1)
+  VLA_GEMM_CASE(uint8_t, __bf16, A_TIME, E_STORE, 4, 4, 1)
+  return false;
+}
+}  // namespace vla

@@ -1,0 +1,27 @@
+// Host-visible lookup of the kernel instantiations compiled into libvla.
+#pragma once
+#include <stddef.h>
+
+namespace vla {
+
+struct KernelRef {
+  const void* fn;
+  int smem;  // dynamic LDS bytes
+};
+
+// GEMM: wt 0 = f32, 1 = bf16, 2 = fp8 (vla_dtype values); am / em from gemm.h.
+bool gemm_lookup_f32(int am, int em, int mb, int wn, int nbw, KernelRef* out);
+bool gemm_lookup_bf16(int am, int em, int mb, int wn, int nbw, KernelRef* out);
+bool gemm_lookup_fp8(int am, int em, int mb, int wn, int nbw, KernelRef* out);
+
+// Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
+bool attn_lookup(int f32, int dp, int hpw, KernelRef* out);
+
+// Misc kernels.
+const void* k_fill_ref();
+const void* k_stage_rows_ref();
+const void* k_rmsnorm_out_ref();
+const void* k_convert_rows_ref();
+bool euler_tail_lookup(int wt, KernelRef* out);
+
+}  // namespace vla

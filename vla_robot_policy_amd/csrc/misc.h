@@ -1,0 +1,123 @@
+// Small kernels around the GEMMs: input staging with row statistics, the
+// standalone final norm, the fused Euler tail of the flow sampler, and a fill.
+#pragma once
+#include "common.h"
+#include "tail.h"
+
+namespace vla {
+
+// Fill n uint32 words with a value (used instead of a memset node so the
+// clearing of counters can sit inside a captured graph).
+__global__ void k_fill_u32(unsigned* p, unsigned v, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// x[r] = src[r - r0] for r in [r0, r1) (bf16 or fp32 source), then per-row
+// (mean, biased variance) of x for every row r < M. One wave per row.
+__global__ __launch_bounds__(256) void k_stage_rows(float* x, int ldx, int M, int N, const void* src, int src_f32,
+                                                  int ld_src, int r0, int r1, float2* stats) {
+  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (r >= M) return;
+  float* xr = x + (size_t)r * ldx;
+  if (src && r >= r0 && r < r1) {
+    for (int c = lane; c < N; c += 64) {
+      size_t o = (size_t)(r - r0) * ld_src + c;
+      xr[c] = src_f32 ? ((const float*)src)[o] : bf2f(((const uint16_t*)src)[o]);
+    }
+  }
+  float s = 0.f;
+  for (int c = lane; c < N; c += 64) s += xr[c];
+  float mean = wave_sum(s) / (float)N;
+  float q = 0.f;
+  for (int c = lane; c < N; c += 64) { float d = xr[c] - mean; q += d * d; }
+  float var = wave_sum(q) / (float)N;
+  if (lane == 0) stats[r] = make_float2(mean, var);
+}
+
+// out[r] = RMSNorm(x[r]) * gain, from the row statistics (mean, var).
+__global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, int M, int N, const float2* stats,
+                                                   const float* gain, float eps, void* out, int ldo, int out_f32) {
+  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (r >= M) return;
+  float2 st = stats[r];
+  float rs = rsqrtf(st.y + st.x * st.x + eps);
+  for (int c = lane; c < N; c += 64) {
+    float v = x[(size_t)r * ldx + c] * rs * gain[c];
+    if (out_f32) ((float*)out)[(size_t)r * ldo + c] = v;
+    else ((uint16_t*)out)[(size_t)r * ldo + c] = f2bf(v);
+  }
+}
+
+template <typename WT> __device__ __forceinline__ float wget(const void* w, size_t i);
+template <> __device__ __forceinline__ float wget<uint16_t>(const void* w, size_t i) { return bf2f(((const uint16_t*)w)[i]); }
+template <> __device__ __forceinline__ float wget<float>(const void* w, size_t i) { return ((const float*)w)[i]; }
+template <> __device__ __forceinline__ float wget<uint8_t>(const void* w, size_t i) { return fp8_to_f32(((const uint8_t*)w)[i]); }
+
+
+
+// One workgroup per action row m:
+//   v = (LN(x_m)(1 + scale) + shift) W_out^T + b_out;  a_m <- a_m + v / K
+//   x_m <- a_m W_in^T + b_in, with its (mean, var) for the next LayerNorm.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
+  extern __shared__ __align__(16) float sh[];
+  float* su = sh;                 // [D]
+  float* sa = sh + p.D;           // [A]
+  __shared__ float red[8];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* arow = p.a_in + (size_t)m * p.A;
+  if (p.w_out) {
+    float2 st = p.stats[m];
+    float rs = rsqrtf(st.y + p.eps);
+    for (int d = tid; d < p.D; d += 256)
+      su[d] = (p.x[(size_t)m * p.D + d] - st.x) * rs * (1.f + p.scale[d]) + p.shift[d];
+    __syncthreads();
+    for (int a = wave; a < p.A; a += 4) {
+      float acc = 0.f;
+      for (int d = lane; d < p.D; d += 64) acc += su[d] * wget<WT>(p.w_out, (size_t)a * p.D + d);
+      acc = wave_sum(acc);
+      if (lane == 0) {
+        float v = acc * (p.s_out ? p.s_out[a] : 1.f) + p.b_out[a];
+        if (p.v_out) p.v_out[(size_t)m * p.A + a] = v;
+        float an = arow[a] + v / (float)p.K;
+        sa[a] = an;
+      }
+    }
+    __syncthreads();
+    for (int a = tid; a < p.A; a += 256) p.a_out[(size_t)m * p.A + a] = sa[a];
+  } else {
+    for (int a = tid; a < p.A; a += 256) {
+      sa[a] = arow[a];
+      if (p.a_out != p.a_in) p.a_out[(size_t)m * p.A + a] = arow[a];
+    }
+  }
+  __syncthreads();
+  if (!p.w_in) return;
+  float s = 0.f;
+  for (int d = tid; d < p.D; d += 256) {
+    float acc = p.b_in[d];
+    float sc = p.s_in ? p.s_in[d] : 1.f;
+    float dot = 0.f;
+    for (int a = 0; a < p.A; a++) dot += sa[a] * wget<WT>(p.w_in, (size_t)d * p.A + a);
+    acc += dot * sc;
+    p.x_out[(size_t)m * p.D + d] = acc;
+    su[d] = acc;
+    s += acc;
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  float mean = (red[0] + red[1] + red[2] + red[3]) / (float)p.D;
+  __syncthreads();
+  float q = 0.f;
+  for (int d = tid; d < p.D; d += 256) { float dd = su[d] - mean; q += dd * dd; }
+  q = wave_sum(q);
+  if (lane == 0) red[4 + wave] = q;
+  __syncthreads();
+  if (tid == 0) p.stats_out[m] = make_float2(mean, (red[4] + red[5] + red[6] + red[7]) / (float)p.D);
+}
+
+}  // namespace vla
