@@ -1,0 +1,225 @@
+"""Benchmark of the batch-1 VLA policy step on one MI355X.
+
+Workload (default): the full single-camera step — ViT (24 layers, 224x224
+image, 14-px patches) -> 2x2 merger -> 36-layer GQA backbone at 104 tokens ->
+projector -> 36-layer DiT in a 4-step flow-matching Euler loop — captured
+once as a hipGraph by libvla and replayed; seeded synthetic weights and
+inputs of that architecture, bf16. One JSON line on stdout.
+
+  python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per VLA step at batch 1 (36L backbone + K-step DiT) + % of MFMA/HBM roofline"
+WORKLOADS = {
+    2: "36-layer backbone prefill, seq 256, bf16 (hidden 2560, GQA 32/8 x 128, SwiGLU 9728), final RMSNorm",
+    3: "DiT flow-matching sampler, bf16: 36 layers x 4 Euler steps, chunk 16x7, 256 context tokens",
+    4: ("full single-camera VLA step, bf16: ViT 24L (224x224, 14-px patches) -> 2x2 merger -> 36L backbone "
+        "at seq 104 (64 visual + 40 text) -> projector -> DiT 36L x 4 Euler steps; one hipGraph"),
+    5: ("two-camera long-context step, fp8 e4m3 weights (per-channel scales), bf16 activations: 36L backbone "
+        "at seq 560 -> projector -> DiT 36L x 10 Euler steps, chunk 50x32; one hipGraph"),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gpu_step_bench(cfg, steps, warmup, kernel_reps):
+    import numpy as np
+    import torch
+    from synth import make_inputs, make_weights
+    from vla_robot_policy_amd import lib
+    from vla_robot_policy_amd.device import DeviceWeights, upload_input, workspace
+
+    t0 = time.time()
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = DeviceWeights(cfg, W, keep_host=False, threads=16)
+    if cfg.kind == "step":
+        model = dw.build_model()
+    log(f"weights generated and uploaded in {time.time() - t0:.1f}s")
+    d = cfg.dit
+    dev = torch.device("cuda:0")
+    images = upload_input(I["image"]) if cfg.vit is not None else None
+    text = upload_input(I["text"])
+    noise = upload_input(I["noise"])
+    actions = torch.empty((d.chunk, d.action_dim), dtype=torch.float32, device=dev)
+    shape = lib.StepShape(n_images=cfg.n_images, n_text=cfg.n_text, chunk=d.chunk, action_dim=d.action_dim,
+                          steps=cfg.steps)
+    io = lib.StepIO(images=None if images is None else images.data_ptr(), text=text.data_ptr(),
+                    noise=noise.data_ptr(), actions=actions.data_ptr(), hidden_out=None, velocities=None)
+    need = lib.vla_step_workspace_bytes(model, shape)
+    ws = workspace(need)
+    st, plan = lib.vla_step_plan_create(model, shape, io, ws, need)
+    lib.check(st)
+    stream = torch.cuda.current_stream().cuda_stream
+    lib.check(lib.vla_step_capture(plan, stream))
+    nodes = lib.vla_step_graph_nodes(plan)
+    log(f"captured {nodes} kernel nodes")
+    for _ in range(warmup):
+        lib.check(lib.vla_step_replay(plan, stream))
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        lib.check(lib.vla_step_replay(plan, stream))
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    total_ms = evs[0].elapsed_time(evs[steps])
+    log(f"{steps} replays: mean {total_ms / steps:.3f} ms, p50 {np.median(per):.3f} ms")
+    # per-kernel durations: each captured kernel relaunched alone between events
+    labels = [lib.vla_step_kernel_label(plan, i) for i in range(nodes)]
+    first, count = {}, {}
+    for i, lb in enumerate(labels):
+        first.setdefault(lb, i)
+        count[lb] = count.get(lb, 0) + 1
+    kern = {}
+    for lb, i in first.items():
+        lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(kernel_reps):
+            lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+        e1.record()
+        torch.cuda.synchronize()
+        kern[lb] = {"avg_us": e0.elapsed_time(e1) * 1e3 / kernel_reps, "count": count[lb]}
+    lib.check(lib.vla_step_replay(plan, stream))   # restore a consistent state
+    torch.cuda.synchronize()
+    lib.vla_step_plan_destroy(plan)
+    return {"ms": total_ms / steps, "p50": float(np.median(per)), "p90": float(np.percentile(per, 90)),
+            "nodes": nodes, "kernels": kern}
+
+
+def cpu_baseline(cfg, reps: int = 2):
+    """Oracle (float64 NumPy, as it stands) on a bounded sample of the step:
+    `reps` layers of each repeated block type at the workload's shapes, the
+    mean per layer scaled by the number of such layers in one step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from synth import make_weights
+    from oracle import dit as odit, llm as ollm, vit as ovit
+    from oracle.io import Weights
+
+    rng = np.random.default_rng(0)
+    W = Weights(make_weights(cfg), keep=True)
+    parts = {}
+
+    def clock(key, n_per_step, fn):
+        fn(0)                                    # converts this layer's weights once
+        t = time.time()
+        for l in range(reps):
+            fn(l)
+        parts[key] = ((time.time() - t) / reps, n_per_step)
+
+    x = rng.standard_normal((cfg.seq, cfg.block.hidden))
+    for l in range(reps):
+        ollm.block(x[:4], W, f"llm.{l}.", cfg.block)
+    clock("llm_layer", cfg.layers, lambda l: ollm.block(x, W, f"llm.{l}.", cfg.block))
+    if cfg.vit is not None:
+        v = cfg.vit
+        z = rng.standard_normal((v.n_patches, v.hidden))
+
+        def vit_layer(l):
+            p = f"vit.{l}."
+            u = z
+            from oracle import ops
+            a = ops.layernorm(u, W[p + "ln1_g"], W[p + "ln1_b"], v.eps)
+            q = ops.linear(a, W[p + "wq"], W[p + "bq"]).reshape(-1, v.heads, v.head_dim)
+            k = ops.linear(a, W[p + "wk"], W[p + "bk"]).reshape(-1, v.heads, v.head_dim)
+            vv = ops.linear(a, W[p + "wv"], W[p + "bv"]).reshape(-1, v.heads, v.head_dim)
+            u = u + ops.linear(ops.attention(q, k, vv, False).reshape(len(u), -1), W[p + "wo"], W[p + "bo"])
+            a = ops.layernorm(u, W[p + "ln2_g"], W[p + "ln2_b"], v.eps)
+            return u + ops.linear(ops.gelu(ops.linear(a, W[p + "w1"], W[p + "b1"])), W[p + "w2"], W[p + "b2"])
+        for l in range(reps):
+            vit_layer(l)
+        clock("vit_layer", v.layers * cfg.n_images, vit_layer)
+    d = cfg.dit
+    xa = rng.standard_normal((d.chunk, d.hidden))
+    sc = rng.standard_normal(d.hidden)
+    ctx = rng.standard_normal((cfg.ctx_len, d.ctx_dim))
+    for l in range(reps):
+        odit.dit_layer(xa, sc, ctx, W, f"dit.{l}.", d)
+    clock("dit_layer_step", d.layers * cfg.steps, lambda l: odit.dit_layer(xa, sc, ctx, W, f"dit.{l}.", d))
+    est = sum(s * n for s, n in parts.values())
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(est * 1e3, 1), "unit": "ms per step (extrapolated)", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 oracle, mean over {reps} layers of each repeated block at the workload's shapes: "
+                       + ", ".join(f"{k} {s * 1e3:.1f} ms x {n}" for k, (s, n) in parts.items())
+                       + "; once-per-step parts (patch embed, merger, projector, time MLP, heads) omitted")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from synth import get_config
+    from vla_robot_policy_amd import roofline
+    cfg = get_config(a.config)
+    if cfg.kind != "step":
+        raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
+    r = gpu_step_bench(cfg, a.steps, a.warmup, a.kernel_reps)
+    b = roofline.bound(cfg)
+    ops = {o.name: o for o in b.ops}
+    # dominant kernel: largest (per-launch duration x launches per step)
+    dom = max(r["kernels"].items(), key=lambda kv: kv[1]["avg_us"] * kv[1]["count"])
+    name, kd = dom
+    roof = None
+    if name in ops:
+        o = ops[name]
+        peaks = roofline.MI355X
+        hbm_bound = o.bytes / peaks["hbm"] >= o.flops / peaks[o.compute]
+        dur = kd["avg_us"] * 1e-6
+        if hbm_bound:
+            ach, peak, unit = o.bytes / dur / 1e9, peaks["hbm"] / 1e9, "GB/s"
+        else:
+            ach, peak, unit = o.flops / dur / 1e12, peaks[o.compute] / 1e12, "TFLOP/s"
+        roof = {"kernel": name, "bound": "hbm" if hbm_bound else "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+                "avg_launch_us": round(kd["avg_us"], 2), "launches_per_step": kd["count"],
+                "algorithmic_bytes_per_launch": o.bytes, "flops_per_launch": o.flops}
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(cfg)
+    ms = r["ms"]
+    line = {
+        "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOADS[a.config], "global_batch": 1, "seq_len": cfg.seq,
+                   "euler_steps": cfg.steps, "parallelism": "single GPU"},
+        "hz": round(1000.0 / ms, 2), "p50_ms": round(r["p50"], 4), "p90_ms": round(r["p90"], 4),
+        "tokens_per_s": round(cfg.seq / (ms * 1e-3), 1),
+        "roofline_bound_ms": round(b.seconds * 1e3, 4), "roofline_frac_step": round(b.seconds * 1e3 / ms, 4),
+        "graph_nodes": r["nodes"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: {"avg_us": round(v["avg_us"], 2), "count": v["count"]} for k, v in sorted(r["kernels"].items())},
+        "pages_context": {"starvla_rtx4090_ms": 32.0, "pi05_rtx4090_bf16_ms": 31.38, "pi05_thor_fp8_ms": 26.32},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

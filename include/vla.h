@@ -254,6 +254,15 @@ vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream);
 vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream);
 /* Kernel nodes in the captured graph (0 before capture). */
 int32_t vla_step_graph_nodes(const vla_step_plan* plan);
+/* Name of the operation of captured kernel `index` (0 <= index < nodes),
+ * e.g. "llm.gate_up", "dit.mlp_down"; NULL when out of range. */
+const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index);
+/* Launch captured kernel `index` once more, on its own, on `stream` (for
+ * timing one kernel with events). It reads and writes the plan's workspace
+ * as in the graph, so intermediate buffers hold arbitrary values afterwards;
+ * the next vla_step_run / vla_step_replay recomputes everything from the
+ * inputs. Valid only after vla_step_capture. */
+vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_t stream);
 void vla_step_plan_destroy(vla_step_plan* plan);
 
 /* ------------------------------------------------------------------ misc */

@@ -55,6 +55,23 @@ vla_status fail(vla_status s, const char* fmt, ...) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// One recorded kernel launch of a schedule (kept by step plans so a single
+// kernel can be relaunched on its own for timing).
+struct LaunchRec {
+  std::string label;
+  const void* fn;
+  dim3 grid, block;
+  size_t smem;
+  std::vector<std::vector<char>> args;
+};
+
+struct ArgRef {
+  const void* p;
+  size_t n;
+};
+template <typename T>
+ArgRef arg(const T& v) { return ArgRef{&v, sizeof(T)}; }
+
 struct Ctx {
   bool plan;               // plan mode: size buffers, launch nothing
   char* base;              // workspace base (launch mode)
@@ -62,12 +79,12 @@ struct Ctx {
   size_t off = 0;
   hipStream_t st = nullptr;
   // shared GEMM scratch (requirements gathered in plan mode)
-  size_t need_part = 0, need_tiles = 0, need_sp = 0;
+  size_t need_part = 0, need_tiles = 0;
   float* part = nullptr;
   unsigned* cnt_tile = nullptr;
-  unsigned* cnt_all = nullptr;
-  float2* stats_part = nullptr;
   int kernels = 0;         // launches issued (or that would be issued)
+  const char* label = "";  // name of the operation being launched
+  std::vector<LaunchRec>* recs = nullptr;
 
   template <typename T>
   T* take(size_t n) {
@@ -77,18 +94,26 @@ struct Ctx {
     return p;
   }
   // Lay out the split-K scratch after the fixed buffers.
-  void take_scratch(size_t part_f, size_t tiles, size_t sp) {
+  void take_scratch(size_t part_f, size_t tiles) {
     part = take<float>(std::max<size_t>(part_f, 1));
     cnt_tile = take<unsigned>(tiles + 1);
-    cnt_all = cnt_tile + tiles;
-    stats_part = take<float2>(std::max<size_t>(sp, 1));
   }
 };
 
-vla_status launch(Ctx& c, const void* fn, dim3 grid, dim3 block, size_t smem, void** args) {
+vla_status launch(Ctx& c, const void* fn, dim3 grid, dim3 block, size_t smem, std::initializer_list<ArgRef> args) {
   c.kernels++;
   if (c.plan) return VLA_OK;
-  VLA_HIP(hipLaunchKernel(fn, grid, block, args, smem, c.st));
+  void* ptrs[16];
+  int i = 0;
+  for (const ArgRef& a : args) ptrs[i++] = const_cast<void*>(a.p);
+  VLA_HIP(hipLaunchKernel(fn, grid, block, ptrs, smem, c.st));
+  if (c.recs) {
+    LaunchRec r;
+    r.label = c.label;
+    r.fn = fn; r.grid = grid; r.block = block; r.smem = smem;
+    for (const ArgRef& a : args) r.args.emplace_back((const char*)a.p, (const char*)a.p + a.n);
+    c.recs->push_back(std::move(r));
+  }
   return VLA_OK;
 }
 
@@ -97,8 +122,8 @@ vla_status zero_counters(Ctx& c) {
   unsigned* p = c.cnt_tile;
   unsigned v = 0;
   int n = (int)(c.need_tiles + 1);
-  void* args[] = {&p, &v, &n};
-  return launch(c, k_fill_ref(), dim3((n + 255) / 256), dim3(256), 0, args);
+  c.label = "fill";
+  return launch(c, k_fill_ref(), dim3((n + 255) / 256), dim3(256), 0, {arg(p), arg(v), arg(n)});
 }
 
 // Kernels that need more than 64 KiB of dynamic LDS are opted in once.
@@ -118,28 +143,44 @@ struct GemmOp {
   int am, em;
 };
 
-void pick_tile(int M, int em, int& mb, int& wn, int& nbw) {
-  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : 16;
+// Row tile (16-row blocks) by M; rows beyond 128 use several row tiles.
+// Narrow tiles: 16 columns with 4 waves splitting K when M <= 16, else 64
+// columns with 4 waves side by side. Wide tiles (RoPE pairs, gate/up pairs):
+// 128 columns with 8 waves side by side.
+void pick_tile(int M, int em, int& mb, int& wn, int& wk, int& nbw) {
+  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : 8;
   bool wide = em == E_ROPE || em == E_SWIGLU;
-  if (wide) { wn = 4; nbw = 2; }
-  else if (mb == 1) { wn = 1; nbw = 1; }
-  else { wn = 4; nbw = 1; }
+  nbw = 1;
+  if (wide) { wn = 8; wk = 1; }
+  else if (mb == 1) { wn = 1; wk = 4; }
+  else { wn = 4; wk = 1; }
 }
 
-vla_status gemm(Ctx& c, GemmArgs a, GemmOp op) {
+// Launch one GEMM. For a residual epilogue, *produced receives the column
+// tiling of the row moments the kernel leaves in a.rs_out.
+vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return fail(VLA_ERR_SHAPE, "gemm: empty shape %d x %d x %d", a.M, a.N, a.K);
-  int mb, wn, nbw;
-  pick_tile(a.M, op.em, mb, wn, nbw);
-  const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * (4 / wn) * 2;
+  int mb, wn, wk, nbw;
+  pick_tile(a.M, op.em, mb, wn, wk, nbw);
+  const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * wk * 4;
   const int bn_out = op.em == E_SWIGLU ? BN / 2 : BN;
   a.n_tiles_n = (a.N + bn_out - 1) / bn_out;
   a.n_tiles_m = (a.M + BM - 1) / BM;
   const int tiles = a.n_tiles_n * a.n_tiles_m;
-  int split = 1;
-  if (tiles < 200) {
-    int max_split = std::max(1, (a.K + BK - 1) / BK);
-    split = std::min(max_split, (320 + tiles - 1) / tiles);
-  }
+  // Split K when one workgroup would stream more than ~192 KiB of weights,
+  // or when a large GEMM has too few tiles to cover the CUs; never beyond
+  // one round of resident workgroups (512-thread tiles hold one workgroup
+  // per CU, 256-thread tiles two), never for small latency-bound GEMMs.
+  const int threads = 64 * wn * wk;
+  const int slots = 256 * (threads >= 512 ? 1 : 2);
+  const double wbytes = op.wdtype == VLA_F32 ? 4.0 : op.wdtype == VLA_BF16 ? 2.0 : 1.0;
+  const double per_wg = (double)BN * a.K * wbytes;
+  const double total = per_wg * tiles / (double)a.n_tiles_m;
+  int split = std::max(1, (int)std::ceil(per_wg / (192.0 * 1024.0)));
+  if (total >= 16.0 * 1024 * 1024 && tiles * split < 200) split = (200 + tiles - 1) / tiles;
+  split = std::min(split, std::max(1, slots / tiles));
+  split = std::min(split, std::max(1, (a.K + BK - 1) / BK));
+  split = std::min(split, SPLIT_MAX);
   int ksplit = (int)align_up((size_t)((a.K + split - 1) / split), (size_t)BK);
   split = (a.K + ksplit - 1) / ksplit;
   a.split = split;
@@ -148,25 +189,31 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op) {
   if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
   if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM) && (a.lda % 4 != 0 || a.K % 4 != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of 4", a.lda, a.K);
+  if (op.em == E_RESID) {
+    if (a.n_tiles_n > 256) return fail(VLA_ERR_SHAPE, "gemm: residual width %d needs more than 256 column tiles", a.N);
+    if (produced) { produced->T = a.n_tiles_n; produced->tw = BN; produced->N = a.N; produced->M = a.M; }
+  }
+  if (op.am == A_NORM || op.am == A_MERGE) {
+    // the prologue gives each normalised row `tpr` threads of up to 32 tile partials each
+    const int nr = op.am == A_MERGE ? 4 * BM : BM;
+    int tpr = 1;
+    while (tpr < 64 && 2 * tpr <= threads / nr) tpr *= 2;
+    if (a.rs.T < 1 || a.rs.T > 32 * tpr) return fail(VLA_ERR_SHAPE, "gemm: row moments over %d tiles (max %d)", a.rs.T, 32 * tpr);
+  }
   size_t part_f = split > 1 ? (size_t)split * tiles * BM * BN : 0;
-  size_t sp = op.em == E_RESID ? (size_t)a.n_tiles_n * a.M : 0;
   c.need_part = std::max(c.need_part, part_f);
   c.need_tiles = std::max(c.need_tiles, (size_t)tiles);
-  c.need_sp = std::max(c.need_sp, sp);
   KernelRef k{};
   bool found = false;
-  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, nbw, &k);
-  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, nbw, &k);
-  else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, nbw, &k);
-  if (!found) return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d", op.wdtype, op.am, op.em, mb, wn, nbw);
+  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, wk, nbw, &k);
+  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, wk, nbw, &k);
+  else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, wk, nbw, &k);
+  if (!found) return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d/%d", op.wdtype, op.am, op.em, mb, wn, wk, nbw);
   if (c.plan) { c.kernels++; return VLA_OK; }
   a.part = c.part;
   a.cnt_tile = c.cnt_tile;
-  a.cnt_all = c.cnt_all;
-  if (op.em == E_RESID) a.stats_part = c.stats_part;
   if (k.smem > 64 * 1024) VLA_TRY(allow_smem(k));
-  void* args[] = {&a};
-  return launch(c, k.fn, dim3(tiles * split), dim3(256), (size_t)k.smem, args);
+  return launch(c, k.fn, dim3(tiles * split), dim3(k.threads), (size_t)k.smem, {arg(a)});
 }
 
 GemmArgs gargs() {
@@ -189,25 +236,52 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
   int nrb = (a.Sq + 16 * rb - 1) / (16 * rb);
   int grid = a.Hkv * (group / hpw) * nrb;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)a.D));
-  void* args[] = {&a};
-  return launch(c, k.fn, dim3(grid), dim3(256), 0, args);
+  return launch(c, k.fn, dim3(grid), dim3(256), 0, {arg(a)});
 }
 
 vla_status stage_rows(Ctx& c, float* x, int ldx, int M, int N, const void* src, int src_f32, int ld_src, int r0, int r1,
                       float2* stats) {
-  void* args[] = {&x, &ldx, &M, &N, &src, &src_f32, &ld_src, &r0, &r1, &stats};
-  return launch(c, k_stage_rows_ref(), dim3((M + 3) / 4), dim3(256), 0, args);
+  return launch(c, k_stage_rows_ref(), dim3((M + 3) / 4), dim3(256), 0,
+                {arg(x), arg(ldx), arg(M), arg(N), arg(src), arg(src_f32), arg(ld_src), arg(r0), arg(r1), arg(stats)});
 }
 
-vla_status rmsnorm_out(Ctx& c, const float* x, int ldx, int M, int N, const float2* stats, const float* gain, float eps,
+vla_status rmsnorm_out(Ctx& c, const float* x, int ldx, int M, int N, RowStats rs, const float* gain, float eps,
                        void* out, int ldo, int out_f32) {
-  void* args[] = {&x, &ldx, &M, &N, &stats, &gain, &eps, &out, &ldo, &out_f32};
-  return launch(c, k_rmsnorm_out_ref(), dim3((M + 3) / 4), dim3(256), 0, args);
+  return launch(c, k_rmsnorm_out_ref(), dim3((M + 3) / 4), dim3(256), 0,
+                {arg(x), arg(ldx), arg(M), arg(N), arg(rs), arg(gain), arg(eps), arg(out), arg(ldo), arg(out_f32)});
+}
+
+// A residual stream: fp32 rows, their per-tile moment buffer (sized for the
+// finest column tiling, 16 columns) and the tiling its last writer used.
+struct Stream {
+  float* x = nullptr;
+  float2* part = nullptr;
+  RowStats rs{};
+};
+
+Stream take_stream(Ctx& c, int M, int N) {
+  Stream st;
+  st.x = c.take<float>((size_t)M * N);
+  st.part = c.take<float2>((size_t)((N + 15) / 16) * M);   // finest tiling: 16 columns
+  st.rs.part = st.part;
+  st.rs.M = M;
+  st.rs.N = N;
+  st.rs.T = 1;
+  st.rs.tw = N;
+  return st;
+}
+
+// Copy rows [r0, r1) from src into the stream (when src is given) and write
+// the moments of every row as one tile.
+vla_status stage_stream(Ctx& c, Stream& st, int M, int N, const void* src, int src_f32, int r0, int r1) {
+  st.rs.T = 1;
+  st.rs.tw = N;
+  return stage_rows(c, st.x, N, M, N, src, src_f32, N, r0, r1, st.part);
 }
 
 vla_status convert_rows(Ctx& c, const float* x, int ldx, int M, int N, void* out, int ldo, int out_f32) {
-  void* args[] = {&x, &ldx, &M, &N, &out, &ldo, &out_f32};
-  return launch(c, k_convert_rows_ref(), dim3((M + 3) / 4), dim3(256), 0, args);
+  return launch(c, k_convert_rows_ref(), dim3((M + 3) / 4), dim3(256), 0,
+                {arg(x), arg(ldx), arg(M), arg(N), arg(out), arg(ldo), arg(out_f32)});
 }
 
 bool dtype_ok(int t) { return t == VLA_F32 || t == VLA_BF16 || t == VLA_FP8_E4M3; }
@@ -239,8 +313,7 @@ vla_status check_block_weights(const vla_block_cfg* cfg, const vla_block_weights
 }
 
 struct BackboneBufs {
-  float* x;        // [S, H] residual
-  float2* stats;   // [S]
+  Stream xs;       // [S, H] residual stream
   void* qkv;       // [S, Nqkv]
   void* ao;        // [S, q_dim]
   void* act;       // [S, I]
@@ -250,15 +323,14 @@ BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   size_t es = cfg.adtype == VLA_F32 ? 4 : 2;
   int nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim;
   BackboneBufs b;
-  b.x = c.take<float>((size_t)S * cfg.hidden);
-  b.stats = c.take<float2>(S);
+  b.xs = take_stream(c, S, cfg.hidden);
   b.qkv = c.take<char>((size_t)S * nqkv * es);
   b.ao = c.take<char>((size_t)S * cfg.n_q_heads * cfg.head_dim * es);
   b.act = c.take<char>((size_t)S * cfg.intermediate * es);
   return b;
 }
 
-vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weights* layers, int n_layers, const BackboneBufs& b,
+vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weights* layers, int n_layers, BackboneBufs& b,
                         int S) {
   const int H = cfg.hidden, D = cfg.head_dim, qd = cfg.n_q_heads * D, kd = cfg.n_kv_heads * D;
   const int nqkv = qd + 2 * kd, I = cfg.intermediate;
@@ -268,15 +340,17 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   for (int l = 0; l < n_layers; l++) {
     const vla_block_weights& w = layers[l];
     {  // RMSNorm -> fused QKV -> RoPE
+    c.label = "llm.qkv";
       GemmArgs a = gargs();
       a.M = S; a.N = nqkv; a.K = H;
-      a.a = b.x; a.lda = H; a.stats = b.stats; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm;
+      a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm;
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
       a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32;
       a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_base = cfg.rope_base;
       VLA_TRY(gemm(c, a, {wt, A_NORM, E_ROPE}));
     }
     {  // causal GQA attention
+    c.label = "llm.attn";
       AttnArgs a{};
       a.q = b.qkv; a.ldq = nqkv;
       a.k = b.qkv ? (const char*)b.qkv + qd * es : nullptr; a.ldk = nqkv;
@@ -286,28 +360,31 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       VLA_TRY(attention(c, a, f32));
     }
     {  // O-proj + residual (+ row statistics)
+    c.label = "llm.o";
       GemmArgs a = gargs();
       a.M = S; a.N = H; a.K = qd;
       a.a = b.ao; a.lda = qd;
       a.w = w.w_o; a.ldw = qd; a.wscale = w.s_o;
-      a.x = b.x; a.ldx = H; a.stats_out = b.stats;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}));
+      a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}, &b.xs.rs));
     }
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
+    c.label = "llm.gate_up";
       GemmArgs a = gargs();
       a.M = S; a.N = I; a.K = H;
-      a.a = b.x; a.lda = H; a.stats = b.stats; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm;
+      a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm;
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
       a.c = b.act; a.ldc = I; a.c_f32 = f32;
       VLA_TRY(gemm(c, a, {wt, A_NORM, E_SWIGLU}));
     }
     {  // down + residual (+ row statistics)
+    c.label = "llm.down";
       GemmArgs a = gargs();
       a.M = S; a.N = H; a.K = I;
       a.a = b.act; a.lda = I;
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
-      a.x = b.x; a.ldx = H; a.stats_out = b.stats;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}));
+      a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}, &b.xs.rs));
     }
   }
   return VLA_OK;
@@ -325,7 +402,7 @@ vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out,
   Ctx p1;
   p1.plan = true;
   p1.off = fixed;
-  p1.take_scratch(p0.need_part, p0.need_tiles, p0.need_sp);
+  p1.take_scratch(p0.need_part, p0.need_tiles);
   size_t need = p1.off;
   if (need_out) { *need_out = need; return VLA_OK; }
   if (!ws) return fail(VLA_ERR_INVALID_ARG, "null workspace");
@@ -334,8 +411,8 @@ vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out,
   Ctx c;
   c.plan = false; c.base = (char*)ws; c.cap = ws_bytes; c.st = st;
   c.off = fixed;
-  c.need_part = p0.need_part; c.need_tiles = p0.need_tiles; c.need_sp = p0.need_sp;
-  c.take_scratch(p0.need_part, p0.need_tiles, p0.need_sp);
+  c.need_part = p0.need_part; c.need_tiles = p0.need_tiles;
+  c.take_scratch(p0.need_part, p0.need_tiles);
   c.off = 0;   // fixed buffers are taken again by the schedule from offset 0
   VLA_TRY(zero_counters(c));
   return sched(c);
@@ -385,14 +462,15 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
   float* mod = c.take<float>((size_t)K * mod_w);
   float* fmod = c.take<float>((size_t)K * 2 * D);
   uint16_t* ckv = c.take<uint16_t>((size_t)C * L * 2 * D);
-  float* x = c.take<float>((size_t)n * D);
-  float2* stats = c.take<float2>(n);
+  Stream xs = take_stream(c, n, D);
+  float* x = xs.x;
   uint16_t* qkv = c.take<uint16_t>((size_t)n * 3 * D);
   uint16_t* ao = c.take<uint16_t>((size_t)n * D);
   uint16_t* q = c.take<uint16_t>((size_t)n * D);
   uint16_t* h = c.take<uint16_t>((size_t)n * cf.mlp);
 
   {  // phi(t_k) -> Linear -> SiLU
+    c.label = "dit.time_fc1";
     GemmArgs a = gargs();
     a.M = K; a.N = D; a.K = cf.tdim;
     a.tsteps = K; a.time_scale = cf.time_scale; a.freq_base = cf.freq_base; a.half = cf.tdim / 2;
@@ -401,6 +479,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     VLA_TRY(gemm(c, a, {wt, A_TIME, E_STORE}));
   }
   {  // Linear -> SiLU: SiLU(c_k) for every step
+    c.label = "dit.time_fc2";
     GemmArgs a = gargs();
     a.M = K; a.N = D; a.K = D;
     a.a = t1; a.lda = D;
@@ -409,6 +488,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
   {  // adaLN modulations of every layer for every step (one launch)
+    c.label = "dit.adaln";
     GemmArgs a = gargs();
     a.M = K; a.N = mod_w; a.K = D;
     a.a = sc; a.lda = D;
@@ -417,6 +497,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
   {  // final-layer modulation
+    c.label = "dit.final_mod";
     GemmArgs a = gargs();
     a.M = K; a.N = 2 * D; a.K = D;
     a.a = sc; a.lda = D;
@@ -425,6 +506,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
   {  // cross-attention K/V of every layer from the fixed context (one launch)
+    c.label = "dit.cross_kv";
     GemmArgs a = gargs();
     a.M = C; a.N = L * 2 * D; a.K = cf.ctx_dim;
     a.a = io.ctx; a.lda = cf.ctx_dim;
@@ -439,9 +521,10 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     TailArgs t{};
     t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
     t.a_in = io.x0; t.a_out = io.actions;
-    t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.stats_out = stats;
-    void* args[] = {&t};
-    VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, args));
+    t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.rs_out = xs.part;
+    xs.rs.T = 1; xs.rs.tw = D;
+    c.label = "dit.in_proj";
+    VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, {arg(t)}));
   }
   for (int k = 0; k < K; k++) {
     for (int l = 0; l < L; l++) {
@@ -449,14 +532,16 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
       const float* m = mod ? mod + (size_t)k * mod_w + (size_t)l * 9 * D : nullptr;
       auto mv = [&](int j) { return m ? m + (size_t)j * D : nullptr; };
       {  // adaLN(LN) -> self-attn QKV
+      c.label = "dit.sa_qkv";
         GemmArgs a = gargs();
         a.M = n; a.N = 3 * D; a.K = D;
-        a.a = x; a.lda = D; a.stats = stats; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(1); a.g_plus_one = 1; a.bsh = mv(0);
+        a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(1); a.g_plus_one = 1; a.bsh = mv(0);
         a.w = w.w_qkv; a.ldw = D; a.wscale = w.s_qkv; a.bias = w.b_qkv;
         a.c = qkv; a.ldc = 3 * D;
         VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
       }
       {
+        c.label = "dit.sa_attn";
         AttnArgs a{};
         a.q = qkv; a.ldq = 3 * D;
         a.k = qkv ? qkv + D : nullptr; a.ldk = 3 * D;
@@ -466,22 +551,25 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         VLA_TRY(attention(c, a, false));
       }
       {  // O-proj, gated residual
+      c.label = "dit.sa_o";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = D;
         a.a = ao; a.lda = D;
         a.w = w.w_o; a.ldw = D; a.wscale = w.s_o; a.bias = w.b_o; a.gate = mv(2);
-        a.x = x; a.ldx = D; a.stats_out = stats;
-        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}));
+        a.x = x; a.ldx = D; a.rs_out = xs.part;
+        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
       }
       {  // adaLN(LN) -> cross-attn query
+      c.label = "dit.ca_q";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = D;
-        a.a = x; a.lda = D; a.stats = stats; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(4); a.g_plus_one = 1; a.bsh = mv(3);
+        a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(4); a.g_plus_one = 1; a.bsh = mv(3);
         a.w = w.w_cq; a.ldw = D; a.wscale = w.s_cq; a.bias = w.b_cq;
         a.c = q; a.ldc = D;
         VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
       }
       {
+        c.label = "dit.ca_attn";
         AttnArgs a{};
         a.q = q; a.ldq = D;
         a.k = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.ldk = L * 2 * D;
@@ -491,42 +579,46 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         VLA_TRY(attention(c, a, false));
       }
       {  // cross-attn out, gated residual
+      c.label = "dit.ca_o";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = D;
         a.a = ao; a.lda = D;
         a.w = w.w_co; a.ldw = D; a.wscale = w.s_co; a.bias = w.b_co; a.gate = mv(5);
-        a.x = x; a.ldx = D; a.stats_out = stats;
-        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}));
+        a.x = x; a.ldx = D; a.rs_out = xs.part;
+        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
       }
       {  // adaLN(LN) -> MLP up -> GELU
+      c.label = "dit.mlp_up";
         GemmArgs a = gargs();
         a.M = n; a.N = cf.mlp; a.K = D;
-        a.a = x; a.lda = D; a.stats = stats; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(7); a.g_plus_one = 1; a.bsh = mv(6);
+        a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(7); a.g_plus_one = 1; a.bsh = mv(6);
         a.w = w.w_up; a.ldw = D; a.wscale = w.s_up; a.bias = w.b_up; a.act = ACT_GELU;
         a.c = h; a.ldc = cf.mlp;
         VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
       }
       {  // MLP down, gated residual
+      c.label = "dit.mlp_down";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = cf.mlp;
         a.a = h; a.lda = cf.mlp;
         a.w = w.w_down; a.ldw = cf.mlp; a.wscale = w.s_down; a.bias = w.b_down; a.gate = mv(8);
-        a.x = x; a.ldx = D; a.stats_out = stats;
-        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}));
+        a.x = x; a.ldx = D; a.rs_out = xs.part;
+        VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
       }
     }
     {  // velocity head + Euler update (+ input projection for the next step)
       TailArgs t{};
       t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
-      t.x = x; t.stats = stats;
+      t.x = x; t.rs = xs.rs;
       t.shift = fmod ? fmod + (size_t)k * 2 * D : nullptr;
       t.scale = fmod ? fmod + (size_t)k * 2 * D + D : nullptr;
       t.w_out = d.w_out; t.s_out = d.s_out; t.b_out = d.b_out;
       t.a_in = io.actions; t.a_out = io.actions;
       t.v_out = io.velocities ? io.velocities + (size_t)k * n * A : nullptr;
-      if (k + 1 < K) { t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.stats_out = stats; }
-      void* args[] = {&t};
-      VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, args));
+      if (k + 1 < K) { t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.rs_out = xs.part; }
+      c.label = "dit.tail";
+      VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, {arg(t)}));
+      xs.rs.T = 1; xs.rs.tw = D;
     }
   }
   return VLA_OK;
@@ -559,31 +651,34 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
   const int grid = cf.image / cf.patch, np = grid * grid, S = n_img * np, D = cf.hidden;
   const int pdim = cf.channels * cf.patch * cf.patch, pitch = (int)align_up(pdim, 8);
   const int nm = np / (cf.merge * cf.merge), Mm = n_img * nm, MD = D * cf.merge * cf.merge;
-  float* z = c.take<float>((size_t)S * D);
-  float2* zs = c.take<float2>(S);
+  Stream zst = take_stream(c, S, D);
+  float* z = zst.x;
   uint16_t* qkv = c.take<uint16_t>((size_t)S * 3 * D);
   uint16_t* ao = c.take<uint16_t>((size_t)S * D);
   uint16_t* h = c.take<uint16_t>((size_t)S * cf.mlp);
   uint16_t* m1 = c.take<uint16_t>((size_t)Mm * MD);
   {  // patchify -> Linear + bias + position table (+ row statistics)
+    c.label = "vit.patch_embed";
     GemmArgs a = gargs();
     a.M = S; a.N = D; a.K = pdim;
     a.a = images; a.img = cf.image; a.patch = cf.patch; a.chans = cf.channels; a.vgrid = grid; a.n_patches = np;
     a.w = v.w_pe; a.ldw = pitch; a.bias = v.b_pe;
-    a.x = z; a.ldx = D; a.x_init = 1; a.addrow = v.pos; a.addrow_rows = np; a.stats_out = zs;
-    VLA_TRY(gemm(c, a, {VLA_BF16, A_PATCH, E_RESID}));
+    a.x = z; a.ldx = D; a.x_init = 1; a.addrow = v.pos; a.addrow_rows = np; a.rs_out = zst.part;
+    VLA_TRY(gemm(c, a, {VLA_BF16, A_PATCH, E_RESID}, &zst.rs));
   }
   for (int l = 0; l < cf.layers; l++) {
     const vla_vit_layer& w = v.layers[l];
     {
+      c.label = "vit.qkv";
       GemmArgs a = gargs();
       a.M = S; a.N = 3 * D; a.K = D;
-      a.a = z; a.lda = D; a.stats = zs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln1_g; a.bsh = w.ln1_b;
+      a.a = z; a.lda = D; a.rs = zst.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln1_g; a.bsh = w.ln1_b;
       a.w = w.w_qkv; a.ldw = D; a.bias = w.b_qkv;
       a.c = qkv; a.ldc = 3 * D;
       VLA_TRY(gemm(c, a, {VLA_BF16, A_NORM, E_STORE}));
     }
     {
+      c.label = "vit.attn";
       AttnArgs a{};
       a.q = qkv; a.ldq = 3 * D;
       a.k = qkv ? qkv + D : nullptr; a.ldk = 3 * D;
@@ -603,41 +698,46 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
       }
     }
     {
+      c.label = "vit.o";
       GemmArgs a = gargs();
       a.M = S; a.N = D; a.K = D;
       a.a = ao; a.lda = D;
       a.w = w.w_o; a.ldw = D; a.bias = w.b_o;
-      a.x = z; a.ldx = D; a.stats_out = zs;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}));
+      a.x = z; a.ldx = D; a.rs_out = zst.part;
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}, &zst.rs));
     }
     {
+      c.label = "vit.up";
       GemmArgs a = gargs();
       a.M = S; a.N = cf.mlp; a.K = D;
-      a.a = z; a.lda = D; a.stats = zs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln2_g; a.bsh = w.ln2_b;
+      a.a = z; a.lda = D; a.rs = zst.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln2_g; a.bsh = w.ln2_b;
       a.w = w.w_up; a.ldw = D; a.bias = w.b_up; a.act = ACT_GELU;
       a.c = h; a.ldc = cf.mlp;
       VLA_TRY(gemm(c, a, {VLA_BF16, A_NORM, E_STORE}));
     }
     {
+      c.label = "vit.down";
       GemmArgs a = gargs();
       a.M = S; a.N = D; a.K = cf.mlp;
       a.a = h; a.lda = cf.mlp;
       a.w = w.w_down; a.ldw = cf.mlp; a.bias = w.b_down;
-      a.x = z; a.ldx = D; a.stats_out = zs;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}));
+      a.x = z; a.ldx = D; a.rs_out = zst.part;
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}, &zst.rs));
     }
   }
-  if (vit_out) VLA_TRY(convert_rows(c, z, D, S, D, vit_out, D, 1));
+  if (vit_out) { c.label = "vit.out"; VLA_TRY(convert_rows(c, z, D, S, D, vit_out, D, 1)); }
   {  // LN -> 2x2 concat -> Linear -> GELU
+    c.label = "mrg.fc1";
     GemmArgs a = gargs();
     a.M = Mm; a.N = MD; a.K = MD;
-    a.a = z; a.lda = D; a.stats = zs; a.norm_rms = 0; a.eps = cf.eps; a.g = v.mln_g; a.bsh = v.mln_b;
+    a.a = z; a.lda = D; a.rs = zst.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = v.mln_g; a.bsh = v.mln_b;
     a.vgrid = grid; a.n_patches = np; a.merge = cf.merge; a.n_merged = nm;
     a.w = v.w_m1; a.ldw = MD; a.bias = v.b_m1; a.act = ACT_GELU;
     a.c = m1; a.ldc = MD;
     VLA_TRY(gemm(c, a, {VLA_BF16, A_MERGE, E_STORE}));
   }
   {  // Linear -> visual tokens (fp32)
+    c.label = "mrg.fc2";
     GemmArgs a = gargs();
     a.M = Mm; a.N = cf.out_dim; a.K = MD;
     a.a = m1; a.lda = MD;
@@ -660,9 +760,11 @@ static vla_status block_sched(Ctx& c, const vla_block_cfg* cfg, const vla_block_
                               int seq) {
   BackboneBufs b = take_backbone_bufs(c, *cfg, seq);
   const int f32 = cfg->adtype == VLA_F32;
-  VLA_TRY(stage_rows(c, b.x, cfg->hidden, seq, cfg->hidden, x_in, f32, cfg->hidden, 0, seq, b.stats));
+  c.label = "llm.stage";
+  VLA_TRY(stage_stream(c, b.xs, seq, cfg->hidden, x_in, f32, 0, seq));
   VLA_TRY(sched_layers(c, *cfg, w, 1, b, seq));
-  return convert_rows(c, b.x, cfg->hidden, seq, cfg->hidden, x_out, cfg->hidden, f32);
+  c.label = "llm.out";
+  return convert_rows(c, b.xs.x, cfg->hidden, seq, cfg->hidden, x_out, cfg->hidden, f32);
 }
 
 vla_status vla_block_forward(const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
@@ -695,10 +797,12 @@ static vla_status backbone_sched(Ctx& c, const vla_backbone* bb, const void* emb
   const vla_block_cfg& cfg = bb->cfg;
   BackboneBufs b = take_backbone_bufs(c, cfg, seq);
   const int f32 = cfg.adtype == VLA_F32;
-  VLA_TRY(stage_rows(c, b.x, cfg.hidden, seq, cfg.hidden, embeds, f32, cfg.hidden, 0, seq, b.stats));
+  c.label = "llm.stage";
+  VLA_TRY(stage_stream(c, b.xs, seq, cfg.hidden, embeds, f32, 0, seq));
   VLA_TRY(sched_layers(c, cfg, bb->layers, bb->n_layers, b, seq));
-  if (bb->final_norm) return rmsnorm_out(c, b.x, cfg.hidden, seq, cfg.hidden, b.stats, bb->final_norm, cfg.eps, out, cfg.hidden, f32);
-  return convert_rows(c, b.x, cfg.hidden, seq, cfg.hidden, out, cfg.hidden, f32);
+  c.label = "llm.final_norm";
+  if (bb->final_norm) return rmsnorm_out(c, b.xs.x, cfg.hidden, seq, cfg.hidden, b.xs.rs, bb->final_norm, cfg.eps, out, cfg.hidden, f32);
+  return convert_rows(c, b.xs.x, cfg.hidden, seq, cfg.hidden, out, cfg.hidden, f32);
 }
 
 vla_status vla_backbone_prefill(const vla_backbone* bb, const void* embeds, int32_t seq, void* hidden_out, void* ws,
@@ -791,6 +895,7 @@ struct vla_step_plan {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   int nodes = 0;
+  std::vector<LaunchRec> recs;   // the captured launches, in order
 };
 
 namespace {
@@ -807,12 +912,16 @@ vla_status step_sched(Ctx& c, const vla_step_plan& P) {
   BackboneBufs b = take_backbone_bufs(c, cfg, S);
   uint16_t* hid = c.take<uint16_t>((size_t)S * H);
   uint16_t* ctx = c.take<uint16_t>((size_t)S * P.dit.cfg.ctx_dim);
-  if (P.has_vit) VLA_TRY(sched_vit(c, P.vit, P.io.images, P.shape.n_images, b.x, H, nullptr));
-  VLA_TRY(stage_rows(c, b.x, H, S, H, P.io.text, 0, H, n_vis, S, b.stats));
+  if (P.has_vit) VLA_TRY(sched_vit(c, P.vit, P.io.images, P.shape.n_images, b.xs.x, H, nullptr));
+  c.label = "llm.stage";
+  VLA_TRY(stage_stream(c, b.xs, S, H, P.io.text, 0, n_vis, S));
   VLA_TRY(sched_layers(c, cfg, P.bb.layers, P.bb.n_layers, b, S));
-  VLA_TRY(rmsnorm_out(c, b.x, H, S, H, b.stats, P.bb.final_norm, cfg.eps, hid, H, 0));
-  if (P.io.hidden_out) VLA_TRY(rmsnorm_out(c, b.x, H, S, H, b.stats, P.bb.final_norm, cfg.eps, P.io.hidden_out, H, 0));
+  c.label = "llm.final_norm";
+  VLA_TRY(rmsnorm_out(c, b.xs.x, H, S, H, b.xs.rs, P.bb.final_norm, cfg.eps, hid, H, 0));
+  c.label = "llm.hidden_out";
+  if (P.io.hidden_out) VLA_TRY(rmsnorm_out(c, b.xs.x, H, S, H, b.xs.rs, P.bb.final_norm, cfg.eps, P.io.hidden_out, H, 0));
   {  // projector to the action expert's context width
+    c.label = "proj";
     GemmArgs a = gargs();
     a.M = S; a.N = P.dit.cfg.ctx_dim; a.K = H;
     a.a = hid; a.lda = H;
@@ -928,9 +1037,11 @@ vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
       Ctx c;
       c.plan = false; c.base = (char*)plan->ws; c.cap = plan->ws_bytes; c.st = cs;
       c.off = fixed;
-      c.need_part = p0.need_part; c.need_tiles = p0.need_tiles; c.need_sp = p0.need_sp;
-      c.take_scratch(p0.need_part, p0.need_tiles, p0.need_sp);
+      c.need_part = p0.need_part; c.need_tiles = p0.need_tiles;
+      c.take_scratch(p0.need_part, p0.need_tiles);
       c.off = 0;
+      plan->recs.clear();
+      c.recs = &plan->recs;
       s = step_sched(c, *plan);
       plan->nodes = c.kernels;
     }
@@ -956,6 +1067,22 @@ vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream) {
 }
 
 int32_t vla_step_graph_nodes(const vla_step_plan* plan) { return plan && plan->exec ? plan->nodes : 0; }
+
+const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index) {
+  if (!plan || index < 0 || index >= (int32_t)plan->recs.size()) return nullptr;
+  return plan->recs[index].label.c_str();
+}
+
+vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  if (!plan->exec) return fail(VLA_ERR_STATE, "plan not captured");
+  if (index < 0 || index >= (int32_t)plan->recs.size()) return fail(VLA_ERR_INVALID_ARG, "kernel index %d out of range", index);
+  LaunchRec& r = plan->recs[index];
+  void* ptrs[16];
+  for (size_t i = 0; i < r.args.size(); i++) ptrs[i] = r.args[i].data();
+  VLA_HIP(hipLaunchKernel(r.fn, r.grid, r.block, ptrs, r.smem, stream));
+  return VLA_OK;
+}
 
 void vla_step_plan_destroy(vla_step_plan* plan) {
   if (!plan) return;

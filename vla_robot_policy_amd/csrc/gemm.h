@@ -1,17 +1,21 @@
 // Weight-streaming GEMM for small M (16..600 rows), y = prologue(A) . W^T,
 // with fused prologues (row norms, patch gather, merge gather, sinusoidal
 // timestep features) and fused epilogues (bias, GELU/SiLU, RoPE, SwiGLU,
-// residual / gated residual with row statistics for the next norm).
+// residual / gated residual with per-tile row moments for the next norm).
 //
 // Layout: A is [M, K] row-major (token-major activations); W is [N, K]
 // row-major (PyTorch Linear); each lane's 16-byte W load is exactly the
 // MFMA B-operand fragment, so weights go HBM -> registers without LDS. A is
-// staged through LDS once per workgroup and shared by its 4 waves.
+// staged through LDS and shared by the workgroup's waves.
+// Pipeline: weights stream through a 4-deep register ring (three chunks in
+// flight while a fourth is consumed), activations through a 2-deep register
+// ring into a double-buffered LDS tile, one barrier per chunk.
 // Split-K partial tiles are reduced in a fixed order by the last workgroup
 // of each output tile (no float atomics), so results are bitwise
 // reproducible run to run.
 #pragma once
 #include "common.h"
+#include "rowstats.h"
 
 namespace vla {
 
@@ -24,7 +28,7 @@ struct GemmArgs {
   // ---- A source
   const void* a;         // BF16/F32/NORM/MERGE: matrix [rows, lda]; PATCH: bf16 images
   int lda;
-  const float2* stats;   // NORM/MERGE: per source row (mean, var)
+  RowStats rs;           // NORM/MERGE: row moments of the source rows
   int norm_rms;          // 1: RMSNorm (no mean subtraction), 0: LayerNorm
   float eps;
   const float* g;        // per-k gain (NULL = 1)
@@ -49,13 +53,11 @@ struct GemmArgs {
   int x_init;                                             // RESID: x = y (+ table) instead of x += y
   const float* addrow; int addrow_rows;                   // RESID: + table[m % rows][n]
   const float* gate;                                      // RESID: per-n gate (NULL = 1)
-  float2* stats_part;                                     // RESID: [n_tiles_n][M] (mean, M2)
-  float2* stats_out;                                      // RESID: [M] (mean, var)
+  float2* rs_out;                                         // RESID: [n_tiles_n][M] tile moments
   // ---- tiling / split-K (filled by the launcher)
   int split, ksplit;
   float* part;
   unsigned* cnt_tile;
-  unsigned* cnt_all;
   int n_tiles_n, n_tiles_m;
 };
 
@@ -103,37 +105,78 @@ __device__ __forceinline__ void lds_store4(__bf16*, char* p, float4 v) {
 }
 __device__ __forceinline__ void lds_store4(float*, char* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
-// ---------------------------------------------------------------- kernel
-template <typename WT, typename CT, int MB, int WN, int NBW, int AM, int EM>
+// ---------------------------------------------------------------- cross-workgroup hand-off
+// Device-scope relaxed atomic accesses compile to sc1 loads / stores, which
+// are coherent across the XCDs' private L2s without the L2 write-back and
+// invalidate that a device-scope fence costs.
+__device__ __forceinline__ void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ float ld_dev(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Called by every thread after its st_dev() stores: waits for them to
+// complete, counts this workgroup in *cnt, and returns true for every
+// workgroup except the one that arrives last.
+__device__ __forceinline__ bool tile_arrive(unsigned* cnt, int expected, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = (old == (unsigned)(expected - 1));
+  }
+  __syncthreads();
+  return !flag[0];
+}
+
+constexpr int SPLIT_MAX = 16;
+
+// ---------------------------------------------------------------- tile geometry
+template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4>
 struct GemmTile {
-  static constexpr int WK = 4 / WN;
+  static constexpr int THREADS = 64 * WN * WK;
+  static constexpr int NW = WN * WK;             // waves
   static constexpr int BM = 16 * MB;
   static constexpr int BN = 16 * NBW * WN;
-  static constexpr int U = 2;                    // 32-wide k-steps per wave per chunk
+  static constexpr int U = UU;                   // 32-wide k-steps per wave per chunk
   static constexpr int BK = 32 * WK * U;         // chunk width
   static constexpr int ESZ = sizeof(CT);
   static constexpr int LROW = BK * ESZ + 16;     // LDS row pitch (bytes), padded
   static constexpr int ABUF = BM * LROW;
-  static constexpr int GPT = BM * BK / 4 / 256;  // 4-element A groups per thread per chunk
+  static constexpr int AG = (AM == A_BF16) ? 8 : 4;  // A elements per loader group
+  static constexpr int AGROUPS = BM * BK / AG;   // A groups per chunk
+  static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
+  static constexpr int TPR = (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 64 ? 64 : 
+                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 32 ? 32 :
+                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 16 ? 16 :
+                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 8 ? 8 :
+                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 4 ? 4 :
+                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 2 ? 2 : 1;  // threads per normalised row
+  static constexpr int MAXL = 32;                // row-moment partials per thread (T <= MAXL * TPR)
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
   static constexpr int SMEM_A = 2 * ABUF;
   static constexpr int SMEM_T = BM * TPITCH * 4;
-  static constexpr int SMEM = (SMEM_A > SMEM_T ? SMEM_A : SMEM_T) + BM * 8 + 64;
-  static_assert(GPT >= 1 && (BM * BK) % 1024 == 0, "A chunk must split evenly over 256 threads");
+  static constexpr int NROWST = (AM == A_MERGE) ? 4 * BM : BM;   // normaliser entries
+  static constexpr int SMEM = (SMEM_A > SMEM_T ? SMEM_A : SMEM_T) + NROWST * 8 + 64;
+  static_assert(THREADS % (BK / AG) == 0, "a thread's A columns must not change between its row groups");
 };
 
-template <typename WT, typename CT, int MB, int WN, int NBW, int AM, int EM>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
-  using T = GemmTile<WT, CT, MB, WN, NBW, AM, EM>;
+// Raw A registers: bf16 sources keep 8 bf16 (copied to LDS as is), others 4 floats.
+template <int AM> struct ARaw { using type = float4; };
+template <> struct ARaw<A_BF16> { using type = uint4; };
+
+// ---------------------------------------------------------------- kernel
+template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4>
+__global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
+  using T = GemmTile<WT, CT, MB, WN, WK, NBW, AM, EM, UU>;
   using WL = WLoad<WT>;
   using F = typename Frag<CT>::type;
-  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, WK = T::WK, U = T::U, GPT = T::GPT;
+  using AR = typename ARaw<AM>::type;
+  constexpr int NT = T::THREADS, NW = T::NW;
+  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, U = T::U, GPT = T::GPT;
   constexpr int LROW = T::LROW, TPITCH = T::TPITCH;
   extern __shared__ __align__(16) char smem[];
   char* sA = smem;
   float* sT = reinterpret_cast<float*>(smem);
   float2* sRow = reinterpret_cast<float2*>(smem + (T::SMEM_A > T::SMEM_T ? T::SMEM_A : T::SMEM_T));
-  int* sFlag = reinterpret_cast<int*>(sRow + BM);
+  int* sFlag = reinterpret_cast<int*>(sRow + T::NROWST);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wk = wave / WN;
@@ -151,17 +194,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   const int kb = s * p.ksplit;
   const int ke = min(p.K, kb + p.ksplit);
   const int nchunks = ke > kb ? (ke - kb + BK - 1) / BK : 0;
-
-  // ---- per-row normaliser (NORM): (mean to subtract, reciprocal std)
-  if (AM == A_NORM) {
-    for (int r = tid; r < BM; r += 256) {
-      int m = m0 + r;
-      float2 st = m < p.M ? p.stats[m] : make_float2(0.f, 0.f);
-      float mu = p.norm_rms ? 0.f : st.x;
-      float var = p.norm_rms ? st.y + st.x * st.x : st.y;
-      sRow[r] = make_float2(mu, rsqrtf(var + p.eps));
-    }
-  }
 
   // ---- weight rows of this wave's n-blocks
   size_t wrow[NBW];
@@ -183,7 +215,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
   const int kl = (lane >> 4) * 8;               // this lane's offset inside a 32-wide k-step
 
-  auto load_b = [&](typename WL::raw (&br)[U][NBW], int kc) {
+  using BR = typename WL::raw;
+  auto load_b = [&](BR (&br)[U][NBW], int kc) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       int k = kc + (u * WK + wk) * 32 + kl;
@@ -193,103 +226,162 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     }
   };
 
-  // ---- A chunk loader: thread owns 4 consecutive k of rows r0 + i*RS
-  constexpr int CPR = BK / 4;                   // groups per row
-  constexpr int RS = 256 / CPR;                 // row stride between a thread's groups
-  const int ar0 = tid / CPR;
-  const int ac4 = (tid % CPR) * 4;
-  float4 areg[GPT];
-  float2 astat[AM == A_MERGE ? GPT : 1];
-  float4 ag = make_float4(1.f, 1.f, 1.f, 1.f), ab = make_float4(0.f, 0.f, 0.f, 0.f);
+  BR b0[U][NBW], b1[U][NBW], b2[U][NBW], b3[U][NBW];
 
-  auto load_a = [&](int kc) {
-    int k = kc + ac4;
-    if (AM == A_NORM || AM == A_MERGE) {
-      int kk = (AM == A_MERGE) ? (k % p.lda) : k;
-      if (k < p.K) {
-        if (p.g) ag = *reinterpret_cast<const float4*>(p.g + kk);
-        else ag = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (p.g_plus_one) { ag.x += 1.f; ag.y += 1.f; ag.z += 1.f; ag.w += 1.f; }
-        if (p.bsh) ab = *reinterpret_cast<const float4*>(p.bsh + kk);
-        else ab = make_float4(0.f, 0.f, 0.f, 0.f);
+  // ---- per-row normaliser (NORM / MERGE): (mean to subtract, reciprocal std).
+  // TPR consecutive threads serve one source row: each merges every TPR-th
+  // column tile of it, then the TPR partial results are merged in a fixed
+  // butterfly. The partial loads are issued here, before the first A and W
+  // loads, and merged after them, so all of them share one memory latency.
+  constexpr int NR = T::NROWST, TPR = T::TPR;
+  constexpr int MAXL = (AM == A_NORM || AM == A_MERGE) ? T::MAXL : 1;
+  constexpr int NPASS = (NR + NT / TPR - 1) / (NT / TPR);   // row passes (1 unless NR > NT / TPR)
+  float2 rsv[NPASS][MAXL];
+  int rsrc[NPASS];
+  const int rr = tid / TPR, jj = tid % TPR;
+  if constexpr (AM == A_NORM || AM == A_MERGE) {
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ps++) {
+      const int r = ps * (NT / TPR) + rr;
+      int src = -1;
+      if (r < NR) {
+        if (AM == A_NORM) {
+          int m = m0 + r;
+          src = m < p.M ? m : -1;
+        } else {
+          int mr = r >> 2, sub = r & 3;           // merged row, 2x2 member
+          int m = m0 + mr;
+          if (m < p.M && sub < p.merge * p.merge) {
+            int per = p.n_merged, im = m / per, mm = m % per;
+            int gq = p.vgrid / p.merge;
+            int R = mm / gq, C = mm % gq;
+            int dy = sub / p.merge, dx = sub % p.merge;
+            src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
+          }
+        }
+      }
+      rsrc[ps] = src;
+#pragma unroll
+      for (int u = 0; u < MAXL; u++) {
+        int t = jj + u * TPR;
+        rsv[ps][u] = (src >= 0 && t < p.rs.T) ? p.rs.part[(size_t)t * p.rs.M + src] : make_float2(0.f, 0.f);
       }
     }
+  }
+  auto merge_rows = [&]() {
+    if constexpr (AM == A_NORM || AM == A_MERGE) {
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ps++) {
+        const int r = ps * (NT / TPR) + rr;
+        const int src = rsrc[ps];
+        float n = 0.f, mean = 0.f, m2 = 0.f;
+#pragma unroll
+        for (int u = 0; u < MAXL; u++) {
+          int t = jj + u * TPR;
+          if (src >= 0 && t < p.rs.T) moments_merge(n, mean, m2, (float)min(p.rs.tw, p.rs.N - t * p.rs.tw), rsv[ps][u].x, rsv[ps][u].y);
+        }
+#pragma unroll
+        for (int o = TPR >> 1; o >= 1; o >>= 1) {
+          float n2 = __shfl_xor(n, o, WAVE), mean2 = __shfl_xor(mean, o, WAVE), m22 = __shfl_xor(m2, o, WAVE);
+          moments_merge(n, mean, m2, n2, mean2, m22);
+        }
+        if (jj == 0 && r < NR) {
+          float var = n > 0.f ? m2 / n : 0.f;
+          float mu = p.norm_rms ? 0.f : mean;
+          float ms = p.norm_rms ? var + mean * mean : var;
+          sRow[r] = src >= 0 ? make_float2(mu, rsqrtf(ms + p.eps)) : make_float2(0.f, 0.f);
+        }
+      }
+    }
+  };
+
+  // ---- A chunk loader: thread owns AG consecutive k of rows r0 + i*RS
+  constexpr int AG = T::AG;
+  constexpr int CPR = BK / AG;                  // groups per row
+  constexpr int RS = NT / CPR;                  // row stride between a thread's groups
+  const int ar0 = tid / CPR;
+  const int ac4 = (tid % CPR) * AG;
+
+  auto load_a = [&](AR (&ar)[GPT], int kc) {
+    int k = kc + ac4;
 #pragma unroll
     for (int i = 0; i < GPT; i++) {
       int r = ar0 + i * RS;
       int m = m0 + r;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      bool ok = m < p.M && k < p.K;
-      if (AM == A_BF16) {
-        if (ok) {
-          uint2 u = *reinterpret_cast<const uint2*>((const uint16_t*)p.a + (size_t)m * p.lda + k);
-          v = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                          __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-        }
-      } else if (AM == A_F32 || AM == A_NORM) {
-        if (ok) v = *reinterpret_cast<const float4*>((const float*)p.a + (size_t)m * p.lda + k);
-      } else if (AM == A_PATCH) {
+      bool ok = r < BM && m < p.M && k < p.K;
+      if constexpr (AM == A_BF16) {
+        ar[i] = ok ? *reinterpret_cast<const uint4*>((const uint16_t*)p.a + (size_t)m * p.lda + k) : make_uint4(0, 0, 0, 0);
+      } else if constexpr (AM == A_F32 || AM == A_NORM) {
+        ar[i] = ok ? *reinterpret_cast<const float4*>((const float*)p.a + (size_t)m * p.lda + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else if constexpr (AM == A_PATCH) {
+        float t4[4] = {0.f, 0.f, 0.f, 0.f};
         if (m < p.M) {
           int im = m / p.n_patches, pi = m % p.n_patches;
           int pr = pi / p.vgrid, pc = pi % p.vgrid;
           int P2 = p.patch * p.patch;
-          float t4[4];
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             int kk = k + e;
-            float val = 0.f;
             if (kk < p.K) {
               int c = kk / P2, rem = kk % P2, ky = rem / p.patch, kx = rem % p.patch;
               size_t off = (((size_t)im * p.chans + c) * p.img + pr * p.patch + ky) * p.img + pc * p.patch + kx;
-              val = bf2f(((const uint16_t*)p.a)[off]);
+              t4[e] = bf2f(((const uint16_t*)p.a)[off]);
             }
-            t4[e] = val;
           }
-          v = make_float4(t4[0], t4[1], t4[2], t4[3]);
         }
-      } else if (AM == A_MERGE) {
+        ar[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+      } else if constexpr (AM == A_MERGE) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (ok) {
           int D = p.lda;
-          int per = p.n_merged;
-          int im = m / per, mm = m % per;
+          int per = p.n_merged, im = m / per, mm = m % per;
           int gq = p.vgrid / p.merge;
           int R = mm / gq, C = mm % gq;
           int sub = k / D, d = k % D;
           int dy = sub / p.merge, dx = sub % p.merge;
           int src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
           v = *reinterpret_cast<const float4*>((const float*)p.a + (size_t)src * D + d);
-          astat[i] = p.stats[src];
-        } else {
-          astat[i] = make_float2(0.f, 1.f);
         }
+        ar[i] = v;
+      } else {
+        ar[i] = make_float4(0.f, 0.f, 0.f, 0.f);   // TIME: computed at store time
       }
-      areg[i] = v;
     }
   };
 
-  auto store_a = [&](int buf, int kc) {
+  auto store_a = [&](int buf, const AR (&ar)[GPT], int kc) {
     char* base = sA + buf * T::ABUF;
+    const int k = kc + ac4;
+    float4 ag = make_float4(1.f, 1.f, 1.f, 1.f), ab = make_float4(0.f, 0.f, 0.f, 0.f);
+    int sub = 0;
+    if constexpr (AM == A_NORM || AM == A_MERGE) {
+      int kk = (AM == A_MERGE) ? (k % p.lda) : k;
+      if (AM == A_MERGE) sub = k / p.lda;
+      if (k < p.K) {
+        if (p.g) ag = *reinterpret_cast<const float4*>(p.g + kk);
+        if (p.g_plus_one) { ag.x += 1.f; ag.y += 1.f; ag.z += 1.f; ag.w += 1.f; }
+        if (p.bsh) ab = *reinterpret_cast<const float4*>(p.bsh + kk);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < GPT; i++) {
       int r = ar0 + i * RS;
+      if (r >= BM) break;
       int m = m0 + r;
-      int k = kc + ac4;
-      float4 v = areg[i];
-      if (AM == A_NORM) {
-        float2 rs = sRow[r];
-        bool ok = m < p.M && k < p.K;
+      bool ok = m < p.M && k < p.K;
+      float4 v;
+      if constexpr (AM == A_BF16) {
+        // raw copy of 8 bf16 (CT is bf16 for every bf16 source)
+        *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
+        continue;
+      } else if constexpr (AM == A_NORM || AM == A_MERGE) {
+        v = ar[i];
+        float2 rs = sRow[AM == A_MERGE ? r * 4 + sub : r];
         v.x = ok ? (v.x - rs.x) * rs.y * ag.x + ab.x : 0.f;
         v.y = ok ? (v.y - rs.x) * rs.y * ag.y + ab.y : 0.f;
         v.z = ok ? (v.z - rs.x) * rs.y * ag.z + ab.z : 0.f;
         v.w = ok ? (v.w - rs.x) * rs.y * ag.w + ab.w : 0.f;
-      } else if (AM == A_MERGE) {
-        bool ok = m < p.M && k < p.K;
-        float mu = astat[i].x, rstd = rsqrtf(astat[i].y + p.eps);
-        v.x = ok ? (v.x - mu) * rstd * ag.x + ab.x : 0.f;
-        v.y = ok ? (v.y - mu) * rstd * ag.y + ab.y : 0.f;
-        v.z = ok ? (v.z - mu) * rstd * ag.z + ab.z : 0.f;
-        v.w = ok ? (v.w - mu) * rstd * ag.w + ab.w : 0.f;
-      } else if (AM == A_TIME) {
+      } else if constexpr (AM == A_TIME) {
         float t4[4];
         float tm = (float)m / (float)p.tsteps;
 #pragma unroll
@@ -306,6 +398,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
           t4[e] = val;
         }
         v = make_float4(t4[0], t4[1], t4[2], t4[3]);
+      } else {
+        v = ar[i];
       }
       lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
     }
@@ -317,7 +411,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; j++) acc[mb][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, typename WL::raw (&br)[U][NBW]) {
+  auto compute = [&](int buf, const BR (&br)[U][NBW]) {
     const char* base = sA + buf * T::ABUF;
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -335,28 +429,50 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     }
   };
 
+  // ---- main loop. Chunk c: weights in ring slot c%4 (issued three chunks
+  // ahead), activations staged into LDS buffer c%2 from register slot c%2
+  // (issued two chunks ahead, stored one chunk ahead). Loads complete in
+  // issue order (vmcnt), so each chunk's activations are issued before its
+  // weights: waiting for A of chunk c+1 never waits for later weights.
+  AR a0[GPT], a1[GPT];
+  if (nchunks > 0) { load_a(a0, kb); load_b(b0, kb); }
+  if (nchunks > 1) { load_a(a1, kb + BK); load_b(b1, kb + BK); }
+  if (nchunks > 2) load_b(b2, kb + 2 * BK);
+  // residual inputs of a small unsplit tile are fetched now as well
+  constexpr int XPT = (BM * BN + NT - 1) / NT;
+  float xpre[XPT <= 4 ? XPT : 1];
+  const bool xpref = EM == E_RESID && XPT <= 4 && p.split == 1 && !p.x_init;
+  if constexpr (EM == E_RESID && XPT <= 4) {
+    if (xpref) {
+#pragma unroll
+      for (int q = 0; q < XPT; q++) {
+        int e = tid + q * NT;
+        int r = e / BN, cc = e % BN;
+        int m = m0 + r, n = nt * BN + cc;
+        xpre[q] = (e < BM * BN && m < p.M && n < p.N) ? p.x[(size_t)m * p.ldx + n] : 0.f;
+      }
+    }
+  }
+  merge_rows();
   __syncthreads();   // sRow ready
-  typename WL::raw b0[U][NBW], b1[U][NBW];
-  if (nchunks > 0) {
-    load_a(kb);
-    load_b(b0, kb);
-    store_a(0, kb);
-  }
+  if (nchunks > 0) store_a(0, a0, kb);
   __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    // even chunk: compute from b0 / buffer 0 while chunk c+1 streams into b1
-    int kc1 = kb + (c + 1) * BK;
-    if (c + 1 < nchunks) { load_a(kc1); load_b(b1, kc1); }
-    compute(0, b0);
-    if (c + 1 < nchunks) store_a(1, kc1);
-    __syncthreads();
-    if (c + 1 >= nchunks) break;
-    int kc2 = kb + (c + 2) * BK;
-    if (c + 2 < nchunks) { load_a(kc2); load_b(b0, kc2); }
-    compute(1, b1);
-    if (c + 2 < nchunks) store_a(0, kc2);
-    __syncthreads();
+
+#define VLA_GEMM_ITER(C, BCUR, BNEXT3, ARELOAD, ASTORE)                     \
+  if ((C) < nchunks) {                                                      \
+    if ((C) + 2 < nchunks) load_a(ARELOAD, kb + ((C) + 2) * BK);            \
+    if ((C) + 3 < nchunks) load_b(BNEXT3, kb + ((C) + 3) * BK);             \
+    compute((C) & 1, BCUR);                                                 \
+    if ((C) + 1 < nchunks) store_a(((C) + 1) & 1, ASTORE, kb + ((C) + 1) * BK); \
+    __syncthreads();                                                        \
   }
+  for (int c = 0; c < nchunks; c += 4) {
+    VLA_GEMM_ITER(c + 0, b0, b3, a0, a1)
+    VLA_GEMM_ITER(c + 1, b1, b0, a1, a0)
+    VLA_GEMM_ITER(c + 2, b2, b1, a0, a1)
+    VLA_GEMM_ITER(c + 3, b3, b2, a1, a0)
+  }
+#undef VLA_GEMM_ITER
 
   // ---- reduce the WK wave slices into the fp32 LDS tile (fixed order)
 #pragma unroll 1
@@ -378,24 +494,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
 
   // ---- split-K: publish the partial tile; the last arriving workgroup sums
-  // all partials in split order
+  // all partials in split order. Partials are written and read with
+  // device-scope atomic accesses (coherent across XCDs without flushing or
+  // invalidating the L2); the counter increment is issued only after every
+  // thread's stores have completed.
   if (p.split > 1) {
     const int tile = mt * p.n_tiles_n + nt;
-    float* mine = p.part + ((size_t)s * p.n_tiles_m * p.n_tiles_n + tile) * (BM * BN);
-    for (int e = tid; e < BM * BN; e += 256) mine[e] = sT[(e / BN) * TPITCH + (e % BN)];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      unsigned old = atomicAdd(p.cnt_tile + tile, 1u);
-      sFlag[0] = (old == (unsigned)(p.split - 1));
-    }
-    __syncthreads();
-    if (!sFlag[0]) return;
-    __threadfence();
-    for (int e = tid; e < BM * BN; e += 256) {
+    const size_t tstride = (size_t)p.n_tiles_m * p.n_tiles_n * (BM * BN);
+    float* mine = p.part + (size_t)s * tstride + (size_t)tile * (BM * BN);
+    for (int e = tid; e < BM * BN; e += NT) st_dev(mine + e, sT[(e / BN) * TPITCH + (e % BN)]);
+    if (tile_arrive(p.cnt_tile + tile, p.split, sFlag)) return;
+    const float* base = p.part + (size_t)tile * (BM * BN);
+    for (int e = tid; e < BM * BN; e += NT) {
+      float v[SPLIT_MAX];
+#pragma unroll
+      for (int q = 0; q < SPLIT_MAX; q++) v[q] = q < p.split ? ld_dev(base + (size_t)q * tstride + e) : 0.f;
       float sum = 0.f;
-      for (int q = 0; q < p.split; q++)
-        sum += p.part[((size_t)q * p.n_tiles_m * p.n_tiles_n + tile) * (BM * BN) + e];
+#pragma unroll
+      for (int q = 0; q < SPLIT_MAX; q++) sum += v[q];
       sT[(e / BN) * TPITCH + (e % BN)] = sum;
     }
     if (tid == 0) p.cnt_tile[tile] = 0u;
@@ -403,8 +519,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   }
 
   // ---- epilogues
-  if (EM == E_STORE) {
-    for (int e = tid; e < BM * BN; e += 256) {
+  if constexpr (EM == E_STORE) {
+    for (int e = tid; e < BM * BN; e += NT) {
       int r = e / BN, cc = e % BN;
       int m = m0 + r, n = nt * BN + cc;
       if (m >= p.M || n >= p.N) continue;
@@ -416,10 +532,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = v;
       else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(v);
     }
-  } else if (EM == E_ROPE) {
+  } else if constexpr (EM == E_ROPE) {
     const int D = p.head_dim, hd = D >> 1;
     const float l2b = log2f(p.rope_base);
-    for (int e = tid; e < BM * BN; e += 256) {
+    for (int e = tid; e < BM * BN; e += NT) {
       int r = e / BN, cc = e % BN;
       int m = m0 + r, n = nt * BN + cc;
       if (m >= p.M || n >= p.N) continue;
@@ -437,11 +553,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
         sincosf((float)(m + p.pos0) * theta, &sn, &cs);
         v = d < hd ? v * cs - v2 * sn : v * cs + v2 * sn;
       }
-      ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(v);
+      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = v;
+      else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(v);
     }
-  } else if (EM == E_SWIGLU) {
+  } else if constexpr (EM == E_SWIGLU) {
     constexpr int BO = BN / 2;
-    for (int e = tid; e < BM * BO; e += 256) {
+    for (int e = tid; e < BM * BO; e += NT) {
       int r = e / BO, cc = e % BO;
       int m = m0 + r, n = nt * BO + cc;
       if (m >= p.M || n >= p.N) continue;
@@ -451,8 +568,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = a;
       else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(a);
     }
-  } else if (EM == E_RESID) {
-    for (int e = tid; e < BM * BN; e += 256) {
+  } else if constexpr (EM == E_RESID) {
+#pragma unroll 1
+    for (int q = 0, e = tid; e < BM * BN; q++, e += NT) {
       int r = e / BN, cc = e % BN;
       int m = m0 + r, n = nt * BN + cc;
       if (m >= p.M || n >= p.N) continue;
@@ -466,15 +584,23 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
         xn = v;
         if (p.addrow) xn += p.addrow[(size_t)(m % p.addrow_rows) * p.N + n];
       } else {
-        xn = *xp + v;
+        float xo = 0.f;
+        bool got = false;
+        if constexpr (XPT <= 4) {
+#pragma unroll
+          for (int qq = 0; qq < XPT; qq++)
+            if (xpref && qq == q) { xo = xpre[qq]; got = true; }
+        }
+        if (!got) xo = *xp;
+        xn = xo + v;
       }
       *xp = xn;
       sT[r * TPITCH + cc] = xn;
     }
     __syncthreads();
-    // per-row moments of this tile's columns
+    // per-row moments of this tile's columns, merged by the next reader
     const int ncols = min(BN, p.N - nt * BN);
-    for (int r = wave; r < BM; r += 4) {
+    for (int r = wave; r < BM; r += NW) {
       int m = m0 + r;
       if (m >= p.M) continue;          // wave-uniform
       float sum = 0.f;
@@ -483,28 +609,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       float sq = 0.f;
       for (int cc = lane; cc < ncols; cc += 64) { float d = sT[r * TPITCH + cc] - mean; sq += d * d; }
       float m2 = wave_sum(sq);
-      if (lane == 0) p.stats_part[(size_t)nt * p.M + m] = make_float2(mean, m2);
+      if (lane == 0) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, m2);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      unsigned total = (unsigned)(p.n_tiles_n * p.n_tiles_m);
-      unsigned old = atomicAdd(p.cnt_all, 1u);
-      sFlag[1] = (old == total - 1);
-    }
-    __syncthreads();
-    if (!sFlag[1]) return;
-    __threadfence();
-    for (int m = tid; m < p.M; m += 256) {
-      float n = 0.f, mean = 0.f, m2 = 0.f;
-      for (int t = 0; t < p.n_tiles_n; t++) {
-        float2 st = p.stats_part[(size_t)t * p.M + m];
-        float nb = (float)min(BN, p.N - t * BN);
-        moments_merge(n, mean, m2, nb, st.x, st.y);
-      }
-      p.stats_out[m] = make_float2(mean, m2 / n);
-    }
-    if (tid == 0) *p.cnt_all = 0u;
   }
 }
 

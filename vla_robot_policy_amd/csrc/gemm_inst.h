@@ -3,21 +3,23 @@
 #include "gemm.h"
 #include "kernels.h"
 
-#define VLA_GEMM_CASE(WT, CT, AMV, EMV, MBV, WNV, NBWV)                                      \
-  if (am == AMV && em == EMV && mb == MBV && wn == WNV && nbw == NBWV) {                     \
-    out->fn = (const void*)&k_gemm<WT, CT, MBV, WNV, NBWV, AMV, EMV>;                        \
-    out->smem = GemmTile<WT, CT, MBV, WNV, NBWV, AMV, EMV>::SMEM;                            \
-    return true;                                                                             \
+#define VLA_GEMM_CASE_U(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, UV)                              \
+  if (am == AMV && em == EMV && mb == MBV && wn == WNV && wk == WKV && nbw == NBWV) {                \
+    out->fn = (const void*)&k_gemm<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV>;                    \
+    out->smem = GemmTile<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV>::SMEM;                        \
+    out->threads = GemmTile<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV>::THREADS;                  \
+    return true;                                                                                  \
   }
+#define VLA_GEMM_CASE(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV) VLA_GEMM_CASE_U(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, 4)
 
-// narrow tiles (BN = 16 for one 16-row block, else 64) and wide tiles (BN = 128)
-#define VLA_GEMM_NARROW(WT, CT, AMV, EMV)  \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 1, 1, 1) \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 4, 4, 1) \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 7, 4, 1) \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 16, 4, 1)
-#define VLA_GEMM_WIDE(WT, CT, AMV, EMV)    \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 1, 4, 2) \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 4, 4, 2) \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 7, 4, 2) \
-  VLA_GEMM_CASE(WT, CT, AMV, EMV, 16, 4, 2)
+// narrow tiles (16 columns for 16-row tiles, else 64) and wide tiles (128 columns)
+#define VLA_GEMM_NARROW(WT, CT, AMV, EMV)     \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 1, 1, 4, 1) \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 4, 4, 1, 1) \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 7, 4, 1, 1) \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 8, 4, 1, 1)
+#define VLA_GEMM_WIDE(WT, CT, AMV, EMV)       \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 1, 8, 1, 1) \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 4, 8, 1, 1) \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 7, 8, 1, 1) \
+  VLA_GEMM_CASE(WT, CT, AMV, EMV, 8, 8, 1, 1)

@@ -6,13 +6,14 @@ namespace vla {
 
 struct KernelRef {
   const void* fn;
-  int smem;  // dynamic LDS bytes
+  int smem;     // dynamic LDS bytes
+  int threads;  // workgroup size
 };
 
 // GEMM: wt 0 = f32, 1 = bf16, 2 = fp8 (vla_dtype values); am / em from gemm.h.
-bool gemm_lookup_f32(int am, int em, int mb, int wn, int nbw, KernelRef* out);
-bool gemm_lookup_bf16(int am, int em, int mb, int wn, int nbw, KernelRef* out);
-bool gemm_lookup_fp8(int am, int em, int mb, int wn, int nbw, KernelRef* out);
+bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out);
+bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out);
+bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out);
 
 // Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
 bool attn_lookup(int f32, int dp, int hpw, KernelRef* out);

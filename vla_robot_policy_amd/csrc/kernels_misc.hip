@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void k_convert_rows(const float* x, int ldx, i
 #define VLA_ATTN_CASE(CT, F32V, DPV, HPWV)          \
   if (f32 == F32V && dp == DPV && hpw == HPWV) {    \
     out->fn = (const void*)&k_attention<CT, DPV, HPWV>; \
-    out->smem = 0;                                  \
+    out->smem = 0; out->threads = 256;              \
     return true;                                    \
   }
 
@@ -41,6 +41,7 @@ const void* k_convert_rows_ref() { return (const void*)&k_convert_rows; }
 
 bool euler_tail_lookup(int wt, KernelRef* out) {
   out->smem = 0;
+  out->threads = 256;
   if (wt == 0) { out->fn = (const void*)&k_euler_tail<float>; return true; }
   if (wt == 1) { out->fn = (const void*)&k_euler_tail<uint16_t>; return true; }
   if (wt == 2) { out->fn = (const void*)&k_euler_tail<uint8_t>; return true; }

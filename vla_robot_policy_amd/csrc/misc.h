@@ -2,6 +2,7 @@
 // standalone final norm, the fused Euler tail of the flow sampler, and a fill.
 #pragma once
 #include "common.h"
+#include "rowstats.h"
 #include "tail.h"
 
 namespace vla {
@@ -13,8 +14,9 @@ __global__ void k_fill_u32(unsigned* p, unsigned v, int n) {
   if (i < n) p[i] = v;
 }
 
-// x[r] = src[r - r0] for r in [r0, r1) (bf16 or fp32 source), then per-row
-// (mean, biased variance) of x for every row r < M. One wave per row.
+// x[r] = src[r - r0] for r in [r0, r1) (bf16 or fp32 source), then the
+// moments (mean, M2) of every row r < M as a single column tile
+// (part[r] = (mean, sum of squared deviations)). One wave per row.
 __global__ __launch_bounds__(256) void k_stage_rows(float* x, int ldx, int M, int N, const void* src, int src_f32,
                                                   int ld_src, int r0, int r1, float2* stats) {
   int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -32,17 +34,20 @@ __global__ __launch_bounds__(256) void k_stage_rows(float* x, int ldx, int M, in
   float mean = wave_sum(s) / (float)N;
   float q = 0.f;
   for (int c = lane; c < N; c += 64) { float d = xr[c] - mean; q += d * d; }
-  float var = wave_sum(q) / (float)N;
-  if (lane == 0) stats[r] = make_float2(mean, var);
+  float m2 = wave_sum(q);
+  if (lane == 0) stats[r] = make_float2(mean, m2);
 }
 
-// out[r] = RMSNorm(x[r]) * gain, from the row statistics (mean, var).
-__global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, int M, int N, const float2* stats,
+// out[r] = RMSNorm(x[r]) * gain, from the row moments left by x's writer.
+__global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, int M, int N, RowStats st_in,
                                                    const float* gain, float eps, void* out, int ldo, int out_f32) {
   int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (r >= M) return;
-  float2 st = stats[r];
+  int rows[1] = {r};
+  float2 mv[1];
+  rows_moments_wave<1>(st_in, rows, mv);
+  float2 st = mv[0];
   float rs = rsqrtf(st.y + st.x * st.x + eps);
   for (int c = lane; c < N; c += 64) {
     float v = x[(size_t)r * ldx + c] * rs * gain[c];
@@ -70,7 +75,15 @@ __global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* arow = p.a_in + (size_t)m * p.A;
   if (p.w_out) {
-    float2 st = p.stats[m];
+    __shared__ float2 smv;
+    if (wave == 0) {
+      int rows[1] = {m};
+      float2 mv[1];
+      rows_moments_wave<1>(p.rs, rows, mv);
+      if (lane == 0) smv = mv[0];
+    }
+    __syncthreads();
+    float2 st = smv;
     float rs = rsqrtf(st.y + p.eps);
     for (int d = tid; d < p.D; d += 256)
       su[d] = (p.x[(size_t)m * p.D + d] - st.x) * rs * (1.f + p.scale[d]) + p.shift[d];
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
   q = wave_sum(q);
   if (lane == 0) red[4 + wave] = q;
   __syncthreads();
-  if (tid == 0) p.stats_out[m] = make_float2(mean, (red[4] + red[5] + red[6] + red[7]) / (float)p.D);
+  if (tid == 0) p.rs_out[m] = make_float2(mean, red[4] + red[5] + red[6] + red[7]);
 }
 
 }  // namespace vla

@@ -1,13 +1,14 @@
 // Arguments of the fused Euler-tail kernel (shared by host and device code).
 #pragma once
 #include <hip/hip_runtime.h>
+#include "rowstats.h"
 
 namespace vla {
 
 struct TailArgs {
   int n, D, A, K;             // action rows, DiT width, action dim, Euler steps
   // velocity head (skipped when w_out == NULL)
-  const float* x; const float2* stats; float eps;
+  const float* x; RowStats rs; float eps;        // residual stream and its row moments
   const float* shift; const float* scale;   // final modulation of this step [D] each
   const void* w_out; const float* s_out; const float* b_out;   // [A, D], per-row scale, [A]
   const float* a_in;          // current actions [n, A]
@@ -15,7 +16,7 @@ struct TailArgs {
   float* v_out;               // optional velocity record [n, A]
   // input projection of the (updated) actions (skipped when w_in == NULL)
   const void* w_in; const float* s_in; const float* b_in;      // [D, A], per-row scale, [D]
-  float* x_out; float2* stats_out;
+  float* x_out; float2* rs_out;                  // new stream, its moments as one tile
 };
 
 }  // namespace vla

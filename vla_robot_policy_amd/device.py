@@ -22,8 +22,9 @@ _NP_RAW = {"f32": np.float32, "bf16": np.int16, "fp8": np.uint8}
 
 
 class DeviceWeights:
-    def __init__(self, cfg, tensors, device: str = "cuda:0", threads: int = 8):
+    def __init__(self, cfg, tensors, device: str = "cuda:0", threads: int = 8, keep_host: bool = True):
         self.cfg = cfg
+        self.keep_host = keep_host
         self.t = tensors
         self.device = torch.device(device)
         self.keep: List[torch.Tensor] = []
@@ -63,7 +64,16 @@ class DeviceWeights:
         return self.up_array(np.concatenate([self.t[n].data for n in names]).astype(np.float32)).data_ptr()
 
     def prefetch(self, names: Sequence[str]) -> None:
+        if not self.keep_host:
+            self.release()
+        self._pending = list(names)
         self.t.generate_all(threads=self.threads, names=list(names))
+
+    def release(self) -> None:
+        """Drop the host copies of the last prefetched group (keep_host=False)."""
+        if getattr(self, "_pending", None):
+            self.t.drop(self._pending)
+            self._pending = []
 
     # ------------------------------------------------------------ components
     def build_backbone(self) -> lib.Backbone:
@@ -100,7 +110,8 @@ class DeviceWeights:
         ada_w, ada_b, ckv_w, ckv_b = [], [], [], []
         for l in range(d.layers):
             p = f"dit.{l}."
-            self.prefetch([n for n in self.t.names() if n.startswith(p)])
+            stacked = ("ada_w", "ada_b", "ca_wk", "ca_wv", "ca_bk", "ca_bv")
+            self.prefetch([n for n in self.t.names() if n.startswith(p) and n[len(p):] not in stacked])
             L = layers[l]
             L.w_qkv, L.s_qkv = self.up_rows([p + "sa_wq", p + "sa_wk", p + "sa_wv"])
             L.b_qkv = self.up_vec([p + "sa_bq", p + "sa_bk", p + "sa_bv"])
@@ -117,6 +128,7 @@ class DeviceWeights:
             ada_w.append(p + "ada_w"); ada_b.append(p + "ada_b")
             ckv_w += [p + "ca_wk", p + "ca_wv"]; ckv_b += [p + "ca_bk", p + "ca_bv"]
         D = lib.Dit(cfg=dc, layers=layers)
+        self.prefetch(ada_w + ada_b + ckv_w + ckv_b)
         D.w_ada, D.s_ada = self.up_rows(ada_w)
         D.b_ada = self.up_vec(ada_b)
         D.w_ckv, D.s_ckv = self.up_rows(ckv_w)
@@ -175,6 +187,9 @@ class DeviceWeights:
         M.b_proj = self.up_vec(["proj.b"])
         M.dit = C.pointer(self.dit)
         self.model = M
+        if not self.keep_host:
+            self.release()
+            self.t.drop(self.t.names())
         return M
 
 

@@ -119,6 +119,8 @@ def load() -> C.CDLL:
         "vla_step_capture": (S, [c_void_p, c_void_p]),
         "vla_step_replay": (S, [c_void_p, c_void_p]),
         "vla_step_graph_nodes": (c_int32, [c_void_p]),
+        "vla_step_kernel_label": (C.c_char_p, [c_void_p, c_int32]),
+        "vla_step_launch_kernel": (S, [c_void_p, c_int32, c_void_p]),
         "vla_step_plan_destroy": (None, [c_void_p]),
         "vla_last_error": (C.c_char_p, []),
         "vla_abi_version": (c_int32, []),
@@ -219,6 +221,15 @@ def vla_step_replay(plan, stream: int = 0) -> int:
 
 def vla_step_graph_nodes(plan) -> int:
     return load().vla_step_graph_nodes(plan)
+
+
+def vla_step_kernel_label(plan, index: int):
+    r = load().vla_step_kernel_label(plan, index)
+    return None if r is None else r.decode()
+
+
+def vla_step_launch_kernel(plan, index: int, stream: int = 0) -> int:
+    return load().vla_step_launch_kernel(plan, index, stream)
 
 
 def vla_step_plan_destroy(plan) -> None:

@@ -126,9 +126,9 @@ def dit_ops(cfg) -> List[Op]:
         # once per policy step (exact hoists: fixed t schedule, fixed context)
         linear_op("dit.time_fc1", "dit_once", K, D, d.tdim, w, 1, bias=True),
         linear_op("dit.time_fc2", "dit_once", K, D, D, w, 1, bias=True),
-        linear_op("dit.adaln", "dit_once", K, d.n_mod * D, D, w, L, bias=True),
+        linear_op("dit.adaln", "dit_once", K, L * d.n_mod * D, D, w, 1, bias=True),
         linear_op("dit.final_mod", "dit_once", K, 2 * D, D, w, 1, bias=True),
-        linear_op("dit.cross_kv", "dit_once", C, 2 * D, d.ctx_dim, w, L, bias=True),
+        linear_op("dit.cross_kv", "dit_once", C, L * 2 * D, d.ctx_dim, w, 1, bias=True),
         # per Euler step
         linear_op("dit.in_proj", "dit_step", n, D, d.action_dim, w, K, bias=True, act_in=4.0 * n * d.action_dim),
     ]
