@@ -35,7 +35,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gpu_step_bench(cfg, steps, warmup, kernel_reps):
+def copy_probe(nbytes: int, reps: int):
+    """A plain device-to-device copy of known size: the reference that turns
+    the HBM byte counters of a profiled run into bytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n * 4} bytes x {reps}")
+
+
+def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
     import numpy as np
     import torch
     from synth import make_inputs, make_weights
@@ -66,6 +79,16 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps):
     lib.check(lib.vla_step_capture(plan, stream))
     nodes = lib.vla_step_graph_nodes(plan)
     log(f"captured {nodes} kernel nodes")
+    labels = [lib.vla_step_kernel_label(plan, i) for i in range(nodes)]
+    if only_label is not None:
+        # one kernel alone, relaunched: the run a hardware-counter pass profiles
+        i = labels.index(only_label)
+        for _ in range(kernel_reps):
+            lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+        torch.cuda.synchronize()
+        lib.vla_step_plan_destroy(plan)
+        log(f"launched {only_label} (node {i}) {kernel_reps} times")
+        return None
     for _ in range(warmup):
         lib.check(lib.vla_step_replay(plan, stream))
     torch.cuda.synchronize()
@@ -79,8 +102,12 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps):
     per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
     total_ms = evs[0].elapsed_time(evs[steps])
     log(f"{steps} replays: mean {total_ms / steps:.3f} ms, p50 {np.median(per):.3f} ms")
-    # per-kernel durations: each captured kernel relaunched alone between events
-    labels = [lib.vla_step_kernel_label(plan, i) for i in range(nodes)]
+    # per-kernel durations: each captured kernel relaunched alone, bracketed by
+    # events on the launch stream, after a 512 MiB read that evicts the 256 MiB
+    # last-level cache with clean lines (inside a step every layer's weights
+    # arrive cold; a write-based flush would leave write-backs to the kernel)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
     first, count = {}, {}
     for i, lb in enumerate(labels):
         first.setdefault(lb, i)
@@ -88,13 +115,18 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps):
     kern = {}
     for lb, i in first.items():
         lib.check(lib.vla_step_launch_kernel(plan, i, stream))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        pairs = []
         for _ in range(kernel_reps):
+            torch.sum(flush, dim=0, out=sink[0])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             lib.check(lib.vla_step_launch_kernel(plan, i, stream))
-        e1.record()
+            e1.record()
+            pairs.append((e0, e1))
         torch.cuda.synchronize()
-        kern[lb] = {"avg_us": e0.elapsed_time(e1) * 1e3 / kernel_reps, "count": count[lb]}
+        us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        kern[lb] = {"avg_us": float(np.mean(us)), "count": count[lb]}
+    del flush
     lib.check(lib.vla_step_replay(plan, stream))   # restore a consistent state
     torch.cuda.synchronize()
     lib.vla_step_plan_destroy(plan)
@@ -168,17 +200,26 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-label", default=None,
+                    help="relaunch only the kernel with this label --kernel-reps times (for counter passes)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="run only a device copy of this many bytes --kernel-reps times (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if a.copy_bytes:
+        copy_probe(a.copy_bytes, a.kernel_reps)
+        return
     from synth import get_config
     from vla_robot_policy_amd import roofline
     cfg = get_config(a.config)
     if cfg.kind != "step":
         raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
-    r = gpu_step_bench(cfg, a.steps, a.warmup, a.kernel_reps)
+    r = gpu_step_bench(cfg, a.steps, a.warmup, a.kernel_reps, a.only_label)
+    if r is None:
+        return
     b = roofline.bound(cfg)
     ops = {o.name: o for o in b.ops}
     # dominant kernel: largest (per-launch duration x launches per step)

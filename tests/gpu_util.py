@@ -10,6 +10,7 @@ import time
 import numpy as np
 import torch
 
+from oracle.io import Weights
 from synth import make_inputs, make_weights
 from vla_robot_policy_amd import lib
 from vla_robot_policy_amd.device import DeviceWeights, bf16_bits_to_float, upload_input, workspace
@@ -134,3 +135,31 @@ def timed(label, fn):
     r = fn()
     say(f"  {label}: {time.time() - t:.1f}s")
     return r
+
+
+class ProgressWeights(Weights):
+    """Oracle weight access that prints which layer the oracle has reached
+    (at most every few seconds), so a long full-size evaluation reports its
+    own progress. Weights whose names start with ``keep_prefix`` (the action
+    expert's, read once per Euler step) keep their float64 form after the
+    first read."""
+
+    def __init__(self, tensors, label: str, every_s: float = 5.0, keep_prefix: str = "dit."):
+        super().__init__(tensors)
+        self.keep_prefix = keep_prefix
+        self.label = label
+        self.every = every_s
+        self.last = time.time()
+        self.t0 = self.last
+        self.n = 0
+
+    def __getitem__(self, name: str):
+        self.n += 1
+        now = time.time()
+        if now - self.last >= self.every:
+            self.last = now
+            say(f"  {self.label}: at {name} after {now - self.t0:.0f}s ({self.n} weight reads)")
+        v = super().__getitem__(name)
+        if name.startswith(self.keep_prefix):
+            self._c[name] = v
+        return v

@@ -9,7 +9,7 @@ import os
 import numpy as np
 
 from oracle.fp8 import decode_e4m3fn, dequantize_rows
-from synth.fp8 import encode_e4m3fn, quantize_rows
+from synth.fp8 import _VALS, encode_e4m3fn, encode_e4m3fn_table, quantize_rows
 from synth.gen import f32_to_bf16_bits, bf16_bits_to_f32
 from synth import small_config, get_config
 from vla_robot_policy_amd import roofline
@@ -50,6 +50,17 @@ def test_encoder_nearest_even_and_saturating(rng):
     assert encode_e4m3fn(np.array([1.0625]))[0] == 0x38
     assert encode_e4m3fn(np.array([1.1875]))[0] == 0x3A     # between 0x39 and 0x3A -> even
     assert encode_e4m3fn(np.array([1e6, -1e6])).tolist() == [0x7E, 0xFE]
+
+
+def test_fast_encoder_equals_table_search(rng):
+    # the bit-level encoder and the nearest-value search over the 127-entry
+    # table agree on every grid value, every midpoint (the tie cases), the
+    # floats just beside each midpoint, the saturating range and random data
+    mids = (_VALS[1:] + _VALS[:-1]) / 2
+    x = np.concatenate([_VALS, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        [0.0, 448, 449, 464, 480, 1e9, 2.0 ** -10, 2.0 ** -12]])
+    x = np.concatenate([x, -x, rng.standard_normal(200000) * np.exp(rng.uniform(-12, 7, 200000))])
+    np.testing.assert_array_equal(encode_e4m3fn(x), encode_e4m3fn_table(x))
 
 
 def test_row_quantisation_bounds(rng):

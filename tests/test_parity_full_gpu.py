@@ -1,0 +1,126 @@
+"""GPU parity at the workloads' full sizes, against the whole float64 oracle.
+
+Each test generates the seeded weights and inputs of one named workload, runs
+it through the C ABI in the launch configuration the benchmark times (the
+whole-step plan captured as one graph and replayed, for the policy steps) and
+compares every graded output with the oracle evaluated on the same stored
+values. Bars: relative L2 error <= 1e-2 for bf16 weights, <= 5e-2 for fp8.
+
+Workloads:
+  - 36-layer backbone prefill, seq 256, hidden 2560, GQA 32/8 x 128, SwiGLU 9728
+  - DiT sampler: 36 layers x 4 Euler steps, chunk 16 x 7, 256 context tokens
+  - full single-camera step: ViT 24L (224x224) -> merger -> backbone at seq 104
+    -> projector -> DiT 36L x 4 steps
+  - fp8 two-camera long-context step: backbone at seq 560 -> DiT 36L x 10
+    steps, chunk 50 x 32
+"""
+
+import numpy as np
+import pytest
+
+from oracle.policy import run_config
+from synth import get_config, make_inputs, make_weights
+
+# minutes of host work each (generation and the float64 oracle)
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util
+    return gpu_util
+
+
+def _generate(gu, cfg):
+    def gen():
+        W = make_weights(cfg)
+        W.generate_all(threads=16)
+        return W, make_inputs(cfg)
+    return gu.timed(f"cfg{cfg.cid} weights and inputs", gen)
+
+
+def test_backbone_full_seq256(gu):
+    cfg = get_config(2)
+    gu.say(f"cfg{cfg.cid}: backbone {cfg.layers} layers, seq {cfg.seq}")
+    W, I = _generate(gu, cfg)
+    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
+    got = gu.timed("gpu", lambda: gu.run_backbone(cfg, dw, gu.upload_input(I["x"]), cfg.seq))
+    want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I)["hidden"])
+    e = gu.relerr(got, want)
+    gu.say(f"backbone seq {cfg.seq}: hidden rel L2 {e:.3e}")
+    assert e <= 1e-2
+
+
+def test_dit_full_ctx256(gu):
+    cfg = get_config(3)
+    gu.say(f"cfg{cfg.cid}: DiT {cfg.dit.layers} layers x {cfg.steps} steps, ctx {cfg.ctx_len}")
+    W, I = _generate(gu, cfg)
+    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
+    acts, vel = gu.timed("gpu", lambda: gu.run_dit(cfg, dw, gu.upload_input(I["ctx"]), gu.upload_input(I["noise"])))
+    want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I))
+    e, ev = gu.relerr(acts, want["actions"]), gu.relerr(vel, want["velocities"])
+    gu.say(f"dit: actions rel L2 {e:.3e}, velocities {ev:.3e}")
+    assert e <= 1e-2 and ev <= 1e-2
+
+
+def _step_graph(gu, cfg, W, I):
+    """Outputs of the whole-step plan: one eager run, then two graph replays
+    that must reproduce it bit for bit."""
+    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
+    r = gu.StepRunner(cfg, dw, I)
+    try:
+        r.run()
+        eager = r.outputs()
+        r.capture()
+        for _ in range(2):
+            r.replay()
+            g = r.outputs()
+            for k in ("actions", "hidden", "velocities"):
+                assert np.array_equal(g[k], eager[k]), k
+    finally:
+        r.close()
+    return dw, eager
+
+
+def test_step_full_single_camera(gu):
+    import torch
+    from vla_robot_policy_amd import lib
+    cfg = get_config(4)
+    v = cfg.vit
+    gu.say(f"cfg{cfg.cid}: ViT {v.layers}L -> backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}")
+    W, I = _generate(gu, cfg)
+    dw, got = gu.timed("gpu step (eager + 2 replays)", lambda: _step_graph(gu, cfg, W, I))
+    # the encoder and merger outputs through their own entry point
+    V = dw.vit
+    toks = torch.empty((v.n_merged, v.out_dim), dtype=torch.float32, device=gu.DEV)
+    z = torch.empty((v.n_patches, v.hidden), dtype=torch.float32, device=gu.DEV)
+    need = lib.vla_vit_workspace_bytes(V, 1)
+    ws = gu.workspace(need)
+    lib.check(lib.vla_vit_encode(V, gu.upload_input(I["image"]), 1, toks, z, ws, need))
+    torch.cuda.synchronize()
+    want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I))
+    errs = {
+        "vit": gu.relerr(z.cpu().numpy(), want["vit"][0]),
+        "merged": gu.relerr(toks.cpu().numpy(), want["merged"]),
+        "hidden": gu.relerr(got["hidden"], want["hidden"]),
+        "actions": gu.relerr(got["actions"], want["actions"]),
+        "velocities": gu.relerr(got["velocities"], want["velocities"]),
+    }
+    gu.say("single-camera step rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-2, k
+
+
+def test_step_full_fp8_long_context(gu):
+    cfg = get_config(5)
+    gu.say(f"cfg{cfg.cid}: fp8 backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}, chunk {cfg.dit.chunk}")
+    W, I = _generate(gu, cfg)
+    _, got = gu.timed("gpu step (eager + 2 replays)", lambda: _step_graph(gu, cfg, W, I))
+    want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I))
+    errs = {k: gu.relerr(got[k], want[k]) for k in ("hidden", "actions", "velocities")}
+    gu.say("fp8 long-context step rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= 5e-2, k

@@ -78,7 +78,8 @@ struct Ctx {
   size_t cap;
   size_t off = 0;
   hipStream_t st = nullptr;
-  // shared GEMM scratch (requirements gathered in plan mode)
+  // shared GEMM scratch (requirements gathered in plan mode): split-K
+  // partial tiles and their counters
   size_t need_part = 0, need_tiles = 0;
   float* part = nullptr;
   unsigned* cnt_tile = nullptr;
@@ -93,10 +94,11 @@ struct Ctx {
     off += n * sizeof(T);
     return p;
   }
-  // Lay out the split-K scratch after the fixed buffers.
-  void take_scratch(size_t part_f, size_t tiles) {
-    part = take<float>(std::max<size_t>(part_f, 1));
-    cnt_tile = take<unsigned>(tiles + 1);
+  // Lay out the GEMM scratch (sized by a plan pass `q`) after the fixed buffers.
+  void take_scratch(const Ctx& q) {
+    need_part = q.need_part; need_tiles = q.need_tiles;
+    part = take<float>(std::max<size_t>(need_part, 1));
+    cnt_tile = take<unsigned>(need_tiles + 1);
   }
 };
 
@@ -141,14 +143,16 @@ vla_status allow_smem(const KernelRef& k) {
 struct GemmOp {
   int wdtype;   // vla_dtype of W
   int am, em;
+  int ac = 0;   // compensated (hi + lo) bf16 activations
 };
 
 // Row tile (16-row blocks) by M; rows beyond 128 use several row tiles.
 // Narrow tiles: 16 columns with 4 waves splitting K when M <= 16, else 64
 // columns with 4 waves side by side. Wide tiles (RoPE pairs, gate/up pairs):
 // 128 columns with 8 waves side by side.
-void pick_tile(int M, int em, int& mb, int& wn, int& wk, int& nbw) {
+void pick_tile(int M, int em, int ac, int& mb, int& wn, int& wk, int& nbw, int& u) {
   mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : 8;
+  u = ac ? 2 : 4;
   bool wide = em == E_ROPE || em == E_SWIGLU;
   nbw = 1;
   if (wide) { wn = 8; wk = 1; }
@@ -160,9 +164,9 @@ void pick_tile(int M, int em, int& mb, int& wn, int& wk, int& nbw) {
 // tiling of the row moments the kernel leaves in a.rs_out.
 vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return fail(VLA_ERR_SHAPE, "gemm: empty shape %d x %d x %d", a.M, a.N, a.K);
-  int mb, wn, wk, nbw;
-  pick_tile(a.M, op.em, mb, wn, wk, nbw);
-  const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * wk * 4;
+  int mb, wn, wk, nbw, u;
+  pick_tile(a.M, op.em, op.ac, mb, wn, wk, nbw, u);
+  const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * wk * u;
   const int bn_out = op.em == E_SWIGLU ? BN / 2 : BN;
   a.n_tiles_n = (a.N + bn_out - 1) / bn_out;
   a.n_tiles_m = (a.M + BM - 1) / BM;
@@ -187,27 +191,29 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   a.ksplit = ksplit;
   // weight-type / alignment requirements of the 8-element fragment loads
   if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
-  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM) && (a.lda % 4 != 0 || a.K % 4 != 0))
-    return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of 4", a.lda, a.K);
+  const int ag = op.am == A_BF16 ? 8 : 4;   // activation elements per 16-byte load
+  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM) && (a.lda % ag != 0 || a.K % ag != 0))
+    return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
+  // buffer-load offsets are 32-bit: operands up to 2 GiB
+  const double wrows = op.em == E_SWIGLU ? (double)a.n_half + a.N : (double)a.N;
+  if (wrows * a.ldw * wbytes >= (double)BUF_LIMIT) return fail(VLA_ERR_SHAPE, "gemm: weight matrix beyond 2 GiB");
+  if (op.am != A_TIME && op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
+    return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
+  if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32)))
+    return fail(VLA_ERR_UNSUPPORTED, "gemm: compensated activations need bf16 weights and a float source");
   if (op.em == E_RESID) {
-    if (a.n_tiles_n > 256) return fail(VLA_ERR_SHAPE, "gemm: residual width %d needs more than 256 column tiles", a.N);
+    if (!a.rs_out && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: residual epilogue without a row-moment output");
+    if (a.n_tiles_n > (a.N + 15) / 16) return fail(VLA_ERR_SHAPE, "gemm: residual tiling finer than 16 columns");
     if (produced) { produced->T = a.n_tiles_n; produced->tw = BN; produced->N = a.N; produced->M = a.M; }
-  }
-  if (op.am == A_NORM || op.am == A_MERGE) {
-    // the prologue gives each normalised row `tpr` threads of up to 32 tile partials each
-    const int nr = op.am == A_MERGE ? 4 * BM : BM;
-    int tpr = 1;
-    while (tpr < 64 && 2 * tpr <= threads / nr) tpr *= 2;
-    if (a.rs.T < 1 || a.rs.T > 32 * tpr) return fail(VLA_ERR_SHAPE, "gemm: row moments over %d tiles (max %d)", a.rs.T, 32 * tpr);
   }
   size_t part_f = split > 1 ? (size_t)split * tiles * BM * BN : 0;
   c.need_part = std::max(c.need_part, part_f);
   c.need_tiles = std::max(c.need_tiles, (size_t)tiles);
   KernelRef k{};
   bool found = false;
-  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, wk, nbw, &k);
-  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, wk, nbw, &k);
-  else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, wk, nbw, &k);
+  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
+  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
+  else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
   if (!found) return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d/%d", op.wdtype, op.am, op.em, mb, wn, wk, nbw);
   if (c.plan) { c.kernels++; return VLA_OK; }
   a.part = c.part;
@@ -319,14 +325,20 @@ struct BackboneBufs {
   void* act;       // [S, I]
 };
 
+// bf16 backbones carry the MLP's activations (the normalised input of gate/up
+// and the SwiGLU output feeding down) as compensated hi + lo bf16 pairs: the
+// two MLP operands dominate the rounding error of a deep stack.
+bool mlp_compensated(const vla_block_cfg& cfg) { return cfg.wdtype == VLA_BF16; }
+
 BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   size_t es = cfg.adtype == VLA_F32 ? 4 : 2;
+  size_t es_act = mlp_compensated(cfg) ? 4 : es;
   int nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim;
   BackboneBufs b;
   b.xs = take_stream(c, S, cfg.hidden);
   b.qkv = c.take<char>((size_t)S * nqkv * es);
   b.ao = c.take<char>((size_t)S * cfg.n_q_heads * cfg.head_dim * es);
-  b.act = c.take<char>((size_t)S * cfg.intermediate * es);
+  b.act = c.take<char>((size_t)S * cfg.intermediate * es_act);
   return b;
 }
 
@@ -337,6 +349,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   const bool f32 = cfg.adtype == VLA_F32;
   const int wt = cfg.wdtype;
   const size_t es = f32 ? 4 : 2;
+  const int comp = mlp_compensated(cfg) ? 1 : 0;
   for (int l = 0; l < n_layers; l++) {
     const vla_block_weights& w = layers[l];
     {  // RMSNorm -> fused QKV -> RoPE
@@ -374,8 +387,8 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       a.M = S; a.N = I; a.K = H;
       a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm;
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
-      a.c = b.act; a.ldc = I; a.c_f32 = f32;
-      VLA_TRY(gemm(c, a, {wt, A_NORM, E_SWIGLU}));
+      a.c = b.act; a.ldc = I; a.c_f32 = f32 || comp;
+      VLA_TRY(gemm(c, a, {wt, A_NORM, E_SWIGLU, comp}));
     }
     {  // down + residual (+ row statistics)
     c.label = "llm.down";
@@ -384,7 +397,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       a.a = b.act; a.lda = I;
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}, &b.xs.rs));
+      VLA_TRY(gemm(c, a, {wt, (f32 || comp) ? A_F32 : A_BF16, E_RESID, comp}, &b.xs.rs));
     }
   }
   return VLA_OK;
@@ -402,7 +415,7 @@ vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out,
   Ctx p1;
   p1.plan = true;
   p1.off = fixed;
-  p1.take_scratch(p0.need_part, p0.need_tiles);
+  p1.take_scratch(p0);
   size_t need = p1.off;
   if (need_out) { *need_out = need; return VLA_OK; }
   if (!ws) return fail(VLA_ERR_INVALID_ARG, "null workspace");
@@ -411,8 +424,7 @@ vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out,
   Ctx c;
   c.plan = false; c.base = (char*)ws; c.cap = ws_bytes; c.st = st;
   c.off = fixed;
-  c.need_part = p0.need_part; c.need_tiles = p0.need_tiles;
-  c.take_scratch(p0.need_part, p0.need_tiles);
+  c.take_scratch(p0);
   c.off = 0;   // fixed buffers are taken again by the schedule from offset 0
   VLA_TRY(zero_counters(c));
   return sched(c);
@@ -1037,8 +1049,7 @@ vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
       Ctx c;
       c.plan = false; c.base = (char*)plan->ws; c.cap = plan->ws_bytes; c.st = cs;
       c.off = fixed;
-      c.need_part = p0.need_part; c.need_tiles = p0.need_tiles;
-      c.take_scratch(p0.need_part, p0.need_tiles);
+      c.take_scratch(p0);
       c.off = 0;
       plan->recs.clear();
       c.recs = &plan->recs;

@@ -99,6 +99,42 @@ __device__ __forceinline__ float fp8_to_f32(uint8_t c) {
   return v[0];
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer loads return zeros for an offset at or beyond the resource's
+// size, so edge tiles select an out-of-range offset instead of branching:
+// every load of a loop is then unconditional and the compiler can wait for
+// exactly the loads a step needs (vmcnt) instead of draining the queue.
+typedef __amdgpu_buffer_rsrc_t brsrc;
+constexpr uint32_t BUF_LIMIT = 0x7FFFFFF0u;   // resource size; larger offsets read 0
+constexpr uint32_t BUF_OOB = BUF_LIMIT;       // the offset used for "no element"
+constexpr int CP_NONE = 0, CP_NT = 2, CP_SC1 = 16;   // cache policy bits of a buffer access
+
+__device__ __forceinline__ brsrc make_brsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)BUF_LIMIT, 0x00020000);
+}
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+template <int CP = CP_NONE>
+__device__ __forceinline__ uint4 bload16(brsrc r, uint32_t off) {
+  i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <int CP = CP_NONE>
+__device__ __forceinline__ uint2 bload8(brsrc r, uint32_t off) {
+  i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ float4 as_f4(uint4 u) {
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+template <int CP = CP_NONE>
+__device__ __forceinline__ float bloadf(brsrc r, uint32_t off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP));
+}
+__device__ __forceinline__ uint16_t bload2(brsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -9,7 +9,14 @@
 // staged through LDS and shared by the workgroup's waves.
 // Pipeline: weights stream through a 4-deep register ring (three chunks in
 // flight while a fourth is consumed), activations through a 2-deep register
-// ring into a double-buffered LDS tile, one barrier per chunk.
+// ring into a double-buffered LDS tile, one barrier per chunk. Every load is
+// a raw buffer load; rows or k beyond the edge get an out-of-range offset
+// (the hardware returns zeros), so the loop has no conditional loads and the
+// waits are exact.
+// Compensated activations (AC = 1): the bf16 A operand is carried as a pair
+// hi + lo (hi = bf16(a), lo = bf16(a - hi)) and both halves meet the same
+// weight fragment, so the product keeps ~16 significant bits of a at twice
+// the MFMA work and LDS traffic; the weights are read once either way.
 // Split-K partial tiles are reduced in a fixed order by the last workgroup
 // of each output tile (no float atomics), so results are bitwise
 // reproducible run to run.
@@ -28,7 +35,7 @@ struct GemmArgs {
   // ---- A source
   const void* a;         // BF16/F32/NORM/MERGE: matrix [rows, lda]; PATCH: bf16 images
   int lda;
-  RowStats rs;           // NORM/MERGE: row moments of the source rows
+  RowStats rs;           // NORM/MERGE: per-tile row moments of the source rows
   int norm_rms;          // 1: RMSNorm (no mean subtraction), 0: LayerNorm
   float eps;
   const float* g;        // per-k gain (NULL = 1)
@@ -53,7 +60,7 @@ struct GemmArgs {
   int x_init;                                             // RESID: x = y (+ table) instead of x += y
   const float* addrow; int addrow_rows;                   // RESID: + table[m % rows][n]
   const float* gate;                                      // RESID: per-n gate (NULL = 1)
-  float2* rs_out;                                         // RESID: [n_tiles_n][M] tile moments
+  float2* rs_out;                                         // RESID: [n_tiles_n][M] tile moments of the new stream
   // ---- tiling / split-K (filled by the launcher)
   int split, ksplit;
   float* part;
@@ -62,31 +69,36 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------- weight fragments
+// Weights are streamed once per use: loads are non-temporal (CP_NT).
 template <typename WT> struct WLoad;
 template <> struct WLoad<uint16_t> {
   using raw = uint4;
   using frag = FragBF16;
-  __device__ static raw zero() { return make_uint4(0, 0, 0, 0); }
-  __device__ static raw load(const void* w, size_t off) { return *reinterpret_cast<const uint4*>((const uint16_t*)w + off); }
+  static constexpr int ESZ = 2;
+  __device__ static raw load(brsrc r, uint32_t off) { return bload16<CP_NT>(r, off); }
   __device__ static frag cvt(raw r) { FragBF16 f; f.v = __builtin_bit_cast(bf16x8, r); return f; }
 };
 template <> struct WLoad<uint8_t> {
   using raw = uint2;
   using frag = FragBF16;
-  __device__ static raw zero() { return make_uint2(0, 0); }
-  __device__ static raw load(const void* w, size_t off) { return *reinterpret_cast<const uint2*>((const uint8_t*)w + off); }
+  static constexpr int ESZ = 1;
+  __device__ static raw load(brsrc r, uint32_t off) { return bload8<CP_NT>(r, off); }
   __device__ static frag cvt(raw r) { return fp8x8_to_frag(r); }
 };
-struct F32x8 { float4 a, b; };
+struct F32x8 { uint4 a, b; };
 template <> struct WLoad<float> {
   using raw = F32x8;
   using frag = FragF32;
-  __device__ static raw zero() { F32x8 r; r.a = make_float4(0, 0, 0, 0); r.b = r.a; return r; }
-  __device__ static raw load(const void* w, size_t off) {
-    const float4* p = reinterpret_cast<const float4*>((const float*)w + off);
-    F32x8 r; r.a = p[0]; r.b = p[1]; return r;
+  static constexpr int ESZ = 4;
+  __device__ static raw load(brsrc r, uint32_t off) {
+    F32x8 v; v.a = bload16<CP_NT>(r, off); v.b = bload16<CP_NT>(r, off == BUF_OOB ? BUF_OOB : off + 16); return v;
   }
-  __device__ static frag cvt(raw r) { FragF32 f; f.lo = (f32x4){r.a.x, r.a.y, r.a.z, r.a.w}; f.hi = (f32x4){r.b.x, r.b.y, r.b.z, r.b.w}; return f; }
+  __device__ static frag cvt(raw r) {
+    FragF32 f;
+    f.lo = (f32x4){__uint_as_float(r.a.x), __uint_as_float(r.a.y), __uint_as_float(r.a.z), __uint_as_float(r.a.w)};
+    f.hi = (f32x4){__uint_as_float(r.b.x), __uint_as_float(r.b.y), __uint_as_float(r.b.z), __uint_as_float(r.b.w)};
+    return f;
+  }
 };
 
 // ---------------------------------------------------------------- LDS A fragments
@@ -104,6 +116,14 @@ __device__ __forceinline__ void lds_store4(__bf16*, char* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 __device__ __forceinline__ void lds_store4(float*, char* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+// hi = bf16(v) into p, lo = bf16(v - hi) into p + plane
+__device__ __forceinline__ void lds_store4_pair(char* p, int plane, float4 v) {
+  float hx = bf2f(f2bf(v.x)), hy = bf2f(f2bf(v.y)), hz = bf2f(f2bf(v.z)), hw = bf2f(f2bf(v.w));
+  uint2 h; h.x = pack_bf2(hx, hy); h.y = pack_bf2(hz, hw);
+  uint2 l; l.x = pack_bf2(v.x - hx, v.y - hy); l.y = pack_bf2(v.z - hz, v.w - hw);
+  *reinterpret_cast<uint2*>(p) = h;
+  *reinterpret_cast<uint2*>(p + plane) = l;
+}
 
 // ---------------------------------------------------------------- cross-workgroup hand-off
 // Device-scope relaxed atomic accesses compile to sc1 loads / stores, which
@@ -111,7 +131,6 @@ __device__ __forceinline__ void lds_store4(float*, char* p, float4 v) { *reinter
 // invalidate that a device-scope fence costs.
 __device__ __forceinline__ void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ float ld_dev(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-
 // Called by every thread after its st_dev() stores: waits for them to
 // complete, counts this workgroup in *cnt, and returns true for every
 // workgroup except the one that arrives last.
@@ -129,7 +148,7 @@ __device__ __forceinline__ bool tile_arrive(unsigned* cnt, int expected, int* fl
 constexpr int SPLIT_MAX = 16;
 
 // ---------------------------------------------------------------- tile geometry
-template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4>
+template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
 struct GemmTile {
   static constexpr int THREADS = 64 * WN * WK;
   static constexpr int NW = WN * WK;             // waves
@@ -139,23 +158,22 @@ struct GemmTile {
   static constexpr int BK = 32 * WK * U;         // chunk width
   static constexpr int ESZ = sizeof(CT);
   static constexpr int LROW = BK * ESZ + 16;     // LDS row pitch (bytes), padded
-  static constexpr int ABUF = BM * LROW;
+  static constexpr int PLANES = AC ? 2 : 1;      // compensated A: hi and lo planes
+  static constexpr int APLANE = BM * LROW;
+  static constexpr int ABUF = PLANES * APLANE;
   static constexpr int AG = (AM == A_BF16) ? 8 : 4;  // A elements per loader group
   static constexpr int AGROUPS = BM * BK / AG;   // A groups per chunk
   static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
-  static constexpr int TPR = (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 64 ? 64 : 
-                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 32 ? 32 :
-                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 16 ? 16 :
-                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 8 ? 8 :
-                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 4 ? 4 :
-                             (THREADS / (AM == A_MERGE ? 4 * BM : BM)) >= 2 ? 2 : 1;  // threads per normalised row
-  static constexpr int MAXL = 32;                // row-moment partials per thread (T <= MAXL * TPR)
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
   static constexpr int SMEM_A = 2 * ABUF;
   static constexpr int SMEM_T = BM * TPITCH * 4;
   static constexpr int NROWST = (AM == A_MERGE) ? 4 * BM : BM;   // normaliser entries
   static constexpr int SMEM = (SMEM_A > SMEM_T ? SMEM_A : SMEM_T) + NROWST * 8 + 64;
+  // threads serving one normalised row: a power of two, at most 64
+  static constexpr int TPR0 = THREADS / NROWST;
+  static constexpr int TPR = TPR0 >= 64 ? 64 : TPR0 >= 32 ? 32 : TPR0 >= 16 ? 16 : TPR0 >= 8 ? 8 : TPR0 >= 4 ? 4 : TPR0 >= 2 ? 2 : 1;
   static_assert(THREADS % (BK / AG) == 0, "a thread's A columns must not change between its row groups");
+  static_assert(!AC || (sizeof(CT) == 2 && (AM == A_NORM || AM == A_F32)), "compensated A needs a float source and bf16 MFMA");
 };
 
 // Raw A registers: bf16 sources keep 8 bf16 (copied to LDS as is), others 4 floats.
@@ -163,9 +181,9 @@ template <int AM> struct ARaw { using type = float4; };
 template <> struct ARaw<A_BF16> { using type = uint4; };
 
 // ---------------------------------------------------------------- kernel
-template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4>
+template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
 __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
-  using T = GemmTile<WT, CT, MB, WN, WK, NBW, AM, EM, UU>;
+  using T = GemmTile<WT, CT, MB, WN, WK, NBW, AM, EM, UU, AC>;
   using WL = WLoad<WT>;
   using F = typename Frag<CT>::type;
   using AR = typename ARaw<AM>::type;
@@ -195,23 +213,25 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const int ke = min(p.K, kb + p.ksplit);
   const int nchunks = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
-  // ---- weight rows of this wave's n-blocks
-  size_t wrow[NBW];
-  bool wok[NBW];
+  // ---- weight rows of this wave's n-blocks (byte offset of k = 0, or OOB)
+  const brsrc wr = make_brsrc(p.w);
+  uint32_t wrow[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; j++) {
     int jb = wn * NBW + j;                      // n-block index within the tile
     int col = lane & 15;
+    int row;
+    bool ok;
     if (EM == E_SWIGLU) {
       constexpr int HB = BN / 32 > 0 ? BN / 32 : 1;  // gate n-blocks (first half), then up n-blocks
       int on = nt * (BN / 2) + (jb % HB) * 16 + col;
-      wok[j] = on < p.N;
-      wrow[j] = (size_t)(jb < HB ? on : p.n_half + on);
+      ok = on < p.N;
+      row = jb < HB ? on : p.n_half + on;
     } else {
-      int n = nt * BN + jb * 16 + col;
-      wok[j] = n < p.N;
-      wrow[j] = (size_t)n;
+      row = nt * BN + jb * 16 + col;
+      ok = row < p.N;
     }
+    wrow[j] = ok ? (uint32_t)row * (uint32_t)p.ldw * WL::ESZ : BUF_OOB;
   }
   const int kl = (lane >> 4) * 8;               // this lane's offset inside a 32-wide k-step
 
@@ -222,24 +242,33 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       int k = kc + (u * WK + wk) * 32 + kl;
 #pragma unroll
       for (int j = 0; j < NBW; j++)
-        br[u][j] = (wok[j] && k < ke) ? WL::load(p.w, wrow[j] * (size_t)p.ldw + k) : WL::zero();
+        br[u][j] = WL::load(wr, (k < ke && wrow[j] != BUF_OOB) ? wrow[j] + (uint32_t)k * WL::ESZ : BUF_OOB);
     }
   };
 
   BR b0[U][NBW], b1[U][NBW], b2[U][NBW], b3[U][NBW];
 
-  // ---- per-row normaliser (NORM / MERGE): (mean to subtract, reciprocal std).
-  // TPR consecutive threads serve one source row: each merges every TPR-th
-  // column tile of it, then the TPR partial results are merged in a fixed
-  // butterfly. The partial loads are issued here, before the first A and W
-  // loads, and merged after them, so all of them share one memory latency.
-  constexpr int NR = T::NROWST, TPR = T::TPR;
-  constexpr int MAXL = (AM == A_NORM || AM == A_MERGE) ? T::MAXL : 1;
-  constexpr int NPASS = (NR + NT / TPR - 1) / (NT / TPR);   // row passes (1 unless NR > NT / TPR)
-  float2 rsv[NPASS][MAXL];
+  // ---- per-row normaliser (NORM / MERGE): (value to subtract, 1/std) of
+  // every source row of the tile. TPR consecutive threads serve a row; the
+  // first LB of each thread's tile partials are requested here, before the
+  // first A and W loads, and merged after them (shifted sums, then a fixed
+  // butterfly), so they share one memory latency with the weights.
+  constexpr int NR = T::NROWST, TPR = T::TPR, LB = 8;
+  constexpr bool NORMED = AM == A_NORM || AM == A_MERGE;
+  constexpr int NPASS = NORMED ? (NR + NT / TPR - 1) / (NT / TPR) : 1;   // row passes
+  float2 rsv[NPASS][NORMED ? LB : 1];
   int rsrc[NPASS];
   const int rr = tid / TPR, jj = tid % TPR;
-  if constexpr (AM == A_NORM || AM == A_MERGE) {
+  const brsrc rsr = make_brsrc(p.rs.part);
+  auto load_parts = [&](float2 (&v)[NORMED ? LB : 1], int src, int t0) {
+#pragma unroll
+    for (int u = 0; u < (NORMED ? LB : 1); u++) {
+      int t = t0 + jj + u * TPR;
+      uint2 b = bload8(rsr, (src >= 0 && t < p.rs.T) ? ((uint32_t)t * p.rs.M + src) * 8u : BUF_OOB);
+      v[u] = make_float2(__uint_as_float(b.x), __uint_as_float(b.y));
+    }
+  };
+  if constexpr (NORMED) {
 #pragma unroll
     for (int ps = 0; ps < NPASS; ps++) {
       const int r = ps * (NT / TPR) + rr;
@@ -249,7 +278,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
           int m = m0 + r;
           src = m < p.M ? m : -1;
         } else {
-          int mr = r >> 2, sub = r & 3;           // merged row, 2x2 member
+          int mr = r >> 2, sub = r & 3;         // merged row, 2x2 member
           int m = m0 + mr;
           if (m < p.M && sub < p.merge * p.merge) {
             int per = p.n_merged, im = m / per, mm = m % per;
@@ -261,36 +290,31 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         }
       }
       rsrc[ps] = src;
-#pragma unroll
-      for (int u = 0; u < MAXL; u++) {
-        int t = jj + u * TPR;
-        rsv[ps][u] = (src >= 0 && t < p.rs.T) ? p.rs.part[(size_t)t * p.rs.M + src] : make_float2(0.f, 0.f);
-      }
+      load_parts(rsv[ps], src, 0);
     }
   }
-  auto merge_rows = [&]() {
-    if constexpr (AM == A_NORM || AM == A_MERGE) {
+  auto row_coeffs = [&]() {
+    if constexpr (NORMED) {
 #pragma unroll
       for (int ps = 0; ps < NPASS; ps++) {
         const int r = ps * (NT / TPR) + rr;
         const int src = rsrc[ps];
-        float n = 0.f, mean = 0.f, m2 = 0.f;
+        ShiftSum a;
+        for (int t0 = 0;; t0 += LB * TPR) {
 #pragma unroll
-        for (int u = 0; u < MAXL; u++) {
-          int t = jj + u * TPR;
-          if (src >= 0 && t < p.rs.T) moments_merge(n, mean, m2, (float)min(p.rs.tw, p.rs.N - t * p.rs.tw), rsv[ps][u].x, rsv[ps][u].y);
+          for (int u = 0; u < LB; u++) {
+            int t = t0 + jj + u * TPR;
+            if (src >= 0 && t < p.rs.T) a.add(tile_count(p.rs, t), rsv[ps][u]);
+          }
+          if (t0 + LB * TPR >= p.rs.T) break;     // uniform: more than LB partials per thread is rare
+          load_parts(rsv[ps], src, t0 + LB * TPR);
         }
-#pragma unroll
-        for (int o = TPR >> 1; o >= 1; o >>= 1) {
-          float n2 = __shfl_xor(n, o, WAVE), mean2 = __shfl_xor(mean, o, WAVE), m22 = __shfl_xor(m2, o, WAVE);
-          moments_merge(n, mean, m2, n2, mean2, m22);
-        }
-        if (jj == 0 && r < NR) {
-          float var = n > 0.f ? m2 / n : 0.f;
-          float mu = p.norm_rms ? 0.f : mean;
-          float ms = p.norm_rms ? var + mean * mean : var;
-          sRow[r] = src >= 0 ? make_float2(mu, rsqrtf(ms + p.eps)) : make_float2(0.f, 0.f);
-        }
+        float n, mean, m2;
+        a.moments(n, mean, m2);
+        group_merge(n, mean, m2, TPR);
+        if (jj == 0 && r < NR)
+          sRow[r] = src >= 0 ? norm_coeffs(make_float2(mean, n > 0.f ? m2 / n : 0.f), p.norm_rms, p.eps)
+                             : make_float2(0.f, 0.f);
       }
     }
   };
@@ -301,6 +325,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   constexpr int RS = NT / CPR;                  // row stride between a thread's groups
   const int ar0 = tid / CPR;
   const int ac4 = (tid % CPR) * AG;
+  const brsrc ars = make_brsrc(p.a);
+  constexpr int AESZ = (AM == A_BF16 || AM == A_PATCH) ? 2 : 4;
 
   auto load_a = [&](AR (&ar)[GPT], int kc) {
     int k = kc + ac4;
@@ -310,39 +336,31 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       int m = m0 + r;
       bool ok = r < BM && m < p.M && k < p.K;
       if constexpr (AM == A_BF16) {
-        ar[i] = ok ? *reinterpret_cast<const uint4*>((const uint16_t*)p.a + (size_t)m * p.lda + k) : make_uint4(0, 0, 0, 0);
+        ar[i] = bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB);
       } else if constexpr (AM == A_F32 || AM == A_NORM) {
-        ar[i] = ok ? *reinterpret_cast<const float4*>((const float*)p.a + (size_t)m * p.lda + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 4u : BUF_OOB));
       } else if constexpr (AM == A_PATCH) {
-        float t4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (m < p.M) {
-          int im = m / p.n_patches, pi = m % p.n_patches;
-          int pr = pi / p.vgrid, pc = pi % p.vgrid;
-          int P2 = p.patch * p.patch;
+        int im = m / p.n_patches, pi = m % p.n_patches;
+        int pr = pi / p.vgrid, pc = pi % p.vgrid;
+        int P2 = p.patch * p.patch;
+        float t4[4];
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            int kk = k + e;
-            if (kk < p.K) {
-              int c = kk / P2, rem = kk % P2, ky = rem / p.patch, kx = rem % p.patch;
-              size_t off = (((size_t)im * p.chans + c) * p.img + pr * p.patch + ky) * p.img + pc * p.patch + kx;
-              t4[e] = bf2f(((const uint16_t*)p.a)[off]);
-            }
-          }
+        for (int e = 0; e < 4; e++) {
+          int kk = k + e;
+          int c = kk / P2, rem = kk % P2, ky = rem / p.patch, kx = rem % p.patch;
+          uint32_t off = ((((uint32_t)im * p.chans + c) * p.img + pr * p.patch + ky) * p.img + pc * p.patch + kx) * 2u;
+          t4[e] = bf2f(bload2(ars, (r < BM && m < p.M && kk < p.K) ? off : BUF_OOB));
         }
         ar[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
       } else if constexpr (AM == A_MERGE) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (ok) {
-          int D = p.lda;
-          int per = p.n_merged, im = m / per, mm = m % per;
-          int gq = p.vgrid / p.merge;
-          int R = mm / gq, C = mm % gq;
-          int sub = k / D, d = k % D;
-          int dy = sub / p.merge, dx = sub % p.merge;
-          int src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
-          v = *reinterpret_cast<const float4*>((const float*)p.a + (size_t)src * D + d);
-        }
-        ar[i] = v;
+        int D = p.lda;
+        int per = p.n_merged, im = m / per, mm = m % per;
+        int gq = p.vgrid / p.merge;
+        int R = mm / gq, C = mm % gq;
+        int sub = k / D, d = k % D;
+        int dy = sub / p.merge, dx = sub % p.merge;
+        int src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
+        ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)src * D + d) * 4u : BUF_OOB));
       } else {
         ar[i] = make_float4(0.f, 0.f, 0.f, 0.f);   // TIME: computed at store time
       }
@@ -371,7 +389,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       bool ok = m < p.M && k < p.K;
       float4 v;
       if constexpr (AM == A_BF16) {
-        // raw copy of 8 bf16 (CT is bf16 for every bf16 source)
+        // raw copy of 8 bf16 (CT is bf16 for every bf16 source; zeros beyond the edge)
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
         continue;
       } else if constexpr (AM == A_NORM || AM == A_MERGE) {
@@ -401,7 +419,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       } else {
         v = ar[i];
       }
-      lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
+      if constexpr (AC) lds_store4_pair(base + r * LROW + ac4 * T::ESZ, T::APLANE, v);
+      else lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
     }
   };
 
@@ -421,10 +440,17 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       for (int j = 0; j < NBW; j++) bf[j] = WL::cvt(br[u][j]);
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
+        const char* ap = base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ;
         F af;
-        lds_frag(af, base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ);
+        lds_frag(af, ap);
 #pragma unroll
         for (int j = 0; j < NBW; j++) mma32(acc[mb][j], af, bf[j]);
+        if constexpr (AC) {
+          F al;
+          lds_frag(al, ap + T::APLANE);
+#pragma unroll
+          for (int j = 0; j < NBW; j++) mma32(acc[mb][j], al, bf[j]);
+        }
       }
     }
   };
@@ -433,37 +459,39 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   // ahead), activations staged into LDS buffer c%2 from register slot c%2
   // (issued two chunks ahead, stored one chunk ahead). Loads complete in
   // issue order (vmcnt), so each chunk's activations are issued before its
-  // weights: waiting for A of chunk c+1 never waits for later weights.
+  // weights: waiting for A of chunk c+1 never waits for later weights. Loads
+  // past the last chunk read zeros (out-of-range offsets) and are never used.
   AR a0[GPT], a1[GPT];
-  if (nchunks > 0) { load_a(a0, kb); load_b(b0, kb); }
-  if (nchunks > 1) { load_a(a1, kb + BK); load_b(b1, kb + BK); }
-  if (nchunks > 2) load_b(b2, kb + 2 * BK);
-  // residual inputs of a small unsplit tile are fetched now as well
+  load_a(a0, kb); load_b(b0, kb);
+  load_a(a1, kb + BK); load_b(b1, kb + BK);
+  load_b(b2, kb + 2 * BK);
+  // residual inputs of a small unsplit tile are fetched now as well (same
+  // element mapping as the epilogue: column tid % BN, rows tid / BN + i * NT / BN)
   constexpr int XPT = (BM * BN + NT - 1) / NT;
   float xpre[XPT <= 4 ? XPT : 1];
   const bool xpref = EM == E_RESID && XPT <= 4 && p.split == 1 && !p.x_init;
   if constexpr (EM == E_RESID && XPT <= 4) {
     if (xpref) {
+      const brsrc xr = make_brsrc(p.x);
+      const int n = nt * BN + tid % BN;
 #pragma unroll
       for (int q = 0; q < XPT; q++) {
-        int e = tid + q * NT;
-        int r = e / BN, cc = e % BN;
-        int m = m0 + r, n = nt * BN + cc;
-        xpre[q] = (e < BM * BN && m < p.M && n < p.N) ? p.x[(size_t)m * p.ldx + n] : 0.f;
+        int m = m0 + tid / BN + q * (NT / BN);
+        xpre[q] = bloadf(xr, (m < p.M && n < p.N) ? ((uint32_t)m * p.ldx + n) * 4u : BUF_OOB);
       }
     }
   }
-  merge_rows();
+  row_coeffs();
   __syncthreads();   // sRow ready
-  if (nchunks > 0) store_a(0, a0, kb);
+  store_a(0, a0, kb);
   __syncthreads();
 
 #define VLA_GEMM_ITER(C, BCUR, BNEXT3, ARELOAD, ASTORE)                     \
-  if ((C) < nchunks) {                                                      \
-    if ((C) + 2 < nchunks) load_a(ARELOAD, kb + ((C) + 2) * BK);            \
-    if ((C) + 3 < nchunks) load_b(BNEXT3, kb + ((C) + 3) * BK);             \
-    compute((C) & 1, BCUR);                                                 \
-    if ((C) + 1 < nchunks) store_a(((C) + 1) & 1, ASTORE, kb + ((C) + 1) * BK); \
+  {                                                                         \
+    load_a(ARELOAD, kb + ((C) + 2) * BK);                                   \
+    load_b(BNEXT3, kb + ((C) + 3) * BK);                                    \
+    if ((C) < nchunks) compute((C) & 1, BCUR);                              \
+    store_a(((C) + 1) & 1, ASTORE, kb + ((C) + 1) * BK);                    \
     __syncthreads();                                                        \
   }
   for (int c = 0; c < nchunks; c += 4) {
@@ -493,121 +521,153 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     __syncthreads();
   }
 
+  // ---- epilogue geometry: NT is a multiple of BN, so each thread keeps one
+  // column cc of the tile and visits rows r0e + i * RPT (i < XPT); per-column
+  // vectors are loaded once and every thread issues all of its loads before
+  // the first wait
+  static_assert(NT % BN == 0 && BM % (NT / BN) == 0, "epilogue: each thread owns one column");
+  constexpr int RPT = NT / BN;
+  constexpr int XPE = BM / RPT;                 // elements per thread
+  const int cc = tid % BN, r0e = tid / BN;
+  const int ncol = nt * BN + cc;                // output column (STORE / ROPE / RESID)
+
+  // residual inputs (unsplit small tiles fetched them before the main loop)
+  float xv[EM == E_RESID ? XPE : 1];
+  if constexpr (EM == E_RESID) {
+    if (!p.x_init) {
+      const brsrc xr = make_brsrc(p.x);
+#pragma unroll
+      for (int i = 0; i < XPE; i++) {
+        int m = m0 + r0e + i * RPT;
+        if constexpr (XPT <= 4 && XPE <= XPT) {
+          if (xpref) { xv[i] = xpre[i]; continue; }
+        }
+        xv[i] = bloadf(xr, (m < p.M && ncol < p.N) ? ((uint32_t)m * p.ldx + ncol) * 4u : BUF_OOB);
+      }
+    }
+  }
+
   // ---- split-K: publish the partial tile; the last arriving workgroup sums
-  // all partials in split order. Partials are written and read with
-  // device-scope atomic accesses (coherent across XCDs without flushing or
-  // invalidating the L2); the counter increment is issued only after every
-  // thread's stores have completed.
+  // all partials in split order. Partials are written with device-scope
+  // atomic stores and read with device-coherent (sc1) loads, so the hand-off
+  // needs no L2 write-back or invalidate; the counter increment is issued
+  // only after every thread's stores have completed.
   if (p.split > 1) {
     const int tile = mt * p.n_tiles_n + nt;
     const size_t tstride = (size_t)p.n_tiles_m * p.n_tiles_n * (BM * BN);
     float* mine = p.part + (size_t)s * tstride + (size_t)tile * (BM * BN);
-    for (int e = tid; e < BM * BN; e += NT) st_dev(mine + e, sT[(e / BN) * TPITCH + (e % BN)]);
-    if (tile_arrive(p.cnt_tile + tile, p.split, sFlag)) return;
-    const float* base = p.part + (size_t)tile * (BM * BN);
-    for (int e = tid; e < BM * BN; e += NT) {
-      float v[SPLIT_MAX];
 #pragma unroll
-      for (int q = 0; q < SPLIT_MAX; q++) v[q] = q < p.split ? ld_dev(base + (size_t)q * tstride + e) : 0.f;
-      float sum = 0.f;
-#pragma unroll
-      for (int q = 0; q < SPLIT_MAX; q++) sum += v[q];
-      sT[(e / BN) * TPITCH + (e % BN)] = sum;
+    for (int i = 0; i < XPE; i++) {
+      int r = r0e + i * RPT;
+      st_dev(mine + r * BN + cc, sT[r * TPITCH + cc]);
     }
+    if (tile_arrive(p.cnt_tile + tile, p.split, sFlag)) return;
+    const brsrc pr = make_brsrc(p.part + (size_t)tile * (BM * BN));
+    float sum[XPE];
+#pragma unroll
+    for (int i = 0; i < XPE; i++) sum[i] = 0.f;
+    for (int q = 0; q < p.split; q++) {
+      float v[XPE];
+#pragma unroll
+      for (int i = 0; i < XPE; i++) v[i] = bloadf<CP_SC1>(pr, (uint32_t)(q * tstride + (r0e + i * RPT) * BN + cc) * 4u);
+#pragma unroll
+      for (int i = 0; i < XPE; i++) sum[i] += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < XPE; i++) sT[(r0e + i * RPT) * TPITCH + cc] = sum[i];
     if (tid == 0) p.cnt_tile[tile] = 0u;
     __syncthreads();
   }
 
   // ---- epilogues
   if constexpr (EM == E_STORE) {
-    for (int e = tid; e < BM * BN; e += NT) {
-      int r = e / BN, cc = e % BN;
-      int m = m0 + r, n = nt * BN + cc;
-      if (m >= p.M || n >= p.N) continue;
-      float v = sT[r * TPITCH + cc];
-      if (p.wscale) v *= p.wscale[n];
-      if (p.bias) v += p.bias[n];
+    const bool cok = ncol < p.N;
+    const float sc = (p.wscale && cok) ? p.wscale[ncol] : 1.f;
+    const float bi = (p.bias && cok) ? p.bias[ncol] : 0.f;
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      int r = r0e + i * RPT, m = m0 + r;
+      if (m >= p.M || !cok) continue;
+      float v = sT[r * TPITCH + cc] * sc + bi;
       if (p.act == ACT_GELU) v = gelu_erf(v);
       else if (p.act == ACT_SILU) v = silu(v);
-      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = v;
-      else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(v);
+      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + ncol] = v;
+      else ((uint16_t*)p.c)[(size_t)m * p.ldc + ncol] = f2bf(v);
     }
   } else if constexpr (EM == E_ROPE) {
     const int D = p.head_dim, hd = D >> 1;
-    const float l2b = log2f(p.rope_base);
-    for (int e = tid; e < BM * BN; e += NT) {
-      int r = e / BN, cc = e % BN;
-      int m = m0 + r, n = nt * BN + cc;
-      if (m >= p.M || n >= p.N) continue;
-      float v = sT[r * TPITCH + cc];
-      if (p.wscale) v *= p.wscale[n];
-      if (n < p.q_cols + p.k_cols) {
-        int d = (n < p.q_cols ? n : n - p.q_cols) % D;
-        int i = d < hd ? d : d - hd;
-        int pc = d < hd ? cc + hd : cc - hd;
-        int pn = d < hd ? n + hd : n - hd;
-        float v2 = sT[r * TPITCH + pc];
-        if (p.wscale) v2 *= p.wscale[pn];
-        float theta = exp2f(-2.0f * (float)i / (float)D * l2b);
+    const bool cok = ncol < p.N;
+    const bool rot = ncol < p.q_cols + p.k_cols;
+    const int d = (ncol < p.q_cols ? ncol : ncol - p.q_cols) % D;
+    const int fi = d < hd ? d : d - hd;
+    const int pc = d < hd ? cc + hd : cc - hd;           // partner column in the tile
+    const int pn = d < hd ? ncol + hd : ncol - hd;
+    const float sc = (p.wscale && cok) ? p.wscale[ncol] : 1.f;
+    const float sc2 = (p.wscale && cok && rot) ? p.wscale[pn] : 1.f;
+    const float theta = exp2f(-2.0f * (float)fi / (float)D * log2f(p.rope_base));
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      int r = r0e + i * RPT, m = m0 + r;
+      if (m >= p.M || !cok) continue;
+      float v = sT[r * TPITCH + cc] * sc;
+      if (rot) {
+        float v2 = sT[r * TPITCH + pc] * sc2;
         float sn, cs;
         sincosf((float)(m + p.pos0) * theta, &sn, &cs);
         v = d < hd ? v * cs - v2 * sn : v * cs + v2 * sn;
       }
-      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = v;
-      else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(v);
+      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + ncol] = v;
+      else ((uint16_t*)p.c)[(size_t)m * p.ldc + ncol] = f2bf(v);
     }
   } else if constexpr (EM == E_SWIGLU) {
     constexpr int BO = BN / 2;
-    for (int e = tid; e < BM * BO; e += NT) {
-      int r = e / BO, cc = e % BO;
-      int m = m0 + r, n = nt * BO + cc;
-      if (m >= p.M || n >= p.N) continue;
-      float gv = sT[r * TPITCH + cc], uv = sT[r * TPITCH + BO + cc];
-      if (p.wscale) { gv *= p.wscale[n]; uv *= p.wscale[p.n_half + n]; }
+    static_assert(NT % BO == 0, "swiglu epilogue: each thread owns one column");
+    constexpr int RPO = NT / BO, XPO = BM / RPO;
+    const int co = tid % BO, r0o = tid / BO;
+    const int n = nt * BO + co;
+    const bool cok = n < p.N;
+    const float sg = (p.wscale && cok) ? p.wscale[n] : 1.f;
+    const float su = (p.wscale && cok) ? p.wscale[p.n_half + n] : 1.f;
+#pragma unroll
+    for (int i = 0; i < XPO; i++) {
+      int r = r0o + i * RPO, m = m0 + r;
+      if (m >= p.M || !cok) continue;
+      float gv = sT[r * TPITCH + co] * sg, uv = sT[r * TPITCH + BO + co] * su;
       float a = silu(gv) * uv;
       if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = a;
       else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(a);
     }
   } else if constexpr (EM == E_RESID) {
-#pragma unroll 1
-    for (int q = 0, e = tid; e < BM * BN; q++, e += NT) {
-      int r = e / BN, cc = e % BN;
-      int m = m0 + r, n = nt * BN + cc;
-      if (m >= p.M || n >= p.N) continue;
-      float v = sT[r * TPITCH + cc];
-      if (p.wscale) v *= p.wscale[n];
-      if (p.bias) v += p.bias[n];
-      if (p.gate) v *= p.gate[n];
-      float* xp = p.x + (size_t)m * p.ldx + n;
+    const bool cok = ncol < p.N;
+    const float sc = (p.wscale && cok) ? p.wscale[ncol] : 1.f;
+    const float bi = (p.bias && cok) ? p.bias[ncol] : 0.f;
+    const float ga = (p.gate && cok) ? p.gate[ncol] : 1.f;
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      int r = r0e + i * RPT, m = m0 + r;
+      if (m >= p.M || !cok) continue;
+      float v = (sT[r * TPITCH + cc] * sc + bi) * ga;
       float xn;
       if (p.x_init) {
         xn = v;
-        if (p.addrow) xn += p.addrow[(size_t)(m % p.addrow_rows) * p.N + n];
+        if (p.addrow) xn += p.addrow[(size_t)(m % p.addrow_rows) * p.N + ncol];
       } else {
-        float xo = 0.f;
-        bool got = false;
-        if constexpr (XPT <= 4) {
-#pragma unroll
-          for (int qq = 0; qq < XPT; qq++)
-            if (xpref && qq == q) { xo = xpre[qq]; got = true; }
-        }
-        if (!got) xo = *xp;
-        xn = xo + v;
+        xn = xv[i] + v;
       }
-      *xp = xn;
+      p.x[(size_t)m * p.ldx + ncol] = xn;
       sT[r * TPITCH + cc] = xn;
     }
     __syncthreads();
-    // per-row moments of this tile's columns, merged by the next reader
+    // moments of this tile's columns per row, merged by the stream's next reader
     const int ncols = min(BN, p.N - nt * BN);
     for (int r = wave; r < BM; r += NW) {
       int m = m0 + r;
       if (m >= p.M) continue;          // wave-uniform
       float sum = 0.f;
-      for (int cc = lane; cc < ncols; cc += 64) sum += sT[r * TPITCH + cc];
+      for (int c2 = lane; c2 < ncols; c2 += 64) sum += sT[r * TPITCH + c2];
       float mean = wave_sum(sum) / (float)ncols;
       float sq = 0.f;
-      for (int cc = lane; cc < ncols; cc += 64) { float d = sT[r * TPITCH + cc] - mean; sq += d * d; }
+      for (int c2 = lane; c2 < ncols; c2 += 64) { float dd = sT[r * TPITCH + c2] - mean; sq += dd * dd; }
       float m2 = wave_sum(sq);
       if (lane == 0) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, m2);
     }

@@ -2,7 +2,7 @@
 #include "gemm_inst.h"
 
 namespace vla {
-bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out) {
+bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out) {
   VLA_GEMM_NARROW(float, float, A_F32, E_STORE)
   VLA_GEMM_NARROW(float, float, A_F32, E_RESID)
   VLA_GEMM_WIDE(float, float, A_NORM, E_ROPE)

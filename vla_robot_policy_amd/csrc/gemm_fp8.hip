@@ -4,7 +4,7 @@
 #include "gemm_inst.h"
 
 namespace vla {
-bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out) {
+bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out) {
   VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_NORM, E_STORE)

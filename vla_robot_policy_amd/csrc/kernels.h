@@ -10,10 +10,11 @@ struct KernelRef {
   int threads;  // workgroup size
 };
 
-// GEMM: wt 0 = f32, 1 = bf16, 2 = fp8 (vla_dtype values); am / em from gemm.h.
-bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out);
-bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out);
-bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, KernelRef* out);
+// GEMM: one lookup per weight type; am / em from gemm.h, tile (mb, wn, wk,
+// nbw), u k-steps per chunk, ac = compensated (hi + lo) bf16 activations.
+bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
+bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
+bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
 
 // Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
 bool attn_lookup(int f32, int dp, int hpw, KernelRef* out);

@@ -15,8 +15,8 @@ __global__ void k_fill_u32(unsigned* p, unsigned v, int n) {
 }
 
 // x[r] = src[r - r0] for r in [r0, r1) (bf16 or fp32 source), then the
-// moments (mean, M2) of every row r < M as a single column tile
-// (part[r] = (mean, sum of squared deviations)). One wave per row.
+// moments of every row r < M as a single column tile (stats[r] = (mean,
+// sum of squared deviations)). One wave per row.
 __global__ __launch_bounds__(256) void k_stage_rows(float* x, int ldx, int M, int N, const void* src, int src_f32,
                                                   int ld_src, int r0, int r1, float2* stats) {
   int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -44,11 +44,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, in
   int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (r >= M) return;
-  int rows[1] = {r};
-  float2 mv[1];
-  rows_moments_wave<1>(st_in, rows, mv);
-  float2 st = mv[0];
-  float rs = rsqrtf(st.y + st.x * st.x + eps);
+  float rs = norm_coeffs(row_moments_wave(st_in, r), 1, eps).y;
   for (int c = lane; c < N; c += 64) {
     float v = x[(size_t)r * ldx + c] * rs * gain[c];
     if (out_f32) ((float*)out)[(size_t)r * ldo + c] = v;
@@ -75,18 +71,15 @@ __global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* arow = p.a_in + (size_t)m * p.A;
   if (p.w_out) {
-    __shared__ float2 smv;
+    __shared__ float2 snc;
     if (wave == 0) {
-      int rows[1] = {m};
-      float2 mv[1];
-      rows_moments_wave<1>(p.rs, rows, mv);
-      if (lane == 0) smv = mv[0];
+      float2 nc = norm_coeffs(row_moments_wave(p.rs, m), 0, p.eps);
+      if (lane == 0) snc = nc;
     }
     __syncthreads();
-    float2 st = smv;
-    float rs = rsqrtf(st.y + p.eps);
+    const float2 nc = snc;
     for (int d = tid; d < p.D; d += 256)
-      su[d] = (p.x[(size_t)m * p.D + d] - st.x) * rs * (1.f + p.scale[d]) + p.shift[d];
+      su[d] = (p.x[(size_t)m * p.D + d] - nc.x) * nc.y * (1.f + p.scale[d]) + p.shift[d];
     __syncthreads();
     for (int a = wave; a < p.A; a += 4) {
       float acc = 0.f;
