@@ -146,12 +146,14 @@ struct GemmOp {
   int ac = 0;   // compensated (hi + lo) bf16 activations
 };
 
-// Row tile (16-row blocks) by M; rows beyond 128 use several row tiles.
+// Row tile (16-row blocks) by M: one tile up to 112 rows; 64-row tiles up to
+// 256 rows (twice the workgroups of 128-row tiles, a quarter of the LDS
+// traffic per MFMA of narrower ones); 128-row tiles beyond.
 // Narrow tiles: 16 columns with 4 waves splitting K when M <= 16, else 64
 // columns with 4 waves side by side. Wide tiles (RoPE pairs, gate/up pairs):
 // 128 columns with 8 waves side by side.
 void pick_tile(int M, int em, int ac, int& mb, int& wn, int& wk, int& nbw, int& u) {
-  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : 8;
+  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : M <= 256 ? 4 : 8;
   u = ac ? 2 : 4;
   bool wide = em == E_ROPE || em == E_SWIGLU;
   nbw = 1;

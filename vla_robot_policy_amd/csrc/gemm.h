@@ -166,7 +166,7 @@ struct GemmTile {
   static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
   static constexpr int SMEM_A = 2 * ABUF;
-  static constexpr int SMEM_T = BM * TPITCH * 4;
+  static constexpr int SMEM_T = WK * BM * TPITCH * 4;   // one fp32 tile slice per k-wave
   static constexpr int NROWST = (AM == A_MERGE) ? 4 * BM : BM;   // normaliser entries
   static constexpr int SMEM = (SMEM_A > SMEM_T ? SMEM_A : SMEM_T) + NROWST * 8 + 64;
   // threads serving one normalised row: a power of two, at most 64
@@ -502,34 +502,45 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   }
 #undef VLA_GEMM_ITER
 
-  // ---- reduce the WK wave slices into the fp32 LDS tile (fixed order)
-#pragma unroll 1
-  for (int w = 0; w < WK; w++) {
-    if (wk == w) {
+  // ---- reduce the WK wave slices into the fp32 LDS tile: every slice is
+  // written at once (slice w at sT + w * BM * TPITCH), one barrier, then the
+  // epilogue threads sum the slices of their elements in slice order
+  // (the main loop ended with a barrier: the aliased A buffers are free)
 #pragma unroll
-      for (int mb = 0; mb < MB; mb++)
+  for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-        for (int j = 0; j < NBW; j++)
+    for (int j = 0; j < NBW; j++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            int r = mb * 16 + (lane >> 4) * 4 + i;
-            int cidx = (wn * NBW + j) * 16 + (lane & 15);
-            float* d = sT + r * TPITCH + cidx;
-            *d = (w == 0) ? acc[mb][j][i] : *d + acc[mb][j][i];
-          }
-    }
-    __syncthreads();
-  }
-
+      for (int i = 0; i < 4; i++) {
+        int r = mb * 16 + (lane >> 4) * 4 + i;
+        int cidx = (wn * NBW + j) * 16 + (lane & 15);
+        sT[(size_t)wk * BM * TPITCH + r * TPITCH + cidx] = acc[mb][j][i];
+      }
+  __syncthreads();
   // ---- epilogue geometry: NT is a multiple of BN, so each thread keeps one
   // column cc of the tile and visits rows r0e + i * RPT (i < XPT); per-column
   // vectors are loaded once and every thread issues all of its loads before
   // the first wait
-  static_assert(NT % BN == 0 && BM % (NT / BN) == 0, "epilogue: each thread owns one column");
+  static_assert(NT % BN == 0, "epilogue: each thread owns one column");
   constexpr int RPT = NT / BN;
-  constexpr int XPE = BM / RPT;                 // elements per thread
+  constexpr int XPE = (BM + RPT - 1) / RPT;     // elements per thread (threads past BM rows idle)
   const int cc = tid % BN, r0e = tid / BN;
   const int ncol = nt * BN + cc;                // output column (STORE / ROPE / RESID)
+  if constexpr (WK > 1) {
+    // sum the K slices of this thread's elements (slice order), into slice 0;
+    // SWIGLU reads other columns, so every thread finishes before any reads
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      int r = r0e + i * RPT;
+      if (r < BM) {
+        float v = sT[r * TPITCH + cc];
+#pragma unroll
+        for (int w = 1; w < WK; w++) v += sT[(size_t)w * BM * TPITCH + r * TPITCH + cc];
+        sT[r * TPITCH + cc] = v;
+      }
+    }
+    __syncthreads();
+  }
 
   // residual inputs (unsplit small tiles fetched them before the main loop)
   float xv[EM == E_RESID ? XPE : 1];
@@ -539,6 +550,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < XPE; i++) {
         int m = m0 + r0e + i * RPT;
+        if (r0e + i * RPT >= BM) { xv[i] = 0.f; continue; }
         if constexpr (XPT <= 4 && XPE <= XPT) {
           if (xpref) { xv[i] = xpre[i]; continue; }
         }
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT;
-      st_dev(mine + r * BN + cc, sT[r * TPITCH + cc]);
+      if (r < BM) st_dev(mine + r * BN + cc, sT[r * TPITCH + cc]);
     }
     if (tile_arrive(p.cnt_tile + tile, p.split, sFlag)) return;
     const brsrc pr = make_brsrc(p.part + (size_t)tile * (BM * BN));
@@ -569,12 +581,14 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     for (int q = 0; q < p.split; q++) {
       float v[XPE];
 #pragma unroll
-      for (int i = 0; i < XPE; i++) v[i] = bloadf<CP_SC1>(pr, (uint32_t)(q * tstride + (r0e + i * RPT) * BN + cc) * 4u);
+      for (int i = 0; i < XPE; i++)
+        v[i] = bloadf<CP_SC1>(pr, r0e + i * RPT < BM ? (uint32_t)(q * tstride + (r0e + i * RPT) * BN + cc) * 4u : BUF_OOB);
 #pragma unroll
       for (int i = 0; i < XPE; i++) sum[i] += v[i];
     }
 #pragma unroll
-    for (int i = 0; i < XPE; i++) sT[(r0e + i * RPT) * TPITCH + cc] = sum[i];
+    for (int i = 0; i < XPE; i++)
+      if (r0e + i * RPT < BM) sT[(r0e + i * RPT) * TPITCH + cc] = sum[i];
     if (tid == 0) p.cnt_tile[tile] = 0u;
     __syncthreads();
   }
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;
-      if (m >= p.M || !cok) continue;
+      if (r >= BM || m >= p.M || !cok) continue;
       float v = sT[r * TPITCH + cc] * sc + bi;
       if (p.act == ACT_GELU) v = gelu_erf(v);
       else if (p.act == ACT_SILU) v = silu(v);
@@ -608,7 +622,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;
-      if (m >= p.M || !cok) continue;
+      if (r >= BM || m >= p.M || !cok) continue;
       float v = sT[r * TPITCH + cc] * sc;
       if (rot) {
         float v2 = sT[r * TPITCH + pc] * sc2;
@@ -622,7 +636,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   } else if constexpr (EM == E_SWIGLU) {
     constexpr int BO = BN / 2;
     static_assert(NT % BO == 0, "swiglu epilogue: each thread owns one column");
-    constexpr int RPO = NT / BO, XPO = BM / RPO;
+    constexpr int RPO = NT / BO, XPO = (BM + RPO - 1) / RPO;
     const int co = tid % BO, r0o = tid / BO;
     const int n = nt * BO + co;
     const bool cok = n < p.N;
@@ -631,7 +645,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < XPO; i++) {
       int r = r0o + i * RPO, m = m0 + r;
-      if (m >= p.M || !cok) continue;
+      if (r >= BM || m >= p.M || !cok) continue;
       float gv = sT[r * TPITCH + co] * sg, uv = sT[r * TPITCH + BO + co] * su;
       float a = silu(gv) * uv;
       if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = a;
@@ -645,7 +659,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;
-      if (m >= p.M || !cok) continue;
+      if (r >= BM || m >= p.M || !cok) continue;
       float v = (sT[r * TPITCH + cc] * sc + bi) * ga;
       float xn;
       if (p.x_init) {
@@ -657,19 +671,26 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       p.x[(size_t)m * p.ldx + ncol] = xn;
       sT[r * TPITCH + cc] = xn;
     }
-    __syncthreads();
-    // moments of this tile's columns per row, merged by the stream's next reader
+    // moments of this tile's columns per row, merged by the stream's next
+    // reader: the G = min(BN, 64) lanes holding a row reduce it together
+    // (all rows of the tile at once); a wider tile adds its waves' halves
+    constexpr int G = BN < 64 ? BN : 64;
+    static_assert(BN <= 64, "residual tiles are at most 64 columns wide");
     const int ncols = min(BN, p.N - nt * BN);
-    for (int r = wave; r < BM; r += NW) {
-      int m = m0 + r;
-      if (m >= p.M) continue;          // wave-uniform
-      float sum = 0.f;
-      for (int c2 = lane; c2 < ncols; c2 += 64) sum += sT[r * TPITCH + c2];
-      float mean = wave_sum(sum) / (float)ncols;
-      float sq = 0.f;
-      for (int c2 = lane; c2 < ncols; c2 += 64) { float dd = sT[r * TPITCH + c2] - mean; sq += dd * dd; }
-      float m2 = wave_sum(sq);
-      if (lane == 0) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, m2);
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      int r = r0e + i * RPT, m = m0 + r;
+      bool live = r < BM && m < p.M && cc < ncols;
+      float v = live ? sT[r * TPITCH + cc] : 0.f;
+      float sum = v;
+#pragma unroll
+      for (int o = G >> 1; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, WAVE);
+      float mean = sum / (float)ncols;
+      float d = live ? v - mean : 0.f;
+      float sq = d * d;
+#pragma unroll
+      for (int o = G >> 1; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, WAVE);
+      if (cc == 0 && r < BM && m < p.M) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, sq);
     }
   }
 }
