@@ -24,6 +24,7 @@
 #include "attention.h"
 #include "kernels.h"
 #include "tail.h"
+#include "dit_stack.h"
 
 using namespace vla;
 
@@ -460,6 +461,25 @@ vla_status check_dit(const vla_dit* d) {
   return VLA_OK;
 }
 
+// Compute units of the current device (one persistent workgroup each); 256
+// when it cannot be queried (sizing a workspace without a device).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+// The persistent layer kernel covers chunks of at most 16 rows whose GEMMs
+// split into 16-column units of one D-wide k-extent each.
+bool dit_stack_ok(const vla_dit_cfg& cf, int n, int G) {
+  const int D = cf.hidden;
+  if (n < 1 || n > 16 || cf.head_dim > DS_DP || cf.head_dim % 8 || D % 32 || D > 4 * DS_KSW * 32) return false;
+  if (cf.mlp % D) return false;
+  const int most = std::max(3 * D / 16, std::max(cf.mlp / 16, (D / 16) * (cf.mlp / D)));
+  return most <= DS_MAXU * G && cf.heads <= DS_MAXU * G;
+}
+
 struct DitIO {
   const void* ctx; int ctx_len;
   const float* x0; int n, A, K;
@@ -482,6 +502,22 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
   uint16_t* ao = c.take<uint16_t>((size_t)n * D);
   uint16_t* q = c.take<uint16_t>((size_t)n * D);
   uint16_t* h = c.take<uint16_t>((size_t)n * cf.mlp);
+  const int G = cu_count();
+  const bool stack = dit_stack_ok(cf, n, G);
+  int* derr = c.take<int>(64);
+  if (stack) {
+    // phase and tile counters of the layer kernel live in the shared counter
+    // array (every kernel leaves its counters at zero); slice partials in the
+    // split-K scratch
+    const int nclr = ds_counter_words(D);
+    c.need_tiles = std::max(c.need_tiles, (size_t)nclr);
+    c.need_part = std::max(c.need_part, (size_t)(cf.mlp / D) * (D / 16) * 256);
+    c.label = "dit.clear";
+    unsigned z = 0;
+    VLA_TRY(launch(c, k_fill_ref(), dim3((nclr + 255) / 256), dim3(256), 0, {arg(c.cnt_tile), arg(z), arg(nclr)}));
+    int one = 1;
+    VLA_TRY(launch(c, k_fill_ref(), dim3(1), dim3(256), 0, {arg(derr), arg(z), arg(one)}));
+  }
 
   {  // phi(t_k) -> Linear -> SiLU
     c.label = "dit.time_fc1";
@@ -540,11 +576,30 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     c.label = "dit.in_proj";
     VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, {arg(t)}));
   }
+  KernelRef lk{};
+  if (stack && !dit_layer_lookup(wt, D, &lk)) return fail(VLA_ERR_UNSUPPORTED, "dit: no layer kernel for wdtype %d", wt);
+  if (stack && !c.plan && lk.smem > 64 * 1024) VLA_TRY(allow_smem(lk));
   for (int k = 0; k < K; k++) {
     for (int l = 0; l < L; l++) {
       const vla_dit_layer& w = d.layers[l];
       const float* m = mod ? mod + (size_t)k * mod_w + (size_t)l * 9 * D : nullptr;
       auto mv = [&](int j) { return m ? m + (size_t)j * D : nullptr; };
+      if (stack) {  // the whole layer in one persistent launch
+        c.label = "dit.layer";
+        DitLayerArgs a{};
+        a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
+        a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
+        a.x = x; a.qkv = qkv; a.q = q; a.ao = ao; a.h = h;
+        a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.cv = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldc = L * 2 * D;
+        a.mod = m;
+        const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
+        const float* ss[6] = {w.s_qkv, w.s_o, w.s_cq, w.s_co, w.s_up, w.s_down};
+        const float* bs[6] = {w.b_qkv, w.b_o, w.b_cq, w.b_co, w.b_up, w.b_down};
+        for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = wt == VLA_FP8_E4M3 ? ss[i] : nullptr; a.b[i] = bs[i]; }
+        a.part = c.part; a.cnt = c.cnt_tile; a.err = derr;
+        VLA_TRY(launch(c, lk.fn, dim3(G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
+        continue;
+      }
       {  // adaLN(LN) -> self-attn QKV
       c.label = "dit.sa_qkv";
         GemmArgs a = gargs();
@@ -623,7 +678,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     {  // velocity head + Euler update (+ input projection for the next step)
       TailArgs t{};
       t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
-      t.x = x; t.rs = xs.rs;
+      t.x = x;
       t.shift = fmod ? fmod + (size_t)k * 2 * D : nullptr;
       t.scale = fmod ? fmod + (size_t)k * 2 * D + D : nullptr;
       t.w_out = d.w_out; t.s_out = d.s_out; t.b_out = d.b_out;

@@ -1,0 +1,597 @@
+// One DiT layer of the flow sampler's action expert as a single persistent
+// kernel, for action chunks of at most 16 rows.
+//
+// Page "AI Infra如何优化VLA - 模型推理性能提升技术拆解" (section 整体方案 and
+// the CUDA Graph section): the action expert is memory-bound and was launch-
+// bound before graphs. At 16 rows every GEMM of a layer is a weight stream of
+// 3-13 MB, far too little to hide a kernel's launch, argument fetch, first
+// load latency and tail; here the eight steps of a layer run in one launch:
+//
+//   0 QKV    u = LN(x)(1 + scale_sa) + shift_sa;  qkv = u Wqkv^T + b
+//   1 SAATT  per head: ao = softmax(q k^T / sqrt(d)) v     (no mask)
+//   2 SAO    x += gate_sa * (ao Wo^T + b)
+//   3 CAQ    u = LN(x)(1 + scale_ca) + shift_ca;  q = u Wcq^T + b
+//   4 CAATT  per head: ao = softmax(q Kc^T / sqrt(d)) Vc    (context K/V)
+//   5 CAO    x += gate_ca * (ao Wco^T + b)
+//   6 UP     u = LN(x)(1 + scale_mlp) + shift_mlp;  h = GELU(u W1^T + b1)
+//   7 DOWN   x += gate_mlp * (h W2^T + b2)
+//
+// Work units: 16 output columns x D input columns of one GEMM (DOWN is split
+// into mlp / D slices of D columns, summed in a fixed order by the last slice
+// of each tile), or one attention head. Unit u of phase p belongs to
+// workgroup (u + base_p) mod G, so a workgroup knows its units in advance and
+// streams their weights into registers before it waits for the previous
+// phase: the HBM latency of the next weights overlaps the current phase.
+// A phase is complete when its counter reaches the number of units (tiles
+// for DOWN). Producers write with device-coherent (sc1) stores, wait for
+// them, then count; consumers poll the counter and read with sc1 loads, so
+// the XCDs' private L2s need no write-back or invalidate. Every wait is
+// bounded: on time-out the workgroup records an error, poisons its outputs
+// with NaN and leaves, so a fault can never hang the device. The workgroup
+// that completes the last DOWN tile resets the counters for the next launch.
+//
+// Each LayerNorm is computed by every workgroup that needs it, from the fp32
+// residual stream staged in LDS (two-pass mean / variance), so no statistics
+// travel between workgroups.
+#pragma once
+#include "common.h"
+
+namespace vla {
+
+enum DitPhase { DP_QKV = 0, DP_SAATT, DP_SAO, DP_CAQ, DP_CAATT, DP_CAO, DP_UP, DP_DOWN, DP_N };
+
+constexpr int DS_THREADS = 256;
+constexpr int DS_KSW = 10;        // 32-wide k-steps per wave per unit: D <= 4 * 10 * 32
+constexpr int DS_MAXU = 2;        // GEMM units per workgroup per phase (the kernel unrolls two)
+// A workgroup's weight registers hold DS_MAXU units of D columns.
+constexpr int DS_WSLOTS = DS_MAXU * DS_KSW;
+constexpr int DS_DP = 96;         // head dim padded for the attention MFMAs
+constexpr int DS_KB = 32;         // keys per attention block
+constexpr unsigned DS_SPIN = 1u << 17;   // polls before a wait gives up (a healthy wait is microseconds)
+// Phase counters: phases before DOWN count into DS_NC slots 256 bytes apart
+// (workgroup w adds to slot w % DS_NC), so arrivals do not serialise on one
+// address; DOWN (few arrivals) uses one counter, whose last arrival resets
+// all of them. Tile counters of the DOWN slices follow.
+constexpr int DS_NC = 16, DS_CSTRIDE = 64;
+constexpr int DS_TILE0 = DP_N * DS_NC * DS_CSTRIDE;
+__host__ __device__ constexpr int ds_counter_words(int D) { return DS_TILE0 + D / 16; }
+
+struct DitLayerArgs {
+  int n, D, H, hd, mlp, C;        // action rows (<= 16), width, heads, head dim, MLP width, context tokens
+  float eps, scale_log2;          // LayerNorm epsilon; log2(e) / sqrt(hd)
+  float* x;                       // [n, D] residual stream (fp32)
+  uint16_t* qkv;                  // [n, 3D] bf16
+  uint16_t* q;                    // [n, D] cross-attention query
+  uint16_t* ao;                   // [n, D] attention output
+  uint16_t* h;                    // [n, mlp] GELU output
+  const uint16_t* ck;             // this layer's context keys, row pitch ldc
+  const uint16_t* cv;             // this layer's context values
+  int ldc;
+  const float* mod;               // [9][D] modulation of this layer and step
+  const void* w[6];               // qkv, o, cq, co, up, down: [N, K] row-major
+  const float* s[6];              // per-row fp8 scales (NULL for bf16)
+  const float* b[6];              // biases
+  float* part;                    // DOWN slice partials [slices][D/16][256]
+  unsigned* cnt;                  // ds_counter_words(D) counters (zero between launches)
+  int* err;                       // set to 1 when a wait times out
+};
+
+__device__ __forceinline__ void st_sc1_f32(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// base must be the same for the whole wave (a buffer resource is uniform)
+__device__ __forceinline__ void st_sc1_u16(brsrc base, uint32_t idx, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, base, idx * 2u, 0, CP_SC1);
+}
+
+// ---------------------------------------------------------------- phase geometry
+__device__ __forceinline__ int ds_units(const DitLayerArgs& a, int ph) {
+  switch (ph) {
+    case DP_QKV: return 3 * a.D / 16;
+    case DP_SAATT: case DP_CAATT: return a.H;
+    case DP_SAO: case DP_CAQ: case DP_CAO: return a.D / 16;
+    case DP_UP: return a.mlp / 16;
+    default: return (a.D / 16) * (a.mlp / a.D);
+  }
+}
+// value of the phase counter once the phase is complete
+__device__ __forceinline__ int ds_target(const DitLayerArgs& a, int ph) { return ph == DP_DOWN ? a.D / 16 : ds_units(a, ph); }
+__device__ __forceinline__ int ds_base(const DitLayerArgs& a, int ph) {
+  int b = 0;
+  for (int q = 0; q < ph; q++) b += ds_units(a, q);
+  return b;
+}
+
+// Wait until the DS_NC slots of a phase counter sum to target (wave 0
+// polls, one slot per lane; the workgroup follows). False after DS_SPIN polls.
+__device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, int* sflag) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    unsigned spins = 0;
+    bool ok = true;
+    while (true) {
+      unsigned v = lane < DS_NC ? __hip_atomic_load(slots + lane * DS_CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+      if (v >= target) break;                      // uniform: every lane holds the sum
+      if (++spins >= DS_SPIN) { ok = false; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) sflag[0] = ok;
+  }
+  __syncthreads();
+  return sflag[0] != 0;
+}
+
+// ---------------------------------------------------------------- weight units
+template <typename WT> struct DsW;
+template <> struct DsW<uint16_t> {
+  using raw = uint4;
+  static constexpr int ESZ = 2;
+  __device__ static raw load(brsrc r, uint32_t off) { return bload16<CP_NT>(r, off); }
+  __device__ static FragBF16 frag(raw v) { FragBF16 f; f.v = __builtin_bit_cast(bf16x8, v); return f; }
+};
+template <> struct DsW<uint8_t> {
+  using raw = uint2;
+  static constexpr int ESZ = 1;
+  __device__ static raw load(brsrc r, uint32_t off) { return bload8<CP_NT>(r, off); }
+  __device__ static FragBF16 frag(raw v) { return fp8x8_to_frag(v); }
+};
+
+struct DsUnit {
+  int wi;        // weight index (0..5)
+  int N, K;      // output width, row length of W (= k extent of the whole GEMM)
+  int n0, k0;    // first output column, first k of this unit
+  int kw;        // k extent of the unit (D)
+};
+
+__device__ __forceinline__ DsUnit ds_unit(const DitLayerArgs& a, int ph, int u) {
+  DsUnit d;
+  d.n0 = 16 * u; d.k0 = 0; d.K = a.D; d.kw = a.D;
+  switch (ph) {
+    case DP_QKV: d.wi = 0; d.N = 3 * a.D; break;
+    case DP_SAO: d.wi = 1; d.N = a.D; break;
+    case DP_CAQ: d.wi = 2; d.N = a.D; break;
+    case DP_CAO: d.wi = 3; d.N = a.D; break;
+    case DP_UP: d.wi = 4; d.N = a.mlp; break;
+    default: {   // DOWN: tile u % (D/16), slice u / (D/16) of D columns
+      const int nt = a.D / 16;
+      d.wi = 5; d.N = a.D; d.K = a.mlp;
+      d.n0 = 16 * (u % nt); d.k0 = (u / nt) * a.D;
+    }
+  }
+  return d;
+}
+
+// The wave's k-steps of a unit: steps s = wave + 4 i (i < NS) of kw / 32,
+// into register slots OFF .. OFF + NS - 1.
+template <typename WT, int OFF, int NS>
+__device__ __forceinline__ void ds_load_unit(const DitLayerArgs& a, const DsUnit& d, typename DsW<WT>::raw (&r)[DS_WSLOTS]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const brsrc wr = make_brsrc(a.w[d.wi]);
+  const int col = d.n0 + (lane & 15);
+  const int ksteps = d.kw / 32;
+#pragma unroll
+  for (int i = 0; i < NS; i++) {
+    int s = wave + 4 * i;
+    int k = d.k0 + s * 32 + (lane >> 4) * 8;
+    bool ok = s < ksteps && col < d.N;
+    r[OFF + i] = DsW<WT>::load(wr, ok ? ((uint32_t)col * d.K + k) * DsW<WT>::ESZ : BUF_OOB);
+  }
+}
+
+// 16 x 16 tile of one unit: A [16][kw] bf16 in LDS (pitch apitch), weights in
+// register slots OFF ..; the wave's partial sum over its k-steps.
+template <typename WT, int OFF, int NS>
+__device__ __forceinline__ f32x4 ds_mma(const char* rA, int apitch, int ksteps, const typename DsW<WT>::raw (&w)[DS_WSLOTS]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NS; i++) {
+    int s = wave + 4 * i;
+    if (s < ksteps) {
+      FragBF16 af;
+      af.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rA + (lane & 15) * apitch + (s * 32 + (lane >> 4) * 8) * 2));
+      mma32(acc, af, DsW<WT>::frag(w[OFF + i]));
+    }
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------- attention of one head (<= 16 queries)
+// The four waves take interleaved blocks of 32 keys (S^T = K Q^T per block,
+// online softmax per lane, O^T = V^T P^T from registers), then their partial
+// (max, sum, O) are combined in LDS. Q and the outputs are coherent (sc1);
+// K / V are read coherently when `kv_sc1`.
+__device__ __forceinline__ FragBF16 ds_gfrag(brsrc r, uint32_t off, bool sc1) {
+  uint4 v = sc1 ? bload16<CP_SC1>(r, off) : bload16(r, off);
+  FragBF16 f; f.v = __builtin_bit_cast(bf16x8, v); return f;
+}
+
+constexpr int DS_SE = DS_KB * (DS_DP / 8) / 64;   // 16-byte K (and V) groups per lane per block
+
+// Requests block `blk` (of nblk) of K and V for this wave: lane-strided
+// 16-byte groups, zeros beyond the keys or the head dim.
+__device__ __forceinline__ void ds_att_load(brsrc kr, brsrc vr, bool sc1, int blk, int nblk, int nk, int ldkv, int hd,
+                                            uint4 (&kv)[DS_SE], uint4 (&vv)[DS_SE]) {
+  const int lane = threadIdx.x & 63;
+  const int kb = blk * DS_KB;
+#pragma unroll
+  for (int i = 0; i < DS_SE; i++) {
+    int e = lane + i * 64;
+    int key = e / (DS_DP / 8), d8 = (e % (DS_DP / 8)) * 8;
+    int j = kb + key;
+    bool ok = blk < nblk && j < nk && d8 < hd;
+    uint32_t off = ok ? ((uint32_t)j * ldkv + d8) * 2u : BUF_OOB;
+    kv[i] = sc1 ? bload16<CP_SC1>(kr, off) : bload16(kr, off);
+    vv[i] = sc1 ? bload16<CP_SC1>(vr, off) : bload16(vr, off);
+  }
+}
+
+// kv / vv hold this wave's first block when `have0` (requested before the
+// caller's wait); each later round is requested before the current one is
+// computed.
+__device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const uint16_t* Kp, const uint16_t* Vp, int ldkv,
+                                             bool kv_sc1, uint16_t* O, int ldo, int nq, int nk, int hd, float scale_log2,
+                                             char* lds, char* lds_o, uint4 (&kv)[DS_SE], uint4 (&vv)[DS_SE], bool have0) {
+  constexpr int KPITCH = DS_DP * 2 + 16, VPITCH = DS_KB * 2 + 16;
+  constexpr int WSTAGE = DS_KB * KPITCH + DS_DP * VPITCH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qn = lane & 15, grp = lane >> 4;
+  char* sK = lds + wave * WSTAGE;
+  char* sV = sK + DS_KB * KPITCH;
+  const brsrc qr = make_brsrc(Q), kr = make_brsrc(Kp), vr = make_brsrc(Vp), orr = make_brsrc(O);
+  const int nblk = (nk + DS_KB - 1) / DS_KB;
+
+  FragBF16 qf[DS_DP / 32];
+#pragma unroll
+  for (int ds = 0; ds < DS_DP / 32; ds++) {
+    int d = ds * 32 + grp * 8;
+    qf[ds] = ds_gfrag(qr, (qn < nq && d < hd) ? ((uint32_t)qn * ldq + d) * 2u : BUF_OOB, true);
+  }
+  if (!have0) ds_att_load(kr, vr, kv_sc1, wave, nblk, nk, ldkv, hd, kv, vv);
+  f32x4 oacc[DS_DP / 16];
+#pragma unroll
+  for (int i = 0; i < DS_DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  for (int r0 = 0; r0 < nblk; r0 += 4) {
+    const int blk = r0 + wave;
+    const int kb = blk * DS_KB;
+    __syncthreads();
+    // K [32][DP] and V^T [DP][32] of this wave's block
+#pragma unroll
+    for (int i = 0; i < DS_SE; i++) {
+      int e = lane + i * 64;
+      int key = e / (DS_DP / 8), d8 = (e % (DS_DP / 8)) * 8;
+      *reinterpret_cast<uint4*>(sK + key * KPITCH + d8 * 2) = kv[i];
+      const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv[i]);
+#pragma unroll
+      for (int t = 0; t < 8; t++) *reinterpret_cast<uint16_t*>(sV + (d8 + t) * VPITCH + key * 2) = ve[t];
+    }
+    __syncthreads();
+    if (r0 + 4 < nblk) ds_att_load(kr, vr, kv_sc1, blk + 4, nblk, nk, ldkv, hd, kv, vv);
+    if (blk < nblk) {
+      f32x4 s[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++) {
+        s[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS_DP / 32; ds++) {
+          FragBF16 kf;
+          kf.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * 2));
+          mma32(s[hb], kf, qf[ds]);
+        }
+      }
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          int j = kb + hb * 16 + grp * 4 + i;
+          float v = j < nk ? s[hb][i] * scale_log2 : -INFINITY;
+          s[hb][i] = v;
+          bmax = fmaxf(bmax, v);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, WAVE));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, WAVE));
+      float mnew = fmaxf(mrun, bmax);
+      float corr = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      float pv[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        pv[i] = (mnew == -INFINITY) ? 0.f : exp2f(s[0][i] - mnew);
+        pv[4 + i] = (mnew == -INFINITY) ? 0.f : exp2f(s[1][i] - mnew);
+        psum += pv[i] + pv[4 + i];
+      }
+      lrun = lrun * corr + psum;
+      mrun = mnew;
+      FragBF16 pf;
+      frag_from_floats(pf, pv);
+#pragma unroll
+      for (int db = 0; db < DS_DP / 16; db++) {
+        oacc[db] = oacc[db] * corr;
+        const char* vrow = sV + (db * 16 + qn) * VPITCH;
+        uint2 lo = *reinterpret_cast<const uint2*>(vrow + (grp * 4) * 2);
+        uint2 hi = *reinterpret_cast<const uint2*>(vrow + (16 + grp * 4) * 2);
+        FragBF16 vf;
+        vf.v = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        mma32(oacc[db], vf, pf);
+      }
+    }
+  }
+  // combine the four waves: per query (max, sum) and O^T partials in LDS
+  float lsum = lrun;
+  lsum += __shfl_xor(lsum, 16, WAVE);
+  lsum += __shfl_xor(lsum, 32, WAVE);
+  float* sml = reinterpret_cast<float*>(lds_o);                  // [4][16][2]
+  float* so = sml + 4 * 16 * 2;                                  // [4][16][DP]
+  __syncthreads();
+  if (grp == 0) { sml[(wave * 16 + qn) * 2] = mrun; sml[(wave * 16 + qn) * 2 + 1] = lsum; }
+#pragma unroll
+  for (int db = 0; db < DS_DP / 16; db++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) so[(wave * 16 + qn) * DS_DP + db * 16 + grp * 4 + i] = oacc[db][i];
+  __syncthreads();
+  for (int e = tid; e < 16 * DS_DP / 4; e += DS_THREADS) {
+    const int q = e / (DS_DP / 4), d = (e % (DS_DP / 4)) * 4;
+    if (q >= nq || d >= hd) continue;
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; w++) { mw[w] = sml[(w * 16 + q) * 2]; M = fmaxf(M, mw[w]); }
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      float f = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
+      L += f * sml[(w * 16 + q) * 2 + 1];
+      float4 o = *reinterpret_cast<const float4*>(so + (w * 16 + q) * DS_DP + d);
+      acc.x += f * o.x; acc.y += f * o.y; acc.z += f * o.z; acc.w += f * o.w;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 pk;
+    pk.x = pack_bf2(acc.x * inv, acc.y * inv);
+    pk.y = pack_bf2(acc.z * inv, acc.w * inv);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(q * ldo + d) * 2u, 0, CP_SC1);
+  }
+}
+
+// ---------------------------------------------------------------- the layer kernel
+// LDS: [region X: attention staging or a norm's shift / scale] [region A:
+// bf16 A operand (16 x D) or attention partials]
+// [4 x 256 fp32 wave sums] [flags]
+__host__ __device__ constexpr int ds_region_x(int) { return 4 * (DS_KB * (DS_DP * 2 + 16) + DS_DP * (DS_KB * 2 + 16)); }
+__host__ __device__ constexpr int ds_region_a(int D) {
+  return (16 * (2 * D + 16) > (4 * 16 * 2 + 4 * 16 * DS_DP) * 4) ? 16 * (2 * D + 16) : (4 * 16 * 2 + 4 * 16 * DS_DP) * 4;
+}
+__host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_x(D) + ds_region_a(D) + 4 * 256 * 4 + 64; }
+
+template <typename WT>
+__global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
+  using WR = typename DsW<WT>::raw;
+  extern __shared__ __align__(16) char smem[];
+  char* rX = smem;
+  char* rA = smem + ds_region_x(a.D);
+  float* red = reinterpret_cast<float*>(rA + ds_region_a(a.D));
+  int* sflag = reinterpret_cast<int*>(red + 4 * 256);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wg = blockIdx.x, G = gridDim.x;
+  const int D = a.D, n = a.n;
+  const int APITCH = D * 2 + 16;
+  const int ntile = D / 16;
+  int finished_tiles = 0;        // DOWN tiles this workgroup completed
+
+  // a failed earlier launch of this run: poison the stream and leave at once
+  if (tid == 0) sflag[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sflag[0]) {
+    for (int e = wg * DS_THREADS + tid; e < n * D; e += G * DS_THREADS) st_sc1_f32(a.x + e, __builtin_nanf(""));
+    return;
+  }
+
+  for (int ph = 0; ph < DP_N; ph++) {
+    const int U = ds_units(a, ph);
+    const int first = ((wg - ds_base(a, ph)) % G + G) % G;
+    if (first >= U) continue;                          // no work in this phase
+    const int nu = min(DS_MAXU, (U - first + G - 1) / G);
+    const bool is_att = ph == DP_SAATT || ph == DP_CAATT;
+
+    const bool norm = ph == DP_QKV || ph == DP_CAQ || ph == DP_UP;
+    // Everything that does not depend on the previous phase is requested
+    // before its wait: the first context K / V block of a cross-attention
+    // head, a LayerNorm's shift / scale, the weights of the GEMM units. Each
+    // kind of phase keeps its own registers across its own wait.
+    auto wait_prev = [&]() -> bool {
+      if (ph == 0 || ds_wait(a.cnt + (ph - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, ph - 1), sflag)) return true;
+      // time-out: record it, poison this workgroup's outputs
+      if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(a.x + e, __builtin_nanf(""));
+      return false;
+    };
+    constexpr int MS = (2 * 4 * DS_KSW * 32 / 4 + DS_THREADS - 1) / DS_THREADS;   // float4 per thread
+
+    if (is_att) {
+      uint4 pkv[DS_SE], pvv[DS_SE];
+      const bool pre_kv = ph == DP_CAATT;
+      if (pre_kv)
+        ds_att_load(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), false, wave,
+                    (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, pkv, pvv);
+      if (!wait_prev()) return;
+      // ---- one head per unit
+      for (int j = 0; j < nu; j++) {
+        const int hh = first + j * G;
+        if (ph == DP_SAATT)
+          ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D, true,
+                       a.ao + hh * a.hd, D, n, n, a.hd, a.scale_log2, rX, rA, pkv, pvv, false);
+        else
+          ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc, false,
+                       a.ao + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rX, rA, pkv, pvv, pre_kv && j == 0);
+      }
+    } else {
+      const int mi = ph == DP_QKV ? 0 : ph == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
+      uint4 pmod[MS];
+      if (norm) {
+        const brsrc mr = make_brsrc(a.mod + (size_t)mi * D);
+#pragma unroll
+        for (int i = 0; i < MS; i++) {
+          int e4 = tid + i * DS_THREADS;
+          pmod[i] = bload16(mr, e4 < 2 * D / 4 ? (uint32_t)e4 * 16u : BUF_OOB);
+        }
+      }
+      WR wreg[DS_WSLOTS];
+      ds_load_unit<WT, 0, DS_KSW>(a, ds_unit(a, ph, first), wreg);
+      if (nu > 1) ds_load_unit<WT, DS_KSW, DS_KSW>(a, ds_unit(a, ph, first + G), wreg);
+      if (!wait_prev()) return;
+      // ---- the A operand [16][D] (bf16) in region A
+      if (norm) {
+        // thread (row r = tid / 16, lane j of the row) holds float4 columns
+        // 4 (j + 16 i), i < D / 64, of x in registers: two-pass mean /
+        // variance over the 16 lanes of the row, then u in bf16 into LDS
+        constexpr int XS = 4 * DS_KSW * 32 / 64;          // float4 per thread at the largest D
+        const int r = tid >> 4, j = tid & 15;
+        const brsrc xr = make_brsrc(a.x);
+        float4 xv[XS];
+#pragma unroll
+        for (int i = 0; i < XS; i++) {
+          int c = 4 * (j + 16 * i);
+          xv[i] = as_f4(bload16<CP_SC1>(xr, (c < D && r < n) ? ((uint32_t)r * D + c) * 4u : BUF_OOB));
+        }
+        // shift | scale (prefetched) into region X
+        float* smod = reinterpret_cast<float*>(rX);
+#pragma unroll
+        for (int i = 0; i < MS; i++) {
+          int e4 = tid + i * DS_THREADS;
+          if (e4 < 2 * D / 4) *reinterpret_cast<uint4*>(smod + e4 * 4) = pmod[i];
+        }
+        __syncthreads();
+        float s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < XS; i++) s1 += (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) s1 += __shfl_xor(s1, o, WAVE);
+        const float mean = s1 / (float)D;
+        float s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < XS; i++) {
+          if (4 * (j + 16 * i) < D) {
+            float d0 = xv[i].x - mean, d1 = xv[i].y - mean, d2 = xv[i].z - mean, d3 = xv[i].w - mean;
+            s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+          }
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o, WAVE);
+        const float rstd = rsqrtf(s2 / (float)D + a.eps);
+#pragma unroll
+        for (int i = 0; i < XS; i++) {
+          int c = 4 * (j + 16 * i);
+          if (c < D) {
+            const float4 shv = *reinterpret_cast<const float4*>(smod + c);
+            const float4 scv = *reinterpret_cast<const float4*>(smod + D + c);
+            float4 u;
+            u.x = r < n ? (xv[i].x - mean) * rstd * (1.f + scv.x) + shv.x : 0.f;
+            u.y = r < n ? (xv[i].y - mean) * rstd * (1.f + scv.y) + shv.y : 0.f;
+            u.z = r < n ? (xv[i].z - mean) * rstd * (1.f + scv.z) + shv.z : 0.f;
+            u.w = r < n ? (xv[i].w - mean) * rstd * (1.f + scv.w) + shv.w : 0.f;
+            uint2 pk;
+            pk.x = pack_bf2(u.x, u.y);
+            pk.y = pack_bf2(u.z, u.w);
+            *reinterpret_cast<uint2*>(rA + r * APITCH + c * 2) = pk;
+          }
+        }
+      }
+      int staged_k0 = -1;
+      auto unit = [&](int j) {
+        const DsUnit d = ds_unit(a, ph, first + j * G);
+        const int apitch = d.kw * 2 + 16;
+        if (!norm && d.k0 != staged_k0) {
+          // bf16 activations: ao (SAO, CAO) or the unit's slice of h (DOWN)
+          const uint16_t* src = ph == DP_DOWN ? a.h : a.ao;
+          const int lds = ph == DP_DOWN ? a.mlp : D;
+          const brsrc sr = make_brsrc(src);
+          constexpr int AS = 16 * 4 * DS_KSW * 32 / 8 / DS_THREADS;   // 16-byte groups per thread at the largest D
+          uint4 av[AS];
+#pragma unroll
+          for (int i = 0; i < AS; i++) {
+            int e8 = tid + i * DS_THREADS;
+            int r = (e8 * 8) / d.kw, c = (e8 * 8) % d.kw;
+            av[i] = bload16<CP_SC1>(sr, (e8 < 16 * d.kw / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
+          }
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < AS; i++) {
+            int e8 = tid + i * DS_THREADS;
+            int r = (e8 * 8) / d.kw, c = (e8 * 8) % d.kw;
+            if (e8 < 16 * d.kw / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
+          }
+          staged_k0 = d.k0;
+        }
+        __syncthreads();
+        // ---- 16 x 16 tile: wave w covers k-steps w, w + 4, ...
+        const int ksteps = d.kw / 32;
+        f32x4 acc = j == 0 ? ds_mma<WT, 0, DS_KSW>(rA, apitch, ksteps, wreg) : ds_mma<WT, DS_KSW, DS_KSW>(rA, apitch, ksteps, wreg);
+#pragma unroll
+        for (int i = 0; i < 4; i++) red[wave * 256 + ((lane >> 4) * 4 + i) * 16 + (lane & 15)] = acc[i];
+        __syncthreads();
+        // ---- epilogue: thread = (row tid / 16, column tid % 16)
+        const int r = tid >> 4, cc = tid & 15, col = d.n0 + cc;
+        float v = red[tid] + red[256 + tid] + red[512 + tid] + red[768 + tid];
+        const float* ws = a.s[d.wi];
+        if (ws) v *= ws[col];
+        if (ph == DP_DOWN) {
+          // publish this slice's partial; the tile's last slice sums them in slice order
+          const int tile = d.n0 / 16, slice = d.k0 / d.kw, nsl = a.mlp / d.kw;
+          st_sc1_f32(a.part + ((size_t)slice * ntile + tile) * 256 + tid, v);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (tid == 0) {
+            unsigned old = __hip_atomic_fetch_add(a.cnt + DS_TILE0 + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sflag[1] = old == (unsigned)(nsl - 1);
+          }
+          __syncthreads();
+          if (!sflag[1]) return;
+          const brsrc pr = make_brsrc(a.part);
+          float sum = 0.f;
+          for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
+          v = sum;
+          if (tid == 0) a.cnt[DS_TILE0 + tile] = 0u;
+          finished_tiles++;
+        }
+        v += a.b[d.wi][col];
+        if (ph == DP_QKV || ph == DP_CAQ || ph == DP_UP) {
+          if (ph == DP_UP) v = gelu_erf(v);
+          uint16_t* out = ph == DP_QKV ? a.qkv : ph == DP_CAQ ? a.q : a.h;
+          const int ldo = ph == DP_QKV ? 3 * D : ph == DP_CAQ ? D : a.mlp;
+          if (r < n && col < d.N) st_sc1_u16(make_brsrc(out), (uint32_t)(r * ldo + col), f2bf(v));
+        } else {
+          // gated residual: x += gate * v
+          const int gi = ph == DP_SAO ? 2 : ph == DP_CAO ? 5 : 8;
+          if (r < n) {
+            float* xp = a.x + (size_t)r * D + col;
+            float xo = bloadf<CP_SC1>(make_brsrc(a.x), (uint32_t)(r * D + col) * 4u);
+            st_sc1_f32(xp, xo + a.mod[(size_t)gi * D + col] * v);
+          }
+        }
+      };
+      unit(0);
+      if (nu > 1) unit(1);
+    }
+    // ---- count this phase's finished units once every store has completed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      sflag[1] = 0;
+      unsigned add = ph == DP_DOWN ? (unsigned)finished_tiles : (unsigned)nu;
+      if (add) {
+        unsigned* slot = a.cnt + ph * DS_NC * DS_CSTRIDE + (ph == DP_DOWN ? 0 : (wg % DS_NC) * DS_CSTRIDE);
+        unsigned old = __hip_atomic_fetch_add(slot, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the last DOWN tile: every unit of every phase is done and no
+        // workgroup polls any more, so the counters can be cleared
+        sflag[1] = ph == DP_DOWN && old + add == (unsigned)ds_target(a, DP_DOWN);
+      }
+    }
+    __syncthreads();
+    if (sflag[1] && tid < DP_N * DS_NC)
+      __hip_atomic_store(a.cnt + tid * DS_CSTRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace vla

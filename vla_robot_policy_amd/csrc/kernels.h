@@ -26,4 +26,7 @@ const void* k_rmsnorm_out_ref();
 const void* k_convert_rows_ref();
 bool euler_tail_lookup(int wt, KernelRef* out);
 
+// Persistent DiT layer kernel (wt 1 = bf16, 2 = fp8) for width D.
+bool dit_layer_lookup(int wt, int D, KernelRef* out);
+
 }  // namespace vla

@@ -71,15 +71,24 @@ __global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* arow = p.a_in + (size_t)m * p.A;
   if (p.w_out) {
-    __shared__ float2 snc;
-    if (wave == 0) {
-      float2 nc = norm_coeffs(row_moments_wave(p.rs, m), 0, p.eps);
-      if (lane == 0) snc = nc;
-    }
+    // LayerNorm of x_m: two-pass mean / variance over the row (this
+    // workgroup reads the whole row anyway)
+    const float* xr = p.x + (size_t)m * p.D;
+    float s1 = 0.f;
+    for (int d = tid; d < p.D; d += 256) s1 += xr[d];
+    s1 = wave_sum(s1);
+    if (lane == 0) red[wave] = s1;
     __syncthreads();
-    const float2 nc = snc;
+    const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)p.D;
+    float s2 = 0.f;
+    for (int d = tid; d < p.D; d += 256) { float dd = xr[d] - mean; s2 += dd * dd; }
+    s2 = wave_sum(s2);
+    if (lane == 0) red[4 + wave] = s2;
+    __syncthreads();
+    const float rstd = rsqrtf((red[4] + red[5] + red[6] + red[7]) / (float)p.D + p.eps);
+    __syncthreads();   // red is reused below
     for (int d = tid; d < p.D; d += 256)
-      su[d] = (p.x[(size_t)m * p.D + d] - nc.x) * nc.y * (1.f + p.scale[d]) + p.shift[d];
+      su[d] = (xr[d] - mean) * rstd * (1.f + p.scale[d]) + p.shift[d];
     __syncthreads();
     for (int a = wave; a < p.A; a += 4) {
       float acc = 0.f;

@@ -8,7 +8,7 @@ namespace vla {
 struct TailArgs {
   int n, D, A, K;             // action rows, DiT width, action dim, Euler steps
   // velocity head (skipped when w_out == NULL)
-  const float* x; RowStats rs; float eps;        // residual stream and its row moments
+  const float* x; float eps;                     // residual stream (its rows are normalised here)
   const float* shift; const float* scale;   // final modulation of this step [D] each
   const void* w_out; const float* s_out; const float* b_out;   // [A, D], per-row scale, [A]
   const float* a_in;          // current actions [n, A]
