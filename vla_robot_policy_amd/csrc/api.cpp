@@ -202,8 +202,9 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (wrows * a.ldw * wbytes >= (double)BUF_LIMIT) return fail(VLA_ERR_SHAPE, "gemm: weight matrix beyond 2 GiB");
   if (op.am != A_TIME && op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
-  if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32)))
-    return fail(VLA_ERR_UNSUPPORTED, "gemm: compensated activations need bf16 weights and a float source");
+  if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32 && op.am != A_BF16)))
+    return fail(VLA_ERR_UNSUPPORTED, "gemm: compensated activations need bf16 weights");
+  if (op.ac && op.am == A_BF16 && !a.a_lo && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: compensated bf16 source without its remainder plane");
   if (op.em == E_RESID) {
     if (!a.rs_out && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: residual epilogue without a row-moment output");
     if (a.n_tiles_n > (a.N + 15) / 16) return fail(VLA_ERR_SHAPE, "gemm: residual tiling finer than 16 columns");
@@ -288,6 +289,16 @@ vla_status stage_stream(Ctx& c, Stream& st, int M, int N, const void* src, int s
   return stage_rows(c, st.x, N, M, N, src, src_f32, N, r0, r1, st.part);
 }
 
+// Normalise M rows of x once, into bf16 (and the remainder plane when out_lo).
+vla_status norm_rows(Ctx& c, const float* x, int ldx, int M, int K, RowStats rs, int rms, float eps, const float* g,
+                     int g_plus_one, const float* bsh, uint16_t* out, uint16_t* out_lo, int ldo) {
+  if (K % 4 != 0 || ldx % 4 != 0 || ldo % 4 != 0) return fail(VLA_ERR_SHAPE, "norm: row length %d must be a multiple of 4", K);
+  NormArgs a{};
+  a.x = x; a.ldx = ldx; a.M = M; a.K = K; a.rs = rs; a.rms = rms; a.eps = eps;
+  a.g = g; a.g_plus_one = g_plus_one; a.bsh = bsh; a.out = out; a.out_lo = out_lo; a.ldo = ldo;
+  return launch(c, k_norm_rows_ref(), dim3(M), dim3(256), 0, {arg(a)});
+}
+
 vla_status convert_rows(Ctx& c, const float* x, int ldx, int M, int N, void* out, int ldo, int out_f32) {
   return launch(c, k_convert_rows_ref(), dim3((M + 3) / 4), dim3(256), 0,
                 {arg(x), arg(ldx), arg(M), arg(N), arg(out), arg(ldo), arg(out_f32)});
@@ -326,6 +337,9 @@ struct BackboneBufs {
   void* qkv;       // [S, Nqkv]
   void* ao;        // [S, q_dim]
   void* act;       // [S, I]
+  uint16_t* xn;    // [S, H] normalised rows (bf16 activations)
+  uint16_t* xn_lo; // [S, H] their remainder plane (compensated MLP)
+  uint16_t* act_lo;// [S, I] remainder plane of the SwiGLU output (compensated MLP)
 };
 
 // bf16 backbones carry the MLP's activations (the normalised input of gate/up
@@ -335,13 +349,19 @@ bool mlp_compensated(const vla_block_cfg& cfg) { return cfg.wdtype == VLA_BF16; 
 
 BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   size_t es = cfg.adtype == VLA_F32 ? 4 : 2;
-  size_t es_act = mlp_compensated(cfg) ? 4 : es;
+  const bool comp = mlp_compensated(cfg);
   int nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim;
   BackboneBufs b;
   b.xs = take_stream(c, S, cfg.hidden);
   b.qkv = c.take<char>((size_t)S * nqkv * es);
   b.ao = c.take<char>((size_t)S * cfg.n_q_heads * cfg.head_dim * es);
-  b.act = c.take<char>((size_t)S * cfg.intermediate * es_act);
+  b.act = c.take<char>((size_t)S * cfg.intermediate * es);
+  b.xn = b.xn_lo = b.act_lo = nullptr;
+  if (cfg.adtype != VLA_F32) b.xn = c.take<uint16_t>((size_t)S * cfg.hidden);
+  if (comp) {
+    b.xn_lo = c.take<uint16_t>((size_t)S * cfg.hidden);
+    b.act_lo = c.take<uint16_t>((size_t)S * cfg.intermediate);
+  }
   return b;
 }
 
@@ -356,14 +376,19 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   for (int l = 0; l < n_layers; l++) {
     const vla_block_weights& w = layers[l];
     {  // RMSNorm -> fused QKV -> RoPE
+      if (!f32) {
+        c.label = "llm.attn_norm";
+        VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, 0, nullptr, b.xn, nullptr, H));
+      }
     c.label = "llm.qkv";
       GemmArgs a = gargs();
       a.M = S; a.N = nqkv; a.K = H;
-      a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm;
+      if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm; }
+      else { a.a = b.xn; a.lda = H; }
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
       a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32;
       a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_base = cfg.rope_base;
-      VLA_TRY(gemm(c, a, {wt, A_NORM, E_ROPE}));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : A_BF16, E_ROPE}));
     }
     {  // causal GQA attention
     c.label = "llm.attn";
@@ -385,22 +410,27 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}, &b.xs.rs));
     }
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
+      if (!f32) {
+        c.label = "llm.mlp_norm";
+        VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, 0, nullptr, b.xn, b.xn_lo, H));
+      }
     c.label = "llm.gate_up";
       GemmArgs a = gargs();
       a.M = S; a.N = I; a.K = H;
-      a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm;
+      if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm; }
+      else { a.a = b.xn; a.a_lo = b.xn_lo; a.lda = H; }
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
-      a.c = b.act; a.ldc = I; a.c_f32 = f32 || comp;
-      VLA_TRY(gemm(c, a, {wt, A_NORM, E_SWIGLU, comp}));
+      a.c = b.act; a.c_lo = b.act_lo; a.ldc = I; a.c_f32 = f32;
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : A_BF16, E_SWIGLU, comp}));
     }
     {  // down + residual (+ row statistics)
     c.label = "llm.down";
       GemmArgs a = gargs();
       a.M = S; a.N = H; a.K = I;
-      a.a = b.act; a.lda = I;
+      a.a = b.act; a.a_lo = b.act_lo; a.lda = I;
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      VLA_TRY(gemm(c, a, {wt, (f32 || comp) ? A_F32 : A_BF16, E_RESID, comp}, &b.xs.rs));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID, comp}, &b.xs.rs));
     }
   }
   return VLA_OK;
@@ -726,6 +756,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
   uint16_t* ao = c.take<uint16_t>((size_t)S * D);
   uint16_t* h = c.take<uint16_t>((size_t)S * cf.mlp);
   uint16_t* m1 = c.take<uint16_t>((size_t)Mm * MD);
+  uint16_t* zn = c.take<uint16_t>((size_t)S * D);      // LayerNorm-ed rows (bf16)
   {  // patchify -> Linear + bias + position table (+ row statistics)
     c.label = "vit.patch_embed";
     GemmArgs a = gargs();
@@ -738,13 +769,15 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
   for (int l = 0; l < cf.layers; l++) {
     const vla_vit_layer& w = v.layers[l];
     {
+      c.label = "vit.ln1";
+      VLA_TRY(norm_rows(c, z, D, S, D, zst.rs, 0, cf.eps, w.ln1_g, 0, w.ln1_b, zn, nullptr, D));
       c.label = "vit.qkv";
       GemmArgs a = gargs();
       a.M = S; a.N = 3 * D; a.K = D;
-      a.a = z; a.lda = D; a.rs = zst.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln1_g; a.bsh = w.ln1_b;
+      a.a = zn; a.lda = D;
       a.w = w.w_qkv; a.ldw = D; a.bias = w.b_qkv;
       a.c = qkv; a.ldc = 3 * D;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_NORM, E_STORE}));
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE}));
     }
     {
       c.label = "vit.attn";
@@ -776,13 +809,15 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
       VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}, &zst.rs));
     }
     {
+      c.label = "vit.ln2";
+      VLA_TRY(norm_rows(c, z, D, S, D, zst.rs, 0, cf.eps, w.ln2_g, 0, w.ln2_b, zn, nullptr, D));
       c.label = "vit.up";
       GemmArgs a = gargs();
       a.M = S; a.N = cf.mlp; a.K = D;
-      a.a = z; a.lda = D; a.rs = zst.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = w.ln2_g; a.bsh = w.ln2_b;
+      a.a = zn; a.lda = D;
       a.w = w.w_up; a.ldw = D; a.bias = w.b_up; a.act = ACT_GELU;
       a.c = h; a.ldc = cf.mlp;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_NORM, E_STORE}));
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE}));
     }
     {
       c.label = "vit.down";

@@ -16,7 +16,8 @@
 // Compensated activations (AC = 1): the bf16 A operand is carried as a pair
 // hi + lo (hi = bf16(a), lo = bf16(a - hi)) and both halves meet the same
 // weight fragment, so the product keeps ~16 significant bits of a at twice
-// the MFMA work and LDS traffic; the weights are read once either way.
+// the MFMA work and LDS traffic; the weights are read once either way. The
+// pair is formed from a float source, or read as two bf16 planes (a, a_lo).
 // Split-K partial tiles are reduced in a fixed order by the last workgroup
 // of each output tile (no float atomics), so results are bitwise
 // reproducible run to run.
@@ -34,6 +35,7 @@ struct GemmArgs {
   int M, N, K;
   // ---- A source
   const void* a;         // BF16/F32/NORM/MERGE: matrix [rows, lda]; PATCH: bf16 images
+  const void* a_lo;      // BF16 with compensation: remainder plane, same layout as a
   int lda;
   RowStats rs;           // NORM/MERGE: per-tile row moments of the source rows
   int norm_rms;          // 1: RMSNorm (no mean subtraction), 0: LayerNorm
@@ -53,6 +55,7 @@ struct GemmArgs {
   const float* bias;
   int act;
   void* c;
+  void* c_lo;            // STORE / SWIGLU in bf16: also the remainder plane bf16(v - hi) (NULL = none)
   int ldc;
   int c_f32;
   int q_cols, k_cols, head_dim, pos0; float rope_base;   // ROPE
@@ -173,12 +176,15 @@ struct GemmTile {
   static constexpr int TPR0 = THREADS / NROWST;
   static constexpr int TPR = TPR0 >= 64 ? 64 : TPR0 >= 32 ? 32 : TPR0 >= 16 ? 16 : TPR0 >= 8 ? 8 : TPR0 >= 4 ? 4 : TPR0 >= 2 ? 2 : 1;
   static_assert(THREADS % (BK / AG) == 0, "a thread's A columns must not change between its row groups");
-  static_assert(!AC || (sizeof(CT) == 2 && (AM == A_NORM || AM == A_F32)), "compensated A needs a float source and bf16 MFMA");
+  static_assert(!AC || (sizeof(CT) == 2 && (AM == A_NORM || AM == A_F32 || AM == A_BF16)), "compensated A needs bf16 MFMA");
 };
 
-// Raw A registers: bf16 sources keep 8 bf16 (copied to LDS as is), others 4 floats.
-template <int AM> struct ARaw { using type = float4; };
-template <> struct ARaw<A_BF16> { using type = uint4; };
+// Raw A registers: bf16 sources keep 8 bf16 (copied to LDS as is; with
+// compensation both planes), others 4 floats.
+struct U4x2 { uint4 h, l; };
+template <int AM, int AC> struct ARaw { using type = float4; };
+template <> struct ARaw<A_BF16, 0> { using type = uint4; };
+template <> struct ARaw<A_BF16, 1> { using type = U4x2; };
 
 // ---------------------------------------------------------------- kernel
 template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   using T = GemmTile<WT, CT, MB, WN, WK, NBW, AM, EM, UU, AC>;
   using WL = WLoad<WT>;
   using F = typename Frag<CT>::type;
-  using AR = typename ARaw<AM>::type;
+  using AR = typename ARaw<AM, AC>::type;
   constexpr int NT = T::THREADS, NW = T::NW;
   constexpr int BM = T::BM, BN = T::BN, BK = T::BK, U = T::U, GPT = T::GPT;
   constexpr int LROW = T::LROW, TPITCH = T::TPITCH;
@@ -335,7 +341,11 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       int r = ar0 + i * RS;
       int m = m0 + r;
       bool ok = r < BM && m < p.M && k < p.K;
-      if constexpr (AM == A_BF16) {
+      if constexpr (AM == A_BF16 && AC) {
+        const uint32_t off = ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB;
+        ar[i].h = bload16(ars, off);
+        ar[i].l = bload16(make_brsrc(p.a_lo), off);
+      } else if constexpr (AM == A_BF16) {
         ar[i] = bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB);
       } else if constexpr (AM == A_F32 || AM == A_NORM) {
         ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 4u : BUF_OOB));
@@ -388,7 +398,12 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       int m = m0 + r;
       bool ok = m < p.M && k < p.K;
       float4 v;
-      if constexpr (AM == A_BF16) {
+      if constexpr (AM == A_BF16 && AC) {
+        // raw copy of both planes
+        *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i].h;
+        *reinterpret_cast<uint4*>(base + T::APLANE + r * LROW + ac4 * T::ESZ) = ar[i].l;
+        continue;
+      } else if constexpr (AM == A_BF16) {
         // raw copy of 8 bf16 (CT is bf16 for every bf16 source; zeros beyond the edge)
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
         continue;
@@ -648,8 +663,13 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       if (r >= BM || m >= p.M || !cok) continue;
       float gv = sT[r * TPITCH + co] * sg, uv = sT[r * TPITCH + BO + co] * su;
       float a = silu(gv) * uv;
-      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + n] = a;
-      else ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = f2bf(a);
+      if (p.c_f32) {
+        ((float*)p.c)[(size_t)m * p.ldc + n] = a;
+      } else {
+        const uint16_t hb = f2bf(a);
+        ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = hb;
+        if (p.c_lo) ((uint16_t*)p.c_lo)[(size_t)m * p.ldc + n] = f2bf(a - bf2f(hb));
+      }
     }
   } else if constexpr (EM == E_RESID) {
     const bool cok = ncol < p.N;

@@ -6,10 +6,10 @@ bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, in
   VLA_GEMM_NARROW(uint16_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_NORM, E_STORE)
-  VLA_GEMM_WIDE(uint16_t, __bf16, A_NORM, E_ROPE)
-  VLA_GEMM_WIDE(uint16_t, __bf16, A_NORM, E_SWIGLU)
-  VLA_GEMM_WIDE_AC(uint16_t, __bf16, A_NORM, E_SWIGLU)
-  VLA_GEMM_NARROW_AC(uint16_t, __bf16, A_F32, E_RESID)
+  VLA_GEMM_WIDE(uint16_t, __bf16, A_BF16, E_ROPE)
+  VLA_GEMM_WIDE(uint16_t, __bf16, A_BF16, E_SWIGLU)
+  VLA_GEMM_WIDE_AC(uint16_t, __bf16, A_BF16, E_SWIGLU)
+  VLA_GEMM_NARROW_AC(uint16_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_PATCH, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_MERGE, E_STORE)
   VLA_GEMM_CASE(uint16_t, __bf16, A_TIME, E_STORE, 1, 1, 4, 1)

@@ -23,6 +23,7 @@ bool attn_lookup(int f32, int dp, int hpw, KernelRef* out);
 const void* k_fill_ref();
 const void* k_stage_rows_ref();
 const void* k_rmsnorm_out_ref();
+const void* k_norm_rows_ref();
 const void* k_convert_rows_ref();
 bool euler_tail_lookup(int wt, KernelRef* out);
 

@@ -37,6 +37,7 @@ bool attn_lookup(int f32, int dp, int hpw, KernelRef* out) {
 const void* k_fill_ref() { return (const void*)&k_fill_u32; }
 const void* k_stage_rows_ref() { return (const void*)&k_stage_rows; }
 const void* k_rmsnorm_out_ref() { return (const void*)&k_rmsnorm_out; }
+const void* k_norm_rows_ref() { return (const void*)&k_norm_rows; }
 const void* k_convert_rows_ref() { return (const void*)&k_convert_rows; }
 
 bool euler_tail_lookup(int wt, KernelRef* out) {

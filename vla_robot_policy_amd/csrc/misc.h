@@ -52,6 +52,40 @@ __global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, in
   }
 }
 
+// One normalised row per workgroup, in bf16, for the GEMMs that read it:
+// RMSNorm (x * rstd * g) or LayerNorm ((x - mean) * rstd * g + b, g given as
+// 1 + g when g_plus_one), the row moments merged from the writer's tiles.
+// With out_lo, also the remainder lo = bf16(v - hi) of each value.
+__global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
+  __shared__ float2 snc;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (tid < 64) {
+    float2 nc = norm_coeffs(row_moments_wave(p.rs, r), p.rms, p.eps);
+    if (tid == 0) snc = nc;
+  }
+  __syncthreads();
+  const float2 nc = snc;
+  const float* xr = p.x + (size_t)r * p.ldx;
+  for (int k = tid * 4; k < p.K; k += 1024) {
+    float4 v = *reinterpret_cast<const float4*>(xr + k);
+    float4 g = p.g ? *reinterpret_cast<const float4*>(p.g + k) : make_float4(1.f, 1.f, 1.f, 1.f);
+    if (p.g && p.g_plus_one) { g.x += 1.f; g.y += 1.f; g.z += 1.f; g.w += 1.f; }
+    float4 b = p.bsh ? *reinterpret_cast<const float4*>(p.bsh + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float u0 = (v.x - nc.x) * nc.y * g.x + b.x, u1 = (v.y - nc.x) * nc.y * g.y + b.y;
+    float u2 = (v.z - nc.x) * nc.y * g.z + b.z, u3 = (v.w - nc.x) * nc.y * g.w + b.w;
+    uint2 h;
+    h.x = pack_bf2(u0, u1);
+    h.y = pack_bf2(u2, u3);
+    *reinterpret_cast<uint2*>(p.out + (size_t)r * p.ldo + k) = h;
+    if (p.out_lo) {
+      uint2 l;
+      l.x = pack_bf2(u0 - bf2f(f2bf(u0)), u1 - bf2f(f2bf(u1)));
+      l.y = pack_bf2(u2 - bf2f(f2bf(u2)), u3 - bf2f(f2bf(u3)));
+      *reinterpret_cast<uint2*>(p.out_lo + (size_t)r * p.ldo + k) = l;
+    }
+  }
+}
+
 template <typename WT> __device__ __forceinline__ float wget(const void* w, size_t i);
 template <> __device__ __forceinline__ float wget<uint16_t>(const void* w, size_t i) { return bf2f(((const uint16_t*)w)[i]); }
 template <> __device__ __forceinline__ float wget<float>(const void* w, size_t i) { return ((const float*)w)[i]; }

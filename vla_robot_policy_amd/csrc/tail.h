@@ -19,4 +19,14 @@ struct TailArgs {
   float* x_out; float2* rs_out;                  // new stream, its moments as one tile
 };
 
+// Arguments of the row-normalisation kernel.
+struct NormArgs {
+  const float* x; int ldx;    // [M, ldx] fp32 rows
+  int M, K;                   // rows, row length (a multiple of 4)
+  RowStats rs;                // the writer's tile moments of x
+  int rms; float eps;         // 1: RMSNorm, 0: LayerNorm
+  const float* g; int g_plus_one; const float* bsh;   // gain (NULL = 1), 1 + g, shift (NULL = 0)
+  uint16_t* out; uint16_t* out_lo; int ldo;            // bf16 result, optional remainder plane
+};
+
 }  // namespace vla
