@@ -160,6 +160,7 @@ void pick_tile(int M, int em, int ac, int& mb, int& wn, int& wk, int& nbw, int& 
   nbw = 1;
   if (wide) { wn = 8; wk = 1; }
   else if (mb == 1) { wn = 1; wk = 4; }
+  else if (ac) { wn = 4; wk = 2; }     // compensated residual GEMMs: two k-waves per column block
   else { wn = 4; wk = 1; }
 }
 
@@ -186,6 +187,7 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   int split = std::max(1, (int)std::ceil(per_wg / (192.0 * 1024.0)));
   if (total >= 16.0 * 1024 * 1024 && tiles * split < 200) split = (200 + tiles - 1) / tiles;
   split = std::min(split, std::max(1, slots / tiles));
+  if (threads >= 512 && op.em == E_RESID) split = std::min(split, std::max(1, 160 / tiles));   // two-k-wave residual tiles
   split = std::min(split, std::max(1, (a.K + BK - 1) / BK));
   split = std::min(split, SPLIT_MAX);
   int ksplit = (int)align_up((size_t)((a.K + split - 1) / split), (size_t)BK);

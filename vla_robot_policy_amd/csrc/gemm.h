@@ -160,7 +160,10 @@ struct GemmTile {
   static constexpr int U = UU;                   // 32-wide k-steps per wave per chunk
   static constexpr int BK = 32 * WK * U;         // chunk width
   static constexpr int ESZ = sizeof(CT);
-  static constexpr int LROW = BK * ESZ + 16;     // LDS row pitch (bytes), padded
+#ifndef VLA_LDS_PAD
+#define VLA_LDS_PAD 16
+#endif
+  static constexpr int LROW = BK * ESZ + VLA_LDS_PAD;   // LDS row pitch (bytes), padded
   static constexpr int PLANES = AC ? 2 : 1;      // compensated A: hi and lo planes
   static constexpr int APLANE = BM * LROW;
   static constexpr int ABUF = PLANES * APLANE;
@@ -445,6 +448,9 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; j++) acc[mb][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  // One k-step: every A fragment of the step is requested from LDS before
+  // the first MFMA, so the reads overlap instead of each MFMA waiting for
+  // its own read.
   auto compute = [&](int buf, const BR (&br)[U][NBW]) {
     const char* base = sA + buf * T::ABUF;
 #pragma unroll
@@ -453,19 +459,22 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       typename WL::frag bf[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; j++) bf[j] = WL::cvt(br[u][j]);
+      F af[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; mb++) {
-        const char* ap = base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ;
-        F af;
-        lds_frag(af, ap);
+      for (int mb = 0; mb < MB; mb++) lds_frag(af[mb], base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ);
+      if constexpr (AC) {
+        F al[MB];
 #pragma unroll
-        for (int j = 0; j < NBW; j++) mma32(acc[mb][j], af, bf[j]);
-        if constexpr (AC) {
-          F al;
-          lds_frag(al, ap + T::APLANE);
+        for (int mb = 0; mb < MB; mb++) lds_frag(al[mb], base + T::APLANE + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ);
 #pragma unroll
-          for (int j = 0; j < NBW; j++) mma32(acc[mb][j], al, bf[j]);
-        }
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+          for (int j = 0; j < NBW; j++) { mma32(acc[mb][j], af[mb], bf[j]); mma32(acc[mb][j], al[mb], bf[j]); }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+          for (int j = 0; j < NBW; j++) mma32(acc[mb][j], af[mb], bf[j]);
       }
     }
   };

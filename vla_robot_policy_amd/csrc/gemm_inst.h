@@ -26,9 +26,9 @@
 // compensated-A variants (two k-steps per chunk: half the LDS of the plain tiles)
 #define VLA_GEMM_NARROW_AC(WT, CT, AMV, EMV)            \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 1, 1, 4, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 4, 1, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 4, 1, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 8, 4, 1, 1, 2, 1)
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 4, 2, 1, 2, 1) \
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 4, 2, 1, 2, 1) \
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 8, 4, 2, 1, 2, 1)
 #define VLA_GEMM_WIDE_AC(WT, CT, AMV, EMV)              \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 1, 8, 1, 1, 2, 1) \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 8, 1, 1, 2, 1) \
