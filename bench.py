@@ -31,6 +31,32 @@ WORKLOADS = {
 }
 
 
+def kernel_source_sha() -> str:
+    """Hash of the HIP sources (the counters of a profile hold for these only)."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "vla_robot_policy_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(label: str):
+    """HBM bytes per launch of `label` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy of known size),
+    or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("label") != label or t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -81,13 +107,15 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
     log(f"captured {nodes} kernel nodes")
     labels = [lib.vla_step_kernel_label(plan, i) for i in range(nodes)]
     if only_label is not None:
-        # one kernel alone, relaunched: the run a hardware-counter pass profiles
-        i = labels.index(only_label)
+        # the kernels of one label alone, relaunched in graph order: the run a
+        # hardware-counter pass profiles
+        idx = [i for i, lb in enumerate(labels) if lb == only_label]
         for _ in range(kernel_reps):
-            lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+            for i in idx:
+                lib.check(lib.vla_step_launch_kernel(plan, i, stream))
         torch.cuda.synchronize()
         lib.vla_step_plan_destroy(plan)
-        log(f"launched {only_label} (node {i}) {kernel_reps} times")
+        log(f"launched the {len(idx)} kernels labelled {only_label} x {kernel_reps}")
         return None
     for _ in range(warmup):
         lib.check(lib.vla_step_replay(plan, stream))
@@ -102,30 +130,29 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
     per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
     total_ms = evs[0].elapsed_time(evs[steps])
     log(f"{steps} replays: mean {total_ms / steps:.3f} ms, p50 {np.median(per):.3f} ms")
-    # per-kernel durations: each captured kernel relaunched alone, bracketed by
-    # events on the launch stream, after a 512 MiB read that evicts the 256 MiB
-    # last-level cache with clean lines (inside a step every layer's weights
-    # arrive cold; a write-based flush would leave write-backs to the kernel)
+    # per-kernel durations: every captured launch of a label is relaunched in
+    # graph order, back to back on the launch stream between two events, as
+    # in a step (each launch reads its own weights, so they arrive from HBM
+    # unless one launch's set is small); a 512 MiB read first evicts the
+    # 256 MiB last-level cache with clean lines
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     sink = torch.empty(1, dtype=torch.float32, device=dev)
-    first, count = {}, {}
+    where, count = {}, {}
     for i, lb in enumerate(labels):
-        first.setdefault(lb, i)
+        where.setdefault(lb, []).append(i)
         count[lb] = count.get(lb, 0) + 1
     kern = {}
-    for lb, i in first.items():
-        lib.check(lib.vla_step_launch_kernel(plan, i, stream))
-        pairs = []
-        for _ in range(kernel_reps):
-            torch.sum(flush, dim=0, out=sink[0])
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            lib.check(lib.vla_step_launch_kernel(plan, i, stream))
-            e1.record()
-            pairs.append((e0, e1))
+    for lb, idx in where.items():
+        reps = max(1, kernel_reps // len(idx))
+        torch.sum(flush, dim=0, out=sink[0])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for i in idx:
+                lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+        e1.record()
         torch.cuda.synchronize()
-        us = [a.elapsed_time(b) * 1e3 for a, b in pairs]
-        kern[lb] = {"avg_us": float(np.mean(us)), "count": count[lb]}
+        kern[lb] = {"avg_us": e0.elapsed_time(e1) * 1e3 / (reps * len(idx)), "count": count[lb]}
     del flush
     lib.check(lib.vla_step_replay(plan, stream))   # restore a consistent state
     torch.cuda.synchronize()
@@ -198,7 +225,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--kernel-reps", type=int, default=40,
+                    help="launches per label for the per-kernel durations (at least one pass over its launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-label", default=None,
                     help="relaunch only the kernel with this label --kernel-reps times (for counter passes)")
@@ -222,6 +250,7 @@ def main():
         return
     b = roofline.bound(cfg)
     ops = {o.name: o for o in b.ops}
+    ops.update(roofline.fused_ops(cfg))
     # dominant kernel: largest (per-launch duration x launches per step)
     dom = max(r["kernels"].items(), key=lambda kv: kv[1]["avg_us"] * kv[1]["count"])
     name, kd = dom
@@ -236,7 +265,7 @@ def main():
         else:
             ach, peak, unit = o.flops / dur / 1e12, peaks[o.compute] / 1e12, "TFLOP/s"
         roof = {"kernel": name, "bound": "hbm" if hbm_bound else "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+                "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(name),
                 "avg_launch_us": round(kd["avg_us"], 2), "launches_per_step": kd["count"],
                 "algorithmic_bytes_per_launch": o.bytes, "flops_per_launch": o.flops}
     cpu = None

@@ -148,6 +148,28 @@ def dit_ops(cfg) -> List[Op]:
     return ops
 
 
+def fused_ops(cfg) -> Dict[str, Op]:
+    """Operators of kernels that fuse several of the ops above, per launch.
+
+    ``dit.layer`` is one DiT layer for one Euler step in a single launch: its
+    algorithmic bytes are what must cross HBM once per launch (the layer's
+    weights and biases, its context K/V, the residual stream in and out and
+    the layer's modulation vectors); intermediate activations stay on chip.
+    Its FLOPs are those of the layer's GEMMs and attention.
+    """
+    out: Dict[str, Op] = {}
+    if cfg.kind in ("dit", "step") and cfg.dit is not None:
+        d = cfg.dit
+        n, D, C, w = d.chunk, d.hidden, cfg.ctx_len, cfg.wdtype
+        parts = {"dit.sa_qkv", "dit.sa_attn", "dit.sa_o", "dit.ca_q", "dit.ca_attn", "dit.ca_o", "dit.mlp_up", "dit.mlp_down"}
+        flops = sum(o.flops for o in dit_ops(cfg) if o.name in parts)
+        weights = (_wbytes(w, 3 * D, D) + 3 * _wbytes(w, D, D) + _wbytes(w, d.mlp, D) + _wbytes(w, D, d.mlp)
+                   + 4.0 * (3 * D + 3 * D + d.mlp + D))
+        nbytes = weights + ACT * C * 2 * D + 4.0 * n * D * 2 + 4.0 * 9 * D
+        out["dit.layer"] = Op("dit.layer", "dit_step", flops, nbytes, d.layers * cfg.steps, _compute(w))
+    return out
+
+
 def step_ops(cfg) -> List[Op]:
     if cfg.kind == "block":
         c = cfg.replace(final_norm=False, layers=1)
