@@ -130,7 +130,7 @@ size_t vla_backbone_workspace_bytes(const vla_backbone* bb, int32_t seq);
 typedef struct {
   int32_t hidden, heads, head_dim, mlp, layers, tdim, ctx_dim;
   float eps, time_scale, freq_base;
-  int32_t wdtype; /* F32, BF16 or FP8_E4M3 */
+  int32_t wdtype; /* BF16 or FP8_E4M3      */
   int32_t flags;  /* must be 0             */
 } vla_dit_cfg;
 
@@ -156,7 +156,7 @@ typedef struct {
   const void* w_out; const float* s_out; const float* b_out; /* [action_dim, hidden]                      */
 } vla_dit;
 
-/* ctx: [ctx_len, ctx_dim] bf16 (F32 for an F32 DiT); x0, actions_out:
+/* ctx: [ctx_len, ctx_dim] bf16; x0, actions_out:
  * float32 [chunk, action_dim] (may alias); velocities_out: optional float32
  * [K, chunk, action_dim] record of every v (NULL to skip). */
 vla_status vla_flow_euler_sample(const vla_dit* dit, const void* ctx, int32_t ctx_len, const float* x0, int32_t chunk,
