@@ -63,8 +63,8 @@ typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2 } vla_dtype;
  *   head h reads KV head h / (n_q_heads / n_kv_heads)), h = x + O W_o^T,
  *   out = h + (SiLU(n W_gate^T) * (n W_up^T)) W_down^T with n = RMSNorm(h,
  *   mlp_norm). RMSNorm(x, g) = x / sqrt(mean(x^2) + eps) * g. No biases.
- * Supported: head_dim in {64, 128}; hidden, intermediate multiples of 8;
- * n_q_heads % n_kv_heads == 0; wdtype F32 with adtype F32, or wdtype
+ * Supported: head_dim in {64, 128}; hidden, intermediate multiples of 8
+ * (of 16 for FP8_E4M3 weights); n_q_heads % n_kv_heads == 0; wdtype F32 with adtype F32, or wdtype
  * BF16 / FP8_E4M3 with adtype BF16.
  */
 typedef struct {
@@ -124,8 +124,8 @@ size_t vla_backbone_workspace_bytes(const vla_backbone* bb, int32_t seq);
  *   K/V = ctx W^T + b of every context row; MLP is Linear-GELU(erf)-Linear;
  *   finally v = (LN(x)(1 + scale_f) + shift_f) W_out^T + b_out with
  *   [shift_f, scale_f] = W_f SiLU(c) + b_f. Every Linear has a bias.
- * Supported: head_dim 80 or 64 (hidden = heads * head_dim); widths
- * multiples of 8; 1 <= chunk <= 64; 1 <= K <= 64; 1 <= ctx_len <= 4096.
+ * Supported: head_dim 80 or 64 (hidden = heads * head_dim); hidden, mlp,
+ * tdim, ctx_dim multiples of 8 (of 16 for FP8_E4M3 weights); 1 <= chunk <= 64; 1 <= K <= 64; 1 <= ctx_len <= 4096.
  */
 typedef struct {
   int32_t hidden, heads, head_dim, mlp, layers, tdim, ctx_dim;

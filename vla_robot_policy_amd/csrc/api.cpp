@@ -149,16 +149,19 @@ struct GemmOp {
 
 // Row tile (16-row blocks) by M: one tile up to 112 rows; 64-row tiles up to
 // 256 rows (twice the workgroups of 128-row tiles, a quarter of the LDS
-// traffic per MFMA of narrower ones); 128-row tiles beyond.
+// traffic per MFMA of narrower ones); 128-row tiles beyond, except for
+// compensated narrow tiles, whose two A planes only fit in LDS at 64 rows.
 // Narrow tiles: 16 columns with 4 waves splitting K when M <= 16, else 64
 // columns with 4 waves side by side. Wide tiles (RoPE pairs, gate/up pairs):
-// 128 columns with 8 waves side by side.
+// 128 columns with 8 waves side by side; compensated, 4 x 2 waves (column
+// blocks x k-steps) with two 16-column blocks per wave.
 void pick_tile(int M, int em, int ac, int& mb, int& wn, int& wk, int& nbw, int& u) {
-  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : M <= 256 ? 4 : 8;
-  u = ac ? 2 : 4;
   bool wide = em == E_ROPE || em == E_SWIGLU;
+  mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : (M <= 256 || (ac && !wide)) ? 4 : 8;
+  u = ac ? 2 : 4;
   nbw = 1;
-  if (wide) { wn = 8; wk = 1; }
+  if (wide && ac) { wn = 4; wk = 2; nbw = 2; u = 1; }   // two column blocks per wave: half the A reads
+  else if (wide) { wn = 8; wk = 1; }
   else if (mb == 1) { wn = 1; wk = 4; }
   else if (ac) { wn = 4; wk = 2; }     // compensated residual GEMMs: two k-waves per column block
   else { wn = 4; wk = 1; }
@@ -196,6 +199,8 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   a.ksplit = ksplit;
   // weight-type / alignment requirements of the 8-element fragment loads
   if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
+  if (op.wdtype == VLA_FP8_E4M3 && (a.K % 16 != 0 || a.ldw % 16 != 0))
+    return fail(VLA_ERR_SHAPE, "gemm: fp8 weights need K %d and pitch %d to be multiples of 16", a.K, a.ldw);
   const int ag = op.am == A_BF16 ? 8 : 4;   // activation elements per 16-byte load
   if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM) && (a.lda % ag != 0 || a.K % ag != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
@@ -204,6 +209,8 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (wrows * a.ldw * wbytes >= (double)BUF_LIMIT) return fail(VLA_ERR_SHAPE, "gemm: weight matrix beyond 2 GiB");
   if (op.am != A_TIME && op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
+  if ((op.em == E_RESID ? (double)a.M * a.ldx * 4.0 : (double)a.M * a.ldc * (a.c_f32 ? 4.0 : 2.0)) >= (double)BUF_LIMIT)
+    return fail(VLA_ERR_SHAPE, "gemm: output matrix beyond 2 GiB");
   if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32 && op.am != A_BF16)))
     return fail(VLA_ERR_UNSUPPORTED, "gemm: compensated activations need bf16 weights");
   if (op.ac && op.am == A_BF16 && !a.a_lo && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: compensated bf16 source without its remainder plane");
@@ -318,6 +325,8 @@ vla_status check_block_cfg(const vla_block_cfg* cfg) {
     return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp32 weights need fp32 activations and vice versa");
   if (cfg->hidden <= 0 || cfg->hidden % 8 || cfg->intermediate <= 0 || cfg->intermediate % 8)
     return fail(VLA_ERR_SHAPE, "block cfg: hidden %d / intermediate %d must be positive multiples of 8", cfg->hidden, cfg->intermediate);
+  if (cfg->wdtype == VLA_FP8_E4M3 && (cfg->hidden % 16 || cfg->intermediate % 16))
+    return fail(VLA_ERR_SHAPE, "block cfg: fp8 weights need hidden %d / intermediate %d to be multiples of 16", cfg->hidden, cfg->intermediate);
   if (cfg->n_kv_heads <= 0 || cfg->n_q_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads)
     return fail(VLA_ERR_SHAPE, "block cfg: n_q_heads %d not a multiple of n_kv_heads %d", cfg->n_q_heads, cfg->n_kv_heads);
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return fail(VLA_ERR_SHAPE, "block cfg: head_dim %d not in {64, 128}", cfg->head_dim);
@@ -477,6 +486,8 @@ vla_status check_dit(const vla_dit* d) {
   if (c.heads <= 0 || c.hidden != c.heads * c.head_dim) return fail(VLA_ERR_SHAPE, "dit: hidden %d != heads*head_dim", c.hidden);
   if (c.hidden % 8 || c.mlp % 8 || c.tdim % 8 || c.ctx_dim % 8 || c.layers <= 0 || c.mlp <= 0)
     return fail(VLA_ERR_SHAPE, "dit: widths must be positive multiples of 8");
+  if (c.wdtype == VLA_FP8_E4M3 && (c.hidden % 16 || c.mlp % 16 || c.tdim % 16 || c.ctx_dim % 16))
+    return fail(VLA_ERR_SHAPE, "dit: fp8 weights need widths that are multiples of 16");
   if (!d->layers || !d->w_ada || !d->b_ada || !d->w_ckv || !d->b_ckv || !d->w_t1 || !d->b_t1 || !d->w_t2 || !d->b_t2 ||
       !d->w_f || !d->b_f || !d->w_in || !d->b_in || !d->w_out || !d->b_out)
     return fail(VLA_ERR_INVALID_ARG, "dit: null tensor pointer");

@@ -4,12 +4,16 @@
 // residual / gated residual with per-tile row moments for the next norm).
 //
 // Layout: A is [M, K] row-major (token-major activations); W is [N, K]
-// row-major (PyTorch Linear); each lane's 16-byte W load is exactly the
-// MFMA B-operand fragment, so weights go HBM -> registers without LDS. A is
-// staged through LDS and shared by the workgroup's waves.
+// row-major (PyTorch Linear). bf16 and fp8 weights are read in whole chunk
+// rows (runs of 128-1024 contiguous bytes: a wave's load covers a few rows,
+// which HBM serves far better than the 16 rows x 64 bytes of an MFMA
+// fragment) and staged through LDS, from where each wave reads its MFMA
+// B fragments; fp32 weights (small reference-precision layers) go straight
+// to registers in fragment order. A is staged through LDS and shared by the
+// workgroup's waves.
 // Pipeline: weights stream through a 4-deep register ring (three chunks in
-// flight while a fourth is consumed), activations through a 2-deep register
-// ring into a double-buffered LDS tile, one barrier per chunk. Every load is
+// flight while a fourth is stored), activations through a 2-deep register
+// ring, both into double-buffered LDS tiles, one barrier per chunk. Every load is
 // a raw buffer load; rows or k beyond the edge get an out-of-range offset
 // (the hardware returns zeros), so the loop has no conditional loads and the
 // waits are exact.
@@ -22,6 +26,7 @@
 // of each output tile (no float atomics), so results are bitwise
 // reproducible run to run.
 #pragma once
+#include <type_traits>
 #include "common.h"
 #include "rowstats.h"
 
@@ -171,10 +176,20 @@ struct GemmTile {
   static constexpr int AGROUPS = BM * BK / AG;   // A groups per chunk
   static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
-  static constexpr int SMEM_A = 2 * ABUF;
+  // weights through LDS (bf16 / fp8): [BN][BK] with padded rows; each thread
+  // loads NWL 16-byte groups per chunk, LPR groups make one chunk row
+  static constexpr bool WLDS = sizeof(WT) <= 2;
+  static constexpr int WROW = BK * (int)sizeof(WT) + 16;
+  static constexpr int WBUF = WLDS ? BN * WROW : 0;
+  static constexpr int LPR = BK * (int)sizeof(WT) / 16;
+  static constexpr int NWL = WLDS ? BN * LPR / THREADS : 1;
+  static_assert(!WLDS || ((BK * (int)sizeof(WT)) % 16 == 0 && (BN * LPR) % THREADS == 0 && THREADS % LPR == 0),
+                "weight chunk rows must split evenly into 16-byte groups over the workgroup");
+  static constexpr int SMEM_A = 2 * ABUF + 2 * WBUF;
   static constexpr int SMEM_T = WK * BM * TPITCH * 4;   // one fp32 tile slice per k-wave
   static constexpr int NROWST = (AM == A_MERGE) ? 4 * BM : BM;   // normaliser entries
   static constexpr int SMEM = (SMEM_A > SMEM_T ? SMEM_A : SMEM_T) + NROWST * 8 + 64;
+  static_assert(SMEM <= 160 * 1024, "tile exceeds the 160 KiB of LDS of a compute unit");
   // threads serving one normalised row: a power of two, at most 64
   static constexpr int TPR0 = THREADS / NROWST;
   static constexpr int TPR = TPR0 >= 64 ? 64 : TPR0 >= 32 ? 32 : TPR0 >= 16 ? 16 : TPR0 >= 8 ? 8 : TPR0 >= 4 ? 4 : TPR0 >= 2 ? 2 : 1;
@@ -222,29 +237,50 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const int ke = min(p.K, kb + p.ksplit);
   const int nchunks = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
-  // ---- weight rows of this wave's n-blocks (byte offset of k = 0, or OOB)
-  const brsrc wr = make_brsrc(p.w);
-  uint32_t wrow[NBW];
-#pragma unroll
-  for (int j = 0; j < NBW; j++) {
-    int jb = wn * NBW + j;                      // n-block index within the tile
-    int col = lane & 15;
-    int row;
+  // ---- per-column epilogue vectors, requested now so that their latency
+  // hides under the main loop instead of opening the epilogue: the thread
+  // serves tile column tid % BN (SwiGLU: tid % (BN / 2)) in every epilogue.
+  // Absent vectors read as 0 through an out-of-range offset.
+  const int ecol = EM == E_SWIGLU ? nt * (BN / 2) + tid % (BN / 2) : nt * BN + tid % BN;
+  const bool ecok = ecol < p.N;
+  int ecol2 = ecol;   // RoPE: the partner column; SwiGLU: the up column
+  if constexpr (EM == E_ROPE) {
+    const int D = p.head_dim, hd = D >> 1;
+    const int d = (ecol < p.q_cols ? ecol : ecol - p.q_cols) % D;
+    ecol2 = ecol < p.q_cols + p.k_cols ? (d < hd ? ecol + hd : ecol - hd) : ecol;
+  }
+  if constexpr (EM == E_SWIGLU) ecol2 = p.n_half + ecol;
+  const float e_sc = bloadf(make_brsrc(p.wscale), (p.wscale && ecok) ? (uint32_t)ecol * 4u : BUF_OOB);
+  const float e_sc2 = (EM == E_ROPE || EM == E_SWIGLU)
+                          ? bloadf(make_brsrc(p.wscale), (p.wscale && ecok) ? (uint32_t)ecol2 * 4u : BUF_OOB) : 0.f;
+  const float e_bi = (EM == E_STORE || EM == E_RESID)
+                         ? bloadf(make_brsrc(p.bias), (p.bias && ecok) ? (uint32_t)ecol * 4u : BUF_OOB) : 0.f;
+  const float e_ga = EM == E_RESID ? bloadf(make_brsrc(p.gate), (p.gate && ecok) ? (uint32_t)ecol * 4u : BUF_OOB) : 0.f;
+
+  // ---- weight row of tile row `row` (byte offset of k = 0, or OOB)
+  auto wrow_of = [&](int row) -> uint32_t {
+    const int jb = row >> 4, col = row & 15;   // n-block within the tile, row within it
+    int wr_;
     bool ok;
     if (EM == E_SWIGLU) {
       constexpr int HB = BN / 32 > 0 ? BN / 32 : 1;  // gate n-blocks (first half), then up n-blocks
       int on = nt * (BN / 2) + (jb % HB) * 16 + col;
       ok = on < p.N;
-      row = jb < HB ? on : p.n_half + on;
+      wr_ = jb < HB ? on : p.n_half + on;
     } else {
-      row = nt * BN + jb * 16 + col;
-      ok = row < p.N;
+      wr_ = nt * BN + row;
+      ok = wr_ < p.N;
     }
-    wrow[j] = ok ? (uint32_t)row * (uint32_t)p.ldw * WL::ESZ : BUF_OOB;
-  }
+    return ok ? (uint32_t)wr_ * (uint32_t)p.ldw * WL::ESZ : BUF_OOB;
+  };
+  const brsrc wr = make_brsrc(p.w);
   const int kl = (lane >> 4) * 8;               // this lane's offset inside a 32-wide k-step
 
+  // fp32 weights: fragments straight to registers (rows of this wave's n-blocks)
   using BR = typename WL::raw;
+  uint32_t wrow[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; j++) wrow[j] = T::WLDS ? BUF_OOB : wrow_of((wn * NBW + j) * 16 + (lane & 15));
   auto load_b = [&](BR (&br)[U][NBW], int kc) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -255,7 +291,34 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     }
   };
 
-  BR b0[U][NBW], b1[U][NBW], b2[U][NBW], b3[U][NBW];
+  // bf16 / fp8 weights: whole chunk rows in 16-byte groups; thread tid takes
+  // group tid % LPR of rows tid / LPR + i * NT / LPR
+  constexpr bool WLDS = T::WLDS;
+  constexpr int LPR = T::LPR, NWL = T::NWL, WROW = T::WROW;
+  char* sW = smem + 2 * T::ABUF;
+  const int wg16 = tid % LPR, wr0 = tid / LPR;
+  uint32_t wro[NWL];
+#pragma unroll
+  for (int i = 0; i < NWL; i++) wro[i] = WLDS ? wrow_of(wr0 + i * (NT / LPR)) : BUF_OOB;
+  auto load_w = [&](uint4 (&v)[NWL], int kc) {
+    const int k = kc + wg16 * (16 / WL::ESZ);
+#pragma unroll
+    for (int i = 0; i < NWL; i++) v[i] = bload16<CP_NT>(wr, (k < ke && wro[i] != BUF_OOB) ? wro[i] + (uint32_t)k * WL::ESZ : BUF_OOB);
+  };
+  auto store_w = [&](int buf, const uint4 (&v)[NWL]) {
+    char* base = sW + buf * T::WBUF + wg16 * 16;
+#pragma unroll
+    for (int i = 0; i < NWL; i++) *reinterpret_cast<uint4*>(base + (wr0 + i * (NT / LPR)) * WROW) = v[i];
+  };
+  // the weight ring: one register slot per chunk in flight
+  using RR = std::conditional_t<WLDS, uint4[NWL], BR[U][NBW]>;
+  auto load_ring = [&](RR& r, int kc) {
+    if constexpr (WLDS) load_w(r, kc);
+    else load_b(r, kc);
+  };
+  auto store_ring = [&](int buf, const RR& r) {
+    if constexpr (WLDS) store_w(buf, r);
+  };
 
   // ---- per-row normaliser (NORM / MERGE): (value to subtract, 1/std) of
   // every source row of the tile. TPR consecutive threads serve a row; the
@@ -448,17 +511,27 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NBW; j++) acc[mb][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // One k-step: every A fragment of the step is requested from LDS before
-  // the first MFMA, so the reads overlap instead of each MFMA waiting for
-  // its own read.
-  auto compute = [&](int buf, const BR (&br)[U][NBW]) {
+  // One k-step: every A and B fragment of the step is requested from LDS
+  // before the first MFMA, so the reads overlap instead of each MFMA waiting
+  // for its own read.
+  auto compute = [&](int buf, const RR& br) {
     const char* base = sA + buf * T::ABUF;
+    const char* wbase = sW + buf * T::WBUF;
 #pragma unroll
     for (int u = 0; u < U; u++) {
       int klocal = (u * WK + wk) * 32 + kl;
       typename WL::frag bf[NBW];
+      if constexpr (WLDS) {
 #pragma unroll
-      for (int j = 0; j < NBW; j++) bf[j] = WL::cvt(br[u][j]);
+        for (int j = 0; j < NBW; j++) {
+          const char* wp = wbase + ((wn * NBW + j) * 16 + (lane & 15)) * WROW + klocal * WL::ESZ;
+          if constexpr (WL::ESZ == 2) bf[j] = WL::cvt(*reinterpret_cast<const uint4*>(wp));
+          else bf[j] = WL::cvt(*reinterpret_cast<const uint2*>(wp));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NBW; j++) bf[j] = WL::cvt(br[u][j]);
+      }
       F af[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) lds_frag(af[mb], base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ);
@@ -466,10 +539,16 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         F al[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) lds_frag(al[mb], base + T::APLANE + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ);
+        // every hi product before the lo ones: MFMAs into one accumulator
+        // are then MB * NBW instructions apart instead of back to back
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-          for (int j = 0; j < NBW; j++) { mma32(acc[mb][j], af[mb], bf[j]); mma32(acc[mb][j], al[mb], bf[j]); }
+          for (int j = 0; j < NBW; j++) mma32(acc[mb][j], af[mb], bf[j]);
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+          for (int j = 0; j < NBW; j++) mma32(acc[mb][j], al[mb], bf[j]);
       } else {
 #pragma unroll
         for (int mb = 0; mb < MB; mb++)
@@ -480,15 +559,17 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   };
 
   // ---- main loop. Chunk c: weights in ring slot c%4 (issued three chunks
-  // ahead), activations staged into LDS buffer c%2 from register slot c%2
-  // (issued two chunks ahead, stored one chunk ahead). Loads complete in
-  // issue order (vmcnt), so each chunk's activations are issued before its
-  // weights: waiting for A of chunk c+1 never waits for later weights. Loads
-  // past the last chunk read zeros (out-of-range offsets) and are never used.
+  // ahead, stored to LDS buffer c%2 one chunk ahead), activations staged into
+  // LDS buffer c%2 from register slot c%2 (issued two chunks ahead, stored one
+  // chunk ahead). Loads complete in issue order (vmcnt), so each chunk's
+  // activations are issued before its weights: waiting for A of chunk c+1
+  // never waits for later weights. Loads past the last chunk read zeros
+  // (out-of-range offsets) and are never used.
   AR a0[GPT], a1[GPT];
-  load_a(a0, kb); load_b(b0, kb);
-  load_a(a1, kb + BK); load_b(b1, kb + BK);
-  load_b(b2, kb + 2 * BK);
+  RR r0, r1, r2, r3;
+  load_a(a0, kb); load_ring(r0, kb);
+  load_a(a1, kb + BK); load_ring(r1, kb + BK);
+  load_ring(r2, kb + 2 * BK);
   // residual inputs of a small unsplit tile are fetched now as well (same
   // element mapping as the epilogue: column tid % BN, rows tid / BN + i * NT / BN)
   constexpr int XPT = (BM * BN + NT - 1) / NT;
@@ -508,21 +589,23 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   row_coeffs();
   __syncthreads();   // sRow ready
   store_a(0, a0, kb);
+  store_ring(0, r0);
   __syncthreads();
 
-#define VLA_GEMM_ITER(C, BCUR, BNEXT3, ARELOAD, ASTORE)                     \
+#define VLA_GEMM_ITER(C, RCUR, RNEXT1, RNEXT3, ARELOAD, ASTORE)             \
   {                                                                         \
     load_a(ARELOAD, kb + ((C) + 2) * BK);                                   \
-    load_b(BNEXT3, kb + ((C) + 3) * BK);                                    \
-    if ((C) < nchunks) compute((C) & 1, BCUR);                              \
+    load_ring(RNEXT3, kb + ((C) + 3) * BK);                                 \
+    if ((C) < nchunks) compute((C) & 1, RCUR);                              \
     store_a(((C) + 1) & 1, ASTORE, kb + ((C) + 1) * BK);                    \
+    store_ring(((C) + 1) & 1, RNEXT1);                                      \
     __syncthreads();                                                        \
   }
   for (int c = 0; c < nchunks; c += 4) {
-    VLA_GEMM_ITER(c + 0, b0, b3, a0, a1)
-    VLA_GEMM_ITER(c + 1, b1, b0, a1, a0)
-    VLA_GEMM_ITER(c + 2, b2, b1, a0, a1)
-    VLA_GEMM_ITER(c + 3, b3, b2, a1, a0)
+    VLA_GEMM_ITER(c + 0, r0, r1, r3, a0, a1)
+    VLA_GEMM_ITER(c + 1, r1, r2, r0, a1, a0)
+    VLA_GEMM_ITER(c + 2, r2, r3, r1, a0, a1)
+    VLA_GEMM_ITER(c + 3, r3, r0, r2, a1, a0)
   }
 #undef VLA_GEMM_ITER
 
@@ -584,53 +667,75 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   }
 
   // ---- split-K: publish the partial tile; the last arriving workgroup sums
-  // all partials in split order. Partials are written with device-scope
-  // atomic stores and read with device-coherent (sc1) loads, so the hand-off
-  // needs no L2 write-back or invalidate; the counter increment is issued
-  // only after every thread's stores have completed.
+  // all partials in split order. Partials move as 16-byte device-coherent
+  // (sc1) stores and loads, so the hand-off needs no L2 write-back or
+  // invalidate; the counter increment is issued only after every thread's
+  // stores have completed. The reducer requests up to four splits' partials
+  // at once.
   if (p.split > 1) {
+    constexpr int C4 = BN / 4;                  // float4 per tile row
+    constexpr int PF4 = (BM * C4 + NT - 1) / NT;
     const int tile = mt * p.n_tiles_n + nt;
     const size_t tstride = (size_t)p.n_tiles_m * p.n_tiles_n * (BM * BN);
-    float* mine = p.part + (size_t)s * tstride + (size_t)tile * (BM * BN);
+    const brsrc pw = make_brsrc(p.part + (size_t)s * tstride + (size_t)tile * (BM * BN));
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      int r = r0e + i * RPT;
-      if (r < BM) st_dev(mine + r * BN + cc, sT[r * TPITCH + cc]);
+    for (int i = 0; i < PF4; i++) {
+      const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4;
+      if (r < BM) {
+        const float4 v = *reinterpret_cast<const float4*>(sT + r * TPITCH + c4 * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), pw, (uint32_t)(r * BN + c4 * 4) * 4u, 0, CP_SC1);
+      }
     }
     if (tile_arrive(p.cnt_tile + tile, p.split, sFlag)) return;
     const brsrc pr = make_brsrc(p.part + (size_t)tile * (BM * BN));
-    float sum[XPE];
+    float4 sum[PF4];
 #pragma unroll
-    for (int i = 0; i < XPE; i++) sum[i] = 0.f;
-    for (int q = 0; q < p.split; q++) {
-      float v[XPE];
+    for (int i = 0; i < PF4; i++) sum[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q0 = 0; q0 < p.split; q0 += 4) {
+      uint4 v[4][PF4];
 #pragma unroll
-      for (int i = 0; i < XPE; i++)
-        v[i] = bloadf<CP_SC1>(pr, r0e + i * RPT < BM ? (uint32_t)(q * tstride + (r0e + i * RPT) * BN + cc) * 4u : BUF_OOB);
+      for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int i = 0; i < XPE; i++) sum[i] += v[i];
+        for (int i = 0; i < PF4; i++) {
+          const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4;
+          v[j][i] = bload16<CP_SC1>(pr, (q0 + j < p.split && r < BM) ? (uint32_t)((q0 + j) * tstride + r * BN + c4 * 4) * 4u : BUF_OOB);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (q0 + j < p.split) {
+#pragma unroll
+          for (int i = 0; i < PF4; i++) {
+            const float4 f = as_f4(v[j][i]);
+            sum[i].x += f.x; sum[i].y += f.y; sum[i].z += f.z; sum[i].w += f.w;
+          }
+        }
     }
 #pragma unroll
-    for (int i = 0; i < XPE; i++)
-      if (r0e + i * RPT < BM) sT[(r0e + i * RPT) * TPITCH + cc] = sum[i];
+    for (int i = 0; i < PF4; i++) {
+      const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4;
+      if (r < BM) *reinterpret_cast<float4*>(sT + r * TPITCH + c4 * 4) = sum[i];
+    }
     if (tid == 0) p.cnt_tile[tile] = 0u;
     __syncthreads();
   }
 
-  // ---- epilogues
+  // ---- epilogues (outputs through buffer stores: 32-bit element offsets)
+  const brsrc cr = make_brsrc(p.c);
+  auto put = [&](uint32_t idx, float v) {
+    if (p.c_f32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), cr, idx * 4u, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), cr, idx * 2u, 0, 0);
+  };
   if constexpr (EM == E_STORE) {
     const bool cok = ncol < p.N;
-    const float sc = (p.wscale && cok) ? p.wscale[ncol] : 1.f;
-    const float bi = (p.bias && cok) ? p.bias[ncol] : 0.f;
+    const float sc = p.wscale ? e_sc : 1.f;
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;
       if (r >= BM || m >= p.M || !cok) continue;
-      float v = sT[r * TPITCH + cc] * sc + bi;
+      float v = sT[r * TPITCH + cc] * sc + e_bi;
       if (p.act == ACT_GELU) v = gelu_erf(v);
       else if (p.act == ACT_SILU) v = silu(v);
-      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + ncol] = v;
-      else ((uint16_t*)p.c)[(size_t)m * p.ldc + ncol] = f2bf(v);
+      put((uint32_t)m * p.ldc + ncol, v);
     }
   } else if constexpr (EM == E_ROPE) {
     const int D = p.head_dim, hd = D >> 1;
@@ -639,23 +744,28 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     const int d = (ncol < p.q_cols ? ncol : ncol - p.q_cols) % D;
     const int fi = d < hd ? d : d - hd;
     const int pc = d < hd ? cc + hd : cc - hd;           // partner column in the tile
-    const int pn = d < hd ? ncol + hd : ncol - hd;
-    const float sc = (p.wscale && cok) ? p.wscale[ncol] : 1.f;
-    const float sc2 = (p.wscale && cok && rot) ? p.wscale[pn] : 1.f;
+    const float sc = p.wscale ? e_sc : 1.f;
+    const float sc2 = p.wscale ? e_sc2 : 1.f;
     const float theta = exp2f(-2.0f * (float)fi / (float)D * log2f(p.rope_base));
+    // the thread's rows step by RPT positions: the first angle from sincosf,
+    // each next one by a rotation through RPT * theta
+    float cs, sn, cd, sd;
+    sincosf((float)(m0 + r0e + p.pos0) * theta, &sn, &cs);
+    sincosf((float)RPT * theta, &sd, &cd);
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;
-      if (r >= BM || m >= p.M || !cok) continue;
-      float v = sT[r * TPITCH + cc] * sc;
-      if (rot) {
-        float v2 = sT[r * TPITCH + pc] * sc2;
-        float sn, cs;
-        sincosf((float)(m + p.pos0) * theta, &sn, &cs);
-        v = d < hd ? v * cs - v2 * sn : v * cs + v2 * sn;
+      if (r < BM && m < p.M && cok) {
+        float v = sT[r * TPITCH + cc] * sc;
+        if (rot) {
+          float v2 = sT[r * TPITCH + pc] * sc2;
+          v = d < hd ? v * cs - v2 * sn : v * cs + v2 * sn;
+        }
+        put((uint32_t)m * p.ldc + ncol, v);
       }
-      if (p.c_f32) ((float*)p.c)[(size_t)m * p.ldc + ncol] = v;
-      else ((uint16_t*)p.c)[(size_t)m * p.ldc + ncol] = f2bf(v);
+      const float c2 = cs * cd - sn * sd;
+      sn = sn * cd + cs * sd;
+      cs = c2;
     }
   } else if constexpr (EM == E_SWIGLU) {
     constexpr int BO = BN / 2;
@@ -664,27 +774,25 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     const int co = tid % BO, r0o = tid / BO;
     const int n = nt * BO + co;
     const bool cok = n < p.N;
-    const float sg = (p.wscale && cok) ? p.wscale[n] : 1.f;
-    const float su = (p.wscale && cok) ? p.wscale[p.n_half + n] : 1.f;
+    const float sg = p.wscale ? e_sc : 1.f;
+    const float su = p.wscale ? e_sc2 : 1.f;
+    const brsrc clr = make_brsrc(p.c_lo);
 #pragma unroll
     for (int i = 0; i < XPO; i++) {
       int r = r0o + i * RPO, m = m0 + r;
       if (r >= BM || m >= p.M || !cok) continue;
       float gv = sT[r * TPITCH + co] * sg, uv = sT[r * TPITCH + BO + co] * su;
       float a = silu(gv) * uv;
-      if (p.c_f32) {
-        ((float*)p.c)[(size_t)m * p.ldc + n] = a;
-      } else {
-        const uint16_t hb = f2bf(a);
-        ((uint16_t*)p.c)[(size_t)m * p.ldc + n] = hb;
-        if (p.c_lo) ((uint16_t*)p.c_lo)[(size_t)m * p.ldc + n] = f2bf(a - bf2f(hb));
-      }
+      const uint32_t idx = (uint32_t)m * p.ldc + n;
+      put(idx, a);
+      if (!p.c_f32 && p.c_lo) __builtin_amdgcn_raw_buffer_store_b16(f2bf(a - bf2f(f2bf(a))), clr, idx * 2u, 0, 0);
     }
   } else if constexpr (EM == E_RESID) {
     const bool cok = ncol < p.N;
-    const float sc = (p.wscale && cok) ? p.wscale[ncol] : 1.f;
-    const float bi = (p.bias && cok) ? p.bias[ncol] : 0.f;
-    const float ga = (p.gate && cok) ? p.gate[ncol] : 1.f;
+    const float sc = p.wscale ? e_sc : 1.f;
+    const float bi = e_bi;
+    const float ga = p.gate ? e_ga : 1.f;
+    const brsrc xw = make_brsrc(p.x);
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;
@@ -697,29 +805,48 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       } else {
         xn = xv[i] + v;
       }
-      p.x[(size_t)m * p.ldx + ncol] = xn;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(xn), xw, ((uint32_t)m * p.ldx + ncol) * 4u, 0, 0);
       sT[r * TPITCH + cc] = xn;
     }
-    // moments of this tile's columns per row, merged by the stream's next
-    // reader: the G = min(BN, 64) lanes holding a row reduce it together
-    // (all rows of the tile at once); a wider tile adds its waves' halves
-    constexpr int G = BN < 64 ? BN : 64;
+    // moments of this tile's columns per row (mean, sum of squared
+    // deviations), merged by the stream's next reader: TPRM consecutive
+    // threads share a row, each sums a strided set of float4 columns of the
+    // LDS tile, then a butterfly over the TPRM lanes; two passes
     static_assert(BN <= 64, "residual tiles are at most 64 columns wide");
+    __syncthreads();
+    constexpr int C4 = BN / 4;
+    constexpr int TPRM0 = NT / BM;
+    constexpr int TPRM1 = TPRM0 >= 16 ? 16 : TPRM0 >= 8 ? 8 : TPRM0 >= 4 ? 4 : TPRM0 >= 2 ? 2 : 1;
+    constexpr int TPRM = TPRM1 > C4 ? C4 : TPRM1;
+    constexpr int F4T = (C4 + TPRM - 1) / TPRM;
     const int ncols = min(BN, p.N - nt * BN);
+    const int jq = tid % TPRM;
+    for (int r = tid / TPRM; r < BM; r += NT / TPRM) {
+      const int m = m0 + r;
+      float4 v[F4T];
+      float s1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      int r = r0e + i * RPT, m = m0 + r;
-      bool live = r < BM && m < p.M && cc < ncols;
-      float v = live ? sT[r * TPITCH + cc] : 0.f;
-      float sum = v;
+      for (int f = 0; f < F4T; f++) {
+        const int c4 = jq + f * TPRM;
+        v[f] = c4 < C4 ? *reinterpret_cast<const float4*>(sT + r * TPITCH + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int c = 4 * c4;
+        s1 += (c < ncols ? v[f].x : 0.f) + (c + 1 < ncols ? v[f].y : 0.f) + (c + 2 < ncols ? v[f].z : 0.f) +
+              (c + 3 < ncols ? v[f].w : 0.f);
+      }
 #pragma unroll
-      for (int o = G >> 1; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, WAVE);
-      float mean = sum / (float)ncols;
-      float d = live ? v - mean : 0.f;
-      float sq = d * d;
+      for (int o = 1; o < TPRM; o <<= 1) s1 += __shfl_xor(s1, o, WAVE);
+      const float mean = s1 / (float)ncols;
+      float sq = 0.f;
 #pragma unroll
-      for (int o = G >> 1; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, WAVE);
-      if (cc == 0 && r < BM && m < p.M) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, sq);
+      for (int f = 0; f < F4T; f++) {
+        const int c = 4 * (jq + f * TPRM);
+        const float d0 = c < ncols ? v[f].x - mean : 0.f, d1 = c + 1 < ncols ? v[f].y - mean : 0.f;
+        const float d2 = c + 2 < ncols ? v[f].z - mean : 0.f, d3 = c + 3 < ncols ? v[f].w - mean : 0.f;
+        sq += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+      }
+#pragma unroll
+      for (int o = 1; o < TPRM; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
+      if (jq == 0 && m < p.M) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, sq);
     }
   }
 }

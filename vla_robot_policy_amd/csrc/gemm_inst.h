@@ -23,14 +23,16 @@
   VLA_GEMM_CASE(WT, CT, AMV, EMV, 4, 8, 1, 1) \
   VLA_GEMM_CASE(WT, CT, AMV, EMV, 7, 8, 1, 1) \
   VLA_GEMM_CASE(WT, CT, AMV, EMV, 8, 8, 1, 1)
-// compensated-A variants (two k-steps per chunk: half the LDS of the plain tiles)
+// compensated-A variants (two k-steps per chunk: half the LDS of the plain
+// tiles); 128-row narrow tiles would not fit in LDS with both A planes
 #define VLA_GEMM_NARROW_AC(WT, CT, AMV, EMV)            \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 1, 1, 4, 1, 2, 1) \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 4, 2, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 4, 2, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 8, 4, 2, 1, 2, 1)
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 4, 2, 1, 2, 1)
+// wide compensated tiles: 4 x 2 waves with two 16-column blocks each, one
+// 32-wide k-step per wave per chunk
 #define VLA_GEMM_WIDE_AC(WT, CT, AMV, EMV)              \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 1, 8, 1, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 8, 1, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 8, 1, 1, 2, 1) \
-  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 8, 8, 1, 1, 2, 1)
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 1, 4, 2, 2, 1, 1) \
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 4, 2, 2, 1, 1) \
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 4, 2, 2, 1, 1) \
+  VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 8, 4, 2, 2, 1, 1)
