@@ -518,6 +518,8 @@ int cu_count() {
 bool dit_stack_ok(const vla_dit_cfg& cf, int n, int G) {
   const int D = cf.hidden;
   if (n < 1 || n > 16 || cf.head_dim > DS_DP || cf.head_dim % 8 || D % 32 || D > 4 * DS_KSW * 32) return false;
+  KernelRef k{};
+  if (!dit_layer_lookup(cf.wdtype, D, &k)) return false;   // widths with an instantiated layer kernel
   if (cf.mlp % D) return false;
   const int most = std::max(3 * D / 16, std::max(cf.mlp / 16, (D / 16) * (cf.mlp / D)));
   return most <= DS_MAXU * G && cf.heads <= DS_MAXU * G;
@@ -541,6 +543,11 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
   uint16_t* ckv = c.take<uint16_t>((size_t)C * L * 2 * D);
   Stream xs = take_stream(c, n, D);
   float* x = xs.x;
+  // the layer kernel's stream buffers: layer l reads xb[l % 2] and writes
+  // xb[(l + 1) % 2] through the per-sublayer buffers x1, x2
+  float* xb[2] = {x, c.take<float>((size_t)n * D)};
+  float* x1 = c.take<float>((size_t)n * D);
+  float* x2 = c.take<float>((size_t)n * D);
   uint16_t* qkv = c.take<uint16_t>((size_t)n * 3 * D);
   uint16_t* ao = c.take<uint16_t>((size_t)n * D);
   uint16_t* q = c.take<uint16_t>((size_t)n * D);
@@ -632,7 +639,8 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         DitLayerArgs a{};
         a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
         a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
-        a.x = x; a.qkv = qkv; a.q = q; a.ao = ao; a.h = h;
+        a.x_in = xb[l & 1]; a.x1 = x1; a.x2 = x2; a.x_out = xb[(l + 1) & 1];
+        a.qkv = qkv; a.q = q; a.ao = ao; a.h = h;
         a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.cv = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldc = L * 2 * D;
         a.mod = m;
         const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
@@ -721,7 +729,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     {  // velocity head + Euler update (+ input projection for the next step)
       TailArgs t{};
       t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
-      t.x = x;
+      t.x = stack ? xb[L & 1] : x;   // the last layer's output
       t.shift = fmod ? fmod + (size_t)k * 2 * D : nullptr;
       t.scale = fmod ? fmod + (size_t)k * 2 * D + D : nullptr;
       t.w_out = d.w_out; t.s_out = d.s_out; t.b_out = d.b_out;

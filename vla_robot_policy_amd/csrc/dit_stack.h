@@ -31,8 +31,9 @@
 // that completes the last DOWN tile resets the counters for the next launch.
 //
 // Each LayerNorm is computed by every workgroup that needs it, from the fp32
-// residual stream staged in LDS (two-pass mean / variance), so no statistics
-// travel between workgroups.
+// residual stream held in registers (two-pass mean / variance), so no
+// statistics travel between workgroups. The width D is a template parameter:
+// every loop over a row is unrolled without bounds branches.
 #pragma once
 #include "common.h"
 
@@ -59,7 +60,14 @@ __host__ __device__ constexpr int ds_counter_words(int D) { return DS_TILE0 + D 
 struct DitLayerArgs {
   int n, D, H, hd, mlp, C;        // action rows (<= 16), width, heads, head dim, MLP width, context tokens
   float eps, scale_log2;          // LayerNorm epsilon; log2(e) / sqrt(hd)
-  float* x;                       // [n, D] residual stream (fp32)
+  // [n, D] residual stream (fp32), one buffer per sublayer: x1 = x_in + the
+  // self-attention branch, x2 = x1 + the cross-attention branch, x_out = x2 +
+  // the MLP branch. Each is written once per launch before anything reads
+  // it, so no L2 can hold a stale copy and readers use ordinary cached loads.
+  const float* x_in;
+  float* x1;
+  float* x2;
+  float* x_out;
   uint16_t* qkv;                  // [n, 3D] bf16
   uint16_t* q;                    // [n, D] cross-attention query
   uint16_t* ao;                   // [n, D] attention output
@@ -161,33 +169,32 @@ __device__ __forceinline__ DsUnit ds_unit(const DitLayerArgs& a, int ph, int u) 
   return d;
 }
 
-// The wave's k-steps of a unit: steps s = wave + 4 i (i < NS) of kw / 32,
+// The wave's k-steps of a unit: steps s = wave + 4 i (i < NS) of KSTEPS,
 // into register slots OFF .. OFF + NS - 1.
-template <typename WT, int OFF, int NS>
+template <typename WT, int OFF, int NS, int KSTEPS>
 __device__ __forceinline__ void ds_load_unit(const DitLayerArgs& a, const DsUnit& d, typename DsW<WT>::raw (&r)[DS_WSLOTS]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const brsrc wr = make_brsrc(a.w[d.wi]);
   const int col = d.n0 + (lane & 15);
-  const int ksteps = d.kw / 32;
 #pragma unroll
   for (int i = 0; i < NS; i++) {
     int s = wave + 4 * i;
     int k = d.k0 + s * 32 + (lane >> 4) * 8;
-    bool ok = s < ksteps && col < d.N;
+    bool ok = s < KSTEPS && col < d.N;
     r[OFF + i] = DsW<WT>::load(wr, ok ? ((uint32_t)col * d.K + k) * DsW<WT>::ESZ : BUF_OOB);
   }
 }
 
 // 16 x 16 tile of one unit: A [16][kw] bf16 in LDS (pitch apitch), weights in
 // register slots OFF ..; the wave's partial sum over its k-steps.
-template <typename WT, int OFF, int NS>
-__device__ __forceinline__ f32x4 ds_mma(const char* rA, int apitch, int ksteps, const typename DsW<WT>::raw (&w)[DS_WSLOTS]) {
+template <typename WT, int OFF, int NS, int KSTEPS>
+__device__ __forceinline__ f32x4 ds_mma(const char* rA, int apitch, const typename DsW<WT>::raw (&w)[DS_WSLOTS]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NS; i++) {
     int s = wave + 4 * i;
-    if (s < ksteps) {
+    if (s < KSTEPS) {
       FragBF16 af;
       af.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rA + (lane & 15) * apitch + (s * 32 + (lane >> 4) * 8) * 2));
       mma32(acc, af, DsW<WT>::frag(w[OFF + i]));
@@ -365,233 +372,260 @@ __host__ __device__ constexpr int ds_region_a(int D) {
 }
 __host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_x(D) + ds_region_a(D) + 4 * 256 * 4 + 64; }
 
-template <typename WT>
-__global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
+// One phase of the layer for this workgroup, specialised per phase so that
+// each phase's registers are allocated for that phase alone. False when the
+// workgroup must leave the kernel (a wait timed out).
+template <typename WT, int D, int PH>
+__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rX, char* rA, float* red, int* sflag, int& finished_tiles) {
   using WR = typename DsW<WT>::raw;
-  extern __shared__ __align__(16) char smem[];
-  char* rX = smem;
-  char* rA = smem + ds_region_x(a.D);
-  float* red = reinterpret_cast<float*>(rA + ds_region_a(a.D));
-  int* sflag = reinterpret_cast<int*>(red + 4 * 256);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x, G = gridDim.x;
-  const int D = a.D, n = a.n;
-  const int APITCH = D * 2 + 16;
-  const int ntile = D / 16;
+  const int n = a.n;
+  constexpr int APITCH = D * 2 + 16;
+  constexpr int ntile = D / 16;
+  constexpr int KSTEPS = D / 32;                     // 32-wide k-steps of a unit (every unit spans D)
+  constexpr int NSW = (KSTEPS + 3) / 4;              // of them per wave
+  const int U = ds_units(a, PH);
+  const int first = ((wg - ds_base(a, PH)) % G + G) % G;
+  if (first >= U) return true;                       // no work in this phase
+  const int nu = min(DS_MAXU, (U - first + G - 1) / G);
+  constexpr bool is_att = PH == DP_SAATT || PH == DP_CAATT;
+
+  constexpr bool norm = PH == DP_QKV || PH == DP_CAQ || PH == DP_UP;
+  // Everything that does not depend on the previous phase is requested
+  // before its wait: the first context K / V block of a cross-attention
+  // head, a LayerNorm's shift / scale, the weights of the GEMM units. Each
+  // kind of phase keeps its own registers across its own wait.
+  auto wait_prev = [&]() -> bool {
+    if (PH == 0 || ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), sflag)) return true;
+    // time-out: record it, poison this workgroup's outputs
+    if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
+    return false;
+  };
+  // LayerNorm geometry: wave w normalises rows 4w .. 4w + 3; lane l holds
+  // float4 column groups l + 64 k (k < KG) of them
+  constexpr int KG = (D / 4 + 63) / 64;
+
+  if constexpr (is_att) {
+    uint4 pkv[DS_SE], pvv[DS_SE];
+    const bool pre_kv = PH == DP_CAATT;
+    if (pre_kv)
+      ds_att_load(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), false, wave,
+                  (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, pkv, pvv);
+    if (!wait_prev()) return false;
+    // ---- one head per unit
+    for (int j = 0; j < nu; j++) {
+      const int hh = first + j * G;
+      if (PH == DP_SAATT)
+        ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D, true,
+                     a.ao + hh * a.hd, D, n, n, a.hd, a.scale_log2, rX, rA, pkv, pvv, false);
+      else
+        ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc, false,
+                     a.ao + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rX, rA, pkv, pvv, pre_kv && j == 0);
+    }
+  } else {
+    const int mi = PH == DP_QKV ? 0 : PH == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
+    // shift and 1 + scale of the lane's column groups (requested before the wait)
+    float4 shv[norm ? KG : 1], gv[norm ? KG : 1];
+    if constexpr (norm) {
+      const brsrc mr = make_brsrc(a.mod + (size_t)mi * D);
+#pragma unroll
+      for (int k = 0; k < KG; k++) {
+        const int cg = lane + 64 * k;
+        shv[k] = as_f4(bload16(mr, cg < D / 4 ? (uint32_t)cg * 16u : BUF_OOB));
+        gv[k] = as_f4(bload16(mr, cg < D / 4 ? (uint32_t)(D + 4 * cg) * 4u : BUF_OOB));
+      }
+    }
+    WR wreg[DS_WSLOTS];
+    ds_load_unit<WT, 0, NSW, KSTEPS>(a, ds_unit(a, PH, first), wreg);
+    if (nu > 1) ds_load_unit<WT, DS_KSW, NSW, KSTEPS>(a, ds_unit(a, PH, first + G), wreg);
+    if (!wait_prev()) return false;
+    // ---- the A operand [16][D] (bf16) in region A
+    if constexpr (norm) {
+      // two-pass mean / variance of each of the wave's 4 rows (wave-wide
+      // sums), then u = LN(x)(1 + scale) + shift in bf16 into LDS. Rows
+      // beyond n read zeros and give finite values that no output uses.
+      const brsrc xr = make_brsrc(PH == DP_QKV ? a.x_in : PH == DP_CAQ ? a.x1 : a.x2);
+      float4 xv[4][KG];
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+        for (int k = 0; k < KG; k++) {
+          const int r = 4 * wave + rr, cg = lane + 64 * k;
+          xv[rr][k] = as_f4(bload16(xr, (cg < D / 4 && r < n) ? ((uint32_t)r * D + 4 * cg) * 4u : BUF_OOB));
+        }
+      float mean[4], rstd[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        float s1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < KG; k++) s1 += (xv[rr][k].x + xv[rr][k].y) + (xv[rr][k].z + xv[rr][k].w);
+        mean[rr] = s1;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) mean[rr] += __shfl_xor(mean[rr], o, WAVE);
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        mean[rr] *= 1.f / (float)D;
+        float s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < KG; k++) {
+          if (lane + 64 * k < D / 4) {
+            const float d0 = xv[rr][k].x - mean[rr], d1 = xv[rr][k].y - mean[rr];
+            const float d2 = xv[rr][k].z - mean[rr], d3 = xv[rr][k].w - mean[rr];
+            s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+          }
+        }
+        rstd[rr] = s2;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) rstd[rr] += __shfl_xor(rstd[rr], o, WAVE);
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) rstd[rr] = rsqrtf(rstd[rr] * (1.f / (float)D) + a.eps);
+#pragma unroll
+      for (int k = 0; k < KG; k++) {
+        const int cg = lane + 64 * k;
+        if (cg < D / 4) {
+          const float4 g = make_float4(1.f + gv[k].x, 1.f + gv[k].y, 1.f + gv[k].z, 1.f + gv[k].w);
+#pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            const float4 xx = xv[rr][k];
+            const float m = mean[rr], rs = rstd[rr];
+            uint2 pk;
+            pk.x = pack_bf2((xx.x - m) * rs * g.x + shv[k].x, (xx.y - m) * rs * g.y + shv[k].y);
+            pk.y = pack_bf2((xx.z - m) * rs * g.z + shv[k].z, (xx.w - m) * rs * g.w + shv[k].w);
+            *reinterpret_cast<uint2*>(rA + (4 * wave + rr) * APITCH + cg * 8) = pk;
+          }
+        }
+      }
+    }
+    int staged_k0 = -1;
+    auto unit = [&](int j) {
+      const DsUnit d = ds_unit(a, PH, first + j * G);
+      constexpr int apitch = APITCH;
+      if (!norm && d.k0 != staged_k0) {
+        // bf16 activations: ao (SAO, CAO) or the unit's slice of h (DOWN)
+        const uint16_t* src = PH == DP_DOWN ? a.h : a.ao;
+        const int lds = PH == DP_DOWN ? a.mlp : D;
+        const brsrc sr = make_brsrc(src);
+        constexpr int AS = (16 * D / 8 + DS_THREADS - 1) / DS_THREADS;   // 16-byte groups per thread
+        uint4 av[AS];
+#pragma unroll
+        for (int i = 0; i < AS; i++) {
+          int e8 = tid + i * DS_THREADS;
+          int r = (e8 * 8) / D, c = (e8 * 8) % D;
+          av[i] = bload16<CP_SC1>(sr, (e8 < 16 * D / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < AS; i++) {
+          int e8 = tid + i * DS_THREADS;
+          int r = (e8 * 8) / D, c = (e8 * 8) % D;
+          if (e8 < 16 * D / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
+        }
+        staged_k0 = d.k0;
+      }
+      __syncthreads();
+      // ---- 16 x 16 tile: wave w covers k-steps w, w + 4, ...
+      f32x4 acc = j == 0 ? ds_mma<WT, 0, NSW, KSTEPS>(rA, apitch, wreg) : ds_mma<WT, DS_KSW, NSW, KSTEPS>(rA, apitch, wreg);
+#pragma unroll
+      for (int i = 0; i < 4; i++) red[wave * 256 + ((lane >> 4) * 4 + i) * 16 + (lane & 15)] = acc[i];
+      __syncthreads();
+      // ---- epilogue: thread = (row tid / 16, column tid % 16)
+      const int r = tid >> 4, cc = tid & 15, col = d.n0 + cc;
+      float v = red[tid] + red[256 + tid] + red[512 + tid] + red[768 + tid];
+      const float* ws = a.s[d.wi];
+      if (ws) v *= ws[col];
+      if (PH == DP_DOWN) {
+        // publish this slice's partial; the tile's last slice sums them in slice order
+        const int tile = d.n0 / 16, slice = d.k0 / d.kw, nsl = a.mlp / d.kw;
+        st_sc1_f32(a.part + ((size_t)slice * ntile + tile) * 256 + tid, v);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+          unsigned old = __hip_atomic_fetch_add(a.cnt + DS_TILE0 + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sflag[1] = old == (unsigned)(nsl - 1);
+        }
+        __syncthreads();
+        if (!sflag[1]) return;
+        const brsrc pr = make_brsrc(a.part);
+        float sum = 0.f;
+        for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
+        v = sum;
+        if (tid == 0) a.cnt[DS_TILE0 + tile] = 0u;
+        finished_tiles++;
+      }
+      v += a.b[d.wi][col];
+      if (PH == DP_QKV || PH == DP_CAQ || PH == DP_UP) {
+        if (PH == DP_UP) v = gelu_erf(v);
+        uint16_t* out = PH == DP_QKV ? a.qkv : PH == DP_CAQ ? a.q : a.h;
+        const int ldo = PH == DP_QKV ? 3 * D : PH == DP_CAQ ? D : a.mlp;
+        if (r < n && col < d.N) st_sc1_u16(make_brsrc(out), (uint32_t)(r * ldo + col), f2bf(v));
+      } else {
+        // gated residual: x += gate * v
+        const int gi = PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8;
+        if (r < n) {
+          const float* xs = PH == DP_SAO ? a.x_in : PH == DP_CAO ? a.x1 : a.x2;
+          float* xd = PH == DP_SAO ? a.x1 : PH == DP_CAO ? a.x2 : a.x_out;
+          float xo = bloadf(make_brsrc(xs), (uint32_t)(r * D + col) * 4u);
+          st_sc1_f32(xd + (size_t)r * D + col, xo + a.mod[(size_t)gi * D + col] * v);
+        }
+      }
+    };
+    unit(0);
+    if (nu > 1) unit(1);
+  }
+  // ---- count this phase's finished units once every store has completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    sflag[1] = 0;
+    unsigned add = PH == DP_DOWN ? (unsigned)finished_tiles : (unsigned)nu;
+    if (add) {
+      unsigned* slot = a.cnt + PH * DS_NC * DS_CSTRIDE + (PH == DP_DOWN ? 0 : (wg % DS_NC) * DS_CSTRIDE);
+      unsigned old = __hip_atomic_fetch_add(slot, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the last DOWN tile: every unit of every phase is done and no
+      // workgroup polls any more, so the counters can be cleared
+      sflag[1] = PH == DP_DOWN && old + add == (unsigned)ds_target(a, DP_DOWN);
+    }
+  }
+  __syncthreads();
+  if (sflag[1] && tid < DP_N * DS_NC)
+    __hip_atomic_store(a.cnt + tid * DS_CSTRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+template <typename WT, int D>
+__global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  char* rX = smem;
+  char* rA = smem + ds_region_x(D);
+  float* red = reinterpret_cast<float*>(rA + ds_region_a(D));
+  int* sflag = reinterpret_cast<int*>(red + 4 * 256);
+  const int tid = threadIdx.x;
+  const int wg = blockIdx.x, G = gridDim.x;
   int finished_tiles = 0;        // DOWN tiles this workgroup completed
 
   // a failed earlier launch of this run: poison the stream and leave at once
   if (tid == 0) sflag[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sflag[0]) {
-    for (int e = wg * DS_THREADS + tid; e < n * D; e += G * DS_THREADS) st_sc1_f32(a.x + e, __builtin_nanf(""));
+    for (int e = wg * DS_THREADS + tid; e < a.n * D; e += G * DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
     return;
   }
-
-  for (int ph = 0; ph < DP_N; ph++) {
-    const int U = ds_units(a, ph);
-    const int first = ((wg - ds_base(a, ph)) % G + G) % G;
-    if (first >= U) continue;                          // no work in this phase
-    const int nu = min(DS_MAXU, (U - first + G - 1) / G);
-    const bool is_att = ph == DP_SAATT || ph == DP_CAATT;
-
-    const bool norm = ph == DP_QKV || ph == DP_CAQ || ph == DP_UP;
-    // Everything that does not depend on the previous phase is requested
-    // before its wait: the first context K / V block of a cross-attention
-    // head, a LayerNorm's shift / scale, the weights of the GEMM units. Each
-    // kind of phase keeps its own registers across its own wait.
-    auto wait_prev = [&]() -> bool {
-      if (ph == 0 || ds_wait(a.cnt + (ph - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, ph - 1), sflag)) return true;
-      // time-out: record it, poison this workgroup's outputs
-      if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(a.x + e, __builtin_nanf(""));
-      return false;
-    };
-    constexpr int MS = (2 * 4 * DS_KSW * 32 / 4 + DS_THREADS - 1) / DS_THREADS;   // float4 per thread
-
-    if (is_att) {
-      uint4 pkv[DS_SE], pvv[DS_SE];
-      const bool pre_kv = ph == DP_CAATT;
-      if (pre_kv)
-        ds_att_load(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), false, wave,
-                    (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, pkv, pvv);
-      if (!wait_prev()) return;
-      // ---- one head per unit
-      for (int j = 0; j < nu; j++) {
-        const int hh = first + j * G;
-        if (ph == DP_SAATT)
-          ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D, true,
-                       a.ao + hh * a.hd, D, n, n, a.hd, a.scale_log2, rX, rA, pkv, pvv, false);
-        else
-          ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc, false,
-                       a.ao + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rX, rA, pkv, pvv, pre_kv && j == 0);
-      }
-    } else {
-      const int mi = ph == DP_QKV ? 0 : ph == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
-      uint4 pmod[MS];
-      if (norm) {
-        const brsrc mr = make_brsrc(a.mod + (size_t)mi * D);
-#pragma unroll
-        for (int i = 0; i < MS; i++) {
-          int e4 = tid + i * DS_THREADS;
-          pmod[i] = bload16(mr, e4 < 2 * D / 4 ? (uint32_t)e4 * 16u : BUF_OOB);
-        }
-      }
-      WR wreg[DS_WSLOTS];
-      ds_load_unit<WT, 0, DS_KSW>(a, ds_unit(a, ph, first), wreg);
-      if (nu > 1) ds_load_unit<WT, DS_KSW, DS_KSW>(a, ds_unit(a, ph, first + G), wreg);
-      if (!wait_prev()) return;
-      // ---- the A operand [16][D] (bf16) in region A
-      if (norm) {
-        // thread (row r = tid / 16, lane j of the row) holds float4 columns
-        // 4 (j + 16 i), i < D / 64, of x in registers: two-pass mean /
-        // variance over the 16 lanes of the row, then u in bf16 into LDS
-        constexpr int XS = 4 * DS_KSW * 32 / 64;          // float4 per thread at the largest D
-        const int r = tid >> 4, j = tid & 15;
-        const brsrc xr = make_brsrc(a.x);
-        float4 xv[XS];
-#pragma unroll
-        for (int i = 0; i < XS; i++) {
-          int c = 4 * (j + 16 * i);
-          xv[i] = as_f4(bload16<CP_SC1>(xr, (c < D && r < n) ? ((uint32_t)r * D + c) * 4u : BUF_OOB));
-        }
-        // shift | scale (prefetched) into region X
-        float* smod = reinterpret_cast<float*>(rX);
-#pragma unroll
-        for (int i = 0; i < MS; i++) {
-          int e4 = tid + i * DS_THREADS;
-          if (e4 < 2 * D / 4) *reinterpret_cast<uint4*>(smod + e4 * 4) = pmod[i];
-        }
-        __syncthreads();
-        float s1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < XS; i++) s1 += (xv[i].x + xv[i].y) + (xv[i].z + xv[i].w);
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) s1 += __shfl_xor(s1, o, WAVE);
-        const float mean = s1 / (float)D;
-        float s2 = 0.f;
-#pragma unroll
-        for (int i = 0; i < XS; i++) {
-          if (4 * (j + 16 * i) < D) {
-            float d0 = xv[i].x - mean, d1 = xv[i].y - mean, d2 = xv[i].z - mean, d3 = xv[i].w - mean;
-            s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
-          }
-        }
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o, WAVE);
-        const float rstd = rsqrtf(s2 / (float)D + a.eps);
-#pragma unroll
-        for (int i = 0; i < XS; i++) {
-          int c = 4 * (j + 16 * i);
-          if (c < D) {
-            const float4 shv = *reinterpret_cast<const float4*>(smod + c);
-            const float4 scv = *reinterpret_cast<const float4*>(smod + D + c);
-            float4 u;
-            u.x = r < n ? (xv[i].x - mean) * rstd * (1.f + scv.x) + shv.x : 0.f;
-            u.y = r < n ? (xv[i].y - mean) * rstd * (1.f + scv.y) + shv.y : 0.f;
-            u.z = r < n ? (xv[i].z - mean) * rstd * (1.f + scv.z) + shv.z : 0.f;
-            u.w = r < n ? (xv[i].w - mean) * rstd * (1.f + scv.w) + shv.w : 0.f;
-            uint2 pk;
-            pk.x = pack_bf2(u.x, u.y);
-            pk.y = pack_bf2(u.z, u.w);
-            *reinterpret_cast<uint2*>(rA + r * APITCH + c * 2) = pk;
-          }
-        }
-      }
-      int staged_k0 = -1;
-      auto unit = [&](int j) {
-        const DsUnit d = ds_unit(a, ph, first + j * G);
-        const int apitch = d.kw * 2 + 16;
-        if (!norm && d.k0 != staged_k0) {
-          // bf16 activations: ao (SAO, CAO) or the unit's slice of h (DOWN)
-          const uint16_t* src = ph == DP_DOWN ? a.h : a.ao;
-          const int lds = ph == DP_DOWN ? a.mlp : D;
-          const brsrc sr = make_brsrc(src);
-          constexpr int AS = 16 * 4 * DS_KSW * 32 / 8 / DS_THREADS;   // 16-byte groups per thread at the largest D
-          uint4 av[AS];
-#pragma unroll
-          for (int i = 0; i < AS; i++) {
-            int e8 = tid + i * DS_THREADS;
-            int r = (e8 * 8) / d.kw, c = (e8 * 8) % d.kw;
-            av[i] = bload16<CP_SC1>(sr, (e8 < 16 * d.kw / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
-          }
-          __syncthreads();
-#pragma unroll
-          for (int i = 0; i < AS; i++) {
-            int e8 = tid + i * DS_THREADS;
-            int r = (e8 * 8) / d.kw, c = (e8 * 8) % d.kw;
-            if (e8 < 16 * d.kw / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
-          }
-          staged_k0 = d.k0;
-        }
-        __syncthreads();
-        // ---- 16 x 16 tile: wave w covers k-steps w, w + 4, ...
-        const int ksteps = d.kw / 32;
-        f32x4 acc = j == 0 ? ds_mma<WT, 0, DS_KSW>(rA, apitch, ksteps, wreg) : ds_mma<WT, DS_KSW, DS_KSW>(rA, apitch, ksteps, wreg);
-#pragma unroll
-        for (int i = 0; i < 4; i++) red[wave * 256 + ((lane >> 4) * 4 + i) * 16 + (lane & 15)] = acc[i];
-        __syncthreads();
-        // ---- epilogue: thread = (row tid / 16, column tid % 16)
-        const int r = tid >> 4, cc = tid & 15, col = d.n0 + cc;
-        float v = red[tid] + red[256 + tid] + red[512 + tid] + red[768 + tid];
-        const float* ws = a.s[d.wi];
-        if (ws) v *= ws[col];
-        if (ph == DP_DOWN) {
-          // publish this slice's partial; the tile's last slice sums them in slice order
-          const int tile = d.n0 / 16, slice = d.k0 / d.kw, nsl = a.mlp / d.kw;
-          st_sc1_f32(a.part + ((size_t)slice * ntile + tile) * 256 + tid, v);
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();
-          if (tid == 0) {
-            unsigned old = __hip_atomic_fetch_add(a.cnt + DS_TILE0 + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sflag[1] = old == (unsigned)(nsl - 1);
-          }
-          __syncthreads();
-          if (!sflag[1]) return;
-          const brsrc pr = make_brsrc(a.part);
-          float sum = 0.f;
-          for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
-          v = sum;
-          if (tid == 0) a.cnt[DS_TILE0 + tile] = 0u;
-          finished_tiles++;
-        }
-        v += a.b[d.wi][col];
-        if (ph == DP_QKV || ph == DP_CAQ || ph == DP_UP) {
-          if (ph == DP_UP) v = gelu_erf(v);
-          uint16_t* out = ph == DP_QKV ? a.qkv : ph == DP_CAQ ? a.q : a.h;
-          const int ldo = ph == DP_QKV ? 3 * D : ph == DP_CAQ ? D : a.mlp;
-          if (r < n && col < d.N) st_sc1_u16(make_brsrc(out), (uint32_t)(r * ldo + col), f2bf(v));
-        } else {
-          // gated residual: x += gate * v
-          const int gi = ph == DP_SAO ? 2 : ph == DP_CAO ? 5 : 8;
-          if (r < n) {
-            float* xp = a.x + (size_t)r * D + col;
-            float xo = bloadf<CP_SC1>(make_brsrc(a.x), (uint32_t)(r * D + col) * 4u);
-            st_sc1_f32(xp, xo + a.mod[(size_t)gi * D + col] * v);
-          }
-        }
-      };
-      unit(0);
-      if (nu > 1) unit(1);
-    }
-    // ---- count this phase's finished units once every store has completed
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      sflag[1] = 0;
-      unsigned add = ph == DP_DOWN ? (unsigned)finished_tiles : (unsigned)nu;
-      if (add) {
-        unsigned* slot = a.cnt + ph * DS_NC * DS_CSTRIDE + (ph == DP_DOWN ? 0 : (wg % DS_NC) * DS_CSTRIDE);
-        unsigned old = __hip_atomic_fetch_add(slot, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // the last DOWN tile: every unit of every phase is done and no
-        // workgroup polls any more, so the counters can be cleared
-        sflag[1] = ph == DP_DOWN && old + add == (unsigned)ds_target(a, DP_DOWN);
-      }
-    }
-    __syncthreads();
-    if (sflag[1] && tid < DP_N * DS_NC)
-      __hip_atomic_store(a.cnt + tid * DS_CSTRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (!ds_phase<WT, D, DP_QKV>(a, rX, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_SAATT>(a, rX, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_SAO>(a, rX, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_CAQ>(a, rX, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_CAATT>(a, rX, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_CAO>(a, rX, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_UP>(a, rX, rA, red, sflag, finished_tiles)) return;
+  ds_phase<WT, D, DP_DOWN>(a, rX, rA, red, sflag, finished_tiles);
 }
 
 }  // namespace vla
