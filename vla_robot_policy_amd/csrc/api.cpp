@@ -513,16 +513,19 @@ int cu_count() {
   return n;
 }
 
-// The persistent layer kernel covers chunks of at most 16 rows whose GEMMs
-// split into 16-column units of one D-wide k-extent each.
+// The persistent layer kernel covers chunks of at most 16 rows, widths with
+// an instantiated kernel, and MLPs whose width is a multiple of 2D (DOWN
+// units span 2D), with enough workgroups for its units.
 bool dit_stack_ok(const vla_dit_cfg& cf, int n, int G) {
   const int D = cf.hidden;
   if (n < 1 || n > 16 || cf.head_dim > DS_DP || cf.head_dim % 8 || D % 32 || D > 4 * DS_KSW * 32) return false;
   KernelRef k{};
   if (!dit_layer_lookup(cf.wdtype, D, &k)) return false;   // widths with an instantiated layer kernel
-  if (cf.mlp % D) return false;
-  const int most = std::max(3 * D / 16, std::max(cf.mlp / 16, (D / 16) * (cf.mlp / D)));
-  return most <= DS_MAXU * G && cf.heads <= DS_MAXU * G;
+  if (cf.mlp % (2 * D)) return false;
+  // up to two 16 x D units per workgroup in QKV, SAO, CAQ, CAO; one 32 x D
+  // unit of UP and one 16 x 2D unit of DOWN
+  if (3 * D / 16 > DS_MAXU * G || cf.heads > DS_MAXU * G) return false;
+  return cf.mlp / 32 <= G && (D / 16) * (cf.mlp / (2 * D)) <= G;
 }
 
 struct DitIO {

@@ -131,8 +131,9 @@ template <int CP = CP_NONE>
 __device__ __forceinline__ float bloadf(brsrc r, uint32_t off) {
   return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP));
 }
+template <int CP = CP_NONE>
 __device__ __forceinline__ uint16_t bload2(brsrc r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
 }
 
 // ---------------------------------------------------------------- wave reductions

@@ -16,9 +16,9 @@
 //   6 UP     u = LN(x)(1 + scale_mlp) + shift_mlp;  h = GELU(u W1^T + b1)
 //   7 DOWN   x += gate_mlp * (h W2^T + b2)
 //
-// Work units: 16 output columns x D input columns of one GEMM (DOWN is split
-// into mlp / D slices of D columns, summed in a fixed order by the last slice
-// of each tile), or one attention head. Unit u of phase p belongs to
+// Work units: 16 output columns x D input columns of one GEMM (32 columns
+// for UP; DOWN is split into mlp / 2D slices of 2D columns, summed in a fixed
+// order by the last slice of each tile), or one attention head. Unit u of phase p belongs to
 // workgroup (u + base_p) mod G, so a workgroup knows its units in advance and
 // streams their weights into registers before it waits for the previous
 // phase: the HBM latency of the next weights overlaps the current phase.
@@ -43,8 +43,9 @@ enum DitPhase { DP_QKV = 0, DP_SAATT, DP_SAO, DP_CAQ, DP_CAATT, DP_CAO, DP_UP, D
 
 constexpr int DS_THREADS = 256;
 constexpr int DS_KSW = 10;        // 32-wide k-steps per wave per unit: D <= 4 * 10 * 32
-constexpr int DS_MAXU = 2;        // GEMM units per workgroup per phase (the kernel unrolls two)
-// A workgroup's weight registers hold DS_MAXU units of D columns.
+constexpr int DS_MAXU = 2;        // 16 x D GEMM units per workgroup per phase (the kernel unrolls two)
+// A workgroup's weight registers hold DS_MAXU units of 16 x D (or one unit
+// of UP or DOWN).
 constexpr int DS_WSLOTS = DS_MAXU * DS_KSW;
 constexpr int DS_DP = 96;         // head dim padded for the attention MFMAs
 constexpr int DS_KB = 32;         // keys per attention block
@@ -96,8 +97,8 @@ __device__ __forceinline__ int ds_units(const DitLayerArgs& a, int ph) {
     case DP_QKV: return 3 * a.D / 16;
     case DP_SAATT: case DP_CAATT: return a.H;
     case DP_SAO: case DP_CAQ: case DP_CAO: return a.D / 16;
-    case DP_UP: return a.mlp / 16;
-    default: return (a.D / 16) * (a.mlp / a.D);
+    case DP_UP: return a.mlp / 32;
+    default: return (a.D / 16) * (a.mlp / (2 * a.D));
   }
 }
 // value of the phase counter once the phase is complete
@@ -144,107 +145,128 @@ template <> struct DsW<uint8_t> {
   __device__ static FragBF16 frag(raw v) { return fp8x8_to_frag(v); }
 };
 
+// A unit is NB blocks of 16 output columns over a k range of KW: 16 columns
+// x D for QKV, SAO, CAQ and CAO; 32 columns x D for UP; 16 columns x 2D (one
+// of mlp / 2D slices, summed in a fixed order by the tile's last slice) for
+// DOWN. The two MLP phases thus have one unit per workgroup at the full
+// model's shapes.
 struct DsUnit {
   int wi;        // weight index (0..5)
-  int N, K;      // output width, row length of W (= k extent of the whole GEMM)
+  int N, K;      // output width, row length of W
   int n0, k0;    // first output column, first k of this unit
-  int kw;        // k extent of the unit (D)
 };
 
 __device__ __forceinline__ DsUnit ds_unit(const DitLayerArgs& a, int ph, int u) {
   DsUnit d;
-  d.n0 = 16 * u; d.k0 = 0; d.K = a.D; d.kw = a.D;
+  d.n0 = 16 * u; d.k0 = 0; d.K = a.D;
   switch (ph) {
     case DP_QKV: d.wi = 0; d.N = 3 * a.D; break;
     case DP_SAO: d.wi = 1; d.N = a.D; break;
     case DP_CAQ: d.wi = 2; d.N = a.D; break;
     case DP_CAO: d.wi = 3; d.N = a.D; break;
-    case DP_UP: d.wi = 4; d.N = a.mlp; break;
-    default: {   // DOWN: tile u % (D/16), slice u / (D/16) of D columns
+    case DP_UP: d.wi = 4; d.N = a.mlp; d.n0 = 32 * u; break;
+    default: {   // DOWN: tile u % (D/16), slice u / (D/16) of 2D columns
       const int nt = a.D / 16;
       d.wi = 5; d.N = a.D; d.K = a.mlp;
-      d.n0 = 16 * (u % nt); d.k0 = (u / nt) * a.D;
+      d.n0 = 16 * (u % nt); d.k0 = (u / nt) * 2 * a.D;
     }
   }
   return d;
 }
 
-// The wave's k-steps of a unit: steps s = wave + 4 i (i < NS) of KSTEPS,
-// into register slots OFF .. OFF + NS - 1.
-template <typename WT, int OFF, int NS, int KSTEPS>
+// The wave's k-steps of a unit: steps s = wave + 4 i (i < NS) of KST for each
+// of the NB column blocks, into register slots OFF + b NS + i.
+template <typename WT, int OFF, int NB, int NS, int KST>
 __device__ __forceinline__ void ds_load_unit(const DitLayerArgs& a, const DsUnit& d, typename DsW<WT>::raw (&r)[DS_WSLOTS]) {
+  static_assert(OFF + NB * NS <= DS_WSLOTS, "unit exceeds the weight registers");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const brsrc wr = make_brsrc(a.w[d.wi]);
-  const int col = d.n0 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < NS; i++) {
-    int s = wave + 4 * i;
-    int k = d.k0 + s * 32 + (lane >> 4) * 8;
-    bool ok = s < KSTEPS && col < d.N;
-    r[OFF + i] = DsW<WT>::load(wr, ok ? ((uint32_t)col * d.K + k) * DsW<WT>::ESZ : BUF_OOB);
+  for (int b = 0; b < NB; b++) {
+    const int col = d.n0 + b * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < NS; i++) {
+      int s = wave + 4 * i;
+      int k = d.k0 + s * 32 + (lane >> 4) * 8;
+      bool ok = s < KST && col < d.N;
+      r[OFF + b * NS + i] = DsW<WT>::load(wr, ok ? ((uint32_t)col * d.K + k) * DsW<WT>::ESZ : BUF_OOB);
+    }
   }
 }
 
-// 16 x 16 tile of one unit: A [16][kw] bf16 in LDS (pitch apitch), weights in
-// register slots OFF ..; the wave's partial sum over its k-steps.
-template <typename WT, int OFF, int NS, int KSTEPS>
-__device__ __forceinline__ f32x4 ds_mma(const char* rA, int apitch, const typename DsW<WT>::raw (&w)[DS_WSLOTS]) {
+// NB 16 x 16 tiles of one unit: A [16][KW] bf16 in LDS (pitch apitch),
+// weights in register slots OFF ..; the wave's partial sums over its k-steps.
+template <typename WT, int OFF, int NB, int NS, int KST>
+__device__ __forceinline__ void ds_mma(const char* rA, int apitch, const typename DsW<WT>::raw (&w)[DS_WSLOTS], f32x4 (&acc)[NB]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < NB; b++) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NS; i++) {
     int s = wave + 4 * i;
-    if (s < KSTEPS) {
+    if (s < KST) {
       FragBF16 af;
       af.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rA + (lane & 15) * apitch + (s * 32 + (lane >> 4) * 8) * 2));
-      mma32(acc, af, DsW<WT>::frag(w[OFF + i]));
+#pragma unroll
+      for (int b = 0; b < NB; b++) mma32(acc[b], af, DsW<WT>::frag(w[OFF + b * NS + i]));
     }
   }
-  return acc;
 }
 
 // ---------------------------------------------------------------- attention of one head (<= 16 queries)
-// The four waves take interleaved blocks of 32 keys (S^T = K Q^T per block,
-// online softmax per lane, O^T = V^T P^T from registers), then their partial
-// (max, sum, O) are combined in LDS. Q and the outputs are coherent (sc1);
-// K / V are read coherently when `kv_sc1`.
+// The four waves take interleaved blocks of 32 keys: S^T = K Q^T per block,
+// online softmax per lane, O^T = V^T P^T, with every MFMA fragment loaded
+// straight from memory (K and Q rows are contiguous in the head dimension;
+// a V^T fragment gathers 8 keys of one column with 2-byte loads, in the key
+// order the lane's P values already have). With more than one block the
+// waves' partial (max, sum, O) are combined in LDS; with one block wave 0
+// writes the output itself. Q and the outputs are coherent (sc1); K / V are
+// read coherently when `kv_sc1`.
 __device__ __forceinline__ FragBF16 ds_gfrag(brsrc r, uint32_t off, bool sc1) {
   uint4 v = sc1 ? bload16<CP_SC1>(r, off) : bload16(r, off);
   FragBF16 f; f.v = __builtin_bit_cast(bf16x8, v); return f;
 }
 
-constexpr int DS_SE = DS_KB * (DS_DP / 8) / 64;   // 16-byte K (and V) groups per lane per block
+// The fragments of one 32-key block: K for the two 16-key halves and the
+// three 32-wide steps of the (padded) head dimension; V^T for the six
+// 16-column blocks, 8 keys each (keys 4g..4g+3 and 16+4g..16+4g+3 of lane
+// group g).
+struct DsAttFr {
+  uint4 k[2][DS_DP / 32];
+  uint16_t v[DS_DP / 16][8];
+};
 
-// Requests block `blk` (of nblk) of K and V for this wave: lane-strided
-// 16-byte groups, zeros beyond the keys or the head dim.
-__device__ __forceinline__ void ds_att_load(brsrc kr, brsrc vr, bool sc1, int blk, int nblk, int nk, int ldkv, int hd,
-                                            uint4 (&kv)[DS_SE], uint4 (&vv)[DS_SE]) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, bool sc1, int blk, int nblk, int nk, int ldkv, int hd,
+                                             DsAttFr& f) {
+  const int lane = threadIdx.x & 63, qn = lane & 15, grp = lane >> 4;
   const int kb = blk * DS_KB;
+  const bool live = blk < nblk;
 #pragma unroll
-  for (int i = 0; i < DS_SE; i++) {
-    int e = lane + i * 64;
-    int key = e / (DS_DP / 8), d8 = (e % (DS_DP / 8)) * 8;
-    int j = kb + key;
-    bool ok = blk < nblk && j < nk && d8 < hd;
-    uint32_t off = ok ? ((uint32_t)j * ldkv + d8) * 2u : BUF_OOB;
-    kv[i] = sc1 ? bload16<CP_SC1>(kr, off) : bload16(kr, off);
-    vv[i] = sc1 ? bload16<CP_SC1>(vr, off) : bload16(vr, off);
-  }
+  for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+    for (int ds = 0; ds < DS_DP / 32; ds++) {
+      const int key = kb + hb * 16 + qn, d = ds * 32 + grp * 8;
+      const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldkv + d) * 2u : BUF_OOB;
+      f.k[hb][ds] = sc1 ? bload16<CP_SC1>(kr, off) : bload16(kr, off);
+    }
+#pragma unroll
+  for (int db = 0; db < DS_DP / 16; db++)
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const int key = kb + (t < 4 ? 4 * grp + t : 16 + 4 * grp + (t - 4)), d = db * 16 + qn;
+      const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldkv + d) * 2u : BUF_OOB;
+      f.v[db][t] = sc1 ? bload2<CP_SC1>(vr, off) : bload2(vr, off);
+    }
 }
 
-// kv / vv hold this wave's first block when `have0` (requested before the
+// `f` holds this wave's first block when `have0` (requested before the
 // caller's wait); each later round is requested before the current one is
 // computed.
 __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const uint16_t* Kp, const uint16_t* Vp, int ldkv,
                                              bool kv_sc1, uint16_t* O, int ldo, int nq, int nk, int hd, float scale_log2,
-                                             char* lds, char* lds_o, uint4 (&kv)[DS_SE], uint4 (&vv)[DS_SE], bool have0) {
-  constexpr int KPITCH = DS_DP * 2 + 16, VPITCH = DS_KB * 2 + 16;
-  constexpr int WSTAGE = DS_KB * KPITCH + DS_DP * VPITCH;
+                                             char* lds_o, DsAttFr& f, bool have0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qn = lane & 15, grp = lane >> 4;
-  char* sK = lds + wave * WSTAGE;
-  char* sV = sK + DS_KB * KPITCH;
   const brsrc qr = make_brsrc(Q), kr = make_brsrc(Kp), vr = make_brsrc(Vp), orr = make_brsrc(O);
   const int nblk = (nk + DS_KB - 1) / DS_KB;
 
@@ -254,7 +276,7 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
     int d = ds * 32 + grp * 8;
     qf[ds] = ds_gfrag(qr, (qn < nq && d < hd) ? ((uint32_t)qn * ldq + d) * 2u : BUF_OOB, true);
   }
-  if (!have0) ds_att_load(kr, vr, kv_sc1, wave, nblk, nk, ldkv, hd, kv, vv);
+  if (!have0) ds_att_frags(kr, vr, kv_sc1, wave, nblk, nk, ldkv, hd, f);
   f32x4 oacc[DS_DP / 16];
 #pragma unroll
   for (int i = 0; i < DS_DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -262,31 +284,30 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
 
   for (int r0 = 0; r0 < nblk; r0 += 4) {
     const int blk = r0 + wave;
-    const int kb = blk * DS_KB;
-    __syncthreads();
-    // K [32][DP] and V^T [DP][32] of this wave's block
-#pragma unroll
-    for (int i = 0; i < DS_SE; i++) {
-      int e = lane + i * 64;
-      int key = e / (DS_DP / 8), d8 = (e % (DS_DP / 8)) * 8;
-      *reinterpret_cast<uint4*>(sK + key * KPITCH + d8 * 2) = kv[i];
-      const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv[i]);
-#pragma unroll
-      for (int t = 0; t < 8; t++) *reinterpret_cast<uint16_t*>(sV + (d8 + t) * VPITCH + key * 2) = ve[t];
-    }
-    __syncthreads();
-    if (r0 + 4 < nblk) ds_att_load(kr, vr, kv_sc1, blk + 4, nblk, nk, ldkv, hd, kv, vv);
     if (blk < nblk) {
+      const int kb = blk * DS_KB;
+      // this block's fragments; the next round's are requested before use
+      FragBF16 kf[2][DS_DP / 32], vf[DS_DP / 16];
+#pragma unroll
+      for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+        for (int ds = 0; ds < DS_DP / 32; ds++) kf[hb][ds].v = __builtin_bit_cast(bf16x8, f.k[hb][ds]);
+#pragma unroll
+      for (int db = 0; db < DS_DP / 16; db++) {
+        uint4 u;
+        u.x = (uint32_t)f.v[db][0] | ((uint32_t)f.v[db][1] << 16);
+        u.y = (uint32_t)f.v[db][2] | ((uint32_t)f.v[db][3] << 16);
+        u.z = (uint32_t)f.v[db][4] | ((uint32_t)f.v[db][5] << 16);
+        u.w = (uint32_t)f.v[db][6] | ((uint32_t)f.v[db][7] << 16);
+        vf[db].v = __builtin_bit_cast(bf16x8, u);
+      }
+      if (r0 + 4 < nblk) ds_att_frags(kr, vr, kv_sc1, blk + 4, nblk, nk, ldkv, hd, f);
       f32x4 s[2];
 #pragma unroll
       for (int hb = 0; hb < 2; hb++) {
         s[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < DS_DP / 32; ds++) {
-          FragBF16 kf;
-          kf.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * 2));
-          mma32(s[hb], kf, qf[ds]);
-        }
+        for (int ds = 0; ds < DS_DP / 32; ds++) mma32(s[hb], kf[hb][ds], qf[ds]);
       }
       float bmax = -INFINITY;
 #pragma unroll
@@ -317,19 +338,32 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
 #pragma unroll
       for (int db = 0; db < DS_DP / 16; db++) {
         oacc[db] = oacc[db] * corr;
-        const char* vrow = sV + (db * 16 + qn) * VPITCH;
-        uint2 lo = *reinterpret_cast<const uint2*>(vrow + (grp * 4) * 2);
-        uint2 hi = *reinterpret_cast<const uint2*>(vrow + (16 + grp * 4) * 2);
-        FragBF16 vf;
-        vf.v = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        mma32(oacc[db], vf, pf);
+        mma32(oacc[db], vf[db], pf);
       }
     }
   }
-  // combine the four waves: per query (max, sum) and O^T partials in LDS
   float lsum = lrun;
   lsum += __shfl_xor(lsum, 16, WAVE);
   lsum += __shfl_xor(lsum, 32, WAVE);
+  if (nblk <= 1) {
+    // one block: wave 0 holds the whole result, O^T[d][q] with d = 16 db +
+    // 4 g + i in lane (q, g)
+    if (wave == 0 && qn < nq) {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+      for (int db = 0; db < DS_DP / 16; db++) {
+        const int d = db * 16 + grp * 4;
+        if (d < hd) {
+          uint2 pk;
+          pk.x = pack_bf2(oacc[db][0] * inv, oacc[db][1] * inv);
+          pk.y = pack_bf2(oacc[db][2] * inv, oacc[db][3] * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(qn * ldo + d) * 2u, 0, CP_SC1);
+        }
+      }
+    }
+    return;
+  }
+  // combine the four waves: per query (max, sum) and O^T partials in LDS
   float* sml = reinterpret_cast<float*>(lds_o);                  // [4][16][2]
   float* so = sml + 4 * 16 * 2;                                  // [4][16][DP]
   __syncthreads();
@@ -349,10 +383,10 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < 4; w++) {
-      float f = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
-      L += f * sml[(w * 16 + q) * 2 + 1];
+      float fw = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
+      L += fw * sml[(w * 16 + q) * 2 + 1];
       float4 o = *reinterpret_cast<const float4*>(so + (w * 16 + q) * DS_DP + d);
-      acc.x += f * o.x; acc.y += f * o.y; acc.z += f * o.z; acc.w += f * o.w;
+      acc.x += fw * o.x; acc.y += fw * o.y; acc.z += fw * o.z; acc.w += fw * o.w;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint2 pk;
@@ -363,32 +397,35 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
 }
 
 // ---------------------------------------------------------------- the layer kernel
-// LDS: [region X: attention staging or a norm's shift / scale] [region A:
-// bf16 A operand (16 x D) or attention partials]
-// [4 x 256 fp32 wave sums] [flags]
-__host__ __device__ constexpr int ds_region_x(int) { return 4 * (DS_KB * (DS_DP * 2 + 16) + DS_DP * (DS_KB * 2 + 16)); }
+// LDS: [region A: bf16 A operand (16 x D, 16 x 2D for DOWN) or attention
+// partials] [4 waves x 2 blocks x 256 fp32 wave sums] [flags]
 __host__ __device__ constexpr int ds_region_a(int D) {
-  return (16 * (2 * D + 16) > (4 * 16 * 2 + 4 * 16 * DS_DP) * 4) ? 16 * (2 * D + 16) : (4 * 16 * 2 + 4 * 16 * DS_DP) * 4;
+  return (16 * (4 * D + 16) > (4 * 16 * 2 + 4 * 16 * DS_DP) * 4) ? 16 * (4 * D + 16) : (4 * 16 * 2 + 4 * 16 * DS_DP) * 4;
 }
-__host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_x(D) + ds_region_a(D) + 4 * 256 * 4 + 64; }
+__host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_a(D) + 2 * 4 * 256 * 4 + 64; }
 
 // One phase of the layer for this workgroup, specialised per phase so that
 // each phase's registers are allocated for that phase alone. False when the
 // workgroup must leave the kernel (a wait timed out).
 template <typename WT, int D, int PH>
-__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rX, char* rA, float* red, int* sflag, int& finished_tiles) {
+__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float* red, int* sflag, int& finished_tiles) {
   using WR = typename DsW<WT>::raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x, G = gridDim.x;
   const int n = a.n;
   constexpr int APITCH = D * 2 + 16;
   constexpr int ntile = D / 16;
-  constexpr int KSTEPS = D / 32;                     // 32-wide k-steps of a unit (every unit spans D)
-  constexpr int NSW = (KSTEPS + 3) / 4;              // of them per wave
+  // unit geometry: NB column blocks of 16 over a k extent KW (a unit of UP
+  // or DOWN fills all weight registers; the other GEMMs take up to two units)
+  constexpr int NB = PH == DP_UP ? 2 : 1;
+  constexpr int KW = PH == DP_DOWN ? 2 * D : D;
+  constexpr int KST = KW / 32;                       // 32-wide k-steps of a unit
+  constexpr int NSW = (KST + 3) / 4;                 // of them per wave
+  constexpr int MAXU = 2 * NB * NSW <= DS_WSLOTS ? 2 : 1;
   const int U = ds_units(a, PH);
   const int first = ((wg - ds_base(a, PH)) % G + G) % G;
   if (first >= U) return true;                       // no work in this phase
-  const int nu = min(DS_MAXU, (U - first + G - 1) / G);
+  const int nu = (U - first + G - 1) / G;           // at most MAXU (checked by the launcher)
   constexpr bool is_att = PH == DP_SAATT || PH == DP_CAATT;
 
   constexpr bool norm = PH == DP_QKV || PH == DP_CAQ || PH == DP_UP;
@@ -408,21 +445,21 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rX, char* 
   constexpr int KG = (D / 4 + 63) / 64;
 
   if constexpr (is_att) {
-    uint4 pkv[DS_SE], pvv[DS_SE];
-    const bool pre_kv = PH == DP_CAATT;
+    DsAttFr f;
+    constexpr bool pre_kv = PH == DP_CAATT;
     if (pre_kv)
-      ds_att_load(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), false, wave,
-                  (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, pkv, pvv);
+      ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), false, wave,
+                   (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, f);
     if (!wait_prev()) return false;
     // ---- one head per unit
     for (int j = 0; j < nu; j++) {
       const int hh = first + j * G;
       if (PH == DP_SAATT)
         ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D, true,
-                     a.ao + hh * a.hd, D, n, n, a.hd, a.scale_log2, rX, rA, pkv, pvv, false);
+                     a.ao + hh * a.hd, D, n, n, a.hd, a.scale_log2, rA, f, false);
       else
         ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc, false,
-                     a.ao + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rX, rA, pkv, pvv, pre_kv && j == 0);
+                     a.ao + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rA, f, pre_kv && j == 0);
     }
   } else {
     const int mi = PH == DP_QKV ? 0 : PH == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
@@ -438,8 +475,9 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rX, char* 
       }
     }
     WR wreg[DS_WSLOTS];
-    ds_load_unit<WT, 0, NSW, KSTEPS>(a, ds_unit(a, PH, first), wreg);
-    if (nu > 1) ds_load_unit<WT, DS_KSW, NSW, KSTEPS>(a, ds_unit(a, PH, first + G), wreg);
+    ds_load_unit<WT, 0, NB, NSW, KST>(a, ds_unit(a, PH, first), wreg);
+    if constexpr (MAXU > 1)
+      if (nu > 1) ds_load_unit<WT, NB * NSW, NB, NSW, KST>(a, ds_unit(a, PH, first + G), wreg);
     if (!wait_prev()) return false;
     // ---- the A operand [16][D] (bf16) in region A
     if constexpr (norm) {
@@ -507,78 +545,88 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rX, char* 
     int staged_k0 = -1;
     auto unit = [&](int j) {
       const DsUnit d = ds_unit(a, PH, first + j * G);
-      constexpr int apitch = APITCH;
+      constexpr int apitch = KW * 2 + 16;
       if (!norm && d.k0 != staged_k0) {
         // bf16 activations: ao (SAO, CAO) or the unit's slice of h (DOWN)
         const uint16_t* src = PH == DP_DOWN ? a.h : a.ao;
         const int lds = PH == DP_DOWN ? a.mlp : D;
         const brsrc sr = make_brsrc(src);
-        constexpr int AS = (16 * D / 8 + DS_THREADS - 1) / DS_THREADS;   // 16-byte groups per thread
+        constexpr int AS = (16 * KW / 8 + DS_THREADS - 1) / DS_THREADS;   // 16-byte groups per thread
         uint4 av[AS];
 #pragma unroll
         for (int i = 0; i < AS; i++) {
           int e8 = tid + i * DS_THREADS;
-          int r = (e8 * 8) / D, c = (e8 * 8) % D;
-          av[i] = bload16<CP_SC1>(sr, (e8 < 16 * D / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
+          int r = (e8 * 8) / KW, c = (e8 * 8) % KW;
+          av[i] = bload16<CP_SC1>(sr, (e8 < 16 * KW / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < AS; i++) {
           int e8 = tid + i * DS_THREADS;
-          int r = (e8 * 8) / D, c = (e8 * 8) % D;
-          if (e8 < 16 * D / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
+          int r = (e8 * 8) / KW, c = (e8 * 8) % KW;
+          if (e8 < 16 * KW / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
         }
         staged_k0 = d.k0;
       }
       __syncthreads();
-      // ---- 16 x 16 tile: wave w covers k-steps w, w + 4, ...
-      f32x4 acc = j == 0 ? ds_mma<WT, 0, NSW, KSTEPS>(rA, apitch, wreg) : ds_mma<WT, DS_KSW, NSW, KSTEPS>(rA, apitch, wreg);
+      // ---- NB 16 x 16 tiles: wave w covers k-steps w, w + 4, ...
+      f32x4 acc[NB];
+      if (j == 0) ds_mma<WT, 0, NB, NSW, KST>(rA, apitch, wreg, acc);
+      else if constexpr (MAXU > 1) ds_mma<WT, NB * NSW, NB, NSW, KST>(rA, apitch, wreg, acc);
 #pragma unroll
-      for (int i = 0; i < 4; i++) red[wave * 256 + ((lane >> 4) * 4 + i) * 16 + (lane & 15)] = acc[i];
+      for (int b = 0; b < NB; b++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) red[(wave * NB + b) * 256 + ((lane >> 4) * 4 + i) * 16 + (lane & 15)] = acc[b][i];
       __syncthreads();
-      // ---- epilogue: thread = (row tid / 16, column tid % 16)
-      const int r = tid >> 4, cc = tid & 15, col = d.n0 + cc;
-      float v = red[tid] + red[256 + tid] + red[512 + tid] + red[768 + tid];
-      const float* ws = a.s[d.wi];
-      if (ws) v *= ws[col];
-      if (PH == DP_DOWN) {
-        // publish this slice's partial; the tile's last slice sums them in slice order
-        const int tile = d.n0 / 16, slice = d.k0 / d.kw, nsl = a.mlp / d.kw;
-        st_sc1_f32(a.part + ((size_t)slice * ntile + tile) * 256 + tid, v);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) {
-          unsigned old = __hip_atomic_fetch_add(a.cnt + DS_TILE0 + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          sflag[1] = old == (unsigned)(nsl - 1);
+      // ---- epilogue: thread = (row tid / 16, column tid % 16 of each block)
+      const int r = tid >> 4, cc = tid & 15;
+#pragma unroll
+      for (int b = 0; b < NB; b++) {
+        const int col = d.n0 + b * 16 + cc;
+        float v = red[(0 * NB + b) * 256 + tid] + red[(1 * NB + b) * 256 + tid] + red[(2 * NB + b) * 256 + tid] +
+                  red[(3 * NB + b) * 256 + tid];
+        const float* ws = a.s[d.wi];
+        if (ws) v *= ws[col];
+        if (PH == DP_DOWN) {
+          // publish this slice's partial; the tile's last slice sums them in slice order
+          const int tile = d.n0 / 16, slice = d.k0 / KW, nsl = a.mlp / KW;
+          st_sc1_f32(a.part + ((size_t)slice * ntile + tile) * 256 + tid, v);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (tid == 0) {
+            unsigned old = __hip_atomic_fetch_add(a.cnt + DS_TILE0 + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sflag[1] = old == (unsigned)(nsl - 1);
+          }
+          __syncthreads();
+          if (!sflag[1]) return;
+          const brsrc pr = make_brsrc(a.part);
+          float sum = 0.f;
+          for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
+          v = sum;
+          if (tid == 0) a.cnt[DS_TILE0 + tile] = 0u;
+          finished_tiles++;
         }
-        __syncthreads();
-        if (!sflag[1]) return;
-        const brsrc pr = make_brsrc(a.part);
-        float sum = 0.f;
-        for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
-        v = sum;
-        if (tid == 0) a.cnt[DS_TILE0 + tile] = 0u;
-        finished_tiles++;
-      }
-      v += a.b[d.wi][col];
-      if (PH == DP_QKV || PH == DP_CAQ || PH == DP_UP) {
-        if (PH == DP_UP) v = gelu_erf(v);
-        uint16_t* out = PH == DP_QKV ? a.qkv : PH == DP_CAQ ? a.q : a.h;
-        const int ldo = PH == DP_QKV ? 3 * D : PH == DP_CAQ ? D : a.mlp;
-        if (r < n && col < d.N) st_sc1_u16(make_brsrc(out), (uint32_t)(r * ldo + col), f2bf(v));
-      } else {
-        // gated residual: x += gate * v
-        const int gi = PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8;
-        if (r < n) {
-          const float* xs = PH == DP_SAO ? a.x_in : PH == DP_CAO ? a.x1 : a.x2;
-          float* xd = PH == DP_SAO ? a.x1 : PH == DP_CAO ? a.x2 : a.x_out;
-          float xo = bloadf(make_brsrc(xs), (uint32_t)(r * D + col) * 4u);
-          st_sc1_f32(xd + (size_t)r * D + col, xo + a.mod[(size_t)gi * D + col] * v);
+        v += a.b[d.wi][col];
+        if (PH == DP_QKV || PH == DP_CAQ || PH == DP_UP) {
+          if (PH == DP_UP) v = gelu_erf(v);
+          uint16_t* out = PH == DP_QKV ? a.qkv : PH == DP_CAQ ? a.q : a.h;
+          const int ldo = PH == DP_QKV ? 3 * D : PH == DP_CAQ ? D : a.mlp;
+          if (r < n && col < d.N) st_sc1_u16(make_brsrc(out), (uint32_t)(r * ldo + col), f2bf(v));
+        } else {
+          // gated residual: x += gate * v
+          const int gi = PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8;
+          if (r < n) {
+            const float* xs = PH == DP_SAO ? a.x_in : PH == DP_CAO ? a.x1 : a.x2;
+            float* xd = PH == DP_SAO ? a.x1 : PH == DP_CAO ? a.x2 : a.x_out;
+            float xo = bloadf(make_brsrc(xs), (uint32_t)(r * D + col) * 4u);
+            st_sc1_f32(xd + (size_t)r * D + col, xo + a.mod[(size_t)gi * D + col] * v);
+          }
         }
       }
     };
     unit(0);
-    if (nu > 1) unit(1);
+    if constexpr (MAXU > 1)
+      if (nu > 1) unit(1);
   }
   // ---- count this phase's finished units once every store has completed
   __builtin_amdgcn_s_waitcnt(0);
@@ -603,10 +651,9 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rX, char* 
 template <typename WT, int D>
 __global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
   extern __shared__ __align__(16) char smem[];
-  char* rX = smem;
-  char* rA = smem + ds_region_x(D);
+  char* rA = smem;
   float* red = reinterpret_cast<float*>(rA + ds_region_a(D));
-  int* sflag = reinterpret_cast<int*>(red + 4 * 256);
+  int* sflag = reinterpret_cast<int*>(red + 2 * 4 * 256);
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, G = gridDim.x;
   int finished_tiles = 0;        // DOWN tiles this workgroup completed
@@ -618,14 +665,14 @@ __global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
     for (int e = wg * DS_THREADS + tid; e < a.n * D; e += G * DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
     return;
   }
-  if (!ds_phase<WT, D, DP_QKV>(a, rX, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_SAATT>(a, rX, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_SAO>(a, rX, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_CAQ>(a, rX, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_CAATT>(a, rX, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_CAO>(a, rX, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_UP>(a, rX, rA, red, sflag, finished_tiles)) return;
-  ds_phase<WT, D, DP_DOWN>(a, rX, rA, red, sflag, finished_tiles);
+  if (!ds_phase<WT, D, DP_QKV>(a, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_SAATT>(a, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_SAO>(a, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_CAQ>(a, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_CAATT>(a, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_CAO>(a, rA, red, sflag, finished_tiles)) return;
+  if (!ds_phase<WT, D, DP_UP>(a, rA, red, sflag, finished_tiles)) return;
+  ds_phase<WT, D, DP_DOWN>(a, rA, red, sflag, finished_tiles);
 }
 
 }  // namespace vla
