@@ -137,6 +137,30 @@ __device__ __forceinline__ uint16_t bload2(brsrc r, uint32_t off) {
 }
 
 // ---------------------------------------------------------------- wave reductions
+// DPP lane moves within rows of 16 lanes (quad permutes and row rotations)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over each row of 16 lanes, in every lane of the row: swap neighbours,
+// swap pairs, then add the quads 4 and 8 lanes around the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);   // row_ror:4
+  v += dpp_f<0x128>(v);   // row_ror:8
+  return v;
+}
+// Sum over the whole wave (wave-uniform result): row sums, then the four
+// rows' sums read from lanes 0, 16, 32, 48 in that order.
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v = row16_sum(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);

@@ -117,10 +117,11 @@ __device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, 
     unsigned spins = 0;
     bool ok = true;
     while (true) {
+      static_assert(DS_NC == 16, "the phase counter slots are one DPP row");
       unsigned v = lane < DS_NC ? __hip_atomic_load(slots + lane * DS_CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-      if (v >= target) break;                      // uniform: every lane holds the sum
+      // exact: counts stay far below 2^24
+      const unsigned tot = (unsigned)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum((float)v)), 0));
+      if (tot >= target) break;                    // uniform: read from lane 0
       if (++spins >= DS_SPIN) { ok = false; break; }
       __builtin_amdgcn_s_sleep(2);
     }
@@ -502,9 +503,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         mean[rr] = s1;
       }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++) mean[rr] += __shfl_xor(mean[rr], o, WAVE);
+      for (int rr = 0; rr < 4; rr++) mean[rr] = wave_sum_rows(mean[rr]);
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
         mean[rr] *= 1.f / (float)D;
@@ -520,9 +519,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         rstd[rr] = s2;
       }
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++) rstd[rr] += __shfl_xor(rstd[rr], o, WAVE);
+      for (int rr = 0; rr < 4; rr++) rstd[rr] = wave_sum_rows(rstd[rr]);
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) rstd[rr] = rsqrtf(rstd[rr] * (1.f / (float)D) + a.eps);
 #pragma unroll
