@@ -600,7 +600,8 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
           float sum = 0.f;
           for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
           v = sum;
-          if (tid == 0) a.cnt[DS_TILE0 + tile] = 0u;
+          // device-scope store, like every other counter update
+          if (tid == 0) __hip_atomic_store(a.cnt + DS_TILE0 + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           finished_tiles++;
         }
         v += a.b[d.wi][col];
