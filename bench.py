@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import sys
 import time
@@ -31,15 +32,25 @@ WORKLOADS = {
 }
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def _strip_comments(text: str) -> str:
+    """C/C++ source without comments, trailing blanks or empty lines."""
+    code = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else "", text)
+    return "\n".join(ln.rstrip() for ln in code.splitlines() if ln.strip())
+
+
 def kernel_source_sha() -> str:
-    """Hash of the HIP sources (the counters of a profile hold for these only)."""
+    """Hash of the HIP sources' code (the counters of a profile hold for this
+    code only; comments do not enter the hash)."""
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "vla_robot_policy_amd", "csrc")
     for name in sorted(os.listdir(src)):
         if name.endswith((".h", ".hip", ".cpp")):
-            with open(os.path.join(src, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(src, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

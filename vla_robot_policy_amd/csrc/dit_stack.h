@@ -24,8 +24,11 @@
 // phase: the HBM latency of the next weights overlaps the current phase.
 // A phase is complete when its counter reaches the number of units (tiles
 // for DOWN). Producers write with device-coherent (sc1) stores, wait for
-// them, then count; consumers poll the counter and read with sc1 loads, so
-// the XCDs' private L2s need no write-back or invalidate. Every wait is
+// them, then count; consumers poll the counter and read the bf16
+// intermediates with sc1 loads, so the XCDs' private L2s need no write-back
+// or invalidate. The fp32 residual stream has one buffer per sublayer, each
+// written once per launch before any read, so it is read with ordinary
+// cached loads (no L2 can hold an older copy of it). Every wait is
 // bounded: on time-out the workgroup records an error, poisons its outputs
 // with NaN and leaves, so a fault can never hang the device. The workgroup
 // that completes the last DOWN tile resets the counters for the next launch.
