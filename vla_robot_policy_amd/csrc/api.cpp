@@ -155,15 +155,32 @@ struct GemmOp {
 // columns with 4 waves side by side. Wide tiles (RoPE pairs, gate/up pairs):
 // 128 columns with 8 waves side by side; compensated, 4 x 2 waves (column
 // blocks x k-steps) with two 16-column blocks per wave.
-void pick_tile(int M, int em, int ac, int& mb, int& wn, int& wk, int& nbw, int& u) {
+// Measured at the workloads' shapes (cold last-level cache, per launch):
+// 64-column tiles for 16-row GEMMs with very many columns (the adaLN
+// modulations: 166 vs 271 us with 16-column tiles), 128-column tiles for
+// taller ones (the cross-attention K/V: 82 vs 108 us), and two k-waves of
+// 32 columns with a two-way split for small residual GEMMs (the ViT output
+// projection: 12.0 vs 14.2 us).
+void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb, int& wn, int& wk, int& nbw, int& u,
+               int& split_hint) {
   bool wide = em == E_ROPE || em == E_SWIGLU;
   mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : (M <= 256 || (ac && !wide)) ? 4 : 8;
   u = ac ? 2 : 4;
   nbw = 1;
+  split_hint = 0;
+  const bool plain_store = em == E_STORE && am == A_BF16 && wdtype != VLA_F32;
   if (wide && ac) { wn = 4; wk = 2; nbw = 2; u = 1; }   // two column blocks per wave: half the A reads
   else if (wide) { wn = 8; wk = 1; }
-  else if (mb == 1) { wn = 1; wk = 4; }
+  else if (mb == 1) {
+    if (plain_store && N >= 16 * 1024) { wn = 4; wk = 1; }
+    else { wn = 1; wk = 4; }
+  }
   else if (ac) { wn = 4; wk = 2; }     // compensated residual GEMMs: two k-waves per column block
+  else if (plain_store && N >= 64 * 1024) { wn = 8; wk = 1; }
+  else if (em == E_RESID && am == A_BF16 && wdtype == VLA_BF16 && mb == 4 && M > 64 && K <= 1024 &&
+           ((N + 63) / 64) * ((M + 63) / 64) < 128) {
+    wn = 2; wk = 2; u = 2; split_hint = 2;
+  }
   else { wn = 4; wk = 1; }
 }
 
@@ -171,8 +188,8 @@ void pick_tile(int M, int em, int ac, int& mb, int& wn, int& wk, int& nbw, int& 
 // tiling of the row moments the kernel leaves in a.rs_out.
 vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return fail(VLA_ERR_SHAPE, "gemm: empty shape %d x %d x %d", a.M, a.N, a.K);
-  int mb, wn, wk, nbw, u;
-  pick_tile(a.M, op.em, op.ac, mb, wn, wk, nbw, u);
+  int mb, wn, wk, nbw, u, split_hint;
+  pick_tile(a.M, a.N, a.K, op.am, op.em, op.ac, op.wdtype, mb, wn, wk, nbw, u, split_hint);
   const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * wk * u;
   const int bn_out = op.em == E_SWIGLU ? BN / 2 : BN;
   a.n_tiles_n = (a.N + bn_out - 1) / bn_out;
@@ -190,7 +207,10 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   int split = std::max(1, (int)std::ceil(per_wg / (192.0 * 1024.0)));
   if (total >= 16.0 * 1024 * 1024 && tiles * split < 200) split = (200 + tiles - 1) / tiles;
   split = std::min(split, std::max(1, slots / tiles));
-  if (threads >= 512 && op.em == E_RESID) split = std::min(split, std::max(1, 160 / tiles));   // two-k-wave residual tiles
+  // two-k-wave residual tiles: up to 240 workgroups (the down projection at
+  // 104 rows: 39.8 us with 6 splits vs 48.4 us with 4)
+  if (threads >= 512 && op.em == E_RESID) split = std::min(split, std::max(1, 240 / tiles));
+  if (split_hint) split = split_hint;
   split = std::min(split, std::max(1, (a.K + BK - 1) / BK));
   split = std::min(split, SPLIT_MAX);
   int ksplit = (int)align_up((size_t)((a.K + split - 1) / split), (size_t)BK);

@@ -6,6 +6,8 @@
 namespace vla {
 bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out) {
   VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_STORE)
+  VLA_GEMM_CASE(uint8_t, __bf16, A_BF16, E_STORE, 1, 4, 1, 1)
+  VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_NORM, E_STORE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_ROPE)
