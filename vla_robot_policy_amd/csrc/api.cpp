@@ -267,6 +267,9 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
   if (a.Hkv <= 0 || a.Hq % a.Hkv != 0) return fail(VLA_ERR_SHAPE, "attention: %d query heads not a multiple of %d kv heads", a.Hq, a.Hkv);
   int dp = a.D <= 64 ? 64 : a.D <= 96 ? 96 : a.D <= 128 ? 128 : 0;
   if (dp == 0 || a.D % 8 != 0) return fail(VLA_ERR_SHAPE, "attention: head_dim %d unsupported", a.D);
+  // 8-element loads of q, k, v rows and 4-element stores of o rows
+  if (a.ldq % 8 || a.ldk % 8 || a.ldv % 8 || a.ldo % 4)
+    return fail(VLA_ERR_SHAPE, "attention: row pitches %d/%d/%d/%d not multiples of 8/8/8/4", a.ldq, a.ldk, a.ldv, a.ldo);
   int group = a.Hq / a.Hkv;
   int hpw = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
   KernelRef k{};
@@ -275,7 +278,8 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
   int nrb = (a.Sq + 16 * rb - 1) / (16 * rb);
   int grid = a.Hkv * (group / hpw) * nrb;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)a.D));
-  return launch(c, k.fn, dim3(grid), dim3(256), 0, {arg(a)});
+  if (!c.plan && k.smem > 64 * 1024) VLA_TRY(allow_smem(k));
+  return launch(c, k.fn, dim3(grid), dim3(256), (size_t)k.smem, {arg(a)});
 }
 
 vla_status stage_rows(Ctx& c, float* x, int ldx, int M, int N, const void* src, int src_f32, int ld_src, int r0, int r1,

@@ -1,7 +1,10 @@
 // Flash attention (online softmax) for GQA / MHA, causal or full, on MFMA.
 //
 // Each wave owns 16 query rows of one query head and walks the keys in
-// blocks of 32 staged in LDS (K row-major, V transposed). The scores are
+// blocks of 32 staged in LDS (K row-major, V transposed), several blocks per
+// stage: a stage's K and V are requested at once (one memory latency for
+// all of them) and the next stage is requested before the current one is
+// computed. The scores are
 // computed transposed, S^T = K Q^T, so a lane holds 8 keys of a single query:
 // the running max / sum of that query live in the lane (plus a 4-way
 // exchange across lane groups), and the exponentiated scores are already in
@@ -27,50 +30,51 @@ template <typename CT> struct ATraits;
 template <> struct ATraits<__bf16> {
   using F = FragBF16;
   static constexpr int ESZ = 2;
+  using raw = uint4;                                   // 8 elements
+  __device__ static raw rload8(brsrc r, uint32_t elem, bool ok) { return bload16(r, ok ? elem * 2u : BUF_OOB); }
+  __device__ static void rstore8(char* dst, const raw& v) { *reinterpret_cast<uint4*>(dst) = v; }
+  __device__ static void rput(char* dst, const raw& v, int t) {
+    const uint32_t word = (t >> 1) == 0 ? v.x : (t >> 1) == 1 ? v.y : (t >> 1) == 2 ? v.z : v.w;
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(t & 1 ? word >> 16 : word);
+  }
   __device__ static F gload(const void* base, size_t off) {
     F f; f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>((const uint16_t*)base + off)); return f;
   }
-  __device__ static void lstore8(char* dst, const void* base, size_t off) {
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>((const uint16_t*)base + off);
-  }
-  __device__ static void lzero8(char* dst) { *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0); }
-  __device__ static float get(const void* base, size_t off) { return bf2f(((const uint16_t*)base)[off]); }
-  __device__ static void lput(char* dst, float v) { *reinterpret_cast<uint16_t*>(dst) = f2bf(v); }
-  __device__ static void lput_raw(char* dst, const void* base, size_t off) {
-    *reinterpret_cast<uint16_t*>(dst) = ((const uint16_t*)base)[off];
-  }
-  __device__ static void lzero1(char* dst) { *reinterpret_cast<uint16_t*>(dst) = 0; }
   __device__ static F lfrag(const char* p) { F f; f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); return f; }
   // V^T fragment: keys {4g..4g+3} at p0 and {16+4g..} at p1 (4 elements each)
   __device__ static F lfrag2(const char* p0, const char* p1) {
     uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
     F f; f.v = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y)); return f;
   }
-  __device__ static void store(void* base, size_t off, float v) { ((uint16_t*)base)[off] = f2bf(v); }
+  __device__ static void store4(void* base, size_t off, float a, float b, float c, float d) {
+    uint2 u; u.x = pack_bf2(a, b); u.y = pack_bf2(c, d);
+    *reinterpret_cast<uint2*>((uint16_t*)base + off) = u;
+  }
 };
 template <> struct ATraits<float> {
   using F = FragF32;
   static constexpr int ESZ = 4;
+  struct raw { float4 a, b; };                         // 8 elements
+  __device__ static raw rload8(brsrc r, uint32_t elem, bool ok) {
+    raw v;
+    v.a = as_f4(bload16(r, ok ? elem * 4u : BUF_OOB));
+    v.b = as_f4(bload16(r, ok ? elem * 4u + 16u : BUF_OOB));
+    return v;
+  }
+  __device__ static void rstore8(char* dst, const raw& v) {
+    reinterpret_cast<float4*>(dst)[0] = v.a;
+    reinterpret_cast<float4*>(dst)[1] = v.b;
+  }
+  __device__ static void rput(char* dst, const raw& v, int t) {
+    const float e = t < 4 ? (t == 0 ? v.a.x : t == 1 ? v.a.y : t == 2 ? v.a.z : v.a.w)
+                          : (t == 4 ? v.b.x : t == 5 ? v.b.y : t == 6 ? v.b.z : v.b.w);
+    *reinterpret_cast<float*>(dst) = e;
+  }
   __device__ static F gload(const void* base, size_t off) {
     const float4* p = reinterpret_cast<const float4*>((const float*)base + off);
     float4 a = p[0], b = p[1];
     F f; f.lo = (f32x4){a.x, a.y, a.z, a.w}; f.hi = (f32x4){b.x, b.y, b.z, b.w}; return f;
   }
-  __device__ static void lstore8(char* dst, const void* base, size_t off) {
-    const float4* p = reinterpret_cast<const float4*>((const float*)base + off);
-    reinterpret_cast<float4*>(dst)[0] = p[0];
-    reinterpret_cast<float4*>(dst)[1] = p[1];
-  }
-  __device__ static void lzero8(char* dst) {
-    reinterpret_cast<float4*>(dst)[0] = make_float4(0, 0, 0, 0);
-    reinterpret_cast<float4*>(dst)[1] = make_float4(0, 0, 0, 0);
-  }
-  __device__ static float get(const void* base, size_t off) { return ((const float*)base)[off]; }
-  __device__ static void lput(char* dst, float v) { *reinterpret_cast<float*>(dst) = v; }
-  __device__ static void lput_raw(char* dst, const void* base, size_t off) {
-    *reinterpret_cast<float*>(dst) = ((const float*)base)[off];
-  }
-  __device__ static void lzero1(char* dst) { *reinterpret_cast<float*>(dst) = 0.f; }
   __device__ static F lfrag(const char* p) {
     float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
     F f; f.lo = (f32x4){a.x, a.y, a.z, a.w}; f.hi = (f32x4){b.x, b.y, b.z, b.w}; return f;
@@ -79,7 +83,24 @@ template <> struct ATraits<float> {
     float4 a = *reinterpret_cast<const float4*>(p0), b = *reinterpret_cast<const float4*>(p1);
     F f; f.lo = (f32x4){a.x, a.y, a.z, a.w}; f.hi = (f32x4){b.x, b.y, b.z, b.w}; return f;
   }
-  __device__ static void store(void* base, size_t off, float v) { ((float*)base)[off] = v; }
+  __device__ static void store4(void* base, size_t off, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>((float*)base + off) = make_float4(a, b, c, d);
+  }
+};
+
+// Blocks of 32 keys staged per round: LDS holds one stage (K [32][DP] and
+// V^T [DP][32] per block, padded rows), registers the next one.
+template <typename CT, int DP>
+struct AttnStage {
+  static constexpr int ESZ = ATraits<CT>::ESZ;
+  static constexpr int KB = 32;
+  static constexpr int KPITCH = DP * ESZ + 16;       // K row pitch (bytes)
+  static constexpr int VPITCH = KB * ESZ + 16;       // V^T row pitch (bytes)
+  static constexpr int KBYTES = KB * KPITCH, VBYTES = DP * VPITCH;
+  static constexpr int NBUF = ESZ == 2 ? 4 : 2;      // blocks per stage
+  static constexpr int GROUPS = KB * (DP / 8);        // 8-element groups per block (K, and V)
+  static constexpr int GPB = (GROUPS + 255) / 256;    // of them per thread
+  static constexpr int SMEM = NBUF * (KBYTES + VBYTES);
 };
 
 // DP: head dim padded to a multiple of 32 (64, 96, 128). HPW: query heads per
@@ -88,13 +109,15 @@ template <typename CT, int DP, int HPW>
 __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   using TR = ATraits<CT>;
   using F = typename TR::F;
+  using ST = AttnStage<CT, DP>;
+  using RAW = typename TR::raw;
   constexpr int ESZ = TR::ESZ;
   constexpr int RB = 4 / HPW;                // 16-row blocks per workgroup
-  constexpr int KB = 32;                     // keys per block
-  constexpr int KPITCH = DP * ESZ + 16;      // K tile row pitch (bytes)
-  constexpr int VPITCH = KB * ESZ + 16;      // V^T tile row pitch (bytes)
-  __shared__ __align__(16) char sK[KB * KPITCH];
-  __shared__ __align__(16) char sV[DP * VPITCH];
+  constexpr int KB = ST::KB, NBUF = ST::NBUF, GPB = ST::GPB;
+  constexpr int KPITCH = ST::KPITCH, VPITCH = ST::VPITCH;
+  extern __shared__ __align__(16) char smem[];
+  char* sK = smem;                            // [NBUF][KB][KPITCH]
+  char* sV = smem + NBUF * ST::KBYTES;        // [NBUF][DP][VPITCH]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int group = p.Hq / p.Hkv;
@@ -109,6 +132,39 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   const int wg_row_end = min(p.Sq, (rb + 1) * RB * 16);
   const int qn = lane & 15, grp = lane >> 4;
   const int qrow = row0 + qn;
+  const int kend = p.causal ? min(p.Sk, wg_row_end) : p.Sk;
+
+  // K / V of one stage (NBUF blocks from key kb0) into registers: thread
+  // group e = tid + i * 256 of a block is key e % 32, dims (e / 32) * 8, so
+  // that a wave's LDS writes (K rows, V^T columns) fall in distinct banks
+  const brsrc kr = make_brsrc(p.k), vr = make_brsrc(p.v);
+  RAW rk[NBUF][GPB], rv[NBUF][GPB];
+  auto load_stage = [&](int kb0) {
+#pragma unroll
+    for (int b = 0; b < NBUF; b++)
+#pragma unroll
+      for (int i = 0; i < GPB; i++) {
+        const int e = tid + i * 256, key = e % KB, d8 = (e / KB) * 8;
+        const int j = kb0 + b * KB + key;
+        const bool ok = e < ST::GROUPS && j < kend && d8 < p.D;
+        rk[b][i] = TR::rload8(kr, (uint32_t)j * p.ldk + (uint32_t)g * p.D + d8, ok);
+        rv[b][i] = TR::rload8(vr, (uint32_t)j * p.ldv + (uint32_t)g * p.D + d8, ok);
+      }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int b = 0; b < NBUF; b++)
+#pragma unroll
+      for (int i = 0; i < GPB; i++) {
+        const int e = tid + i * 256, key = e % KB, d8 = (e / KB) * 8;
+        if (e >= ST::GROUPS) continue;
+        TR::rstore8(sK + b * ST::KBYTES + key * KPITCH + d8 * ESZ, rk[b][i]);
+        char* vd = sV + b * ST::VBYTES + key * ESZ;
+#pragma unroll
+        for (int t = 0; t < 8; t++) TR::rput(vd + (d8 + t) * VPITCH, rv[b][i], t);
+      }
+  };
+  load_stage(0);
 
   // Q^T fragments (B operand): query qn, dims ds*32 + grp*8 .. +8
   F qf[DP / 32];
@@ -124,84 +180,77 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   for (int i = 0; i < DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  const int kend = p.causal ? min(p.Sk, wg_row_end) : p.Sk;
-  for (int kb = 0; kb < kend; kb += KB) {
+  for (int kb0 = 0; kb0 < kend; kb0 += NBUF * KB) {
+    __syncthreads();                          // the previous stage's readers are done
+    store_stage();
     __syncthreads();
-    // stage K [32][DP] and V^T [DP][32] of kv head g
-    for (int e = tid; e < KB * (DP / 8); e += 256) {
-      int key = e / (DP / 8), d8 = (e % (DP / 8)) * 8;
-      int j = kb + key;
-      char* kd = sK + key * KPITCH + d8 * ESZ;
-      if (j < p.Sk && d8 < p.D) {
-        TR::lstore8(kd, p.k, (size_t)j * p.ldk + (size_t)g * p.D + d8);
-        size_t vo = (size_t)j * p.ldv + (size_t)g * p.D + d8;
+    if (kb0 + NBUF * KB < kend) load_stage(kb0 + NBUF * KB);   // next stage in flight
 #pragma unroll
-        for (int t = 0; t < 8; t++) TR::lput_raw(sV + (d8 + t) * VPITCH + key * ESZ, p.v, vo + t);
-      } else {
-        TR::lzero8(kd);
+    for (int b = 0; b < NBUF; b++) {
+      const int kb = kb0 + b * KB;
+      if (kb >= kend) break;
+      const char* bK = sK + b * ST::KBYTES;
+      const char* bV = sV + b * ST::VBYTES;
+      // S^T for keys kb + hb*16 + 4*grp + i, query qn
+      f32x4 s[2];
 #pragma unroll
-        for (int t = 0; t < 8; t++) TR::lzero1(sV + (d8 + t) * VPITCH + key * ESZ);
+      for (int hb = 0; hb < 2; hb++) {
+        s[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DP / 32; ds++) {
+          F kf = TR::lfrag(bK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * ESZ);
+          mma32(s[hb], kf, qf[ds]);
+        }
       }
-    }
-    __syncthreads();
-    // S^T for keys kb + hb*16 + 4*grp + i, query qn
-    f32x4 s[2];
+      float bmax = -INFINITY;
 #pragma unroll
-    for (int hb = 0; hb < 2; hb++) {
-      s[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < 2; hb++)
 #pragma unroll
-      for (int ds = 0; ds < DP / 32; ds++) {
-        F kf = TR::lfrag(sK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * ESZ);
-        mma32(s[hb], kf, qf[ds]);
-      }
-    }
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int hb = 0; hb < 2; hb++)
+        for (int i = 0; i < 4; i++) {
+          int j = kb + hb * 16 + grp * 4 + i;
+          bool ok = j < p.Sk && (!p.causal || j <= qrow);
+          float v = ok ? s[hb][i] * p.scale_log2 : -INFINITY;
+          s[hb][i] = v;
+          bmax = fmaxf(bmax, v);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, WAVE));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, WAVE));
+      float mnew = fmaxf(mrun, bmax);
+      float corr = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      float pv[8];
+      float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        int j = kb + hb * 16 + grp * 4 + i;
-        bool ok = j < p.Sk && (!p.causal || j <= qrow);
-        float v = ok ? s[hb][i] * p.scale_log2 : -INFINITY;
-        s[hb][i] = v;
-        bmax = fmaxf(bmax, v);
+        pv[i] = (mnew == -INFINITY) ? 0.f : exp2f(s[0][i] - mnew);
+        pv[4 + i] = (mnew == -INFINITY) ? 0.f : exp2f(s[1][i] - mnew);
+        psum += pv[i] + pv[4 + i];
       }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, WAVE));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, WAVE));
-    float mnew = fmaxf(mrun, bmax);
-    float corr = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
-    float pv[8];
-    float psum = 0.f;
+      lrun = lrun * corr + psum;
+      mrun = mnew;
+      F pf;
+      frag_from_floats(pf, pv);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      pv[i] = (mnew == -INFINITY) ? 0.f : exp2f(s[0][i] - mnew);
-      pv[4 + i] = (mnew == -INFINITY) ? 0.f : exp2f(s[1][i] - mnew);
-      psum += pv[i] + pv[4 + i];
-    }
-    lrun = lrun * corr + psum;
-    mrun = mnew;
-    F pf;
-    frag_from_floats(pf, pv);
-#pragma unroll
-    for (int db = 0; db < DP / 16; db++) {
-      oacc[db] = oacc[db] * corr;
-      const char* vr = sV + (db * 16 + qn) * VPITCH;
-      F vf = TR::lfrag2(vr + (grp * 4) * ESZ, vr + (16 + grp * 4) * ESZ);
-      mma32(oacc[db], vf, pf);
+      for (int db = 0; db < DP / 16; db++) {
+        oacc[db] = oacc[db] * corr;
+        const char* vrow = bV + (db * 16 + qn) * VPITCH;
+        F vf = TR::lfrag2(vrow + (grp * 4) * ESZ, vrow + (16 + grp * 4) * ESZ);
+        mma32(oacc[db], vf, pf);
+      }
     }
   }
   float lsum = lrun;
   lsum += __shfl_xor(lsum, 16, WAVE);
   lsum += __shfl_xor(lsum, 32, WAVE);
   float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // O^T[d][q]: the lane's 4 consecutive dims d = 16 db + 4 grp + i of query qrow
   if (qrow < p.Sq) {
 #pragma unroll
-    for (int db = 0; db < DP / 16; db++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        int d = db * 16 + grp * 4 + i;
-        if (d < p.D) TR::store(p.o, (size_t)qrow * p.ldo + (size_t)head * p.D + d, oacc[db][i] * inv);
-      }
+    for (int db = 0; db < DP / 16; db++) {
+      const int d = db * 16 + grp * 4;
+      if (d < p.D)
+        TR::store4(p.o, (size_t)qrow * p.ldo + (size_t)head * p.D + d, oacc[db][0] * inv, oacc[db][1] * inv,
+                   oacc[db][2] * inv, oacc[db][3] * inv);
+    }
   }
 }
 

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void k_convert_rows(const float* x, int ldx, i
 #define VLA_ATTN_CASE(CT, F32V, DPV, HPWV)          \
   if (f32 == F32V && dp == DPV && hpw == HPWV) {    \
     out->fn = (const void*)&k_attention<CT, DPV, HPWV>; \
-    out->smem = 0; out->threads = 256;              \
+    out->smem = AttnStage<CT, DPV>::SMEM; out->threads = 256; \
     return true;                                    \
   }
 
