@@ -59,20 +59,30 @@ __global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, in
 __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
   __shared__ float2 snc;
   const int r = blockIdx.x, tid = threadIdx.x;
+  const float* xr = p.x + (size_t)r * p.ldx;
+  // the row's first 4096 values (and their gain / shift) are requested
+  // before the row moments, so both share one memory latency
+  constexpr int PRE = 4;
+  float4 v[PRE], g[PRE], b[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; i++) {
+    const int k = tid * 4 + i * 1024;
+    const bool ok = k < p.K;
+    v[i] = ok ? *reinterpret_cast<const float4*>(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    g[i] = ok && p.g ? *reinterpret_cast<const float4*>(p.g + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    b[i] = ok && p.bsh ? *reinterpret_cast<const float4*>(p.bsh + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (tid < 64) {
     float2 nc = norm_coeffs(row_moments_wave(p.rs, r), p.rms, p.eps);
     if (tid == 0) snc = nc;
   }
   __syncthreads();
   const float2 nc = snc;
-  const float* xr = p.x + (size_t)r * p.ldx;
-  for (int k = tid * 4; k < p.K; k += 1024) {
-    float4 v = *reinterpret_cast<const float4*>(xr + k);
-    float4 g = p.g ? *reinterpret_cast<const float4*>(p.g + k) : make_float4(1.f, 1.f, 1.f, 1.f);
-    if (p.g && p.g_plus_one) { g.x += 1.f; g.y += 1.f; g.z += 1.f; g.w += 1.f; }
-    float4 b = p.bsh ? *reinterpret_cast<const float4*>(p.bsh + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float u0 = (v.x - nc.x) * nc.y * g.x + b.x, u1 = (v.y - nc.x) * nc.y * g.y + b.y;
-    float u2 = (v.z - nc.x) * nc.y * g.z + b.z, u3 = (v.w - nc.x) * nc.y * g.w + b.w;
+  auto put = [&](int k, float4 x, float4 gg, float4 bb) {
+    if (!p.g) gg = make_float4(1.f, 1.f, 1.f, 1.f);
+    else if (p.g_plus_one) { gg.x += 1.f; gg.y += 1.f; gg.z += 1.f; gg.w += 1.f; }
+    const float u0 = (x.x - nc.x) * nc.y * gg.x + bb.x, u1 = (x.y - nc.x) * nc.y * gg.y + bb.y;
+    const float u2 = (x.z - nc.x) * nc.y * gg.z + bb.z, u3 = (x.w - nc.x) * nc.y * gg.w + bb.w;
     uint2 h;
     h.x = pack_bf2(u0, u1);
     h.y = pack_bf2(u2, u3);
@@ -83,6 +93,17 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
       l.y = pack_bf2(u2 - bf2f(f2bf(u2)), u3 - bf2f(f2bf(u3)));
       *reinterpret_cast<uint2*>(p.out_lo + (size_t)r * p.ldo + k) = l;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < PRE; i++) {
+    const int k = tid * 4 + i * 1024;
+    if (k < p.K) put(k, v[i], g[i], b[i]);
+  }
+  for (int k = tid * 4 + PRE * 1024; k < p.K; k += 1024) {
+    const float4 x = *reinterpret_cast<const float4*>(xr + k);
+    const float4 gg = p.g ? *reinterpret_cast<const float4*>(p.g + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 bb = p.bsh ? *reinterpret_cast<const float4*>(p.bsh + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    put(k, x, gg, bb);
   }
 }
 
