@@ -410,9 +410,13 @@ __host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_a(D) +
 
 // One phase of the layer for this workgroup, specialised per phase so that
 // each phase's registers are allocated for that phase alone. False when the
-// workgroup must leave the kernel (a wait timed out).
+// workgroup must leave the kernel (a wait timed out). `wdown` holds the
+// workgroup's DOWN unit: a workgroup that also has an UP unit requests it
+// together with the UP weights (it is idle long before UP starts), so its
+// DOWN phase does not begin with a weight fetch queued ahead of its wait.
 template <typename WT, int D, int PH>
-__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float* red, int* sflag, int& finished_tiles) {
+__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float* red, int* sflag, int& finished_tiles,
+                                         typename DsW<WT>::raw (&wdown)[DS_WSLOTS], bool& have_down) {
   using WR = typename DsW<WT>::raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x, G = gridDim.x;
@@ -479,9 +483,23 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       }
     }
     WR wreg[DS_WSLOTS];
-    ds_load_unit<WT, 0, NB, NSW, KST>(a, ds_unit(a, PH, first), wreg);
-    if constexpr (MAXU > 1)
-      if (nu > 1) ds_load_unit<WT, NB * NSW, NB, NSW, KST>(a, ds_unit(a, PH, first + G), wreg);
+    auto& wuse = [&]() -> WR (&)[DS_WSLOTS] {
+      if constexpr (PH == DP_DOWN) return wdown;
+      else return wreg;
+    }();
+    if (!(PH == DP_DOWN && have_down)) {
+      ds_load_unit<WT, 0, NB, NSW, KST>(a, ds_unit(a, PH, first), wuse);
+      if constexpr (MAXU > 1)
+        if (nu > 1) ds_load_unit<WT, NB * NSW, NB, NSW, KST>(a, ds_unit(a, PH, first + G), wuse);
+    }
+    if constexpr (PH == DP_UP) {
+      const int fd = ((wg - ds_base(a, DP_DOWN)) % G + G) % G;
+      if (fd < ds_units(a, DP_DOWN)) {
+        constexpr int KSTD = 2 * D / 32, NSWD = (KSTD + 3) / 4;
+        ds_load_unit<WT, 0, 1, NSWD, KSTD>(a, ds_unit(a, DP_DOWN, fd), wdown);
+        have_down = true;
+      }
+    }
     if (!wait_prev()) return false;
     // ---- the A operand [16][D] (bf16) in region A
     if constexpr (norm) {
@@ -571,8 +589,8 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       __syncthreads();
       // ---- NB 16 x 16 tiles: wave w covers k-steps w, w + 4, ...
       f32x4 acc[NB];
-      if (j == 0) ds_mma<WT, 0, NB, NSW, KST>(rA, apitch, wreg, acc);
-      else if constexpr (MAXU > 1) ds_mma<WT, NB * NSW, NB, NSW, KST>(rA, apitch, wreg, acc);
+      if (j == 0) ds_mma<WT, 0, NB, NSW, KST>(rA, apitch, wuse, acc);
+      else if constexpr (MAXU > 1) ds_mma<WT, NB * NSW, NB, NSW, KST>(rA, apitch, wuse, acc);
 #pragma unroll
       for (int b = 0; b < NB; b++)
 #pragma unroll
@@ -658,6 +676,8 @@ __global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
   const int tid = threadIdx.x;
   const int wg = blockIdx.x, G = gridDim.x;
   int finished_tiles = 0;        // DOWN tiles this workgroup completed
+  typename DsW<WT>::raw wdown[DS_WSLOTS];
+  bool have_down = false;
 
   // a failed earlier launch of this run: poison the stream and leave at once
   if (tid == 0) sflag[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -666,14 +686,14 @@ __global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
     for (int e = wg * DS_THREADS + tid; e < a.n * D; e += G * DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
     return;
   }
-  if (!ds_phase<WT, D, DP_QKV>(a, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_SAATT>(a, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_SAO>(a, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_CAQ>(a, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_CAATT>(a, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_CAO>(a, rA, red, sflag, finished_tiles)) return;
-  if (!ds_phase<WT, D, DP_UP>(a, rA, red, sflag, finished_tiles)) return;
-  ds_phase<WT, D, DP_DOWN>(a, rA, red, sflag, finished_tiles);
+  if (!ds_phase<WT, D, DP_QKV>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_SAATT>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_SAO>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_CAQ>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_CAATT>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_CAO>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_UP>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  ds_phase<WT, D, DP_DOWN>(a, rA, red, sflag, finished_tiles, wdown, have_down);
 }
 
 }  // namespace vla
