@@ -674,6 +674,8 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         const float* ss[6] = {w.s_qkv, w.s_o, w.s_cq, w.s_co, w.s_up, w.s_down};
         const float* bs[6] = {w.b_qkv, w.b_o, w.b_cq, w.b_co, w.b_up, w.b_down};
         for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = wt == VLA_FP8_E4M3 ? ss[i] : nullptr; a.b[i] = bs[i]; }
+        const bool last_launch = k == K - 1 && l == L - 1;
+        a.wq_next = last_launch ? nullptr : d.layers[(l + 1) % L].w_qkv;
         a.part = c.part; a.cnt = c.cnt_tile; a.err = derr;
         VLA_TRY(launch(c, lk.fn, dim3(G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
         continue;
