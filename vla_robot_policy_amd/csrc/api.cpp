@@ -582,6 +582,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
   const int G = cu_count();
   const bool stack = dit_stack_ok(cf, n, G);
   int* derr = c.take<int>(64);
+  uint16_t* aos = stack ? c.take<uint16_t>((size_t)n * D) : nullptr;   // the layer kernel's self-attention output
   if (stack) {
     // phase and tile counters of the layer kernel live in the shared counter
     // array (every kernel leaves its counters at zero); slice partials in the
@@ -667,7 +668,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
         a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
         a.x_in = xb[l & 1]; a.x1 = x1; a.x2 = x2; a.x_out = xb[(l + 1) & 1];
-        a.qkv = qkv; a.q = q; a.ao = ao; a.h = h;
+        a.qkv = qkv; a.q = q; a.aos = aos; a.aoc = ao; a.h = h;
         a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.cv = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldc = L * 2 * D;
         a.mod = m;
         const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};

@@ -24,11 +24,11 @@
 // phase: the HBM latency of the next weights overlaps the current phase.
 // A phase is complete when its counter reaches the number of units (tiles
 // for DOWN). Producers write with device-coherent (sc1) stores, wait for
-// them, then count; consumers poll the counter and read the bf16
-// intermediates with sc1 loads, so the XCDs' private L2s need no write-back
-// or invalidate. The fp32 residual stream has one buffer per sublayer, each
-// written once per launch before any read, so it is read with ordinary
-// cached loads (no L2 can hold an older copy of it). Every wait is
+// them, then count; consumers poll the counter. Every buffer written inside
+// the launch (the fp32 residual stream has one buffer per sublayer; the two
+// attentions have one output buffer each) is written once before anything
+// reads it, so once its phase is counted it is read with ordinary cached
+// loads: no XCD's private L2 can hold an older copy. Every wait is
 // bounded: on time-out the workgroup records an error, poisons its outputs
 // with NaN and leaves, so a fault can never hang the device. The workgroup
 // that completes the last DOWN tile resets the counters for the next launch.
@@ -74,7 +74,8 @@ struct DitLayerArgs {
   float* x_out;
   uint16_t* qkv;                  // [n, 3D] bf16
   uint16_t* q;                    // [n, D] cross-attention query
-  uint16_t* ao;                   // [n, D] attention output
+  uint16_t* aos;                  // [n, D] self-attention output
+  uint16_t* aoc;                  // [n, D] cross-attention output
   uint16_t* h;                    // [n, mlp] GELU output
   const uint16_t* ck;             // this layer's context keys, row pitch ldc
   const uint16_t* cv;             // this layer's context values
@@ -225,11 +226,10 @@ __device__ __forceinline__ void ds_mma(const char* rA, int apitch, const typenam
 // a V^T fragment gathers 8 keys of one column with 2-byte loads, in the key
 // order the lane's P values already have). With more than one block the
 // waves' partial (max, sum, O) are combined in LDS; with one block wave 0
-// writes the output itself. Q and the outputs are coherent (sc1); K / V are
-// read coherently when `kv_sc1`.
-__device__ __forceinline__ FragBF16 ds_gfrag(brsrc r, uint32_t off, bool sc1) {
-  uint4 v = sc1 ? bload16<CP_SC1>(r, off) : bload16(r, off);
-  FragBF16 f; f.v = __builtin_bit_cast(bf16x8, v); return f;
+// writes the output itself. Inputs are complete when this runs (cached
+// loads); the outputs are device-coherent (sc1) stores.
+__device__ __forceinline__ FragBF16 ds_gfrag(brsrc r, uint32_t off) {
+  FragBF16 f; f.v = __builtin_bit_cast(bf16x8, bload16(r, off)); return f;
 }
 
 // The fragments of one 32-key block: K for the two 16-key halves and the
@@ -241,8 +241,7 @@ struct DsAttFr {
   uint16_t v[DS_DP / 16][8];
 };
 
-__device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, bool sc1, int blk, int nblk, int nk, int ldkv, int hd,
-                                             DsAttFr& f) {
+__device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nblk, int nk, int ldkv, int hd, DsAttFr& f) {
   const int lane = threadIdx.x & 63, qn = lane & 15, grp = lane >> 4;
   const int kb = blk * DS_KB;
   const bool live = blk < nblk;
@@ -252,7 +251,7 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, bool sc1, int b
     for (int ds = 0; ds < DS_DP / 32; ds++) {
       const int key = kb + hb * 16 + qn, d = ds * 32 + grp * 8;
       const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldkv + d) * 2u : BUF_OOB;
-      f.k[hb][ds] = sc1 ? bload16<CP_SC1>(kr, off) : bload16(kr, off);
+      f.k[hb][ds] = bload16(kr, off);
     }
 #pragma unroll
   for (int db = 0; db < DS_DP / 16; db++)
@@ -260,7 +259,7 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, bool sc1, int b
     for (int t = 0; t < 8; t++) {
       const int key = kb + (t < 4 ? 4 * grp + t : 16 + 4 * grp + (t - 4)), d = db * 16 + qn;
       const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldkv + d) * 2u : BUF_OOB;
-      f.v[db][t] = sc1 ? bload2<CP_SC1>(vr, off) : bload2(vr, off);
+      f.v[db][t] = bload2(vr, off);
     }
 }
 
@@ -268,7 +267,7 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, bool sc1, int b
 // caller's wait); each later round is requested before the current one is
 // computed.
 __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const uint16_t* Kp, const uint16_t* Vp, int ldkv,
-                                             bool kv_sc1, uint16_t* O, int ldo, int nq, int nk, int hd, float scale_log2,
+                                             uint16_t* O, int ldo, int nq, int nk, int hd, float scale_log2,
                                              char* lds_o, DsAttFr& f, bool have0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qn = lane & 15, grp = lane >> 4;
@@ -279,9 +278,9 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
 #pragma unroll
   for (int ds = 0; ds < DS_DP / 32; ds++) {
     int d = ds * 32 + grp * 8;
-    qf[ds] = ds_gfrag(qr, (qn < nq && d < hd) ? ((uint32_t)qn * ldq + d) * 2u : BUF_OOB, true);
+    qf[ds] = ds_gfrag(qr, (qn < nq && d < hd) ? ((uint32_t)qn * ldq + d) * 2u : BUF_OOB);
   }
-  if (!have0) ds_att_frags(kr, vr, kv_sc1, wave, nblk, nk, ldkv, hd, f);
+  if (!have0) ds_att_frags(kr, vr, wave, nblk, nk, ldkv, hd, f);
   f32x4 oacc[DS_DP / 16];
 #pragma unroll
   for (int i = 0; i < DS_DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -306,7 +305,7 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
         u.w = (uint32_t)f.v[db][6] | ((uint32_t)f.v[db][7] << 16);
         vf[db].v = __builtin_bit_cast(bf16x8, u);
       }
-      if (r0 + 4 < nblk) ds_att_frags(kr, vr, kv_sc1, blk + 4, nblk, nk, ldkv, hd, f);
+      if (r0 + 4 < nblk) ds_att_frags(kr, vr, blk + 4, nblk, nk, ldkv, hd, f);
       f32x4 s[2];
 #pragma unroll
       for (int hb = 0; hb < 2; hb++) {
@@ -480,18 +479,18 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
     DsAttFr f;
     constexpr bool pre_kv = PH == DP_CAATT;
     if (pre_kv)
-      ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), false, wave,
+      ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), wave,
                    (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, f);
     if (!wait_prev()) return false;
     // ---- one head per unit
     for (int j = 0; j < nu; j++) {
       const int hh = first + j * G;
       if (PH == DP_SAATT)
-        ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D, true,
-                     a.ao + hh * a.hd, D, n, n, a.hd, a.scale_log2, rA, f, false);
+        ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D,
+                     a.aos + hh * a.hd, D, n, n, a.hd, a.scale_log2, rA, f, false);
       else
-        ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc, false,
-                     a.ao + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rA, f, pre_kv && j == 0);
+        ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc,
+                     a.aoc + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rA, f, pre_kv && j == 0);
     }
   } else {
     const int mi = PH == DP_QKV ? 0 : PH == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
@@ -590,7 +589,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       constexpr int apitch = KW * 2 + 16;
       if (!norm && d.k0 != staged_k0) {
         // bf16 activations: ao (SAO, CAO) or the unit's slice of h (DOWN)
-        const uint16_t* src = PH == DP_DOWN ? a.h : a.ao;
+        const uint16_t* src = PH == DP_DOWN ? a.h : PH == DP_SAO ? a.aos : a.aoc;
         const int lds = PH == DP_DOWN ? a.mlp : D;
         const brsrc sr = make_brsrc(src);
         constexpr int AS = (16 * KW / 8 + DS_THREADS - 1) / DS_THREADS;   // 16-byte groups per thread
@@ -599,7 +598,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         for (int i = 0; i < AS; i++) {
           int e8 = tid + i * DS_THREADS;
           int r = (e8 * 8) / KW, c = (e8 * 8) % KW;
-          av[i] = bload16<CP_SC1>(sr, (e8 < 16 * KW / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
+          av[i] = bload16(sr, (e8 < 16 * KW / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
         }
         __syncthreads();
 #pragma unroll
