@@ -13,6 +13,10 @@ Page "AI Infra如何优化VLA - 模型推理性能提升技术拆解":
 Block (no biases, consistent with the decoder family the page names):
   h   = x + Attn(RoPE(Q), RoPE(K), V) W_o^T,   [Q|K|V] = RMSNorm(x, g1) W_qkv^T
   out = h + (SiLU(n W_g^T) * (n W_u^T)) W_d^T,  n = RMSNorm(h, g2)
+With QK-norm (section 算子开发 counts RMSNorm calls on Q and K besides the
+two pre-norms), every query and key head vector is RMS-normalised over the
+head dimension with its own gain (q_norm, k_norm) before RoPE:
+  Q_h <- RMSNorm(Q_h, q_norm),  K_g <- RMSNorm(K_g, k_norm).
 """
 
 from __future__ import annotations
@@ -31,6 +35,9 @@ def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
     q = ops.linear(n, W[prefix + "wq"]).reshape(S, Hq, D)
     k = ops.linear(n, W[prefix + "wk"]).reshape(S, Hkv, D)
     v = ops.linear(n, W[prefix + "wv"]).reshape(S, Hkv, D)
+    if getattr(shape, "qk_norm", False):
+        q = ops.rmsnorm(q, W[prefix + "q_norm"], shape.eps)
+        k = ops.rmsnorm(k, W[prefix + "k_norm"], shape.eps)
     pos = np.arange(S) + pos0
     q = ops.rope(q, pos, shape.rope_base)
     k = ops.rope(k, pos, shape.rope_base)

@@ -38,6 +38,7 @@ class BlockShape:
     intermediate: int
     rope_base: float
     eps: float = 1e-6
+    qk_norm: bool = False    # per-head RMSNorm of Q and K before RoPE
 
     @property
     def q_dim(self) -> int:

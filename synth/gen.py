@@ -174,6 +174,8 @@ def backbone_specs(cfg: Config) -> List[Spec]:
             Spec(p + "wu", (b.intermediate, H), "w", m, fan_in=H),
             Spec(p + "wd", (H, b.intermediate), "w", m, fan_in=b.intermediate),
         ]
+        if b.qk_norm:
+            out += [Spec(p + "q_norm", (b.head_dim,), "gain", "f32"), Spec(p + "k_norm", (b.head_dim,), "gain", "f32")]
     if cfg.final_norm:
         out.append(Spec("llm.final_norm", (H,), "gain", "f32"))
     return out

@@ -27,6 +27,56 @@ def block_weights(rng, shape, scale=None, zero=False):
     })
 
 
+def qk_block_weights(rng, shape):
+    W = block_weights(rng, shape)
+    W["l.q_norm"] = rng.uniform(0.5, 1.5, shape.head_dim)
+    W["l.k_norm"] = rng.uniform(0.5, 1.5, shape.head_dim)
+    return W
+
+
+@pytest.mark.parametrize("which, head", [("l.wq", 1), ("l.wk", 0)])
+def test_block_qk_norm_removes_each_head_scale(rng, which, head):
+    """QK-norm normalises every query / key head vector: scaling one head's
+    rows of W_q (or W_k) leaves the block output unchanged up to the eps
+    term, while without QK-norm the same scaling changes the attention."""
+    import dataclasses
+    qk = dataclasses.replace(SMALL_BLOCK, qk_norm=True)
+    W = qk_block_weights(rng, qk)
+    x = rng.standard_normal((11, qk.hidden))
+    D = qk.head_dim
+    Ws = DictW(W)
+    Ws[which] = W[which].copy()
+    Ws[which][head * D:(head + 1) * D] *= 7.0
+    y, ys = llm.block(x, W, "l.", qk), llm.block(x, Ws, "l.", qk)
+    assert np.max(np.abs(ys - y)) / np.max(np.abs(y)) < 1e-6
+    y0, y0s = llm.block(x, W, "l.", SMALL_BLOCK), llm.block(x, Ws, "l.", SMALL_BLOCK)
+    assert np.max(np.abs(y0s - y0)) / np.max(np.abs(y0)) > 1e-3
+
+
+def test_block_qk_norm_unit_gains_give_unit_rms_heads(rng, monkeypatch):
+    """With unit gains each head vector reaching RoPE has mean square
+    ms / (ms + eps) of its pre-norm value (RMSNorm's closed form), and the
+    gains multiply it per dimension."""
+    import dataclasses
+    qk = dataclasses.replace(SMALL_BLOCK, qk_norm=True)
+    W = qk_block_weights(rng, qk)
+    W["l.q_norm"] = np.ones(qk.head_dim)
+    seen = {}
+    real_rope = ops.rope
+
+    def spy(t, pos, base):
+        seen.setdefault("q", t)    # first call: the queries
+        return real_rope(t, pos, base)
+
+    monkeypatch.setattr(ops, "rope", spy)
+    x = rng.standard_normal((6, qk.hidden))
+    llm.block(x, W, "l.", qk)
+    n = ops.rmsnorm(x, W["l.attn_norm"], qk.eps)
+    q_raw = (n @ W["l.wq"].T).reshape(6, qk.n_q_heads, qk.head_dim)
+    ms = np.mean(q_raw * q_raw, axis=-1)
+    np.testing.assert_allclose(np.mean(seen["q"] ** 2, axis=-1), ms / (ms + qk.eps), rtol=1e-12)
+
+
 def test_block_zero_weights_is_identity(rng):
     W = block_weights(rng, SMALL_BLOCK, zero=True)
     x = rng.standard_normal((9, SMALL_BLOCK.hidden))
