@@ -209,7 +209,9 @@ def test_euler_exact_cases(rng):
     x0 = rng.standard_normal((4, 3))
     c = rng.standard_normal((4, 3))
     for K in (1, 4, 10):
-        np.testing.assert_allclose(dit.euler_sample(x0, K, lambda x, t: c), x0 + c, rtol=1e-14)
+        # K fp64 additions of c/K: rounding at most ~K eps (|x0| + |c|) per element
+        got = dit.euler_sample(x0, K, lambda x, t: c)
+        assert np.all(np.abs(got - (x0 + c)) <= 2 * K * np.finfo(float).eps * (np.abs(x0) + np.abs(c)))
         a = 0.7
         np.testing.assert_allclose(dit.euler_sample(x0, K, lambda x, t: a * x), (1 + a / K) ** K * x0, rtol=1e-13)
         f = lambda t: np.sin(3 * t) + t * t
