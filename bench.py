@@ -241,6 +241,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-label", default=None,
                     help="relaunch only the kernel with this label --kernel-reps times (for counter passes)")
+    ap.add_argument("--qk-norm", action="store_true",
+                    help="backbone blocks with QK-norm (per-head RMSNorm of Q and K before RoPE); not the default workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device copy of this many bytes --kernel-reps times (counter calibration)")
     a = ap.parse_args()
@@ -254,6 +256,9 @@ def main():
     from synth import get_config
     from vla_robot_policy_amd import roofline
     cfg = get_config(a.config)
+    if a.qk_norm:
+        import dataclasses
+        cfg = cfg.replace(block=dataclasses.replace(cfg.block, qk_norm=True))
     if cfg.kind != "step":
         raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
     r = gpu_step_bench(cfg, a.steps, a.warmup, a.kernel_reps, a.only_label)
@@ -288,7 +293,8 @@ def main():
         "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOADS[a.config], "global_batch": 1, "seq_len": cfg.seq,
+        "config": {"workload": WORKLOADS[a.config] + ("; backbone with QK-norm" if a.qk_norm else ""),
+                   "global_batch": 1, "seq_len": cfg.seq,
                    "euler_steps": cfg.steps, "parallelism": "single GPU"},
         "hz": round(1000.0 / ms, 2), "p50_ms": round(r["p50"], 4), "p90_ms": round(r["p90"], 4),
         "tokens_per_s": round(cfg.seq / (ms * 1e-3), 1),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define VLA_ABI_VERSION 1
+#define VLA_ABI_VERSION 2   /* 2: vla_block_weights gained q_norm, k_norm */
 
 typedef enum {
   VLA_OK = 0,
@@ -63,16 +63,22 @@ typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2 } vla_dtype;
  *   head h reads KV head h / (n_q_heads / n_kv_heads)), h = x + O W_o^T,
  *   out = h + (SiLU(n W_gate^T) * (n W_up^T)) W_down^T with n = RMSNorm(h,
  *   mlp_norm). RMSNorm(x, g) = x / sqrt(mean(x^2) + eps) * g. No biases.
+ * With flags & VLA_BLOCK_QK_NORM (QK-norm; section 算子开发 counts RMSNorm
+ * calls on Q and K besides the pre-norms), every query and key head vector
+ * is RMS-normalised over head_dim before RoPE: Q_h <- Q_h / sqrt(mean(Q_h^2)
+ * + eps) * q_norm, K_g likewise with k_norm; it needs n_q_heads * head_dim
+ * to be a multiple of 128.
  * Supported: head_dim in {64, 128}; hidden, intermediate multiples of 8
  * (of 16 for FP8_E4M3 weights); n_q_heads % n_kv_heads == 0; wdtype F32 with adtype F32, or wdtype
  * BF16 / FP8_E4M3 with adtype BF16.
  */
+#define VLA_BLOCK_QK_NORM 1
 typedef struct {
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, intermediate;
   float rope_base, eps;
   int32_t wdtype;  /* vla_dtype of the Linear weights                  */
   int32_t adtype;  /* vla_dtype of x_in / x_out / embeddings: F32, BF16 */
-  int32_t flags;   /* must be 0                                        */
+  int32_t flags;   /* 0 or VLA_BLOCK_QK_NORM                           */
 } vla_block_cfg;
 
 typedef struct {
@@ -86,6 +92,8 @@ typedef struct {
   const float* s_gate_up;
   const void* w_down;     /* [hidden, intermediate]                                */
   const float* s_down;
+  const float* q_norm;    /* [head_dim], VLA_BLOCK_QK_NORM only (else ignored)     */
+  const float* k_norm;    /* [head_dim], VLA_BLOCK_QK_NORM only                    */
 } vla_block_weights;
 
 /* x_in, x_out: [seq, hidden] in cfg->adtype (may alias). */

@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     assert len(syms) >= 17
     for s in syms:
         assert hasattr(L, s), s
-    assert lib.vla_abi_version() == 1
+    assert lib.vla_abi_version() == 2
 
 
 def llm_cfg(**kw):
@@ -39,7 +39,9 @@ def test_workspace_sizes_scale_with_shape():
     (dict(head_dim=96), lib.VLA_ERR_SHAPE),
     (dict(n_kv_heads=5), lib.VLA_ERR_SHAPE),
     (dict(hidden=2561), lib.VLA_ERR_SHAPE),
-    (dict(flags=1), lib.VLA_ERR_UNSUPPORTED),
+    (dict(flags=2), lib.VLA_ERR_UNSUPPORTED),
+    (dict(flags=lib.VLA_BLOCK_QK_NORM), lib.VLA_ERR_INVALID_ARG),                  # no q_norm / k_norm
+    (dict(flags=lib.VLA_BLOCK_QK_NORM, n_q_heads=3, n_kv_heads=1, head_dim=64), lib.VLA_ERR_UNSUPPORTED),
     (dict(wdtype=7), lib.VLA_ERR_INVALID_ARG),
     (dict(wdtype=lib.VLA_F32), lib.VLA_ERR_UNSUPPORTED),
 ])

@@ -39,6 +39,36 @@ def test_block_small(gu, wdtype, seq):
     assert e <= gu.TOL[wdtype]
 
 
+@pytest.mark.parametrize("wdtype,seq", [("f32", 37), ("bf16", 130), ("fp8", 37)])
+def test_block_qk_norm(gu, wdtype, seq):
+    # QK-norm in the RoPE epilogue: head_dim 64, two heads per 128-column tile
+    import dataclasses
+    from synth.configs import SMALL_BLOCK
+    cfg = small_config("block", wdtype, seq=seq, block=dataclasses.replace(SMALL_BLOCK, qk_norm=True))
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = gu.DeviceWeights(cfg, W)
+    got = gu.run_block(cfg, dw, gu.upload_input(I["x"]), seq)
+    want = ollm.block(to_f64(I["x"]), Weights(W), "llm.0.", cfg.block)
+    e = gu.relerr(got, want)
+    gu.say(f"block qk-norm {wdtype} seq {seq}: rel L2 {e:.3e}")
+    assert e <= gu.TOL[wdtype]
+
+
+def test_backbone_qk_norm_head128(gu):
+    # QK-norm with one 128-dim head per tile, split-K QKV, two layers
+    from synth.configs import BlockShape
+    blk = BlockShape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024, rope_base=1e6,
+                     qk_norm=True)
+    cfg = small_config("backbone", "bf16", block=blk, layers=2, seq=45)
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = gu.DeviceWeights(cfg, W)
+    got = gu.run_backbone(cfg, dw, gu.upload_input(I["x"]), cfg.seq)
+    want = run_config(cfg, W, I)["hidden"]
+    e = gu.relerr(got, want)
+    gu.say(f"backbone qk-norm 8/2 x128 S=45: rel L2 {e:.3e}")
+    assert e <= 1e-2
+
+
 def test_block_cfg1(gu):
     cfg = get_config(1)
     W, I = make_weights(cfg), make_inputs(cfg)

@@ -342,7 +342,7 @@ bool dtype_ok(int t) { return t == VLA_F32 || t == VLA_BF16 || t == VLA_FP8_E4M3
 // ------------------------------------------------------------------ backbone
 vla_status check_block_cfg(const vla_block_cfg* cfg) {
   if (!cfg) return fail(VLA_ERR_INVALID_ARG, "null block cfg");
-  if (cfg->flags != 0) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags must be 0");
+  if (cfg->flags & ~VLA_BLOCK_QK_NORM) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags 0x%x: unknown bits", cfg->flags);
   if (!dtype_ok(cfg->wdtype) || (cfg->adtype != VLA_F32 && cfg->adtype != VLA_BF16))
     return fail(VLA_ERR_INVALID_ARG, "block cfg: bad dtype (w %d, act %d)", cfg->wdtype, cfg->adtype);
   if ((cfg->wdtype == VLA_F32) != (cfg->adtype == VLA_F32))
@@ -355,6 +355,11 @@ vla_status check_block_cfg(const vla_block_cfg* cfg) {
     return fail(VLA_ERR_SHAPE, "block cfg: n_q_heads %d not a multiple of n_kv_heads %d", cfg->n_q_heads, cfg->n_kv_heads);
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return fail(VLA_ERR_SHAPE, "block cfg: head_dim %d not in {64, 128}", cfg->head_dim);
   if (!(cfg->eps >= 0.f) || !(cfg->rope_base > 1.f)) return fail(VLA_ERR_INVALID_ARG, "block cfg: bad eps / rope_base");
+  // QK-norm runs in the RoPE epilogue of the 128-column QKV tiles: a tile
+  // holds whole heads and lies within the query or the key / value columns
+  if ((cfg->flags & VLA_BLOCK_QK_NORM) && (cfg->n_q_heads * cfg->head_dim) % 128)
+    return fail(VLA_ERR_UNSUPPORTED, "block cfg: QK-norm needs n_q_heads * head_dim %d to be a multiple of 128",
+                cfg->n_q_heads * cfg->head_dim);
   return VLA_OK;
 }
 
@@ -364,6 +369,8 @@ vla_status check_block_weights(const vla_block_cfg* cfg, const vla_block_weights
     return fail(VLA_ERR_INVALID_ARG, "block weights: null tensor pointer");
   if (cfg->wdtype == VLA_FP8_E4M3 && (!w->s_qkv || !w->s_o || !w->s_gate_up || !w->s_down))
     return fail(VLA_ERR_INVALID_ARG, "block weights: fp8 weights need scales");
+  if ((cfg->flags & VLA_BLOCK_QK_NORM) && (!w->q_norm || !w->k_norm))
+    return fail(VLA_ERR_INVALID_ARG, "block weights: QK-norm needs q_norm and k_norm");
   return VLA_OK;
 }
 
@@ -423,6 +430,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
       a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32;
       a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_base = cfg.rope_base;
+      if (cfg.flags & VLA_BLOCK_QK_NORM) { a.qk_norm = 1; a.qk_eps = cfg.eps; a.qn_g = w.q_norm; a.kn_g = w.k_norm; }
       VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : A_BF16, E_ROPE}));
     }
     {  // causal GQA attention

@@ -64,6 +64,8 @@ struct GemmArgs {
   int ldc;
   int c_f32;
   int q_cols, k_cols, head_dim, pos0; float rope_base;   // ROPE
+  int qk_norm; float qk_eps;                              // ROPE: per-head RMSNorm of q and k first
+  const float* qn_g; const float* kn_g;                   //   with gains [head_dim]; tiles hold whole heads
   float* x; int ldx;                                      // RESID
   int x_init;                                             // RESID: x = y (+ table) instead of x += y
   const float* addrow; int addrow_rows;                   // RESID: + table[m % rows][n]
@@ -256,6 +258,20 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const float e_bi = (EM == E_STORE || EM == E_RESID)
                          ? bloadf(make_brsrc(p.bias), (p.bias && ecok) ? (uint32_t)ecol * 4u : BUF_OOB) : 0.f;
   const float e_ga = EM == E_RESID ? bloadf(make_brsrc(p.gate), (p.gate && ecok) ? (uint32_t)ecol * 4u : BUF_OOB) : 0.f;
+  // QK-norm gains of the column and of its RoPE partner (a tile lies within
+  // the query columns or within the key / value columns, so the gain vector
+  // is the same for the whole workgroup)
+  float e_g1 = 1.f, e_g2 = 1.f;
+  if constexpr (EM == E_ROPE) {
+    if (p.qk_norm) {
+      const int D = p.head_dim, hd = D >> 1;
+      const int d1 = (ecol < p.q_cols ? ecol : ecol - p.q_cols) % D, d2 = d1 < hd ? d1 + hd : d1 - hd;
+      const brsrc gr = make_brsrc(nt * BN < p.q_cols ? p.qn_g : p.kn_g);
+      const bool ok = ecol < p.q_cols + p.k_cols;
+      e_g1 = bloadf(gr, ok ? (uint32_t)d1 * 4u : BUF_OOB);
+      e_g2 = bloadf(gr, ok ? (uint32_t)d2 * 4u : BUF_OOB);
+    }
+  }
 
   // ---- weight row of tile row `row` (byte offset of k = 0, or OOB)
   auto wrow_of = [&](int row) -> uint32_t {
@@ -744,8 +760,45 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     const int d = (ncol < p.q_cols ? ncol : ncol - p.q_cols) % D;
     const int fi = d < hd ? d : d - hd;
     const int pc = d < hd ? cc + hd : cc - hd;           // partner column in the tile
-    const float sc = p.wscale ? e_sc : 1.f;
-    const float sc2 = p.wscale ? e_sc2 : 1.f;
+    float sc = p.wscale ? e_sc : 1.f;
+    float sc2 = p.wscale ? e_sc2 : 1.f;
+    // QK-norm: the inverse RMS of every (row, head) of the tile over the
+    // head's D columns, from the scaled values; four threads per pair, then
+    // a butterfly over them. The tile's heads start at multiples of D.
+    float* const qinv = reinterpret_cast<float*>(sRow);   // [BM][BN / D], free after the main loop
+    const int nht = BN / D;
+    if (p.qk_norm) {
+      if (p.wscale) {
+#pragma unroll
+        for (int i = 0; i < XPE; i++) {
+          const int r = r0e + i * RPT;
+          if (r < BM) sT[r * TPITCH + cc] *= e_sc;
+        }
+        __syncthreads();
+        sc = sc2 = 1.f;
+      }
+      const int j4 = tid & 3;
+      // head_dim as a compile-time constant: the float4 reads of a row are
+      // unrolled and issued together
+      auto rows = [&](auto dc) {
+        constexpr int DD = decltype(dc)::value, NH = BN / DD, NF = DD / 16;
+        for (int pr = tid >> 2; pr < BM * NH; pr += NT / 4) {
+          const float* row = sT + (pr / NH) * TPITCH + (pr % NH) * DD;
+          float sq = 0.f;
+#pragma unroll
+          for (int i = 0; i < NF; i++) {
+            const float4 x = *reinterpret_cast<const float4*>(row + (j4 + 4 * i) * 4);
+            sq += (x.x * x.x + x.y * x.y) + (x.z * x.z + x.w * x.w);
+          }
+          sq += __shfl_xor(sq, 1, WAVE);
+          sq += __shfl_xor(sq, 2, WAVE);
+          if (j4 == 0) qinv[pr] = rsqrtf(sq / (float)DD + p.qk_eps);
+        }
+      };
+      if (D == 128) rows(std::integral_constant<int, 128>{});
+      else rows(std::integral_constant<int, 64>{});
+      __syncthreads();
+    }
     const float theta = exp2f(-2.0f * (float)fi / (float)D * log2f(p.rope_base));
     // the thread's rows step by RPT positions: the first angle from sincosf,
     // each next one by a rotation through RPT * theta
@@ -759,6 +812,11 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         float v = sT[r * TPITCH + cc] * sc;
         if (rot) {
           float v2 = sT[r * TPITCH + pc] * sc2;
+          if (p.qk_norm) {
+            const float qs = qinv[r * nht + cc / D];
+            v *= qs * e_g1;
+            v2 *= qs * e_g2;
+          }
           v = d < hd ? v * cs - v2 * sn : v * cs + v2 * sn;
         }
         put((uint32_t)m * p.ldc + ncol, v);

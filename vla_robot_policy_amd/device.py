@@ -82,11 +82,12 @@ class DeviceWeights:
         bc = lib.BlockCfg(hidden=b.hidden, n_q_heads=b.n_q_heads, n_kv_heads=b.n_kv_heads, head_dim=b.head_dim,
                           intermediate=b.intermediate, rope_base=b.rope_base, eps=b.eps,
                           wdtype=lib.DTYPE_CODE[cfg.wdtype], adtype=lib.VLA_F32 if cfg.wdtype == "f32" else lib.VLA_BF16,
-                          flags=0)
+                          flags=lib.VLA_BLOCK_QK_NORM if b.qk_norm else 0)
         layers = (lib.BlockWeights * cfg.layers)()
         for l in range(cfg.layers):
             p = f"llm.{l}."
-            self.prefetch([p + n for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "wg", "wu", "wd")])
+            extra = ("q_norm", "k_norm") if b.qk_norm else ()
+            self.prefetch([p + n for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "wg", "wu", "wd") + extra])
             L = layers[l]
             L.attn_norm = self.up(p + "attn_norm")
             L.w_qkv, L.s_qkv = self.up_rows([p + "wq", p + "wk", p + "wv"])
@@ -94,6 +95,9 @@ class DeviceWeights:
             L.mlp_norm = self.up(p + "mlp_norm")
             L.w_gate_up, L.s_gate_up = self.up_rows([p + "wg", p + "wu"])
             L.w_down, L.s_down = self.up_rows([p + "wd"])
+            if b.qk_norm:
+                L.q_norm = self.up(p + "q_norm")
+                L.k_norm = self.up(p + "k_norm")
         final = self.up("llm.final_norm") if cfg.final_norm else None
         self.block_cfg = bc
         self._bb_layers = layers

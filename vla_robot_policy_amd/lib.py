@@ -20,6 +20,7 @@ VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_SHAPE, VLA_ERR_UNSUPPORTED, VLA_ERR_WORKSPA
     0, -1, -2, -3, -4, -5, -6)
 VLA_F32, VLA_BF16, VLA_FP8_E4M3 = 0, 1, 2
 DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3}
+VLA_BLOCK_QK_NORM = 1
 
 
 class VlaError(RuntimeError):
@@ -36,7 +37,7 @@ class BlockCfg(C.Structure):
 
 class BlockWeights(C.Structure):
     _fields_ = [(n, c_void_p) for n in ("attn_norm", "w_qkv", "s_qkv", "w_o", "s_o", "mlp_norm", "w_gate_up",
-                                         "s_gate_up", "w_down", "s_down")]
+                                         "s_gate_up", "w_down", "s_down", "q_norm", "k_norm")]
 
 
 class Backbone(C.Structure):
