@@ -85,6 +85,81 @@ def copy_probe(nbytes: int, reps: int):
     log(f"copied {n * 4} bytes x {reps}")
 
 
+def shape_cache_bench(cfg, texts, steps, warmup):
+    """Step latency per text length from one plan sized for the longest
+    (vla_step_run_shape: the first call of a length runs eagerly and
+    captures it, later calls replay its graph). Prints its own JSON line."""
+    import numpy as np
+    import torch
+    from synth import make_inputs, make_weights
+    from vla_robot_policy_amd import lib
+    from vla_robot_policy_amd.device import DeviceWeights, upload_input, workspace
+
+    n_vis = cfg.seq - cfg.n_text
+    top = cfg.replace(n_text=max(texts), seq=n_vis + max(texts), ctx_len=n_vis + max(texts))
+    W, I = make_weights(top), make_inputs(top)
+    dw = DeviceWeights(top, W, keep_host=False, threads=16)
+    model = dw.build_model()
+    d = top.dit
+    dev = torch.device("cuda:0")
+    images = upload_input(I["image"]) if top.vit is not None else None
+    text, noise = upload_input(I["text"]), upload_input(I["noise"])
+    actions = torch.empty((d.chunk, d.action_dim), dtype=torch.float32, device=dev)
+
+    def shape(nt):
+        return lib.StepShape(n_images=top.n_images, n_text=nt, chunk=d.chunk, action_dim=d.action_dim, steps=top.steps)
+
+    io = lib.StepIO(images=None if images is None else images.data_ptr(), text=text.data_ptr(),
+                    noise=noise.data_ptr(), actions=actions.data_ptr(), hidden_out=None, velocities=None)
+    need = lib.vla_step_workspace_bytes(model, shape(max(texts)))
+    ws = workspace(need)
+    st, plan = lib.vla_step_plan_create(model, shape(max(texts)), io, ws, need)
+    lib.check(st)
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    try:
+        for nt in texts:
+            torch.cuda.synchronize()
+            t = time.time()
+            lib.check(lib.vla_step_run_shape(plan, shape(nt), stream))
+            torch.cuda.synchronize()
+            miss = (time.time() - t) * 1e3
+            for _ in range(warmup):
+                lib.check(lib.vla_step_run_shape(plan, shape(nt), stream))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                lib.check(lib.vla_step_run_shape(plan, shape(nt), stream))
+            e1.record()
+            torch.cuda.synchronize()
+            rows.append({"n_text": nt, "seq": n_vis + nt, "first_call_ms": round(miss, 2),
+                         "replay_ms": round(e0.elapsed_time(e1) / steps, 4)})
+            log(f"n_text {nt}: first call {miss:.1f} ms (eager + capture), replay {rows[-1]['replay_ms']:.3f} ms")
+        # every call switches to another length: each replay starts with the
+        # counter-clearing fill of its layout
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            lib.check(lib.vla_step_run_shape(plan, shape(texts[i % len(texts)]), stream))
+        e1.record()
+        torch.cuda.synchronize()
+        switch = e0.elapsed_time(e1) / steps
+        st, info = lib.vla_step_cache_info(plan)
+        lib.check(st)
+    finally:
+        lib.vla_step_plan_destroy(plan)
+    line = {"metric": "ms per VLA step by text length, one plan with shape-keyed graphs", "unit": "ms",
+            "higher_is_better": False, "steps": steps, "warmup": warmup, "data": "synthetic",
+            "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16",
+            "config": {"workload": f"{n_vis} visual tokens + text lengths {texts}; plan sized for n_text {max(texts)}",
+                       "global_batch": 1, "euler_steps": top.steps},
+            "shapes": rows, "alternating_replay_ms": round(switch, 4),
+            "cache": {"entries": info.entries, "hits": info.hits, "misses": info.misses, "evictions": info.evictions}}
+    print(json.dumps(line), flush=True)
+
+
 def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
     import numpy as np
     import torch
@@ -243,6 +318,9 @@ def main():
                     help="relaunch only the kernel with this label --kernel-reps times (for counter passes)")
     ap.add_argument("--qk-norm", action="store_true",
                     help="backbone blocks with QK-norm (per-head RMSNorm of Q and K before RoPE); not the default workload")
+    ap.add_argument("--shape-cache", default=None,
+                    help="comma-separated text lengths: time each from one plan sized for the longest "
+                         "(shape-keyed graphs) and print that line instead of the headline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device copy of this many bytes --kernel-reps times (counter calibration)")
     a = ap.parse_args()
@@ -261,6 +339,9 @@ def main():
         cfg = cfg.replace(block=dataclasses.replace(cfg.block, qk_norm=True))
     if cfg.kind != "step":
         raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
+    if a.shape_cache:
+        shape_cache_bench(cfg, [int(t) for t in a.shape_cache.split(",")], a.steps, a.warmup)
+        return
     r = gpu_step_bench(cfg, a.steps, a.warmup, a.kernel_reps, a.only_label)
     if r is None:
         return

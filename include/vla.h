@@ -258,7 +258,9 @@ vla_status vla_step_run(vla_step_plan* plan, hipStream_t stream);
 /* Capture one pass into a hipGraph and instantiate it (one eager warm-up
  * pass is launched first). VLA_ERR_STATE if already captured. */
 vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream);
-/* Replay the captured graph (VLA_ERR_STATE if not captured). */
+/* Replay the captured graph (VLA_ERR_STATE if not captured). After a pass of
+ * another shape (vla_step_run_shape) it first clears the counters the graph
+ * expects at zero, with one small fill kernel. */
 vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream);
 /* Kernel nodes in the captured graph (0 before capture). */
 int32_t vla_step_graph_nodes(const vla_step_plan* plan);
@@ -271,6 +273,36 @@ const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index);
  * the next vla_step_run / vla_step_replay recomputes everything from the
  * inputs. Valid only after vla_step_capture. */
 vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_t stream);
+
+/* Shape-keyed graphs ([R] CUDA Graph: when the sequence length changes, the
+ * LLM graph falls back to an eager pass and is captured again, the cached
+ * length being what a call is matched against). One pass of `shape`, which
+ * may be smaller than the plan's: n_images, n_text, chunk and steps at most
+ * the plan's, action_dim equal to it. The plan's buffers serve as packed
+ * prefixes for that shape: images [n_images, C, image, image], text
+ * [n_text, hidden], noise and actions [chunk, action_dim], hidden_out
+ * [seq, hidden], velocities [steps, chunk, action_dim].
+ *   - A shape seen before replays its graph (the plan's own shape replays the
+ *     vla_step_capture graph when there is one); asynchronous like a replay.
+ *   - A new shape runs one eager pass, whose outputs are this call's, then
+ *     synchronises `stream` and captures the shape into a graph (nothing of
+ *     the capture runs). At most VLA_STEP_GRAPH_CACHE such graphs are kept;
+ *     adding one more destroys the least recently used.
+ * Every shape shares the plan's workspace, so passes of any shapes must be
+ * ordered on one stream. Errors: VLA_ERR_SHAPE (outside the plan's shape),
+ * VLA_ERR_WORKSPACE (the shape needs more workspace than the plan holds),
+ * VLA_ERR_HIP; the cache is unchanged after an error. */
+#define VLA_STEP_GRAPH_CACHE 8
+vla_status vla_step_run_shape(vla_step_plan* plan, const vla_step_shape* shape, hipStream_t stream);
+
+typedef struct {
+  int32_t entries;    /* graphs held for shapes other than the plan's own      */
+  int32_t hits;       /* vla_step_run_shape calls that replayed a graph         */
+  int32_t misses;     /* calls that ran eagerly and captured a new shape        */
+  int32_t evictions;  /* graphs destroyed to make room                          */
+} vla_step_cache_stats;
+vla_status vla_step_cache_info(const vla_step_plan* plan, vla_step_cache_stats* out);
+
 void vla_step_plan_destroy(vla_step_plan* plan);
 
 /* ------------------------------------------------------------------ misc */

@@ -79,3 +79,46 @@ def test_dit_and_step_validation():
     assert st == lib.VLA_ERR_INVALID_ARG and plan is None
     assert lib.vla_step_replay(None) == lib.VLA_ERR_INVALID_ARG
     assert lib.vla_step_graph_nodes(None) == 0
+
+
+def _fake_struct(cls, addr, **kw):
+    s = cls(**kw)
+    for name, typ in cls._fields_:
+        if typ is C.c_void_p and name not in kw:
+            setattr(s, name, addr)
+    return s
+
+
+def test_step_run_shape_validation():
+    """vla_step_run_shape rejects shapes the plan's buffers cannot serve
+    before anything is launched (host-only plan over placeholder addresses)."""
+    fake = 1 << 20
+    bl = (lib.BlockWeights * 2)(*[_fake_struct(lib.BlockWeights, fake, q_norm=None, k_norm=None) for _ in range(2)])
+    bb = lib.Backbone(cfg=llm_cfg(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, intermediate=1024), n_layers=2,
+                      layers=bl, final_norm=fake)
+    dc = lib.DitCfg(hidden=512, heads=8, head_dim=64, mlp=2048, layers=2, tdim=256, ctx_dim=512, eps=1e-6,
+                    time_scale=1000.0, freq_base=10000.0, wdtype=lib.VLA_BF16, flags=0)
+    dl = (lib.DitLayer * 2)(*[_fake_struct(lib.DitLayer, fake) for _ in range(2)])
+    d = _fake_struct(lib.Dit, fake, cfg=dc, layers=dl)
+    model = lib.Model(vit=None, backbone=C.pointer(bb), w_proj=fake, s_proj=None, b_proj=fake, dit=C.pointer(d))
+    shape = lib.StepShape(n_images=0, n_text=40, chunk=16, action_dim=7, steps=4)
+    need = lib.vla_step_workspace_bytes(model, shape)
+    assert need > 0, lib.vla_last_error()
+    io = lib.StepIO(images=None, text=fake, noise=fake, actions=fake, hidden_out=None, velocities=None)
+    st, plan = lib.vla_step_plan_create(model, shape, io, fake, need)
+    assert st == lib.VLA_OK, lib.vla_last_error()
+    try:
+        for kw in (dict(n_text=41), dict(chunk=17), dict(steps=5), dict(action_dim=6), dict(n_text=0)):
+            bad = lib.StepShape(**{**dict(n_images=0, n_text=40, chunk=16, action_dim=7, steps=4), **kw})
+            assert lib.vla_step_run_shape(plan, bad) == lib.VLA_ERR_SHAPE, kw
+            assert lib.vla_last_error()
+        # images requested from a plan without a vision encoder
+        st = lib.vla_step_run_shape(plan, lib.StepShape(n_images=1, n_text=8, chunk=16, action_dim=7, steps=4))
+        assert st in (lib.VLA_ERR_INVALID_ARG, lib.VLA_ERR_SHAPE)
+        st, info = lib.vla_step_cache_info(plan)
+        assert st == lib.VLA_OK
+        assert (info.entries, info.hits, info.misses, info.evictions) == (0, 0, 0, 0)
+    finally:
+        lib.vla_step_plan_destroy(plan)
+    assert lib.vla_step_run_shape(None, shape) == lib.VLA_ERR_INVALID_ARG
+    assert lib.vla_step_cache_info(None)[0] == lib.VLA_ERR_INVALID_ARG

@@ -1,0 +1,132 @@
+"""Shape-keyed step graphs on the GPU (page "AI Infra如何优化VLA - 模型推理性能
+提升技术拆解", section CUDA Graph: a changed sequence length falls back to an
+eager pass and is captured again, matched by the cached length).
+
+One plan is created for a maximum shape; vla_step_run_shape then serves
+smaller shapes from the same buffers, used as packed prefixes. Each shape's
+first call (eager) is checked against the float64 oracle on the matching
+prefix of the seeded inputs; later calls replay a cached graph and must
+reproduce the first call bit for bit, also when other shapes ran between
+them and when the plan's own captured graph is replayed in between."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle.io import Weights, to_f64
+from oracle.policy import vla_step
+from synth import make_inputs, make_weights, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util
+    return gpu_util
+
+
+def _outputs(gu, r, cfg, sh):
+    """Prefix views of the plan's output buffers for shape `sh`."""
+    out = r.outputs()
+    H = cfg.block.hidden
+    n_vis = sh.n_images * cfg.vit.n_merged
+    seq = n_vis + sh.n_text
+    c, a, k = sh.chunk, sh.action_dim, sh.steps
+    return {"actions": out["actions"].reshape(-1)[:c * a].reshape(c, a),
+            "velocities": out["velocities"].reshape(-1)[:k * c * a].reshape(k, c, a),
+            "hidden": out["hidden"].reshape(-1)[:seq * H].reshape(seq, H)}
+
+
+def _oracle(cfg, W, I, sh):
+    c2 = cfg.replace(n_images=sh.n_images, n_text=sh.n_text, steps=sh.steps,
+                     seq=sh.n_images * cfg.vit.n_merged + sh.n_text,
+                     ctx_len=sh.n_images * cfg.vit.n_merged + sh.n_text,
+                     dit=dataclasses.replace(cfg.dit, chunk=sh.chunk))
+    if sh.n_images == 0:
+        c2 = c2.replace(vit=None)
+    img = to_f64(I["image"])[:sh.n_images]
+    return vla_step(img, to_f64(I["text"])[:sh.n_text], to_f64(I["noise"])[:sh.chunk], W, c2)
+
+
+def test_step_shape_cache(gu):
+    from vla_robot_policy_amd import lib
+    base = small_config("step", "bf16")
+    n_vis1 = base.vit.n_merged
+    cfg = base.replace(n_images=2, n_text=21, seq=2 * n_vis1 + 21, ctx_len=2 * n_vis1 + 21)
+    W, I = make_weights(cfg), make_inputs(cfg)
+    Wo = Weights(W)
+    dw = gu.DeviceWeights(cfg, W)
+    r = gu.StepRunner(cfg, dw, I)
+    tol = gu.TOL["bf16"]
+
+    def shape(ni, nt, c, k):
+        return lib.StepShape(n_images=ni, n_text=nt, chunk=c, action_dim=cfg.dit.action_dim, steps=k)
+
+    def run(sh):
+        lib.check(lib.vla_step_run_shape(r.plan, sh))
+        return _outputs(gu, r, cfg, sh)
+
+    def stats():
+        st, s = lib.vla_step_cache_info(r.plan)
+        lib.check(st)
+        return (s.entries, s.hits, s.misses, s.evictions)
+
+    try:
+        A = shape(2, 21, cfg.dit.chunk, cfg.steps)      # the plan's own shape
+        B = shape(1, 13, 3, 2)
+        C = shape(0, 17, 5, 1)                          # text only: the vision encoder is skipped
+        first = {}
+        for name, sh in (("A", A), ("B", B), ("C", C)):
+            got = run(sh)
+            want = _oracle(cfg, Wo, I, sh)
+            for k in ("hidden", "actions", "velocities"):
+                assert got[k].shape == want[k].shape, (name, k)
+                e = gu.relerr(got[k], want[k])
+                gu.say(f"shape {name}: {k} rel L2 {e:.3e}")
+                assert e <= tol, (name, k, e)
+            first[name] = got
+        assert stats() == (3, 0, 3, 0)
+        # replays, in an order that puts other layouts between repeats
+        for name, sh in (("B", B), ("A", A), ("C", C), ("B", B)):
+            got = run(sh)
+            for k in got:
+                assert np.array_equal(got[k], first[name][k]), (name, k)
+        assert stats() == (3, 4, 3, 0)
+        # the plan's own graph, replayed after another shape ran
+        r.capture()
+        run(B)
+        r.replay()
+        got = _outputs(gu, r, cfg, A)
+        for k in got:
+            assert np.array_equal(got[k], first["A"][k]), ("replay", k)
+        got = run(A)                                    # served by the plan's own graph
+        for k in got:
+            assert np.array_equal(got[k], first["A"][k]), ("A via plan graph", k)
+        assert stats() == (3, 6, 3, 0)
+        # least recently used eviction: six new shapes fill the cache (8
+        # entries); the sixth pushes out A's cache copy, the least recently
+        # used (A itself is now served by the plan's own graph)
+        for nt in range(1, 7):
+            run(shape(0, nt, 2, 1))
+        assert stats() == (8, 6, 9, 1)
+        got = run(C)                                    # still cached: a hit
+        assert stats() == (8, 7, 9, 1)
+        for k in got:
+            assert np.array_equal(got[k], first["C"][k]), ("C after an eviction", k)
+        run(shape(0, 7, 2, 1))                          # evicts B, now the least recently used
+        assert stats() == (8, 7, 10, 2)
+        got = run(B)                                    # a miss again: eager pass, then recaptured
+        assert stats() == (8, 7, 11, 3)
+        for k in got:
+            assert np.array_equal(got[k], first["B"][k]), ("B recaptured", k)
+        # a shape beyond the plan is rejected and changes nothing
+        before = stats()
+        assert lib.vla_step_run_shape(r.plan, shape(2, 22, cfg.dit.chunk, cfg.steps)) == lib.VLA_ERR_SHAPE
+        assert stats() == before
+    finally:
+        r.close()

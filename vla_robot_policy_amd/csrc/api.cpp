@@ -1059,23 +1059,44 @@ struct vla_step_plan {
   hipGraphExec_t exec = nullptr;
   int nodes = 0;
   std::vector<LaunchRec> recs;   // the captured launches, in order
+  // Split-K and phase counters of the plan's own shape. Every kernel leaves
+  // the counters it uses at zero, so a pass can start without clearing them
+  // only when the last pass on this workspace had the same layout.
+  unsigned* cnt = nullptr;
+  int ncnt = 0;
+  vla_step_shape zeroed{};       // layout whose counters are known to be zero
+  bool zeroed_valid = false;
+  // graphs of other shapes (vla_step_run_shape), least recently used evicted
+  struct Entry {
+    vla_step_shape shape{};
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int nodes = 0;
+    unsigned* cnt = nullptr;
+    int ncnt = 0;
+    uint64_t used = 0;
+  };
+  std::vector<Entry> cache;
+  uint64_t tick = 0;
+  vla_step_cache_stats stats{};
 };
 
 namespace {
 
-vla_status step_sched(Ctx& c, const vla_step_plan& P) {
+vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) {
   const vla_block_cfg& cfg = P.bb.cfg;
   const int H = cfg.hidden;
+  const bool vit = P.has_vit && sh.n_images > 0;
   int n_vis = 0;
-  if (P.has_vit) {
+  if (vit) {
     const int grid = P.vit.cfg.image / P.vit.cfg.patch;
-    n_vis = P.shape.n_images * (grid * grid) / (P.vit.cfg.merge * P.vit.cfg.merge);
+    n_vis = sh.n_images * (grid * grid) / (P.vit.cfg.merge * P.vit.cfg.merge);
   }
-  const int S = n_vis + P.shape.n_text;
+  const int S = n_vis + sh.n_text;
   BackboneBufs b = take_backbone_bufs(c, cfg, S);
   uint16_t* hid = c.take<uint16_t>((size_t)S * H);
   uint16_t* ctx = c.take<uint16_t>((size_t)S * P.dit.cfg.ctx_dim);
-  if (P.has_vit) VLA_TRY(sched_vit(c, P.vit, P.io.images, P.shape.n_images, b.xs.x, H, nullptr));
+  if (vit) VLA_TRY(sched_vit(c, P.vit, P.io.images, sh.n_images, b.xs.x, H, nullptr));
   c.label = "llm.stage";
   VLA_TRY(stage_stream(c, b.xs, S, H, P.io.text, 0, n_vis, S));
   VLA_TRY(sched_layers(c, cfg, P.bb.layers, P.bb.n_layers, b, S));
@@ -1092,7 +1113,7 @@ vla_status step_sched(Ctx& c, const vla_step_plan& P) {
     a.c = ctx; a.ldc = P.dit.cfg.ctx_dim;
     VLA_TRY(gemm(c, a, {cfg.wdtype, A_BF16, E_STORE}));
   }
-  DitIO io{ctx, S, P.io.noise, P.shape.chunk, P.shape.action_dim, P.shape.steps, P.io.actions, P.io.velocities};
+  DitIO io{ctx, S, P.io.noise, sh.chunk, sh.action_dim, sh.steps, P.io.actions, P.io.velocities};
   return sched_dit(c, P.dit, io);
 }
 
@@ -1148,7 +1169,7 @@ size_t vla_step_workspace_bytes(const vla_model* model, const vla_step_shape* sh
   vla_step_plan P;
   fill_plan(P, model, shape);
   size_t need = 0;
-  if (two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, P); }) != VLA_OK) return 0;
+  if (two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, P, P.shape); }) != VLA_OK) return 0;
   return need;
 }
 
@@ -1163,7 +1184,7 @@ vla_status vla_step_plan_create(const vla_model* model, const vla_step_shape* sh
   fill_plan(*P, model, shape);
   P->io = *io;
   size_t need = 0;
-  vla_status s = two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, *P); });
+  vla_status s = two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, *P, P->shape); });
   if (s != VLA_OK) { delete P; return s; }
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) { delete P; return fail(VLA_ERR_INVALID_ARG, "workspace null or not 256-byte aligned"); }
   if (ws_bytes < need) { delete P; return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need); }
@@ -1173,39 +1194,66 @@ vla_status vla_step_plan_create(const vla_model* model, const vla_step_shape* sh
   return VLA_OK;
 }
 
-vla_status vla_step_run(vla_step_plan* plan, hipStream_t stream) {
-  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
-  return two_pass(plan->ws, plan->ws_bytes, stream, nullptr, [&](Ctx& c) { return step_sched(c, *plan); });
+}  // extern "C"
+
+namespace {
+
+bool same_shape(const vla_step_shape& a, const vla_step_shape& b) {
+  return a.n_images == b.n_images && a.n_text == b.n_text && a.chunk == b.chunk && a.action_dim == b.action_dim &&
+         a.steps == b.steps;
 }
 
-vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
-  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
-  if (plan->exec) return fail(VLA_ERR_STATE, "plan already captured");
-  // warm-up pass (also clears the self-resetting split-K counters)
-  VLA_TRY(vla_step_run(plan, stream));
+// A shape the plan's buffers can serve: every count at most the plan's
+// (inputs and outputs are used as packed prefixes), the same action width,
+// and a workspace need that fits what the plan was given.
+vla_status check_sub_shape(const vla_step_plan& P, const vla_step_shape& s) {
+  vla_model m{P.has_vit ? &P.vit : nullptr, &P.bb, P.w_proj, P.s_proj, P.b_proj, &P.dit};
+  VLA_TRY(check_step(&m, &s));
+  const vla_step_shape& M = P.shape;
+  if (s.n_images > M.n_images || s.n_text > M.n_text || s.chunk > M.chunk || s.steps > M.steps)
+    return fail(VLA_ERR_SHAPE, "step shape (%d images, %d text, chunk %d, %d steps) exceeds the plan's (%d, %d, %d, %d)",
+                s.n_images, s.n_text, s.chunk, s.steps, M.n_images, M.n_text, M.chunk, M.steps);
+  if (s.action_dim != M.action_dim)
+    return fail(VLA_ERR_SHAPE, "step action_dim %d != the plan's %d", s.action_dim, M.action_dim);
+  size_t need = 0;
+  VLA_TRY(two_pass(nullptr, 0, nullptr, &need, [&](Ctx& c) { return step_sched(c, P, s); }));
+  if (need > P.ws_bytes) return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < %zu required by this shape", P.ws_bytes, need);
+  return VLA_OK;
+}
+
+struct Captured {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int nodes = 0;
+  unsigned* cnt = nullptr;
+  int ncnt = 0;
+};
+
+// Record one pass of shape `sh` into a graph (nothing runs). The counters
+// must be zero when the graph starts; the caller arranges that.
+vla_status capture_pass(const vla_step_plan& P, const vla_step_shape& sh, std::vector<LaunchRec>* recs, Captured& out) {
   hipStream_t cs = nullptr;
   VLA_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
-  VLA_HIP(hipStreamSynchronize(stream));
   vla_status s = VLA_OK;
   hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) { (void)hipStreamDestroy(cs); return fail(VLA_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)); }
   {
-    // The counters are already zero after the warm-up pass and every kernel
-    // leaves them zero, so the captured pass launches no clearing node.
     Ctx p0;
     p0.plan = true;
-    s = step_sched(p0, *plan);
+    s = step_sched(p0, P, sh);
     if (s == VLA_OK) {
       size_t fixed = p0.off;
       Ctx c;
-      c.plan = false; c.base = (char*)plan->ws; c.cap = plan->ws_bytes; c.st = cs;
+      c.plan = false; c.base = (char*)P.ws; c.cap = P.ws_bytes; c.st = cs;
       c.off = fixed;
       c.take_scratch(p0);
       c.off = 0;
-      plan->recs.clear();
-      c.recs = &plan->recs;
-      s = step_sched(c, *plan);
-      plan->nodes = c.kernels;
+      if (recs) recs->clear();
+      c.recs = recs;
+      s = step_sched(c, P, sh);
+      out.nodes = c.kernels;
+      out.cnt = c.cnt_tile;
+      out.ncnt = (int)(c.need_tiles + 1);
     }
   }
   hipGraph_t g = nullptr;
@@ -1216,15 +1264,122 @@ vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
   hipGraphExec_t ex = nullptr;
   e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
   if (e != hipSuccess) { (void)hipGraphDestroy(g); return fail(VLA_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e)); }
-  plan->graph = g;
-  plan->exec = ex;
+  out.graph = g;
+  out.exec = ex;
+  return VLA_OK;
+}
+
+// Eager pass of shape `sh` (clears that layout's counters first).
+vla_status run_eager(vla_step_plan& P, const vla_step_shape& sh, hipStream_t stream) {
+  P.zeroed_valid = false;
+  VLA_TRY(two_pass(P.ws, P.ws_bytes, stream, nullptr, [&](Ctx& c) { return step_sched(c, P, sh); }));
+  P.zeroed = sh;
+  P.zeroed_valid = true;
+  return VLA_OK;
+}
+
+// Before a graph of shape `sh` starts: when the last pass on the workspace
+// had another layout, its buffers may cover this layout's counters, so clear
+// them with a fill kernel on the stream.
+vla_status ready_counters(vla_step_plan& P, const vla_step_shape& sh, unsigned* cnt, int ncnt, hipStream_t stream) {
+  if (P.zeroed_valid && same_shape(P.zeroed, sh)) return VLA_OK;
+  Ctx c;
+  c.plan = false; c.st = stream;
+  unsigned z = 0;
+  c.label = "fill";
+  VLA_TRY(launch(c, k_fill_ref(), dim3((ncnt + 255) / 256), dim3(256), 0, {arg(cnt), arg(z), arg(ncnt)}));
+  P.zeroed = sh;
+  P.zeroed_valid = true;
+  return VLA_OK;
+}
+
+void drop(vla_step_plan::Entry& en) {
+  if (en.exec) (void)hipGraphExecDestroy(en.exec);
+  if (en.graph) (void)hipGraphDestroy(en.graph);
+  en.exec = nullptr; en.graph = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+vla_status vla_step_run(vla_step_plan* plan, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  return run_eager(*plan, plan->shape, stream);
+}
+
+vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  if (plan->exec) return fail(VLA_ERR_STATE, "plan already captured");
+  // warm-up pass; it leaves the counters at zero, so the captured pass
+  // launches no clearing node
+  VLA_TRY(vla_step_run(plan, stream));
+  VLA_HIP(hipStreamSynchronize(stream));
+  Captured cp;
+  VLA_TRY(capture_pass(*plan, plan->shape, &plan->recs, cp));
+  plan->graph = cp.graph;
+  plan->exec = cp.exec;
+  plan->nodes = cp.nodes;
+  plan->cnt = cp.cnt;
+  plan->ncnt = cp.ncnt;
   return VLA_OK;
 }
 
 vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream) {
   if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
   if (!plan->exec) return fail(VLA_ERR_STATE, "plan not captured");
+  VLA_TRY(ready_counters(*plan, plan->shape, plan->cnt, plan->ncnt, stream));
   VLA_HIP(hipGraphLaunch(plan->exec, stream));
+  return VLA_OK;
+}
+
+vla_status vla_step_run_shape(vla_step_plan* plan, const vla_step_shape* shape, hipStream_t stream) {
+  if (!plan || !shape) return fail(VLA_ERR_INVALID_ARG, "null plan/shape");
+  const vla_step_shape sh = *shape;
+  plan->tick++;
+  // shapes already captured were validated when they were first seen
+  if (plan->exec && same_shape(sh, plan->shape)) {
+    VLA_TRY(vla_step_replay(plan, stream));
+    plan->stats.hits++;
+    return VLA_OK;
+  }
+  for (auto& en : plan->cache) {
+    if (!same_shape(en.shape, sh)) continue;
+    VLA_TRY(ready_counters(*plan, sh, en.cnt, en.ncnt, stream));
+    VLA_HIP(hipGraphLaunch(en.exec, stream));
+    en.used = plan->tick;
+    plan->stats.hits++;
+    return VLA_OK;
+  }
+  // miss: an eager pass produces this call's outputs, then the shape is
+  // captured for the next calls
+  VLA_TRY(check_sub_shape(*plan, sh));
+  VLA_TRY(run_eager(*plan, sh, stream));
+  VLA_HIP(hipStreamSynchronize(stream));
+  Captured cp;
+  VLA_TRY(capture_pass(*plan, sh, nullptr, cp));
+  plan->stats.misses++;
+  if ((int)plan->cache.size() >= VLA_STEP_GRAPH_CACHE) {
+    auto lru = std::min_element(plan->cache.begin(), plan->cache.end(),
+                                [](const vla_step_plan::Entry& x, const vla_step_plan::Entry& y) { return x.used < y.used; });
+    drop(*lru);
+    plan->cache.erase(lru);
+    plan->stats.evictions++;
+  }
+  vla_step_plan::Entry en;
+  en.shape = sh;
+  en.graph = cp.graph; en.exec = cp.exec; en.nodes = cp.nodes;
+  en.cnt = cp.cnt; en.ncnt = cp.ncnt;
+  en.used = plan->tick;
+  plan->cache.push_back(en);
+  plan->stats.entries = (int32_t)plan->cache.size();
+  return VLA_OK;
+}
+
+vla_status vla_step_cache_info(const vla_step_plan* plan, vla_step_cache_stats* out) {
+  if (!plan || !out) return fail(VLA_ERR_INVALID_ARG, "null plan/out");
+  *out = plan->stats;
+  out->entries = (int32_t)plan->cache.size();
   return VLA_OK;
 }
 
@@ -1239,6 +1394,7 @@ vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_
   if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
   if (!plan->exec) return fail(VLA_ERR_STATE, "plan not captured");
   if (index < 0 || index >= (int32_t)plan->recs.size()) return fail(VLA_ERR_INVALID_ARG, "kernel index %d out of range", index);
+  VLA_TRY(ready_counters(*plan, plan->shape, plan->cnt, plan->ncnt, stream));
   LaunchRec& r = plan->recs[index];
   void* ptrs[16];
   for (size_t i = 0; i < r.args.size(); i++) ptrs[i] = r.args[i].data();
@@ -1248,6 +1404,7 @@ vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_
 
 void vla_step_plan_destroy(vla_step_plan* plan) {
   if (!plan) return;
+  for (auto& en : plan->cache) drop(en);
   if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
   if (plan->graph) (void)hipGraphDestroy(plan->graph);
   delete plan;

@@ -21,6 +21,7 @@ VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_SHAPE, VLA_ERR_UNSUPPORTED, VLA_ERR_WORKSPA
 VLA_F32, VLA_BF16, VLA_FP8_E4M3 = 0, 1, 2
 DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3}
 VLA_BLOCK_QK_NORM = 1
+VLA_STEP_GRAPH_CACHE = 8
 
 
 class VlaError(RuntimeError):
@@ -90,6 +91,10 @@ class StepIO(C.Structure):
     _fields_ = [(n, c_void_p) for n in ("images", "text", "noise", "actions", "hidden_out", "velocities")]
 
 
+class StepCacheStats(C.Structure):
+    _fields_ = [(n, c_int32) for n in ("entries", "hits", "misses", "evictions")]
+
+
 _lib = None
 
 
@@ -122,6 +127,8 @@ def load() -> C.CDLL:
         "vla_step_graph_nodes": (c_int32, [c_void_p]),
         "vla_step_kernel_label": (C.c_char_p, [c_void_p, c_int32]),
         "vla_step_launch_kernel": (S, [c_void_p, c_int32, c_void_p]),
+        "vla_step_run_shape": (S, [c_void_p, POINTER(StepShape), c_void_p]),
+        "vla_step_cache_info": (S, [c_void_p, POINTER(StepCacheStats)]),
         "vla_step_plan_destroy": (None, [c_void_p]),
         "vla_last_error": (C.c_char_p, []),
         "vla_abi_version": (c_int32, []),
@@ -231,6 +238,16 @@ def vla_step_kernel_label(plan, index: int):
 
 def vla_step_launch_kernel(plan, index: int, stream: int = 0) -> int:
     return load().vla_step_launch_kernel(plan, index, stream)
+
+
+def vla_step_run_shape(plan, shape: StepShape, stream: int = 0) -> int:
+    return load().vla_step_run_shape(plan, C.byref(shape), stream)
+
+
+def vla_step_cache_info(plan):
+    out = StepCacheStats()
+    st = load().vla_step_cache_info(plan, C.byref(out))
+    return st, out
 
 
 def vla_step_plan_destroy(plan) -> None:
