@@ -96,3 +96,19 @@ def euler_sample(x0: np.ndarray, K: int, velocity: Callable[[np.ndarray, float],
 def flow_sample(noise: np.ndarray, ctx: np.ndarray, W, d, K: int,
                 record: Optional[List[np.ndarray]] = None) -> np.ndarray:
     return euler_sample(noise, K, lambda a, t: dit_velocity(a, t, ctx, W, d), record)
+
+
+def flow_sample_stale(noise: np.ndarray, ctx_prev: np.ndarray, ctx_cur: np.ndarray, W, d, K: int, n_stale: int,
+                      record: Optional[List[np.ndarray]] = None) -> np.ndarray:
+    """The sampler of one control cycle under V-AEFusion (page "跨XPU平台表征视觉-
+    语言-动作模型：机器人部署中的约束与加速", section 5.3 and Figure 9): the
+    action expert starts denoising while the VLM still works on the current
+    observation, so its first n_stale Euler steps (the stale steps) are
+    conditioned on the previous cycle's context and the remaining K - n_stale
+    steps on the current one. The time grid and the update are the plain
+    sampler's; only the conditioning of each step changes."""
+    if not 0 <= n_stale <= K:
+        raise ValueError(f"n_stale {n_stale} outside [0, {K}]")
+    conds = iter([ctx_prev] * n_stale + [ctx_cur] * (K - n_stale))
+    return euler_sample(noise, K, lambda a, t: dit_velocity(a, t, next(conds), W, d), record)
+

@@ -23,7 +23,9 @@ def projector(h: np.ndarray, W) -> np.ndarray:
     return linear(h, W["proj.w"], W["proj.b"])
 
 
-def vla_step(image, text: np.ndarray, noise: np.ndarray, W, cfg) -> Dict[str, np.ndarray]:
+def vlm(image, text: np.ndarray, W, cfg) -> Dict[str, np.ndarray]:
+    """Vision encoder, backbone and projector: the context the action head
+    attends to ("ctx"), with the intermediate outputs that are graded."""
     out: Dict[str, np.ndarray] = {}
     rows: List[np.ndarray] = []
     if cfg.vit is not None:
@@ -39,8 +41,29 @@ def vla_step(image, text: np.ndarray, noise: np.ndarray, W, cfg) -> Dict[str, np
     E = np.concatenate(rows)
     out["hidden"] = llm.backbone(E, W, cfg)
     out["ctx"] = projector(out["hidden"], W)
+    return out
+
+
+def vla_step(image, text: np.ndarray, noise: np.ndarray, W, cfg) -> Dict[str, np.ndarray]:
+    out = vlm(image, text, W, cfg)
     rec: List[np.ndarray] = []
     out["actions"] = dit.flow_sample(noise, out["ctx"], W, cfg.dit, cfg.steps, rec)
+    out["velocities"] = np.stack(rec)
+    return out
+
+
+def vla_cycle_fused(image, text: np.ndarray, noise: np.ndarray, ctx_prev, W, cfg, n_stale: int) -> Dict[str, np.ndarray]:
+    """One control cycle under V-AEFusion (page "跨XPU平台表征视觉-语言-动作模型：
+    机器人部署中的约束与加速", section 5.3): the VLM of this cycle yields ctx
+    as in vla_step; the action expert's first n_stale steps use ctx_prev, the
+    context of the previous cycle, and the rest use ctx. With no previous
+    cycle (ctx_prev None) every step uses ctx. Returns vla_step's outputs;
+    "ctx" is what the next cycle receives as ctx_prev."""
+    out = vlm(image, text, W, cfg)
+    if ctx_prev is None:
+        ctx_prev, n_stale = out["ctx"], 0
+    rec: List[np.ndarray] = []
+    out["actions"] = dit.flow_sample_stale(noise, ctx_prev, out["ctx"], W, cfg.dit, cfg.steps, n_stale, rec)
     out["velocities"] = np.stack(rec)
     return out
 
