@@ -160,6 +160,69 @@ def shape_cache_bench(cfg, texts, steps, warmup):
     print(json.dumps(line), flush=True)
 
 
+def fused_bench(cfg, n_stale, steps, warmup):
+    """Cycle time of V-AEFusion (the action expert's first n_stale Euler steps
+    on the previous cycle's context, alongside the VLM) against the plain
+    step, both captured and replayed; prints its own JSON line."""
+    import numpy as np
+    import torch
+    from synth import make_inputs, make_weights
+    from vla_robot_policy_amd import lib
+    from vla_robot_policy_amd.device import DeviceWeights, upload_input, workspace
+
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = DeviceWeights(cfg, W, keep_host=False, threads=16)
+    model = dw.build_model()
+    d = cfg.dit
+    dev = torch.device("cuda:0")
+    images = upload_input(I["image"]) if cfg.vit is not None else None
+    text, noise = upload_input(I["text"]), upload_input(I["noise"])
+    actions = torch.empty((d.chunk, d.action_dim), dtype=torch.float32, device=dev)
+    shape = lib.StepShape(n_images=cfg.n_images, n_text=cfg.n_text, chunk=d.chunk, action_dim=d.action_dim,
+                          steps=cfg.steps)
+    io = lib.StepIO(images=None if images is None else images.data_ptr(), text=text.data_ptr(),
+                    noise=noise.data_ptr(), actions=actions.data_ptr(), hidden_out=None, velocities=None)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fused):
+        if fused:
+            need = lib.vla_step_fused_workspace_bytes(model, shape)
+            ws = workspace(need)
+            st, plan = lib.vla_step_plan_create_fused(model, shape, io, n_stale, ws, need)
+        else:
+            need = lib.vla_step_workspace_bytes(model, shape)
+            ws = workspace(need)
+            st, plan = lib.vla_step_plan_create(model, shape, io, ws, need)
+        lib.check(st)
+        try:
+            lib.check(lib.vla_step_capture(plan, stream))
+            for _ in range(warmup):
+                lib.check(lib.vla_step_replay(plan, stream))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                lib.check(lib.vla_step_replay(plan, stream))
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps, lib.vla_step_graph_nodes(plan)
+        finally:
+            lib.vla_step_plan_destroy(plan)
+
+    plain_ms, plain_nodes = timed(False)
+    log(f"plain step {plain_ms:.3f} ms ({plain_nodes} nodes)")
+    fused_ms, fused_nodes = timed(True)
+    log(f"fused cycle {fused_ms:.3f} ms ({fused_nodes} nodes), {n_stale} of {cfg.steps} steps stale")
+    line = {"metric": "ms per control cycle, V-AEFusion (stale action-expert steps alongside the VLM)", "unit": "ms",
+            "value": round(fused_ms, 4), "higher_is_better": False, "steps": steps, "warmup": warmup,
+            "data": "synthetic", "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16",
+            "config": {"workload": f"{cfg.name}: {n_stale} of {cfg.steps} Euler steps stale", "global_batch": 1,
+                       "seq_len": cfg.seq, "euler_steps": cfg.steps},
+            "plain_step_ms": round(plain_ms, 4), "speedup": round(plain_ms / fused_ms, 4),
+            "graph_nodes": {"plain": plain_nodes, "fused": fused_nodes}}
+    print(json.dumps(line), flush=True)
+
+
 def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
     import numpy as np
     import torch
@@ -321,6 +384,9 @@ def main():
     ap.add_argument("--shape-cache", default=None,
                     help="comma-separated text lengths: time each from one plan sized for the longest "
                          "(shape-keyed graphs) and print that line instead of the headline")
+    ap.add_argument("--fused", type=int, default=None, metavar="N_STALE",
+                    help="time V-AEFusion cycles with N_STALE stale Euler steps against the plain step "
+                         "and print that line instead of the headline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device copy of this many bytes --kernel-reps times (counter calibration)")
     a = ap.parse_args()
@@ -339,6 +405,9 @@ def main():
         cfg = cfg.replace(block=dataclasses.replace(cfg.block, qk_norm=True))
     if cfg.kind != "step":
         raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
+    if a.fused is not None:
+        fused_bench(cfg, a.fused, a.steps, a.warmup)
+        return
     if a.shape_cache:
         shape_cache_bench(cfg, [int(t) for t in a.shape_cache.split(",")], a.steps, a.warmup)
         return

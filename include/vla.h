@@ -13,6 +13,9 @@
  *   [A]  "开源 APXInf 把 VLA 推理压到 26 毫秒": capture the whole inference
  *        graph on the first call and replay it every control cycle; FP8
  *        weights.
+ *   [X]  "跨XPU平台表征视觉-语言-动作模型：机器人部署中的约束与加速": section
+ *        5.3 V-AEFusion and Figure 9 (the action expert's first denoising
+ *        steps run on the previous cycle's features, alongside the VLM).
  *
  * Conventions for every entry point
  *   - Activations are row-major [rows, features] (token-major). A Linear
@@ -302,6 +305,31 @@ typedef struct {
   int32_t evictions;  /* graphs destroyed to make room                          */
 } vla_step_cache_stats;
 vla_status vla_step_cache_info(const vla_step_plan* plan, vla_step_cache_stats* out);
+
+/* V-AEFusion plans ([X] 5.3, Figure 9). Every pass of such a plan is one
+ * control cycle c. The action expert's first n_stale Euler steps of cycle c
+ * cross-attend to the context of cycle c-1 and run alongside the vision
+ * encoder, backbone and projector of cycle c (a second stream in an eager
+ * pass, a second branch of the captured graph); the remaining steps wait for
+ * cycle c's context. The first cycle of a plan has no previous context, so
+ * none of its steps is stale. 0 <= n_stale <= steps.
+ *   - The workspace (vla_step_fused_workspace_bytes) holds the cross-
+ *     attention K/V of the last two contexts and separate scratch for the
+ *     two branches; the caller's buffers are as for vla_step_plan_create.
+ *   - vla_step_run runs one cycle eagerly. vla_step_capture runs one cycle
+ *     as its warm-up, then captures one graph per parity of the cycle count;
+ *     vla_step_replay replays the graph of the next cycle. The first pass
+ *     creates a non-blocking stream and three events (default priority),
+ *     kept until vla_step_plan_destroy.
+ *   - vla_step_run_shape returns VLA_ERR_UNSUPPORTED.
+ * Errors as for vla_step_plan_create; VLA_ERR_SHAPE for n_stale outside
+ * [0, steps]. */
+size_t vla_step_fused_workspace_bytes(const vla_model* model, const vla_step_shape* shape);
+vla_status vla_step_plan_create_fused(const vla_model* model, const vla_step_shape* shape, const vla_step_io* io,
+                                      int32_t n_stale, void* ws, size_t ws_bytes, vla_step_plan** out);
+/* Passes run by a plan so far (eager, replayed or through
+ * vla_step_run_shape): the cycle count of a fused plan. */
+int64_t vla_step_cycles(const vla_step_plan* plan);
 
 void vla_step_plan_destroy(vla_step_plan* plan);
 

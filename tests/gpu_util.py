@@ -84,7 +84,7 @@ def run_dit(cfg, dw: DeviceWeights, ctx: torch.Tensor, noise: torch.Tensor, ctx_
 class StepRunner:
     """A vla_step plan over static device I/O buffers."""
 
-    def __init__(self, cfg, dw: DeviceWeights, inputs, with_hidden=True):
+    def __init__(self, cfg, dw: DeviceWeights, inputs, with_hidden=True, n_stale=None):
         self.cfg = cfg
         self.dw = dw
         model = dw.model if dw.model is not None else dw.build_model()
@@ -101,11 +101,24 @@ class StepRunner:
                              noise=self.noise.data_ptr(), actions=self.actions.data_ptr(),
                              hidden_out=None if self.hidden is None else self.hidden.data_ptr(),
                              velocities=self.vel.data_ptr())
-        need = lib.vla_step_workspace_bytes(model, self.shape)
-        assert need > 0, lib.vla_last_error()
-        self.ws = workspace(need)
-        st, self.plan = lib.vla_step_plan_create(model, self.shape, self.io, self.ws, need)
+        if n_stale is None:
+            need = lib.vla_step_workspace_bytes(model, self.shape)
+            assert need > 0, lib.vla_last_error()
+            self.ws = workspace(need)
+            st, self.plan = lib.vla_step_plan_create(model, self.shape, self.io, self.ws, need)
+        else:   # a V-AEFusion plan: every pass is one control cycle
+            need = lib.vla_step_fused_workspace_bytes(model, self.shape)
+            assert need > 0, lib.vla_last_error()
+            self.ws = workspace(need)
+            st, self.plan = lib.vla_step_plan_create_fused(model, self.shape, self.io, n_stale, self.ws, need)
         lib.check(st)
+
+    def load(self, inputs):
+        """Refresh the static input buffers in place (the plan keeps their addresses)."""
+        if self.images is not None:
+            self.images.copy_(upload_input(inputs["image"]))
+        self.text.copy_(upload_input(inputs["text"]))
+        self.noise.copy_(upload_input(inputs["noise"]))
 
     def run(self, stream=0):
         lib.check(lib.vla_step_run(self.plan, stream))

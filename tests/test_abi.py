@@ -122,3 +122,38 @@ def test_step_run_shape_validation():
         lib.vla_step_plan_destroy(plan)
     assert lib.vla_step_run_shape(None, shape) == lib.VLA_ERR_INVALID_ARG
     assert lib.vla_step_cache_info(None)[0] == lib.VLA_ERR_INVALID_ARG
+
+
+def test_fused_plan_validation():
+    """V-AEFusion plans: stale-step count bounds, workspace sizing and the
+    calls a fused plan refuses, all checked on the host."""
+    fake = 1 << 20
+    bl = (lib.BlockWeights * 2)(*[_fake_struct(lib.BlockWeights, fake, q_norm=None, k_norm=None) for _ in range(2)])
+    bb = lib.Backbone(cfg=llm_cfg(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, intermediate=1024), n_layers=2,
+                      layers=bl, final_norm=fake)
+    dc = lib.DitCfg(hidden=512, heads=8, head_dim=64, mlp=2048, layers=2, tdim=256, ctx_dim=512, eps=1e-6,
+                    time_scale=1000.0, freq_base=10000.0, wdtype=lib.VLA_BF16, flags=0)
+    dl = (lib.DitLayer * 2)(*[_fake_struct(lib.DitLayer, fake) for _ in range(2)])
+    d = _fake_struct(lib.Dit, fake, cfg=dc, layers=dl)
+    model = lib.Model(vit=None, backbone=C.pointer(bb), w_proj=fake, s_proj=None, b_proj=fake, dit=C.pointer(d))
+    shape = lib.StepShape(n_images=0, n_text=40, chunk=16, action_dim=7, steps=4)
+    plain = lib.vla_step_workspace_bytes(model, shape)
+    need = lib.vla_step_fused_workspace_bytes(model, shape)
+    # two cross-attention K/V buffers (40 x 2 layers x 2 x 512 bf16 each) and a second scratch
+    assert need >= plain + 40 * 2 * 2 * 512 * 2
+    io = lib.StepIO(images=None, text=fake, noise=fake, actions=fake, hidden_out=None, velocities=None)
+    for bad in (-1, 5):
+        st, plan = lib.vla_step_plan_create_fused(model, shape, io, bad, fake, need)
+        assert st == lib.VLA_ERR_SHAPE and plan is None
+    st, plan = lib.vla_step_plan_create_fused(model, shape, io, 2, fake, need - 256)
+    assert st == lib.VLA_ERR_WORKSPACE and plan is None
+    st, plan = lib.vla_step_plan_create_fused(model, shape, io, 2, fake, need)
+    assert st == lib.VLA_OK, lib.vla_last_error()
+    try:
+        assert lib.vla_step_run_shape(plan, shape) == lib.VLA_ERR_UNSUPPORTED
+        assert lib.vla_step_replay(plan) == lib.VLA_ERR_STATE          # nothing captured yet
+        assert lib.vla_step_cycles(plan) == 0
+        assert lib.vla_step_graph_nodes(plan) == 0
+    finally:
+        lib.vla_step_plan_destroy(plan)
+    assert lib.vla_step_cycles(None) == 0

@@ -114,6 +114,53 @@ def test_step_full_single_camera(gu):
         assert e <= 1e-2, k
 
 
+def test_step_full_single_camera_fused(gu):
+    """V-AEFusion at the single-camera workload (2 of 4 Euler steps stale),
+    captured and replayed: the persistent DiT layer kernel runs alongside the
+    full VLM. Cycle 0 (no previous context) and a cycle whose observation is
+    unchanged must equal the plain step bit for bit; a cycle on a new
+    observation is checked against the oracle's fused cycle."""
+    from oracle.io import Weights, to_f64
+    from oracle.policy import vla_cycle_fused, vlm
+    cfg = get_config(4)
+    W, I0 = _generate(gu, cfg)
+    I1 = make_inputs(cfg.replace(cid=cfg.cid + 100))
+    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
+    plain = {}
+    p = gu.StepRunner(cfg, dw, I0)
+    try:
+        for name, I in (("I0", I0), ("I1", I1)):
+            p.load(I)
+            p.run()
+            plain[name] = p.outputs()
+    finally:
+        p.close()
+    f = gu.StepRunner(cfg, dw, I0, n_stale=2)
+    try:
+        f.capture()                                    # cycle 0 on I0
+        got = f.outputs()
+        for k in got:
+            assert np.array_equal(got[k], plain["I0"][k]), ("cycle 0", k)
+        f.replay()                                     # cycle 1, I0 again
+        got = f.outputs()
+        for k in got:
+            assert np.array_equal(got[k], plain["I0"][k]), ("unchanged observation", k)
+        f.load(I1)
+        f.replay()                                     # cycle 2: stale steps on I0's context
+        got = f.outputs()
+    finally:
+        f.close()
+    Wo = gu.ProgressWeights(W, "oracle")
+    args = lambda I: (to_f64(I["image"]), to_f64(I["text"]), to_f64(I["noise"]))
+    prev = gu.timed("oracle VLM of I0", lambda: vlm(args(I0)[0], args(I0)[1], Wo, cfg))["ctx"]
+    want = gu.timed("oracle fused cycle", lambda: vla_cycle_fused(*args(I1), prev, Wo, cfg, 2))
+    errs = {k: gu.relerr(got[k], want[k]) for k in ("hidden", "actions", "velocities")}
+    gu.say("fused single-camera cycle rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-2, k
+    assert not np.array_equal(got["actions"], plain["I1"]["actions"])   # the stale steps did matter
+
+
 def test_step_full_fp8_long_context(gu):
     cfg = get_config(5)
     gu.say(f"cfg{cfg.cid}: fp8 backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}, chunk {cfg.dit.chunk}")

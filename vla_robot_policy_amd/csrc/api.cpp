@@ -566,32 +566,43 @@ struct DitIO {
   float* actions; float* velocities;
 };
 
-vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
+// The sampler's buffers (all but the context's cross-attention K/V) and the
+// state its parts hand on: the residual stream's row-statistics tiling.
+struct DitState {
+  uint16_t* t1 = nullptr; uint16_t* sc = nullptr; float* mod = nullptr; float* fmod = nullptr;
+  Stream xs{};
+  float* xb[2] = {nullptr, nullptr};
+  float* x1 = nullptr; float* x2 = nullptr;
+  uint16_t* qkv = nullptr; uint16_t* ao = nullptr; uint16_t* q = nullptr; uint16_t* h = nullptr;
+  int* derr = nullptr; uint16_t* aos = nullptr;
+  bool stack = false;
+  int G = 0;
+};
+
+// Buffers of the sampler; clears the layer kernel's counters.
+vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   const vla_dit_cfg& cf = d.cfg;
-  const int D = cf.hidden, L = cf.layers, K = io.K, n = io.n, A = io.A, C = io.ctx_len;
-  const int wt = cf.wdtype;
+  const int D = cf.hidden, L = cf.layers, K = io.K, n = io.n;
   const int mod_w = L * 9 * D;
-  uint16_t* t1 = c.take<uint16_t>((size_t)K * D);
-  uint16_t* sc = c.take<uint16_t>((size_t)K * D);
-  float* mod = c.take<float>((size_t)K * mod_w);
-  float* fmod = c.take<float>((size_t)K * 2 * D);
-  uint16_t* ckv = c.take<uint16_t>((size_t)C * L * 2 * D);
-  Stream xs = take_stream(c, n, D);
-  float* x = xs.x;
+  s.t1 = c.take<uint16_t>((size_t)K * D);
+  s.sc = c.take<uint16_t>((size_t)K * D);
+  s.mod = c.take<float>((size_t)K * mod_w);
+  s.fmod = c.take<float>((size_t)K * 2 * D);
+  s.xs = take_stream(c, n, D);
   // the layer kernel's stream buffers: layer l reads xb[l % 2] and writes
   // xb[(l + 1) % 2] through the per-sublayer buffers x1, x2
-  float* xb[2] = {x, c.take<float>((size_t)n * D)};
-  float* x1 = c.take<float>((size_t)n * D);
-  float* x2 = c.take<float>((size_t)n * D);
-  uint16_t* qkv = c.take<uint16_t>((size_t)n * 3 * D);
-  uint16_t* ao = c.take<uint16_t>((size_t)n * D);
-  uint16_t* q = c.take<uint16_t>((size_t)n * D);
-  uint16_t* h = c.take<uint16_t>((size_t)n * cf.mlp);
-  const int G = cu_count();
-  const bool stack = dit_stack_ok(cf, n, G);
-  int* derr = c.take<int>(64);
-  uint16_t* aos = stack ? c.take<uint16_t>((size_t)n * D) : nullptr;   // the layer kernel's self-attention output
-  if (stack) {
+  s.xb[0] = s.xs.x; s.xb[1] = c.take<float>((size_t)n * D);
+  s.x1 = c.take<float>((size_t)n * D);
+  s.x2 = c.take<float>((size_t)n * D);
+  s.qkv = c.take<uint16_t>((size_t)n * 3 * D);
+  s.ao = c.take<uint16_t>((size_t)n * D);
+  s.q = c.take<uint16_t>((size_t)n * D);
+  s.h = c.take<uint16_t>((size_t)n * cf.mlp);
+  s.G = cu_count();
+  s.stack = dit_stack_ok(cf, n, s.G);
+  s.derr = c.take<int>(64);
+  s.aos = s.stack ? c.take<uint16_t>((size_t)n * D) : nullptr;   // the layer kernel's self-attention output
+  if (s.stack) {
     // phase and tile counters of the layer kernel live in the shared counter
     // array (every kernel leaves its counters at zero); slice partials in the
     // split-K scratch
@@ -602,81 +613,109 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     unsigned z = 0;
     VLA_TRY(launch(c, k_fill_ref(), dim3((nclr + 255) / 256), dim3(256), 0, {arg(c.cnt_tile), arg(z), arg(nclr)}));
     int one = 1;
-    VLA_TRY(launch(c, k_fill_ref(), dim3(1), dim3(256), 0, {arg(derr), arg(z), arg(one)}));
+    VLA_TRY(launch(c, k_fill_ref(), dim3(1), dim3(256), 0, {arg(s.derr), arg(z), arg(one)}));
   }
+  return VLA_OK;
+}
 
+// Conditioning of every step from the fixed time grid: SiLU(c_k), the adaLN
+// modulations of every layer and the final-layer modulation.
+vla_status dit_conditioning(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
+  const vla_dit_cfg& cf = d.cfg;
+  const int D = cf.hidden, L = cf.layers, K = io.K, wt = cf.wdtype;
+  const int mod_w = L * 9 * D;
   {  // phi(t_k) -> Linear -> SiLU
     c.label = "dit.time_fc1";
     GemmArgs a = gargs();
     a.M = K; a.N = D; a.K = cf.tdim;
     a.tsteps = K; a.time_scale = cf.time_scale; a.freq_base = cf.freq_base; a.half = cf.tdim / 2;
     a.w = d.w_t1; a.ldw = cf.tdim; a.wscale = d.s_t1; a.bias = d.b_t1; a.act = ACT_SILU;
-    a.c = t1; a.ldc = D;
+    a.c = s.t1; a.ldc = D;
     VLA_TRY(gemm(c, a, {wt, A_TIME, E_STORE}));
   }
   {  // Linear -> SiLU: SiLU(c_k) for every step
     c.label = "dit.time_fc2";
     GemmArgs a = gargs();
     a.M = K; a.N = D; a.K = D;
-    a.a = t1; a.lda = D;
+    a.a = s.t1; a.lda = D;
     a.w = d.w_t2; a.ldw = D; a.wscale = d.s_t2; a.bias = d.b_t2; a.act = ACT_SILU;
-    a.c = sc; a.ldc = D;
+    a.c = s.sc; a.ldc = D;
     VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
   {  // adaLN modulations of every layer for every step (one launch)
     c.label = "dit.adaln";
     GemmArgs a = gargs();
     a.M = K; a.N = mod_w; a.K = D;
-    a.a = sc; a.lda = D;
+    a.a = s.sc; a.lda = D;
     a.w = d.w_ada; a.ldw = D; a.wscale = d.s_ada; a.bias = d.b_ada;
-    a.c = mod; a.ldc = mod_w; a.c_f32 = 1;
+    a.c = s.mod; a.ldc = mod_w; a.c_f32 = 1;
     VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
   {  // final-layer modulation
     c.label = "dit.final_mod";
     GemmArgs a = gargs();
     a.M = K; a.N = 2 * D; a.K = D;
-    a.a = sc; a.lda = D;
+    a.a = s.sc; a.lda = D;
     a.w = d.w_f; a.ldw = D; a.wscale = d.s_f; a.bias = d.b_f;
-    a.c = fmod; a.ldc = 2 * D; a.c_f32 = 1;
+    a.c = s.fmod; a.ldc = 2 * D; a.c_f32 = 1;
     VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
-  {  // cross-attention K/V of every layer from the fixed context (one launch)
-    c.label = "dit.cross_kv";
-    GemmArgs a = gargs();
-    a.M = C; a.N = L * 2 * D; a.K = cf.ctx_dim;
-    a.a = io.ctx; a.lda = cf.ctx_dim;
-    a.w = d.w_ckv; a.ldw = cf.ctx_dim; a.wscale = d.s_ckv; a.bias = d.b_ckv;
-    a.c = ckv; a.ldc = L * 2 * D;
-    VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
-  }
+  return VLA_OK;
+}
+
+// Cross-attention K/V of every layer from a context (one launch).
+vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16_t* ckv) {
+  const vla_dit_cfg& cf = d.cfg;
+  const int D = cf.hidden, L = cf.layers;
+  c.label = "dit.cross_kv";
+  GemmArgs a = gargs();
+  a.M = C; a.N = L * 2 * D; a.K = cf.ctx_dim;
+  a.a = ctx; a.lda = cf.ctx_dim;
+  a.w = d.w_ckv; a.ldw = cf.ctx_dim; a.wscale = d.s_ckv; a.bias = d.b_ckv;
+  a.c = ckv; a.ldc = L * 2 * D;
+  return gemm(c, a, {cf.wdtype, A_BF16, E_STORE});
+}
+
+// a_0 = x0 -> x = a_0 W_in^T + b_in (+ row statistics)
+vla_status dit_in_proj(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
+  const vla_dit_cfg& cf = d.cfg;
+  KernelRef tail{};
+  euler_tail_lookup(cf.wdtype, &tail);
+  TailArgs t{};
+  t.n = io.n; t.D = cf.hidden; t.A = io.A; t.K = io.K; t.eps = cf.eps;
+  t.a_in = io.x0; t.a_out = io.actions;
+  t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = s.xs.x; t.rs_out = s.xs.part;
+  s.xs.rs.T = 1; s.xs.rs.tw = cf.hidden;
+  c.label = "dit.in_proj";
+  return launch(c, tail.fn, dim3(io.n), dim3(256), (size_t)(cf.hidden + io.A) * sizeof(float), {arg(t)});
+}
+
+// Euler steps k0 .. k1-1 of the K-step sampler, cross-attending to `ckv`.
+vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, const uint16_t* ckv, int k0, int k1) {
+  const vla_dit_cfg& cf = d.cfg;
+  const int D = cf.hidden, L = cf.layers, K = io.K, n = io.n, A = io.A, C = io.ctx_len;
+  const int wt = cf.wdtype;
+  const int mod_w = L * 9 * D;
+  float* x = s.xs.x;
+  Stream& xs = s.xs;
   KernelRef tail{};
   euler_tail_lookup(wt, &tail);
   const size_t tail_smem = (size_t)(D + A) * sizeof(float);
-  {  // a_0 = x0 -> x = a_0 W_in^T + b_in (+ row statistics)
-    TailArgs t{};
-    t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
-    t.a_in = io.x0; t.a_out = io.actions;
-    t.w_in = d.w_in; t.s_in = d.s_in; t.b_in = d.b_in; t.x_out = x; t.rs_out = xs.part;
-    xs.rs.T = 1; xs.rs.tw = D;
-    c.label = "dit.in_proj";
-    VLA_TRY(launch(c, tail.fn, dim3(n), dim3(256), tail_smem, {arg(t)}));
-  }
   KernelRef lk{};
-  if (stack && !dit_layer_lookup(wt, D, &lk)) return fail(VLA_ERR_UNSUPPORTED, "dit: no layer kernel for wdtype %d", wt);
-  if (stack && !c.plan && lk.smem > 64 * 1024) VLA_TRY(allow_smem(lk));
-  for (int k = 0; k < K; k++) {
+  if (s.stack && !dit_layer_lookup(wt, D, &lk)) return fail(VLA_ERR_UNSUPPORTED, "dit: no layer kernel for wdtype %d", wt);
+  if (s.stack && !c.plan && lk.smem > 64 * 1024) VLA_TRY(allow_smem(lk));
+  for (int k = k0; k < k1; k++) {
     for (int l = 0; l < L; l++) {
       const vla_dit_layer& w = d.layers[l];
-      const float* m = mod ? mod + (size_t)k * mod_w + (size_t)l * 9 * D : nullptr;
+      const float* m = s.mod ? s.mod + (size_t)k * mod_w + (size_t)l * 9 * D : nullptr;
       auto mv = [&](int j) { return m ? m + (size_t)j * D : nullptr; };
-      if (stack) {  // the whole layer in one persistent launch
+      if (s.stack) {  // the whole layer in one persistent launch
         c.label = "dit.layer";
         DitLayerArgs a{};
         a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
         a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
-        a.x_in = xb[l & 1]; a.x1 = x1; a.x2 = x2; a.x_out = xb[(l + 1) & 1];
-        a.qkv = qkv; a.q = q; a.aos = aos; a.aoc = ao; a.h = h;
+        a.x_in = s.xb[l & 1]; a.x1 = s.x1; a.x2 = s.x2; a.x_out = s.xb[(l + 1) & 1];
+        a.qkv = s.qkv; a.q = s.q; a.aos = s.aos; a.aoc = s.ao; a.h = s.h;
         a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.cv = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldc = L * 2 * D;
         a.mod = m;
         const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
@@ -685,8 +724,8 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = wt == VLA_FP8_E4M3 ? ss[i] : nullptr; a.b[i] = bs[i]; }
         const bool last_launch = k == K - 1 && l == L - 1;
         a.wq_next = last_launch ? nullptr : d.layers[(l + 1) % L].w_qkv;
-        a.part = c.part; a.cnt = c.cnt_tile; a.err = derr;
-        VLA_TRY(launch(c, lk.fn, dim3(G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
+        a.part = c.part; a.cnt = c.cnt_tile; a.err = s.derr;
+        VLA_TRY(launch(c, lk.fn, dim3(s.G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
         continue;
       }
       {  // adaLN(LN) -> self-attn QKV
@@ -695,16 +734,16 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         a.M = n; a.N = 3 * D; a.K = D;
         a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(1); a.g_plus_one = 1; a.bsh = mv(0);
         a.w = w.w_qkv; a.ldw = D; a.wscale = w.s_qkv; a.bias = w.b_qkv;
-        a.c = qkv; a.ldc = 3 * D;
+        a.c = s.qkv; a.ldc = 3 * D;
         VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
       }
       {
         c.label = "dit.sa_attn";
         AttnArgs a{};
-        a.q = qkv; a.ldq = 3 * D;
-        a.k = qkv ? qkv + D : nullptr; a.ldk = 3 * D;
-        a.v = qkv ? qkv + 2 * D : nullptr; a.ldv = 3 * D;
-        a.o = ao; a.ldo = D;
+        a.q = s.qkv; a.ldq = 3 * D;
+        a.k = s.qkv ? s.qkv + D : nullptr; a.ldk = 3 * D;
+        a.v = s.qkv ? s.qkv + 2 * D : nullptr; a.ldv = 3 * D;
+        a.o = s.ao; a.ldo = D;
         a.Sq = n; a.Sk = n; a.Hq = cf.heads; a.Hkv = cf.heads; a.D = cf.head_dim; a.causal = 0;
         VLA_TRY(attention(c, a, false));
       }
@@ -712,7 +751,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
       c.label = "dit.sa_o";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = D;
-        a.a = ao; a.lda = D;
+        a.a = s.ao; a.lda = D;
         a.w = w.w_o; a.ldw = D; a.wscale = w.s_o; a.bias = w.b_o; a.gate = mv(2);
         a.x = x; a.ldx = D; a.rs_out = xs.part;
         VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
@@ -723,16 +762,16 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         a.M = n; a.N = D; a.K = D;
         a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(4); a.g_plus_one = 1; a.bsh = mv(3);
         a.w = w.w_cq; a.ldw = D; a.wscale = w.s_cq; a.bias = w.b_cq;
-        a.c = q; a.ldc = D;
+        a.c = s.q; a.ldc = D;
         VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
       }
       {
         c.label = "dit.ca_attn";
         AttnArgs a{};
-        a.q = q; a.ldq = D;
+        a.q = s.q; a.ldq = D;
         a.k = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.ldk = L * 2 * D;
         a.v = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldv = L * 2 * D;
-        a.o = ao; a.ldo = D;
+        a.o = s.ao; a.ldo = D;
         a.Sq = n; a.Sk = C; a.Hq = cf.heads; a.Hkv = cf.heads; a.D = cf.head_dim; a.causal = 0;
         VLA_TRY(attention(c, a, false));
       }
@@ -740,7 +779,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
       c.label = "dit.ca_o";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = D;
-        a.a = ao; a.lda = D;
+        a.a = s.ao; a.lda = D;
         a.w = w.w_co; a.ldw = D; a.wscale = w.s_co; a.bias = w.b_co; a.gate = mv(5);
         a.x = x; a.ldx = D; a.rs_out = xs.part;
         VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
@@ -751,14 +790,14 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
         a.M = n; a.N = cf.mlp; a.K = D;
         a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(7); a.g_plus_one = 1; a.bsh = mv(6);
         a.w = w.w_up; a.ldw = D; a.wscale = w.s_up; a.bias = w.b_up; a.act = ACT_GELU;
-        a.c = h; a.ldc = cf.mlp;
+        a.c = s.h; a.ldc = cf.mlp;
         VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
       }
       {  // MLP down, gated residual
       c.label = "dit.mlp_down";
         GemmArgs a = gargs();
         a.M = n; a.N = D; a.K = cf.mlp;
-        a.a = h; a.lda = cf.mlp;
+        a.a = s.h; a.lda = cf.mlp;
         a.w = w.w_down; a.ldw = cf.mlp; a.wscale = w.s_down; a.bias = w.b_down; a.gate = mv(8);
         a.x = x; a.ldx = D; a.rs_out = xs.part;
         VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
@@ -767,9 +806,9 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     {  // velocity head + Euler update (+ input projection for the next step)
       TailArgs t{};
       t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
-      t.x = stack ? xb[L & 1] : x;   // the last layer's output
-      t.shift = fmod ? fmod + (size_t)k * 2 * D : nullptr;
-      t.scale = fmod ? fmod + (size_t)k * 2 * D + D : nullptr;
+      t.x = s.stack ? s.xb[L & 1] : x;   // the last layer's output
+      t.shift = s.fmod ? s.fmod + (size_t)k * 2 * D : nullptr;
+      t.scale = s.fmod ? s.fmod + (size_t)k * 2 * D + D : nullptr;
       t.w_out = d.w_out; t.s_out = d.s_out; t.b_out = d.b_out;
       t.a_in = io.actions; t.a_out = io.actions;
       t.v_out = io.velocities ? io.velocities + (size_t)k * n * A : nullptr;
@@ -780,6 +819,16 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
     }
   }
   return VLA_OK;
+}
+
+vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
+  DitState s;
+  VLA_TRY(dit_begin(c, d, io, s));
+  uint16_t* ckv = c.take<uint16_t>((size_t)io.ctx_len * d.cfg.layers * 2 * d.cfg.hidden);
+  VLA_TRY(dit_conditioning(c, d, io, s));
+  VLA_TRY(dit_cross_kv(c, d, io.ctx, io.ctx_len, ckv));
+  VLA_TRY(dit_in_proj(c, d, io, s));
+  return dit_steps(c, d, io, s, ckv, 0, io.K);
 }
 
 // ------------------------------------------------------------------ ViT
@@ -1041,6 +1090,10 @@ size_t vla_vit_workspace_bytes(const vla_vit* vit, int32_t n_images) {
 }  // extern "C"
 
 // ================================================================== step plan
+// Events of a fused cycle: fork (both branches start after the work the
+// caller queued), context ready, action branch done.
+struct FusedEvents { hipEvent_t fork = nullptr, ctx_ready = nullptr, done = nullptr; };
+
 struct vla_step_plan {
   // deep copies of the host-side descriptors
   vla_vit vit{};
@@ -1079,11 +1132,21 @@ struct vla_step_plan {
   std::vector<Entry> cache;
   uint64_t tick = 0;
   vla_step_cache_stats stats{};
+  int64_t cycles = 0;            // passes run (eager or replayed)
+  // V-AEFusion plans (n_stale >= 0): the action branch's stream, the
+  // cycle's events, and one graph per parity of the cycle count
+  int n_stale = -1;
+  hipStream_t aux = nullptr;
+  FusedEvents fev{};
+  hipGraph_t fgraph[2] = {nullptr, nullptr};
+  hipGraphExec_t fexec[2] = {nullptr, nullptr};
 };
 
 namespace {
 
-vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) {
+// Vision encoder, backbone with final norm and projector of one step: the
+// context rows the action expert attends to.
+vla_status vlm_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh, uint16_t*& ctx, int& S) {
   const vla_block_cfg& cfg = P.bb.cfg;
   const int H = cfg.hidden;
   const bool vit = P.has_vit && sh.n_images > 0;
@@ -1092,10 +1155,10 @@ vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) 
     const int grid = P.vit.cfg.image / P.vit.cfg.patch;
     n_vis = sh.n_images * (grid * grid) / (P.vit.cfg.merge * P.vit.cfg.merge);
   }
-  const int S = n_vis + sh.n_text;
+  S = n_vis + sh.n_text;
   BackboneBufs b = take_backbone_bufs(c, cfg, S);
   uint16_t* hid = c.take<uint16_t>((size_t)S * H);
-  uint16_t* ctx = c.take<uint16_t>((size_t)S * P.dit.cfg.ctx_dim);
+  ctx = c.take<uint16_t>((size_t)S * P.dit.cfg.ctx_dim);
   if (vit) VLA_TRY(sched_vit(c, P.vit, P.io.images, sh.n_images, b.xs.x, H, nullptr));
   c.label = "llm.stage";
   VLA_TRY(stage_stream(c, b.xs, S, H, P.io.text, 0, n_vis, S));
@@ -1113,8 +1176,94 @@ vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) 
     a.c = ctx; a.ldc = P.dit.cfg.ctx_dim;
     VLA_TRY(gemm(c, a, {cfg.wdtype, A_BF16, E_STORE}));
   }
+  return VLA_OK;
+}
+
+vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) {
+  uint16_t* ctx = nullptr;
+  int S = 0;
+  VLA_TRY(vlm_sched(c, P, sh, ctx, S));
   DitIO io{ctx, S, P.io.noise, sh.chunk, sh.action_dim, sh.steps, P.io.actions, P.io.velocities};
   return sched_dit(c, P.dit, io);
+}
+
+// One V-AEFusion cycle on two contexts. `cv` (the caller's stream) runs the
+// vision encoder, backbone, projector and the cross-attention K/V of this
+// cycle into ckv[parity]; `ca` (the action branch) computes the conditioning,
+// the input projection and the first n_stale Euler steps against ckv[parity^1],
+// the previous cycle's, while the VLM runs, then the remaining steps against
+// ckv[parity] once it is ready. Both cross-K/V buffers come first in the
+// layout, so every cycle finds them at the same addresses.
+vla_status fused_sched(Ctx& cv, Ctx& ca, const vla_step_plan& P, const vla_step_shape& sh, int n_stale, int parity,
+                       const FusedEvents* ev, bool clear) {
+  const vla_dit_cfg& cf = P.dit.cfg;
+  const int grid = P.has_vit ? P.vit.cfg.image / P.vit.cfg.patch : 0;
+  const int n_vis = P.has_vit && sh.n_images > 0 ? sh.n_images * grid * grid / (P.vit.cfg.merge * P.vit.cfg.merge) : 0;
+  const int C = n_vis + sh.n_text;
+  const size_t ckv_elems = (size_t)C * cf.layers * 2 * cf.hidden;
+  uint16_t* ckv2 = cv.take<uint16_t>(2 * ckv_elems);
+  uint16_t* cur = ckv2 ? ckv2 + (size_t)parity * ckv_elems : nullptr;
+  uint16_t* prev = ckv2 ? ckv2 + (size_t)(parity ^ 1) * ckv_elems : nullptr;
+  const bool live = !cv.plan;
+  if (live) {
+    VLA_HIP(hipEventRecord(ev->fork, cv.st));
+    VLA_HIP(hipStreamWaitEvent(ca.st, ev->fork, 0));
+  }
+  if (clear) { VLA_TRY(zero_counters(cv)); VLA_TRY(zero_counters(ca)); }
+  DitIO io{nullptr, C, P.io.noise, sh.chunk, sh.action_dim, sh.steps, P.io.actions, P.io.velocities};
+  DitState ds;
+  VLA_TRY(dit_begin(ca, P.dit, io, ds));
+  VLA_TRY(dit_conditioning(ca, P.dit, io, ds));
+  VLA_TRY(dit_in_proj(ca, P.dit, io, ds));
+  VLA_TRY(dit_steps(ca, P.dit, io, ds, prev, 0, n_stale));
+  uint16_t* ctx = nullptr;
+  int S = 0;
+  VLA_TRY(vlm_sched(cv, P, sh, ctx, S));
+  VLA_TRY(dit_cross_kv(cv, P.dit, ctx, S, cur));
+  if (live) {
+    VLA_HIP(hipEventRecord(ev->ctx_ready, cv.st));
+    VLA_HIP(hipStreamWaitEvent(ca.st, ev->ctx_ready, 0));
+  }
+  VLA_TRY(dit_steps(ca, P.dit, io, ds, cur, n_stale, sh.steps));
+  if (live) {
+    VLA_HIP(hipEventRecord(ev->done, ca.st));
+    VLA_HIP(hipStreamWaitEvent(cv.st, ev->done, 0));
+  }
+  return VLA_OK;
+}
+
+// Workspace of a fused plan: [VLM buffers][action buffers][VLM scratch]
+// [action scratch]; each branch has its own split-K scratch and counters.
+struct FusedLayout {
+  size_t off_b = 0, scr_a = 0, scr_b = 0, need = 0;
+  Ctx a0, b0;   // plan passes: sizes and scratch needs of each branch
+};
+
+vla_status fused_layout(const vla_step_plan& P, FusedLayout& L) {
+  L.a0.plan = true;
+  L.b0.plan = true;
+  VLA_TRY(fused_sched(L.a0, L.b0, P, P.shape, 0, 0, nullptr, false));
+  size_t off = align_up(L.a0.off, 256);
+  L.off_b = off;
+  off += align_up(L.b0.off, 256);
+  Ctx t;
+  t.plan = true; t.off = off;
+  t.take_scratch(L.a0);
+  L.scr_a = off;
+  off = align_up(t.off, 256);
+  Ctx u;
+  u.plan = true; u.off = off - L.off_b;
+  L.scr_b = u.off;
+  u.take_scratch(L.b0);
+  L.need = L.off_b + u.off;
+  return VLA_OK;
+}
+
+void fused_ctxs(const vla_step_plan& P, const FusedLayout& L, hipStream_t sv, hipStream_t sa, Ctx& cv, Ctx& ca) {
+  cv.plan = false; cv.base = (char*)P.ws; cv.cap = P.ws_bytes; cv.st = sv;
+  cv.off = L.scr_a; cv.take_scratch(L.a0); cv.off = 0;
+  ca.plan = false; ca.base = (char*)P.ws + L.off_b; ca.cap = P.ws_bytes - L.off_b; ca.st = sa;
+  ca.off = L.scr_b; ca.take_scratch(L.b0); ca.off = 0;
 }
 
 vla_status check_step(const vla_model* m, const vla_step_shape* s) {
@@ -1188,6 +1337,38 @@ vla_status vla_step_plan_create(const vla_model* model, const vla_step_shape* sh
   if (s != VLA_OK) { delete P; return s; }
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) { delete P; return fail(VLA_ERR_INVALID_ARG, "workspace null or not 256-byte aligned"); }
   if (ws_bytes < need) { delete P; return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need); }
+  P->ws = ws;
+  P->ws_bytes = ws_bytes;
+  *out = P;
+  return VLA_OK;
+}
+
+size_t vla_step_fused_workspace_bytes(const vla_model* model, const vla_step_shape* shape) {
+  if (check_step(model, shape) != VLA_OK) return 0;
+  vla_step_plan P;
+  fill_plan(P, model, shape);
+  FusedLayout L;
+  if (fused_layout(P, L) != VLA_OK) return 0;
+  return L.need;
+}
+
+vla_status vla_step_plan_create_fused(const vla_model* model, const vla_step_shape* shape, const vla_step_io* io,
+                                      int32_t n_stale, void* ws, size_t ws_bytes, vla_step_plan** out) {
+  if (!out) return fail(VLA_ERR_INVALID_ARG, "null plan out pointer");
+  *out = nullptr;
+  VLA_TRY(check_step(model, shape));
+  if (n_stale < 0 || n_stale > shape->steps) return fail(VLA_ERR_SHAPE, "n_stale %d outside [0, %d]", n_stale, shape->steps);
+  if (!io || !io->text || !io->noise || !io->actions || (shape->n_images > 0 && !io->images))
+    return fail(VLA_ERR_INVALID_ARG, "step io: null buffer");
+  vla_step_plan* P = new vla_step_plan();
+  fill_plan(*P, model, shape);
+  P->io = *io;
+  P->n_stale = n_stale;
+  FusedLayout L;
+  vla_status s = fused_layout(*P, L);
+  if (s != VLA_OK) { delete P; return s; }
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) { delete P; return fail(VLA_ERR_INVALID_ARG, "workspace null or not 256-byte aligned"); }
+  if (ws_bytes < L.need) { delete P; return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.need); }
   P->ws = ws;
   P->ws_bytes = ws_bytes;
   *out = P;
@@ -1293,6 +1474,61 @@ vla_status ready_counters(vla_step_plan& P, const vla_step_shape& sh, unsigned* 
   return VLA_OK;
 }
 
+// The action branch's stream and the cycle's events (default priority),
+// made on the first pass of a fused plan and kept until it is destroyed.
+vla_status fused_ready(vla_step_plan& P) {
+  if (!P.aux) VLA_HIP(hipStreamCreateWithFlags(&P.aux, hipStreamNonBlocking));
+  hipEvent_t* evs[3] = {&P.fev.fork, &P.fev.ctx_ready, &P.fev.done};
+  for (hipEvent_t* e : evs)
+    if (!*e) VLA_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  return VLA_OK;
+}
+
+// One eager cycle of a fused plan (the first cycle has no previous context:
+// none of its steps is stale).
+vla_status run_fused(vla_step_plan& P, hipStream_t stream) {
+  VLA_TRY(fused_ready(P));
+  FusedLayout L;
+  VLA_TRY(fused_layout(P, L));
+  Ctx cv, ca;
+  fused_ctxs(P, L, stream, P.aux, cv, ca);
+  const int n = P.cycles == 0 ? 0 : P.n_stale;
+  VLA_TRY(fused_sched(cv, ca, P, P.shape, n, (int)(P.cycles & 1), &P.fev, true));
+  P.cycles++;
+  return VLA_OK;
+}
+
+// Record the fused cycle of one parity into a graph (nothing runs): the
+// action branch forks from the capturing stream and joins it again.
+vla_status capture_fused(vla_step_plan& P, int parity, std::vector<LaunchRec>* recs, hipGraph_t& g_out,
+                         hipGraphExec_t& ex_out, int& nodes) {
+  FusedLayout L;
+  VLA_TRY(fused_layout(P, L));
+  hipStream_t cs = nullptr;
+  VLA_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) { (void)hipStreamDestroy(cs); return fail(VLA_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e)); }
+  Ctx cv, ca;
+  fused_ctxs(P, L, cs, P.aux, cv, ca);
+  if (recs) recs->clear();
+  cv.recs = recs; ca.recs = recs;
+  vla_status s = fused_sched(cv, ca, P, P.shape, P.n_stale, parity, &P.fev, false);
+  nodes = cv.kernels + ca.kernels;
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (s != VLA_OK) { if (g) (void)hipGraphDestroy(g); return s; }
+  if (e != hipSuccess) return fail(VLA_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) { (void)hipGraphDestroy(g); return fail(VLA_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e)); }
+  g_out = g;
+  ex_out = ex;
+  return VLA_OK;
+}
+
+bool captured(const vla_step_plan* p) { return p->exec || p->fexec[0]; }
+
 void drop(vla_step_plan::Entry& en) {
   if (en.exec) (void)hipGraphExecDestroy(en.exec);
   if (en.graph) (void)hipGraphDestroy(en.graph);
@@ -1305,16 +1541,31 @@ extern "C" {
 
 vla_status vla_step_run(vla_step_plan* plan, hipStream_t stream) {
   if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
-  return run_eager(*plan, plan->shape, stream);
+  if (plan->n_stale >= 0) return run_fused(*plan, stream);
+  VLA_TRY(run_eager(*plan, plan->shape, stream));
+  plan->cycles++;
+  return VLA_OK;
 }
 
 vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
   if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
-  if (plan->exec) return fail(VLA_ERR_STATE, "plan already captured");
+  if (captured(plan)) return fail(VLA_ERR_STATE, "plan already captured");
   // warm-up pass; it leaves the counters at zero, so the captured pass
   // launches no clearing node
   VLA_TRY(vla_step_run(plan, stream));
   VLA_HIP(hipStreamSynchronize(stream));
+  if (plan->n_stale >= 0) {
+    for (int p = 0; p < 2; p++) {
+      vla_status s = capture_fused(*plan, p, p == 0 ? &plan->recs : nullptr, plan->fgraph[p], plan->fexec[p], plan->nodes);
+      if (s != VLA_OK) {
+        if (plan->fexec[0]) (void)hipGraphExecDestroy(plan->fexec[0]);
+        if (plan->fgraph[0]) (void)hipGraphDestroy(plan->fgraph[0]);
+        plan->fexec[0] = nullptr; plan->fgraph[0] = nullptr;
+        return s;
+      }
+    }
+    return VLA_OK;
+  }
   Captured cp;
   VLA_TRY(capture_pass(*plan, plan->shape, &plan->recs, cp));
   plan->graph = cp.graph;
@@ -1327,19 +1578,26 @@ vla_status vla_step_capture(vla_step_plan* plan, hipStream_t stream) {
 
 vla_status vla_step_replay(vla_step_plan* plan, hipStream_t stream) {
   if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
-  if (!plan->exec) return fail(VLA_ERR_STATE, "plan not captured");
+  if (!captured(plan)) return fail(VLA_ERR_STATE, "plan not captured");
+  if (plan->n_stale >= 0) {
+    VLA_HIP(hipGraphLaunch(plan->fexec[plan->cycles & 1], stream));
+    plan->cycles++;
+    return VLA_OK;
+  }
   VLA_TRY(ready_counters(*plan, plan->shape, plan->cnt, plan->ncnt, stream));
   VLA_HIP(hipGraphLaunch(plan->exec, stream));
+  plan->cycles++;
   return VLA_OK;
 }
 
 vla_status vla_step_run_shape(vla_step_plan* plan, const vla_step_shape* shape, hipStream_t stream) {
   if (!plan || !shape) return fail(VLA_ERR_INVALID_ARG, "null plan/shape");
+  if (plan->n_stale >= 0) return fail(VLA_ERR_UNSUPPORTED, "a fused plan runs its own shape only");
   const vla_step_shape sh = *shape;
   plan->tick++;
   // shapes already captured were validated when they were first seen
   if (plan->exec && same_shape(sh, plan->shape)) {
-    VLA_TRY(vla_step_replay(plan, stream));
+    VLA_TRY(vla_step_replay(plan, stream));   // counts the cycle
     plan->stats.hits++;
     return VLA_OK;
   }
@@ -1349,12 +1607,14 @@ vla_status vla_step_run_shape(vla_step_plan* plan, const vla_step_shape* shape, 
     VLA_HIP(hipGraphLaunch(en.exec, stream));
     en.used = plan->tick;
     plan->stats.hits++;
+    plan->cycles++;
     return VLA_OK;
   }
   // miss: an eager pass produces this call's outputs, then the shape is
   // captured for the next calls
   VLA_TRY(check_sub_shape(*plan, sh));
   VLA_TRY(run_eager(*plan, sh, stream));
+  plan->cycles++;
   VLA_HIP(hipStreamSynchronize(stream));
   Captured cp;
   VLA_TRY(capture_pass(*plan, sh, nullptr, cp));
@@ -1383,7 +1643,9 @@ vla_status vla_step_cache_info(const vla_step_plan* plan, vla_step_cache_stats* 
   return VLA_OK;
 }
 
-int32_t vla_step_graph_nodes(const vla_step_plan* plan) { return plan && plan->exec ? plan->nodes : 0; }
+int32_t vla_step_graph_nodes(const vla_step_plan* plan) { return plan && captured(plan) ? plan->nodes : 0; }
+
+int64_t vla_step_cycles(const vla_step_plan* plan) { return plan ? plan->cycles : 0; }
 
 const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index) {
   if (!plan || index < 0 || index >= (int32_t)plan->recs.size()) return nullptr;
@@ -1392,9 +1654,9 @@ const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index) {
 
 vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_t stream) {
   if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
-  if (!plan->exec) return fail(VLA_ERR_STATE, "plan not captured");
+  if (!captured(plan)) return fail(VLA_ERR_STATE, "plan not captured");
   if (index < 0 || index >= (int32_t)plan->recs.size()) return fail(VLA_ERR_INVALID_ARG, "kernel index %d out of range", index);
-  VLA_TRY(ready_counters(*plan, plan->shape, plan->cnt, plan->ncnt, stream));
+  if (plan->n_stale < 0) VLA_TRY(ready_counters(*plan, plan->shape, plan->cnt, plan->ncnt, stream));
   LaunchRec& r = plan->recs[index];
   void* ptrs[16];
   for (size_t i = 0; i < r.args.size(); i++) ptrs[i] = r.args[i].data();
@@ -1407,6 +1669,14 @@ void vla_step_plan_destroy(vla_step_plan* plan) {
   for (auto& en : plan->cache) drop(en);
   if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
   if (plan->graph) (void)hipGraphDestroy(plan->graph);
+  for (int p = 0; p < 2; p++) {
+    if (plan->fexec[p]) (void)hipGraphExecDestroy(plan->fexec[p]);
+    if (plan->fgraph[p]) (void)hipGraphDestroy(plan->fgraph[p]);
+  }
+  if (plan->fev.fork) (void)hipEventDestroy(plan->fev.fork);
+  if (plan->fev.ctx_ready) (void)hipEventDestroy(plan->fev.ctx_ready);
+  if (plan->fev.done) (void)hipEventDestroy(plan->fev.done);
+  if (plan->aux) (void)hipStreamDestroy(plan->aux);
   delete plan;
 }
 

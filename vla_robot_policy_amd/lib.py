@@ -128,6 +128,10 @@ def load() -> C.CDLL:
         "vla_step_kernel_label": (C.c_char_p, [c_void_p, c_int32]),
         "vla_step_launch_kernel": (S, [c_void_p, c_int32, c_void_p]),
         "vla_step_run_shape": (S, [c_void_p, POINTER(StepShape), c_void_p]),
+        "vla_step_fused_workspace_bytes": (c_size_t, [POINTER(Model), POINTER(StepShape)]),
+        "vla_step_plan_create_fused": (S, [POINTER(Model), POINTER(StepShape), POINTER(StepIO), c_int32, c_void_p,
+                                           c_size_t, POINTER(c_void_p)]),
+        "vla_step_cycles": (C.c_int64, [c_void_p]),
         "vla_step_cache_info": (S, [c_void_p, POINTER(StepCacheStats)]),
         "vla_step_plan_destroy": (None, [c_void_p]),
         "vla_last_error": (C.c_char_p, []),
@@ -238,6 +242,21 @@ def vla_step_kernel_label(plan, index: int):
 
 def vla_step_launch_kernel(plan, index: int, stream: int = 0) -> int:
     return load().vla_step_launch_kernel(plan, index, stream)
+
+
+def vla_step_fused_workspace_bytes(model: Model, shape: StepShape) -> int:
+    return load().vla_step_fused_workspace_bytes(C.byref(model), C.byref(shape))
+
+
+def vla_step_plan_create_fused(model: Model, shape: StepShape, io: StepIO, n_stale: int, ws, ws_bytes: int):
+    out = c_void_p()
+    st = load().vla_step_plan_create_fused(C.byref(model), C.byref(shape), C.byref(io), n_stale, _p(ws), ws_bytes,
+                                           C.byref(out))
+    return st, out.value
+
+
+def vla_step_cycles(plan) -> int:
+    return load().vla_step_cycles(plan)
 
 
 def vla_step_run_shape(plan, shape: StepShape, stream: int = 0) -> int:
