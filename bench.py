@@ -379,6 +379,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-label", default=None,
                     help="relaunch only the kernel with this label --kernel-reps times (for counter passes)")
+    ap.add_argument("--euler-steps", type=int, default=None,
+                    help="Euler steps of the sampler (1 = one-step generation); not the default workload")
     ap.add_argument("--qk-norm", action="store_true",
                     help="backbone blocks with QK-norm (per-head RMSNorm of Q and K before RoPE); not the default workload")
     ap.add_argument("--shape-cache", default=None,
@@ -403,6 +405,12 @@ def main():
     if a.qk_norm:
         import dataclasses
         cfg = cfg.replace(block=dataclasses.replace(cfg.block, qk_norm=True))
+    variant = "; backbone with QK-norm" if a.qk_norm else ""
+    if a.euler_steps is not None:
+        if not 1 <= a.euler_steps <= 64:
+            raise SystemExit("--euler-steps must be in [1, 64]")
+        cfg = cfg.replace(steps=a.euler_steps)
+        variant += f"; sampler run for {a.euler_steps} Euler step{'s' if a.euler_steps > 1 else ''} instead of the workload's"
     if cfg.kind != "step":
         raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
     if a.fused is not None:
@@ -443,7 +451,7 @@ def main():
         "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOADS[a.config] + ("; backbone with QK-norm" if a.qk_norm else ""),
+        "config": {"workload": WORKLOADS[a.config] + variant,
                    "global_batch": 1, "seq_len": cfg.seq,
                    "euler_steps": cfg.steps, "parallelism": "single GPU"},
         "hz": round(1000.0 / ms, 2), "p50_ms": round(r["p50"], 4), "p90_ms": round(r["p90"], 4),

@@ -114,6 +114,20 @@ def test_step_full_single_camera(gu):
         assert e <= 1e-2, k
 
 
+def test_step_full_single_camera_one_step(gu):
+    """One-step generation (K = 1) at the single-camera workload: the
+    sampler's only step is also its last launch, so the DiT layer kernel
+    reads no next-launch weights ahead on the final layer."""
+    cfg = get_config(4).replace(steps=1)
+    W, I = _generate(gu, cfg)
+    _, got = gu.timed("gpu step (eager + 2 replays)", lambda: _step_graph(gu, cfg, W, I))
+    want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I))
+    errs = {k: gu.relerr(got[k], want[k]) for k in ("hidden", "actions", "velocities")}
+    gu.say("one-step single-camera rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= 1e-2, k
+
+
 def test_step_full_single_camera_fused(gu):
     """V-AEFusion at the single-camera workload (2 of 4 Euler steps stale),
     captured and replayed: the persistent DiT layer kernel runs alongside the
