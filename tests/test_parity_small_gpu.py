@@ -27,7 +27,7 @@ def gu():
 
 
 @pytest.mark.parametrize("wdtype", ["f32", "bf16", "fp8"])
-@pytest.mark.parametrize("seq", [37, 1, 130])
+@pytest.mark.parametrize("seq", [37, 1, 130, 400])     # 400: causal attention with its keys split over workgroups
 def test_block_small(gu, wdtype, seq):
     cfg = small_config("block", wdtype, seq=seq)
     W, I = make_weights(cfg), make_inputs(cfg)
@@ -135,7 +135,8 @@ def test_dit_small(gu, wdtype):
     assert e <= gu.TOL[wdtype] and ev <= gu.TOL[wdtype]
 
 
-@pytest.mark.parametrize("chunk,ctx_len,K", [(1, 1, 1), (16, 7, 2), (50, 33, 2)])
+# (16, 400, 2), (5, 530, 1): cross-attention with its keys split over workgroups
+@pytest.mark.parametrize("chunk,ctx_len,K", [(1, 1, 1), (16, 7, 2), (50, 33, 2), (16, 400, 2), (5, 530, 1)])
 def test_dit_edges(gu, chunk, ctx_len, K):
     import torch
     cfg = small_config("dit", "bf16")

@@ -272,14 +272,31 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
     return fail(VLA_ERR_SHAPE, "attention: row pitches %d/%d/%d/%d not multiples of 8/8/8/4", a.ldq, a.ldk, a.ldv, a.ldo);
   int group = a.Hq / a.Hkv;
   int hpw = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-  KernelRef k{};
-  if (!attn_lookup(f32 ? 1 : 0, dp, hpw, &k)) return fail(VLA_ERR_UNSUPPORTED, "attention: no kernel for D %d", a.D);
+  KernelRef k{}, km{};
+  if (!attn_lookup(f32 ? 1 : 0, dp, hpw, &k, &km)) return fail(VLA_ERR_UNSUPPORTED, "attention: no kernel for D %d", a.D);
   int rb = 4 / hpw;
   int nrb = (a.Sq + 16 * rb - 1) / (16 * rb);
-  int grid = a.Hkv * (group / hpw) * nrb;
+  int tiles = a.Hkv * (group / hpw) * nrb;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)a.D));
+  // Few tiles with long key loops (cross-attention of a small chunk to a
+  // long context): share each tile's keys out to several workgroups of at
+  // least two 32-key blocks, up to about 192 workgroups, and merge their
+  // partials in a second launch. Short loops gain nothing from a split.
+  const int kblocks = (a.Sk + 31) / 32;
+  int nsplit = 1;
+  if (kblocks >= 12 && tiles <= 64) nsplit = std::min({kblocks / 2, 192 / tiles, ATTN_SPLIT_MAX});
+  a.kchunk = ((kblocks + nsplit - 1) / nsplit) * 32;
+  a.nsplit = nsplit = (a.Sk + a.kchunk - 1) / a.kchunk;
+  if (nsplit > 1) {
+    const size_t pw = 16 * (size_t)(dp + 2);
+    c.need_part = std::max(c.need_part, (size_t)tiles * nsplit * 4 * pw);
+    a.part = c.part;
+  }
   if (!c.plan && k.smem > 64 * 1024) VLA_TRY(allow_smem(k));
-  return launch(c, k.fn, dim3(grid), dim3(256), (size_t)k.smem, {arg(a)});
+  VLA_TRY(launch(c, k.fn, dim3(tiles * nsplit), dim3(256), (size_t)k.smem, {arg(a)}));
+  if (nsplit == 1) return VLA_OK;
+  const int per_tile = (4 * 16 * (dp / 4) + 255) / 256;
+  return launch(c, km.fn, dim3(tiles * per_tile), dim3(256), 0, {arg(a)});
 }
 
 vla_status stage_rows(Ctx& c, float* x, int ldx, int M, int N, const void* src, int src_f32, int ld_src, int r0, int r1,
@@ -575,6 +592,7 @@ struct DitState {
   float* x1 = nullptr; float* x2 = nullptr;
   uint16_t* qkv = nullptr; uint16_t* ao = nullptr; uint16_t* q = nullptr; uint16_t* h = nullptr;
   int* derr = nullptr; uint16_t* aos = nullptr;
+  uint16_t* u = nullptr;   // modulated LayerNorm rows of the launch-per-operation path (bf16)
   bool stack = false;
   int G = 0;
 };
@@ -602,6 +620,7 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.stack = dit_stack_ok(cf, n, s.G);
   s.derr = c.take<int>(64);
   s.aos = s.stack ? c.take<uint16_t>((size_t)n * D) : nullptr;   // the layer kernel's self-attention output
+  s.u = !s.stack && cf.wdtype != VLA_F32 ? c.take<uint16_t>((size_t)n * D) : nullptr;
   if (s.stack) {
     // phase and tile counters of the layer kernel live in the shared counter
     // array (every kernel leaves its counters at zero); slice partials in the
@@ -728,14 +747,29 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         VLA_TRY(launch(c, lk.fn, dim3(s.G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
         continue;
       }
+      // The modulated LayerNorm u = LN(x)(1 + scale) + shift of a sublayer's
+      // input: bf16 / fp8 weights take u from one row-norm launch (each of
+      // the GEMM's workgroups would otherwise normalise every row again);
+      // fp32 weights normalise in the GEMM's prologue.
+      auto modln = [&](GemmArgs& a, int sh, int sc, const char* label) -> vla_status {
+        if (s.u) {
+          c.label = label;
+          VLA_TRY(norm_rows(c, x, D, n, D, xs.rs, 0, cf.eps, mv(sc), 1, mv(sh), s.u, nullptr, D));
+          a.a = s.u; a.lda = D;
+        } else {
+          a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(sc); a.g_plus_one = 1; a.bsh = mv(sh);
+        }
+        return VLA_OK;
+      };
+      const int am_norm = s.u ? A_BF16 : A_NORM;
       {  // adaLN(LN) -> self-attn QKV
-      c.label = "dit.sa_qkv";
         GemmArgs a = gargs();
+        VLA_TRY(modln(a, 0, 1, "dit.sa_norm"));
+        c.label = "dit.sa_qkv";
         a.M = n; a.N = 3 * D; a.K = D;
-        a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(1); a.g_plus_one = 1; a.bsh = mv(0);
         a.w = w.w_qkv; a.ldw = D; a.wscale = w.s_qkv; a.bias = w.b_qkv;
         a.c = s.qkv; a.ldc = 3 * D;
-        VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
+        VLA_TRY(gemm(c, a, {wt, am_norm, E_STORE}));
       }
       {
         c.label = "dit.sa_attn";
@@ -757,13 +791,13 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
       }
       {  // adaLN(LN) -> cross-attn query
-      c.label = "dit.ca_q";
         GemmArgs a = gargs();
+        VLA_TRY(modln(a, 3, 4, "dit.ca_norm"));
+        c.label = "dit.ca_q";
         a.M = n; a.N = D; a.K = D;
-        a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(4); a.g_plus_one = 1; a.bsh = mv(3);
         a.w = w.w_cq; a.ldw = D; a.wscale = w.s_cq; a.bias = w.b_cq;
         a.c = s.q; a.ldc = D;
-        VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
+        VLA_TRY(gemm(c, a, {wt, am_norm, E_STORE}));
       }
       {
         c.label = "dit.ca_attn";
@@ -785,13 +819,13 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         VLA_TRY(gemm(c, a, {wt, A_BF16, E_RESID}, &xs.rs));
       }
       {  // adaLN(LN) -> MLP up -> GELU
-      c.label = "dit.mlp_up";
         GemmArgs a = gargs();
+        VLA_TRY(modln(a, 6, 7, "dit.mlp_norm"));
+        c.label = "dit.mlp_up";
         a.M = n; a.N = cf.mlp; a.K = D;
-        a.a = x; a.lda = D; a.rs = xs.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = mv(7); a.g_plus_one = 1; a.bsh = mv(6);
         a.w = w.w_up; a.ldw = D; a.wscale = w.s_up; a.bias = w.b_up; a.act = ACT_GELU;
         a.c = s.h; a.ldc = cf.mlp;
-        VLA_TRY(gemm(c, a, {wt, A_NORM, E_STORE}));
+        VLA_TRY(gemm(c, a, {wt, am_norm, E_STORE}));
       }
       {  // MLP down, gated residual
       c.label = "dit.mlp_down";

@@ -24,7 +24,15 @@ struct AttnArgs {
   int Sq, Sk, Hq, Hkv, D;
   int causal;                // key j visible to query i iff j <= i
   float scale_log2;          // log2(e) / sqrt(D)
+  // key split (filled by the launcher): the keys of every tile are shared
+  // out to nsplit workgroups of kchunk keys each; each writes its partial
+  // (unnormalised O, running max and sum per query) to part, and
+  // k_attn_merge combines them in split order
+  int nsplit, kchunk;
+  float* part;
 };
+
+constexpr int ATTN_SPLIT_MAX = 16;
 
 template <typename CT> struct ATraits;
 template <> struct ATraits<__bf16> {
@@ -124,6 +132,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   const int hsets = group / HPW;             // head subsets per kv head
   const int nrb = (p.Sq + 16 * RB - 1) / (16 * RB);
   int bid = blockIdx.x;
+  const int sp = bid % p.nsplit;  bid /= p.nsplit;
+  const int tile = bid;
   const int rb = bid % nrb;  bid /= nrb;
   const int hs = bid % hsets; bid /= hsets;
   const int g = bid;                          // kv head
@@ -132,7 +142,10 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   const int wg_row_end = min(p.Sq, (rb + 1) * RB * 16);
   const int qn = lane & 15, grp = lane >> 4;
   const int qrow = row0 + qn;
-  const int kend = p.causal ? min(p.Sk, wg_row_end) : p.Sk;
+  // this workgroup's keys: [kbeg, kend) of the tile's visible keys
+  const int kvis = p.causal ? min(p.Sk, wg_row_end) : p.Sk;
+  const int kbeg = sp * p.kchunk;
+  const int kend = min(kvis, kbeg + p.kchunk);
 
   // K / V of one stage (NBUF blocks from key kb0) into registers: thread
   // group e = tid + i * 256 of a block is key e % 32, dims (e / 32) * 8, so
@@ -164,7 +177,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
         for (int t = 0; t < 8; t++) TR::rput(vd + (d8 + t) * VPITCH, rv[b][i], t);
       }
   };
-  load_stage(0);
+  load_stage(kbeg);
 
   // Q^T fragments (B operand): query qn, dims ds*32 + grp*8 .. +8
   F qf[DP / 32];
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   for (int i = 0; i < DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  for (int kb0 = 0; kb0 < kend; kb0 += NBUF * KB) {
+  for (int kb0 = kbeg; kb0 < kend; kb0 += NBUF * KB) {
     __syncthreads();                          // the previous stage's readers are done
     store_stage();
     __syncthreads();
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           int j = kb + hb * 16 + grp * 4 + i;
-          bool ok = j < p.Sk && (!p.causal || j <= qrow);
+          bool ok = j < kend && (!p.causal || j <= qrow);
           float v = ok ? s[hb][i] * p.scale_log2 : -INFINITY;
           s[hb][i] = v;
           bmax = fmaxf(bmax, v);
@@ -241,6 +254,19 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   float lsum = lrun;
   lsum += __shfl_xor(lsum, 16, WAVE);
   lsum += __shfl_xor(lsum, 32, WAVE);
+  if (p.nsplit > 1) {
+    // partial of this split: [wave][query][DP] unnormalised O, then the
+    // running max and sum of each query
+    constexpr int PW = 16 * (DP + 2);                   // floats per wave
+    float* pt = p.part + ((size_t)(tile * p.nsplit + sp) * 4 + wave) * PW;
+#pragma unroll
+    for (int db = 0; db < DP / 16; db++) {
+      const int d = db * 16 + grp * 4;
+      *reinterpret_cast<float4*>(pt + qn * DP + d) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+    }
+    if (grp == 0) { pt[16 * DP + qn] = mrun; pt[16 * DP + 16 + qn] = lsum; }
+    return;
+  }
   float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   // O^T[d][q]: the lane's 4 consecutive dims d = 16 db + 4 grp + i of query qrow
   if (qrow < p.Sq) {
@@ -252,6 +278,55 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
                    oacc[db][2] * inv, oacc[db][3] * inv);
     }
   }
+}
+
+// Merge of a key-split attention: one thread per 4 output dims of one query
+// of one head, every split's partial requested at once and combined in split
+// order (max, rescaled sums), so results do not depend on timing.
+template <typename CT, int DP, int HPW>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs p) {
+  using TR = ATraits<CT>;
+  constexpr int RB = 4 / HPW, PW = 16 * (DP + 2), ITEMS = 4 * 16 * (DP / 4);
+  const int group = p.Hq / p.Hkv, hsets = group / HPW;
+  const int nrb = (p.Sq + 16 * RB - 1) / (16 * RB);
+  const int per_tile = (ITEMS + 255) / 256;
+  const int tile = blockIdx.x / per_tile;
+  const int e = (blockIdx.x % per_tile) * 256 + threadIdx.x;
+  if (e >= ITEMS) return;
+  const int w = e / (16 * (DP / 4)), q = (e / (DP / 4)) % 16, d = (e % (DP / 4)) * 4;
+  int t_ = tile;
+  const int rb = t_ % nrb; t_ /= nrb;
+  const int hs = t_ % hsets;
+  const int g = t_ / hsets;
+  const int row = (rb * RB + w / HPW) * 16 + q, head = g * group + hs * HPW + (w % HPW);
+  if (row >= p.Sq || d >= p.D) return;
+  float m[ATTN_SPLIT_MAX], l[ATTN_SPLIT_MAX];
+  float4 o[ATTN_SPLIT_MAX];
+#pragma unroll
+  for (int t = 0; t < ATTN_SPLIT_MAX; t++) {
+    if (t < p.nsplit) {
+      const float* pt = p.part + ((size_t)(tile * p.nsplit + t) * 4 + w) * PW;
+      m[t] = pt[16 * DP + q];
+      l[t] = pt[16 * DP + 16 + q];
+      o[t] = *reinterpret_cast<const float4*>(pt + q * DP + d);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < ATTN_SPLIT_MAX; t++)
+    if (t < p.nsplit) M = fmaxf(M, m[t]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int t = 0; t < ATTN_SPLIT_MAX; t++) {
+    if (t < p.nsplit && m[t] != -INFINITY) {           // a split without a visible key adds nothing
+      const float f = exp2f(m[t] - M);
+      L += f * l[t];
+      acc.x += f * o[t].x; acc.y += f * o[t].y; acc.z += f * o[t].z; acc.w += f * o[t].w;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  TR::store4(p.o, (size_t)row * p.ldo + (size_t)head * p.D + d, acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 }  // namespace vla

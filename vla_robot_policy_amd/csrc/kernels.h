@@ -17,7 +17,8 @@ bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, in
 bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
 
 // Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
-bool attn_lookup(int f32, int dp, int hpw, KernelRef* out);
+// the attention kernel and the merge of its key-split partials
+bool attn_lookup(int f32, int dp, int hpw, KernelRef* out, KernelRef* merge);
 
 // Misc kernels.
 const void* k_fill_ref();

@@ -22,10 +22,11 @@ __global__ __launch_bounds__(256) void k_convert_rows(const float* x, int ldx, i
   if (f32 == F32V && dp == DPV && hpw == HPWV) {    \
     out->fn = (const void*)&k_attention<CT, DPV, HPWV>; \
     out->smem = AttnStage<CT, DPV>::SMEM; out->threads = 256; \
+    if (merge) { merge->fn = (const void*)&k_attn_merge<CT, DPV, HPWV>; merge->smem = 0; merge->threads = 256; } \
     return true;                                    \
   }
 
-bool attn_lookup(int f32, int dp, int hpw, KernelRef* out) {
+bool attn_lookup(int f32, int dp, int hpw, KernelRef* out, KernelRef* merge) {
   VLA_ATTN_CASE(__bf16, 0, 64, 1) VLA_ATTN_CASE(__bf16, 0, 64, 2) VLA_ATTN_CASE(__bf16, 0, 64, 4)
   VLA_ATTN_CASE(__bf16, 0, 96, 1) VLA_ATTN_CASE(__bf16, 0, 96, 2) VLA_ATTN_CASE(__bf16, 0, 96, 4)
   VLA_ATTN_CASE(__bf16, 0, 128, 1) VLA_ATTN_CASE(__bf16, 0, 128, 2) VLA_ATTN_CASE(__bf16, 0, 128, 4)
