@@ -9,6 +9,7 @@ bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int
   VLA_GEMM_CASE(uint8_t, __bf16, A_BF16, E_STORE, 1, 4, 1, 1)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_RESID)
+  VLA_GEMM_CASE_X(uint8_t, __bf16, A_BF16, E_RESID, 4, 2, 2, 1, 2, 0)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_NORM, E_STORE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_ROPE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_SWIGLU)
