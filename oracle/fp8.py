@@ -34,3 +34,44 @@ _TABLE = decode_e4m3fn(np.arange(256))
 
 def dequantize_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return _TABLE[np.asarray(codes, dtype=np.uint8)] * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+# ---------------------------------------------------------------- activations
+# W8A8 (page "开源 APXInf 把 VLA 推理压到 26 毫秒", same section: FP8 applied to
+# the weights and the activations). Plain reading where the page is silent:
+# each activation row (token) gets its own scale at run time, s = max|x| / 448,
+# and x / s is rounded to the nearest E4M3FN value (ties to the even code,
+# saturating at 448). The decision is taken in float32, the precision the
+# kernels compute it in: x and max|x| are float32 values, x * (448 / max|x|)
+# is one float32 multiply by a float32 reciprocal.
+
+_FINITE = _TABLE[:0x7F]                       # non-negative finite values, ascending, codes 0x00..0x7E
+
+
+def encode_e4m3fn_nearest(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3FN code of each value by search over the decoded table
+    (ties to the even code, saturating at +-448)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), 448.0)
+    hi = np.clip(np.searchsorted(_FINITE, a, side="left"), 0, len(_FINITE) - 1)
+    lo = np.clip(hi - 1, 0, len(_FINITE) - 1)
+    d_hi, d_lo = _FINITE[hi] - a, a - _FINITE[lo]
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(y) & (code != 0), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_act_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row E4M3FN codes and float32 scales of activations x [M, K]."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=1)
+    inv = np.where(amax > 0, np.float32(448.0) / np.where(amax > 0, amax, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    y = (x32 * inv[:, None]).astype(np.float32)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    return encode_e4m3fn_nearest(y), scale
+
+
+def fake_quant_act_rows(x: np.ndarray) -> np.ndarray:
+    """The values W8A8 GEMMs see for activations x: codes times row scale."""
+    codes, scale = quantize_act_rows(x)
+    return dequantize_rows(codes, scale)
+

@@ -17,6 +17,9 @@ With QK-norm (section 算子开发 counts RMSNorm calls on Q and K besides the
 two pre-norms), every query and key head vector is RMS-normalised over the
 head dimension with its own gain (q_norm, k_norm) before RoPE:
   Q_h <- RMSNorm(Q_h, q_norm),  K_g <- RMSNorm(K_g, k_norm).
+With W8A8 (page "开源 APXInf 把 VLA 推理压到 26 毫秒": FP8 weights and
+activations), the input rows of the four Linears (n, the attention output,
+n2 and the SwiGLU product) are replaced by their per-token FP8 values first.
 """
 
 from __future__ import annotations
@@ -24,6 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import ops
+from .fp8 import fake_quant_act_rows
 
 
 def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
@@ -31,7 +35,10 @@ def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     S, H = x.shape
     Hq, Hkv, D = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
-    n = ops.rmsnorm(x, W[prefix + "attn_norm"], shape.eps)
+    # W8A8: every Linear of the block reads its input rows as per-token E4M3FN
+    # codes times the row's scale (oracle/fp8.py)
+    act = fake_quant_act_rows if getattr(shape, "a8", False) else (lambda t: t)
+    n = act(ops.rmsnorm(x, W[prefix + "attn_norm"], shape.eps))
     q = ops.linear(n, W[prefix + "wq"]).reshape(S, Hq, D)
     k = ops.linear(n, W[prefix + "wk"]).reshape(S, Hkv, D)
     v = ops.linear(n, W[prefix + "wv"]).reshape(S, Hkv, D)
@@ -41,10 +48,10 @@ def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
     pos = np.arange(S) + pos0
     q = ops.rope(q, pos, shape.rope_base)
     k = ops.rope(k, pos, shape.rope_base)
-    o = ops.attention(q, k, v, causal=True).reshape(S, Hq * D)
+    o = act(ops.attention(q, k, v, causal=True).reshape(S, Hq * D))
     h = x + ops.linear(o, W[prefix + "wo"])
-    n2 = ops.rmsnorm(h, W[prefix + "mlp_norm"], shape.eps)
-    a = ops.silu(ops.linear(n2, W[prefix + "wg"])) * ops.linear(n2, W[prefix + "wu"])
+    n2 = act(ops.rmsnorm(h, W[prefix + "mlp_norm"], shape.eps))
+    a = act(ops.silu(ops.linear(n2, W[prefix + "wg"])) * ops.linear(n2, W[prefix + "wu"]))
     return h + ops.linear(a, W[prefix + "wd"])
 
 

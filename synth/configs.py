@@ -38,7 +38,8 @@ class BlockShape:
     intermediate: int
     rope_base: float
     eps: float = 1e-6
-    qk_norm: bool = False    # per-head RMSNorm of Q and K before RoPE
+    qk_norm: bool = False   # per-head RMSNorm of Q and K before RoPE
+    a8: bool = False        # W8A8: per-token fp8 activations into the block's Linears (fp8 weights)
 
     @property
     def q_dim(self) -> int:
