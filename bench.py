@@ -381,6 +381,8 @@ def main():
                     help="relaunch only the kernel with this label --kernel-reps times (for counter passes)")
     ap.add_argument("--euler-steps", type=int, default=None,
                     help="Euler steps of the sampler (1 = one-step generation); not the default workload")
+    ap.add_argument("--a8", action="store_true",
+                    help="W8A8: per-token fp8 activations into the backbone's Linears (fp8 workload); not the default")
     ap.add_argument("--qk-norm", action="store_true",
                     help="backbone blocks with QK-norm (per-head RMSNorm of Q and K before RoPE); not the default workload")
     ap.add_argument("--shape-cache", default=None,
@@ -406,6 +408,12 @@ def main():
         import dataclasses
         cfg = cfg.replace(block=dataclasses.replace(cfg.block, qk_norm=True))
     variant = "; backbone with QK-norm" if a.qk_norm else ""
+    if a.a8:
+        if cfg.wdtype != "fp8":
+            raise SystemExit("--a8 needs the fp8 workload (--config 5)")
+        import dataclasses
+        cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8=True))
+        variant += "; W8A8: per-token fp8 activations into the backbone's Linears, fp8 MFMA"
     if a.euler_steps is not None:
         if not 1 <= a.euler_steps <= 64:
             raise SystemExit("--euler-steps must be in [1, 64]")

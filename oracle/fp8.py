@@ -50,14 +50,16 @@ _FINITE = _TABLE[:0x7F]                       # non-negative finite values, asce
 
 def encode_e4m3fn_nearest(y: np.ndarray) -> np.ndarray:
     """Nearest E4M3FN code of each value by search over the decoded table
-    (ties to the even code, saturating at +-448)."""
+    (ties to the even code, saturating at +-448). The sign bit is the
+    value's, so a negative value that rounds to zero is -0 (0x80), as in
+    IEEE rounding; the page does not say, and both zeros decode to 0."""
     y = np.asarray(y, dtype=np.float64)
     a = np.minimum(np.abs(y), 448.0)
     hi = np.clip(np.searchsorted(_FINITE, a, side="left"), 0, len(_FINITE) - 1)
     lo = np.clip(hi - 1, 0, len(_FINITE) - 1)
     d_hi, d_lo = _FINITE[hi] - a, a - _FINITE[lo]
     code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
-    return (code | np.where(np.signbit(y) & (code != 0), 0x80, 0)).astype(np.uint8)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
 
 
 def quantize_act_rows(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

@@ -39,7 +39,9 @@ def test_workspace_sizes_scale_with_shape():
     (dict(head_dim=96), lib.VLA_ERR_SHAPE),
     (dict(n_kv_heads=5), lib.VLA_ERR_SHAPE),
     (dict(hidden=2561), lib.VLA_ERR_SHAPE),
-    (dict(flags=2), lib.VLA_ERR_UNSUPPORTED),
+    (dict(flags=4), lib.VLA_ERR_UNSUPPORTED),                                       # unknown bit
+    (dict(flags=lib.VLA_BLOCK_A8), lib.VLA_ERR_UNSUPPORTED),                        # fp8 activations, bf16 weights
+    (dict(flags=lib.VLA_BLOCK_A8, wdtype=lib.VLA_FP8_E4M3, hidden=5120, n_q_heads=40), lib.VLA_ERR_UNSUPPORTED),  # hidden > 4096
     (dict(flags=lib.VLA_BLOCK_QK_NORM), lib.VLA_ERR_INVALID_ARG),                  # no q_norm / k_norm
     (dict(flags=lib.VLA_BLOCK_QK_NORM, n_q_heads=3, n_kv_heads=1, head_dim=64), lib.VLA_ERR_UNSUPPORTED),
     (dict(wdtype=7), lib.VLA_ERR_INVALID_ARG),

@@ -54,6 +54,43 @@ def test_block_qk_norm(gu, wdtype, seq):
     assert e <= gu.TOL[wdtype]
 
 
+def _a8(cfg):
+    import dataclasses
+    return cfg.replace(block=dataclasses.replace(cfg.block, a8=True))
+
+
+@pytest.mark.parametrize("seq", [37, 1, 130, 400])
+def test_block_a8(gu, seq):
+    """W8A8 block: per-token fp8 activations into fp8 MFMAs. Within the fp8
+    bar of the oracle's W8A8 block, and closer to it than to the same block
+    without activation quantisation."""
+    import dataclasses
+    cfg = _a8(small_config("block", "fp8", seq=seq))
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = gu.DeviceWeights(cfg, W)
+    got = gu.run_block(cfg, dw, gu.upload_input(I["x"]), seq)
+    x, Wo = to_f64(I["x"]), Weights(W)
+    want = ollm.block(x, Wo, "llm.0.", cfg.block)
+    plain = ollm.block(x, Wo, "llm.0.", dataclasses.replace(cfg.block, a8=False))
+    e = gu.relerr(got, want)
+    # on the block's update (out - x), where the quantisation shows
+    e_a8, e_plain = gu.relerr(got - x, want - x), gu.relerr(got - x, plain - x)
+    gu.say(f"block W8A8 seq {seq}: rel L2 {e:.3e}; update vs W8A8 oracle {e_a8:.3e}, vs unquantised {e_plain:.3e}")
+    assert e <= gu.TOL["fp8"]
+    assert e_a8 < 0.8 * e_plain
+
+
+def test_backbone_a8(gu):
+    cfg = _a8(small_config("backbone", "fp8"))
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = gu.DeviceWeights(cfg, W)
+    got = gu.run_backbone(cfg, dw, gu.upload_input(I["x"]), cfg.seq)
+    want = run_config(cfg, W, I)["hidden"]
+    e = gu.relerr(got, want)
+    gu.say(f"backbone W8A8: rel L2 {e:.3e}")
+    assert e <= gu.TOL["fp8"]
+
+
 def test_backbone_qk_norm_head128(gu):
     # QK-norm with one 128-dim head per tile, split-K QKV, two layers
     from synth.configs import BlockShape

@@ -229,8 +229,9 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
   if (op.wdtype == VLA_FP8_E4M3 && (a.K % 16 != 0 || a.ldw % 16 != 0))
     return fail(VLA_ERR_SHAPE, "gemm: fp8 weights need K %d and pitch %d to be multiples of 16", a.K, a.ldw);
-  const int ag = op.am == A_BF16 ? 8 : 4;   // activation elements per 16-byte load
-  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM) && (a.lda % ag != 0 || a.K % ag != 0))
+  const int ag = op.am == A_BF16 ? 8 : op.am == A_FP8 ? 16 : 4;   // activation elements per 16-byte load
+  if (op.am == A_FP8 && !a.a_scale && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: fp8 activations without row scales");
+  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM || op.am == A_FP8) && (a.lda % ag != 0 || a.K % ag != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
   // buffer-load offsets are 32-bit: operands up to 2 GiB
   const double wrows = op.em == E_SWIGLU ? (double)a.n_half + a.N : (double)a.N;
@@ -357,6 +358,23 @@ vla_status norm_rows(Ctx& c, const float* x, int ldx, int M, int K, RowStats rs,
   return launch(c, k_norm_rows_ref(), dim3(M), dim3(256), 0, {arg(a)});
 }
 
+// W8A8: the normalised rows as E4M3FN codes with one scale per row (K <= 4096)
+vla_status norm_rows8(Ctx& c, const float* x, int ldx, int M, int K, RowStats rs, int rms, float eps, const float* g,
+                      uint8_t* out8, float* oscale, int ldo) {
+  if (K % 4 != 0 || K > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return fail(VLA_ERR_SHAPE, "norm (fp8 out): row length %d", K);
+  NormArgs a{};
+  a.x = x; a.ldx = ldx; a.M = M; a.K = K; a.rs = rs; a.rms = rms; a.eps = eps;
+  a.g = g; a.out8 = out8; a.oscale = oscale; a.ldo = ldo;
+  return launch(c, k_norm_rows_ref(), dim3(M), dim3(256), 0, {arg(a)});
+}
+
+// W8A8: E4M3FN codes of bf16 or fp32 rows with one scale per row (K <= 16384)
+vla_status quant_rows(Ctx& c, const void* x, int x_f32, int ldx, int M, int K, uint8_t* out, int ldo, float* scale) {
+  if (K % 8 != 0 || K > 16384 || ldx % 8 != 0 || ldo % 8 != 0) return fail(VLA_ERR_SHAPE, "quant rows: row length %d", K);
+  return launch(c, k_quant_rows_ref(), dim3(M), dim3(256), 0,
+                {arg(x), arg(x_f32), arg(ldx), arg(K), arg(out), arg(ldo), arg(scale)});
+}
+
 vla_status convert_rows(Ctx& c, const float* x, int ldx, int M, int N, void* out, int ldo, int out_f32) {
   return launch(c, k_convert_rows_ref(), dim3((M + 3) / 4), dim3(256), 0,
                 {arg(x), arg(ldx), arg(M), arg(N), arg(out), arg(ldo), arg(out_f32)});
@@ -367,7 +385,14 @@ bool dtype_ok(int t) { return t == VLA_F32 || t == VLA_BF16 || t == VLA_FP8_E4M3
 // ------------------------------------------------------------------ backbone
 vla_status check_block_cfg(const vla_block_cfg* cfg) {
   if (!cfg) return fail(VLA_ERR_INVALID_ARG, "null block cfg");
-  if (cfg->flags & ~VLA_BLOCK_QK_NORM) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags 0x%x: unknown bits", cfg->flags);
+  if (cfg->flags & ~(VLA_BLOCK_QK_NORM | VLA_BLOCK_A8)) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags 0x%x: unknown bits", cfg->flags);
+  if (cfg->flags & VLA_BLOCK_A8) {
+    if (cfg->wdtype != VLA_FP8_E4M3 || cfg->adtype != VLA_BF16)
+      return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp8 activations need fp8 weights and bf16 activations");
+    const int qd = cfg->n_q_heads * cfg->head_dim;
+    if (cfg->hidden > 4096 || cfg->hidden % 16 || qd > 16384 || qd % 16 || cfg->intermediate > 16384 || cfg->intermediate % 16)
+      return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp8 activations need hidden <= 4096 and Linear inputs <= 16384 wide, multiples of 16");
+  }
   if (!dtype_ok(cfg->wdtype) || (cfg->adtype != VLA_F32 && cfg->adtype != VLA_BF16))
     return fail(VLA_ERR_INVALID_ARG, "block cfg: bad dtype (w %d, act %d)", cfg->wdtype, cfg->adtype);
   if ((cfg->wdtype == VLA_F32) != (cfg->adtype == VLA_F32))
@@ -407,6 +432,8 @@ struct BackboneBufs {
   uint16_t* xn;    // [S, H] normalised rows (bf16 activations)
   uint16_t* xn_lo; // [S, H] their remainder plane (compensated MLP)
   uint16_t* act_lo;// [S, I] remainder plane of the SwiGLU output (compensated MLP)
+  uint8_t* q8;     // [S, max(H, q_dim, I)] E4M3FN codes of the next Linear's input (fp8 activations)
+  float* q8s;      // [S] their row scales
 };
 
 // bf16 backbones carry the MLP's activations (the normalised input of gate/up
@@ -420,11 +447,21 @@ BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   int nqkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim;
   BackboneBufs b;
   b.xs = take_stream(c, S, cfg.hidden);
-  b.qkv = c.take<char>((size_t)S * nqkv * es);
-  b.ao = c.take<char>((size_t)S * cfg.n_q_heads * cfg.head_dim * es);
-  b.act = c.take<char>((size_t)S * cfg.intermediate * es);
+  // W8A8 keeps q, k, v, the attention (fp32 kernel) and the SwiGLU product
+  // in fp32 until they are quantised: rounding to bf16 before an fp8 code is
+  // chosen moves about one value in thirty to a neighbouring code
+  const size_t eq = (cfg.flags & VLA_BLOCK_A8) ? 4 : es;
+  b.qkv = c.take<char>((size_t)S * nqkv * eq);
+  b.ao = c.take<char>((size_t)S * cfg.n_q_heads * cfg.head_dim * eq);
+  b.act = c.take<char>((size_t)S * cfg.intermediate * eq);
   b.xn = b.xn_lo = b.act_lo = nullptr;
+  b.q8 = nullptr; b.q8s = nullptr;
   if (cfg.adtype != VLA_F32) b.xn = c.take<uint16_t>((size_t)S * cfg.hidden);
+  if (cfg.flags & VLA_BLOCK_A8) {
+    const int w = std::max({cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.intermediate});
+    b.q8 = c.take<uint8_t>((size_t)S * w);
+    b.q8s = c.take<float>((size_t)S);
+  }
   if (comp) {
     b.xn_lo = c.take<uint16_t>((size_t)S * cfg.hidden);
     b.act_lo = c.take<uint16_t>((size_t)S * cfg.intermediate);
@@ -440,10 +477,17 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   const int wt = cfg.wdtype;
   const size_t es = f32 ? 4 : 2;
   const int comp = mlp_compensated(cfg) ? 1 : 0;
+  // W8A8: each Linear reads its input as per-row E4M3FN codes (the norms
+  // write codes, the attention and SwiGLU outputs are quantised by a row pass)
+  const bool a8 = (cfg.flags & VLA_BLOCK_A8) != 0;
+  const int am_bf = a8 ? A_FP8 : A_BF16;
   for (int l = 0; l < n_layers; l++) {
     const vla_block_weights& w = layers[l];
     {  // RMSNorm -> fused QKV -> RoPE
-      if (!f32) {
+      if (a8) {
+        c.label = "llm.attn_norm";
+        VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, b.q8, b.q8s, H));
+      } else if (!f32) {
         c.label = "llm.attn_norm";
         VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, 0, nullptr, b.xn, nullptr, H));
       }
@@ -451,34 +495,44 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       GemmArgs a = gargs();
       a.M = S; a.N = nqkv; a.K = H;
       if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm; }
+      else if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = H; }
       else { a.a = b.xn; a.lda = H; }
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
-      a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32;
+      a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32 || a8;
       a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_base = cfg.rope_base;
       if (cfg.flags & VLA_BLOCK_QK_NORM) { a.qk_norm = 1; a.qk_eps = cfg.eps; a.qn_g = w.q_norm; a.kn_g = w.k_norm; }
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : A_BF16, E_ROPE}));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_ROPE}));
     }
     {  // causal GQA attention
     c.label = "llm.attn";
       AttnArgs a{};
+      const size_t eq = f32 || a8 ? 4 : 2;
       a.q = b.qkv; a.ldq = nqkv;
-      a.k = b.qkv ? (const char*)b.qkv + qd * es : nullptr; a.ldk = nqkv;
-      a.v = b.qkv ? (const char*)b.qkv + (qd + kd) * es : nullptr; a.ldv = nqkv;
+      a.k = b.qkv ? (const char*)b.qkv + qd * eq : nullptr; a.ldk = nqkv;
+      a.v = b.qkv ? (const char*)b.qkv + (qd + kd) * eq : nullptr; a.ldv = nqkv;
       a.o = b.ao; a.ldo = qd;
       a.Sq = S; a.Sk = S; a.Hq = cfg.n_q_heads; a.Hkv = cfg.n_kv_heads; a.D = D; a.causal = 1;
-      VLA_TRY(attention(c, a, f32));
+      VLA_TRY(attention(c, a, f32 || a8));
     }
     {  // O-proj + residual (+ row statistics)
+      if (a8) {
+        c.label = "llm.o_quant";
+        VLA_TRY(quant_rows(c, b.ao, 1, qd, S, qd, b.q8, qd, b.q8s));
+      }
     c.label = "llm.o";
       GemmArgs a = gargs();
       a.M = S; a.N = H; a.K = qd;
-      a.a = b.ao; a.lda = qd;
+      if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = qd; }
+      else { a.a = b.ao; a.lda = qd; }
       a.w = w.w_o; a.ldw = qd; a.wscale = w.s_o;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID}, &b.xs.rs));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID}, &b.xs.rs));
     }
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
-      if (!f32) {
+      if (a8) {
+        c.label = "llm.mlp_norm";
+        VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, b.q8, b.q8s, H));
+      } else if (!f32) {
         c.label = "llm.mlp_norm";
         VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, 0, nullptr, b.xn, b.xn_lo, H));
       }
@@ -486,19 +540,25 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       GemmArgs a = gargs();
       a.M = S; a.N = I; a.K = H;
       if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm; }
+      else if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = H; }
       else { a.a = b.xn; a.a_lo = b.xn_lo; a.lda = H; }
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
-      a.c = b.act; a.c_lo = b.act_lo; a.ldc = I; a.c_f32 = f32;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : A_BF16, E_SWIGLU, comp}));
+      a.c = b.act; a.c_lo = b.act_lo; a.ldc = I; a.c_f32 = f32 || a8;
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_SWIGLU, comp}));
     }
     {  // down + residual (+ row statistics)
+      if (a8) {
+        c.label = "llm.down_quant";
+        VLA_TRY(quant_rows(c, b.act, 1, I, S, I, b.q8, I, b.q8s));
+      }
     c.label = "llm.down";
       GemmArgs a = gargs();
       a.M = S; a.N = H; a.K = I;
-      a.a = b.act; a.a_lo = b.act_lo; a.lda = I;
+      if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = I; }
+      else { a.a = b.act; a.a_lo = b.act_lo; a.lda = I; }
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : A_BF16, E_RESID, comp}, &b.xs.rs));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, comp}, &b.xs.rs));
     }
   }
   return VLA_OK;
@@ -1354,6 +1414,19 @@ void fill_plan(vla_step_plan& P, const vla_model* m, const vla_step_shape* s) {
 }  // namespace
 
 extern "C" {
+
+vla_status vla_quantize_rows_e4m3(const void* x, int32_t x_dtype, int32_t rows, int32_t K, int32_t ldx, uint8_t* codes,
+                                  int32_t ldc, float* scales, hipStream_t stream) {
+  if (!x || !codes || !scales) return fail(VLA_ERR_INVALID_ARG, "quantize rows: null pointer");
+  if (x_dtype != VLA_BF16 && x_dtype != VLA_F32) return fail(VLA_ERR_UNSUPPORTED, "quantize rows: input dtype %d", x_dtype);
+  if (rows < 0 || K < 8 || K > 16384 || K % 8 || ldx < K || ldx % 8 || ldc < K || ldc % 8)
+    return fail(VLA_ERR_SHAPE, "quantize rows: K %d (a multiple of 8 in [8, 16384]) with pitches %d, %d", K, ldx, ldc);
+  if (rows == 0) return VLA_OK;
+  Ctx c;
+  c.plan = false; c.st = stream;
+  c.label = "quantize_rows";
+  return quant_rows(c, x, x_dtype == VLA_F32 ? 1 : 0, ldx, rows, K, codes, ldc, scales);
+}
 
 size_t vla_step_workspace_bytes(const vla_model* model, const vla_step_shape* shape) {
   if (check_step(model, shape) != VLA_OK) return 0;

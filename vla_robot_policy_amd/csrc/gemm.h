@@ -32,7 +32,7 @@
 
 namespace vla {
 
-enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_TIME = 5 };
+enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_TIME = 5, A_FP8 = 6 };
 enum EMode { E_STORE = 0, E_ROPE = 1, E_SWIGLU = 2, E_RESID = 3 };
 enum ActKind { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 
@@ -41,6 +41,9 @@ struct GemmArgs {
   // ---- A source
   const void* a;         // BF16/F32/NORM/MERGE: matrix [rows, lda]; PATCH: bf16 images
   const void* a_lo;      // BF16 with compensation: remainder plane, same layout as a
+  const float* a_scale;  // FP8: E4M3FN codes [rows, lda] in a, one float32 scale per row here
+                         // (W8A8: the codes are staged as bytes and widened to bf16 at fragment
+                         // load, which is exact, so the bf16 MFMA forms exact products)
   int lda;
   RowStats rs;           // NORM/MERGE: per-tile row moments of the source rows
   int norm_rms;          // 1: RMSNorm (no mean subtraction), 0: LayerNorm
@@ -166,7 +169,7 @@ struct GemmTile {
   static constexpr int BN = 16 * NBW * WN;
   static constexpr int U = UU;                   // 32-wide k-steps per wave per chunk
   static constexpr int BK = 32 * WK * U;         // chunk width
-  static constexpr int ESZ = sizeof(CT);
+  static constexpr int ESZ = AM == A_FP8 ? 1 : (int)sizeof(CT);   // bytes per A element in LDS
 #ifndef VLA_LDS_PAD
 #define VLA_LDS_PAD 16
 #endif
@@ -174,7 +177,7 @@ struct GemmTile {
   static constexpr int PLANES = AC ? 2 : 1;      // compensated A: hi and lo planes
   static constexpr int APLANE = BM * LROW;
   static constexpr int ABUF = PLANES * APLANE;
-  static constexpr int AG = (AM == A_BF16) ? 8 : 4;  // A elements per loader group
+  static constexpr int AG = (AM == A_BF16) ? 8 : (AM == A_FP8) ? 16 : 4;  // A elements per loader group
   static constexpr int AGROUPS = BM * BK / AG;   // A groups per chunk
   static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
@@ -205,6 +208,7 @@ struct U4x2 { uint4 h, l; };
 template <int AM, int AC> struct ARaw { using type = float4; };
 template <> struct ARaw<A_BF16, 0> { using type = uint4; };
 template <> struct ARaw<A_BF16, 1> { using type = U4x2; };
+template <> struct ARaw<A_FP8, 0> { using type = uint4; };
 
 // ---------------------------------------------------------------- kernel
 template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
@@ -414,7 +418,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const int ar0 = tid / CPR;
   const int ac4 = (tid % CPR) * AG;
   const brsrc ars = make_brsrc(p.a);
-  constexpr int AESZ = (AM == A_BF16 || AM == A_PATCH) ? 2 : 4;
 
   auto load_a = [&](AR (&ar)[GPT], int kc) {
     int k = kc + ac4;
@@ -429,6 +432,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         ar[i].l = bload16(make_brsrc(p.a_lo), off);
       } else if constexpr (AM == A_BF16) {
         ar[i] = bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB);
+      } else if constexpr (AM == A_FP8) {
+        ar[i] = bload16(ars, ok ? (uint32_t)m * p.lda + k : BUF_OOB);
       } else if constexpr (AM == A_F32 || AM == A_NORM) {
         ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 4u : BUF_OOB));
       } else if constexpr (AM == A_PATCH) {
@@ -485,8 +490,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i].h;
         *reinterpret_cast<uint4*>(base + T::APLANE + r * LROW + ac4 * T::ESZ) = ar[i].l;
         continue;
-      } else if constexpr (AM == A_BF16) {
-        // raw copy of 8 bf16 (CT is bf16 for every bf16 source; zeros beyond the edge)
+      } else if constexpr (AM == A_BF16 || AM == A_FP8) {
+        // raw copy of 8 bf16 or 16 fp8 codes (CT is the source type; zeros beyond the edge)
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
         continue;
       } else if constexpr (AM == A_NORM || AM == A_MERGE) {
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         v = ar[i];
       }
       if constexpr (AC) lds_store4_pair(base + r * LROW + ac4 * T::ESZ, T::APLANE, v);
-      else lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
+      else if constexpr (AM != A_FP8) lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
     }
   };
 
@@ -550,7 +555,11 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       }
       F af[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; mb++) lds_frag(af[mb], base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ);
+      for (int mb = 0; mb < MB; mb++) {
+        const char* ap = base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ;
+        if constexpr (AM == A_FP8) af[mb] = fp8x8_to_frag(*reinterpret_cast<const uint2*>(ap));
+        else lds_frag(af[mb], ap);
+      }
       if constexpr (AC) {
         F al[MB];
 #pragma unroll
@@ -735,6 +744,24 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     __syncthreads();
   }
 
+  // ---- W8A8: the per-row scale of the activation codes (the weights'
+  // per-column scale is applied by the epilogues)
+  if constexpr (AM == A_FP8) {
+    const brsrc sr = make_brsrc(p.a_scale);
+    float rsc[XPE];
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      const int r = r0e + i * RPT, m = m0 + r;
+      rsc[i] = bloadf(sr, (r < BM && m < p.M) ? (uint32_t)m * 4u : BUF_OOB);
+    }
+#pragma unroll
+    for (int i = 0; i < XPE; i++) {
+      const int r = r0e + i * RPT;
+      if (r < BM) sT[r * TPITCH + cc] *= rsc[i];
+    }
+    __syncthreads();
+  }
+
   // ---- epilogues (outputs through buffer stores: 32-bit element offsets)
   const brsrc cr = make_brsrc(p.c);
   auto put = [&](uint32_t idx, float v) {
@@ -799,12 +826,18 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       else rows(std::integral_constant<int, 64>{});
       __syncthreads();
     }
-    const float theta = exp2f(-2.0f * (float)fi / (float)D * log2f(p.rope_base));
-    // the thread's rows step by RPT positions: the first angle from sincosf,
-    // each next one by a rotation through RPT * theta
+    // the thread's rows step by RPT positions: the first angle and the step
+    // come from a double-precision frequency and product reduced to [-pi, pi]
+    // in double (a float frequency times a position of several hundred is off
+    // by up to 1e-4 rad), each next angle by a rotation through the step
+    const double theta = pow((double)p.rope_base, -2.0 * (double)fi / (double)D);
+    auto sincos_reduced = [](double a, float* sn_, float* cs_) {
+      a -= rint(a * (0.5 / M_PI)) * (2.0 * M_PI);
+      sincosf((float)a, sn_, cs_);
+    };
     float cs, sn, cd, sd;
-    sincosf((float)(m0 + r0e + p.pos0) * theta, &sn, &cs);
-    sincosf((float)RPT * theta, &sd, &cd);
+    sincos_reduced((double)(m0 + r0e + p.pos0) * theta, &sn, &cs);
+    sincos_reduced((double)RPT * theta, &sd, &cd);
 #pragma unroll
     for (int i = 0; i < XPE; i++) {
       int r = r0e + i * RPT, m = m0 + r;

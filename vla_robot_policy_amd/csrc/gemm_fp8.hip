@@ -1,6 +1,11 @@
 // GEMM instantiations for fp8 (OCP E4M3FN) weights with per-row scales:
 // codes are widened to bf16 in registers (exact), bf16 MFMA, fp32 accumulate,
-// scale applied per output column in the epilogue.
+// scale applied per output column in the epilogue. W8A8 (A_FP8): activation
+// codes (per-row scales) are staged as bytes and widened to bf16 like the
+// weights, so the bf16 MFMA forms exact code products with full fp32
+// accumulation; both scales are applied to the fp32 tile. (The fp8 MFMA's
+// internal accumulation is coarser: 5e-5 relative error at K = 1024 against
+// 2e-7 this way, and a per-token requantisation in every layer amplifies it.)
 #include "gemm_inst.h"
 
 namespace vla {
@@ -15,6 +20,9 @@ bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_SWIGLU)
   VLA_GEMM_CASE(uint8_t, __bf16, A_TIME, E_STORE, 1, 1, 4, 1)
   VLA_GEMM_CASE(uint8_t, __bf16, A_TIME, E_STORE, 4, 4, 1, 1)
+  VLA_GEMM_WIDE(uint8_t, __bf16, A_FP8, E_ROPE)
+  VLA_GEMM_WIDE(uint8_t, __bf16, A_FP8, E_SWIGLU)
+  VLA_GEMM_NARROW(uint8_t, __bf16, A_FP8, E_RESID)
   return false;
 }
 }  // namespace vla

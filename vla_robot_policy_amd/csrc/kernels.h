@@ -25,6 +25,7 @@ const void* k_fill_ref();
 const void* k_stage_rows_ref();
 const void* k_rmsnorm_out_ref();
 const void* k_norm_rows_ref();
+const void* k_quant_rows_ref();
 const void* k_convert_rows_ref();
 bool euler_tail_lookup(int wt, KernelRef* out);
 

@@ -39,6 +39,7 @@ const void* k_fill_ref() { return (const void*)&k_fill_u32; }
 const void* k_stage_rows_ref() { return (const void*)&k_stage_rows; }
 const void* k_rmsnorm_out_ref() { return (const void*)&k_rmsnorm_out; }
 const void* k_norm_rows_ref() { return (const void*)&k_norm_rows; }
+const void* k_quant_rows_ref() { return (const void*)&k_quant_rows; }
 const void* k_convert_rows_ref() { return (const void*)&k_convert_rows; }
 
 bool euler_tail_lookup(int wt, KernelRef* out) {

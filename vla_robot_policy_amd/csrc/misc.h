@@ -53,6 +53,72 @@ __global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, in
 }
 
 // One normalised row per workgroup, in bf16, for the GEMMs that read it:
+// Largest value over a 256-thread workgroup (every thread gets it).
+__device__ __forceinline__ float block_max256(float v) {
+  __shared__ float wm[4];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+}
+
+// Four E4M3FN codes (bytes in order x, y, z, w) of u * inv, clamped to the
+// largest finite magnitude and rounded to nearest even by the converter.
+__device__ __forceinline__ uint32_t e4m3x4(float4 u, float inv) {
+  auto c = [&](float t) { return fminf(fmaxf(t * inv, -448.f), 448.f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(u.x), c(u.y), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c(u.z), c(u.w), w, true);
+  return (uint32_t)w;
+}
+
+// W8A8: E4M3FN codes of bf16 or fp32 rows [M, ldx] (K values each, K a
+// multiple of 8 and at most 16384), one float32 scale max|x| / 448 per row;
+// one workgroup per row, the row held in registers.
+__global__ __launch_bounds__(256) void k_quant_rows(const void* x, int x_f32, int ldx, int K, uint8_t* out, int ldo,
+                                                    float* scale) {
+  constexpr int G = 8;                           // 8-value groups per thread
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float4 v[G][2];
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < G; i++) {
+    const int k = (tid + i * 256) * 8;
+    v[i][0] = v[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < K) {
+      if (x_f32) {
+        const float* xr = (const float*)x + (size_t)r * ldx + k;
+        v[i][0] = *reinterpret_cast<const float4*>(xr);
+        v[i][1] = *reinterpret_cast<const float4*>(xr + 4);
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>((const uint16_t*)x + (size_t)r * ldx + k);
+        auto f4 = [](uint32_t a, uint32_t b) {
+          return make_float4(bf2f((uint16_t)(a & 0xFFFFu)), bf2f((uint16_t)(a >> 16)), bf2f((uint16_t)(b & 0xFFFFu)),
+                             bf2f((uint16_t)(b >> 16)));
+        };
+        v[i][0] = f4(w.x, w.y);
+        v[i][1] = f4(w.z, w.w);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      am = fmaxf(am, fmaxf(fmaxf(fabsf(v[i][h].x), fabsf(v[i][h].y)), fmaxf(fabsf(v[i][h].z), fabsf(v[i][h].w))));
+  }
+  am = block_max256(am);
+  const float inv = am > 0.f ? __fdiv_rn(448.f, am) : 0.f;
+#pragma unroll
+  for (int i = 0; i < G; i++) {
+    const int k = (tid + i * 256) * 8;
+    if (k >= K) continue;
+    uint2 c;
+    c.x = e4m3x4(v[i][0], inv);
+    c.y = e4m3x4(v[i][1], inv);
+    *reinterpret_cast<uint2*>(out + (size_t)r * ldo + k) = c;
+  }
+  if (tid == 0) scale[r] = __fdiv_rn(am, 448.f);
+}
+
 // RMSNorm (x * rstd * g) or LayerNorm ((x - mean) * rstd * g + b, g given as
 // 1 + g when g_plus_one), the row moments merged from the writer's tiles.
 // With out_lo, also the remainder lo = bf16(v - hi) of each value.
@@ -78,11 +144,36 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
   }
   __syncthreads();
   const float2 nc = snc;
-  auto put = [&](int k, float4 x, float4 gg, float4 bb) {
+  auto norm4 = [&](float4 x, float4 gg, float4 bb) -> float4 {
     if (!p.g) gg = make_float4(1.f, 1.f, 1.f, 1.f);
     else if (p.g_plus_one) { gg.x += 1.f; gg.y += 1.f; gg.z += 1.f; gg.w += 1.f; }
-    const float u0 = (x.x - nc.x) * nc.y * gg.x + bb.x, u1 = (x.y - nc.x) * nc.y * gg.y + bb.y;
-    const float u2 = (x.z - nc.x) * nc.y * gg.z + bb.z, u3 = (x.w - nc.x) * nc.y * gg.w + bb.w;
+    return make_float4((x.x - nc.x) * nc.y * gg.x + bb.x, (x.y - nc.x) * nc.y * gg.y + bb.y,
+                       (x.z - nc.x) * nc.y * gg.z + bb.z, (x.w - nc.x) * nc.y * gg.w + bb.w);
+  };
+  if (p.out8) {
+    // W8A8: the normalised row as E4M3FN codes with the scale max|u| / 448
+    // (the whole row is in this thread's registers: K <= 4 * 1024)
+    float4 u[PRE];
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < PRE; i++) {
+      const int k = tid * 4 + i * 1024;
+      u[i] = k < p.K ? norm4(v[i], g[i], b[i]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      am = fmaxf(am, fmaxf(fmaxf(fabsf(u[i].x), fabsf(u[i].y)), fmaxf(fabsf(u[i].z), fabsf(u[i].w))));
+    }
+    am = block_max256(am);
+    const float inv = am > 0.f ? __fdiv_rn(448.f, am) : 0.f;
+#pragma unroll
+    for (int i = 0; i < PRE; i++) {
+      const int k = tid * 4 + i * 1024;
+      if (k < p.K) *reinterpret_cast<uint32_t*>(p.out8 + (size_t)r * p.ldo + k) = e4m3x4(u[i], inv);
+    }
+    if (tid == 0) p.oscale[r] = __fdiv_rn(am, 448.f);
+    return;
+  }
+  auto put = [&](int k, float4 x, float4 gg, float4 bb) {
+    const float4 uu = norm4(x, gg, bb);
+    const float u0 = uu.x, u1 = uu.y, u2 = uu.z, u3 = uu.w;
     uint2 h;
     h.x = pack_bf2(u0, u1);
     h.y = pack_bf2(u2, u3);

@@ -82,7 +82,7 @@ class DeviceWeights:
         bc = lib.BlockCfg(hidden=b.hidden, n_q_heads=b.n_q_heads, n_kv_heads=b.n_kv_heads, head_dim=b.head_dim,
                           intermediate=b.intermediate, rope_base=b.rope_base, eps=b.eps,
                           wdtype=lib.DTYPE_CODE[cfg.wdtype], adtype=lib.VLA_F32 if cfg.wdtype == "f32" else lib.VLA_BF16,
-                          flags=lib.VLA_BLOCK_QK_NORM if b.qk_norm else 0)
+                          flags=(lib.VLA_BLOCK_QK_NORM if b.qk_norm else 0) | (lib.VLA_BLOCK_A8 if b.a8 else 0))
         layers = (lib.BlockWeights * cfg.layers)()
         for l in range(cfg.layers):
             p = f"llm.{l}."

@@ -21,6 +21,7 @@ VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_SHAPE, VLA_ERR_UNSUPPORTED, VLA_ERR_WORKSPA
 VLA_F32, VLA_BF16, VLA_FP8_E4M3 = 0, 1, 2
 DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3}
 VLA_BLOCK_QK_NORM = 1
+VLA_BLOCK_A8 = 2
 VLA_STEP_GRAPH_CACHE = 8
 
 
@@ -127,6 +128,7 @@ def load() -> C.CDLL:
         "vla_step_graph_nodes": (c_int32, [c_void_p]),
         "vla_step_kernel_label": (C.c_char_p, [c_void_p, c_int32]),
         "vla_step_launch_kernel": (S, [c_void_p, c_int32, c_void_p]),
+        "vla_quantize_rows_e4m3": (S, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
         "vla_step_run_shape": (S, [c_void_p, POINTER(StepShape), c_void_p]),
         "vla_step_fused_workspace_bytes": (c_size_t, [POINTER(Model), POINTER(StepShape)]),
         "vla_step_plan_create_fused": (S, [POINTER(Model), POINTER(StepShape), POINTER(StepIO), c_int32, c_void_p,
@@ -242,6 +244,10 @@ def vla_step_kernel_label(plan, index: int):
 
 def vla_step_launch_kernel(plan, index: int, stream: int = 0) -> int:
     return load().vla_step_launch_kernel(plan, index, stream)
+
+
+def vla_quantize_rows_e4m3(x, x_dtype: int, rows: int, K: int, ldx: int, codes, ldc: int, scales, stream: int = 0) -> int:
+    return load().vla_quantize_rows_e4m3(_p(x), x_dtype, rows, K, ldx, _p(codes), ldc, _p(scales), stream)
 
 
 def vla_step_fused_workspace_bytes(model: Model, shape: StepShape) -> int:
