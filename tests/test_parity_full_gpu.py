@@ -39,12 +39,12 @@ def _generate(gu, cfg):
         W = make_weights(cfg)
         W.generate_all(threads=16)
         return W, make_inputs(cfg)
-    return gu.timed(f"cfg{cfg.cid} weights and inputs", gen)
+    return gu.timed(f"{cfg.name} weights and inputs", gen)
 
 
 def test_backbone_full_seq256(gu):
     cfg = get_config(2)
-    gu.say(f"cfg{cfg.cid}: backbone {cfg.layers} layers, seq {cfg.seq}")
+    gu.say(f"{cfg.name}: backbone {cfg.layers} layers, seq {cfg.seq}")
     W, I = _generate(gu, cfg)
     dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
     got = gu.timed("gpu", lambda: gu.run_backbone(cfg, dw, gu.upload_input(I["x"]), cfg.seq))
@@ -56,7 +56,7 @@ def test_backbone_full_seq256(gu):
 
 def test_dit_full_ctx256(gu):
     cfg = get_config(3)
-    gu.say(f"cfg{cfg.cid}: DiT {cfg.dit.layers} layers x {cfg.steps} steps, ctx {cfg.ctx_len}")
+    gu.say(f"{cfg.name}: DiT {cfg.dit.layers} layers x {cfg.steps} steps, ctx {cfg.ctx_len}")
     W, I = _generate(gu, cfg)
     dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
     acts, vel = gu.timed("gpu", lambda: gu.run_dit(cfg, dw, gu.upload_input(I["ctx"]), gu.upload_input(I["noise"])))
@@ -90,7 +90,7 @@ def test_step_full_single_camera(gu):
     from vla_robot_policy_amd import lib
     cfg = get_config(4)
     v = cfg.vit
-    gu.say(f"cfg{cfg.cid}: ViT {v.layers}L -> backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}")
+    gu.say(f"{cfg.name}: ViT {v.layers}L -> backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}")
     W, I = _generate(gu, cfg)
     dw, got = gu.timed("gpu step (eager + 2 replays)", lambda: _step_graph(gu, cfg, W, I))
     # the encoder and merger outputs through their own entry point
@@ -128,15 +128,18 @@ def test_step_full_single_camera_one_step(gu):
         assert e <= 1e-2, k
 
 
-def test_step_full_single_camera_fused(gu):
-    """V-AEFusion at the single-camera workload (2 of 4 Euler steps stale),
-    captured and replayed: the persistent DiT layer kernel runs alongside the
-    full VLM. Cycle 0 (no previous context) and a cycle whose observation is
-    unchanged must equal the plain step bit for bit; a cycle on a new
-    observation is checked against the oracle's fused cycle."""
-    from oracle.io import Weights, to_f64
+@pytest.mark.parametrize("cid, n_stale, tol", [(4, 2, 1e-2), (5, 5, 5e-2)], ids=["single_camera", "fp8_long_context"])
+def test_step_full_fused(gu, cid, n_stale, tol):
+    """V-AEFusion at the full workloads, captured and replayed: the single
+    camera (2 of 4 Euler steps stale, the persistent DiT layer kernel beside
+    the full VLM) and the fp8 long context (5 of 10 stale, the chunk-50 action
+    expert's launch-per-operation path beside the backbone). Cycle 0 (no
+    previous context) and a cycle whose observation is unchanged must equal
+    the plain step bit for bit; a cycle on a new observation is checked
+    against the oracle's fused cycle."""
+    from oracle.io import to_f64
     from oracle.policy import vla_cycle_fused, vlm
-    cfg = get_config(4)
+    cfg = get_config(cid)
     W, I0 = _generate(gu, cfg)
     I1 = make_inputs(cfg.replace(cid=cfg.cid + 100))
     dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
@@ -149,7 +152,7 @@ def test_step_full_single_camera_fused(gu):
             plain[name] = p.outputs()
     finally:
         p.close()
-    f = gu.StepRunner(cfg, dw, I0, n_stale=2)
+    f = gu.StepRunner(cfg, dw, I0, n_stale=n_stale)
     try:
         f.capture()                                    # cycle 0 on I0
         got = f.outputs()
@@ -165,19 +168,20 @@ def test_step_full_single_camera_fused(gu):
     finally:
         f.close()
     Wo = gu.ProgressWeights(W, "oracle")
-    args = lambda I: (to_f64(I["image"]), to_f64(I["text"]), to_f64(I["noise"]))
-    prev = gu.timed("oracle VLM of I0", lambda: vlm(args(I0)[0], args(I0)[1], Wo, cfg))["ctx"]
-    want = gu.timed("oracle fused cycle", lambda: vla_cycle_fused(*args(I1), prev, Wo, cfg, 2))
+    img = lambda I: to_f64(I["image"]) if cfg.vit is not None else None
+    prev = gu.timed("oracle VLM of I0", lambda: vlm(img(I0), to_f64(I0["text"]), Wo, cfg))["ctx"]
+    want = gu.timed("oracle fused cycle",
+                    lambda: vla_cycle_fused(img(I1), to_f64(I1["text"]), to_f64(I1["noise"]), prev, Wo, cfg, n_stale))
     errs = {k: gu.relerr(got[k], want[k]) for k in ("hidden", "actions", "velocities")}
-    gu.say("fused single-camera cycle rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()))
+    gu.say(f"fused {cfg.name} cycle rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items()))
     for k, e in errs.items():
-        assert e <= 1e-2, k
+        assert e <= tol, k
     assert not np.array_equal(got["actions"], plain["I1"]["actions"])   # the stale steps did matter
 
 
 def test_step_full_fp8_long_context(gu):
     cfg = get_config(5)
-    gu.say(f"cfg{cfg.cid}: fp8 backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}, chunk {cfg.dit.chunk}")
+    gu.say(f"{cfg.name}: fp8 backbone seq {cfg.seq} -> DiT {cfg.dit.layers}L x {cfg.steps}, chunk {cfg.dit.chunk}")
     W, I = _generate(gu, cfg)
     _, got = gu.timed("gpu step (eager + 2 replays)", lambda: _step_graph(gu, cfg, W, I))
     want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I))
