@@ -1,25 +1,25 @@
 """Shapes of the five named workloads and of the reduced test shapes.
 
-The named workloads are the ones the policy is measured on:
+The named workloads are the ones the policy is measured on (get_config ids):
 
-  cfg1  one pre-norm transformer block, fp32, seq 64 (hidden 256, 4 q / 2 kv
-        heads of 64, SwiGLU 688, RoPE base 1e4, RMSNorm eps 1e-6)
-  cfg2  36-layer VLM backbone prefill, bf16 weights, seq 256 (hidden 2560,
-        GQA 32/8 x 128, SwiGLU 9728, RoPE base 1e6, final RMSNorm)
-  cfg3  DiT action expert in a 4-step flow-matching Euler loop, bf16
-        (36 layers, hidden 1280, 16 heads, GELU MLP 5120, adaLN from a
-        sinusoidal timestep embedding, 16x7 action chunk, 256 ctx tokens)
-  cfg4  full single-camera step: ViT (24 layers, hidden 1024, 16 heads,
-        224x224 image in 14-px patches) -> 2x2 merger -> 64 visual + 40 text
-        tokens through the cfg2 backbone at seq 104 -> projector -> cfg3 DiT
-  cfg5  560-token backbone (embeddings given) + DiT with a 50x32 chunk and
-        10 Euler steps, every Linear weight in fp8 e4m3 with a float32 scale
-        per output channel, activations bf16
+  1  one pre-norm transformer block, fp32, seq 64 (hidden 256, 4 q / 2 kv
+     heads of 64, SwiGLU 688, RoPE base 1e4, RMSNorm eps 1e-6)
+  2  36-layer VLM backbone prefill, bf16 weights, seq 256 (hidden 2560,
+     GQA 32/8 x 128, SwiGLU 9728, RoPE base 1e6, final RMSNorm)
+  3  DiT action expert in a 4-step flow-matching Euler loop, bf16
+     (36 layers, hidden 1280, 16 heads, GELU MLP 5120, adaLN from a
+     sinusoidal timestep embedding, 16x7 action chunk, 256 ctx tokens)
+  4  full single-camera step: ViT (24 layers, hidden 1024, 16 heads,
+     224x224 image in 14-px patches) -> 2x2 merger -> 64 visual + 40 text
+     tokens through the 36-layer backbone at seq 104 -> projector -> the DiT
+  5  two-camera long-context step: 560-token backbone (embeddings given) +
+     DiT with a 50x32 chunk and 10 Euler steps, every Linear weight in fp8
+     e4m3 with a float32 scale per output channel, activations bf16
 
 Where the pages leave a shape open the plain reading is taken: the Q width
 is heads*head_dim (4096 for the backbone, not the hidden size); the DiT
-context width equals the DiT hidden size; the cfg5 sequence has no vision
-encoder in front of it (its 560 embeddings are given).
+context width equals the DiT hidden size; the long-context sequence has no
+vision encoder in front of it (its 560 embeddings are given).
 """
 
 from __future__ import annotations

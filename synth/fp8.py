@@ -1,6 +1,6 @@
-"""Storage encoding of fp8 weights (OCP E4M3FN) used to *produce* the cfg5 inputs.
+"""Storage encoding of fp8 weights (OCP E4M3FN) used to *produce* the long-context workload's weights.
 
-A cfg5 Linear weight is stored as E4M3FN codes q[n, k] plus one float32 scale
+A Linear weight of that workload is stored as E4M3FN codes q[n, k] plus one float32 scale
 s[n] per output channel, s[n] = max_k |W[n, k]| / 448 (448 is the largest
 finite E4M3FN magnitude). q is W/s rounded to the nearest E4M3FN value, ties
 to the value whose code is even, saturating at +-448. The (q, s) pair is the

@@ -106,14 +106,14 @@ def test_backbone_qk_norm_head128(gu):
     assert e <= 1e-2
 
 
-def test_block_cfg1(gu):
+def test_block_fp32_seq64(gu):
     cfg = get_config(1)
     W, I = make_weights(cfg), make_inputs(cfg)
     dw = gu.DeviceWeights(cfg, W)
     got = gu.run_block(cfg, dw, gu.upload_input(I["x"]), cfg.seq)
     want = run_config(cfg, W, I)["out"]
     e = gu.relerr(got, want)
-    gu.say(f"cfg1 block fp32 seq 64: rel L2 {e:.3e}")
+    gu.say(f"block fp32 seq 64 (hidden 256): rel L2 {e:.3e}")
     assert e <= 1e-4
 
 
