@@ -1317,7 +1317,16 @@ vla_status fused_sched(Ctx& cv, Ctx& ca, const vla_step_plan& P, const vla_step_
   VLA_TRY(dit_begin(ca, P.dit, io, ds));
   VLA_TRY(dit_conditioning(ca, P.dit, io, ds));
   VLA_TRY(dit_in_proj(ca, P.dit, io, ds));
+  // the stale steps share the GPU with the VLM: the layer kernel takes the
+  // fewest workgroups it can run on, leaving the other compute units free
+  const int g_all = ds.G;
+  if (ds.stack) {
+    int g = g_all;
+    while (g > 1 && dit_stack_ok(cf, sh.chunk, g - 16)) g -= 16;
+    ds.G = g;
+  }
   VLA_TRY(dit_steps(ca, P.dit, io, ds, prev, 0, n_stale));
+  ds.G = g_all;
   uint16_t* ctx = nullptr;
   int S = 0;
   VLA_TRY(vlm_sched(cv, P, sh, ctx, S));
