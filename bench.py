@@ -152,7 +152,7 @@ def shape_cache_bench(cfg, texts, steps, warmup):
         lib.vla_step_plan_destroy(plan)
     line = {"metric": "ms per VLA step by text length, one plan with shape-keyed graphs", "unit": "ms",
             "higher_is_better": False, "steps": steps, "warmup": warmup, "data": "synthetic",
-            "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16",
+            "dtype": cfg.wdtype if cfg.wdtype in ("fp8", "int8") else "bf16",
             "config": {"workload": f"{n_vis} visual tokens + text lengths {texts}; plan sized for n_text {max(texts)}",
                        "global_batch": 1, "euler_steps": top.steps},
             "shapes": rows, "alternating_replay_ms": round(switch, 4),
@@ -215,7 +215,7 @@ def fused_bench(cfg, n_stale, steps, warmup):
     log(f"fused cycle {fused_ms:.3f} ms ({fused_nodes} nodes), {n_stale} of {cfg.steps} steps stale")
     line = {"metric": "ms per control cycle, V-AEFusion (stale action-expert steps alongside the VLM)", "unit": "ms",
             "value": round(fused_ms, 4), "higher_is_better": False, "steps": steps, "warmup": warmup,
-            "data": "synthetic", "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16",
+            "data": "synthetic", "dtype": cfg.wdtype if cfg.wdtype in ("fp8", "int8") else "bf16",
             "config": {"workload": f"{cfg.name}: {n_stale} of {cfg.steps} Euler steps stale", "global_batch": 1,
                        "seq_len": cfg.seq, "euler_steps": cfg.steps},
             "plain_step_ms": round(plain_ms, 4), "speedup": round(plain_ms / fused_ms, 4),
@@ -383,6 +383,8 @@ def main():
                     help="Euler steps of the sampler (1 = one-step generation); not the default workload")
     ap.add_argument("--a8", action="store_true",
                     help="W8A8: per-token fp8 activations into the backbone's Linears (fp8 workload); not the default")
+    ap.add_argument("--int8", action="store_true",
+                    help="the fp8 workload with int8 weights and per-token int8 activations in the backbone (W8A8 integer)")
     ap.add_argument("--qk-norm", action="store_true",
                     help="backbone blocks with QK-norm (per-head RMSNorm of Q and K before RoPE); not the default workload")
     ap.add_argument("--shape-cache", default=None,
@@ -408,12 +410,14 @@ def main():
         import dataclasses
         cfg = cfg.replace(block=dataclasses.replace(cfg.block, qk_norm=True))
     variant = "; backbone with QK-norm" if a.qk_norm else ""
-    if a.a8:
+    if a.a8 or a.int8:
         if cfg.wdtype != "fp8":
-            raise SystemExit("--a8 needs the fp8 workload (--config 5)")
+            raise SystemExit("--a8 / --int8 need the fp8 workload (--config 5)")
         import dataclasses
-        cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8=True))
-        variant += "; W8A8: per-token fp8 activations into the backbone's Linears, fp8 MFMA"
+        fmt = "int8" if a.int8 else "fp8"
+        cfg = cfg.replace(wdtype=fmt, block=dataclasses.replace(cfg.block, a8=fmt))
+        variant += (f"; W8A8 {fmt}: {fmt} weights, per-token {fmt} activations into the backbone's Linears "
+                    "(codes widened to bf16 for exact products)")
     if a.euler_steps is not None:
         if not 1 <= a.euler_steps <= 64:
             raise SystemExit("--euler-steps must be in [1, 64]")
@@ -458,7 +462,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(ms, 4), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8" if cfg.wdtype == "fp8" else "bf16", "data": "synthetic",
+        "dtype": cfg.wdtype if cfg.wdtype in ("fp8", "int8") else "bf16", "data": "synthetic",
         "config": {"workload": WORKLOADS[a.config] + variant,
                    "global_batch": 1, "seq_len": cfg.seq,
                    "euler_steps": cfg.steps, "parallelism": "single GPU"},

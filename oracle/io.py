@@ -21,6 +21,8 @@ def to_f64(t) -> np.ndarray:
         return u.view(np.float32).astype(np.float64)
     if t.dtype == "fp8":
         return dequantize_rows(t.data, t.scale)
+    if t.dtype == "int8":   # integer codes times the row's scale
+        return np.asarray(t.data, dtype=np.float64) * np.asarray(t.scale, dtype=np.float64)[:, None]
     raise ValueError(t.dtype)
 
 

@@ -18,8 +18,9 @@ two pre-norms), every query and key head vector is RMS-normalised over the
 head dimension with its own gain (q_norm, k_norm) before RoPE:
   Q_h <- RMSNorm(Q_h, q_norm),  K_g <- RMSNorm(K_g, k_norm).
 With W8A8 (page "开源 APXInf 把 VLA 推理压到 26 毫秒": FP8 weights and
-activations), the input rows of the four Linears (n, the attention output,
-n2 and the SwiGLU product) are replaced by their per-token FP8 values first.
+activations, INT8 where FP8 units are missing), the input rows of the four
+Linears (n, the attention output, n2 and the SwiGLU product) are replaced by
+their per-token FP8 (oracle/fp8.py) or INT8 (oracle/int8.py) values first.
 """
 
 from __future__ import annotations
@@ -28,6 +29,7 @@ import numpy as np
 
 from . import ops
 from .fp8 import fake_quant_act_rows
+from .int8 import fake_quant_act_rows as fake_quant_act_rows_int8
 
 
 def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
@@ -37,7 +39,8 @@ def block(x: np.ndarray, W, prefix: str, shape, pos0: int = 0) -> np.ndarray:
     Hq, Hkv, D = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     # W8A8: every Linear of the block reads its input rows as per-token E4M3FN
     # codes times the row's scale (oracle/fp8.py)
-    act = fake_quant_act_rows if getattr(shape, "a8", False) else (lambda t: t)
+    a8 = getattr(shape, "a8", "")
+    act = {"fp8": fake_quant_act_rows, "int8": fake_quant_act_rows_int8}.get(a8, lambda t: t)
     n = act(ops.rmsnorm(x, W[prefix + "attn_norm"], shape.eps))
     q = ops.linear(n, W[prefix + "wq"]).reshape(S, Hq, D)
     k = ops.linear(n, W[prefix + "wk"]).reshape(S, Hkv, D)

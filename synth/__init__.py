@@ -12,6 +12,8 @@ Storage dtypes:
     even from a float32 draw)
   * ``fp8``  -> numpy uint8 holding OCP E4M3FN codes plus a float32 scale per
     output channel (row of the ``[N_out, K_in]`` weight); see ``synth.fp8``.
+  * ``int8`` -> numpy int8 codes in [-127, 127] plus a float32 scale per
+    output channel; see ``synth.int8``.
 """
 
 from .configs import (  # noqa: F401

@@ -39,7 +39,7 @@ class BlockShape:
     rope_base: float
     eps: float = 1e-6
     qk_norm: bool = False   # per-head RMSNorm of Q and K before RoPE
-    a8: bool = False        # W8A8: per-token fp8 activations into the block's Linears (fp8 weights)
+    a8: str = ""            # W8A8: per-token activations into the block's Linears, "fp8" or "int8" ("": off)
 
     @property
     def q_dim(self) -> int:
@@ -111,7 +111,7 @@ class Config:
     cid: int                 # seed root; 1..5 for the named workloads
     name: str
     kind: str                # 'block' | 'backbone' | 'dit' | 'step'
-    wdtype: str              # 'f32' | 'bf16' | 'fp8'
+    wdtype: str              # 'f32' | 'bf16' | 'fp8' | 'int8'
     block: Optional[BlockShape] = None
     layers: int = 0          # backbone layers
     seq: int = 0             # backbone sequence length

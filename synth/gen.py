@@ -28,6 +28,7 @@ import numpy as np
 
 from .configs import Config
 from . import fp8 as _fp8
+from . import int8 as _int8
 
 KIND_WEIGHTS, KIND_INPUTS, KIND_NOISE = 0, 1, 2
 
@@ -48,7 +49,7 @@ class Spec:
     name: str
     shape: Tuple[int, ...]
     init: str        # 'w' | 'bias' | 'gain' | 'ada_bias' | 'normal'
-    store: str       # 'f32' | 'bf16' | 'fp8'
+    store: str       # 'f32' | 'bf16' | 'fp8' | 'int8'
     kind: int = KIND_WEIGHTS
     fan_in: int = 1
 
@@ -100,6 +101,9 @@ def _draw(cfg: Config, spec: Spec) -> Tensor:
     if spec.store == "fp8":
         codes, scale = _fp8.quantize_rows(v)
         return Tensor(spec.name, "fp8", codes, scale)
+    if spec.store == "int8":
+        codes, scale = _int8.quantize_rows(v)
+        return Tensor(spec.name, "int8", codes, scale)
     raise ValueError(spec.store)
 
 
@@ -144,7 +148,7 @@ class TensorSet:
         total = 0
         for s in self.specs.values():
             n = int(np.prod(s.shape))
-            total += n * {"f32": 4, "bf16": 2, "fp8": 1}[s.store] + (4 * s.shape[0] if s.store == "fp8" else 0)
+            total += n * {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[s.store] + (4 * s.shape[0] if s.store in ("fp8", "int8") else 0)
         return total
 
 
@@ -183,7 +187,7 @@ def backbone_specs(cfg: Config) -> List[Spec]:
 
 def vit_specs(cfg: Config) -> List[Spec]:
     v = cfg.vit
-    m = "bf16" if cfg.wdtype == "fp8" else _mat(cfg)
+    m = "bf16" if cfg.wdtype in ("fp8", "int8") else _mat(cfg)
     D = v.hidden
     out = [
         Spec("vit.pe_w", (D, v.patch_dim), "w", m, fan_in=v.patch_dim),

@@ -44,7 +44,7 @@ def hidden(cfg, W, x, perturb):
 
 def main():
     cfg = get_config(5)
-    cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8=True))
+    cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8="fp8"))
     Wt = make_weights(cfg)
     Wt.generate_all(threads=8)
     W = Weights(Wt)

@@ -85,7 +85,7 @@ def test_a8_block_is_close_to_the_unquantized_block(rng):
     W = Weights(make_weights(cfg))
     x = to_f64(make_inputs(cfg)["x"])
     plain = llm.block(x, W, "llm.0.", cfg.block)
-    a8 = llm.block(x, W, "llm.0.", dataclasses.replace(cfg.block, a8=True))
+    a8 = llm.block(x, W, "llm.0.", dataclasses.replace(cfg.block, a8="fp8"))
     d = np.linalg.norm(a8 - plain) / np.linalg.norm(plain - x)     # relative to the block's update
     # four quantized inputs of about 2^-5 relative rounding each: a few percent, not zero
     assert 1e-3 < d < 0.1, d

@@ -204,7 +204,7 @@ def test_step_full_fp8_long_context_a8(gu):
     import json
     import os
     cfg = get_config(5)
-    cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8=True))
+    cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8="fp8"))
     with open(os.path.join(os.path.dirname(__file__), "golden", "a8_conditioning.json")) as f:
         floor = json.load(f)["hidden_rel_l2_deviation"]
     W, I = _generate(gu, cfg)

@@ -56,7 +56,7 @@ def test_block_qk_norm(gu, wdtype, seq):
 
 def _a8(cfg):
     import dataclasses
-    return cfg.replace(block=dataclasses.replace(cfg.block, a8=True))
+    return cfg.replace(block=dataclasses.replace(cfg.block, a8="fp8"))
 
 
 @pytest.mark.parametrize("seq", [37, 1, 130, 400])
@@ -71,7 +71,7 @@ def test_block_a8(gu, seq):
     got = gu.run_block(cfg, dw, gu.upload_input(I["x"]), seq)
     x, Wo = to_f64(I["x"]), Weights(W)
     want = ollm.block(x, Wo, "llm.0.", cfg.block)
-    plain = ollm.block(x, Wo, "llm.0.", dataclasses.replace(cfg.block, a8=False))
+    plain = ollm.block(x, Wo, "llm.0.", dataclasses.replace(cfg.block, a8=""))
     e = gu.relerr(got, want)
     # on the block's update (out - x), where the quantisation shows
     e_a8, e_plain = gu.relerr(got - x, want - x), gu.relerr(got - x, plain - x)

@@ -18,7 +18,7 @@ import torch
 
 from . import lib
 
-_NP_RAW = {"f32": np.float32, "bf16": np.int16, "fp8": np.uint8}
+_NP_RAW = {"f32": np.float32, "bf16": np.int16, "fp8": np.uint8, "int8": np.int8}
 
 
 class DeviceWeights:
@@ -49,14 +49,14 @@ class DeviceWeights:
         return self.up_array(self.t[name].data).data_ptr()
 
     def up_rows(self, names: Sequence[str], pad_cols: int = 0):
-        """Concatenate matrices along rows (and their fp8 scales); returns (w, s)."""
+        """Concatenate matrices along rows (and their 8-bit scales); returns (w, s)."""
         ts = [self.t[n] for n in names]
         data = np.concatenate([t.data for t in ts], axis=0)
         if pad_cols:
             data = np.pad(data, ((0, 0), (0, pad_cols)))
         w = self.up_array(data).data_ptr()
         s = None
-        if ts[0].dtype == "fp8":
+        if ts[0].dtype in ("fp8", "int8"):
             s = self.up_array(np.concatenate([t.scale for t in ts])).data_ptr()
         return w, s
 

@@ -18,8 +18,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "vla.h")
 
 VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_SHAPE, VLA_ERR_UNSUPPORTED, VLA_ERR_WORKSPACE, VLA_ERR_HIP, VLA_ERR_STATE = (
     0, -1, -2, -3, -4, -5, -6)
-VLA_F32, VLA_BF16, VLA_FP8_E4M3 = 0, 1, 2
-DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3}
+VLA_F32, VLA_BF16, VLA_FP8_E4M3, VLA_INT8 = 0, 1, 2, 3
+DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3, "int8": VLA_INT8}
 VLA_BLOCK_QK_NORM = 1
 VLA_BLOCK_A8 = 2
 VLA_STEP_GRAPH_CACHE = 8

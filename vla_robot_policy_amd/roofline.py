@@ -57,13 +57,13 @@ def _wbytes(wdtype: str, n: int, k: int) -> float:
         return 4.0 * n * k
     if wdtype == "bf16":
         return 2.0 * n * k
-    if wdtype == "fp8":
+    if wdtype in ("fp8", "int8"):
         return 1.0 * n * k + 4.0 * n      # codes + one float32 scale per output channel
     raise ValueError(wdtype)
 
 
 def _compute(wdtype: str) -> str:
-    # W8A16 runs on the bf16 matrix cores (activations are bf16)
+    # 8-bit weights run on the bf16 matrix cores (their codes widen to bf16 exactly)
     return "f32" if wdtype == "f32" else "bf16"
 
 
@@ -102,7 +102,7 @@ def vit_ops(cfg) -> List[Op]:
     v = cfg.vit
     n = cfg.n_images
     S, D = v.n_patches, v.hidden
-    w = "bf16" if cfg.wdtype == "fp8" else cfg.wdtype
+    w = "bf16" if cfg.wdtype in ("fp8", "int8") else cfg.wdtype
     ops = [linear_op("vit.patch_embed", "vit", S, D, v.patch_dim, w, n, bias=True,
                      extra_bytes=4.0 * S * D)]
     L = v.layers * n
