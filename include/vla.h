@@ -57,7 +57,9 @@ typedef enum {
   VLA_ERR_STATE = -6        /* plan used out of order / already captured  */
 } vla_status;
 
-typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2 } vla_dtype;
+/* VLA_INT8 ([A]: INT8 where FP8 units are missing): int8 weight codes in
+ * [-127, 127] with one float32 scale per output row, like FP8_E4M3. */
+typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2, VLA_INT8 = 3 } vla_dtype;
 
 /* ------------------------------------------------------------------ block
  * One pre-norm decoder block ([R] 整体方案, 算子开发, 算子融合):
@@ -71,14 +73,18 @@ typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2 } vla_dtype;
  * is RMS-normalised over head_dim before RoPE: Q_h <- Q_h / sqrt(mean(Q_h^2)
  * + eps) * q_norm, K_g likewise with k_norm; it needs n_q_heads * head_dim
  * to be a multiple of 128.
- * With flags & VLA_BLOCK_A8 (W8A8; [A]: FP8 weights and activations), the
- * input rows of the four Linears (the two normalised rows, the attention
- * output and the SwiGLU product) are rounded to OCP E4M3FN codes with one
- * scale per row, s = max|row| / 448 (nearest value, ties to the even code,
- * from float32), and the Linears run on fp8 MFMAs: y = (codes . W codes^T)
- * * s_row * s_channel. Needs FP8_E4M3 weights, BF16 activations, hidden <=
- * 4096, and the Linear inputs (hidden, n_q_heads * head_dim, intermediate)
- * multiples of 16 and at most 16384 wide; VLA_ERR_UNSUPPORTED otherwise.
+ * With flags & VLA_BLOCK_A8 (W8A8; [A]: FP8 weights and activations, INT8
+ * where FP8 units are missing), the input rows of the four Linears (the two
+ * normalised rows, the attention output and the SwiGLU product) become 8-bit
+ * codes in the weights' format with one scale per row: E4M3FN with s =
+ * max|row| / 448 (nearest value, ties to the even code), or int8 with s =
+ * max|row| / 127 (nearest integer, halves to even), decided from float32.
+ * y = (codes . W codes^T) * s_row * s_channel, with exact code products and
+ * float32 accumulation; q, k, v, the attention and the SwiGLU product stay
+ * float32 until quantised. Needs FP8_E4M3 or INT8 weights, BF16 activations,
+ * hidden <= 4096, and the Linear inputs (hidden, n_q_heads * head_dim,
+ * intermediate) multiples of 16 and at most 16384 wide;
+ * VLA_ERR_UNSUPPORTED otherwise.
  * Supported: head_dim in {64, 128}; hidden, intermediate multiples of 8
  * (of 16 for FP8_E4M3 weights); n_q_heads % n_kv_heads == 0; wdtype F32 with adtype F32, or wdtype
  * BF16 / FP8_E4M3 with adtype BF16.
@@ -228,18 +234,19 @@ vla_status vla_vit_encode(const vla_vit* vit, const void* images, int32_t n_imag
                           void* ws, size_t ws_bytes, hipStream_t stream);
 size_t vla_vit_workspace_bytes(const vla_vit* vit, int32_t n_images);
 
-/* W8A8 activation quantiser ([A]: FP8 weights and activations): each of
- * `rows` rows x[r, 0..K) (x_dtype VLA_BF16 or VLA_F32, row pitch ldx
- * elements) becomes K OCP E4M3FN
- * codes (row pitch ldc bytes) and one float32 scale s[r] = max|x[r]| / 448;
- * codes[r, k] is x[r, k] * (448 / max|x[r]|) in float32, clamped to +-448
- * and rounded to the nearest E4M3FN value, ties to the even code. A zero row
- * gets zero codes and scale 0. K a multiple of 8 in [8, 16384]; pitches
- * multiples of 8. A negative value that rounds to zero keeps its sign
- * (code 0x80). This is the pass a VLA_BLOCK_A8 block runs on the attention
- * output and the SwiGLU product (both in float32). */
-vla_status vla_quantize_rows_e4m3(const void* x, int32_t x_dtype, int32_t rows, int32_t K, int32_t ldx, uint8_t* codes,
-                                  int32_t ldc, float* scales, hipStream_t stream);
+/* W8A8 activation quantiser ([A]: FP8 or INT8 activations): each of `rows`
+ * rows x[r, 0..K) (x_dtype VLA_BF16 or VLA_F32, row pitch ldx elements)
+ * becomes K codes (row pitch ldc bytes) and one float32 scale s[r] =
+ * max|x[r]| / qmax. code_dtype VLA_FP8_E4M3: qmax 448, codes[r, k] is
+ * x[r, k] * (448 / max|x[r]|) in float32, clamped to +-448 and rounded to
+ * the nearest E4M3FN value, ties to the even code; a negative value that
+ * rounds to zero keeps its sign (0x80). code_dtype VLA_INT8: qmax 127, the
+ * nearest integer (halves to even) clipped to +-127. A zero row gets zero
+ * codes and scale 0. K a multiple of 8 in [8, 16384]; pitches multiples of
+ * 8. This is the pass a VLA_BLOCK_A8 block runs on the attention output and
+ * the SwiGLU product (both float32). */
+vla_status vla_quantize_rows(const void* x, int32_t x_dtype, int32_t code_dtype, int32_t rows, int32_t K, int32_t ldx,
+                             void* codes, int32_t ldc, float* scales, hipStream_t stream);
 
 /* ------------------------------------------------------------------ whole step
  * The full policy step ([R] 整体方案: vision -> LLM (with projection layers)

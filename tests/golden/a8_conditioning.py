@@ -4,10 +4,12 @@ relative 6e-8 (float32 rounding) before it is quantised, and the hidden state
 after the final norm is compared with the unperturbed one. Per-token fp8
 requantisation in every Linear turns such perturbations into whole-code steps
 that later layers amplify, so this deviation is a floor for any float32
-implementation of the model against the float64 oracle. Writes
-tests/golden/a8_conditioning.json (several minutes on 8 cores):
+implementation of the model against the float64 oracle. Writes one entry
+per activation format into tests/golden/a8_conditioning.json (several
+minutes each on 8 cores):
 
-    python tests/golden/a8_conditioning.py
+    python tests/golden/a8_conditioning.py fp8
+    python tests/golden/a8_conditioning.py int8
 """
 
 import dataclasses
@@ -20,7 +22,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 sys.path.insert(0, ROOT)
 
-from oracle import fp8, llm, ops  # noqa: E402
+from oracle import llm, ops  # noqa: E402
 from oracle.io import Weights, to_f64  # noqa: E402
 from synth import get_config, make_inputs, make_weights  # noqa: E402
 
@@ -29,22 +31,24 @@ SEED = 0
 
 
 def hidden(cfg, W, x, perturb):
-    orig = llm.fake_quant_act_rows
+    name = {"fp8": "fake_quant_act_rows", "int8": "fake_quant_act_rows_int8"}[cfg.block.a8]
+    orig = getattr(llm, name)
     if perturb:
         rng = np.random.default_rng(SEED)
-        llm.fake_quant_act_rows = lambda t: orig(t * (1 + REL * rng.uniform(-1, 1, t.shape)))
+        setattr(llm, name, lambda t: orig(t * (1 + REL * rng.uniform(-1, 1, t.shape))))
     try:
         h = x
         for l in range(cfg.layers):
             h = llm.block(h, W, f"llm.{l}.", cfg.block)
         return ops.rmsnorm(h, W["llm.final_norm"], cfg.block.eps)
     finally:
-        llm.fake_quant_act_rows = orig
+        setattr(llm, name, orig)
 
 
 def main():
+    fmt = sys.argv[1] if len(sys.argv) > 1 else "fp8"
     cfg = get_config(5)
-    cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8="fp8"))
+    cfg = cfg.replace(wdtype=fmt, block=dataclasses.replace(cfg.block, a8=fmt))
     Wt = make_weights(cfg)
     Wt.generate_all(threads=8)
     W = Weights(Wt)
@@ -52,13 +56,21 @@ def main():
     a = hidden(cfg, W, x, False)
     b = hidden(cfg, W, x, True)
     dev = float(np.linalg.norm(b - a) / np.linalg.norm(a))
-    out = {"workload": cfg.name + " backbone, W8A8", "perturbation_rel": REL, "seed": SEED,
-           "hidden_rel_l2_deviation": dev,
-           "source": "tests/golden/a8_conditioning.py (float64 oracle only)"}
+    entry = {"workload": f"two-camera long-context backbone (36 layers, seq 560), W8A8 with {fmt} weights and activations",
+             "perturbation_rel": REL,
+             "seed": SEED, "hidden_rel_l2_deviation": dev,
+             "source": f"tests/golden/a8_conditioning.py {fmt} (float64 oracle only)"}
     path = os.path.join(ROOT, "tests", "golden", "a8_conditioning.json")
+    table = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            table = json.load(f)
+        if "hidden_rel_l2_deviation" in table:     # a single-format file
+            table = {"fp8": table}
+    table[fmt] = entry
     with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out))
+        json.dump(table, f, indent=1)
+    print(json.dumps(entry))
 
 
 if __name__ == "__main__":

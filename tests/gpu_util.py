@@ -16,7 +16,7 @@ from vla_robot_policy_amd import lib
 from vla_robot_policy_amd.device import DeviceWeights, bf16_bits_to_float, upload_input, workspace
 
 DEV = "cuda:0"
-TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 5e-2}
+TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 5e-2, "int8": 5e-2}
 
 
 def say(*a):

@@ -191,28 +191,29 @@ def test_step_full_fp8_long_context(gu):
         assert e <= 5e-2, k
 
 
-def test_step_full_fp8_long_context_a8(gu):
-    """The fp8 long-context step with W8A8 in the backbone (per-token fp8
-    activations into its Linears), replayed from its graph, against the
-    oracle's W8A8 model. Actions and velocities meet the fp8 bar. The hidden
-    state of this 36-layer W8A8 backbone is ill-conditioned: the float64
-    oracle itself moves by the deviation stored in
-    tests/golden/a8_conditioning.json (0.18) when its activations are
-    perturbed at float32 rounding level before each quantisation, so the
-    hidden state is held to 1.5 times that floor."""
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_step_full_long_context_w8a8(gu, fmt):
+    """The long-context step with W8A8 in the backbone (fp8 or int8 weights
+    with per-token activations of the same format into its Linears),
+    replayed from its graph, against the oracle's W8A8 model. Actions and
+    velocities meet the 8-bit bar. The hidden state of this 36-layer W8A8
+    backbone is ill-conditioned: the float64 oracle itself moves by the
+    deviation stored in tests/golden/a8_conditioning.json (0.18 for fp8, 0.13
+    for int8) when its activations are perturbed at float32 rounding level
+    before each quantisation, so the hidden state is held to 1.5 times that
+    floor."""
     import dataclasses
     import json
     import os
     cfg = get_config(5)
-    cfg = cfg.replace(block=dataclasses.replace(cfg.block, a8="fp8"))
+    cfg = cfg.replace(wdtype=fmt, block=dataclasses.replace(cfg.block, a8=fmt))
     with open(os.path.join(os.path.dirname(__file__), "golden", "a8_conditioning.json")) as f:
-        floor = json.load(f)["hidden_rel_l2_deviation"]
+        floor = json.load(f)[fmt]["hidden_rel_l2_deviation"]
     W, I = _generate(gu, cfg)
     _, got = gu.timed("gpu step (eager + 2 replays)", lambda: _step_graph(gu, cfg, W, I))
     want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I))
     errs = {k: gu.relerr(got[k], want[k]) for k in ("hidden", "actions", "velocities")}
-    gu.say("W8A8 long-context step rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items())
+    gu.say(f"W8A8 {fmt} long-context step rel L2: " + ", ".join(f"{k} {e:.3e}" for k, e in errs.items())
            + f" (hidden-state floor of the oracle itself {floor:.3e})")
     assert errs["actions"] <= 5e-2 and errs["velocities"] <= 5e-2
     assert errs["hidden"] <= 1.5 * floor
-

@@ -26,7 +26,7 @@ def gu():
     return gpu_util
 
 
-@pytest.mark.parametrize("wdtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["f32", "bf16", "fp8", "int8"])
 @pytest.mark.parametrize("seq", [37, 1, 130, 400])     # 400: causal attention with its keys split over workgroups
 def test_block_small(gu, wdtype, seq):
     cfg = small_config("block", wdtype, seq=seq)
@@ -56,16 +56,17 @@ def test_block_qk_norm(gu, wdtype, seq):
 
 def _a8(cfg):
     import dataclasses
-    return cfg.replace(block=dataclasses.replace(cfg.block, a8="fp8"))
+    return cfg.replace(block=dataclasses.replace(cfg.block, a8=cfg.wdtype))
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
 @pytest.mark.parametrize("seq", [37, 1, 130, 400])
-def test_block_a8(gu, seq):
-    """W8A8 block: per-token fp8 activations into fp8 MFMAs. Within the fp8
-    bar of the oracle's W8A8 block, and closer to it than to the same block
-    without activation quantisation."""
+def test_block_a8(gu, seq, fmt):
+    """W8A8 block (fp8 or int8 weights and per-token activations). Within the
+    8-bit bar of the oracle's W8A8 block, and closer to it than to the same
+    block without activation quantisation."""
     import dataclasses
-    cfg = _a8(small_config("block", "fp8", seq=seq))
+    cfg = _a8(small_config("block", fmt, seq=seq))
     W, I = make_weights(cfg), make_inputs(cfg)
     dw = gu.DeviceWeights(cfg, W)
     got = gu.run_block(cfg, dw, gu.upload_input(I["x"]), seq)
@@ -75,20 +76,21 @@ def test_block_a8(gu, seq):
     e = gu.relerr(got, want)
     # on the block's update (out - x), where the quantisation shows
     e_a8, e_plain = gu.relerr(got - x, want - x), gu.relerr(got - x, plain - x)
-    gu.say(f"block W8A8 seq {seq}: rel L2 {e:.3e}; update vs W8A8 oracle {e_a8:.3e}, vs unquantised {e_plain:.3e}")
-    assert e <= gu.TOL["fp8"]
+    gu.say(f"block W8A8 {fmt} seq {seq}: rel L2 {e:.3e}; update vs W8A8 oracle {e_a8:.3e}, vs unquantised {e_plain:.3e}")
+    assert e <= gu.TOL[fmt]
     assert e_a8 < 0.8 * e_plain
 
 
-def test_backbone_a8(gu):
-    cfg = _a8(small_config("backbone", "fp8"))
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_backbone_a8(gu, fmt):
+    cfg = _a8(small_config("backbone", fmt))
     W, I = make_weights(cfg), make_inputs(cfg)
     dw = gu.DeviceWeights(cfg, W)
     got = gu.run_backbone(cfg, dw, gu.upload_input(I["x"]), cfg.seq)
     want = run_config(cfg, W, I)["hidden"]
     e = gu.relerr(got, want)
-    gu.say(f"backbone W8A8: rel L2 {e:.3e}")
-    assert e <= gu.TOL["fp8"]
+    gu.say(f"backbone W8A8 {fmt}: rel L2 {e:.3e}")
+    assert e <= gu.TOL[fmt]
 
 
 def test_backbone_qk_norm_head128(gu):
@@ -117,7 +119,7 @@ def test_block_fp32_seq64(gu):
     assert e <= 1e-4
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "int8"])
 def test_backbone_small(gu, wdtype):
     cfg = small_config("backbone", wdtype)
     W, I = make_weights(cfg), make_inputs(cfg)
@@ -159,7 +161,7 @@ def test_backbone_causality_bitwise(gu):
     assert np.array_equal(y1, y3)            # run-to-run bitwise reproducible
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "int8"])
 def test_dit_small(gu, wdtype):
     cfg = small_config("dit", wdtype)
     W, I = make_weights(cfg), make_inputs(cfg)
@@ -210,10 +212,10 @@ def test_vit_small(gu):
     assert ez <= 1e-2 and em <= 1e-2
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "int8"])
 def test_step_small_eager_and_graph(gu, wdtype):
     cfg = small_config("step", wdtype)
-    if wdtype == "fp8":
+    if wdtype in ("fp8", "int8"):
         cfg = cfg.replace(vit=None, n_images=0, n_text=13, seq=13, ctx_len=13)
     W, I = make_weights(cfg), make_inputs(cfg)
     dw = gu.DeviceWeights(cfg, W)

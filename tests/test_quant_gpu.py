@@ -1,5 +1,5 @@
-"""The W8A8 activation quantiser on the GPU (vla_quantize_rows_e4m3) against
-the oracle's (oracle/fp8.py), bit for bit: both take their decisions from
+"""The W8A8 activation quantiser on the GPU (vla_quantize_rows, E4M3FN and
+int8 codes) against the oracle's (oracle/fp8.py, oracle/int8.py), bit for bit: both take their decisions from
 the same float32 values (bf16 inputs are exact in float32), so every code
 and every scale must agree. Rows cover a zero row, codes in the E4M3FN
 subnormal range, exact ties (a row maximum of 448 makes the multiplier 1),
@@ -8,7 +8,8 @@ saturation at the row maximum, and magnitudes from 1e-3 to 1e3."""
 import numpy as np
 import pytest
 
-from oracle.fp8 import quantize_act_rows
+from oracle import fp8 as ofp8
+from oracle import int8 as oint8
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +48,8 @@ def _rows(rng, K):
 
 @pytest.mark.parametrize("K", [264, 4096, 9728])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_quantize_rows_bitwise(gu, K, dtype):
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_quantize_rows_bitwise(gu, K, dtype, fmt):
     import torch
     from vla_robot_policy_amd import lib
     rng = np.random.default_rng(11)
@@ -64,9 +66,11 @@ def test_quantize_rows_bitwise(gu, K, dtype):
     R = x32.shape[0]
     codes = torch.empty((R, K), dtype=torch.uint8, device=gu.DEV)
     scales = torch.empty(R, dtype=torch.float32, device=gu.DEV)
-    lib.check(lib.vla_quantize_rows_e4m3(xd, code, R, K, K, codes, K, scales))
+    cd = lib.VLA_FP8_E4M3 if fmt == "fp8" else lib.VLA_INT8
+    lib.check(lib.vla_quantize_rows(xd, code, cd, R, K, K, codes, K, scales))
     torch.cuda.synchronize()
-    want_c, want_s = quantize_act_rows(x32)
+    want_c, want_s = (ofp8 if fmt == "fp8" else oint8).quantize_act_rows(x32)
+    want_c = want_c.view(np.uint8)
     got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
     bad = np.argwhere(got_c != want_c)
     if bad.size:

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvla.so")
-SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_f32.hip", "kernels_misc.hip", "dit_stack.hip"]
+SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_int8.hip", "gemm_f32.hip", "kernels_misc.hip", "dit_stack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -227,11 +227,11 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   a.ksplit = ksplit;
   // weight-type / alignment requirements of the 8-element fragment loads
   if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
-  if (op.wdtype == VLA_FP8_E4M3 && (a.K % 16 != 0 || a.ldw % 16 != 0))
-    return fail(VLA_ERR_SHAPE, "gemm: fp8 weights need K %d and pitch %d to be multiples of 16", a.K, a.ldw);
-  const int ag = op.am == A_BF16 ? 8 : op.am == A_FP8 ? 16 : 4;   // activation elements per 16-byte load
-  if (op.am == A_FP8 && !a.a_scale && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: fp8 activations without row scales");
-  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM || op.am == A_FP8) && (a.lda % ag != 0 || a.K % ag != 0))
+  if ((op.wdtype == VLA_FP8_E4M3 || op.wdtype == VLA_INT8) && (a.K % 16 != 0 || a.ldw % 16 != 0))
+    return fail(VLA_ERR_SHAPE, "gemm: 8-bit weights need K %d and pitch %d to be multiples of 16", a.K, a.ldw);
+  const int ag = op.am == A_BF16 ? 8 : a_codes(op.am) ? 16 : 4;   // activation elements per 16-byte load
+  if (a_codes(op.am) && !a.a_scale && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: 8-bit activations without row scales");
+  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM || a_codes(op.am)) && (a.lda % ag != 0 || a.K % ag != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
   // buffer-load offsets are 32-bit: operands up to 2 GiB
   const double wrows = op.em == E_SWIGLU ? (double)a.n_half + a.N : (double)a.N;
@@ -255,6 +255,7 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   bool found = false;
   if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
   else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
+  else if (op.wdtype == VLA_INT8) found = gemm_lookup_int8(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
   else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
   if (!found) return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d/%d", op.wdtype, op.am, op.em, mb, wn, wk, nbw);
   if (c.plan) { c.kernels++; return VLA_OK; }
@@ -360,19 +361,20 @@ vla_status norm_rows(Ctx& c, const float* x, int ldx, int M, int K, RowStats rs,
 
 // W8A8: the normalised rows as E4M3FN codes with one scale per row (K <= 4096)
 vla_status norm_rows8(Ctx& c, const float* x, int ldx, int M, int K, RowStats rs, int rms, float eps, const float* g,
-                      uint8_t* out8, float* oscale, int ldo) {
+                      uint8_t* out8, float* oscale, int ldo, int int8) {
   if (K % 4 != 0 || K > 4096 || ldx % 4 != 0 || ldo % 4 != 0) return fail(VLA_ERR_SHAPE, "norm (fp8 out): row length %d", K);
   NormArgs a{};
   a.x = x; a.ldx = ldx; a.M = M; a.K = K; a.rs = rs; a.rms = rms; a.eps = eps;
-  a.g = g; a.out8 = out8; a.oscale = oscale; a.ldo = ldo;
+  a.g = g; a.out8 = out8; a.oscale = oscale; a.ldo = ldo; a.out8_int8 = int8;
   return launch(c, k_norm_rows_ref(), dim3(M), dim3(256), 0, {arg(a)});
 }
 
-// W8A8: E4M3FN codes of bf16 or fp32 rows with one scale per row (K <= 16384)
-vla_status quant_rows(Ctx& c, const void* x, int x_f32, int ldx, int M, int K, uint8_t* out, int ldo, float* scale) {
+// W8A8: E4M3FN or int8 codes of bf16 or fp32 rows with one scale per row (K <= 16384)
+vla_status quant_rows(Ctx& c, const void* x, int x_f32, int ldx, int M, int K, uint8_t* out, int ldo, float* scale,
+                      int int8) {
   if (K % 8 != 0 || K > 16384 || ldx % 8 != 0 || ldo % 8 != 0) return fail(VLA_ERR_SHAPE, "quant rows: row length %d", K);
   return launch(c, k_quant_rows_ref(), dim3(M), dim3(256), 0,
-                {arg(x), arg(x_f32), arg(ldx), arg(K), arg(out), arg(ldo), arg(scale)});
+                {arg(x), arg(x_f32), arg(ldx), arg(K), arg(out), arg(ldo), arg(scale), arg(int8)});
 }
 
 vla_status convert_rows(Ctx& c, const float* x, int ldx, int M, int N, void* out, int ldo, int out_f32) {
@@ -380,18 +382,20 @@ vla_status convert_rows(Ctx& c, const float* x, int ldx, int M, int N, void* out
                 {arg(x), arg(ldx), arg(M), arg(N), arg(out), arg(ldo), arg(out_f32)});
 }
 
-bool dtype_ok(int t) { return t == VLA_F32 || t == VLA_BF16 || t == VLA_FP8_E4M3; }
+bool dtype_ok(int t) { return t == VLA_F32 || t == VLA_BF16 || t == VLA_FP8_E4M3 || t == VLA_INT8; }
+// 8-bit weights (E4M3FN or int8 codes) carry one float32 scale per output row
+bool scaled8(int t) { return t == VLA_FP8_E4M3 || t == VLA_INT8; }
 
 // ------------------------------------------------------------------ backbone
 vla_status check_block_cfg(const vla_block_cfg* cfg) {
   if (!cfg) return fail(VLA_ERR_INVALID_ARG, "null block cfg");
   if (cfg->flags & ~(VLA_BLOCK_QK_NORM | VLA_BLOCK_A8)) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags 0x%x: unknown bits", cfg->flags);
   if (cfg->flags & VLA_BLOCK_A8) {
-    if (cfg->wdtype != VLA_FP8_E4M3 || cfg->adtype != VLA_BF16)
-      return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp8 activations need fp8 weights and bf16 activations");
+    if (!scaled8(cfg->wdtype) || cfg->adtype != VLA_BF16)
+      return fail(VLA_ERR_UNSUPPORTED, "block cfg: 8-bit activations need fp8 or int8 weights and bf16 activations");
     const int qd = cfg->n_q_heads * cfg->head_dim;
     if (cfg->hidden > 4096 || cfg->hidden % 16 || qd > 16384 || qd % 16 || cfg->intermediate > 16384 || cfg->intermediate % 16)
-      return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp8 activations need hidden <= 4096 and Linear inputs <= 16384 wide, multiples of 16");
+      return fail(VLA_ERR_UNSUPPORTED, "block cfg: 8-bit activations need hidden <= 4096 and Linear inputs <= 16384 wide, multiples of 16");
   }
   if (!dtype_ok(cfg->wdtype) || (cfg->adtype != VLA_F32 && cfg->adtype != VLA_BF16))
     return fail(VLA_ERR_INVALID_ARG, "block cfg: bad dtype (w %d, act %d)", cfg->wdtype, cfg->adtype);
@@ -399,7 +403,7 @@ vla_status check_block_cfg(const vla_block_cfg* cfg) {
     return fail(VLA_ERR_UNSUPPORTED, "block cfg: fp32 weights need fp32 activations and vice versa");
   if (cfg->hidden <= 0 || cfg->hidden % 8 || cfg->intermediate <= 0 || cfg->intermediate % 8)
     return fail(VLA_ERR_SHAPE, "block cfg: hidden %d / intermediate %d must be positive multiples of 8", cfg->hidden, cfg->intermediate);
-  if (cfg->wdtype == VLA_FP8_E4M3 && (cfg->hidden % 16 || cfg->intermediate % 16))
+  if (scaled8(cfg->wdtype) && (cfg->hidden % 16 || cfg->intermediate % 16))
     return fail(VLA_ERR_SHAPE, "block cfg: fp8 weights need hidden %d / intermediate %d to be multiples of 16", cfg->hidden, cfg->intermediate);
   if (cfg->n_kv_heads <= 0 || cfg->n_q_heads <= 0 || cfg->n_q_heads % cfg->n_kv_heads)
     return fail(VLA_ERR_SHAPE, "block cfg: n_q_heads %d not a multiple of n_kv_heads %d", cfg->n_q_heads, cfg->n_kv_heads);
@@ -417,7 +421,7 @@ vla_status check_block_weights(const vla_block_cfg* cfg, const vla_block_weights
   if (!w) return fail(VLA_ERR_INVALID_ARG, "null block weights");
   if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
     return fail(VLA_ERR_INVALID_ARG, "block weights: null tensor pointer");
-  if (cfg->wdtype == VLA_FP8_E4M3 && (!w->s_qkv || !w->s_o || !w->s_gate_up || !w->s_down))
+  if (scaled8(cfg->wdtype) && (!w->s_qkv || !w->s_o || !w->s_gate_up || !w->s_down))
     return fail(VLA_ERR_INVALID_ARG, "block weights: fp8 weights need scales");
   if ((cfg->flags & VLA_BLOCK_QK_NORM) && (!w->q_norm || !w->k_norm))
     return fail(VLA_ERR_INVALID_ARG, "block weights: QK-norm needs q_norm and k_norm");
@@ -480,13 +484,14 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   // W8A8: each Linear reads its input as per-row E4M3FN codes (the norms
   // write codes, the attention and SwiGLU outputs are quantised by a row pass)
   const bool a8 = (cfg.flags & VLA_BLOCK_A8) != 0;
-  const int am_bf = a8 ? A_FP8 : A_BF16;
+  const int i8 = wt == VLA_INT8 ? 1 : 0;              // the activation codes follow the weights' format
+  const int am_bf = a8 ? (i8 ? A_I8 : A_FP8) : A_BF16;
   for (int l = 0; l < n_layers; l++) {
     const vla_block_weights& w = layers[l];
     {  // RMSNorm -> fused QKV -> RoPE
       if (a8) {
         c.label = "llm.attn_norm";
-        VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, b.q8, b.q8s, H));
+        VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, b.q8, b.q8s, H, i8));
       } else if (!f32) {
         c.label = "llm.attn_norm";
         VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, 0, nullptr, b.xn, nullptr, H));
@@ -517,7 +522,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
     {  // O-proj + residual (+ row statistics)
       if (a8) {
         c.label = "llm.o_quant";
-        VLA_TRY(quant_rows(c, b.ao, 1, qd, S, qd, b.q8, qd, b.q8s));
+        VLA_TRY(quant_rows(c, b.ao, 1, qd, S, qd, b.q8, qd, b.q8s, i8));
       }
     c.label = "llm.o";
       GemmArgs a = gargs();
@@ -531,7 +536,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
       if (a8) {
         c.label = "llm.mlp_norm";
-        VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, b.q8, b.q8s, H));
+        VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, b.q8, b.q8s, H, i8));
       } else if (!f32) {
         c.label = "llm.mlp_norm";
         VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, 0, nullptr, b.xn, b.xn_lo, H));
@@ -549,7 +554,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
     {  // down + residual (+ row statistics)
       if (a8) {
         c.label = "llm.down_quant";
-        VLA_TRY(quant_rows(c, b.act, 1, I, S, I, b.q8, I, b.q8s));
+        VLA_TRY(quant_rows(c, b.act, 1, I, S, I, b.q8, I, b.q8s, i8));
       }
     c.label = "llm.down";
       GemmArgs a = gargs();
@@ -598,12 +603,12 @@ vla_status check_dit(const vla_dit* d) {
   if (!d) return fail(VLA_ERR_INVALID_ARG, "null dit");
   const vla_dit_cfg& c = d->cfg;
   if (c.flags != 0) return fail(VLA_ERR_UNSUPPORTED, "dit cfg flags must be 0");
-  if (c.wdtype != VLA_BF16 && c.wdtype != VLA_FP8_E4M3) return fail(VLA_ERR_UNSUPPORTED, "dit: weights must be bf16 or fp8");
+  if (c.wdtype != VLA_BF16 && !scaled8(c.wdtype)) return fail(VLA_ERR_UNSUPPORTED, "dit: weights must be bf16, fp8 or int8");
   if (c.head_dim != 80 && c.head_dim != 64) return fail(VLA_ERR_SHAPE, "dit: head_dim %d not in {64, 80}", c.head_dim);
   if (c.heads <= 0 || c.hidden != c.heads * c.head_dim) return fail(VLA_ERR_SHAPE, "dit: hidden %d != heads*head_dim", c.hidden);
   if (c.hidden % 8 || c.mlp % 8 || c.tdim % 8 || c.ctx_dim % 8 || c.layers <= 0 || c.mlp <= 0)
     return fail(VLA_ERR_SHAPE, "dit: widths must be positive multiples of 8");
-  if (c.wdtype == VLA_FP8_E4M3 && (c.hidden % 16 || c.mlp % 16 || c.tdim % 16 || c.ctx_dim % 16))
+  if (scaled8(c.wdtype) && (c.hidden % 16 || c.mlp % 16 || c.tdim % 16 || c.ctx_dim % 16))
     return fail(VLA_ERR_SHAPE, "dit: fp8 weights need widths that are multiples of 16");
   if (!d->layers || !d->w_ada || !d->b_ada || !d->w_ckv || !d->b_ckv || !d->w_t1 || !d->b_t1 || !d->w_t2 || !d->b_t2 ||
       !d->w_f || !d->b_f || !d->w_in || !d->b_in || !d->w_out || !d->b_out)
@@ -613,10 +618,10 @@ vla_status check_dit(const vla_dit* d) {
     if (!L.w_qkv || !L.b_qkv || !L.w_o || !L.b_o || !L.w_cq || !L.b_cq || !L.w_co || !L.b_co || !L.w_up || !L.b_up ||
         !L.w_down || !L.b_down)
       return fail(VLA_ERR_INVALID_ARG, "dit layer %d: null tensor pointer", l);
-    if (c.wdtype == VLA_FP8_E4M3 && (!L.s_qkv || !L.s_o || !L.s_cq || !L.s_co || !L.s_up || !L.s_down))
+    if (scaled8(c.wdtype) && (!L.s_qkv || !L.s_o || !L.s_cq || !L.s_co || !L.s_up || !L.s_down))
       return fail(VLA_ERR_INVALID_ARG, "dit layer %d: fp8 weights need scales", l);
   }
-  if (c.wdtype == VLA_FP8_E4M3 && (!d->s_ada || !d->s_ckv || !d->s_t1 || !d->s_t2 || !d->s_f || !d->s_in || !d->s_out))
+  if (scaled8(c.wdtype) && (!d->s_ada || !d->s_ckv || !d->s_t1 || !d->s_t2 || !d->s_f || !d->s_in || !d->s_out))
     return fail(VLA_ERR_INVALID_ARG, "dit: fp8 weights need scales");
   return VLA_OK;
 }
@@ -808,7 +813,7 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
         const float* ss[6] = {w.s_qkv, w.s_o, w.s_cq, w.s_co, w.s_up, w.s_down};
         const float* bs[6] = {w.b_qkv, w.b_o, w.b_cq, w.b_co, w.b_up, w.b_down};
-        for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = wt == VLA_FP8_E4M3 ? ss[i] : nullptr; a.b[i] = bs[i]; }
+        for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = scaled8(wt) ? ss[i] : nullptr; a.b[i] = bs[i]; }
         const bool last_launch = k == K - 1 && l == L - 1;
         a.wq_next = last_launch ? nullptr : d.layers[(l + 1) % L].w_qkv;
         a.part = c.part; a.cnt = c.cnt_tile; a.err = s.derr;
@@ -1385,7 +1390,7 @@ vla_status check_step(const vla_model* m, const vla_step_shape* s) {
   VLA_TRY(check_dit(m->dit));
   if (m->dit->cfg.wdtype != m->backbone->cfg.wdtype) return fail(VLA_ERR_UNSUPPORTED, "step: backbone and DiT weight dtypes differ");
   if (!m->w_proj || !m->b_proj) return fail(VLA_ERR_INVALID_ARG, "step: null projector");
-  if (m->backbone->cfg.wdtype == VLA_FP8_E4M3 && !m->s_proj) return fail(VLA_ERR_INVALID_ARG, "step: fp8 projector needs scales");
+  if (scaled8(m->backbone->cfg.wdtype) && !m->s_proj) return fail(VLA_ERR_INVALID_ARG, "step: 8-bit projector needs scales");
   if (s->n_images < 0 || s->n_text < 0) return fail(VLA_ERR_SHAPE, "step: negative token counts");
   if (s->n_images > 0) {
     VLA_TRY(check_vit(m->vit));
@@ -1424,17 +1429,19 @@ void fill_plan(vla_step_plan& P, const vla_model* m, const vla_step_shape* s) {
 
 extern "C" {
 
-vla_status vla_quantize_rows_e4m3(const void* x, int32_t x_dtype, int32_t rows, int32_t K, int32_t ldx, uint8_t* codes,
-                                  int32_t ldc, float* scales, hipStream_t stream) {
+vla_status vla_quantize_rows(const void* x, int32_t x_dtype, int32_t code_dtype, int32_t rows, int32_t K, int32_t ldx,
+                             void* codes, int32_t ldc, float* scales, hipStream_t stream) {
   if (!x || !codes || !scales) return fail(VLA_ERR_INVALID_ARG, "quantize rows: null pointer");
   if (x_dtype != VLA_BF16 && x_dtype != VLA_F32) return fail(VLA_ERR_UNSUPPORTED, "quantize rows: input dtype %d", x_dtype);
+  if (!scaled8(code_dtype)) return fail(VLA_ERR_UNSUPPORTED, "quantize rows: code dtype %d", code_dtype);
   if (rows < 0 || K < 8 || K > 16384 || K % 8 || ldx < K || ldx % 8 || ldc < K || ldc % 8)
     return fail(VLA_ERR_SHAPE, "quantize rows: K %d (a multiple of 8 in [8, 16384]) with pitches %d, %d", K, ldx, ldc);
   if (rows == 0) return VLA_OK;
   Ctx c;
   c.plan = false; c.st = stream;
   c.label = "quantize_rows";
-  return quant_rows(c, x, x_dtype == VLA_F32 ? 1 : 0, ldx, rows, K, codes, ldc, scales);
+  return quant_rows(c, x, x_dtype == VLA_F32 ? 1 : 0, ldx, rows, K, (uint8_t*)codes, ldc, scales,
+                    code_dtype == VLA_INT8 ? 1 : 0);
 }
 
 size_t vla_step_workspace_bytes(const vla_model* model, const vla_step_shape* shape) {

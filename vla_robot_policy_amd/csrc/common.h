@@ -94,6 +94,22 @@ __device__ __forceinline__ FragBF16 fp8x8_to_frag(uint2 codes) {
   return f;
 }
 
+// Eight int8 codes widened to bf16: |code| <= 127 needs 7 significant bits,
+// so the float32 value's upper half is the exact bf16
+__device__ __forceinline__ FragBF16 int8x8_to_frag(uint2 codes) {
+  uint32_t h[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint32_t w = j < 2 ? codes.x : codes.y;
+    const int sh = (j & 1) * 16;
+    const float lo = (float)(int8_t)(w >> sh), hi = (float)(int8_t)(w >> (sh + 8));
+    h[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  FragBF16 f;
+  f.v = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  return f;
+}
+
 __device__ __forceinline__ float fp8_to_f32(uint8_t c) {
   f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
   return v[0];

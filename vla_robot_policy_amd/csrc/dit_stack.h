@@ -150,6 +150,12 @@ template <> struct DsW<uint8_t> {
   __device__ static raw load(brsrc r, uint32_t off) { return bload8<CP_NT>(r, off); }
   __device__ static FragBF16 frag(raw v) { return fp8x8_to_frag(v); }
 };
+template <> struct DsW<int8_t> {
+  using raw = uint2;
+  static constexpr int ESZ = 1;
+  __device__ static raw load(brsrc r, uint32_t off) { return bload8<CP_NT>(r, off); }
+  __device__ static FragBF16 frag(raw v) { return int8x8_to_frag(v); }
+};
 
 // A unit is NB blocks of 16 output columns over a k range of KW: 16 columns
 // x D for QKV, SAO, CAQ and CAO; 32 columns x D for UP; 16 columns x 2D (one

@@ -32,7 +32,9 @@
 
 namespace vla {
 
-enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_TIME = 5, A_FP8 = 6 };
+enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_TIME = 5, A_FP8 = 6, A_I8 = 7 };
+// 8-bit activation codes with a per-row scale (W8A8)
+constexpr bool a_codes(int am) { return am == A_FP8 || am == A_I8; }
 enum EMode { E_STORE = 0, E_ROPE = 1, E_SWIGLU = 2, E_RESID = 3 };
 enum ActKind { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 
@@ -41,7 +43,7 @@ struct GemmArgs {
   // ---- A source
   const void* a;         // BF16/F32/NORM/MERGE: matrix [rows, lda]; PATCH: bf16 images
   const void* a_lo;      // BF16 with compensation: remainder plane, same layout as a
-  const float* a_scale;  // FP8: E4M3FN codes [rows, lda] in a, one float32 scale per row here
+  const float* a_scale;  // FP8 / I8: E4M3FN or int8 codes [rows, lda] in a, one float32 scale per row here
                          // (W8A8: the codes are staged as bytes and widened to bf16 at fragment
                          // load, which is exact, so the bf16 MFMA forms exact products)
   int lda;
@@ -97,6 +99,13 @@ template <> struct WLoad<uint8_t> {
   static constexpr int ESZ = 1;
   __device__ static raw load(brsrc r, uint32_t off) { return bload8<CP_NT>(r, off); }
   __device__ static frag cvt(raw r) { return fp8x8_to_frag(r); }
+};
+template <> struct WLoad<int8_t> {
+  using raw = uint2;
+  using frag = FragBF16;
+  static constexpr int ESZ = 1;
+  __device__ static raw load(brsrc r, uint32_t off) { return bload8<CP_NT>(r, off); }
+  __device__ static frag cvt(raw r) { return int8x8_to_frag(r); }
 };
 struct F32x8 { uint4 a, b; };
 template <> struct WLoad<float> {
@@ -169,7 +178,7 @@ struct GemmTile {
   static constexpr int BN = 16 * NBW * WN;
   static constexpr int U = UU;                   // 32-wide k-steps per wave per chunk
   static constexpr int BK = 32 * WK * U;         // chunk width
-  static constexpr int ESZ = AM == A_FP8 ? 1 : (int)sizeof(CT);   // bytes per A element in LDS
+  static constexpr int ESZ = a_codes(AM) ? 1 : (int)sizeof(CT);   // bytes per A element in LDS
 #ifndef VLA_LDS_PAD
 #define VLA_LDS_PAD 16
 #endif
@@ -177,7 +186,7 @@ struct GemmTile {
   static constexpr int PLANES = AC ? 2 : 1;      // compensated A: hi and lo planes
   static constexpr int APLANE = BM * LROW;
   static constexpr int ABUF = PLANES * APLANE;
-  static constexpr int AG = (AM == A_BF16) ? 8 : (AM == A_FP8) ? 16 : 4;  // A elements per loader group
+  static constexpr int AG = (AM == A_BF16) ? 8 : a_codes(AM) ? 16 : 4;  // A elements per loader group
   static constexpr int AGROUPS = BM * BK / AG;   // A groups per chunk
   static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
@@ -209,6 +218,7 @@ template <int AM, int AC> struct ARaw { using type = float4; };
 template <> struct ARaw<A_BF16, 0> { using type = uint4; };
 template <> struct ARaw<A_BF16, 1> { using type = U4x2; };
 template <> struct ARaw<A_FP8, 0> { using type = uint4; };
+template <> struct ARaw<A_I8, 0> { using type = uint4; };
 
 // ---------------------------------------------------------------- kernel
 template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         ar[i].l = bload16(make_brsrc(p.a_lo), off);
       } else if constexpr (AM == A_BF16) {
         ar[i] = bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB);
-      } else if constexpr (AM == A_FP8) {
+      } else if constexpr (a_codes(AM)) {
         ar[i] = bload16(ars, ok ? (uint32_t)m * p.lda + k : BUF_OOB);
       } else if constexpr (AM == A_F32 || AM == A_NORM) {
         ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 4u : BUF_OOB));
@@ -490,7 +500,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i].h;
         *reinterpret_cast<uint4*>(base + T::APLANE + r * LROW + ac4 * T::ESZ) = ar[i].l;
         continue;
-      } else if constexpr (AM == A_BF16 || AM == A_FP8) {
+      } else if constexpr (AM == A_BF16 || a_codes(AM)) {
         // raw copy of 8 bf16 or 16 fp8 codes (CT is the source type; zeros beyond the edge)
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
         continue;
@@ -522,7 +532,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         v = ar[i];
       }
       if constexpr (AC) lds_store4_pair(base + r * LROW + ac4 * T::ESZ, T::APLANE, v);
-      else if constexpr (AM != A_FP8) lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
+      else if constexpr (!a_codes(AM)) lds_store4((CT*)nullptr, base + r * LROW + ac4 * T::ESZ, v);
     }
   };
 
@@ -558,6 +568,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       for (int mb = 0; mb < MB; mb++) {
         const char* ap = base + (mb * 16 + (lane & 15)) * LROW + klocal * T::ESZ;
         if constexpr (AM == A_FP8) af[mb] = fp8x8_to_frag(*reinterpret_cast<const uint2*>(ap));
+        else if constexpr (AM == A_I8) af[mb] = int8x8_to_frag(*reinterpret_cast<const uint2*>(ap));
         else lds_frag(af[mb], ap);
       }
       if constexpr (AC) {
@@ -746,7 +757,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 
   // ---- W8A8: the per-row scale of the activation codes (the weights'
   // per-column scale is applied by the epilogues)
-  if constexpr (AM == A_FP8) {
+  if constexpr (a_codes(AM)) {
     const brsrc sr = make_brsrc(p.a_scale);
     float rsc[XPE];
 #pragma unroll

@@ -15,6 +15,7 @@ struct KernelRef {
 bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
 bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
 bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
+bool gemm_lookup_int8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
 
 // Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
 // the attention kernel and the merge of its key-split partials

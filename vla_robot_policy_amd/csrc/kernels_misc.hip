@@ -48,6 +48,7 @@ bool euler_tail_lookup(int wt, KernelRef* out) {
   if (wt == 0) { out->fn = (const void*)&k_euler_tail<float>; return true; }
   if (wt == 1) { out->fn = (const void*)&k_euler_tail<uint16_t>; return true; }
   if (wt == 2) { out->fn = (const void*)&k_euler_tail<uint8_t>; return true; }
+  if (wt == 3) { out->fn = (const void*)&k_euler_tail<int8_t>; return true; }
   return false;
 }
 

@@ -72,12 +72,21 @@ __device__ __forceinline__ uint32_t e4m3x4(float4 u, float inv) {
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c(u.z), c(u.w), w, true);
   return (uint32_t)w;
 }
+// Four int8 codes of u * inv: nearest integer (halves to even), clipped to 127.
+__device__ __forceinline__ uint32_t i8x4(float4 u, float inv) {
+  auto c = [&](float t) { return (uint32_t)(int)fminf(fmaxf(rintf(t * inv), -127.f), 127.f) & 0xFFu; };
+  return c(u.x) | (c(u.y) << 8) | (c(u.z) << 16) | (c(u.w) << 24);
+}
+// 8-bit codes of four values: E4M3FN (qmax 448) or int8 (qmax 127)
+__device__ __forceinline__ uint32_t codes4(float4 u, float inv, int int8) { return int8 ? i8x4(u, inv) : e4m3x4(u, inv); }
 
-// W8A8: E4M3FN codes of bf16 or fp32 rows [M, ldx] (K values each, K a
-// multiple of 8 and at most 16384), one float32 scale max|x| / 448 per row;
-// one workgroup per row, the row held in registers.
+// W8A8: E4M3FN (int8 = 0) or int8 (int8 = 1) codes of bf16 or fp32 rows
+// [M, ldx] (K values each, K a multiple of 8 and at most 16384), one float32
+// scale max|x| / qmax per row (qmax 448 or 127); one workgroup per row, the
+// row held in registers.
 __global__ __launch_bounds__(256) void k_quant_rows(const void* x, int x_f32, int ldx, int K, uint8_t* out, int ldo,
-                                                    float* scale) {
+                                                    float* scale, int int8) {
+  const float qmax = int8 ? 127.f : 448.f;
   constexpr int G = 8;                           // 8-value groups per thread
   const int r = blockIdx.x, tid = threadIdx.x;
   float4 v[G][2];
@@ -106,17 +115,17 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* x, int x_f32, in
       am = fmaxf(am, fmaxf(fmaxf(fabsf(v[i][h].x), fabsf(v[i][h].y)), fmaxf(fabsf(v[i][h].z), fabsf(v[i][h].w))));
   }
   am = block_max256(am);
-  const float inv = am > 0.f ? __fdiv_rn(448.f, am) : 0.f;
+  const float inv = am > 0.f ? __fdiv_rn(qmax, am) : 0.f;
 #pragma unroll
   for (int i = 0; i < G; i++) {
     const int k = (tid + i * 256) * 8;
     if (k >= K) continue;
     uint2 c;
-    c.x = e4m3x4(v[i][0], inv);
-    c.y = e4m3x4(v[i][1], inv);
+    c.x = codes4(v[i][0], inv, int8);
+    c.y = codes4(v[i][1], inv, int8);
     *reinterpret_cast<uint2*>(out + (size_t)r * ldo + k) = c;
   }
-  if (tid == 0) scale[r] = __fdiv_rn(am, 448.f);
+  if (tid == 0) scale[r] = __fdiv_rn(am, qmax);
 }
 
 // RMSNorm (x * rstd * g) or LayerNorm ((x - mean) * rstd * g + b, g given as
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
                        (x.z - nc.x) * nc.y * gg.z + bb.z, (x.w - nc.x) * nc.y * gg.w + bb.w);
   };
   if (p.out8) {
-    // W8A8: the normalised row as E4M3FN codes with the scale max|u| / 448
+    // W8A8: the normalised row as 8-bit codes with the scale max|u| / qmax
     // (the whole row is in this thread's registers: K <= 4 * 1024)
     float4 u[PRE];
     float am = 0.f;
@@ -162,13 +171,14 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
       am = fmaxf(am, fmaxf(fmaxf(fabsf(u[i].x), fabsf(u[i].y)), fmaxf(fabsf(u[i].z), fabsf(u[i].w))));
     }
     am = block_max256(am);
-    const float inv = am > 0.f ? __fdiv_rn(448.f, am) : 0.f;
+    const float qmax = p.out8_int8 ? 127.f : 448.f;
+    const float inv = am > 0.f ? __fdiv_rn(qmax, am) : 0.f;
 #pragma unroll
     for (int i = 0; i < PRE; i++) {
       const int k = tid * 4 + i * 1024;
-      if (k < p.K) *reinterpret_cast<uint32_t*>(p.out8 + (size_t)r * p.ldo + k) = e4m3x4(u[i], inv);
+      if (k < p.K) *reinterpret_cast<uint32_t*>(p.out8 + (size_t)r * p.ldo + k) = codes4(u[i], inv, p.out8_int8);
     }
-    if (tid == 0) p.oscale[r] = __fdiv_rn(am, 448.f);
+    if (tid == 0) p.oscale[r] = __fdiv_rn(am, qmax);
     return;
   }
   auto put = [&](int k, float4 x, float4 gg, float4 bb) {
@@ -202,6 +212,7 @@ template <typename WT> __device__ __forceinline__ float wget(const void* w, size
 template <> __device__ __forceinline__ float wget<uint16_t>(const void* w, size_t i) { return bf2f(((const uint16_t*)w)[i]); }
 template <> __device__ __forceinline__ float wget<float>(const void* w, size_t i) { return ((const float*)w)[i]; }
 template <> __device__ __forceinline__ float wget<uint8_t>(const void* w, size_t i) { return fp8_to_f32(((const uint8_t*)w)[i]); }
+template <> __device__ __forceinline__ float wget<int8_t>(const void* w, size_t i) { return (float)((const int8_t*)w)[i]; }
 
 
 

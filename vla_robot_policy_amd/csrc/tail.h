@@ -27,7 +27,8 @@ struct NormArgs {
   int rms; float eps;         // 1: RMSNorm, 0: LayerNorm
   const float* g; int g_plus_one; const float* bsh;   // gain (NULL = 1), 1 + g, shift (NULL = 0)
   uint16_t* out; uint16_t* out_lo; int ldo;            // bf16 result, optional remainder plane
-  uint8_t* out8; float* oscale;                        // instead: E4M3FN codes [M, ldo] and row scales (K <= 4096)
+  uint8_t* out8; float* oscale;                        // instead: 8-bit codes [M, ldo] and row scales (K <= 4096)
+  int out8_int8;                                       //   int8 codes (else E4M3FN)
 };
 
 }  // namespace vla

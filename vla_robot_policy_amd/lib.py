@@ -128,7 +128,7 @@ def load() -> C.CDLL:
         "vla_step_graph_nodes": (c_int32, [c_void_p]),
         "vla_step_kernel_label": (C.c_char_p, [c_void_p, c_int32]),
         "vla_step_launch_kernel": (S, [c_void_p, c_int32, c_void_p]),
-        "vla_quantize_rows_e4m3": (S, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+        "vla_quantize_rows": (S, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
         "vla_step_run_shape": (S, [c_void_p, POINTER(StepShape), c_void_p]),
         "vla_step_fused_workspace_bytes": (c_size_t, [POINTER(Model), POINTER(StepShape)]),
         "vla_step_plan_create_fused": (S, [POINTER(Model), POINTER(StepShape), POINTER(StepIO), c_int32, c_void_p,
@@ -246,8 +246,9 @@ def vla_step_launch_kernel(plan, index: int, stream: int = 0) -> int:
     return load().vla_step_launch_kernel(plan, index, stream)
 
 
-def vla_quantize_rows_e4m3(x, x_dtype: int, rows: int, K: int, ldx: int, codes, ldc: int, scales, stream: int = 0) -> int:
-    return load().vla_quantize_rows_e4m3(_p(x), x_dtype, rows, K, ldx, _p(codes), ldc, _p(scales), stream)
+def vla_quantize_rows(x, x_dtype: int, code_dtype: int, rows: int, K: int, ldx: int, codes, ldc: int, scales,
+                      stream: int = 0) -> int:
+    return load().vla_quantize_rows(_p(x), x_dtype, code_dtype, rows, K, ldx, _p(codes), ldc, _p(scales), stream)
 
 
 def vla_step_fused_workspace_bytes(model: Model, shape: StepShape) -> int:
