@@ -541,6 +541,19 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   for (int mb = 0; mb < MB; mb++)
 #pragma unroll
     for (int j = 0; j < NBW; j++) acc[mb][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // W8A8 integer: int8 codes of both operands meet in int8 MFMAs with exact
+  // int32 accumulation. One 16x16x64 instruction takes two of the 32-wide
+  // k-steps: each lane passes its 8 codes of both steps, on the A and the B
+  // side alike, so the pairs of k it multiplies are the same.
+  constexpr bool I8MMA = AM == A_I8 && std::is_same_v<WT, int8_t> && T::WLDS;
+  static_assert(!I8MMA || U % 2 == 0, "int8 MFMAs take the k-steps in pairs");
+  i32x4 acci[I8MMA ? MB : 1][I8MMA ? NBW : 1];
+  if constexpr (I8MMA) {
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int j = 0; j < NBW; j++) acci[mb][j] = (i32x4){0, 0, 0, 0};
+  }
 
   // One k-step: every A and B fragment of the step is requested from LDS
   // before the first MFMA, so the reads overlap instead of each MFMA waiting
@@ -548,6 +561,32 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   auto compute = [&](int buf, const RR& br) {
     const char* base = sA + buf * T::ABUF;
     const char* wbase = sW + buf * T::WBUF;
+    if constexpr (I8MMA) {
+      auto pair = [](const char* p0, const char* p1) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(p0), hi = *reinterpret_cast<const uint2*>(p1);
+        return (i32x4){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      };
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        const int k0 = (u * WK + wk) * 32 + kl, k1 = ((u + 1) * WK + wk) * 32 + kl;
+        i32x4 bi[NBW], ai[MB];
+#pragma unroll
+        for (int j = 0; j < NBW; j++) {
+          const char* wp = wbase + ((wn * NBW + j) * 16 + (lane & 15)) * WROW;
+          bi[j] = pair(wp + k0, wp + k1);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+          const char* ap = base + (mb * 16 + (lane & 15)) * LROW;
+          ai[mb] = pair(ap + k0, ap + k1);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+          for (int j = 0; j < NBW; j++) acci[mb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai[mb], bi[j], acci[mb][j], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < U; u++) {
       int klocal = (u * WK + wk) * 32 + kl;
@@ -644,6 +683,15 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     VLA_GEMM_ITER(c + 3, r3, r0, r2, a1, a0)
   }
 #undef VLA_GEMM_ITER
+
+  if constexpr (I8MMA) {
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int j = 0; j < NBW; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[mb][j][i] = (float)acci[mb][j][i];
+  }
 
   // ---- reduce the WK wave slices into the fp32 LDS tile: every slice is
   // written at once (slice w at sT + w * BM * TPITCH), one barrier, then the
