@@ -664,7 +664,12 @@ struct DitState {
   float* xb[2] = {nullptr, nullptr};
   float* x1 = nullptr; float* x2 = nullptr;
   uint16_t* qkv = nullptr; uint16_t* ao = nullptr; uint16_t* q = nullptr; uint16_t* h = nullptr;
-  int* derr = nullptr; uint16_t* aos = nullptr;
+  int* derr = nullptr;
+  uint16_t* aos = nullptr;   // the layer kernel's self-attention output
+  // the layer kernel's flagged words (two bf16 + a flag each): QKV output
+  // and cross-attention query, one block
+  uint2* fw = nullptr; size_t fw_words = 0;
+  uint2* fqkv = nullptr; uint2* fq = nullptr;
   uint16_t* u = nullptr;   // modulated LayerNorm rows of the launch-per-operation path (bf16)
   bool stack = false;
   int G = 0;
@@ -685,14 +690,21 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.xb[0] = s.xs.x; s.xb[1] = c.take<float>((size_t)n * D);
   s.x1 = c.take<float>((size_t)n * D);
   s.x2 = c.take<float>((size_t)n * D);
-  s.qkv = c.take<uint16_t>((size_t)n * 3 * D);
-  s.ao = c.take<uint16_t>((size_t)n * D);
-  s.q = c.take<uint16_t>((size_t)n * D);
-  s.h = c.take<uint16_t>((size_t)n * cf.mlp);
   s.G = cu_count();
   s.stack = dit_stack_ok(cf, n, s.G);
+  if (s.stack) {
+    const size_t wq = (size_t)n * 3 * D / 2, wd = (size_t)n * D / 2;
+    s.fw_words = wq + wd;
+    s.fw = c.take<uint2>(s.fw_words);
+    s.fqkv = s.fw; s.fq = s.fqkv + wq;
+    s.aos = c.take<uint16_t>((size_t)n * D);
+  } else {
+    s.qkv = c.take<uint16_t>((size_t)n * 3 * D);
+    s.q = c.take<uint16_t>((size_t)n * D);
+  }
+  s.ao = c.take<uint16_t>((size_t)n * D);
+  s.h = c.take<uint16_t>((size_t)n * cf.mlp);
   s.derr = c.take<int>(64);
-  s.aos = s.stack ? c.take<uint16_t>((size_t)n * D) : nullptr;   // the layer kernel's self-attention output
   s.u = !s.stack && cf.wdtype != VLA_F32 ? c.take<uint16_t>((size_t)n * D) : nullptr;
   if (s.stack) {
     // phase and tile counters of the layer kernel live in the shared counter
@@ -706,6 +718,9 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
     VLA_TRY(launch(c, k_fill_ref(), dim3((nclr + 255) / 256), dim3(256), 0, {arg(c.cnt_tile), arg(z), arg(nclr)}));
     int one = 1;
     VLA_TRY(launch(c, k_fill_ref(), dim3(1), dim3(256), 0, {arg(s.derr), arg(z), arg(one)}));
+    // flagged words start at flag 0; the run's launches use flags 1, 2, ...
+    const int nfw = (int)(s.fw_words * 2);
+    VLA_TRY(launch(c, k_fill_ref(), dim3((nfw + 255) / 256), dim3(256), 0, {arg(s.fw), arg(z), arg(nfw)}));
   }
   return VLA_OK;
 }
@@ -807,7 +822,8 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
         a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
         a.x_in = s.xb[l & 1]; a.x1 = s.x1; a.x2 = s.x2; a.x_out = s.xb[(l + 1) & 1];
-        a.qkv = s.qkv; a.q = s.q; a.aos = s.aos; a.aoc = s.ao; a.h = s.h;
+        a.qkv = s.fqkv; a.q = s.fq; a.aos = s.aos; a.aoc = s.ao; a.h = s.h;
+        a.flag = 1u + (unsigned)(k * L + l);   // increasing over the run, whose start cleared the words
         a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.cv = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldc = L * 2 * D;
         a.mod = m;
         const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};

@@ -22,16 +22,19 @@
 // workgroup (u + base_p) mod G, so a workgroup knows its units in advance and
 // streams their weights into registers before it waits for the previous
 // phase: the HBM latency of the next weights overlaps the current phase.
-// A phase is complete when its counter reaches the number of units (tiles
-// for DOWN). Producers write with device-coherent (sc1) stores, wait for
-// them, then count; consumers poll the counter. Every buffer written inside
-// the launch (the fp32 residual stream has one buffer per sublayer; the two
-// attentions have one output buffer each) is written once before anything
-// reads it, so once its phase is counted it is read with ordinary cached
-// loads: no XCD's private L2 can hold an older copy. Every wait is
-// bounded: on time-out the workgroup records an error, poisons its outputs
-// with NaN and leaves, so a fault can never hang the device. The workgroup
-// that completes the last DOWN tile resets the counters for the next launch.
+// The outputs of QKV and CAQ, which only the attention phases' few
+// workgroups read, travel as flagged words (below): the attention polls the
+// words of its head, and the load that sees them there is the load that
+// brings them. Every other phase hands on by counters: it writes with
+// device-coherent (sc1) stores, waits for them, then counts, and the next
+// phase polls the counter. Every buffer written inside the launch (the fp32
+// residual stream has one buffer per sublayer) is written once before
+// anything reads it, so once its phase is counted it is read with ordinary
+// cached loads: no XCD's private L2 can hold an older copy.
+// Every wait is bounded: on time-out the workgroup records an error,
+// poisons its outputs with NaN and leaves, so a fault can never hang the
+// device. The workgroup that completes the last DOWN tile resets the
+// counters for the next launch.
 //
 // Each LayerNorm is computed by every workgroup that needs it, from the fp32
 // residual stream held in registers (two-pass mean / variance), so no
@@ -72,8 +75,9 @@ struct DitLayerArgs {
   float* x1;
   float* x2;
   float* x_out;
-  uint16_t* qkv;                  // [n, 3D] bf16
-  uint16_t* q;                    // [n, D] cross-attention query
+  // flagged words (two bf16 of adjacent columns + flag): [n, 3D / 2], [n, D / 2]
+  uint2* qkv;
+  uint2* q;                       // cross-attention query
   uint16_t* aos;                  // [n, D] self-attention output
   uint16_t* aoc;                  // [n, D] cross-attention output
   uint16_t* h;                    // [n, mlp] GELU output
@@ -88,12 +92,55 @@ struct DitLayerArgs {
   float* part;                    // DOWN slice partials [slices][D/16][256]
   unsigned* cnt;                  // ds_counter_words(D) counters (zero between launches)
   int* err;                       // set to 1 when a wait times out
+  unsigned flag;                  // this launch's word flag: nonzero, and above every flag written since the words were cleared
 };
 
 __device__ __forceinline__ void st_sc1_f32(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-// base must be the same for the whole wave (a buffer resource is uniform)
-__device__ __forceinline__ void st_sc1_u16(brsrc base, uint32_t idx, uint16_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16(v, base, idx * 2u, 0, CP_SC1);
+
+// ---------------------------------------------------------------- flagged words
+// A flagged word is 8 bytes: two bf16 of adjacent columns, then the flag of
+// the launch that wrote it, stored by one device-coherent 8-byte store (an
+// aligned 8-byte store reaches memory whole, so a reader sees the old or
+// the new word, never half of each). A consumer polls until every word it
+// needs carries the launch's flag; the producer neither waits for its stores
+// nor counts. The buffers are cleared before a sampler run and the flags of
+// its launches increase, so no word left by an earlier launch can pass.
+__device__ __forceinline__ void st_fw(brsrc r, uint32_t word, uint32_t data, uint32_t flag) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, make_uint2(data, flag)), r, word * 8u, 0, CP_SC1);
+}
+
+// Poll NCH chunks of two flagged words per thread. word(i) is chunk i's first
+// word, -1 for no chunk, -2 for a chunk of zeros (a row beyond the chunk);
+// put(i, data) takes its four bf16 once both of its flags are the launch's.
+// Every pending chunk is read each round: the pollers are the attention
+// phases' few workgroups, with a head's rows each (a few KB). False after
+// DS_SPIN rounds.
+template <int NCH, typename WordF, typename PutF>
+__device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, WordF word, PutF put) {
+  static_assert(NCH <= 64, "one pending bit per chunk");
+  uint4 v[NCH];
+  uint64_t pend = 0;
+#pragma unroll
+  for (int i = 0; i < NCH; i++) {
+    const int w = word(i);
+    if (w >= 0) pend |= 1ull << i;
+    else if (w == -2) put(i, make_uint2(0u, 0u));
+    v[i] = bload16<CP_SC1>(r, w >= 0 ? (uint32_t)w * 8u : BUF_OOB);
+  }
+  for (unsigned spins = 0;; spins++) {
+#pragma unroll
+    for (int i = 0; i < NCH; i++)
+      if ((pend >> i & 1) && v[i].y == flag && v[i].w == flag) {
+        put(i, make_uint2(v[i].x, v[i].z));
+        pend &= ~(1ull << i);
+      }
+    if (!pend) return true;
+    if (spins >= DS_SPIN) return false;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int i = 0; i < NCH; i++)
+      if (pend >> i & 1) v[i] = bload16<CP_SC1>(r, (uint32_t)word(i) * 8u);
+  }
 }
 
 // ---------------------------------------------------------------- phase geometry
@@ -226,17 +273,14 @@ __device__ __forceinline__ void ds_mma(const char* rA, int apitch, const typenam
 }
 
 // ---------------------------------------------------------------- attention of one head (<= 16 queries)
-// The four waves take interleaved blocks of 32 keys: S^T = K Q^T per block,
-// online softmax per lane, O^T = V^T P^T, with every MFMA fragment loaded
-// straight from memory (K and Q rows are contiguous in the head dimension;
+// Cross-attention: the four waves take interleaved blocks of 32 context
+// keys: S^T = K Q^T per block, online softmax per lane, O^T = V^T P^T. Q
+// comes from LDS (staged from its flagged words); the K and V fragments are
+// loaded straight from memory (K rows are contiguous in the head dimension;
 // a V^T fragment gathers 8 keys of one column with 2-byte loads, in the key
 // order the lane's P values already have). With more than one block the
 // waves' partial (max, sum, O) are combined in LDS; with one block wave 0
-// writes the output itself. Inputs are complete when this runs (cached
-// loads); the outputs are device-coherent (sc1) stores.
-__device__ __forceinline__ FragBF16 ds_gfrag(brsrc r, uint32_t off) {
-  FragBF16 f; f.v = __builtin_bit_cast(bf16x8, bload16(r, off)); return f;
-}
+// writes the output itself (device-coherent bf16 stores).
 
 // The fragments of one 32-key block: K for the two 16-key halves and the
 // three 32-wide steps of the (padded) head dimension; V^T for the six
@@ -272,20 +316,20 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nb
 // `f` holds this wave's first block when `have0` (requested before the
 // caller's wait); each later round is requested before the current one is
 // computed.
-__device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const uint16_t* Kp, const uint16_t* Vp, int ldkv,
-                                             uint16_t* O, int ldo, int nq, int nk, int hd, float scale_log2,
-                                             char* lds_o, DsAttFr& f, bool have0) {
+// qs: Q rows [16][DS_DP] bf16 in LDS, zero beyond nq rows and hd columns;
+// the output goes to columns oc .. oc + hd of O's rows (ldo bf16 columns).
+__device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp, const uint16_t* Vp, int ldkv, uint16_t* O,
+                                             int ldo, int oc, int nq, int nk, int hd, float scale_log2, char* lds_o,
+                                             DsAttFr& f, bool have0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qn = lane & 15, grp = lane >> 4;
-  const brsrc qr = make_brsrc(Q), kr = make_brsrc(Kp), vr = make_brsrc(Vp), orr = make_brsrc(O);
+  const brsrc kr = make_brsrc(Kp), vr = make_brsrc(Vp), orr = make_brsrc(O);
   const int nblk = (nk + DS_KB - 1) / DS_KB;
 
   FragBF16 qf[DS_DP / 32];
 #pragma unroll
-  for (int ds = 0; ds < DS_DP / 32; ds++) {
-    int d = ds * 32 + grp * 8;
-    qf[ds] = ds_gfrag(qr, (qn < nq && d < hd) ? ((uint32_t)qn * ldq + d) * 2u : BUF_OOB);
-  }
+  for (int ds = 0; ds < DS_DP / 32; ds++)
+    qf[ds].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qs + (qn * DS_DP + ds * 32 + grp * 8) * 2));
   if (!have0) ds_att_frags(kr, vr, wave, nblk, nk, ldkv, hd, f);
   f32x4 oacc[DS_DP / 16];
 #pragma unroll
@@ -367,7 +411,8 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
           uint2 pk;
           pk.x = pack_bf2(oacc[db][0] * inv, oacc[db][1] * inv);
           pk.y = pack_bf2(oacc[db][2] * inv, oacc[db][3] * inv);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(qn * ldo + d) * 2u, 0, CP_SC1);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(qn * ldo + oc + d) * 2u, 0,
+                                                CP_SC1);
         }
       }
     }
@@ -402,15 +447,86 @@ __device__ __forceinline__ void ds_attention(const uint16_t* Q, int ldq, const u
     uint2 pk;
     pk.x = pack_bf2(acc.x * inv, acc.y * inv);
     pk.y = pack_bf2(acc.z * inv, acc.w * inv);
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(q * ldo + d) * 2u, 0, CP_SC1);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(q * ldo + oc + d) * 2u, 0, CP_SC1);
   }
 }
 
+// Self-attention of one head over the chunk's n <= 16 rows, from LDS: Q and
+// K rows [16][DS_DP] and V transposed [DS_DP][16], zero beyond n rows and hd
+// columns. Wave 0 computes S^T = K Q^T, the softmax and O^T = V^T P^T as
+// one 32-key block whose keys 16..31 are absent (their P is zero), with the
+// arithmetic of the cross-attention's single-block case.
+__device__ __forceinline__ void ds_self_att(const char* st, uint16_t* O, int ldo, int oc, int n, int hd, float scale_log2) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63, qn = lane & 15, grp = lane >> 4;
+  const char* qs = st;
+  const char* ks = st + 16 * DS_DP * 2;
+  const char* vt = st + 2 * 16 * DS_DP * 2;
+  f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < DS_DP / 32; ds++) {
+    FragBF16 qf, kf;
+    qf.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qs + (qn * DS_DP + ds * 32 + grp * 8) * 2));
+    kf.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ks + (qn * DS_DP + ds * 32 + grp * 8) * 2));
+    mma32(s, kf, qf);
+  }
+  // lane (query qn, group g) holds the scores of keys 4g .. 4g + 3
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float v = grp * 4 + i < n ? s[i] * scale_log2 : -INFINITY;
+    s[i] = v;
+    m = fmaxf(m, v);
+  }
+  m = fmaxf(m, __shfl_xor(m, 16, WAVE));
+  m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+  float pv[8], l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    pv[i] = exp2f(s[i] - m);
+    pv[4 + i] = 0.f;
+    l += pv[i];
+  }
+  l += __shfl_xor(l, 16, WAVE);
+  l += __shfl_xor(l, 32, WAVE);
+  FragBF16 pf;
+  frag_from_floats(pf, pv);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const brsrc orr = make_brsrc(O);
+#pragma unroll
+  for (int db = 0; db < DS_DP / 16; db++) {
+    const uint2 v2 = *reinterpret_cast<const uint2*>(vt + ((db * 16 + qn) * 16 + 4 * grp) * 2);
+    FragBF16 vf;
+    vf.v = __builtin_bit_cast(bf16x8, make_uint4(v2.x, v2.y, 0u, 0u));
+    f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+    mma32(o, vf, pf);
+    const int d = db * 16 + grp * 4;
+    if (qn < n && d < hd) {
+      uint2 pk;
+      pk.x = pack_bf2(o[0] * inv, o[1] * inv);
+      pk.y = pack_bf2(o[2] * inv, o[3] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pk), orr, (uint32_t)(qn * ldo + oc + d) * 2u, 0,
+                                            CP_SC1);
+    }
+  }
+}
+
+// True when every thread of the workgroup passed (sflag[2] is cleared at the
+// kernel's start and set only by a failure, after which the workgroup leaves).
+__device__ __forceinline__ bool ds_all(bool ok, int* sflag) {
+  if (!ok) sflag[2] = 1;
+  __syncthreads();
+  return sflag[2] == 0;
+}
+
 // ---------------------------------------------------------------- the layer kernel
-// LDS: [region A: bf16 A operand (16 x D, 16 x 2D for DOWN) or attention
-// partials] [4 waves x 2 blocks x 256 fp32 wave sums] [flags]
+// LDS: [region A: bf16 A operand (16 x D, 16 x 2D for DOWN), or attention
+// partials then the head's staged Q, K, V^T] [4 waves x 2 blocks x 256 fp32
+// wave sums] [flags]
+constexpr int DS_ATT_PART = (4 * 16 * 2 + 4 * 16 * DS_DP) * 4;
+constexpr int DS_ATT_STAGE = 3 * 16 * DS_DP * 2;
 __host__ __device__ constexpr int ds_region_a(int D) {
-  return (16 * (4 * D + 16) > (4 * 16 * 2 + 4 * 16 * DS_DP) * 4) ? 16 * (4 * D + 16) : (4 * 16 * 2 + 4 * 16 * DS_DP) * 4;
+  return 16 * (4 * D + 16) > DS_ATT_PART + DS_ATT_STAGE ? 16 * (4 * D + 16) : DS_ATT_PART + DS_ATT_STAGE;
 }
 __host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_a(D) + 2 * 4 * 256 * 4 + 64; }
 
@@ -470,12 +586,16 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
   // before its wait: the first context K / V block of a cross-attention
   // head, a LayerNorm's shift / scale, the weights of the GEMM units. Each
   // kind of phase keeps its own registers across its own wait.
-  auto wait_prev = [&]() -> bool {
-    if (PH == 0 || ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), sflag)) return true;
-    // time-out: record it, poison this workgroup's outputs
+  // a wait timed out: record it, poison this workgroup's outputs
+  auto fail = [&]() -> bool {
     if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
     return false;
+  };
+  // every phase but QKV and the attentions waits for the previous phase's counter
+  auto wait_prev = [&]() -> bool {
+    if (PH == 0 || ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), sflag)) return true;
+    return fail();
   };
   // LayerNorm geometry: wave w normalises rows 4w .. 4w + 3; lane l holds
   // float4 column groups l + 64 k (k < KG) of them
@@ -483,20 +603,72 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
 
   if constexpr (is_att) {
     DsAttFr f;
-    constexpr bool pre_kv = PH == DP_CAATT;
-    if (pre_kv)
+    constexpr bool cross = PH == DP_CAATT;
+    if (cross)
       ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), wave,
                    (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, f);
-    if (!wait_prev()) return false;
+    // the head's rows are staged after the partials: Q [16][DS_DP], and for
+    // the self-attention K [16][DS_DP] and V^T [DS_DP][16], zero beyond n
+    // rows (written by the poll) and hd columns (written here)
+    char* st = rA + DS_ATT_PART;
+    uint16_t* st16 = reinterpret_cast<uint16_t*>(st);
+    const int hd = a.hd, hq = hd / 4, pad = DS_DP - hd;
+    for (int e = tid; e < 16 * pad; e += DS_THREADS) {
+      const int r = e / pad, c = hd + e % pad;
+      st16[r * DS_DP + c] = 0;
+      if (!cross) {
+        st16[16 * DS_DP + r * DS_DP + c] = 0;
+        st16[2 * 16 * DS_DP + c * 16 + r] = 0;
+      }
+    }
     // ---- one head per unit
     for (int j = 0; j < nu; j++) {
       const int hh = first + j * G;
-      if (PH == DP_SAATT)
-        ds_attention(a.qkv + hh * a.hd, 3 * D, a.qkv + D + hh * a.hd, a.qkv + 2 * D + hh * a.hd, 3 * D,
-                     a.aos + hh * a.hd, D, n, n, a.hd, a.scale_log2, rA, f, false);
+      if (j) __syncthreads();   // the previous head's staged rows and partials have been read
+      bool ok;
+      if constexpr (cross) {
+        constexpr int NCH = (16 * DS_DP / 4 + DS_THREADS - 1) / DS_THREADS;
+        ok = ds_poll<NCH>(
+            make_brsrc(a.q), a.flag,
+            [&](int i) -> int {
+              const int e = tid + i * DS_THREADS;
+              if (e >= 16 * hq) return -1;
+              const int r = e / hq, c = 4 * (e % hq);
+              return r < n ? (r * D + hh * hd + c) / 2 : -2;
+            },
+            [&](int i, uint2 v) {
+              const int e = tid + i * DS_THREADS, r = e / hq, c = 4 * (e % hq);
+              *reinterpret_cast<uint2*>(st + (r * DS_DP + c) * 2) = v;
+            });
+      } else {
+        constexpr int NCH = (3 * 16 * DS_DP / 4 + DS_THREADS - 1) / DS_THREADS;
+        ok = ds_poll<NCH>(
+            make_brsrc(a.qkv), a.flag,
+            [&](int i) -> int {
+              const int e = tid + i * DS_THREADS;
+              if (e >= 3 * 16 * hq) return -1;
+              const int mtx = e / (16 * hq), rem = e % (16 * hq), r = rem / hq, c = 4 * (rem % hq);
+              return r < n ? (r * 3 * D + mtx * D + hh * hd + c) / 2 : -2;
+            },
+            [&](int i, uint2 v) {
+              const int e = tid + i * DS_THREADS;
+              const int mtx = e / (16 * hq), rem = e % (16 * hq), r = rem / hq, c = 4 * (rem % hq);
+              if (mtx < 2) {
+                *reinterpret_cast<uint2*>(st + (mtx * 16 * DS_DP + r * DS_DP + c) * 2) = v;
+              } else {
+                uint16_t* vt = st16 + 2 * 16 * DS_DP;
+                vt[(c + 0) * 16 + r] = (uint16_t)v.x;
+                vt[(c + 1) * 16 + r] = (uint16_t)(v.x >> 16);
+                vt[(c + 2) * 16 + r] = (uint16_t)v.y;
+                vt[(c + 3) * 16 + r] = (uint16_t)(v.y >> 16);
+              }
+            });
+      }
+      if (!ds_all(ok, sflag)) return fail();
+      if constexpr (cross)
+        ds_attention(st, a.ck + hh * hd, a.cv + hh * hd, a.ldc, a.aoc, D, hh * hd, n, a.C, hd, a.scale_log2, rA, f, j == 0);
       else
-        ds_attention(a.q + hh * a.hd, D, a.ck + hh * a.hd, a.cv + hh * a.hd, a.ldc,
-                     a.aoc + hh * a.hd, D, n, a.C, a.hd, a.scale_log2, rA, f, pre_kv && j == 0);
+        ds_self_att(st, a.aos, D, hh * hd, n, hd, a.scale_log2);
     }
   } else {
     const int mi = PH == DP_QKV ? 0 : PH == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
@@ -530,7 +702,28 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       }
     }
     if (!wait_prev()) return false;
-    // ---- the A operand [16][D] (bf16) in region A
+    // ---- the A operand [16][KW] (bf16) in region A
+    if constexpr (!norm) {
+      // SAO, CAO: the attention output; DOWN: the unit's slice of h (a
+      // workgroup's units share their k range). Rows beyond n are zeros.
+      const DsUnit d0 = ds_unit(a, PH, first);
+      const uint16_t* src = PH == DP_DOWN ? a.h : PH == DP_SAO ? a.aos : a.aoc;
+      const int lds = PH == DP_DOWN ? a.mlp : D;
+      const brsrc sr = make_brsrc(src);
+      constexpr int apitch = KW * 2 + 16;
+      constexpr int AS = (16 * KW / 8 + DS_THREADS - 1) / DS_THREADS;   // 16-byte groups per thread
+      uint4 av[AS];
+#pragma unroll
+      for (int i = 0; i < AS; i++) {
+        const int e8 = tid + i * DS_THREADS, r = (e8 * 8) / KW, c = (e8 * 8) % KW;
+        av[i] = bload16(sr, (e8 < 16 * KW / 8 && r < n) ? ((uint32_t)r * lds + d0.k0 + c) * 2u : BUF_OOB);
+      }
+#pragma unroll
+      for (int i = 0; i < AS; i++) {
+        const int e8 = tid + i * DS_THREADS, r = (e8 * 8) / KW, c = (e8 * 8) % KW;
+        if (e8 < 16 * KW / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
+      }
+    }
     if constexpr (norm) {
       // two-pass mean / variance of each of the wave's 4 rows (wave-wide
       // sums), then u = LN(x)(1 + scale) + shift in bf16 into LDS. Rows
@@ -589,32 +782,9 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         }
       }
     }
-    int staged_k0 = -1;
     auto unit = [&](int j) {
       const DsUnit d = ds_unit(a, PH, first + j * G);
       constexpr int apitch = KW * 2 + 16;
-      if (!norm && d.k0 != staged_k0) {
-        // bf16 activations: ao (SAO, CAO) or the unit's slice of h (DOWN)
-        const uint16_t* src = PH == DP_DOWN ? a.h : PH == DP_SAO ? a.aos : a.aoc;
-        const int lds = PH == DP_DOWN ? a.mlp : D;
-        const brsrc sr = make_brsrc(src);
-        constexpr int AS = (16 * KW / 8 + DS_THREADS - 1) / DS_THREADS;   // 16-byte groups per thread
-        uint4 av[AS];
-#pragma unroll
-        for (int i = 0; i < AS; i++) {
-          int e8 = tid + i * DS_THREADS;
-          int r = (e8 * 8) / KW, c = (e8 * 8) % KW;
-          av[i] = bload16(sr, (e8 < 16 * KW / 8 && r < n) ? ((uint32_t)r * lds + d.k0 + c) * 2u : BUF_OOB);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < AS; i++) {
-          int e8 = tid + i * DS_THREADS;
-          int r = (e8 * 8) / KW, c = (e8 * 8) % KW;
-          if (e8 < 16 * KW / 8) *reinterpret_cast<uint4*>(rA + r * apitch + c * 2) = av[i];
-        }
-        staged_k0 = d.k0;
-      }
       __syncthreads();
       // ---- NB 16 x 16 tiles: wave w covers k-steps w, w + 4, ...
       f32x4 acc[NB];
@@ -657,9 +827,19 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         v += a.b[d.wi][col];
         if (PH == DP_QKV || PH == DP_CAQ || PH == DP_UP) {
           if (PH == DP_UP) v = gelu_erf(v);
-          uint16_t* out = PH == DP_QKV ? a.qkv : PH == DP_CAQ ? a.q : a.h;
-          const int ldo = PH == DP_QKV ? 3 * D : PH == DP_CAQ ? D : a.mlp;
-          if (r < n && col < d.N) st_sc1_u16(make_brsrc(out), (uint32_t)(r * ldo + col), f2bf(v));
+          const uint32_t bits = f2bf(v);
+          if constexpr (PH == DP_UP) {
+            if (r < n && col < d.N)
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bits, make_brsrc(a.h), (uint32_t)(r * a.mlp + col) * 2u, 0, CP_SC1);
+          } else {
+            // even columns store the flagged word of their pair (the odd
+            // column is the next lane, same row)
+            uint2* out = PH == DP_QKV ? a.qkv : a.q;
+            const int ldo = PH == DP_QKV ? 3 * D : D;
+            const uint32_t odd = (uint32_t)__shfl_xor((int)bits, 1, WAVE);
+            if (!(cc & 1) && r < n && col < d.N)
+              st_fw(make_brsrc(out), (uint32_t)(r * ldo + col) / 2u, bits | (odd << 16), a.flag);
+          }
         } else {
           // gated residual: x += gate * v
           const int gi = PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8;
@@ -677,6 +857,11 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       if (nu > 1) unit(1);
   }
   // ---- count this phase's finished units once every store has completed
+  // (QKV and CAQ write flagged words and do not count)
+  if constexpr (PH == DP_QKV || PH == DP_CAQ) {
+    __syncthreads();   // region A is free for the next phase
+    return true;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -709,7 +894,10 @@ __global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
   bool have_down = false;
 
   // a failed earlier launch of this run: poison the stream and leave at once
-  if (tid == 0) sflag[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    sflag[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sflag[2] = 0;
+  }
   __syncthreads();
   if (sflag[0]) {
     for (int e = wg * DS_THREADS + tid; e < a.n * D; e += G * DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
