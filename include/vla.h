@@ -303,7 +303,12 @@ const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index);
  * timing one kernel with events). It reads and writes the plan's workspace
  * as in the graph, so intermediate buffers hold arbitrary values afterwards;
  * the next vla_step_run / vla_step_replay recomputes everything from the
- * inputs. Valid only after vla_step_capture. */
+ * inputs. Valid only after vla_step_capture. The DiT layer kernel hands QKV
+ * and the cross query to its attention phases as words tagged with the
+ * launch's position in the sampler run; launched again right after itself,
+ * it can take its previous run's words, which hold the same values (its
+ * inputs are unchanged), without waiting. To time that kernel, launch its
+ * captured launches in graph order, as a replay would. */
 vla_status vla_step_launch_kernel(vla_step_plan* plan, int32_t index, hipStream_t stream);
 
 /* Shape-keyed graphs ([R] CUDA Graph: when the sequence length changes, the
