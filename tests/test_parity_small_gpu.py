@@ -189,6 +189,26 @@ def test_dit_edges(gu, chunk, ctx_len, K):
     assert e <= 1e-2
 
 
+# head dim 64 (the other supported one besides 80) at two widths with a
+# layer kernel: the self-attention's staged rows with 32 zero columns, 8 and
+# 16 heads, a full 16-row chunk
+@pytest.mark.parametrize("hidden,heads,hd,mlp", [(512, 8, 64, 1024), (1024, 16, 64, 2048)])
+def test_dit_head_dims(gu, hidden, heads, hd, mlp):
+    cfg = small_config("dit", "bf16")
+    d = {**cfg.dit.__dict__, "hidden": hidden, "heads": heads, "head_dim": hd, "mlp": mlp, "chunk": 16}
+    cfg = cfg.replace(dit=cfg.dit.__class__(**d), ctx_len=40, steps=2)
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = gu.DeviceWeights(cfg, W)
+    acts, vel = gu.run_dit(cfg, dw, gu.upload_input(I["ctx"]), gu.upload_input(I["noise"]))
+    acts2, _ = gu.run_dit(cfg, dw, gu.upload_input(I["ctx"]), gu.upload_input(I["noise"]))
+    assert np.array_equal(acts, acts2)       # a second run (words cleared, flags from 1 again) is bitwise the same
+    want = run_config(cfg, W, I)
+    e = gu.relerr(acts, want["actions"])
+    ev = gu.relerr(vel, want["velocities"])
+    gu.say(f"dit D {hidden} hd {hd}: actions rel L2 {e:.3e}, velocities {ev:.3e}")
+    assert e <= 1e-2 and ev <= 1e-2
+
+
 def test_vit_small(gu):
     import torch
     cfg = small_config("step", "bf16")
