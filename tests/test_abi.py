@@ -159,3 +159,28 @@ def test_fused_plan_validation():
     finally:
         lib.vla_step_plan_destroy(plan)
     assert lib.vla_step_cycles(None) == 0
+
+
+# vla_quantize_rows validates on the host; none of these cases launches (the
+# addresses are placeholders that are never dereferenced)
+@pytest.mark.parametrize("args,code", [
+    (dict(x=None), lib.VLA_ERR_INVALID_ARG),
+    (dict(codes=None), lib.VLA_ERR_INVALID_ARG),
+    (dict(scales=None), lib.VLA_ERR_INVALID_ARG),
+    (dict(x_dtype=lib.VLA_FP8_E4M3), lib.VLA_ERR_UNSUPPORTED),      # inputs are bf16 or fp32
+    (dict(code_dtype=lib.VLA_BF16), lib.VLA_ERR_UNSUPPORTED),  # codes are E4M3FN or int8
+    (dict(K=12, ldx=16, ldc=16), lib.VLA_ERR_SHAPE),           # K a multiple of 8
+    (dict(K=16392, ldx=16392, ldc=16392), lib.VLA_ERR_SHAPE),  # K at most 16384
+    (dict(ldx=8), lib.VLA_ERR_SHAPE),                          # pitch below K
+    (dict(ldc=20), lib.VLA_ERR_SHAPE),                         # pitch not a multiple of 8
+    (dict(rows=-1), lib.VLA_ERR_SHAPE),
+    (dict(rows=0), lib.VLA_OK),                                # nothing to do: no launch
+])
+def test_quantize_rows_validation(args, code):
+    a = dict(x=0x10000, x_dtype=lib.VLA_BF16, code_dtype=lib.VLA_FP8_E4M3, rows=4, K=16, ldx=16, codes=0x20000, ldc=16,
+             scales=0x30000)
+    a.update(args)
+    assert lib.vla_quantize_rows(**a) == code
+    a["code_dtype"] = lib.VLA_INT8
+    if "code_dtype" not in args:
+        assert lib.vla_quantize_rows(**a) == code
