@@ -29,20 +29,25 @@ def patchify(img: np.ndarray, patch: int) -> np.ndarray:
     return out
 
 
+def vit_layer(z: np.ndarray, W, p: str, v) -> np.ndarray:
+    """One pre-norm encoder block on the patch rows z [S, D]: z + MHA(LN1(z)),
+    then + MLP(LN2(.)), with biased projections and no mask."""
+    S = z.shape[0]
+    u = ops.layernorm(z, W[p + "ln1_g"], W[p + "ln1_b"], v.eps)
+    q = ops.linear(u, W[p + "wq"], W[p + "bq"]).reshape(S, v.heads, v.head_dim)
+    k = ops.linear(u, W[p + "wk"], W[p + "bk"]).reshape(S, v.heads, v.head_dim)
+    vv = ops.linear(u, W[p + "wv"], W[p + "bv"]).reshape(S, v.heads, v.head_dim)
+    o = ops.attention(q, k, vv, causal=False).reshape(S, v.heads * v.head_dim)
+    z = z + ops.linear(o, W[p + "wo"], W[p + "bo"])
+    u = ops.layernorm(z, W[p + "ln2_g"], W[p + "ln2_b"], v.eps)
+    return z + ops.linear(ops.gelu(ops.linear(u, W[p + "w1"], W[p + "b1"])), W[p + "w2"], W[p + "b2"])
+
+
 def vit(img: np.ndarray, W, v) -> np.ndarray:
     z = ops.linear(patchify(np.asarray(img, dtype=np.float64), v.patch), W["vit.pe_w"], W["vit.pe_b"])
     z = z + W["vit.pos"]
-    S = z.shape[0]
     for l in range(v.layers):
-        p = f"vit.{l}."
-        u = ops.layernorm(z, W[p + "ln1_g"], W[p + "ln1_b"], v.eps)
-        q = ops.linear(u, W[p + "wq"], W[p + "bq"]).reshape(S, v.heads, v.head_dim)
-        k = ops.linear(u, W[p + "wk"], W[p + "bk"]).reshape(S, v.heads, v.head_dim)
-        vv = ops.linear(u, W[p + "wv"], W[p + "bv"]).reshape(S, v.heads, v.head_dim)
-        o = ops.attention(q, k, vv, causal=False).reshape(S, v.heads * v.head_dim)
-        z = z + ops.linear(o, W[p + "wo"], W[p + "bo"])
-        u = ops.layernorm(z, W[p + "ln2_g"], W[p + "ln2_b"], v.eps)
-        z = z + ops.linear(ops.gelu(ops.linear(u, W[p + "w1"], W[p + "b1"])), W[p + "w2"], W[p + "b2"])
+        z = vit_layer(z, W, f"vit.{l}.", v)
     return z
 
 
