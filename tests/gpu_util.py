@@ -11,6 +11,7 @@ import numpy as np
 import torch
 
 from oracle.io import Weights
+from tests.parity import relerr  # noqa: F401  (global and per-row bars)
 from synth import make_inputs, make_weights
 from vla_robot_policy_amd import lib
 from vla_robot_policy_amd.device import DeviceWeights, bf16_bits_to_float, upload_input, workspace
@@ -24,12 +25,6 @@ def say(*a):
     sys.stdout.flush()
 
 
-def relerr(got, want) -> float:
-    got = np.asarray(got, dtype=np.float64)
-    want = np.asarray(want, dtype=np.float64)
-    assert got.shape == want.shape, (got.shape, want.shape)
-    assert np.all(np.isfinite(got)), "non-finite values in GPU output"
-    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
 
 
 def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
@@ -66,7 +61,17 @@ def run_backbone(cfg, dw: DeviceWeights, e_in: torch.Tensor, seq: int) -> np.nda
     return to_host(out, act_dtype(cfg))
 
 
-def run_dit(cfg, dw: DeviceWeights, ctx: torch.Tensor, noise: torch.Tensor, ctx_len=None, K=None):
+def dit_workspace(cfg, dw: DeviceWeights, ctx_len=None, K=None):
+    dit = dw.dit if dw.dit is not None else dw.build_dit()
+    d = cfg.dit
+    need = lib.vla_dit_workspace_bytes(dit, cfg.ctx_len if ctx_len is None else ctx_len, d.chunk, d.action_dim,
+                                       cfg.steps if K is None else K)
+    return workspace(need), need
+
+
+def run_dit(cfg, dw: DeviceWeights, ctx: torch.Tensor, noise: torch.Tensor, ctx_len=None, K=None, ws=None):
+    """The Euler sampler through vla_flow_euler_sample; `ws` = (buffer, bytes)
+    to run on a given workspace (default: a fresh one)."""
     d = cfg.dit
     dit = dw.dit if dw.dit is not None else dw.build_dit()
     ctx_len = cfg.ctx_len if ctx_len is None else ctx_len
@@ -74,9 +79,10 @@ def run_dit(cfg, dw: DeviceWeights, ctx: torch.Tensor, noise: torch.Tensor, ctx_
     n, A = noise.shape
     acts = torch.empty((n, A), dtype=torch.float32, device=DEV)
     vel = torch.empty((K, n, A), dtype=torch.float32, device=DEV)
-    need = lib.vla_dit_workspace_bytes(dit, ctx_len, n, A, K)
-    ws = workspace(need)
-    lib.check(lib.vla_flow_euler_sample(dit, ctx, ctx_len, noise, n, A, K, acts, vel, ws, need))
+    if ws is None:
+        need = lib.vla_dit_workspace_bytes(dit, ctx_len, n, A, K)
+        ws = (workspace(need), need)
+    lib.check(lib.vla_flow_euler_sample(dit, ctx, ctx_len, noise, n, A, K, acts, vel, ws[0], ws[1]))
     torch.cuda.synchronize()
     return acts.cpu().numpy().astype(np.float64), vel.cpu().numpy().astype(np.float64)
 

@@ -86,8 +86,7 @@ def test_step_shape_cache(gu):
             want = _oracle(cfg, Wo, I, sh)
             for k in ("hidden", "actions", "velocities"):
                 assert got[k].shape == want[k].shape, (name, k)
-                e = gu.relerr(got[k], want[k])
-                gu.say(f"shape {name}: {k} rel L2 {e:.3e}")
+                e = gu.relerr(got[k], want[k], tol, f"shape {name} {k}")
                 assert e <= tol, (name, k, e)
             first[name] = got
         assert stats() == (3, 0, 3, 0)
