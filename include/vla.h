@@ -54,7 +54,8 @@ typedef enum {
   VLA_ERR_UNSUPPORTED = -3, /* valid but not implemented combination      */
   VLA_ERR_WORKSPACE = -4,   /* ws_bytes below the required size           */
   VLA_ERR_HIP = -5,         /* HIP runtime error                          */
-  VLA_ERR_STATE = -6        /* plan used out of order / already captured  */
+  VLA_ERR_STATE = -6,       /* plan used out of order / already captured  */
+  VLA_ERR_TIMEOUT = -7      /* a device-side bounded wait gave up (see vla_workspace_status) */
 } vla_status;
 
 /* VLA_INT8 ([A]: INT8 where FP8 units are missing): int8 weight codes in
@@ -366,6 +367,30 @@ vla_status vla_step_plan_create_fused(const vla_model* model, const vla_step_sha
 int64_t vla_step_cycles(const vla_step_plan* plan);
 
 void vla_step_plan_destroy(vla_step_plan* plan);
+
+/* ------------------------------------------------------------------ status
+ * Device-side failures. For chunks of at most 16 rows the action expert runs
+ * one persistent kernel per DiT layer whose workgroups hand results to each
+ * other through device counters and tagged words. Every such wait is bounded
+ * (2^17 polls, far beyond a healthy wait of microseconds); when one gives up,
+ * the kernel sets word 0 of the workspace's status block (the workspace's
+ * first 256 bytes, cleared at the start of every sampler pass), fills the
+ * layer's output rows with NaN and leaves, and every later layer launch of
+ * the pass sees the word and leaves at once with NaN outputs. The failure is
+ * therefore never a hang; it shows as NaN actions and velocities and as this
+ * status. Every host call of the pass still returns VLA_OK (the calls are
+ * asynchronous), so a caller that must know asks here after the pass.
+ *
+ * vla_workspace_status: synchronises `stream`, then reads word 0 of the
+ * workspace `ws` of the last pass (vla_flow_euler_sample, or a step plan's
+ * workspace): VLA_OK, or VLA_ERR_TIMEOUT when a wait gave up in that pass.
+ * vla_step_status: the same for a plan's workspace; after VLA_ERR_TIMEOUT
+ * the plan's next replay first clears its counters with a fill kernel.
+ * The environment variable VLA_DIT_SPIN_LIMIT (a positive poll count below
+ * 2^17) lowers the bound for later passes, so that the time-out path can be
+ * exercised: with a limit of 1 a wait gives up after one unsuccessful poll. */
+vla_status vla_workspace_status(const void* ws, hipStream_t stream);
+vla_status vla_step_status(vla_step_plan* plan, hipStream_t stream);
 
 /* ------------------------------------------------------------------ misc */
 const char* vla_last_error(void);

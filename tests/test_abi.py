@@ -184,3 +184,17 @@ def test_quantize_rows_validation(args, code):
     a["code_dtype"] = lib.VLA_INT8
     if "code_dtype" not in args:
         assert lib.vla_quantize_rows(**a) == code
+
+
+def test_status_calls_reject_null():
+    # (no GPU call: both fail validation first)
+    assert lib.vla_workspace_status(None) == lib.VLA_ERR_INVALID_ARG
+    assert lib.vla_step_status(None) == lib.VLA_ERR_INVALID_ARG
+    assert "null" in lib.vla_last_error()
+
+
+def test_workspaces_reserve_the_status_block():
+    # every workspace starts with the 256-byte status block: a block's
+    # workspace is at least that plus its buffers
+    assert lib.vla_block_workspace_bytes(llm_cfg(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                                 intermediate=688), 1) > 256

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <set>
@@ -73,11 +74,17 @@ struct ArgRef {
 template <typename T>
 ArgRef arg(const T& v) { return ArgRef{&v, sizeof(T)}; }
 
+// The first STATUS_BYTES of every workspace hold its status words (word 0:
+// set by the DiT layer kernel when one of its bounded waits gives up); the
+// buffers of a schedule start after them.
+constexpr size_t STATUS_BYTES = 256;
+
 struct Ctx {
   bool plan;               // plan mode: size buffers, launch nothing
   char* base;              // workspace base (launch mode)
   size_t cap;
-  size_t off = 0;
+  size_t off = STATUS_BYTES;
+  int* status = nullptr;   // the workspace's status words (launch mode)
   hipStream_t st = nullptr;
   // shared GEMM scratch (requirements gathered in plan mode): split-K
   // partial tiles and their counters
@@ -589,9 +596,10 @@ vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out,
   if (ws_bytes < need) return fail(VLA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
   Ctx c;
   c.plan = false; c.base = (char*)ws; c.cap = ws_bytes; c.st = st;
+  c.status = (int*)ws;
   c.off = fixed;
   c.take_scratch(p0);
-  c.off = 0;   // fixed buffers are taken again by the schedule from offset 0
+  c.off = STATUS_BYTES;   // fixed buffers are taken again by the schedule after the status words
   VLA_TRY(zero_counters(c));
   return sched(c);
 }
@@ -673,7 +681,18 @@ struct DitState {
   uint16_t* u = nullptr;   // modulated LayerNorm rows of the launch-per-operation path (bf16)
   bool stack = false;
   int G = 0;
+  unsigned spin = DS_SPIN;   // poll limit of the layer kernel's bounded waits
 };
+
+// Poll limit of the layer kernel's bounded waits: DS_SPIN, or fewer when the
+// environment variable VLA_DIT_SPIN_LIMIT asks for it (a test of the
+// time-out path makes every wait give up almost at once; nothing hangs).
+unsigned dit_spin_limit() {
+  const char* e = getenv("VLA_DIT_SPIN_LIMIT");
+  if (!e || !*e) return DS_SPIN;
+  const long v = strtol(e, nullptr, 10);
+  return v >= 1 && v < (long)DS_SPIN ? (unsigned)v : DS_SPIN;
+}
 
 // Buffers of the sampler; clears the layer kernel's counters.
 vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
@@ -692,6 +711,7 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.x2 = c.take<float>((size_t)n * D);
   s.G = cu_count();
   s.stack = dit_stack_ok(cf, n, s.G);
+  s.spin = dit_spin_limit();
   if (s.stack) {
     const size_t wq = (size_t)n * 3 * D / 2, wd = (size_t)n * D / 2;
     s.fw_words = wq + wd;
@@ -704,7 +724,7 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   }
   s.ao = c.take<uint16_t>((size_t)n * D);
   s.h = c.take<uint16_t>((size_t)n * cf.mlp);
-  s.derr = c.take<int>(64);
+  s.derr = c.status;      // word 0 of the workspace's status block
   s.u = !s.stack && cf.wdtype != VLA_F32 ? c.take<uint16_t>((size_t)n * D) : nullptr;
   if (s.stack) {
     // phase and tile counters of the layer kernel live in the shared counter
@@ -832,7 +852,7 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = scaled8(wt) ? ss[i] : nullptr; a.b[i] = bs[i]; }
         const bool last_launch = k == K - 1 && l == L - 1;
         a.wq_next = last_launch ? nullptr : d.layers[(l + 1) % L].w_qkv;
-        a.part = c.part; a.cnt = c.cnt_tile; a.err = s.derr;
+        a.part = c.part; a.cnt = c.cnt_tile; a.err = s.derr; a.spin = s.spin;
         VLA_TRY(launch(c, lk.fn, dim3(s.G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
         continue;
       }
@@ -1089,6 +1109,17 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
 extern "C" {
 
 const char* vla_last_error(void) { return g_err.c_str(); }
+
+vla_status vla_workspace_status(const void* ws, hipStream_t stream) {
+  if (!ws) return fail(VLA_ERR_INVALID_ARG, "null workspace");
+  VLA_HIP(hipStreamSynchronize(stream));
+  int word = 0;
+  VLA_HIP(hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost));
+  if (word != 0)
+    return fail(VLA_ERR_TIMEOUT, "a bounded wait of the DiT layer kernel gave up in the last pass on this workspace; "
+                                 "its actions and velocities hold NaN");
+  return VLA_OK;
+}
 int32_t vla_abi_version(void) { return VLA_ABI_VERSION; }
 
 static vla_status block_sched(Ctx& c, const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
@@ -1302,12 +1333,25 @@ vla_status vlm_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh, u
   return VLA_OK;
 }
 
+// The sampler's buffers and clearing fills come first: a layer kernel that
+// timed out in the previous pass may have left phase counters set in the
+// counter array the VLM's split-K GEMMs share, and the fills reset them
+// before any GEMM of this pass runs.
 vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) {
+  const int grid = P.has_vit ? P.vit.cfg.image / P.vit.cfg.patch : 0;
+  const int n_vis = P.has_vit && sh.n_images > 0 ? sh.n_images * grid * grid / (P.vit.cfg.merge * P.vit.cfg.merge) : 0;
+  DitIO io{nullptr, n_vis + sh.n_text, P.io.noise, sh.chunk, sh.action_dim, sh.steps, P.io.actions, P.io.velocities};
+  DitState ds;
+  VLA_TRY(dit_begin(c, P.dit, io, ds));
   uint16_t* ctx = nullptr;
   int S = 0;
   VLA_TRY(vlm_sched(c, P, sh, ctx, S));
-  DitIO io{ctx, S, P.io.noise, sh.chunk, sh.action_dim, sh.steps, P.io.actions, P.io.velocities};
-  return sched_dit(c, P.dit, io);
+  io.ctx = ctx;
+  uint16_t* ckv = c.take<uint16_t>((size_t)io.ctx_len * P.dit.cfg.layers * 2 * P.dit.cfg.hidden);
+  VLA_TRY(dit_conditioning(c, P.dit, io, ds));
+  VLA_TRY(dit_cross_kv(c, P.dit, io.ctx, io.ctx_len, ckv));
+  VLA_TRY(dit_in_proj(c, P.dit, io, ds));
+  return dit_steps(c, P.dit, io, ds, ckv, 0, io.K);
 }
 
 // One V-AEFusion cycle on two contexts. `cv` (the caller's stream) runs the
@@ -1391,11 +1435,14 @@ vla_status fused_layout(const vla_step_plan& P, FusedLayout& L) {
   return VLA_OK;
 }
 
+// Both branches report into the workspace's status words (only the action
+// branch runs the DiT layer kernel).
 void fused_ctxs(const vla_step_plan& P, const FusedLayout& L, hipStream_t sv, hipStream_t sa, Ctx& cv, Ctx& ca) {
   cv.plan = false; cv.base = (char*)P.ws; cv.cap = P.ws_bytes; cv.st = sv;
-  cv.off = L.scr_a; cv.take_scratch(L.a0); cv.off = 0;
+  cv.status = ca.status = (int*)P.ws;
+  cv.off = L.scr_a; cv.take_scratch(L.a0); cv.off = STATUS_BYTES;
   ca.plan = false; ca.base = (char*)P.ws + L.off_b; ca.cap = P.ws_bytes - L.off_b; ca.st = sa;
-  ca.off = L.scr_b; ca.take_scratch(L.b0); ca.off = 0;
+  ca.off = L.scr_b; ca.take_scratch(L.b0); ca.off = STATUS_BYTES;
 }
 
 vla_status check_step(const vla_model* m, const vla_step_shape* s) {
@@ -1573,9 +1620,10 @@ vla_status capture_pass(const vla_step_plan& P, const vla_step_shape& sh, std::v
       size_t fixed = p0.off;
       Ctx c;
       c.plan = false; c.base = (char*)P.ws; c.cap = P.ws_bytes; c.st = cs;
+      c.status = (int*)P.ws;
       c.off = fixed;
       c.take_scratch(p0);
-      c.off = 0;
+      c.off = STATUS_BYTES;
       if (recs) recs->clear();
       c.recs = recs;
       s = step_sched(c, P, sh);
@@ -1793,6 +1841,14 @@ vla_status vla_step_cache_info(const vla_step_plan* plan, vla_step_cache_stats* 
 int32_t vla_step_graph_nodes(const vla_step_plan* plan) { return plan && captured(plan) ? plan->nodes : 0; }
 
 int64_t vla_step_cycles(const vla_step_plan* plan) { return plan ? plan->cycles : 0; }
+
+vla_status vla_step_status(vla_step_plan* plan, hipStream_t stream) {
+  if (!plan) return fail(VLA_ERR_INVALID_ARG, "null plan");
+  const vla_status s = vla_workspace_status(plan->ws, stream);
+  // a timed-out layer kernel leaves its counters set: clear them before the next graph
+  if (s == VLA_ERR_TIMEOUT) plan->zeroed_valid = false;
+  return s;
+}
 
 const char* vla_step_kernel_label(const vla_step_plan* plan, int32_t index) {
   if (!plan || index < 0 || index >= (int32_t)plan->recs.size()) return nullptr;

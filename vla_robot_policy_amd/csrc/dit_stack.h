@@ -92,6 +92,7 @@ struct DitLayerArgs {
   float* part;                    // DOWN slice partials [slices][D/16][256]
   unsigned* cnt;                  // ds_counter_words(D) counters (zero between launches)
   int* err;                       // set to 1 when a wait times out
+  unsigned spin;                  // polls before a wait gives up (DS_SPIN unless the host asks for fewer)
   unsigned flag;                  // this launch's word flag: nonzero, and above every flag written since the words were cleared
 };
 
@@ -116,7 +117,7 @@ __device__ __forceinline__ void st_fw(brsrc r, uint32_t word, uint32_t data, uin
 // phases' few workgroups, with a head's rows each (a few KB). False after
 // DS_SPIN rounds.
 template <int NCH, typename WordF, typename PutF>
-__device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, WordF word, PutF put) {
+__device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, unsigned spin, WordF word, PutF put) {
   static_assert(NCH <= 64, "one pending bit per chunk");
   uint4 v[NCH];
   uint64_t pend = 0;
@@ -135,7 +136,7 @@ __device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, WordF word, PutF
         pend &= ~(1ull << i);
       }
     if (!pend) return true;
-    if (spins >= DS_SPIN) return false;
+    if (spins >= spin) return false;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int i = 0; i < NCH; i++)
@@ -163,7 +164,7 @@ __device__ __forceinline__ int ds_base(const DitLayerArgs& a, int ph) {
 
 // Wait until the DS_NC slots of a phase counter sum to target (wave 0
 // polls, one slot per lane; the workgroup follows). False after DS_SPIN polls.
-__device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, int* sflag) {
+__device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, unsigned spin, int* sflag) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     unsigned spins = 0;
@@ -174,7 +175,7 @@ __device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, 
       // exact: counts stay far below 2^24
       const unsigned tot = (unsigned)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum((float)v)), 0));
       if (tot >= target) break;                    // uniform: read from lane 0
-      if (++spins >= DS_SPIN) { ok = false; break; }
+      if (++spins >= spin) { ok = false; break; }
       __builtin_amdgcn_s_sleep(2);
     }
     if (lane == 0) sflag[0] = ok;
@@ -594,7 +595,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
   };
   // every phase but QKV and the attentions waits for the previous phase's counter
   auto wait_prev = [&]() -> bool {
-    if (PH == 0 || ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), sflag)) return true;
+    if (PH == 0 || ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), a.spin, sflag)) return true;
     return fail();
   };
   // LayerNorm geometry: wave w normalises rows 4w .. 4w + 3; lane l holds
@@ -629,7 +630,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       if constexpr (cross) {
         constexpr int NCH = (16 * DS_DP / 4 + DS_THREADS - 1) / DS_THREADS;
         ok = ds_poll<NCH>(
-            make_brsrc(a.q), a.flag,
+            make_brsrc(a.q), a.flag, a.spin,
             [&](int i) -> int {
               const int e = tid + i * DS_THREADS;
               if (e >= 16 * hq) return -1;
@@ -643,7 +644,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       } else {
         constexpr int NCH = (3 * 16 * DS_DP / 4 + DS_THREADS - 1) / DS_THREADS;
         ok = ds_poll<NCH>(
-            make_brsrc(a.qkv), a.flag,
+            make_brsrc(a.qkv), a.flag, a.spin,
             [&](int i) -> int {
               const int e = tid + i * DS_THREADS;
               if (e >= 3 * 16 * hq) return -1;

@@ -13,11 +13,14 @@ import re
 from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvla.so")
+# VLA_LIB_PATH selects another build of the same library (the host-side
+# AddressSanitizer build of build_asan.py); the default is the in-tree one
+LIB_PATH = os.environ.get("VLA_LIB_PATH") or os.path.join(HERE, "libvla.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "vla.h")
 
 VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_SHAPE, VLA_ERR_UNSUPPORTED, VLA_ERR_WORKSPACE, VLA_ERR_HIP, VLA_ERR_STATE = (
     0, -1, -2, -3, -4, -5, -6)
+VLA_ERR_TIMEOUT = -7
 VLA_F32, VLA_BF16, VLA_FP8_E4M3, VLA_INT8 = 0, 1, 2, 3
 DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3, "int8": VLA_INT8}
 VLA_BLOCK_QK_NORM = 1
@@ -136,6 +139,8 @@ def load() -> C.CDLL:
         "vla_step_cycles": (C.c_int64, [c_void_p]),
         "vla_step_cache_info": (S, [c_void_p, POINTER(StepCacheStats)]),
         "vla_step_plan_destroy": (None, [c_void_p]),
+        "vla_workspace_status": (S, [c_void_p, c_void_p]),
+        "vla_step_status": (S, [c_void_p, c_void_p]),
         "vla_last_error": (C.c_char_p, []),
         "vla_abi_version": (c_int32, []),
     }
@@ -274,6 +279,14 @@ def vla_step_cache_info(plan):
     out = StepCacheStats()
     st = load().vla_step_cache_info(plan, C.byref(out))
     return st, out
+
+
+def vla_workspace_status(ws, stream: int = 0) -> int:
+    return load().vla_workspace_status(_p(ws), stream)
+
+
+def vla_step_status(plan, stream: int = 0) -> int:
+    return load().vla_step_status(plan, stream)
 
 
 def vla_step_plan_destroy(plan) -> None:
