@@ -256,15 +256,24 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
     log(f"captured {nodes} kernel nodes")
     labels = [lib.vla_step_kernel_label(plan, i) for i in range(nodes)]
     if only_label is not None:
-        # the kernels of one label alone, relaunched in graph order: the run a
-        # hardware-counter pass profiles
-        idx = [i for i, lb in enumerate(labels) if lb == only_label]
-        for _ in range(kernel_reps):
-            for i in idx:
-                lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+        # the kernels of the named labels alone, each label's launches
+        # relaunched in graph order, label after label: the run a
+        # hardware-counter pass profiles. The launch sequence goes to stderr
+        # as one JSON line, so the profiler's dispatches (the last ones of the
+        # process) can be attributed to labels.
+        names = sorted(set(labels)) if only_label == "all" else only_label.split(",")
+        seq = []
         torch.cuda.synchronize()
+        for lb in names:
+            idx = [i for i, x in enumerate(labels) if x == lb]
+            for _ in range(kernel_reps):
+                for i in idx:
+                    lib.check(lib.vla_step_launch_kernel(plan, i, stream))
+            torch.cuda.synchronize()
+            seq.append({"label": lb, "launches": len(idx) * kernel_reps, "per_step": len(idx)})
         lib.vla_step_plan_destroy(plan)
-        log(f"launched the {len(idx)} kernels labelled {only_label} x {kernel_reps}")
+        print("[bench] launch sequence " + json.dumps(seq), file=sys.stderr, flush=True)
+        log(f"launched {sum(s['launches'] for s in seq)} kernels of {len(seq)} labels")
         return None
     for _ in range(warmup):
         lib.check(lib.vla_step_replay(plan, stream))
@@ -310,10 +319,10 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
             "nodes": nodes, "kernels": kern}
 
 
-def cpu_baseline(cfg, reps: int = 2):
+def cpu_baseline(cfg, reps: int = 3):
     """Oracle (float64 NumPy, as it stands) on a bounded sample of the step:
     `reps` layers of each repeated block type at the workload's shapes, the
-    mean per layer scaled by the number of such layers in one step."""
+    median per layer scaled by the number of such layers in one step."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from synth import make_weights
@@ -325,34 +334,23 @@ def cpu_baseline(cfg, reps: int = 2):
     parts = {}
 
     def clock(key, n_per_step, fn):
-        fn(0)                                    # converts this layer's weights once
-        t = time.time()
+        ts = []
         for l in range(reps):
+            t = time.time()
             fn(l)
-        parts[key] = ((time.time() - t) / reps, n_per_step)
+            ts.append(time.time() - t)
+        parts[key] = (float(np.median(ts)), n_per_step)
 
     x = rng.standard_normal((cfg.seq, cfg.block.hidden))
-    for l in range(reps):
+    for l in range(reps):          # converts each sampled layer's weights once, untimed
         ollm.block(x[:4], W, f"llm.{l}.", cfg.block)
     clock("llm_layer", cfg.layers, lambda l: ollm.block(x, W, f"llm.{l}.", cfg.block))
     if cfg.vit is not None:
         v = cfg.vit
         z = rng.standard_normal((v.n_patches, v.hidden))
-
-        def vit_layer(l):
-            p = f"vit.{l}."
-            u = z
-            from oracle import ops
-            a = ops.layernorm(u, W[p + "ln1_g"], W[p + "ln1_b"], v.eps)
-            q = ops.linear(a, W[p + "wq"], W[p + "bq"]).reshape(-1, v.heads, v.head_dim)
-            k = ops.linear(a, W[p + "wk"], W[p + "bk"]).reshape(-1, v.heads, v.head_dim)
-            vv = ops.linear(a, W[p + "wv"], W[p + "bv"]).reshape(-1, v.heads, v.head_dim)
-            u = u + ops.linear(ops.attention(q, k, vv, False).reshape(len(u), -1), W[p + "wo"], W[p + "bo"])
-            a = ops.layernorm(u, W[p + "ln2_g"], W[p + "ln2_b"], v.eps)
-            return u + ops.linear(ops.gelu(ops.linear(a, W[p + "w1"], W[p + "b1"])), W[p + "w2"], W[p + "b2"])
         for l in range(reps):
-            vit_layer(l)
-        clock("vit_layer", v.layers * cfg.n_images, vit_layer)
+            ovit.vit_layer(z[:4], W, f"vit.{l}.", v)
+        clock("vit_layer", v.layers * cfg.n_images, lambda l: ovit.vit_layer(z, W, f"vit.{l}.", v))
     d = cfg.dit
     xa = rng.standard_normal((d.chunk, d.hidden))
     sc = rng.standard_normal(d.hidden)
@@ -361,9 +359,11 @@ def cpu_baseline(cfg, reps: int = 2):
         odit.dit_layer(xa, sc, ctx, W, f"dit.{l}.", d)
     clock("dit_layer_step", d.layers * cfg.steps, lambda l: odit.dit_layer(xa, sc, ctx, W, f"dit.{l}.", d))
     est = sum(s * n for s, n in parts.values())
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(est * 1e3, 1), "unit": "ms per step (extrapolated)", "cores": int(threads), "kind": "oracle",
-            "sample": (f"float64 oracle, mean over {reps} layers of each repeated block at the workload's shapes: "
+    blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(est * 1e3, 1), "unit": "ms per step (extrapolated)", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": int(blas), "kind": "oracle",
+            "sample": (f"float64 oracle (oracle.llm.block, oracle.vit.vit_layer, oracle.dit.dit_layer), median over "
+                       f"{reps} layers of each repeated block at the workload's shapes: "
                        + ", ".join(f"{k} {s * 1e3:.1f} ms x {n}" for k, (s, n) in parts.items())
                        + "; once-per-step parts (patch embed, merger, projector, time MLP, heads) omitted")}
 
