@@ -120,6 +120,24 @@ vla_status vla_block_forward(const vla_block_cfg* cfg, const vla_block_weights* 
                              int32_t seq, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t vla_block_workspace_bytes(const vla_block_cfg* cfg, int32_t seq);
 
+/* vla_block_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same operation, arguments (minus ws,
+ * ws_bytes), layouts and results as vla_block_forward; the scratch is a
+ * static device array of VLA_STATIC_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per GPU, held from the library's load until the process
+ * ends. The call allocates nothing (no hipMalloc / hipFree, no other
+ * allocating routine). Every call on a GPU shares that GPU's array and
+ * leaves its contents behind; each pass first zeroes the counters it needs
+ * with a fill kernel, so nothing has to be cleared by the caller, but calls
+ * that overlap on one GPU (other streams, other host threads) race on the
+ * array: order them on one stream. Errors as vla_block_forward, and
+ * VLA_ERR_WORKSPACE when vla_block_workspace_bytes(cfg, seq) exceeds the
+ * array (about seq 560 for the 2560-wide bf16 block). */
+#define VLA_STATIC_SCRATCH_BYTES (64u << 20)
+vla_status vla_block_forward_static(const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
+                                    int32_t seq, hipStream_t stream);
+
 /* ------------------------------------------------------------------ backbone
  * The decoder prefill ([R] 整体方案; CUDA Graph: "36 layers to the final
  * RMSNorm"): n_layers blocks over the embeddings, then RMSNorm(final_norm)

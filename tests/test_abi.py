@@ -198,3 +198,16 @@ def test_workspaces_reserve_the_status_block():
     # workspace is at least that plus its buffers
     assert lib.vla_block_workspace_bytes(llm_cfg(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
                                                  intermediate=688), 1) > 256
+
+
+def test_static_block_rejects_shapes_beyond_its_scratch():
+    # the 2560-wide bf16 block at seq 1024 needs ~79 MiB, above the 64 MiB
+    # static array: refused before anything is launched or resolved
+    assert lib.vla_block_workspace_bytes(llm_cfg(), 1024) > lib.VLA_STATIC_SCRATCH_BYTES
+    w = lib.BlockWeights()
+    for f in w._fields_:
+        if f[0] not in ("q_norm", "k_norm") and not f[0].startswith("s_"):
+            setattr(w, f[0], 256)
+    st = lib.vla_block_forward_static(llm_cfg(), w, 256, 512, 1024)
+    assert st == lib.VLA_ERR_WORKSPACE, lib.vla_last_error()
+    assert "static" in lib.vla_last_error()

@@ -1151,6 +1151,59 @@ size_t vla_block_workspace_bytes(const vla_block_cfg* cfg, int32_t seq) {
   return need;
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free block
+// Scratch of vla_block_forward_static: a file-scope device array, one copy
+// per GPU (each GPU the library runs on holds it until the process ends).
+// On the host the array's name is only a stand-in for the symbol; its
+// device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device and kept here, and only that address is ever handed to
+// kernels.
+static __device__ __align__(256) char scratch[VLA_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // by device ordinal
+
+vla_status scratch_ptr(void** out) {
+  int dev = 0;
+  VLA_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    VLA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255) != 0)
+      return fail(VLA_ERR_HIP, "static scratch: unusable device address %p", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+vla_status vla_block_forward_static(const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
+                                    int32_t seq, hipStream_t stream) {
+  VLA_TRY(check_block_cfg(cfg));
+  VLA_TRY(check_block_weights(cfg, w));
+  if (!x_in || !x_out) return fail(VLA_ERR_INVALID_ARG, "null input/output");
+  if (seq < 1 || seq > 4096) return fail(VLA_ERR_SHAPE, "seq %d outside [1, 4096]", seq);
+  auto sched = [&](Ctx& c) { return block_sched(c, cfg, w, x_in, x_out, seq); };
+  size_t need = 0;
+  VLA_TRY(two_pass(nullptr, 0, nullptr, &need, sched));
+  if (need > (size_t)VLA_STATIC_SCRATCH_BYTES)
+    return fail(VLA_ERR_WORKSPACE, "block at seq %d needs %zu bytes of scratch, above the static array's %zu", seq, need,
+                (size_t)VLA_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  VLA_TRY(scratch_ptr(&ws));
+  // the pass starts with a fill kernel that zeroes its split-K counters;
+  // every other buffer of the block is written before it is read
+  return two_pass(ws, (size_t)VLA_STATIC_SCRATCH_BYTES, stream, nullptr, sched);
+}
+
 static vla_status check_backbone(const vla_backbone* bb) {
   if (!bb) return fail(VLA_ERR_INVALID_ARG, "null backbone");
   VLA_TRY(check_block_cfg(&bb->cfg));

@@ -115,6 +115,7 @@ def load() -> C.CDLL:
     sig = {
         "vla_block_forward": (S, [POINTER(BlockCfg), POINTER(BlockWeights), c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
         "vla_block_workspace_bytes": (c_size_t, [POINTER(BlockCfg), c_int32]),
+        "vla_block_forward_static": (S, [POINTER(BlockCfg), POINTER(BlockWeights), c_void_p, c_void_p, c_int32, c_void_p]),
         "vla_backbone_prefill": (S, [POINTER(Backbone), c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
         "vla_backbone_workspace_bytes": (c_size_t, [POINTER(Backbone), c_int32]),
         "vla_flow_euler_sample": (S, [POINTER(Dit), c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
@@ -188,6 +189,13 @@ def vla_block_workspace_bytes(cfg: BlockCfg, seq: int) -> int:
 
 def vla_block_forward(cfg: BlockCfg, w: BlockWeights, x_in, x_out, seq: int, ws, ws_bytes: int, stream: int = 0) -> int:
     return load().vla_block_forward(C.byref(cfg), C.byref(w), _p(x_in), _p(x_out), seq, _p(ws), ws_bytes, stream)
+
+
+VLA_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def vla_block_forward_static(cfg: BlockCfg, w: BlockWeights, x_in, x_out, seq: int, stream: int = 0) -> int:
+    return load().vla_block_forward_static(C.byref(cfg), C.byref(w), _p(x_in), _p(x_out), seq, stream)
 
 
 def vla_backbone_workspace_bytes(bb: Backbone, seq: int) -> int:
