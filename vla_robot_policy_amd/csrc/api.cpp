@@ -243,7 +243,7 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   // buffer-load offsets are 32-bit: operands up to 2 GiB
   const double wrows = op.em == E_SWIGLU ? (double)a.n_half + a.N : (double)a.N;
   if (wrows * a.ldw * wbytes >= (double)BUF_LIMIT) return fail(VLA_ERR_SHAPE, "gemm: weight matrix beyond 2 GiB");
-  if (op.am != A_TIME && op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
+  if (op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
   if ((op.em == E_RESID ? (double)a.M * a.ldx * 4.0 : (double)a.M * a.ldc * (a.c_f32 ? 4.0 : 2.0)) >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: output matrix beyond 2 GiB");
@@ -318,12 +318,16 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
 
 vla_status stage_rows(Ctx& c, float* x, int ldx, int M, int N, const void* src, int src_f32, int ld_src, int r0, int r1,
                       float2* stats) {
+  if (N % 4 || ldx % 4 || (src && ld_src % 4))
+    return fail(VLA_ERR_SHAPE, "stage rows: width %d and pitches %d, %d must be multiples of 4", N, ldx, ld_src);
   return launch(c, k_stage_rows_ref(), dim3((M + 3) / 4), dim3(256), 0,
                 {arg(x), arg(ldx), arg(M), arg(N), arg(src), arg(src_f32), arg(ld_src), arg(r0), arg(r1), arg(stats)});
 }
 
 vla_status rmsnorm_out(Ctx& c, const float* x, int ldx, int M, int N, RowStats rs, const float* gain, float eps,
                        void* out, int ldo, int out_f32) {
+  if (N % 4 || ldx % 4 || ldo % 4)
+    return fail(VLA_ERR_SHAPE, "rmsnorm out: width %d and pitches %d, %d must be multiples of 4", N, ldx, ldo);
   return launch(c, k_rmsnorm_out_ref(), dim3((M + 3) / 4), dim3(256), 0,
                 {arg(x), arg(ldx), arg(M), arg(N), arg(rs), arg(gain), arg(eps), arg(out), arg(ldo), arg(out_f32)});
 }
@@ -667,6 +671,7 @@ struct DitIO {
 // The sampler's buffers (all but the context's cross-attention K/V) and the
 // state its parts hand on: the residual stream's row-statistics tiling.
 struct DitState {
+  uint16_t* phi = nullptr;   // sinusoidal features of the time grid [K, tdim]
   uint16_t* t1 = nullptr; uint16_t* sc = nullptr; float* mod = nullptr; float* fmod = nullptr;
   Stream xs{};
   float* xb[2] = {nullptr, nullptr};
@@ -699,6 +704,7 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   const vla_dit_cfg& cf = d.cfg;
   const int D = cf.hidden, L = cf.layers, K = io.K, n = io.n;
   const int mod_w = L * 9 * D;
+  s.phi = c.take<uint16_t>((size_t)K * cf.tdim);
   s.t1 = c.take<uint16_t>((size_t)K * D);
   s.sc = c.take<uint16_t>((size_t)K * D);
   s.mod = c.take<float>((size_t)K * mod_w);
@@ -751,14 +757,18 @@ vla_status dit_conditioning(Ctx& c, const vla_dit& d, const DitIO& io, DitState&
   const vla_dit_cfg& cf = d.cfg;
   const int D = cf.hidden, L = cf.layers, K = io.K, wt = cf.wdtype;
   const int mod_w = L * 9 * D;
-  {  // phi(t_k) -> Linear -> SiLU
+  {  // phi(t_k) once for the whole grid, then Linear -> SiLU
+    c.label = "dit.time_embed";
+    const int half = cf.tdim / 2, ne = K * half;
+    VLA_TRY(launch(c, k_time_embed_ref(), dim3((ne + 255) / 256), dim3(256), 0,
+                   {arg(s.phi), arg(K), arg(half), arg(cf.time_scale), arg(cf.freq_base)}));
     c.label = "dit.time_fc1";
     GemmArgs a = gargs();
     a.M = K; a.N = D; a.K = cf.tdim;
-    a.tsteps = K; a.time_scale = cf.time_scale; a.freq_base = cf.freq_base; a.half = cf.tdim / 2;
+    a.a = s.phi; a.lda = cf.tdim;
     a.w = d.w_t1; a.ldw = cf.tdim; a.wscale = d.s_t1; a.bias = d.b_t1; a.act = ACT_SILU;
     a.c = s.t1; a.ldc = D;
-    VLA_TRY(gemm(c, a, {wt, A_TIME, E_STORE}));
+    VLA_TRY(gemm(c, a, {wt, A_BF16, E_STORE}));
   }
   {  // Linear -> SiLU: SiLU(c_k) for every step
     c.label = "dit.time_fc2";

@@ -1,6 +1,6 @@
 // Weight-streaming GEMM for small M (16..600 rows), y = prologue(A) . W^T,
-// with fused prologues (row norms, patch gather, merge gather, sinusoidal
-// timestep features) and fused epilogues (bias, GELU/SiLU, RoPE, SwiGLU,
+// with fused prologues (row norms, patch gather, merge gather) and fused
+// epilogues (bias, GELU/SiLU, RoPE, SwiGLU,
 // residual / gated residual with per-tile row moments for the next norm).
 //
 // Layout: A is [M, K] row-major (token-major activations); W is [N, K]
@@ -32,7 +32,7 @@
 
 namespace vla {
 
-enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_TIME = 5, A_FP8 = 6, A_I8 = 7 };
+enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_FP8 = 6, A_I8 = 7 };
 // 8-bit activation codes with a per-row scale (W8A8)
 constexpr bool a_codes(int am) { return am == A_FP8 || am == A_I8; }
 enum EMode { E_STORE = 0, E_ROPE = 1, E_SWIGLU = 2, E_RESID = 3 };
@@ -55,7 +55,6 @@ struct GemmArgs {
   const float* bsh;      // per-k shift (NULL = 0)
   int img, patch, chans, vgrid, n_patches;   // PATCH / MERGE geometry
   int merge, n_merged;                       // MERGE
-  int tsteps; float time_scale, freq_base; int half;   // TIME
   // ---- W
   const void* w;
   int ldw;
@@ -468,8 +467,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         int dy = sub / p.merge, dx = sub % p.merge;
         int src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
         ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)src * D + d) * 4u : BUF_OOB));
-      } else {
-        ar[i] = make_float4(0.f, 0.f, 0.f, 0.f);   // TIME: computed at store time
       }
     }
   };
@@ -511,23 +508,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         v.y = ok ? (v.y - rs.x) * rs.y * ag.y + ab.y : 0.f;
         v.z = ok ? (v.z - rs.x) * rs.y * ag.z + ab.z : 0.f;
         v.w = ok ? (v.w - rs.x) * rs.y * ag.w + ab.w : 0.f;
-      } else if constexpr (AM == A_TIME) {
-        float t4[4];
-        float tm = (float)m / (float)p.tsteps;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          int kk = k + e;
-          float val = 0.f;
-          if (m < p.M && kk < p.K) {
-            int i2 = kk < p.half ? kk : kk - p.half;
-            float w = powf(p.freq_base, -(float)i2 / (float)p.half);
-            float sn, cs;
-            sincosf(p.time_scale * tm * w, &sn, &cs);
-            val = kk < p.half ? cs : sn;
-          }
-          t4[e] = val;
-        }
-        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
       } else {
         v = ar[i];
       }

@@ -15,8 +15,6 @@ bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, in
   VLA_GEMM_NARROW_AC(uint16_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_PATCH, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_MERGE, E_STORE)
-  VLA_GEMM_CASE(uint16_t, __bf16, A_TIME, E_STORE, 1, 1, 4, 1)
-  VLA_GEMM_CASE(uint16_t, __bf16, A_TIME, E_STORE, 4, 4, 1, 1)
   return false;
 }
 }  // namespace vla

@@ -18,8 +18,6 @@ bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int
   VLA_GEMM_NARROW(uint8_t, __bf16, A_NORM, E_STORE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_ROPE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_SWIGLU)
-  VLA_GEMM_CASE(uint8_t, __bf16, A_TIME, E_STORE, 1, 1, 4, 1)
-  VLA_GEMM_CASE(uint8_t, __bf16, A_TIME, E_STORE, 4, 4, 1, 1)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_FP8, E_ROPE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_FP8, E_SWIGLU)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_FP8, E_RESID)

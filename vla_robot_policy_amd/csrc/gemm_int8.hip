@@ -15,8 +15,6 @@ bool gemm_lookup_int8(int am, int em, int mb, int wn, int wk, int nbw, int u, in
   VLA_GEMM_NARROW(int8_t, __bf16, A_NORM, E_STORE)
   VLA_GEMM_WIDE(int8_t, __bf16, A_BF16, E_ROPE)
   VLA_GEMM_WIDE(int8_t, __bf16, A_BF16, E_SWIGLU)
-  VLA_GEMM_CASE(int8_t, __bf16, A_TIME, E_STORE, 1, 1, 4, 1)
-  VLA_GEMM_CASE(int8_t, __bf16, A_TIME, E_STORE, 4, 4, 1, 1)
   VLA_GEMM_WIDE(int8_t, __bf16, A_I8, E_ROPE)
   VLA_GEMM_WIDE(int8_t, __bf16, A_I8, E_SWIGLU)
   VLA_GEMM_NARROW(int8_t, __bf16, A_I8, E_RESID)

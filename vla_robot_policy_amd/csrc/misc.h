@@ -14,42 +14,119 @@ __global__ void k_fill_u32(unsigned* p, unsigned v, int n) {
   if (i < n) p[i] = v;
 }
 
+// Rows are read as float4 (bf16: four values per 8-byte load); a lane holds
+// RW_V of them per pass, every load of a pass requested before the first is
+// used, so a row costs one memory latency per 4096 columns.
+constexpr int RW_V = 16;
+
+__device__ __forceinline__ float4 bf16x4_to_f4(uint2 b) {
+  return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u), __uint_as_float(b.y << 16),
+                     __uint_as_float(b.y & 0xFFFF0000u));
+}
+
 // x[r] = src[r - r0] for r in [r0, r1) (bf16 or fp32 source), then the
 // moments of every row r < M as a single column tile (stats[r] = (mean,
-// sum of squared deviations)). One wave per row.
+// sum of squared deviations)). One wave per row; N, ldx and ld_src are
+// multiples of 4 (checked by the launcher). Each pass of 4096 columns gives
+// exact two-pass moments from registers; passes merge by Chan et al.
 __global__ __launch_bounds__(256) void k_stage_rows(float* x, int ldx, int M, int N, const void* src, int src_f32,
                                                   int ld_src, int r0, int r1, float2* stats) {
-  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (r >= M) return;
   float* xr = x + (size_t)r * ldx;
-  if (src && r >= r0 && r < r1) {
-    for (int c = lane; c < N; c += 64) {
-      size_t o = (size_t)(r - r0) * ld_src + c;
-      xr[c] = src_f32 ? ((const float*)src)[o] : bf2f(((const uint16_t*)src)[o]);
+  const bool copy = src && r >= r0 && r < r1;
+  const brsrc xs = make_brsrc(xr);
+  const brsrc ss = make_brsrc(!copy ? (const void*)xr
+                                    : src_f32 ? (const void*)((const float*)src + (size_t)(r - r0) * ld_src)
+                                              : (const void*)((const uint16_t*)src + (size_t)(r - r0) * ld_src));
+  float n = 0.f, mean = 0.f, m2 = 0.f;
+  for (int c0 = 0; c0 < N; c0 += 64 * 4 * RW_V) {
+    float4 v[RW_V];
+#pragma unroll
+    for (int i = 0; i < RW_V; i++) {
+      const int c = c0 + (lane + 64 * i) * 4;
+      const bool ok = c < N;
+      if (copy && !src_f32) v[i] = bf16x4_to_f4(bload8(ss, ok ? (uint32_t)c * 2u : BUF_OOB));
+      else v[i] = as_f4(bload16(copy ? ss : xs, ok ? (uint32_t)c * 4u : BUF_OOB));
     }
+    if (copy) {
+#pragma unroll
+      for (int i = 0; i < RW_V; i++) {
+        const int c = c0 + (lane + 64 * i) * 4;
+        if (c < N) *reinterpret_cast<float4*>(xr + c) = v[i];
+      }
+    }
+    const int cn = min(N - c0, 64 * 4 * RW_V);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < RW_V; i++) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);   // zeros beyond N
+    const float cm = wave_sum(s) / (float)cn;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < RW_V; i++) {
+      if (c0 + (lane + 64 * i) * 4 < N) {
+        const float d0 = v[i].x - cm, d1 = v[i].y - cm, d2 = v[i].z - cm, d3 = v[i].w - cm;
+        q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+      }
+    }
+    moments_merge(n, mean, m2, (float)cn, cm, wave_sum(q));
   }
-  float s = 0.f;
-  for (int c = lane; c < N; c += 64) s += xr[c];
-  float mean = wave_sum(s) / (float)N;
-  float q = 0.f;
-  for (int c = lane; c < N; c += 64) { float d = xr[c] - mean; q += d * d; }
-  float m2 = wave_sum(q);
   if (lane == 0) stats[r] = make_float2(mean, m2);
 }
 
 // out[r] = RMSNorm(x[r]) * gain, from the row moments left by x's writer.
+// One wave per row; the row and the gains are requested before the row
+// moments are merged, so both share one memory latency.
 __global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, int M, int N, RowStats st_in,
                                                    const float* gain, float eps, void* out, int ldo, int out_f32) {
-  int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (r >= M) return;
-  float rs = norm_coeffs(row_moments_wave(st_in, r), 1, eps).y;
-  for (int c = lane; c < N; c += 64) {
-    float v = x[(size_t)r * ldx + c] * rs * gain[c];
-    if (out_f32) ((float*)out)[(size_t)r * ldo + c] = v;
-    else ((uint16_t*)out)[(size_t)r * ldo + c] = f2bf(v);
+  const brsrc xs = make_brsrc(x + (size_t)r * ldx), gs = make_brsrc(gain);
+  float rs = 0.f;
+  for (int c0 = 0; c0 < N; c0 += 64 * 4 * RW_V) {
+    float4 v[RW_V], g[RW_V];
+#pragma unroll
+    for (int i = 0; i < RW_V; i++) {
+      const int c = c0 + (lane + 64 * i) * 4;
+      v[i] = as_f4(bload16(xs, c < N ? (uint32_t)c * 4u : BUF_OOB));
+      g[i] = as_f4(bload16(gs, c < N ? (uint32_t)c * 4u : BUF_OOB));
+    }
+    if (c0 == 0) rs = norm_coeffs(row_moments_wave(st_in, r), 1, eps).y;
+#pragma unroll
+    for (int i = 0; i < RW_V; i++) {
+      const int c = c0 + (lane + 64 * i) * 4;
+      if (c >= N) continue;
+      const float4 y = make_float4(v[i].x * rs * g[i].x, v[i].y * rs * g[i].y, v[i].z * rs * g[i].z, v[i].w * rs * g[i].w);
+      if (out_f32) {
+        *reinterpret_cast<float4*>((float*)out + (size_t)r * ldo + c) = y;
+      } else {
+        uint2 u;
+        u.x = pack_bf2(y.x, y.y);
+        u.y = pack_bf2(y.z, y.w);
+        *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)r * ldo + c) = u;
+      }
+    }
   }
+}
+
+// Sinusoidal features of the sampler's time grid t_k = k / K (k < K): row k
+// is [cos(s t_k w_i) | sin(s t_k w_i)], w_i = base^(-i / half), i < half, in
+// bf16 [K][2 half]. The frequency and the argument are formed in double and
+// reduced to [-pi, pi] before the float sine and cosine (the arguments reach
+// s radians).
+__global__ __launch_bounds__(256) void k_time_embed(uint16_t* phi, int K, int half, float time_scale, float freq_base) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= K * half) return;
+  const int k = e / half, i = e % half;
+  const double w = pow((double)freq_base, -(double)i / (double)half);
+  double a = (double)time_scale * ((double)k / (double)K) * w;
+  a -= rint(a * (0.5 / M_PI)) * (2.0 * M_PI);
+  float sn, cs;
+  sincosf((float)a, &sn, &cs);
+  phi[(size_t)k * 2 * half + i] = f2bf(cs);
+  phi[(size_t)k * 2 * half + half + i] = f2bf(sn);
 }
 
 // One normalised row per workgroup, in bf16, for the GEMMs that read it:
