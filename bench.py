@@ -31,6 +31,9 @@ WORKLOADS = {
         "at seq 560 -> projector -> DiT 36L x 10 Euler steps, chunk 50x32; one hipGraph"),
 }
 
+# backbone Linears in the packed layout of vla_pack_weights (--row-major: as
+# uploaded); the results are bitwise the same
+PACKED = True
 
 _CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
 
@@ -98,7 +101,7 @@ def shape_cache_bench(cfg, texts, steps, warmup):
     n_vis = cfg.seq - cfg.n_text
     top = cfg.replace(n_text=max(texts), seq=n_vis + max(texts), ctx_len=n_vis + max(texts))
     W, I = make_weights(top), make_inputs(top)
-    dw = DeviceWeights(top, W, keep_host=False, threads=16)
+    dw = DeviceWeights(top, W, keep_host=False, threads=16, packed=PACKED and not top.block.a8)
     model = dw.build_model()
     d = top.dit
     dev = torch.device("cuda:0")
@@ -171,7 +174,7 @@ def fused_bench(cfg, n_stale, steps, warmup):
     from vla_robot_policy_amd.device import DeviceWeights, upload_input, workspace
 
     W, I = make_weights(cfg), make_inputs(cfg)
-    dw = DeviceWeights(cfg, W, keep_host=False, threads=16)
+    dw = DeviceWeights(cfg, W, keep_host=False, threads=16, packed=PACKED and not cfg.block.a8)
     model = dw.build_model()
     d = cfg.dit
     dev = torch.device("cuda:0")
@@ -232,7 +235,7 @@ def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
 
     t0 = time.time()
     W, I = make_weights(cfg), make_inputs(cfg)
-    dw = DeviceWeights(cfg, W, keep_host=False, threads=16)
+    dw = DeviceWeights(cfg, W, keep_host=False, threads=16, packed=PACKED and not cfg.block.a8)
     if cfg.kind == "step":
         model = dw.build_model()
     log(f"weights generated and uploaded in {time.time() - t0:.1f}s")
@@ -393,6 +396,8 @@ def main():
     ap.add_argument("--fused", type=int, default=None, metavar="N_STALE",
                     help="time V-AEFusion cycles with N_STALE stale Euler steps against the plain step "
                          "and print that line instead of the headline")
+    ap.add_argument("--row-major", action="store_true",
+                    help="backbone weights as row-major matrices instead of the packed layout of vla_pack_weights")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a device copy of this many bytes --kernel-reps times (counter calibration)")
     a = ap.parse_args()
@@ -403,6 +408,8 @@ def main():
     if a.copy_bytes:
         copy_probe(a.copy_bytes, a.kernel_reps)
         return
+    global PACKED
+    PACKED = not a.row_major
     from synth import get_config
     from vla_robot_policy_amd import roofline
     cfg = get_config(a.config)

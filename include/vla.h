@@ -23,8 +23,9 @@
  *     bf16 tensors are raw bfloat16 bit patterns (uint16); fp8 tensors are
  *     OCP E4M3FN codes (uint8) with one float32 scale per output row; norm
  *     gains, biases, positional tables and modulation vectors are float32.
- *   - All tensor pointers are DEVICE pointers, 16-byte aligned, owned by the
- *     caller. The library never allocates device memory in a run, capture or
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned (the widest
+ *     single access any kernel makes; hipMalloc and torch allocations are
+ *     256-byte aligned and satisfy it), owned by the caller. The library never allocates device memory in a run, capture or
  *     replay call; scratch space is the caller's workspace (ws, ws_bytes),
  *     whose required size the matching *_workspace_bytes() returns. The
  *     workspace content need not be initialised.
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define VLA_ABI_VERSION 2   /* 2: vla_block_weights gained q_norm, k_norm */
+#define VLA_ABI_VERSION 3   /* 2: vla_block_weights gained q_norm, k_norm; 3: packed weights */
 
 typedef enum {
   VLA_OK = 0,
@@ -86,18 +87,25 @@ typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2, VLA_INT8 = 3 } vla_d
  * hidden <= 4096, and the Linear inputs (hidden, n_q_heads * head_dim,
  * intermediate) multiples of 16 and at most 16384 wide;
  * VLA_ERR_UNSUPPORTED otherwise.
+ * With flags & VLA_BLOCK_PACKED, w_qkv, w_o, w_gate_up and w_down are the
+ * packed copies vla_pack_weights writes of the row-major matrices above
+ * (each packed on its own, N and K as listed; scales unchanged). Needs BF16,
+ * FP8_E4M3 or INT8 weights without VLA_BLOCK_A8, and intermediate a
+ * multiple of 16; VLA_ERR_UNSUPPORTED otherwise. Results are bitwise those
+ * of the row-major weights.
  * Supported: head_dim in {64, 128}; hidden, intermediate multiples of 8
  * (of 16 for FP8_E4M3 weights); n_q_heads % n_kv_heads == 0; wdtype F32 with adtype F32, or wdtype
  * BF16 / FP8_E4M3 with adtype BF16.
  */
 #define VLA_BLOCK_QK_NORM 1
 #define VLA_BLOCK_A8 2
+#define VLA_BLOCK_PACKED 4
 typedef struct {
   int32_t hidden, n_q_heads, n_kv_heads, head_dim, intermediate;
   float rope_base, eps;
   int32_t wdtype;  /* vla_dtype of the Linear weights                  */
   int32_t adtype;  /* vla_dtype of x_in / x_out / embeddings: F32, BF16 */
-  int32_t flags;   /* VLA_BLOCK_QK_NORM | VLA_BLOCK_A8, or 0           */
+  int32_t flags;   /* VLA_BLOCK_QK_NORM | VLA_BLOCK_A8 | VLA_BLOCK_PACKED */
 } vla_block_cfg;
 
 typedef struct {
@@ -137,6 +145,30 @@ size_t vla_block_workspace_bytes(const vla_block_cfg* cfg, int32_t seq);
 #define VLA_STATIC_SCRATCH_BYTES (64u << 20)
 vla_status vla_block_forward_static(const vla_block_cfg* cfg, const vla_block_weights* w, const void* x_in, void* x_out,
                                     int32_t seq, hipStream_t stream);
+
+/* ------------------------------------------------------------------ weight packing
+ * [R] 自研推理框架: weights reach the engine as ready device tensors, laid
+ * out once at load time for the kernels that read them. A packed matrix
+ * holds the same values as the row-major W[N, K] (pitch ldw elements),
+ * regrouped so that one 64-lane wave load is one MFMA operand block: blocks
+ * of 16 rows x 32 k, ordered [row block][k block] (row block nb, k block kb
+ * at element offset (nb * ceil(K/32) + kb) * 512), lane l of a block holding
+ * the 8 consecutive values of row 16 nb + l % 16 at k = 32 kb + 8 (l / 16)
+ * .. + 7. Rows beyond N and k beyond K are zero. 8-bit scales stay per row
+ * and unpacked.
+ * vla_packed_bytes: size of the packed copy, ceil(N/16) * ceil(K/32) * 512
+ * elements of the weight type (a multiple of 512 bytes, so packed matrices
+ * placed back to back keep their alignment); 0 for an unsupported dtype
+ * (only BF16, FP8_E4M3, INT8 pack) or N, K < 1.
+ * vla_pack_weights: one kernel on stream, reading w (device, [N, ldw],
+ * ldw >= K) and writing packed (device, vla_packed_bytes(wdtype, N, K)
+ * bytes, 16-byte aligned, caller-owned, must not overlap w). Asynchronous:
+ * w must stay valid until the stream reaches the kernel. Errors:
+ * VLA_ERR_UNSUPPORTED (dtype), VLA_ERR_INVALID_ARG (null or misaligned
+ * pointer), VLA_ERR_SHAPE (N, K < 1, ldw < K, or more than 2 GiB packed). */
+size_t vla_packed_bytes(int32_t wdtype, int32_t N, int32_t K);
+vla_status vla_pack_weights(int32_t wdtype, const void* w, int32_t N, int32_t K, int32_t ldw, void* packed,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------ backbone
  * The decoder prefill ([R] 整体方案; CUDA Graph: "36 layers to the final

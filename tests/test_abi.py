@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     assert len(syms) >= 17
     for s in syms:
         assert hasattr(L, s), s
-    assert lib.vla_abi_version() == 2
+    assert lib.vla_abi_version() == 3
 
 
 def llm_cfg(**kw):
@@ -39,7 +39,10 @@ def test_workspace_sizes_scale_with_shape():
     (dict(head_dim=96), lib.VLA_ERR_SHAPE),
     (dict(n_kv_heads=5), lib.VLA_ERR_SHAPE),
     (dict(hidden=2561), lib.VLA_ERR_SHAPE),
-    (dict(flags=4), lib.VLA_ERR_UNSUPPORTED),                                       # unknown bit
+    (dict(flags=8), lib.VLA_ERR_UNSUPPORTED),                                       # unknown bit
+    (dict(flags=lib.VLA_BLOCK_PACKED, wdtype=lib.VLA_F32, adtype=lib.VLA_F32), lib.VLA_ERR_UNSUPPORTED),  # fp32 does not pack
+    (dict(flags=lib.VLA_BLOCK_PACKED | lib.VLA_BLOCK_A8, wdtype=lib.VLA_FP8_E4M3), lib.VLA_ERR_UNSUPPORTED),
+    (dict(flags=lib.VLA_BLOCK_PACKED, intermediate=9736), lib.VLA_ERR_UNSUPPORTED),  # up rows off a 16-row block
     (dict(flags=lib.VLA_BLOCK_A8), lib.VLA_ERR_UNSUPPORTED),                        # fp8 activations, bf16 weights
     (dict(flags=lib.VLA_BLOCK_A8, wdtype=lib.VLA_FP8_E4M3, hidden=5120, n_q_heads=40), lib.VLA_ERR_UNSUPPORTED),  # hidden > 4096
     (dict(flags=lib.VLA_BLOCK_QK_NORM), lib.VLA_ERR_INVALID_ARG),                  # no q_norm / k_norm
@@ -211,3 +214,27 @@ def test_static_block_rejects_shapes_beyond_its_scratch():
     st = lib.vla_block_forward_static(llm_cfg(), w, 256, 512, 1024)
     assert st == lib.VLA_ERR_WORKSPACE, lib.vla_last_error()
     assert "static" in lib.vla_last_error()
+
+
+def test_packed_bytes():
+    # ceil(N/16) * ceil(K/32) blocks of 512 elements
+    assert lib.vla_packed_bytes(lib.VLA_BF16, 6144, 2560) == 6144 * 2560 * 2
+    assert lib.vla_packed_bytes(lib.VLA_FP8_E4M3, 2560, 9728) == 2560 * 9728
+    assert lib.vla_packed_bytes(lib.VLA_INT8, 37, 70) == 3 * 3 * 512
+    assert lib.vla_packed_bytes(lib.VLA_BF16, 1, 1) == 1024
+    assert lib.vla_packed_bytes(lib.VLA_F32, 64, 64) == 0
+    assert lib.vla_packed_bytes(lib.VLA_BF16, 0, 64) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((lib.VLA_F32, 1 << 20, 16, 32, 32, 1 << 21), lib.VLA_ERR_UNSUPPORTED),
+    ((lib.VLA_BF16, None, 16, 32, 32, 1 << 21), lib.VLA_ERR_INVALID_ARG),
+    ((lib.VLA_BF16, 1 << 20, 16, 32, 32, None), lib.VLA_ERR_INVALID_ARG),
+    ((lib.VLA_BF16, 1 << 20, 16, 32, 32, (1 << 21) + 8), lib.VLA_ERR_INVALID_ARG),   # misaligned output
+    ((lib.VLA_BF16, 1 << 20, 16, 32, 16, 1 << 21), lib.VLA_ERR_SHAPE),              # pitch < K
+    ((lib.VLA_INT8, 1 << 20, 0, 32, 32, 1 << 21), lib.VLA_ERR_SHAPE),
+    ((lib.VLA_BF16, 1 << 20, 1 << 17, 1 << 13, 1 << 13, 1 << 21), lib.VLA_ERR_SHAPE),  # 2 GiB packed
+])
+def test_pack_weights_validation(args, code):
+    assert lib.vla_pack_weights(*args) == code
+    assert lib.vla_last_error()

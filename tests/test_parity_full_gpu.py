@@ -2,7 +2,9 @@
 
 Each test generates the seeded weights and inputs of one named workload, runs
 it through the C ABI in the launch configuration the benchmark times (the
-whole-step plan captured as one graph and replayed, for the policy steps) and
+whole-step plan captured as one graph and replayed, for the policy steps;
+backbone weights packed by vla_pack_weights, except in the fused tests, which
+keep them row-major) and
 compares every graded output with the oracle evaluated on the same stored
 values. Bars: relative L2 error <= 1e-2 for bf16 weights, <= 5e-2 for fp8.
 
@@ -46,7 +48,7 @@ def test_backbone_full_seq256(gu):
     cfg = get_config(2)
     gu.say(f"{cfg.name}: backbone {cfg.layers} layers, seq {cfg.seq}")
     W, I = _generate(gu, cfg)
-    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
+    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16, packed=True))
     got = gu.timed("gpu", lambda: gu.run_backbone(cfg, dw, gu.upload_input(I["x"]), cfg.seq))
     want = gu.timed("oracle", lambda: run_config(cfg, gu.ProgressWeights(W, "oracle"), I)["hidden"])
     e = gu.relerr(got, want, 1e-2, f"backbone seq {cfg.seq} hidden")
@@ -66,9 +68,10 @@ def test_dit_full_ctx256(gu):
 
 
 def _step_graph(gu, cfg, W, I):
-    """Outputs of the whole-step plan: one eager run, then two graph replays
-    that must reproduce it bit for bit."""
-    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16))
+    """Outputs of the whole-step plan on packed backbone weights (as the
+    benchmark runs it; row-major for W8A8, which does not pack): one eager
+    run, then two graph replays that must reproduce it bit for bit."""
+    dw = gu.timed("upload", lambda: gu.DeviceWeights(cfg, W, threads=16, packed=not cfg.block.a8))
     r = gu.StepRunner(cfg, dw, I)
     try:
         r.run()

@@ -152,6 +152,7 @@ struct GemmOp {
   int wdtype;   // vla_dtype of W
   int am, em;
   int ac = 0;   // compensated (hi + lo) bf16 activations
+  int pk = 0;   // W in the packed layout of vla_pack_weights
 };
 
 // Row tile (16-row blocks) by M: one tile up to 112 rows; 64-row tiles up to
@@ -168,8 +169,14 @@ struct GemmOp {
 // taller ones (the cross-attention K/V: 82 vs 108 us), and two k-waves of
 // 32 columns with a two-way split for small residual GEMMs (the ViT output
 // projection: 12.0 vs 14.2 us).
-void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb, int& wn, int& wk, int& nbw, int& u,
-               int& split_hint, int& target_wgs) {
+// Backbone shapes of 65-112 rows (measured at 104): the RoPE tile with two
+// k-steps per wave and four activation chunks in flight (QKV 21.1 -> 20.1
+// us), the O projection on 32-column tiles of two k-waves (18.5 -> 16.0 us),
+// the compensated down projection with one k-step per wave and four
+// activation chunks in flight (37.2 -> 32.2 us). Packed weights (pk) take the
+// same tiles (and give the same bits).
+void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb, int& wn, int& wk, int& nbw,
+               int& u, int& aq, int& split_hint, int& target_wgs) {
   bool wide = em == E_ROPE || em == E_SWIGLU;
   mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : (M <= 256 || (ac && !wide)) ? 4 : 8;
   u = ac ? 2 : 4;
@@ -196,14 +203,20 @@ void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb,
   else if (mid_rows && em == E_RESID) { wn = 2; wk = 2; u = 2; target_wgs = 160; }
   else if (mid_rows && em == E_STORE) { wn = 4; wk = 1; target_wgs = 80; }
   else { wn = 4; wk = 1; }
+  aq = 2;
+  if (mb == 7 && am == A_BF16 && wdtype != VLA_F32) {
+    if (em == E_ROPE && !ac) { u = 2; aq = 4; }
+    else if (em == E_RESID && !ac) { wn = 2; wk = 2; nbw = 1; u = 2; split_hint = 0; target_wgs = 0; }
+    else if (em == E_RESID && ac) { u = 1; aq = 4; }
+  }
 }
 
 // Launch one GEMM. For a residual epilogue, *produced receives the column
 // tiling of the row moments the kernel leaves in a.rs_out.
 vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return fail(VLA_ERR_SHAPE, "gemm: empty shape %d x %d x %d", a.M, a.N, a.K);
-  int mb, wn, wk, nbw, u, split_hint, target_wgs;
-  pick_tile(a.M, a.N, a.K, op.am, op.em, op.ac, op.wdtype, mb, wn, wk, nbw, u, split_hint, target_wgs);
+  int mb, wn, wk, nbw, u, aq, split_hint, target_wgs;
+  pick_tile(a.M, a.N, a.K, op.am, op.em, op.ac, op.wdtype, mb, wn, wk, nbw, u, aq, split_hint, target_wgs);
   const int BM = 16 * mb, BN = 16 * nbw * wn, BK = 32 * wk * u;
   const int bn_out = op.em == E_SWIGLU ? BN / 2 : BN;
   a.n_tiles_n = (a.N + bn_out - 1) / bn_out;
@@ -240,9 +253,19 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a_codes(op.am) && !a.a_scale && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: 8-bit activations without row scales");
   if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM || a_codes(op.am)) && (a.lda % ag != 0 || a.K % ag != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
+  // the epilogues store 4 consecutive columns at once and read the
+  // per-column vectors as float4
+  if (a.N % 4 != 0 || (op.em == E_RESID ? a.ldx % 4 != 0 : a.ldc % 4 != 0))
+    return fail(VLA_ERR_SHAPE, "gemm: N %d and the output pitch must be multiples of 4", a.N);
+  for (const void* v : {(const void*)a.bias, (const void*)a.wscale, (const void*)a.gate, (const void*)a.c, (const void*)a.x,
+                        (const void*)a.rope_cos, (const void*)a.rope_sin, (const void*)a.addrow})
+    if (reinterpret_cast<uintptr_t>(v) & 15) return fail(VLA_ERR_INVALID_ARG, "gemm: output or epilogue vector not 16-byte aligned");
   // buffer-load offsets are 32-bit: operands up to 2 GiB
   const double wrows = op.em == E_SWIGLU ? (double)a.n_half + a.N : (double)a.N;
   if (wrows * a.ldw * wbytes >= (double)BUF_LIMIT) return fail(VLA_ERR_SHAPE, "gemm: weight matrix beyond 2 GiB");
+  if (op.pk && (std::ceil(wrows / 16.0) * std::ceil(a.K / 32.0) * 512.0 * wbytes >= (double)BUF_LIMIT ||
+                (op.em == E_SWIGLU && a.n_half % 16)))
+    return fail(VLA_ERR_SHAPE, "gemm: packed weight matrix beyond 2 GiB, or gate/up halves not on 16-row blocks");
   if (op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
   if ((op.em == E_RESID ? (double)a.M * a.ldx * 4.0 : (double)a.M * a.ldc * (a.c_f32 ? 4.0 : 2.0)) >= (double)BUF_LIMIT)
@@ -260,11 +283,14 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   c.need_tiles = std::max(c.need_tiles, (size_t)tiles);
   KernelRef k{};
   bool found = false;
-  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
-  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
-  else if (op.wdtype == VLA_INT8) found = gemm_lookup_int8(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
-  else if (op.wdtype == VLA_F32) found = gemm_lookup_f32(op.am, op.em, mb, wn, wk, nbw, u, op.ac, &k);
-  if (!found) return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d/%d", op.wdtype, op.am, op.em, mb, wn, wk, nbw);
+  const GemmPick g{op.am, op.em, mb, wn, wk, nbw, u, op.ac, aq, op.pk};
+  if (op.wdtype == VLA_BF16) found = gemm_lookup_bf16(g, &k);
+  else if (op.wdtype == VLA_FP8_E4M3) found = gemm_lookup_fp8(g, &k);
+  else if (op.wdtype == VLA_INT8) found = gemm_lookup_int8(g, &k);
+  else if (op.wdtype == VLA_F32 && !op.pk) found = gemm_lookup_f32(g, &k);
+  if (!found)
+    return fail(VLA_ERR_UNSUPPORTED, "gemm: no kernel for wdtype %d am %d em %d tile %d/%d/%d/%d u %d ac %d aq %d packed %d",
+                op.wdtype, op.am, op.em, mb, wn, wk, nbw, u, op.ac, aq, op.pk);
   if (c.plan) { c.kernels++; return VLA_OK; }
   a.part = c.part;
   a.cnt_tile = c.cnt_tile;
@@ -400,7 +426,16 @@ bool scaled8(int t) { return t == VLA_FP8_E4M3 || t == VLA_INT8; }
 // ------------------------------------------------------------------ backbone
 vla_status check_block_cfg(const vla_block_cfg* cfg) {
   if (!cfg) return fail(VLA_ERR_INVALID_ARG, "null block cfg");
-  if (cfg->flags & ~(VLA_BLOCK_QK_NORM | VLA_BLOCK_A8)) return fail(VLA_ERR_UNSUPPORTED, "block cfg flags 0x%x: unknown bits", cfg->flags);
+  if (cfg->flags & ~(VLA_BLOCK_QK_NORM | VLA_BLOCK_A8 | VLA_BLOCK_PACKED))
+    return fail(VLA_ERR_UNSUPPORTED, "block cfg flags 0x%x: unknown bits", cfg->flags);
+  if (cfg->flags & VLA_BLOCK_PACKED) {
+    if (cfg->wdtype == VLA_F32)
+      return fail(VLA_ERR_UNSUPPORTED, "block cfg: packed weights need bf16, fp8 or int8 weights and bf16 activations");
+    if (cfg->flags & VLA_BLOCK_A8) return fail(VLA_ERR_UNSUPPORTED, "block cfg: packed weights with 8-bit activations");
+    // the up rows of the gate/up matrix start a new 16-row block
+    if (cfg->intermediate % 16)
+      return fail(VLA_ERR_UNSUPPORTED, "block cfg: packed weights need intermediate %d to be a multiple of 16", cfg->intermediate);
+  }
   if (cfg->flags & VLA_BLOCK_A8) {
     if (!scaled8(cfg->wdtype) || cfg->adtype != VLA_BF16)
       return fail(VLA_ERR_UNSUPPORTED, "block cfg: 8-bit activations need fp8 or int8 weights and bf16 activations");
@@ -428,10 +463,16 @@ vla_status check_block_cfg(const vla_block_cfg* cfg) {
   return VLA_OK;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 vla_status check_block_weights(const vla_block_cfg* cfg, const vla_block_weights* w) {
   if (!w) return fail(VLA_ERR_INVALID_ARG, "null block weights");
   if (!w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
     return fail(VLA_ERR_INVALID_ARG, "block weights: null tensor pointer");
+  for (const void* v : {(const void*)w->attn_norm, w->w_qkv, (const void*)w->s_qkv, w->w_o, (const void*)w->s_o,
+                        (const void*)w->mlp_norm, w->w_gate_up, (const void*)w->s_gate_up, w->w_down,
+                        (const void*)w->s_down, (const void*)w->q_norm, (const void*)w->k_norm})
+    if (!aligned16(v)) return fail(VLA_ERR_INVALID_ARG, "block weights: tensor not 16-byte aligned");
   if (scaled8(cfg->wdtype) && (!w->s_qkv || !w->s_o || !w->s_gate_up || !w->s_down))
     return fail(VLA_ERR_INVALID_ARG, "block weights: fp8 weights need scales");
   if ((cfg->flags & VLA_BLOCK_QK_NORM) && (!w->q_norm || !w->k_norm))
@@ -449,6 +490,8 @@ struct BackboneBufs {
   uint16_t* act_lo;// [S, I] remainder plane of the SwiGLU output (compensated MLP)
   uint8_t* q8;     // [S, max(H, q_dim, I)] E4M3FN codes of the next Linear's input (fp8 activations)
   float* q8s;      // [S] their row scales
+  float* rope_cos; // [S, head_dim / 2] RoPE tables of the pass (positions 0 .. S-1)
+  float* rope_sin;
 };
 
 // bf16 backbones carry the MLP's activations (the normalised input of gate/up
@@ -471,6 +514,8 @@ BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   b.act = c.take<char>((size_t)S * cfg.intermediate * eq);
   b.xn = b.xn_lo = b.act_lo = nullptr;
   b.q8 = nullptr; b.q8s = nullptr;
+  b.rope_cos = c.take<float>((size_t)S * (cfg.head_dim / 2));
+  b.rope_sin = c.take<float>((size_t)S * (cfg.head_dim / 2));
   if (cfg.adtype != VLA_F32) b.xn = c.take<uint16_t>((size_t)S * cfg.hidden);
   if (cfg.flags & VLA_BLOCK_A8) {
     const int w = std::max({cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.intermediate});
@@ -492,11 +537,18 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   const int wt = cfg.wdtype;
   const size_t es = f32 ? 4 : 2;
   const int comp = mlp_compensated(cfg) ? 1 : 0;
+  const int pk = (cfg.flags & VLA_BLOCK_PACKED) ? 1 : 0;   // W in the packed layout of vla_pack_weights
   // W8A8: each Linear reads its input as per-row E4M3FN codes (the norms
   // write codes, the attention and SwiGLU outputs are quantised by a row pass)
   const bool a8 = (cfg.flags & VLA_BLOCK_A8) != 0;
   const int i8 = wt == VLA_INT8 ? 1 : 0;              // the activation codes follow the weights' format
   const int am_bf = a8 ? (i8 ? A_I8 : A_FP8) : A_BF16;
+  {  // cos / sin of every position's RoPE angles, once for the pass
+    c.label = "llm.rope_table";
+    const int ne = S * (D / 2);
+    VLA_TRY(launch(c, k_rope_table_ref(), dim3((ne + 255) / 256), dim3(256), 0,
+                   {arg(b.rope_cos), arg(b.rope_sin), arg(S), arg(D), arg(cfg.rope_base)}));
+  }
   for (int l = 0; l < n_layers; l++) {
     const vla_block_weights& w = layers[l];
     {  // RMSNorm -> fused QKV -> RoPE
@@ -515,9 +567,9 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.xn; a.lda = H; }
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
       a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32 || a8;
-      a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_base = cfg.rope_base;
+      a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_cos = b.rope_cos; a.rope_sin = b.rope_sin;
       if (cfg.flags & VLA_BLOCK_QK_NORM) { a.qk_norm = 1; a.qk_eps = cfg.eps; a.qn_g = w.q_norm; a.kn_g = w.k_norm; }
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_ROPE}));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_ROPE, 0, pk}));
     }
     {  // causal GQA attention
     c.label = "llm.attn";
@@ -542,7 +594,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.ao; a.lda = qd; }
       a.w = w.w_o; a.ldw = qd; a.wscale = w.s_o;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID}, &b.xs.rs));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, 0, pk}, &b.xs.rs));
     }
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
       if (a8) {
@@ -560,7 +612,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.xn; a.a_lo = b.xn_lo; a.lda = H; }
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
       a.c = b.act; a.c_lo = b.act_lo; a.ldc = I; a.c_f32 = f32 || a8;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_SWIGLU, comp}));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_SWIGLU, comp, pk}));
     }
     {  // down + residual (+ row statistics)
       if (a8) {
@@ -574,7 +626,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.act; a.a_lo = b.act_lo; a.lda = I; }
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, comp}, &b.xs.rs));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, comp, pk}, &b.xs.rs));
     }
   }
   return VLA_OK;
@@ -608,7 +660,6 @@ vla_status two_pass(void* ws, size_t ws_bytes, hipStream_t st, size_t* need_out,
   return sched(c);
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // ------------------------------------------------------------------ DiT
 vla_status check_dit(const vla_dit* d) {
@@ -1119,6 +1170,28 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
 extern "C" {
 
 const char* vla_last_error(void) { return g_err.c_str(); }
+
+size_t vla_packed_bytes(int32_t wdtype, int32_t N, int32_t K) {
+  if ((wdtype != VLA_BF16 && !scaled8(wdtype)) || N < 1 || K < 1) return 0;
+  const size_t esz = wdtype == VLA_BF16 ? 2 : 1;
+  return (size_t)((N + 15) / 16) * (size_t)((K + 31) / 32) * 512 * esz;
+}
+
+vla_status vla_pack_weights(int32_t wdtype, const void* w, int32_t N, int32_t K, int32_t ldw, void* packed,
+                            hipStream_t stream) {
+  if (wdtype != VLA_BF16 && !scaled8(wdtype)) return fail(VLA_ERR_UNSUPPORTED, "pack weights: dtype %d (bf16, fp8 or int8)", wdtype);
+  if (!w || !packed) return fail(VLA_ERR_INVALID_ARG, "pack weights: null pointer");
+  if ((reinterpret_cast<uintptr_t>(packed) & 15) != 0) return fail(VLA_ERR_INVALID_ARG, "pack weights: output not 16-byte aligned");
+  if (N < 1 || K < 1 || ldw < K) return fail(VLA_ERR_SHAPE, "pack weights: N %d, K %d, pitch %d", N, K, ldw);
+  const size_t chunks = vla_packed_bytes(wdtype, N, K) / (wdtype == VLA_BF16 ? 16 : 8);
+  if (vla_packed_bytes(wdtype, N, K) >= (size_t)BUF_LIMIT) return fail(VLA_ERR_SHAPE, "pack weights: matrix beyond 2 GiB");
+  Ctx c;
+  c.plan = false; c.st = stream;
+  c.label = "pack_weights";
+  const int esz = wdtype == VLA_BF16 ? 2 : 1;
+  return launch(c, k_pack_weights_ref(), dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                {arg(w), arg(N), arg(K), arg(ldw), arg(esz), arg(packed)});
+}
 
 vla_status vla_workspace_status(const void* ws, hipStream_t stream) {
   if (!ws) return fail(VLA_ERR_INVALID_ARG, "null workspace");

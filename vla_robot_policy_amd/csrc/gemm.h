@@ -67,7 +67,8 @@ struct GemmArgs {
   void* c_lo;            // STORE / SWIGLU in bf16: also the remainder plane bf16(v - hi) (NULL = none)
   int ldc;
   int c_f32;
-  int q_cols, k_cols, head_dim, pos0; float rope_base;   // ROPE
+  int q_cols, k_cols, head_dim, pos0;                     // ROPE: rotated columns, head size, first position
+  const float* rope_cos; const float* rope_sin;           // ROPE: [position][head_dim / 2] tables of the pass
   int qk_norm; float qk_eps;                              // ROPE: per-head RMSNorm of q and k first
   const float* qn_g; const float* kn_g;                   //   with gains [head_dim]; tiles hold whole heads
   float* x; int ldx;                                      // RESID
@@ -169,7 +170,8 @@ __device__ __forceinline__ bool tile_arrive(unsigned* cnt, int expected, int* fl
 constexpr int SPLIT_MAX = 16;
 
 // ---------------------------------------------------------------- tile geometry
-template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
+template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0, int AQ = 2,
+          int PK = 0>
 struct GemmTile {
   static constexpr int THREADS = 64 * WN * WK;
   static constexpr int NW = WN * WK;             // waves
@@ -191,7 +193,9 @@ struct GemmTile {
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
   // weights through LDS (bf16 / fp8): [BN][BK] with padded rows; each thread
   // loads NWL 16-byte groups per chunk, LPR groups make one chunk row
-  static constexpr bool WLDS = sizeof(WT) <= 2;
+  // packed weights (PK) go straight to registers: each wave load is one
+  // contiguous fragment block
+  static constexpr bool WLDS = sizeof(WT) <= 2 && !PK;
   static constexpr int WROW = BK * (int)sizeof(WT) + 16;
   static constexpr int WBUF = WLDS ? BN * WROW : 0;
   static constexpr int LPR = BK * (int)sizeof(WT) / 16;
@@ -220,9 +224,11 @@ template <> struct ARaw<A_FP8, 0> { using type = uint4; };
 template <> struct ARaw<A_I8, 0> { using type = uint4; };
 
 // ---------------------------------------------------------------- kernel
-template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0>
+template <typename WT, typename CT, int MB, int WN, int WK, int NBW, int AM, int EM, int UU = 4, int AC = 0, int AQ = 2,
+          int PK = 0>
 __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
-  using T = GemmTile<WT, CT, MB, WN, WK, NBW, AM, EM, UU, AC>;
+  using T = GemmTile<WT, CT, MB, WN, WK, NBW, AM, EM, UU, AC, AQ, PK>;
+  static_assert(AQ == 2 || AQ == 4, "activation chunks in flight: 2 or 4");
   using WL = WLoad<WT>;
   using F = typename Frag<CT>::type;
   using AR = typename ARaw<AM, AC>::type;
@@ -252,37 +258,45 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const int ke = min(p.K, kb + p.ksplit);
   const int nchunks = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
-  // ---- per-column epilogue vectors, requested now so that their latency
-  // hides under the main loop instead of opening the epilogue: the thread
-  // serves tile column tid % BN (SwiGLU: tid % (BN / 2)) in every epilogue.
-  // Absent vectors read as 0 through an out-of-range offset.
-  const int ecol = EM == E_SWIGLU ? nt * (BN / 2) + tid % (BN / 2) : nt * BN + tid % BN;
+  // ---- epilogue geometry: each thread owns a group of 4 consecutive output
+  // columns of the tile (SwiGLU: 4 gate columns and their 4 up columns) and
+  // visits rows er0 + i * ERS (i < EXP) of it. Its per-column vectors (4
+  // columns each, 16-byte loads) are requested now, so that their latency
+  // hides under the main loop instead of opening the epilogue; absent
+  // vectors read as 0 through an out-of-range offset.
+  constexpr int EW = EM == E_SWIGLU ? BN / 2 : BN;      // output columns of a tile
+  static_assert(EW % 4 == 0 && NT % (EW / 4) == 0, "epilogue: whole 4-column groups per thread");
+  constexpr int EC4 = EW / 4, ERS = NT / EC4, EXP = (BM + ERS - 1) / ERS;
+  const int etc = (tid % EC4) * 4;                     // first tile column of the thread's group
+  const int er0 = tid / EC4;
+  const int ecol = nt * EW + etc;                      // first output column of the group
   const bool ecok = ecol < p.N;
-  int ecol2 = ecol;   // RoPE: the partner column; SwiGLU: the up column
+  int ecol2 = ecol;   // RoPE: the partner columns; SwiGLU: the up columns
   if constexpr (EM == E_ROPE) {
     const int D = p.head_dim, hd = D >> 1;
     const int d = (ecol < p.q_cols ? ecol : ecol - p.q_cols) % D;
     ecol2 = ecol < p.q_cols + p.k_cols ? (d < hd ? ecol + hd : ecol - hd) : ecol;
   }
   if constexpr (EM == E_SWIGLU) ecol2 = p.n_half + ecol;
-  const float e_sc = bloadf(make_brsrc(p.wscale), (p.wscale && ecok) ? (uint32_t)ecol * 4u : BUF_OOB);
-  const float e_sc2 = (EM == E_ROPE || EM == E_SWIGLU)
-                          ? bloadf(make_brsrc(p.wscale), (p.wscale && ecok) ? (uint32_t)ecol2 * 4u : BUF_OOB) : 0.f;
-  const float e_bi = (EM == E_STORE || EM == E_RESID)
-                         ? bloadf(make_brsrc(p.bias), (p.bias && ecok) ? (uint32_t)ecol * 4u : BUF_OOB) : 0.f;
-  const float e_ga = EM == E_RESID ? bloadf(make_brsrc(p.gate), (p.gate && ecok) ? (uint32_t)ecol * 4u : BUF_OOB) : 0.f;
-  // QK-norm gains of the column and of its RoPE partner (a tile lies within
-  // the query columns or within the key / value columns, so the gain vector
-  // is the same for the whole workgroup)
-  float e_g1 = 1.f, e_g2 = 1.f;
+  auto vec4 = [&](const float* v, int col, bool ok) {
+    return as_f4(bload16(make_brsrc(v), (v && ok) ? (uint32_t)col * 4u : BUF_OOB));
+  };
+  const float4 e_sc = vec4(p.wscale, ecol, ecok);
+  const float4 e_sc2 = (EM == E_ROPE || EM == E_SWIGLU) ? vec4(p.wscale, ecol2, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 e_bi = (EM == E_STORE || EM == E_RESID) ? vec4(p.bias, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 e_ga = EM == E_RESID ? vec4(p.gate, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
+  // QK-norm gains of the columns and of their RoPE partners (a tile lies
+  // within the query columns or within the key / value columns, so the gain
+  // vector is the same for the whole workgroup)
+  float4 e_g1 = make_float4(1.f, 1.f, 1.f, 1.f), e_g2 = e_g1;
   if constexpr (EM == E_ROPE) {
     if (p.qk_norm) {
       const int D = p.head_dim, hd = D >> 1;
       const int d1 = (ecol < p.q_cols ? ecol : ecol - p.q_cols) % D, d2 = d1 < hd ? d1 + hd : d1 - hd;
-      const brsrc gr = make_brsrc(nt * BN < p.q_cols ? p.qn_g : p.kn_g);
+      const float* g = nt * BN < p.q_cols ? p.qn_g : p.kn_g;
       const bool ok = ecol < p.q_cols + p.k_cols;
-      e_g1 = bloadf(gr, ok ? (uint32_t)d1 * 4u : BUF_OOB);
-      e_g2 = bloadf(gr, ok ? (uint32_t)d2 * 4u : BUF_OOB);
+      e_g1 = vec4(g, d1, ok);
+      e_g2 = vec4(g, d2, ok);
     }
   }
 
@@ -305,18 +319,31 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const brsrc wr = make_brsrc(p.w);
   const int kl = (lane >> 4) * 8;               // this lane's offset inside a 32-wide k-step
 
-  // fp32 weights: fragments straight to registers (rows of this wave's n-blocks)
+  // fp32 and packed weights: fragments straight to registers (rows of this
+  // wave's n-blocks). A packed matrix (vla_pack_weights) is stored as blocks
+  // of 16 rows x 32 k ordered [row block][k block], lane l of a block holding
+  // the 8 values of row l % 16 at k 8 (l / 16) .. + 7: the block of row
+  // block nb and k-step ks starts at byte (nb * KB + ks) * 64 * 8 * ESZ.
   using BR = typename WL::raw;
   uint32_t wrow[NBW];
+  const uint32_t pk_kb = (uint32_t)(p.K + 31) / 32;      // k blocks per packed row block
 #pragma unroll
-  for (int j = 0; j < NBW; j++) wrow[j] = T::WLDS ? BUF_OOB : wrow_of((wn * NBW + j) * 16 + (lane & 15));
+  for (int j = 0; j < NBW; j++) {
+    const uint32_t w0 = T::WLDS ? BUF_OOB : wrow_of((wn * NBW + j) * 16 + (lane & 15));
+    // packed: the lane's offset inside its row block's first k block
+    wrow[j] = (!PK || w0 == BUF_OOB) ? w0 : (w0 / ((uint32_t)p.ldw * WL::ESZ) / 16u * pk_kb * 64u + (uint32_t)lane) * 8u * WL::ESZ;
+  }
   auto load_b = [&](BR (&br)[U][NBW], int kc) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       int k = kc + (u * WK + wk) * 32 + kl;
 #pragma unroll
-      for (int j = 0; j < NBW; j++)
-        br[u][j] = WL::load(wr, (k < ke && wrow[j] != BUF_OOB) ? wrow[j] + (uint32_t)k * WL::ESZ : BUF_OOB);
+      for (int j = 0; j < NBW; j++) {
+        if constexpr (PK)
+          br[u][j] = WL::load(wr, (k < ke && wrow[j] != BUF_OOB) ? wrow[j] + (uint32_t)(k >> 5) * 64u * 8u * WL::ESZ : BUF_OOB);
+        else
+          br[u][j] = WL::load(wr, (k < ke && wrow[j] != BUF_OOB) ? wrow[j] + (uint32_t)k * WL::ESZ : BUF_OOB);
+      }
     }
   };
 
@@ -525,7 +552,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   // int32 accumulation. One 16x16x64 instruction takes two of the 32-wide
   // k-steps: each lane passes its 8 codes of both steps, on the A and the B
   // side alike, so the pairs of k it multiplies are the same.
-  constexpr bool I8MMA = AM == A_I8 && std::is_same_v<WT, int8_t> && T::WLDS;
+  constexpr bool I8MMA = AM == A_I8 && std::is_same_v<WT, int8_t> && (T::WLDS || PK);
   static_assert(!I8MMA || U % 2 == 0, "int8 MFMAs take the k-steps in pairs");
   i32x4 acci[I8MMA ? MB : 1][I8MMA ? NBW : 1];
   if constexpr (I8MMA) {
@@ -552,8 +579,12 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         i32x4 bi[NBW], ai[MB];
 #pragma unroll
         for (int j = 0; j < NBW; j++) {
-          const char* wp = wbase + ((wn * NBW + j) * 16 + (lane & 15)) * WROW;
-          bi[j] = pair(wp + k0, wp + k1);
+          if constexpr (PK) {
+            bi[j] = (i32x4){(int)br[u][j].x, (int)br[u][j].y, (int)br[u + 1][j].x, (int)br[u + 1][j].y};
+          } else {
+            const char* wp = wbase + ((wn * NBW + j) * 16 + (lane & 15)) * WROW;
+            bi[j] = pair(wp + k0, wp + k1);
+          }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
@@ -620,27 +651,28 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   // activations are issued before its weights: waiting for A of chunk c+1
   // never waits for later weights. Loads past the last chunk read zeros
   // (out-of-range offsets) and are never used.
-  AR a0[GPT], a1[GPT];
+  AR a0[GPT], a1[GPT], a2[AQ == 4 ? GPT : 1], a3[AQ == 4 ? GPT : 1];
   RR r0, r1, r2, r3;
   load_a(a0, kb); load_ring(r0, kb);
   load_a(a1, kb + BK); load_ring(r1, kb + BK);
+  if constexpr (AQ == 4) load_a(a2, kb + 2 * BK);
   load_ring(r2, kb + 2 * BK);
-  // residual inputs of a small unsplit tile are fetched now as well (same
-  // element mapping as the epilogue: column tid % BN, rows tid / BN + i * NT / BN)
-  constexpr int XPT = (BM * BN + NT - 1) / NT;
-  float xpre[XPT <= 4 ? XPT : 1];
-  const bool xpref = EM == E_RESID && XPT <= 4 && p.split == 1 && !p.x_init;
-  if constexpr (EM == E_RESID && XPT <= 4) {
-    if (xpref) {
+  // residual rows of the thread's column group (every workgroup of a split
+  // tile fetches them; only the one that completes the tile uses them):
+  // requested now when they take at most 8 registers' worth of float4
+  float4 xv[EM == E_RESID ? EXP : 1];
+  auto load_x = [&]() {
+    if constexpr (EM == E_RESID) {
       const brsrc xr = make_brsrc(p.x);
-      const int n = nt * BN + tid % BN;
 #pragma unroll
-      for (int q = 0; q < XPT; q++) {
-        int m = m0 + tid / BN + q * (NT / BN);
-        xpre[q] = bloadf(xr, (m < p.M && n < p.N) ? ((uint32_t)m * p.ldx + n) * 4u : BUF_OOB);
+      for (int i = 0; i < EXP; i++) {
+        const int r = er0 + i * ERS, m = m0 + r;
+        xv[i] = as_f4(bload16(xr, (!p.x_init && r < BM && m < p.M && ecok) ? ((uint32_t)m * p.ldx + ecol) * 4u : BUF_OOB));
       }
     }
-  }
+  };
+  constexpr bool XEARLY = EM == E_RESID && EXP <= 8;
+  if constexpr (XEARLY) load_x();
   row_coeffs();
   __syncthreads();   // sRow ready
   store_a(0, a0, kb);
@@ -656,13 +688,35 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     store_ring(((C) + 1) & 1, RNEXT1);                                      \
     __syncthreads();                                                        \
   }
-  for (int c = 0; c < nchunks; c += 4) {
-    VLA_GEMM_ITER(c + 0, r0, r1, r3, a0, a1)
-    VLA_GEMM_ITER(c + 1, r1, r2, r0, a1, a0)
-    VLA_GEMM_ITER(c + 2, r2, r3, r1, a0, a1)
-    VLA_GEMM_ITER(c + 3, r3, r0, r2, a1, a0)
+  // with four activation chunks in flight (AQ = 4) they are issued three
+  // chunks ahead, like the weights: a chunk of compensated (hi + lo) rows is
+  // as large as its weights, and two in flight do not cover the latency
+#define VLA_GEMM_ITER4(C, RCUR, RNEXT1, RNEXT3, ARELOAD, ASTORE)            \
+  {                                                                         \
+    load_a(ARELOAD, kb + ((C) + 3) * BK);                                   \
+    load_ring(RNEXT3, kb + ((C) + 3) * BK);                                 \
+    if ((C) < nchunks) compute((C) & 1, RCUR);                              \
+    store_a(((C) + 1) & 1, ASTORE, kb + ((C) + 1) * BK);                    \
+    store_ring(((C) + 1) & 1, RNEXT1);                                      \
+    __syncthreads();                                                        \
+  }
+  if constexpr (AQ == 4) {
+    for (int c = 0; c < nchunks; c += 4) {
+      VLA_GEMM_ITER4(c + 0, r0, r1, r3, a3, a1)
+      VLA_GEMM_ITER4(c + 1, r1, r2, r0, a0, a2)
+      VLA_GEMM_ITER4(c + 2, r2, r3, r1, a1, a3)
+      VLA_GEMM_ITER4(c + 3, r3, r0, r2, a2, a0)
+    }
+  } else {
+    for (int c = 0; c < nchunks; c += 4) {
+      VLA_GEMM_ITER(c + 0, r0, r1, r3, a0, a1)
+      VLA_GEMM_ITER(c + 1, r1, r2, r0, a1, a0)
+      VLA_GEMM_ITER(c + 2, r2, r3, r1, a0, a1)
+      VLA_GEMM_ITER(c + 3, r3, r0, r2, a1, a0)
+    }
   }
 #undef VLA_GEMM_ITER
+#undef VLA_GEMM_ITER4
 
   if constexpr (I8MMA) {
 #pragma unroll
@@ -673,10 +727,10 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         for (int i = 0; i < 4; i++) acc[mb][j][i] = (float)acci[mb][j][i];
   }
 
-  // ---- reduce the WK wave slices into the fp32 LDS tile: every slice is
-  // written at once (slice w at sT + w * BM * TPITCH), one barrier, then the
-  // epilogue threads sum the slices of their elements in slice order
-  // (the main loop ended with a barrier: the aliased A buffers are free)
+  // ---- the accumulators into the fp32 LDS tile: every wave writes its k
+  // slice (slice w at sT + w * BM * TPITCH), one barrier, then each thread
+  // sums the slices of its elements in slice order (the main loop ended with
+  // a barrier: the aliased A buffers are free)
 #pragma unroll
   for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -687,55 +741,57 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         int cidx = (wn * NBW + j) * 16 + (lane & 15);
         sT[(size_t)wk * BM * TPITCH + r * TPITCH + cidx] = acc[mb][j][i];
       }
+  if constexpr (EM == E_RESID && !XEARLY) load_x();
+  // RoPE: cos and sin of the group's angles at each row's position, from
+  // the pass's tables [position][head_dim / 2], requested before the split-K
+  // hand-off so their latency hides under it
+  constexpr int NRT = EM == E_ROPE ? EXP : 1;
+  float4 rcs[NRT], rsn[NRT];
+  if constexpr (EM == E_ROPE) {
+    const int D = p.head_dim, hd = D >> 1;
+    const int d = (ecol < p.q_cols ? ecol : ecol - p.q_cols) % D;
+    const int fi = d < hd ? d : d - hd;
+    const bool rot = ecol < p.q_cols + p.k_cols;
+    const brsrc cosr = make_brsrc(p.rope_cos), sinr = make_brsrc(p.rope_sin);
+#pragma unroll
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS, m = m0 + r;
+      const uint32_t off = (rot && r < BM && m < p.M && ecok) ? ((uint32_t)(m + p.pos0) * hd + fi) * 4u : BUF_OOB;
+      rcs[i] = as_f4(bload16(cosr, off));
+      rsn[i] = as_f4(bload16(sinr, off));
+    }
+  }
   __syncthreads();
-  // ---- epilogue geometry: NT is a multiple of BN, so each thread keeps one
-  // column cc of the tile and visits rows r0e + i * RPT (i < XPT); per-column
-  // vectors are loaded once and every thread issues all of its loads before
-  // the first wait
-  static_assert(NT % BN == 0, "epilogue: each thread owns one column");
-  constexpr int RPT = NT / BN;
-  constexpr int XPE = (BM + RPT - 1) / RPT;     // elements per thread (threads past BM rows idle)
-  const int cc = tid % BN, r0e = tid / BN;
-  const int ncol = nt * BN + cc;                // output column (STORE / ROPE / RESID)
+  auto ld4 = [&](int r, int c) { return *reinterpret_cast<const float4*>(sT + r * TPITCH + c); };
+  auto st4 = [&](int r, int c, float4 v) { *reinterpret_cast<float4*>(sT + r * TPITCH + c) = v; };
+  constexpr int NG = EM == E_SWIGLU ? 2 : 1;          // column groups per thread (gate, up)
   if constexpr (WK > 1) {
-    // sum the K slices of this thread's elements (slice order), into slice 0;
-    // SWIGLU reads other columns, so every thread finishes before any reads
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      int r = r0e + i * RPT;
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS;
       if (r < BM) {
-        float v = sT[r * TPITCH + cc];
 #pragma unroll
-        for (int w = 1; w < WK; w++) v += sT[(size_t)w * BM * TPITCH + r * TPITCH + cc];
-        sT[r * TPITCH + cc] = v;
+        for (int g = 0; g < NG; g++) {
+          const int c = etc + g * EW;
+          float4 v = ld4(r, c);
+#pragma unroll
+          for (int w = 1; w < WK; w++) {
+            const float4 o = *reinterpret_cast<const float4*>(sT + (size_t)w * BM * TPITCH + r * TPITCH + c);
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          st4(r, c, v);
+        }
       }
     }
     __syncthreads();
   }
 
-  // residual inputs (unsplit small tiles fetched them before the main loop)
-  float xv[EM == E_RESID ? XPE : 1];
-  if constexpr (EM == E_RESID) {
-    if (!p.x_init) {
-      const brsrc xr = make_brsrc(p.x);
-#pragma unroll
-      for (int i = 0; i < XPE; i++) {
-        int m = m0 + r0e + i * RPT;
-        if (r0e + i * RPT >= BM) { xv[i] = 0.f; continue; }
-        if constexpr (XPT <= 4 && XPE <= XPT) {
-          if (xpref) { xv[i] = xpre[i]; continue; }
-        }
-        xv[i] = bloadf(xr, (m < p.M && ncol < p.N) ? ((uint32_t)m * p.ldx + ncol) * 4u : BUF_OOB);
-      }
-    }
-  }
-
   // ---- split-K: publish the partial tile; the last arriving workgroup sums
-  // all partials in split order. Partials move as 16-byte device-coherent
-  // (sc1) stores and loads, so the hand-off needs no L2 write-back or
-  // invalidate; the counter increment is issued only after every thread's
-  // stores have completed. The reducer requests up to four splits' partials
-  // at once.
+  // all partials in split order (its own from LDS). Partials move as 16-byte
+  // device-coherent (sc1) stores and loads, so the hand-off needs no L2
+  // write-back or invalidate; the counter increment is issued only after
+  // every thread's stores have completed. The reducer requests the other
+  // splits' partials several at a time (as many as 64 registers hold).
   if (p.split > 1) {
     constexpr int C4 = BN / 4;                  // float4 per tile row
     constexpr int PF4 = (BM * C4 + NT - 1) / NT;
@@ -745,31 +801,33 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < PF4; i++) {
       const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4;
-      if (r < BM) {
-        const float4 v = *reinterpret_cast<const float4*>(sT + r * TPITCH + c4 * 4);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), pw, (uint32_t)(r * BN + c4 * 4) * 4u, 0, CP_SC1);
-      }
+      if (r < BM)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, ld4(r, c4 * 4)), pw, (uint32_t)(r * BN + c4 * 4) * 4u, 0, CP_SC1);
     }
     if (tile_arrive(p.cnt_tile + tile, p.split, sFlag)) return;
     const brsrc pr = make_brsrc(p.part + (size_t)tile * (BM * BN));
     float4 sum[PF4];
 #pragma unroll
     for (int i = 0; i < PF4; i++) sum[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q0 = 0; q0 < p.split; q0 += 4) {
-      uint4 v[4][PF4];
+    constexpr int QR = 16 / PF4 >= 8 ? 8 : 16 / PF4 >= 1 ? 16 / PF4 : 1;   // partials per round
+    for (int q0 = 0; q0 < p.split; q0 += QR) {
+      uint4 v[QR][PF4];
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < QR; j++)
 #pragma unroll
         for (int i = 0; i < PF4; i++) {
-          const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4;
-          v[j][i] = bload16<CP_SC1>(pr, (q0 + j < p.split && r < BM) ? (uint32_t)((q0 + j) * tstride + r * BN + c4 * 4) * 4u : BUF_OOB);
+          const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4, q = q0 + j;
+          v[j][i] = bload16<CP_SC1>(pr, (q < p.split && q != s && r < BM) ? (uint32_t)(q * tstride + r * BN + c4 * 4) * 4u
+                                                                          : BUF_OOB);
         }
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < QR; j++)
         if (q0 + j < p.split) {
 #pragma unroll
           for (int i = 0; i < PF4; i++) {
-            const float4 f = as_f4(v[j][i]);
+            const int e4 = tid + i * NT;
+            const float4 f = q0 + j == s ? (e4 / C4 < BM ? ld4(e4 / C4, (e4 % C4) * 4) : make_float4(0.f, 0.f, 0.f, 0.f))
+                                         : as_f4(v[j][i]);
             sum[i].x += f.x; sum[i].y += f.y; sum[i].z += f.z; sum[i].w += f.w;
           }
         }
@@ -777,57 +835,89 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < PF4; i++) {
       const int e4 = tid + i * NT, r = e4 / C4, c4 = e4 % C4;
-      if (r < BM) *reinterpret_cast<float4*>(sT + r * TPITCH + c4 * 4) = sum[i];
+      if (r < BM) st4(r, c4 * 4, sum[i]);
     }
     if (tid == 0) p.cnt_tile[tile] = 0u;
     __syncthreads();
   }
 
-  // ---- W8A8: the per-row scale of the activation codes (the weights'
-  // per-column scale is applied by the epilogues)
+  auto mul4 = [](float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); };
+  auto fma4 = [](float4 a, float4 b, float4 c) {
+    return make_float4(a.x * b.x + c.x, a.y * b.y + c.y, a.z * b.z + c.z, a.w * b.w + c.w);
+  };
+  const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f), zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  // W8A8: the per-row scale of the activation codes, applied to the tile in
+  // place (RoPE partners and QK-norm statistics read other threads' columns;
+  // the weights' per-column scales are applied below)
   if constexpr (a_codes(AM)) {
     const brsrc sr = make_brsrc(p.a_scale);
-    float rsc[XPE];
+    float rsc[EXP];
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      const int r = r0e + i * RPT, m = m0 + r;
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS, m = m0 + r;
       rsc[i] = bloadf(sr, (r < BM && m < p.M) ? (uint32_t)m * 4u : BUF_OOB);
     }
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      const int r = r0e + i * RPT;
-      if (r < BM) sT[r * TPITCH + cc] *= rsc[i];
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS;
+      if (r < BM) {
+#pragma unroll
+        for (int g = 0; g < NG; g++) st4(r, etc + g * EW, mul4(ld4(r, etc + g * EW), make_float4(rsc[i], rsc[i], rsc[i], rsc[i])));
+      }
     }
     __syncthreads();
   }
-
-  // ---- epilogues (outputs through buffer stores: 32-bit element offsets)
-  const brsrc cr = make_brsrc(p.c);
-  auto put = [&](uint32_t idx, float v) {
-    if (p.c_f32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), cr, idx * 4u, 0, 0);
-    else __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), cr, idx * 2u, 0, 0);
-  };
-  if constexpr (EM == E_STORE) {
-    const bool cok = ncol < p.N;
-    const float sc = p.wscale ? e_sc : 1.f;
+  // ---- the thread's elements: rows er0 + i * ERS, columns etc .. etc + 3
+  // (and the up columns EW + etc for SwiGLU), every LDS read issued before
+  // the arithmetic and every store after it
+  float4 y[NG][EXP];
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      int r = r0e + i * RPT, m = m0 + r;
-      if (r >= BM || m >= p.M || !cok) continue;
-      float v = sT[r * TPITCH + cc] * sc + e_bi;
-      if (p.act == ACT_GELU) v = gelu_erf(v);
-      else if (p.act == ACT_SILU) v = silu(v);
-      put((uint32_t)m * p.ldc + ncol, v);
+  for (int i = 0; i < EXP; i++) {
+    const int r = er0 + i * ERS;
+#pragma unroll
+    for (int g = 0; g < NG; g++) y[g][i] = r < BM ? ld4(r, etc + g * EW) : zero4;
+  }
+  // outputs through buffer stores (32-bit element offsets): 4 values as one
+  // 16-byte float32 store or one 8-byte bf16 store (ldc and the columns are
+  // multiples of 4, checked by the launcher)
+  const brsrc cr = make_brsrc(p.c);
+  auto put4 = [&](uint32_t idx, float4 v) {
+    if (p.c_f32) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), cr, idx * 4u, 0, 0);
+    } else {
+      const uint2 u = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, u), cr, idx * 2u, 0, 0);
     }
+  };
+  auto row_ok = [&](int i) { const int r = er0 + i * ERS; return r < BM && m0 + r < p.M && ecok; };
+
+  if constexpr (EM == E_STORE) {
+    const float4 sc = p.wscale ? e_sc : one4;
+#pragma unroll
+    for (int i = 0; i < EXP; i++) y[0][i] = fma4(y[0][i], sc, e_bi);
+    auto act4 = [&](auto f) {
+#pragma unroll
+      for (int i = 0; i < EXP; i++) y[0][i] = make_float4(f(y[0][i].x), f(y[0][i].y), f(y[0][i].z), f(y[0][i].w));
+    };
+    if (p.act == ACT_GELU) act4([](float z) { return gelu_erf(z); });
+    else if (p.act == ACT_SILU) act4([](float z) { return silu(z); });
+#pragma unroll
+    for (int i = 0; i < EXP; i++)
+      if (row_ok(i)) put4((uint32_t)(m0 + er0 + i * ERS) * p.ldc + ecol, y[0][i]);
   } else if constexpr (EM == E_ROPE) {
     const int D = p.head_dim, hd = D >> 1;
-    const bool cok = ncol < p.N;
-    const bool rot = ncol < p.q_cols + p.k_cols;
-    const int d = (ncol < p.q_cols ? ncol : ncol - p.q_cols) % D;
-    const int fi = d < hd ? d : d - hd;
-    const int pc = d < hd ? cc + hd : cc - hd;           // partner column in the tile
-    float sc = p.wscale ? e_sc : 1.f;
-    float sc2 = p.wscale ? e_sc2 : 1.f;
+    const bool rot = ecol < p.q_cols + p.k_cols;
+    const int d = (ecol < p.q_cols ? ecol : ecol - p.q_cols) % D;
+    const int ptc = d < hd ? etc + hd : etc - hd;       // partner columns in the tile
+    float4 sc = p.wscale ? e_sc : one4, sc2 = p.wscale ? e_sc2 : one4;
+    const float4* cs = rcs;
+    const float4* sn = rsn;
+    float4 y2[EXP];
+#pragma unroll
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS;
+      y2[i] = (rot && r < BM) ? ld4(r, ptc) : zero4;
+    }
     // QK-norm: the inverse RMS of every (row, head) of the tile over the
     // head's D columns, from the scaled values; four threads per pair, then
     // a butterfly over them. The tile's heads start at multiples of D.
@@ -835,17 +925,22 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     const int nht = BN / D;
     if (p.qk_norm) {
       if (p.wscale) {
+        __syncthreads();   // every thread has read its partner columns
 #pragma unroll
-        for (int i = 0; i < XPE; i++) {
-          const int r = r0e + i * RPT;
-          if (r < BM) sT[r * TPITCH + cc] *= e_sc;
+        for (int i = 0; i < EXP; i++) {
+          const int r = er0 + i * ERS;
+          if (r < BM) st4(r, etc, mul4(y[0][i], e_sc));
         }
         __syncthreads();
-        sc = sc2 = 1.f;
+#pragma unroll
+        for (int i = 0; i < EXP; i++) {
+          const int r = er0 + i * ERS;
+          y[0][i] = r < BM ? ld4(r, etc) : zero4;
+          y2[i] = (rot && r < BM) ? ld4(r, ptc) : zero4;
+        }
+        sc = sc2 = one4;
       }
       const int j4 = tid & 3;
-      // head_dim as a compile-time constant: the float4 reads of a row are
-      // unrolled and issued together
       auto rows = [&](auto dc) {
         constexpr int DD = decltype(dc)::value, NH = BN / DD, NF = DD / 16;
         for (int pr = tid >> 2; pr < BM * NH; pr += NT / 4) {
@@ -865,78 +960,60 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       else rows(std::integral_constant<int, 64>{});
       __syncthreads();
     }
-    // the thread's rows step by RPT positions: the first angle and the step
-    // come from a double-precision frequency and product reduced to [-pi, pi]
-    // in double (a float frequency times a position of several hundred is off
-    // by up to 1e-4 rad), each next angle by a rotation through the step
-    const double theta = pow((double)p.rope_base, -2.0 * (double)fi / (double)D);
-    auto sincos_reduced = [](double a, float* sn_, float* cs_) {
-      a -= rint(a * (0.5 / M_PI)) * (2.0 * M_PI);
-      sincosf((float)a, sn_, cs_);
-    };
-    float cs, sn, cd, sd;
-    sincos_reduced((double)(m0 + r0e + p.pos0) * theta, &sn, &cs);
-    sincos_reduced((double)RPT * theta, &sd, &cd);
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      int r = r0e + i * RPT, m = m0 + r;
-      if (r < BM && m < p.M && cok) {
-        float v = sT[r * TPITCH + cc] * sc;
-        if (rot) {
-          float v2 = sT[r * TPITCH + pc] * sc2;
-          if (p.qk_norm) {
-            const float qs = qinv[r * nht + cc / D];
-            v *= qs * e_g1;
-            v2 *= qs * e_g2;
-          }
-          v = d < hd ? v * cs - v2 * sn : v * cs + v2 * sn;
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS;
+      float4 v = mul4(y[0][i], sc);
+      if (rot) {
+        float4 v2 = mul4(y2[i], sc2);
+        if (p.qk_norm) {
+          const float qs = r < BM ? qinv[r * nht + etc / D] : 0.f;
+          v = mul4(v, make_float4(qs * e_g1.x, qs * e_g1.y, qs * e_g1.z, qs * e_g1.w));
+          v2 = mul4(v2, make_float4(qs * e_g2.x, qs * e_g2.y, qs * e_g2.z, qs * e_g2.w));
         }
-        put((uint32_t)m * p.ldc + ncol, v);
+        const float sgn = d < hd ? -1.f : 1.f;          // first half: v cos - v2 sin; second: v cos + v2 sin
+        v = make_float4(v.x * cs[i].x + sgn * v2.x * sn[i].x, v.y * cs[i].y + sgn * v2.y * sn[i].y,
+                        v.z * cs[i].z + sgn * v2.z * sn[i].z, v.w * cs[i].w + sgn * v2.w * sn[i].w);
       }
-      const float c2 = cs * cd - sn * sd;
-      sn = sn * cd + cs * sd;
-      cs = c2;
+      if (row_ok(i)) put4((uint32_t)(m0 + r) * p.ldc + ecol, v);
     }
   } else if constexpr (EM == E_SWIGLU) {
-    constexpr int BO = BN / 2;
-    static_assert(NT % BO == 0, "swiglu epilogue: each thread owns one column");
-    constexpr int RPO = NT / BO, XPO = (BM + RPO - 1) / RPO;
-    const int co = tid % BO, r0o = tid / BO;
-    const int n = nt * BO + co;
-    const bool cok = n < p.N;
-    const float sg = p.wscale ? e_sc : 1.f;
-    const float su = p.wscale ? e_sc2 : 1.f;
+    const float4 sg = p.wscale ? e_sc : one4, su = p.wscale ? e_sc2 : one4;
     const brsrc clr = make_brsrc(p.c_lo);
 #pragma unroll
-    for (int i = 0; i < XPO; i++) {
-      int r = r0o + i * RPO, m = m0 + r;
-      if (r >= BM || m >= p.M || !cok) continue;
-      float gv = sT[r * TPITCH + co] * sg, uv = sT[r * TPITCH + BO + co] * su;
-      float a = silu(gv) * uv;
-      const uint32_t idx = (uint32_t)m * p.ldc + n;
-      put(idx, a);
-      if (!p.c_f32 && p.c_lo) __builtin_amdgcn_raw_buffer_store_b16(f2bf(a - bf2f(f2bf(a))), clr, idx * 2u, 0, 0);
+    for (int i = 0; i < EXP; i++) {
+      const float4 gv = mul4(y[0][i], sg), uv = mul4(y[1][i], su);
+      const float4 a = make_float4(silu(gv.x) * uv.x, silu(gv.y) * uv.y, silu(gv.z) * uv.z, silu(gv.w) * uv.w);
+      if (!row_ok(i)) continue;
+      const uint32_t idx = (uint32_t)(m0 + er0 + i * ERS) * p.ldc + ecol;
+      put4(idx, a);
+      if (!p.c_f32 && p.c_lo) {
+        auto lo = [](float v) { return v - bf2f(f2bf(v)); };
+        const uint2 u = make_uint2(pack_bf2(lo(a.x), lo(a.y)), pack_bf2(lo(a.z), lo(a.w)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, u), clr, idx * 2u, 0, 0);
+      }
     }
   } else if constexpr (EM == E_RESID) {
-    const bool cok = ncol < p.N;
-    const float sc = p.wscale ? e_sc : 1.f;
-    const float bi = e_bi;
-    const float ga = p.gate ? e_ga : 1.f;
+    const float4 sc = p.wscale ? e_sc : one4;
+    const float4 ga = p.gate ? e_ga : one4;
     const brsrc xw = make_brsrc(p.x);
+    const brsrc ar = make_brsrc(p.addrow);
+    float4 add[EXP];
 #pragma unroll
-    for (int i = 0; i < XPE; i++) {
-      int r = r0e + i * RPT, m = m0 + r;
-      if (r >= BM || m >= p.M || !cok) continue;
-      float v = (sT[r * TPITCH + cc] * sc + bi) * ga;
-      float xn;
-      if (p.x_init) {
-        xn = v;
-        if (p.addrow) xn += p.addrow[(size_t)(m % p.addrow_rows) * p.N + ncol];
-      } else {
-        xn = xv[i] + v;
-      }
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(xn), xw, ((uint32_t)m * p.ldx + ncol) * 4u, 0, 0);
-      sT[r * TPITCH + cc] = xn;
+    for (int i = 0; i < EXP; i++) {
+      const int m = m0 + er0 + i * ERS;
+      add[i] = as_f4(bload16(ar, (p.x_init && p.addrow && row_ok(i))
+                                      ? ((uint32_t)(m % p.addrow_rows) * p.N + ecol) * 4u : BUF_OOB));
+    }
+#pragma unroll
+    for (int i = 0; i < EXP; i++) {
+      const int r = er0 + i * ERS, m = m0 + r;
+      const float4 v = mul4(fma4(y[0][i], sc, e_bi), ga);
+      const float4 base = p.x_init ? add[i] : xv[i];
+      const float4 xn = make_float4(base.x + v.x, base.y + v.y, base.z + v.z, base.w + v.w);
+      if (!row_ok(i)) continue;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, xn), xw, ((uint32_t)m * p.ldx + ecol) * 4u, 0, 0);
+      st4(r, etc, xn);
     }
     // moments of this tile's columns per row (mean, sum of squared
     // deviations), merged by the stream's next reader: TPRM consecutive

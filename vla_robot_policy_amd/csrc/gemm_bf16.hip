@@ -2,7 +2,7 @@
 #include "gemm_inst.h"
 
 namespace vla {
-bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out) {
+bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_NARROW(uint16_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_CASE(uint16_t, __bf16, A_BF16, E_STORE, 1, 4, 1, 1)
   VLA_GEMM_WIDE(uint16_t, __bf16, A_BF16, E_STORE)
@@ -15,6 +15,23 @@ bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, in
   VLA_GEMM_NARROW_AC(uint16_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_PATCH, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_MERGE, E_STORE)
+  // compensated MLP tiles: down at 65-112 rows with one k-step per wave and
+  // four activation chunks in flight; the packed gate/up and down tiles
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 7, 4, 2, 1, 1, 1, 4, 0)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 7, 4, 2, 1, 1, 1, 4, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 1, 4, 2, 2, 1, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 4, 4, 2, 2, 1, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 7, 4, 2, 2, 1, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 8, 4, 2, 2, 1, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 1, 1, 4, 1, 2, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 4, 4, 2, 1, 2, 1, 2, 1)
+  VLA_GEMM_BACKBONE_M7(uint16_t, 0)
+  VLA_GEMM_BACKBONE_M7(uint16_t, 1)
+  VLA_GEMM_PACKED_ROWS(uint16_t, 1)
+  VLA_GEMM_PACKED_ROWS(uint16_t, 4)
+  VLA_GEMM_PACKED_ROWS(uint16_t, 7)
+  VLA_GEMM_PACKED_ROWS(uint16_t, 8)
+  VLA_GEMM_PACKED_RESID(uint16_t)
   return false;
 }
 }  // namespace vla

@@ -9,7 +9,7 @@
 #include "gemm_inst.h"
 
 namespace vla {
-bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out) {
+bool gemm_lookup_fp8(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_NARROW(uint8_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_CASE(uint8_t, __bf16, A_BF16, E_STORE, 1, 4, 1, 1)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_BF16, E_STORE)
@@ -21,6 +21,13 @@ bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int
   VLA_GEMM_WIDE(uint8_t, __bf16, A_FP8, E_ROPE)
   VLA_GEMM_WIDE(uint8_t, __bf16, A_FP8, E_SWIGLU)
   VLA_GEMM_NARROW(uint8_t, __bf16, A_FP8, E_RESID)
+  VLA_GEMM_BACKBONE_M7(uint8_t, 0)
+  VLA_GEMM_BACKBONE_M7(uint8_t, 1)
+  VLA_GEMM_PACKED_ROWS(uint8_t, 1)
+  VLA_GEMM_PACKED_ROWS(uint8_t, 4)
+  VLA_GEMM_PACKED_ROWS(uint8_t, 7)
+  VLA_GEMM_PACKED_ROWS(uint8_t, 8)
+  VLA_GEMM_PACKED_RESID(uint8_t)
   return false;
 }
 }  // namespace vla

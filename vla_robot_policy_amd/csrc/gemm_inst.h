@@ -3,13 +3,16 @@
 #include "gemm.h"
 #include "kernels.h"
 
-#define VLA_GEMM_CASE_X(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, UV, ACV)                                     \
-  if (am == AMV && em == EMV && mb == MBV && wn == WNV && wk == WKV && nbw == NBWV && u == UV && ac == ACV) { \
-    out->fn = (const void*)&k_gemm<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV, ACV>;                          \
-    out->smem = GemmTile<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV, ACV>::SMEM;                              \
-    out->threads = GemmTile<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV, ACV>::THREADS;                        \
-    return true;                                                                                             \
+#define VLA_GEMM_CASE_F(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, UV, ACV, AQV, PKV)                               \
+  if (g.am == AMV && g.em == EMV && g.mb == MBV && g.wn == WNV && g.wk == WKV && g.nbw == NBWV && g.u == UV &&      \
+      g.ac == ACV && g.aq == AQV && g.pk == PKV) {                                                                  \
+    out->fn = (const void*)&k_gemm<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV, ACV, AQV, PKV>;                      \
+    out->smem = GemmTile<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV, ACV, AQV, PKV>::SMEM;                          \
+    out->threads = GemmTile<WT, CT, MBV, WNV, WKV, NBWV, AMV, EMV, UV, ACV, AQV, PKV>::THREADS;                    \
+    return true;                                                                                                   \
   }
+#define VLA_GEMM_CASE_X(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, UV, ACV) \
+  VLA_GEMM_CASE_F(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, UV, ACV, 2, 0)
 #define VLA_GEMM_CASE(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV) VLA_GEMM_CASE_X(WT, CT, AMV, EMV, MBV, WNV, WKV, NBWV, 4, 0)
 
 // narrow tiles (16 columns for 16-row tiles, else 64) and wide tiles (128 columns)
@@ -36,3 +39,21 @@
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 4, 4, 2, 2, 1, 1) \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 7, 4, 2, 2, 1, 1) \
   VLA_GEMM_CASE_X(WT, CT, AMV, EMV, 8, 4, 2, 2, 1, 1)
+
+// Backbone tiles of the 65-112-row shapes (measured at 104 rows: QKV 21.1 ->
+// 20.1 us, O projection 18.5 -> 16.0, down 37.2 -> 32.2; with packed
+// weights 18.9, 15.5 and 30.7, gate/up 49.9 -> 47.0), and the packed-weight
+// counterparts of every backbone tile (PK = 1) for all row tilings.
+#define VLA_GEMM_BACKBONE_M7(WT, PKV)                                            \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_ROPE, 7, 8, 1, 1, 2, 0, 4, PKV)        \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 7, 2, 2, 1, 2, 0, 2, PKV)
+#define VLA_GEMM_PACKED_ROWS(WT, MBV)                                            \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_ROPE, MBV, 8, 1, 1, 4, 0, 2, 1)        \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_SWIGLU, MBV, 8, 1, 1, 4, 0, 2, 1)      \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, MBV, 4, 1, 1, 4, 0, 2, 1)
+// the other residual tiles of the row-major picks, so that packed weights
+// give the same tiles and the same bits: 16 rows over four k-waves, and two
+// k-waves of 32 columns for 17..64 rows
+#define VLA_GEMM_PACKED_RESID(WT)                                                \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 1, 1, 4, 1, 4, 0, 2, 1)         \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 4, 2, 2, 1, 2, 0, 2, 1)

@@ -6,7 +6,7 @@
 #include "gemm_inst.h"
 
 namespace vla {
-bool gemm_lookup_int8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out) {
+bool gemm_lookup_int8(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_NARROW(int8_t, __bf16, A_BF16, E_STORE)
   VLA_GEMM_CASE(int8_t, __bf16, A_BF16, E_STORE, 1, 4, 1, 1)
   VLA_GEMM_WIDE(int8_t, __bf16, A_BF16, E_STORE)
@@ -18,6 +18,13 @@ bool gemm_lookup_int8(int am, int em, int mb, int wn, int wk, int nbw, int u, in
   VLA_GEMM_WIDE(int8_t, __bf16, A_I8, E_ROPE)
   VLA_GEMM_WIDE(int8_t, __bf16, A_I8, E_SWIGLU)
   VLA_GEMM_NARROW(int8_t, __bf16, A_I8, E_RESID)
+  VLA_GEMM_BACKBONE_M7(int8_t, 0)
+  VLA_GEMM_BACKBONE_M7(int8_t, 1)
+  VLA_GEMM_PACKED_ROWS(int8_t, 1)
+  VLA_GEMM_PACKED_ROWS(int8_t, 4)
+  VLA_GEMM_PACKED_ROWS(int8_t, 7)
+  VLA_GEMM_PACKED_ROWS(int8_t, 8)
+  VLA_GEMM_PACKED_RESID(int8_t)
   return false;
 }
 }  // namespace vla

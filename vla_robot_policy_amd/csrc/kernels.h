@@ -11,11 +11,15 @@ struct KernelRef {
 };
 
 // GEMM: one lookup per weight type; am / em from gemm.h, tile (mb, wn, wk,
-// nbw), u k-steps per chunk, ac = compensated (hi + lo) bf16 activations.
-bool gemm_lookup_f32(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
-bool gemm_lookup_bf16(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
-bool gemm_lookup_fp8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
-bool gemm_lookup_int8(int am, int em, int mb, int wn, int wk, int nbw, int u, int ac, KernelRef* out);
+// nbw), u k-steps per chunk, ac = compensated (hi + lo) bf16 activations,
+// aq = activation chunks in flight (2 or 4), pk = packed weights.
+struct GemmPick {
+  int am, em, mb, wn, wk, nbw, u, ac, aq, pk;
+};
+bool gemm_lookup_f32(const GemmPick& g, KernelRef* out);
+bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out);
+bool gemm_lookup_fp8(const GemmPick& g, KernelRef* out);
+bool gemm_lookup_int8(const GemmPick& g, KernelRef* out);
 
 // Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
 // the attention kernel and the merge of its key-split partials
@@ -26,6 +30,8 @@ const void* k_fill_ref();
 const void* k_stage_rows_ref();
 const void* k_rmsnorm_out_ref();
 const void* k_time_embed_ref();
+const void* k_rope_table_ref();
+const void* k_pack_weights_ref();
 const void* k_norm_rows_ref();
 const void* k_quant_rows_ref();
 const void* k_convert_rows_ref();

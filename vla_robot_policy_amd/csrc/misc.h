@@ -111,6 +111,54 @@ __global__ __launch_bounds__(256) void k_rmsnorm_out(const float* x, int ldx, in
   }
 }
 
+// Packed weight layout (vla_pack_weights): a row-major W [N, K] of esz-byte
+// elements (2: bf16, 1: E4M3FN or int8 codes) becomes blocks of 16 rows x 32
+// columns, ordered [row block][column block]; inside a block, lane l of a
+// wave holds the 8 elements of row l % 16 at columns 8 (l / 16) .. + 7, the
+// B operand fragment of one 16x16x32 MFMA step, so a wave-wide load of one
+// block is contiguous (1 KB for bf16). Rows and columns beyond N and K are
+// zero. One thread per 8-element lane chunk.
+__global__ __launch_bounds__(256) void k_pack_weights(const uint8_t* w, int N, int K, int ldw, int esz, uint8_t* out) {
+  const int KB = (K + 31) / 32, NB = (N + 15) / 16;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (size_t)NB * KB * 64) return;
+  const int lane = (int)(e % 64);
+  const size_t blk = e / 64;
+  const int kb = (int)(blk % KB), nb = (int)(blk / KB);
+  const int row = nb * 16 + lane % 16, k0 = kb * 32 + (lane / 16) * 8;
+  uint8_t v[16];
+#pragma unroll
+  for (int j = 0; j < 8; j++)
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      if (b >= esz) continue;
+      const int k = k0 + j;
+      v[j * esz + b] = (row < N && k < K) ? w[((size_t)row * ldw + k) * esz + b] : (uint8_t)0;
+    }
+  uint8_t* o = out + e * 8 * esz;
+  for (int i = 0; i < 8 * esz; i++) o[i] = v[i];
+}
+
+// RoPE tables of a pass: cs[pos][i] = cos(pos theta_i), sn[pos][i] =
+// sin(pos theta_i), theta_i = base^(-2i / D), i < D / 2, pos < S (half-split
+// rotation of the pairs (i, i + D/2)). The frequency and the angle are formed
+// in double and reduced to [-pi, pi] before the float sine and cosine: a
+// float frequency times a position of several hundred is off by up to 1e-4
+// radians.
+__global__ __launch_bounds__(256) void k_rope_table(float* cs, float* sn, int S, int D, float base) {
+  const int hd = D / 2;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= S * hd) return;
+  const int pos = e / hd, i = e % hd;
+  const double theta = pow((double)base, -2.0 * (double)i / (double)D);
+  double a = (double)pos * theta;
+  a -= rint(a * (0.5 / M_PI)) * (2.0 * M_PI);
+  float s, c;
+  sincosf((float)a, &s, &c);
+  cs[e] = c;
+  sn[e] = s;
+}
+
 // Sinusoidal features of the sampler's time grid t_k = k / K (k < K): row k
 // is [cos(s t_k w_i) | sin(s t_k w_i)], w_i = base^(-i / half), i < half, in
 // bf16 [K][2 half]. The frequency and the argument are formed in double and

@@ -22,8 +22,12 @@ _NP_RAW = {"f32": np.float32, "bf16": np.int16, "fp8": np.uint8, "int8": np.int8
 
 
 class DeviceWeights:
-    def __init__(self, cfg, tensors, device: str = "cuda:0", threads: int = 8, keep_host: bool = True):
+    def __init__(self, cfg, tensors, device: str = "cuda:0", threads: int = 8, keep_host: bool = True,
+                 packed: bool = False):
         self.cfg = cfg
+        # backbone Linears in the packed layout of vla_pack_weights (bf16 / 8-bit
+        # weights with bf16 activations only)
+        self.packed = packed
         self.keep_host = keep_host
         self.t = tensors
         self.device = torch.device(device)
@@ -60,6 +64,21 @@ class DeviceWeights:
             s = self.up_array(np.concatenate([t.scale for t in ts])).data_ptr()
         return w, s
 
+    def up_rows_packed(self, names: Sequence[str]):
+        """up_rows, then the matrix repacked on the device by vla_pack_weights
+        (the row-major upload is dropped once the packing kernel has run)."""
+        w, s = self.up_rows(names)
+        src = next(t for t in reversed(self.keep) if t.data_ptr() == w)
+        n = sum(self.t[x].data.shape[0] for x in names)
+        k = self.t[names[0]].data.shape[1]
+        code = lib.DTYPE_CODE[self.cfg.wdtype]
+        out = torch.empty(lib.vla_packed_bytes(code, n, k), dtype=torch.uint8, device=self.device)
+        lib.check(lib.vla_pack_weights(code, src, n, k, k, out, torch.cuda.current_stream(self.device).cuda_stream))
+        torch.cuda.synchronize(self.device)
+        self.keep = [t for t in self.keep if t is not src]
+        self.keep.append(out)
+        return out.data_ptr(), s
+
     def up_vec(self, names: Sequence[str]) -> int:
         return self.up_array(np.concatenate([self.t[n].data for n in names]).astype(np.float32)).data_ptr()
 
@@ -82,7 +101,9 @@ class DeviceWeights:
         bc = lib.BlockCfg(hidden=b.hidden, n_q_heads=b.n_q_heads, n_kv_heads=b.n_kv_heads, head_dim=b.head_dim,
                           intermediate=b.intermediate, rope_base=b.rope_base, eps=b.eps,
                           wdtype=lib.DTYPE_CODE[cfg.wdtype], adtype=lib.VLA_F32 if cfg.wdtype == "f32" else lib.VLA_BF16,
-                          flags=(lib.VLA_BLOCK_QK_NORM if b.qk_norm else 0) | (lib.VLA_BLOCK_A8 if b.a8 else 0))
+                          flags=(lib.VLA_BLOCK_QK_NORM if b.qk_norm else 0) | (lib.VLA_BLOCK_A8 if b.a8 else 0)
+                          | (lib.VLA_BLOCK_PACKED if self.packed else 0))
+        rows = self.up_rows_packed if self.packed else self.up_rows
         layers = (lib.BlockWeights * cfg.layers)()
         for l in range(cfg.layers):
             p = f"llm.{l}."
@@ -90,11 +111,11 @@ class DeviceWeights:
             self.prefetch([p + n for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "wg", "wu", "wd") + extra])
             L = layers[l]
             L.attn_norm = self.up(p + "attn_norm")
-            L.w_qkv, L.s_qkv = self.up_rows([p + "wq", p + "wk", p + "wv"])
-            L.w_o, L.s_o = self.up_rows([p + "wo"])
+            L.w_qkv, L.s_qkv = rows([p + "wq", p + "wk", p + "wv"])
+            L.w_o, L.s_o = rows([p + "wo"])
             L.mlp_norm = self.up(p + "mlp_norm")
-            L.w_gate_up, L.s_gate_up = self.up_rows([p + "wg", p + "wu"])
-            L.w_down, L.s_down = self.up_rows([p + "wd"])
+            L.w_gate_up, L.s_gate_up = rows([p + "wg", p + "wu"])
+            L.w_down, L.s_down = rows([p + "wd"])
             if b.qk_norm:
                 L.q_norm = self.up(p + "q_norm")
                 L.k_norm = self.up(p + "k_norm")

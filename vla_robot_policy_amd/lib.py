@@ -25,6 +25,7 @@ VLA_F32, VLA_BF16, VLA_FP8_E4M3, VLA_INT8 = 0, 1, 2, 3
 DTYPE_CODE = {"f32": VLA_F32, "bf16": VLA_BF16, "fp8": VLA_FP8_E4M3, "int8": VLA_INT8}
 VLA_BLOCK_QK_NORM = 1
 VLA_BLOCK_A8 = 2
+VLA_BLOCK_PACKED = 4
 VLA_STEP_GRAPH_CACHE = 8
 
 
@@ -116,6 +117,8 @@ def load() -> C.CDLL:
         "vla_block_forward": (S, [POINTER(BlockCfg), POINTER(BlockWeights), c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
         "vla_block_workspace_bytes": (c_size_t, [POINTER(BlockCfg), c_int32]),
         "vla_block_forward_static": (S, [POINTER(BlockCfg), POINTER(BlockWeights), c_void_p, c_void_p, c_int32, c_void_p]),
+        "vla_packed_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+        "vla_pack_weights": (S, [c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
         "vla_backbone_prefill": (S, [POINTER(Backbone), c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
         "vla_backbone_workspace_bytes": (c_size_t, [POINTER(Backbone), c_int32]),
         "vla_flow_euler_sample": (S, [POINTER(Dit), c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
@@ -196,6 +199,14 @@ VLA_STATIC_SCRATCH_BYTES = 64 << 20
 
 def vla_block_forward_static(cfg: BlockCfg, w: BlockWeights, x_in, x_out, seq: int, stream: int = 0) -> int:
     return load().vla_block_forward_static(C.byref(cfg), C.byref(w), _p(x_in), _p(x_out), seq, stream)
+
+
+def vla_packed_bytes(wdtype: int, n: int, k: int) -> int:
+    return load().vla_packed_bytes(wdtype, n, k)
+
+
+def vla_pack_weights(wdtype: int, w, n: int, k: int, ldw: int, packed, stream: int = 0) -> int:
+    return load().vla_pack_weights(wdtype, _p(w), n, k, ldw, _p(packed), stream)
 
 
 def vla_backbone_workspace_bytes(bb: Backbone, seq: int) -> int:
