@@ -733,7 +733,7 @@ struct DitState {
   // the layer kernel's flagged words (two bf16 + a flag each): QKV output
   // and cross-attention query, one block
   uint2* fw = nullptr; size_t fw_words = 0;
-  uint2* fqkv = nullptr; uint2* fq = nullptr;
+  uint2* fqkv = nullptr; uint2* fq = nullptr; uint2* fdp = nullptr;
   uint16_t* u = nullptr;   // modulated LayerNorm rows of the launch-per-operation path (bf16)
   bool stack = false;
   int G = 0;
@@ -770,10 +770,10 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.stack = dit_stack_ok(cf, n, s.G);
   s.spin = dit_spin_limit();
   if (s.stack) {
-    const size_t wq = (size_t)n * 3 * D / 2, wd = (size_t)n * D / 2;
-    s.fw_words = wq + wd;
+    const size_t wq = (size_t)n * 3 * D / 2, wd = (size_t)n * D / 2, wp = (size_t)ds_dpart_words(D, cf.mlp);
+    s.fw_words = wq + wd + wp;
     s.fw = c.take<uint2>(s.fw_words);
-    s.fqkv = s.fw; s.fq = s.fqkv + wq;
+    s.fqkv = s.fw; s.fq = s.fqkv + wq; s.fdp = s.fq + wd;
     s.aos = c.take<uint16_t>((size_t)n * D);
   } else {
     s.qkv = c.take<uint16_t>((size_t)n * 3 * D);
@@ -784,12 +784,10 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.derr = c.status;      // word 0 of the workspace's status block
   s.u = !s.stack && cf.wdtype != VLA_F32 ? c.take<uint16_t>((size_t)n * D) : nullptr;
   if (s.stack) {
-    // phase and tile counters of the layer kernel live in the shared counter
-    // array (every kernel leaves its counters at zero); slice partials in the
-    // split-K scratch
+    // phase counters of the layer kernel live in the shared counter array
+    // (every kernel leaves its counters at zero)
     const int nclr = ds_counter_words(D);
     c.need_tiles = std::max(c.need_tiles, (size_t)nclr);
-    c.need_part = std::max(c.need_part, (size_t)(cf.mlp / D) * (D / 16) * 256);
     c.label = "dit.clear";
     unsigned z = 0;
     VLA_TRY(launch(c, k_fill_ref(), dim3((nclr + 255) / 256), dim3(256), 0, {arg(c.cnt_tile), arg(z), arg(nclr)}));
@@ -913,7 +911,7 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = scaled8(wt) ? ss[i] : nullptr; a.b[i] = bs[i]; }
         const bool last_launch = k == K - 1 && l == L - 1;
         a.wq_next = last_launch ? nullptr : d.layers[(l + 1) % L].w_qkv;
-        a.part = c.part; a.cnt = c.cnt_tile; a.err = s.derr; a.spin = s.spin;
+        a.dpart = s.fdp; a.cnt = c.cnt_tile; a.err = s.derr; a.spin = s.spin;
         VLA_TRY(launch(c, lk.fn, dim3(s.G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
         continue;
       }

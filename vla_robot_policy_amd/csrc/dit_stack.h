@@ -59,10 +59,11 @@ constexpr unsigned DS_SPIN = 1u << 17;   // polls before a wait gives up (a heal
 // Phase counters: phases before DOWN count into DS_NC slots 256 bytes apart
 // (workgroup w adds to slot w % DS_NC), so arrivals do not serialise on one
 // address; DOWN (few arrivals) uses one counter, whose last arrival resets
-// all of them. Tile counters of the DOWN slices follow.
+// all of them.
 constexpr int DS_NC = 16, DS_CSTRIDE = 64;
-constexpr int DS_TILE0 = DP_N * DS_NC * DS_CSTRIDE;
-__host__ __device__ constexpr int ds_counter_words(int D) { return DS_TILE0 + D / 16; }
+__host__ __device__ constexpr int ds_counter_words(int) { return DP_N * DS_NC * DS_CSTRIDE; }
+// flagged words of the DOWN slice partials: slices 1 .. of every tile
+__host__ __device__ constexpr int ds_dpart_words(int D, int mlp) { return (mlp / (2 * D) - 1) * (D / 16) * 256; }
 
 struct DitLayerArgs {
   int n, D, H, hd, mlp, C;        // action rows (<= 16), width, heads, head dim, MLP width, context tokens
@@ -89,7 +90,7 @@ struct DitLayerArgs {
   const void* wq_next;            // the next launch's QKV weights (NULL: none), read ahead into the memory-side cache
   const float* s[6];              // per-row fp8 scales (NULL for bf16)
   const float* b[6];              // biases
-  float* part;                    // DOWN slice partials [slices][D/16][256]
+  uint2* dpart;                   // DOWN partials of slices 1..: flagged words [slices - 1][D/16][256]
   unsigned* cnt;                  // ds_counter_words(D) counters (zero between launches)
   int* err;                       // set to 1 when a wait times out
   unsigned spin;                  // polls before a wait gives up (DS_SPIN unless the host asks for fewer)
@@ -163,14 +164,17 @@ __device__ __forceinline__ int ds_base(const DitLayerArgs& a, int ph) {
 }
 
 // Wait until the DS_NC slots of a phase counter sum to target (wave 0
-// polls, one slot per lane; the workgroup follows). False after DS_SPIN polls.
+// polls, one slot per lane; the workgroup follows). False after `spin`
+// polls. One read is in flight at a time: the barrier that follows waits
+// for every outstanding read, so reads issued ahead only delay the exit
+// (measured: 3.5 us per layer with four in flight).
 __device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, unsigned spin, int* sflag) {
   if (threadIdx.x < 64) {
+    static_assert(DS_NC == 16, "the phase counter slots are one DPP row");
     const int lane = threadIdx.x;
     unsigned spins = 0;
     bool ok = true;
     while (true) {
-      static_assert(DS_NC == 16, "the phase counter slots are one DPP row");
       unsigned v = lane < DS_NC ? __hip_atomic_load(slots + lane * DS_CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       // exact: counts stay far below 2^24
       const unsigned tot = (unsigned)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum((float)v)), 0));
@@ -182,6 +186,28 @@ __device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, 
   }
   __syncthreads();
   return sflag[0] != 0;
+}
+
+// Read bytes [i, i + 1) / n of the next launch's QKV weights and drop them
+// (the memory-side cache keeps them for that launch's first phase).
+template <typename WT, int D>
+__device__ __forceinline__ void ds_prefetch_qkv_share(const DitLayerArgs& a, int i, int n) {
+  const size_t total = (size_t)3 * D * D * sizeof(WT);
+  const size_t share = (total / n + 4095) & ~(size_t)4095;
+  const size_t b0 = (size_t)i * share, b1 = b0 + share < total ? b0 + share : total;
+  const brsrc nr = make_brsrc(a.wq_next);
+  uint32_t acc = 0;
+  for (size_t off = b0 + (size_t)threadIdx.x * 16; off < b1; off += (size_t)DS_THREADS * 16 * 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const size_t o = off + (size_t)k * DS_THREADS * 16;
+      v[k] = bload16(nr, o < b1 ? (uint32_t)o : BUF_OOB);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) acc ^= v[k].x;
+  }
+  if (acc == 0x9E3779B9u) a.err[1] = 0;   // keeps the loads; practically never taken
 }
 
 // ---------------------------------------------------------------- weight units
@@ -538,8 +564,8 @@ __host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_a(D) +
 // together with the UP weights (it is idle long before UP starts), so its
 // DOWN phase does not begin with a weight fetch queued ahead of its wait.
 template <typename WT, int D, int PH>
-__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float* red, int* sflag, int& finished_tiles,
-                                         typename DsW<WT>::raw (&wdown)[DS_WSLOTS], bool& have_down) {
+__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, char* rA, float* red, int* sflag,
+                                         int& finished_tiles, typename DsW<WT>::raw (&wdown)[DS_WSLOTS], bool& have_down) {
   using WR = typename DsW<WT>::raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x, G = gridDim.x;
@@ -555,30 +581,14 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
   constexpr int MAXU = 2 * NB * NSW <= DS_WSLOTS ? 2 : 1;
   const int U = ds_units(a, PH);
   const int first = ((wg - ds_base(a, PH)) % G + G) % G;
-  if constexpr (PH == DP_DOWN) {
-    // workgroups without a DOWN unit read the next launch's QKV weights,
-    // so that its first phase finds them in the memory-side cache
-    if (first >= U && a.wq_next) {
-      const size_t total = (size_t)3 * D * D * sizeof(WT);
-      const int idle = G - U, i = first - U;
-      const size_t share = (total / idle + 4095) & ~(size_t)4095;
-      const size_t b0 = (size_t)i * share, b1 = b0 + share < total ? b0 + share : total;
-      const brsrc nr = make_brsrc(a.wq_next);
-      uint32_t acc = 0;
-      for (size_t off = b0 + (size_t)tid * 16; off < b1; off += (size_t)DS_THREADS * 16 * 8) {
-        uint4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const size_t o = off + (size_t)k * DS_THREADS * 16;
-          v[k] = bload16(nr, o < b1 ? (uint32_t)o : BUF_OOB);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; k++) acc ^= v[k].x;
-      }
-      if (acc == 0x9E3779B9u) a.err[1] = 0;   // keeps the loads; practically never taken
+  if (first >= U) {                                  // no work in this phase
+    if constexpr (PH == DP_UP) {
+      // nor in DOWN: read a share of the next launch's QKV weights
+      const int fd = ((wg - ds_base(a, DP_DOWN)) % G + G) % G, ud = ds_units(a, DP_DOWN);
+      if (fd >= ud && a.wq_next) ds_prefetch_qkv_share<WT, D>(a, fd - ud, G - ud);
     }
+    return true;
   }
-  if (first >= U) return true;                       // no work in this phase
   const int nu = (U - first + G - 1) / G;           // at most MAXU (checked by the launcher)
   constexpr bool is_att = PH == DP_SAATT || PH == DP_CAATT;
 
@@ -593,9 +603,11 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
     for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
     return false;
   };
-  // every phase but QKV and the attentions waits for the previous phase's counter
+  // every phase but QKV and the attentions waits for the previous phase's
+  // counter; after a failed earlier launch of the run, the first wait leaves
   auto wait_prev = [&]() -> bool {
-    if (PH == 0 || ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), a.spin, sflag)) return true;
+    if (PH == 0) return true;
+    if (!prev_err && ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), a.spin, sflag)) return true;
     return fail();
   };
   // LayerNorm geometry: wave w normalises rows 4w .. 4w + 3; lane l holds
@@ -622,6 +634,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         st16[2 * 16 * DS_DP + c * 16 + r] = 0;
       }
     }
+    if (prev_err) return fail();
     // ---- one head per unit
     for (int j = 0; j < nu; j++) {
       const int hh = first + j * G;
@@ -684,6 +697,43 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         gv[k] = as_f4(bload16(mr, cg < D / 4 ? (uint32_t)(D + 4 * cg) * 4u : BUF_OOB));
       }
     }
+    // per-column epilogue vectors of each unit (bias, 8-bit weight scale,
+    // residual gate): inputs of the launch, requested before anything waits
+    float pb[MAXU][NB], ps[MAXU][NB], pg[MAXU][NB];
+    {
+      const int wi = ds_unit(a, PH, first).wi;
+      const bool scaled = a.s[wi] != nullptr;
+      const brsrc br = make_brsrc(a.b[wi]), sr = make_brsrc(a.s[wi]);
+      const brsrc gr = make_brsrc(a.mod + (size_t)(PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8) * D);
+#pragma unroll
+      for (int j = 0; j < MAXU; j++) {
+        const DsUnit d = ds_unit(a, PH, first + j * G);
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+          const int col = d.n0 + b * 16 + (tid & 15);
+          const uint32_t off = (j < nu && col < d.N) ? (uint32_t)col * 4u : BUF_OOB;
+          pb[j][b] = bloadf(br, off);
+          ps[j][b] = scaled ? bloadf(sr, off) : 1.f;
+          pg[j][b] = norm ? 0.f : bloadf(gr, off);
+        }
+      }
+    }
+    // LayerNorm input rows: wave w holds rows 4w .. 4w + 3, lane l the float4
+    // column groups l + 64 k. QKV's input is final at launch, so its rows are
+    // requested ahead of its weights (loads complete in order); the other
+    // LayerNorms read theirs after the wait.
+    float4 xv[norm ? 4 : 1][norm ? KG : 1];
+    auto load_x = [&]() {
+      const brsrc xr = make_brsrc(PH == DP_QKV ? a.x_in : PH == DP_CAQ ? a.x1 : a.x2);
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+        for (int k = 0; k < KG; k++) {
+          const int r = 4 * wave + rr, cg = lane + 64 * k;
+          xv[rr][k] = as_f4(bload16(xr, (cg < D / 4 && r < n) ? ((uint32_t)r * D + 4 * cg) * 4u : BUF_OOB));
+        }
+    };
+    if constexpr (PH == DP_QKV) load_x();
     WR wreg[DS_WSLOTS];
     auto& wuse = [&]() -> WR (&)[DS_WSLOTS] {
       if constexpr (PH == DP_DOWN) return wdown;
@@ -695,15 +745,23 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         if (nu > 1) ds_load_unit<WT, NB * NSW, NB, NSW, KST>(a, ds_unit(a, PH, first + G), wuse);
     }
     if constexpr (PH == DP_UP) {
-      const int fd = ((wg - ds_base(a, DP_DOWN)) % G + G) % G;
-      if (fd < ds_units(a, DP_DOWN)) {
+      const int fd = ((wg - ds_base(a, DP_DOWN)) % G + G) % G, ud = ds_units(a, DP_DOWN);
+      if (fd < ud) {
         constexpr int KSTD = 2 * D / 32, NSWD = (KSTD + 3) / 4;
         ds_load_unit<WT, 0, 1, NSWD, KSTD>(a, ds_unit(a, DP_DOWN, fd), wdown);
         have_down = true;
+      } else if (a.wq_next) {
+        // a workgroup with UP but no DOWN work is idle from here to UP's
+        // wait: it reads its share of the next launch's QKV weights, so that
+        // launch's first phase finds them in the memory-side cache (HBM is
+        // quiet here; the UP weights were requested earlier and, needed only
+        // after the cross-attention, have time to arrive)
+        ds_prefetch_qkv_share<WT, D>(a, fd - ud, G - ud);
       }
     }
     if (!wait_prev()) return false;
     // ---- the A operand [16][KW] (bf16) in region A
+    float xpre[MAXU];
     if constexpr (!norm) {
       // SAO, CAO: the attention output; DOWN: the unit's slice of h (a
       // workgroup's units share their k range). Rows beyond n are zeros.
@@ -719,6 +777,14 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         const int e8 = tid + i * DS_THREADS, r = (e8 * 8) / KW, c = (e8 * 8) % KW;
         av[i] = bload16(sr, (e8 < 16 * KW / 8 && r < n) ? ((uint32_t)r * lds + d0.k0 + c) * 2u : BUF_OOB);
       }
+      // the residual input at this thread's epilogue element of each unit,
+      // requested with the A operand rather than after the product
+      const brsrc xr = make_brsrc(PH == DP_SAO ? a.x_in : PH == DP_CAO ? a.x1 : a.x2);
+#pragma unroll
+      for (int j = 0; j < MAXU; j++) {
+        const int r = tid >> 4, col = ds_unit(a, PH, first + j * G).n0 + (tid & 15);
+        xpre[j] = bloadf(xr, (j < nu && r < n) ? (uint32_t)(r * D + col) * 4u : BUF_OOB);
+      }
 #pragma unroll
       for (int i = 0; i < AS; i++) {
         const int e8 = tid + i * DS_THREADS, r = (e8 * 8) / KW, c = (e8 * 8) % KW;
@@ -729,15 +795,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
       // two-pass mean / variance of each of the wave's 4 rows (wave-wide
       // sums), then u = LN(x)(1 + scale) + shift in bf16 into LDS. Rows
       // beyond n read zeros and give finite values that no output uses.
-      const brsrc xr = make_brsrc(PH == DP_QKV ? a.x_in : PH == DP_CAQ ? a.x1 : a.x2);
-      float4 xv[4][KG];
-#pragma unroll
-      for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-        for (int k = 0; k < KG; k++) {
-          const int r = 4 * wave + rr, cg = lane + 64 * k;
-          xv[rr][k] = as_f4(bload16(xr, (cg < D / 4 && r < n) ? ((uint32_t)r * D + 4 * cg) * 4u : BUF_OOB));
-        }
+      if constexpr (PH != DP_QKV) load_x();
       float mean[4], rstd[4];
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
@@ -783,6 +841,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         }
       }
     }
+    bool timed_out = false;   // a DOWN partial never arrived
     auto unit = [&](int j) {
       const DsUnit d = ds_unit(a, PH, first + j * G);
       constexpr int apitch = KW * 2 + 16;
@@ -803,29 +862,29 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
         const int col = d.n0 + b * 16 + cc;
         float v = red[(0 * NB + b) * 256 + tid] + red[(1 * NB + b) * 256 + tid] + red[(2 * NB + b) * 256 + tid] +
                   red[(3 * NB + b) * 256 + tid];
-        const float* ws = a.s[d.wi];
-        if (ws) v *= ws[col];
+        if (a.s[d.wi]) v *= ps[j][b];
         if (PH == DP_DOWN) {
-          // publish this slice's partial; the tile's last slice sums them in slice order
+          // slices 1.. publish their partial as flagged words and are done;
+          // the tile's slice-0 unit adds them to its own in slice order
           const int tile = d.n0 / 16, slice = d.k0 / KW, nsl = a.mlp / KW;
-          st_sc1_f32(a.part + ((size_t)slice * ntile + tile) * 256 + tid, v);
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();
-          if (tid == 0) {
-            unsigned old = __hip_atomic_fetch_add(a.cnt + DS_TILE0 + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sflag[1] = old == (unsigned)(nsl - 1);
+          const brsrc pr = make_brsrc(a.dpart);
+          if (slice > 0) {
+            st_fw(pr, (uint32_t)((slice - 1) * ntile + tile) * 256u + tid, __float_as_uint(v), a.flag);
+            return;
           }
-          __syncthreads();
-          if (!sflag[1]) return;
-          const brsrc pr = make_brsrc(a.part);
-          float sum = 0.f;
-          for (int q = 0; q < nsl; q++) sum += bloadf<CP_SC1>(pr, (uint32_t)(((size_t)q * ntile + tile) * 256 + tid) * 4u);
-          v = sum;
-          // device-scope store, like every other counter update
-          if (tid == 0) __hip_atomic_store(a.cnt + DS_TILE0 + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int q = 1; q < nsl; q++) {
+            const uint32_t off = ((uint32_t)((q - 1) * ntile + tile) * 256u + tid) * 8u;
+            uint2 w = bload8<CP_SC1>(pr, off);
+            for (unsigned spins = 0; w.y != a.flag; spins++) {
+              if (spins >= a.spin) { timed_out = true; break; }
+              __builtin_amdgcn_s_sleep(1);
+              w = bload8<CP_SC1>(pr, off);
+            }
+            v += __uint_as_float(w.x);
+          }
           finished_tiles++;
         }
-        v += a.b[d.wi][col];
+        v += pb[j][b];
         if (PH == DP_QKV || PH == DP_CAQ || PH == DP_UP) {
           if (PH == DP_UP) v = gelu_erf(v);
           const uint32_t bits = f2bf(v);
@@ -843,12 +902,9 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
           }
         } else {
           // gated residual: x += gate * v
-          const int gi = PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8;
           if (r < n) {
-            const float* xs = PH == DP_SAO ? a.x_in : PH == DP_CAO ? a.x1 : a.x2;
             float* xd = PH == DP_SAO ? a.x1 : PH == DP_CAO ? a.x2 : a.x_out;
-            float xo = bloadf(make_brsrc(xs), (uint32_t)(r * D + col) * 4u);
-            st_sc1_f32(xd + (size_t)r * D + col, xo + a.mod[(size_t)gi * D + col] * v);
+            st_sc1_f32(xd + (size_t)r * D + col, xpre[j] + pg[j][b] * v);
           }
         }
       }
@@ -856,6 +912,8 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, char* rA, float*
     unit(0);
     if constexpr (MAXU > 1)
       if (nu > 1) unit(1);
+    if constexpr (PH == DP_DOWN)
+      if (!ds_all(!timed_out, sflag)) return fail();
   }
   // ---- count this phase's finished units once every store has completed
   // (QKV and CAQ write flagged words and do not count)
@@ -894,24 +952,20 @@ __global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
   typename DsW<WT>::raw wdown[DS_WSLOTS];
   bool have_down = false;
 
-  // a failed earlier launch of this run: poison the stream and leave at once
-  if (tid == 0) {
-    sflag[0] = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sflag[2] = 0;
-  }
+  // A failed earlier launch of this run: its flag is requested now and
+  // acted on at this launch's first wait, where the workgroup poisons the
+  // stream and leaves (QKV waits for nothing, so it needs no check).
+  if (tid == 0) sflag[2] = 0;
   __syncthreads();
-  if (sflag[0]) {
-    for (int e = wg * DS_THREADS + tid; e < a.n * D; e += G * DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
-    return;
-  }
-  if (!ds_phase<WT, D, DP_QKV>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_SAATT>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_SAO>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_CAQ>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_CAATT>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_CAO>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_UP>(a, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  ds_phase<WT, D, DP_DOWN>(a, rA, red, sflag, finished_tiles, wdown, have_down);
+  const int prev_err = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!ds_phase<WT, D, DP_QKV>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_SAATT>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_SAO>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_CAQ>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_CAATT>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_CAO>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  if (!ds_phase<WT, D, DP_UP>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
+  ds_phase<WT, D, DP_DOWN>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down);
 }
 
 }  // namespace vla
