@@ -849,8 +849,13 @@ vla_status dit_conditioning(Ctx& c, const vla_dit& d, const DitIO& io, DitState&
   return VLA_OK;
 }
 
-// Cross-attention K/V of every layer from a context (one launch).
-vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16_t* ckv) {
+// Keys per row of the transposed context values the layer kernel reads.
+int dit_vt_pitch(int C) { return (C + 31) / 32 * 32; }
+size_t dit_vt_elems(const vla_dit_cfg& cf, int C) { return (size_t)cf.layers * cf.hidden * dit_vt_pitch(C); }
+
+// Cross-attention K/V of every layer from a context (one launch), and for
+// the layer kernel (vt not null) the values transposed.
+vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16_t* ckv, uint16_t* vt) {
   const vla_dit_cfg& cf = d.cfg;
   const int D = cf.hidden, L = cf.layers;
   c.label = "dit.cross_kv";
@@ -859,7 +864,13 @@ vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16
   a.a = ctx; a.lda = cf.ctx_dim;
   a.w = d.w_ckv; a.ldw = cf.ctx_dim; a.wscale = d.s_ckv; a.bias = d.b_ckv;
   a.c = ckv; a.ldc = L * 2 * D;
-  return gemm(c, a, {cf.wdtype, A_BF16, E_STORE});
+  VLA_TRY(gemm(c, a, {cf.wdtype, A_BF16, E_STORE}));
+  if (!vt) return VLA_OK;
+  c.label = "dit.cross_vt";
+  const int Cp = dit_vt_pitch(C);
+  const size_t nt = (size_t)L * (Cp / 8) * D;
+  return launch(c, k_ctx_vt_ref(), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0,
+                {arg((const uint16_t*)ckv), arg(C), arg(L), arg(D), arg(Cp), arg(vt)});
 }
 
 // a_0 = x0 -> x = a_0 W_in^T + b_in (+ row statistics)
@@ -876,8 +887,10 @@ vla_status dit_in_proj(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   return launch(c, tail.fn, dim3(io.n), dim3(256), (size_t)(cf.hidden + io.A) * sizeof(float), {arg(t)});
 }
 
-// Euler steps k0 .. k1-1 of the K-step sampler, cross-attending to `ckv`.
-vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, const uint16_t* ckv, int k0, int k1) {
+// Euler steps k0 .. k1-1 of the K-step sampler, cross-attending to `ckv`
+// (the layer kernel: keys from ckv, values from their transpose vt).
+vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, const uint16_t* ckv, const uint16_t* vt,
+                     int k0, int k1) {
   const vla_dit_cfg& cf = d.cfg;
   const int D = cf.hidden, L = cf.layers, K = io.K, n = io.n, A = io.A, C = io.ctx_len;
   const int wt = cf.wdtype;
@@ -903,7 +916,8 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         a.x_in = s.xb[l & 1]; a.x1 = s.x1; a.x2 = s.x2; a.x_out = s.xb[(l + 1) & 1];
         a.qkv = s.fqkv; a.q = s.fq; a.aos = s.aos; a.aoc = s.ao; a.h = s.h;
         a.flag = 1u + (unsigned)(k * L + l);   // increasing over the run, whose start cleared the words
-        a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.cv = ckv ? ckv + (size_t)l * 2 * D + D : nullptr; a.ldc = L * 2 * D;
+        a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.ldc = L * 2 * D;
+        a.ldvt = dit_vt_pitch(C); a.cv = vt ? vt + (size_t)l * D * a.ldvt : nullptr;
         a.mod = m;
         const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
         const float* ss[6] = {w.s_qkv, w.s_o, w.s_cq, w.s_co, w.s_up, w.s_down};
@@ -1027,10 +1041,11 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
   DitState s;
   VLA_TRY(dit_begin(c, d, io, s));
   uint16_t* ckv = c.take<uint16_t>((size_t)io.ctx_len * d.cfg.layers * 2 * d.cfg.hidden);
+  uint16_t* vt = s.stack ? c.take<uint16_t>(dit_vt_elems(d.cfg, io.ctx_len)) : nullptr;
   VLA_TRY(dit_conditioning(c, d, io, s));
-  VLA_TRY(dit_cross_kv(c, d, io.ctx, io.ctx_len, ckv));
+  VLA_TRY(dit_cross_kv(c, d, io.ctx, io.ctx_len, ckv, vt));
   VLA_TRY(dit_in_proj(c, d, io, s));
-  return dit_steps(c, d, io, s, ckv, 0, io.K);
+  return dit_steps(c, d, io, s, ckv, vt, 0, io.K);
 }
 
 // ------------------------------------------------------------------ ViT
@@ -1482,10 +1497,11 @@ vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) 
   VLA_TRY(vlm_sched(c, P, sh, ctx, S));
   io.ctx = ctx;
   uint16_t* ckv = c.take<uint16_t>((size_t)io.ctx_len * P.dit.cfg.layers * 2 * P.dit.cfg.hidden);
+  uint16_t* vt = ds.stack ? c.take<uint16_t>(dit_vt_elems(P.dit.cfg, io.ctx_len)) : nullptr;
   VLA_TRY(dit_conditioning(c, P.dit, io, ds));
-  VLA_TRY(dit_cross_kv(c, P.dit, io.ctx, io.ctx_len, ckv));
+  VLA_TRY(dit_cross_kv(c, P.dit, io.ctx, io.ctx_len, ckv, vt));
   VLA_TRY(dit_in_proj(c, P.dit, io, ds));
-  return dit_steps(c, P.dit, io, ds, ckv, 0, io.K);
+  return dit_steps(c, P.dit, io, ds, ckv, vt, 0, io.K);
 }
 
 // One V-AEFusion cycle on two contexts. `cv` (the caller's stream) runs the
@@ -1505,6 +1521,11 @@ vla_status fused_sched(Ctx& cv, Ctx& ca, const vla_step_plan& P, const vla_step_
   uint16_t* ckv2 = cv.take<uint16_t>(2 * ckv_elems);
   uint16_t* cur = ckv2 ? ckv2 + (size_t)parity * ckv_elems : nullptr;
   uint16_t* prev = ckv2 ? ckv2 + (size_t)(parity ^ 1) * ckv_elems : nullptr;
+  // the layer kernel's transposed values, double-buffered the same way
+  const size_t vt_elems = dit_stack_ok(cf, sh.chunk, cu_count()) ? dit_vt_elems(cf, C) : 0;
+  uint16_t* vt2 = vt_elems ? cv.take<uint16_t>(2 * vt_elems) : nullptr;
+  uint16_t* cur_vt = vt2 ? vt2 + (size_t)parity * vt_elems : nullptr;
+  uint16_t* prev_vt = vt2 ? vt2 + (size_t)(parity ^ 1) * vt_elems : nullptr;
   const bool live = !cv.plan;
   if (live) {
     VLA_HIP(hipEventRecord(ev->fork, cv.st));
@@ -1524,17 +1545,17 @@ vla_status fused_sched(Ctx& cv, Ctx& ca, const vla_step_plan& P, const vla_step_
     while (g > 1 && dit_stack_ok(cf, sh.chunk, g - 16)) g -= 16;
     ds.G = g;
   }
-  VLA_TRY(dit_steps(ca, P.dit, io, ds, prev, 0, n_stale));
+  VLA_TRY(dit_steps(ca, P.dit, io, ds, prev, prev_vt, 0, n_stale));
   ds.G = g_all;
   uint16_t* ctx = nullptr;
   int S = 0;
   VLA_TRY(vlm_sched(cv, P, sh, ctx, S));
-  VLA_TRY(dit_cross_kv(cv, P.dit, ctx, S, cur));
+  VLA_TRY(dit_cross_kv(cv, P.dit, ctx, S, cur, cur_vt));
   if (live) {
     VLA_HIP(hipEventRecord(ev->ctx_ready, cv.st));
     VLA_HIP(hipStreamWaitEvent(ca.st, ev->ctx_ready, 0));
   }
-  VLA_TRY(dit_steps(ca, P.dit, io, ds, cur, n_stale, sh.steps));
+  VLA_TRY(dit_steps(ca, P.dit, io, ds, cur, cur_vt, n_stale, sh.steps));
   if (live) {
     VLA_HIP(hipEventRecord(ev->done, ca.st));
     VLA_HIP(hipStreamWaitEvent(cv.st, ev->done, 0));

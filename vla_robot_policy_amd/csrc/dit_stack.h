@@ -82,9 +82,9 @@ struct DitLayerArgs {
   uint16_t* aos;                  // [n, D] self-attention output
   uint16_t* aoc;                  // [n, D] cross-attention output
   uint16_t* h;                    // [n, mlp] GELU output
-  const uint16_t* ck;             // this layer's context keys, row pitch ldc
-  const uint16_t* cv;             // this layer's context values
-  int ldc;
+  const uint16_t* ck;             // this layer's context keys [C][D], row pitch ldc
+  const uint16_t* cv;             // this layer's context values transposed: [D][ldvt], zero beyond C keys
+  int ldc, ldvt;                  // ldvt: a multiple of 32, >= C
   const float* mod;               // [9][D] modulation of this layer and step
   const void* w[6];               // qkv, o, cq, co, up, down: [N, K] row-major
   const void* wq_next;            // the next launch's QKV weights (NULL: none), read ahead into the memory-side cache
@@ -302,23 +302,30 @@ __device__ __forceinline__ void ds_mma(const char* rA, int apitch, const typenam
 // ---------------------------------------------------------------- attention of one head (<= 16 queries)
 // Cross-attention: the four waves take interleaved blocks of 32 context
 // keys: S^T = K Q^T per block, online softmax per lane, O^T = V^T P^T. Q
-// comes from LDS (staged from its flagged words); the K and V fragments are
-// loaded straight from memory (K rows are contiguous in the head dimension;
-// a V^T fragment gathers 8 keys of one column with 2-byte loads, in the key
-// order the lane's P values already have). With more than one block the
-// waves' partial (max, sum, O) are combined in LDS; with one block wave 0
-// writes the output itself (device-coherent bf16 stores).
+// comes from LDS (staged from its flagged words); the K and V^T fragments
+// are 16-byte loads straight from memory: K rows are contiguous in the head
+// dimension, and the values are stored transposed (one row of keys per head
+// column). The K rows of a block are taken in the order that leaves lane
+// group g the scores of keys 8g .. 8g + 7 (keys 8g + i from the first
+// 16-row half, 8g + 4 + i from the second), so the lane's P fragment and the
+// V^T fragment it multiplies cover 8 consecutive keys. With more than one
+// block the waves' partial (max, sum, O) are combined in LDS; with one block
+// wave 0 writes the output itself (device-coherent bf16 stores).
+
+// Key of row r (< 16) of half hb of a block: lane group r / 4 holds rows
+// 4 (r / 4) .. + 3 of each half.
+__device__ __forceinline__ int ds_key_of_row(int hb, int r) { return 8 * (r >> 2) + 4 * hb + (r & 3); }
 
 // The fragments of one 32-key block: K for the two 16-key halves and the
 // three 32-wide steps of the (padded) head dimension; V^T for the six
-// 16-column blocks, 8 keys each (keys 4g..4g+3 and 16+4g..16+4g+3 of lane
-// group g).
+// 16-column blocks, keys 8g .. 8g + 7 of lane group g.
 struct DsAttFr {
   uint4 k[2][DS_DP / 32];
-  uint16_t v[DS_DP / 16][8];
+  uint4 v[DS_DP / 16];
 };
 
-__device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nblk, int nk, int ldkv, int hd, DsAttFr& f) {
+__device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nblk, int nk, int ldk, int ldvt, int hd,
+                                             DsAttFr& f) {
   const int lane = threadIdx.x & 63, qn = lane & 15, grp = lane >> 4;
   const int kb = blk * DS_KB;
   const bool live = blk < nblk;
@@ -326,18 +333,16 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nb
   for (int hb = 0; hb < 2; hb++)
 #pragma unroll
     for (int ds = 0; ds < DS_DP / 32; ds++) {
-      const int key = kb + hb * 16 + qn, d = ds * 32 + grp * 8;
-      const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldkv + d) * 2u : BUF_OOB;
+      const int key = kb + ds_key_of_row(hb, qn), d = ds * 32 + grp * 8;
+      const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldk + d) * 2u : BUF_OOB;
       f.k[hb][ds] = bload16(kr, off);
     }
+  // keys up to the block's end lie within the zero-padded rows of V^T
 #pragma unroll
-  for (int db = 0; db < DS_DP / 16; db++)
-#pragma unroll
-    for (int t = 0; t < 8; t++) {
-      const int key = kb + (t < 4 ? 4 * grp + t : 16 + 4 * grp + (t - 4)), d = db * 16 + qn;
-      const uint32_t off = (live && key < nk && d < hd) ? ((uint32_t)key * ldkv + d) * 2u : BUF_OOB;
-      f.v[db][t] = bload2(vr, off);
-    }
+  for (int db = 0; db < DS_DP / 16; db++) {
+    const int d = db * 16 + qn;
+    f.v[db] = bload16(vr, (live && d < hd) ? ((uint32_t)d * ldvt + kb + 8 * grp) * 2u : BUF_OOB);
+  }
 }
 
 // `f` holds this wave's first block when `have0` (requested before the
@@ -345,19 +350,19 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nb
 // computed.
 // qs: Q rows [16][DS_DP] bf16 in LDS, zero beyond nq rows and hd columns;
 // the output goes to columns oc .. oc + hd of O's rows (ldo bf16 columns).
-__device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp, const uint16_t* Vp, int ldkv, uint16_t* O,
-                                             int ldo, int oc, int nq, int nk, int hd, float scale_log2, char* lds_o,
-                                             DsAttFr& f, bool have0) {
+__device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp, const uint16_t* Vt, int ldk, int ldvt,
+                                             uint16_t* O, int ldo, int oc, int nq, int nk, int hd, float scale_log2,
+                                             char* lds_o, DsAttFr& f, bool have0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qn = lane & 15, grp = lane >> 4;
-  const brsrc kr = make_brsrc(Kp), vr = make_brsrc(Vp), orr = make_brsrc(O);
+  const brsrc kr = make_brsrc(Kp), vr = make_brsrc(Vt), orr = make_brsrc(O);
   const int nblk = (nk + DS_KB - 1) / DS_KB;
 
   FragBF16 qf[DS_DP / 32];
 #pragma unroll
   for (int ds = 0; ds < DS_DP / 32; ds++)
     qf[ds].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qs + (qn * DS_DP + ds * 32 + grp * 8) * 2));
-  if (!have0) ds_att_frags(kr, vr, wave, nblk, nk, ldkv, hd, f);
+  if (!have0) ds_att_frags(kr, vr, wave, nblk, nk, ldk, ldvt, hd, f);
   f32x4 oacc[DS_DP / 16];
 #pragma unroll
   for (int i = 0; i < DS_DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -374,15 +379,8 @@ __device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp,
 #pragma unroll
         for (int ds = 0; ds < DS_DP / 32; ds++) kf[hb][ds].v = __builtin_bit_cast(bf16x8, f.k[hb][ds]);
 #pragma unroll
-      for (int db = 0; db < DS_DP / 16; db++) {
-        uint4 u;
-        u.x = (uint32_t)f.v[db][0] | ((uint32_t)f.v[db][1] << 16);
-        u.y = (uint32_t)f.v[db][2] | ((uint32_t)f.v[db][3] << 16);
-        u.z = (uint32_t)f.v[db][4] | ((uint32_t)f.v[db][5] << 16);
-        u.w = (uint32_t)f.v[db][6] | ((uint32_t)f.v[db][7] << 16);
-        vf[db].v = __builtin_bit_cast(bf16x8, u);
-      }
-      if (r0 + 4 < nblk) ds_att_frags(kr, vr, blk + 4, nblk, nk, ldkv, hd, f);
+      for (int db = 0; db < DS_DP / 16; db++) vf[db].v = __builtin_bit_cast(bf16x8, f.v[db]);
+      if (r0 + 4 < nblk) ds_att_frags(kr, vr, blk + 4, nblk, nk, ldk, ldvt, hd, f);
       f32x4 s[2];
 #pragma unroll
       for (int hb = 0; hb < 2; hb++) {
@@ -395,7 +393,7 @@ __device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp,
       for (int hb = 0; hb < 2; hb++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          int j = kb + hb * 16 + grp * 4 + i;
+          const int j = kb + ds_key_of_row(hb, grp * 4 + i);
           float v = j < nk ? s[hb][i] * scale_log2 : -INFINITY;
           s[hb][i] = v;
           bmax = fmaxf(bmax, v);
@@ -618,8 +616,8 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
     DsAttFr f;
     constexpr bool cross = PH == DP_CAATT;
     if (cross)
-      ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + first * a.hd), wave,
-                   (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.hd, f);
+      ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + (size_t)first * a.hd * a.ldvt), wave,
+                   (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.ldvt, a.hd, f);
     // the head's rows are staged after the partials: Q [16][DS_DP], and for
     // the self-attention K [16][DS_DP] and V^T [DS_DP][16], zero beyond n
     // rows (written by the poll) and hd columns (written here)
@@ -680,7 +678,8 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       }
       if (!ds_all(ok, sflag)) return fail();
       if constexpr (cross)
-        ds_attention(st, a.ck + hh * hd, a.cv + hh * hd, a.ldc, a.aoc, D, hh * hd, n, a.C, hd, a.scale_log2, rA, f, j == 0);
+        ds_attention(st, a.ck + hh * hd, a.cv + (size_t)hh * hd * a.ldvt, a.ldc, a.ldvt, a.aoc, D, hh * hd, n, a.C, hd,
+                     a.scale_log2, rA, f, j == 0);
       else
         ds_self_att(st, a.aos, D, hh * hd, n, hd, a.scale_log2);
     }

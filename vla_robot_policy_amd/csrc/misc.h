@@ -139,6 +139,31 @@ __global__ __launch_bounds__(256) void k_pack_weights(const uint8_t* w, int N, i
   for (int i = 0; i < 8 * esz; i++) o[i] = v[i];
 }
 
+// Context values of every layer transposed for the action expert's
+// cross-attention: vt[l][d][c] = V_l[c][d], where V_l is columns l 2D + D ..
+// l 2D + 2D - 1 of the cross K / V rows kv[c] (C rows, pitch L 2D), and zero
+// for c >= C (Cp keys per row, a multiple of 8). A thread writes 8 keys of
+// one (l, d); consecutive threads take consecutive d, so each of its 8 reads
+// is coalesced across the wave.
+__global__ __launch_bounds__(256) void k_ctx_vt(const uint16_t* kv, int C, int L, int D, int Cp, uint16_t* vt) {
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n8 = Cp / 8;
+  if (e >= (size_t)L * n8 * D) return;
+  const int d = (int)(e % D);
+  const size_t r = e / D;
+  const int c0 = (int)(r % n8) * 8, l = (int)(r / n8);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int c = c0 + 2 * j;
+    const size_t base = (size_t)l * 2 * D + D + d, ld = (size_t)L * 2 * D;
+    const uint32_t lo = c < C ? kv[(size_t)c * ld + base] : 0u;
+    const uint32_t hi = c + 1 < C ? kv[(size_t)(c + 1) * ld + base] : 0u;
+    w[j] = lo | (hi << 16);
+  }
+  *reinterpret_cast<uint4*>(vt + ((size_t)l * D + d) * Cp + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // RoPE tables of a pass: cs[pos][i] = cos(pos theta_i), sn[pos][i] =
 // sin(pos theta_i), theta_i = base^(-2i / D), i < D / 2, pos < S (half-split
 // rotation of the pairs (i, i + D/2)). The frequency and the angle are formed
