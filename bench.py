@@ -57,18 +57,20 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(label: str):
+def measured_traffic(label: str, config: int):
     """HBM bytes per launch of `label` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE passes scaled by a plain copy of known size),
-    or None when there is none or the kernels changed since it was taken."""
+    or None when there is none, it was taken on another workload, or the
+    kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("label") != label or t.get("kernel_source_sha") != kernel_source_sha():
+    v = t.get("labels", {}).get(label)
+    if v is None or t.get("config") != config or t.get("kernel_source_sha") != kernel_source_sha():
         return None
-    return float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+    return float(v["fetch_bytes_per_launch"]) + float(v["write_bytes_per_launch"])
 
 
 def log(msg):
@@ -224,6 +226,87 @@ def fused_bench(cfg, n_stale, steps, warmup):
             "plain_step_ms": round(plain_ms, 4), "speedup": round(plain_ms / fused_ms, 4),
             "graph_nodes": {"plain": plain_nodes, "fused": fused_nodes}}
     print(json.dumps(line), flush=True)
+
+
+def phase_of(label: str) -> str:
+    """Roofline phase of a kernel label (the phases of roofline.bound)."""
+    if label.startswith(("vit.", "mrg.")):
+        return "vit"
+    if label.startswith("llm."):
+        return "backbone"
+    if label == "proj":
+        return "projector"
+    if label in ("dit.time_embed", "dit.time_fc1", "dit.time_fc2", "dit.adaln", "dit.final_mod", "dit.cross_kv",
+                 "dit.cross_vt", "dit.clear"):
+        return "dit_once"
+    if label.startswith("dit."):
+        return "dit_step"
+    return "other"
+
+
+def phase_fractions(kernels, bound):
+    """Measured time per phase (sum of each label's per-launch duration x
+    launches per step) against the phase's roofline bound."""
+    meas = {}
+    for lb, v in kernels.items():
+        ph = phase_of(lb)
+        meas[ph] = meas.get(ph, 0.0) + v["avg_us"] * v["count"] * 1e-3
+    out = {}
+    for ph in sorted(set(meas) | set(bound.per_phase)):
+        m, b = meas.get(ph, 0.0), bound.per_phase.get(ph, 0.0) * 1e3
+        out[ph] = {"ms": round(m, 4), "bound_ms": round(b, 4), "frac": round(b / m, 4) if m else None}
+    return out
+
+
+def component_bench(cfg, steps, warmup):
+    """Backbone prefill alone (vla_backbone_prefill) or the flow sampler
+    alone (vla_flow_euler_sample), launched eagerly back to back on one
+    stream; returns (ms per call, p50, p90)."""
+    import numpy as np
+    import torch
+    from synth import make_inputs, make_weights
+    from vla_robot_policy_amd import lib
+    from vla_robot_policy_amd.device import DeviceWeights, upload_input, workspace
+
+    t0 = time.time()
+    W, I = make_weights(cfg), make_inputs(cfg)
+    dw = DeviceWeights(cfg, W, keep_host=False, threads=16, packed=PACKED and cfg.kind == "backbone" and not cfg.block.a8)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    if cfg.kind == "backbone":
+        bb = dw.build_backbone()
+        x = upload_input(I["x"])
+        out = torch.empty((cfg.seq, cfg.block.hidden), dtype=torch.int16, device=dev)
+        need = lib.vla_backbone_workspace_bytes(bb, cfg.seq)
+        ws = workspace(need)
+
+        def call():
+            lib.check(lib.vla_backbone_prefill(bb, x, cfg.seq, out, ws, need, stream))
+    else:
+        dit = dw.build_dit()
+        d = cfg.dit
+        ctx, noise = upload_input(I["ctx"]), upload_input(I["noise"])
+        acts = torch.empty((d.chunk, d.action_dim), dtype=torch.float32, device=dev)
+        need = lib.vla_dit_workspace_bytes(dit, cfg.ctx_len, d.chunk, d.action_dim, cfg.steps)
+        ws = workspace(need)
+
+        def call():
+            lib.check(lib.vla_flow_euler_sample(dit, ctx, cfg.ctx_len, noise, d.chunk, d.action_dim, cfg.steps, acts,
+                                                None, ws, need, stream))
+    log(f"weights generated and uploaded in {time.time() - t0:.1f}s")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        call()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    ms = evs[0].elapsed_time(evs[steps]) / steps
+    log(f"{steps} calls: mean {ms:.3f} ms, p50 {np.median(per):.3f} ms")
+    return ms, float(np.median(per)), float(np.percentile(per, 90))
 
 
 def gpu_step_bench(cfg, steps, warmup, kernel_reps, only_label=None):
@@ -430,8 +513,25 @@ def main():
             raise SystemExit("--euler-steps must be in [1, 64]")
         cfg = cfg.replace(steps=a.euler_steps)
         variant += f"; sampler run for {a.euler_steps} Euler step{'s' if a.euler_steps > 1 else ''} instead of the workload's"
+    if cfg.kind in ("backbone", "dit"):
+        if a.only_label or a.fused is not None or a.shape_cache:
+            raise SystemExit("--only-label, --fused and --shape-cache need a policy step (--config 4 or 5)")
+        ms, p50, p90 = component_bench(cfg, a.steps, a.warmup)
+        b = roofline.bound(cfg)
+        what = "36-layer backbone prefill" if cfg.kind == "backbone" else "flow-matching action sampler"
+        print(json.dumps({
+            "metric": f"ms per {what} at batch 1 + % of MFMA/HBM roofline", "value": round(ms, 4), "unit": "ms",
+            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": cfg.wdtype if cfg.wdtype in ("fp8", "int8") else "bf16",
+            "data": "synthetic",
+            "config": {"workload": WORKLOADS[a.config] + variant, "global_batch": 1, "seq_len": cfg.seq if cfg.kind == "backbone" else None,
+                       "euler_steps": cfg.steps if cfg.kind == "dit" else None, "parallelism": "single GPU"},
+            "p50_ms": round(p50, 4), "p90_ms": round(p90, 4),
+            "roofline_bound_ms": round(b.seconds * 1e3, 4), "roofline_frac": round(b.seconds * 1e3 / ms, 4),
+            "launch": "eager (one entry-point call per step, kernels queued back to back)"}), flush=True)
+        return
     if cfg.kind != "step":
-        raise SystemExit("bench.py times whole policy steps: --config 4 or 5")
+        raise SystemExit("bench.py times policy steps (--config 4 or 5), the backbone (2) or the sampler (3)")
     if a.fused is not None:
         fused_bench(cfg, a.fused, a.steps, a.warmup)
         return
@@ -458,7 +558,7 @@ def main():
         else:
             ach, peak, unit = o.flops / dur / 1e12, peaks[o.compute] / 1e12, "TFLOP/s"
         roof = {"kernel": name, "bound": "hbm" if hbm_bound else "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(name),
+                "unit": unit, "frac": round(ach / peak, 4), "traffic": measured_traffic(name, a.config),
                 "avg_launch_us": round(kd["avg_us"], 2), "launches_per_step": kd["count"],
                 "algorithmic_bytes_per_launch": o.bytes, "flops_per_launch": o.flops}
     cpu = None
@@ -476,6 +576,7 @@ def main():
         "hz": round(1000.0 / ms, 2), "p50_ms": round(r["p50"], 4), "p90_ms": round(r["p90"], 4),
         "tokens_per_s": round(cfg.seq / (ms * 1e-3), 1),
         "roofline_bound_ms": round(b.seconds * 1e3, 4), "roofline_frac_step": round(b.seconds * 1e3 / ms, 4),
+        "phases": phase_fractions(r["kernels"], b),
         "graph_nodes": r["nodes"],
         "roofline": roof,
         "cpu_baseline": cpu,
