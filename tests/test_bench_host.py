@@ -43,17 +43,17 @@ def test_code_hash_ignores_comments_only(tmp_path, edit, same):
 
 def test_committed_traffic_matches_sources_or_is_withheld():
     b = _bench(ROOT)
-    t = b.measured_traffic("dit.layer", 4)
+    t = b.measured_traffic("dit.layers", 4)
     assert t is None or t > 0
     assert b.measured_traffic("no.such.label", 4) is None
-    assert b.measured_traffic("dit.layer", 99) is None          # another workload's counters
+    assert b.measured_traffic("dit.layers", 99) is None          # another workload's counters
 
 
 def test_phase_of_covers_every_step_label():
     b = _bench(ROOT)
     labels = ["vit.patch_embed", "vit.ln1", "mrg.fc1", "llm.stage", "llm.rope_table", "llm.qkv", "llm.final_norm",
               "proj", "dit.time_embed", "dit.adaln", "dit.cross_kv", "dit.cross_vt", "dit.clear", "dit.in_proj",
-              "dit.layer", "dit.tail", "dit.sa_qkv", "dit.mlp_down"]
+              "dit.layers", "dit.tail", "dit.sa_qkv", "dit.mlp_down"]
     ph = {lb: b.phase_of(lb) for lb in labels}
     assert "other" not in ph.values(), ph
-    assert ph["dit.cross_kv"] == "dit_once" and ph["dit.layer"] == "dit_step" and ph["dit.sa_qkv"] == "dit_step"
+    assert ph["dit.cross_kv"] == "dit_once" and ph["dit.layers"] == "dit_step" and ph["dit.sa_qkv"] == "dit_step"

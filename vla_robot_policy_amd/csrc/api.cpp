@@ -725,8 +725,11 @@ struct DitState {
   uint16_t* phi = nullptr;   // sinusoidal features of the time grid [K, tdim]
   uint16_t* t1 = nullptr; uint16_t* sc = nullptr; float* mod = nullptr; float* fmod = nullptr;
   Stream xs{};
-  float* xb[2] = {nullptr, nullptr};
+  // the layers kernel's per-layer buffers: layer l reads lx[l] (lx[0] is
+  // xs.x) and writes lx[l + 1] through x1[l], x2[l]; aos, ao, h likewise
+  float* lx = nullptr;
   float* x1 = nullptr; float* x2 = nullptr;
+  DitLayerPtrs* tab = nullptr;   // the layers' weights, in device memory
   uint16_t* qkv = nullptr; uint16_t* ao = nullptr; uint16_t* q = nullptr; uint16_t* h = nullptr;
   int* derr = nullptr;
   uint16_t* aos = nullptr;   // the layer kernel's self-attention output
@@ -761,26 +764,29 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.mod = c.take<float>((size_t)K * mod_w);
   s.fmod = c.take<float>((size_t)K * 2 * D);
   s.xs = take_stream(c, n, D);
-  // the layer kernel's stream buffers: layer l reads xb[l % 2] and writes
-  // xb[(l + 1) % 2] through the per-sublayer buffers x1, x2
-  s.xb[0] = s.xs.x; s.xb[1] = c.take<float>((size_t)n * D);
-  s.x1 = c.take<float>((size_t)n * D);
-  s.x2 = c.take<float>((size_t)n * D);
   s.G = cu_count();
   s.stack = dit_stack_ok(cf, n, s.G);
   s.spin = dit_spin_limit();
   if (s.stack) {
+    const size_t nd = (size_t)n * D;
+    s.lx = c.take<float>((size_t)(L + 1) * nd);
+    s.xs.x = s.lx;
+    s.x1 = c.take<float>((size_t)L * nd);
+    s.x2 = c.take<float>((size_t)L * nd);
+    s.aos = c.take<uint16_t>((size_t)L * nd);
+    s.ao = c.take<uint16_t>((size_t)L * nd);
+    s.h = c.take<uint16_t>((size_t)L * n * cf.mlp);
+    s.tab = c.take<DitLayerPtrs>((size_t)L);
     const size_t wq = (size_t)n * 3 * D / 2, wd = (size_t)n * D / 2, wp = (size_t)ds_dpart_words(D, cf.mlp);
     s.fw_words = wq + wd + wp;
     s.fw = c.take<uint2>(s.fw_words);
     s.fqkv = s.fw; s.fq = s.fqkv + wq; s.fdp = s.fq + wd;
-    s.aos = c.take<uint16_t>((size_t)n * D);
   } else {
     s.qkv = c.take<uint16_t>((size_t)n * 3 * D);
     s.q = c.take<uint16_t>((size_t)n * D);
+    s.ao = c.take<uint16_t>((size_t)n * D);
+    s.h = c.take<uint16_t>((size_t)n * cf.mlp);
   }
-  s.ao = c.take<uint16_t>((size_t)n * D);
-  s.h = c.take<uint16_t>((size_t)n * cf.mlp);
   s.derr = c.status;      // word 0 of the workspace's status block
   s.u = !s.stack && cf.wdtype != VLA_F32 ? c.take<uint16_t>((size_t)n * D) : nullptr;
   if (s.stack) {
@@ -793,9 +799,25 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
     VLA_TRY(launch(c, k_fill_ref(), dim3((nclr + 255) / 256), dim3(256), 0, {arg(c.cnt_tile), arg(z), arg(nclr)}));
     int one = 1;
     VLA_TRY(launch(c, k_fill_ref(), dim3(1), dim3(256), 0, {arg(s.derr), arg(z), arg(one)}));
-    // flagged words start at flag 0; the run's launches use flags 1, 2, ...
+    // flagged words start at flag 0; the run's layers use flags 1, 2, ...
     const int nfw = (int)(s.fw_words * 2);
     VLA_TRY(launch(c, k_fill_ref(), dim3((nfw + 255) / 256), dim3(256), 0, {arg(s.fw), arg(z), arg(nfw)}));
+    // the layers' weight table, DS_TAB_CHUNK layers per fill
+    c.label = "dit.table";
+    const bool sc = scaled8(cf.wdtype);
+    for (int l0 = 0; l0 < L; l0 += DS_TAB_CHUNK) {
+      DitTableArgs t{};
+      t.n = std::min(DS_TAB_CHUNK, L - l0);
+      t.out = s.tab ? s.tab + l0 : nullptr;
+      for (int i = 0; i < t.n; i++) {
+        const vla_dit_layer& w = d.layers[l0 + i];
+        const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
+        const float* ss[6] = {w.s_qkv, w.s_o, w.s_cq, w.s_co, w.s_up, w.s_down};
+        const float* bs[6] = {w.b_qkv, w.b_o, w.b_cq, w.b_co, w.b_up, w.b_down};
+        for (int j = 0; j < 6; j++) { t.p[i].w[j] = ws[j]; t.p[i].s[j] = sc ? ss[j] : nullptr; t.p[i].b[j] = bs[j]; }
+      }
+      VLA_TRY(launch(c, k_dit_table_ref(), dim3(1), dim3(64), 0, {arg(t)}));
+    }
   }
   return VLA_OK;
 }
@@ -904,31 +926,27 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
   if (s.stack && !dit_layer_lookup(wt, D, &lk)) return fail(VLA_ERR_UNSUPPORTED, "dit: no layer kernel for wdtype %d", wt);
   if (s.stack && !c.plan && lk.smem > 64 * 1024) VLA_TRY(allow_smem(lk));
   for (int k = k0; k < k1; k++) {
-    for (int l = 0; l < L; l++) {
+    if (s.stack) {  // every layer of the step in one persistent launch
+      c.label = "dit.layers";
+      DitLayerArgs a{};
+      a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
+      a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
+      a.l0 = 0; a.l1 = L;
+      a.tab = s.tab;
+      a.mod = s.mod ? s.mod + (size_t)k * mod_w : nullptr;
+      a.ckv = ckv; a.ldc = L * 2 * D;
+      a.vt = vt; a.ldvt = dit_vt_pitch(C);
+      a.xs = s.lx; a.x1 = s.x1; a.x2 = s.x2; a.aos = s.aos; a.aoc = s.ao; a.h = s.h;
+      a.qkv = s.fqkv; a.q = s.fq; a.dpart = s.fdp;
+      a.wq_next = k + 1 < K ? d.layers[0].w_qkv : nullptr;
+      a.cnt = c.cnt_tile; a.err = s.derr; a.spin = s.spin;
+      a.flag0 = 1u + (unsigned)(k * L);   // increasing over the run, whose start cleared the words
+      VLA_TRY(launch(c, lk.fn, dim3(s.G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
+    }
+    for (int l = 0; l < L && !s.stack; l++) {
       const vla_dit_layer& w = d.layers[l];
       const float* m = s.mod ? s.mod + (size_t)k * mod_w + (size_t)l * 9 * D : nullptr;
       auto mv = [&](int j) { return m ? m + (size_t)j * D : nullptr; };
-      if (s.stack) {  // the whole layer in one persistent launch
-        c.label = "dit.layer";
-        DitLayerArgs a{};
-        a.n = n; a.D = D; a.H = cf.heads; a.hd = cf.head_dim; a.mlp = cf.mlp; a.C = C;
-        a.eps = cf.eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cf.head_dim));
-        a.x_in = s.xb[l & 1]; a.x1 = s.x1; a.x2 = s.x2; a.x_out = s.xb[(l + 1) & 1];
-        a.qkv = s.fqkv; a.q = s.fq; a.aos = s.aos; a.aoc = s.ao; a.h = s.h;
-        a.flag = 1u + (unsigned)(k * L + l);   // increasing over the run, whose start cleared the words
-        a.ck = ckv ? ckv + (size_t)l * 2 * D : nullptr; a.ldc = L * 2 * D;
-        a.ldvt = dit_vt_pitch(C); a.cv = vt ? vt + (size_t)l * D * a.ldvt : nullptr;
-        a.mod = m;
-        const void* ws[6] = {w.w_qkv, w.w_o, w.w_cq, w.w_co, w.w_up, w.w_down};
-        const float* ss[6] = {w.s_qkv, w.s_o, w.s_cq, w.s_co, w.s_up, w.s_down};
-        const float* bs[6] = {w.b_qkv, w.b_o, w.b_cq, w.b_co, w.b_up, w.b_down};
-        for (int i = 0; i < 6; i++) { a.w[i] = ws[i]; a.s[i] = scaled8(wt) ? ss[i] : nullptr; a.b[i] = bs[i]; }
-        const bool last_launch = k == K - 1 && l == L - 1;
-        a.wq_next = last_launch ? nullptr : d.layers[(l + 1) % L].w_qkv;
-        a.dpart = s.fdp; a.cnt = c.cnt_tile; a.err = s.derr; a.spin = s.spin;
-        VLA_TRY(launch(c, lk.fn, dim3(s.G), dim3(lk.threads), (size_t)lk.smem, {arg(a)}));
-        continue;
-      }
       // The modulated LayerNorm u = LN(x)(1 + scale) + shift of a sublayer's
       // input: bf16 / fp8 weights take u from one row-norm launch (each of
       // the GEMM's workgroups would otherwise normalise every row again);
@@ -1022,7 +1040,7 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
     {  // velocity head + Euler update (+ input projection for the next step)
       TailArgs t{};
       t.n = n; t.D = D; t.A = A; t.K = K; t.eps = cf.eps;
-      t.x = s.stack ? s.xb[L & 1] : x;   // the last layer's output
+      t.x = s.stack ? s.lx + (size_t)L * n * D : x;   // the last layer's output
       t.shift = s.fmod ? s.fmod + (size_t)k * 2 * D : nullptr;
       t.scale = s.fmod ? s.fmod + (size_t)k * 2 * D + D : nullptr;
       t.w_out = d.w_out; t.s_out = d.s_out; t.b_out = d.b_out;

@@ -1,11 +1,12 @@
-// One DiT layer of the flow sampler's action expert as a single persistent
-// kernel, for action chunks of at most 16 rows.
+// The DiT layers of one Euler step of the flow sampler's action expert as a
+// single persistent kernel, for action chunks of at most 16 rows.
 //
 // Page "AI Infra如何优化VLA - 模型推理性能提升技术拆解" (section 整体方案 and
 // the CUDA Graph section): the action expert is memory-bound and was launch-
 // bound before graphs. At 16 rows every GEMM of a layer is a weight stream of
 // 3-13 MB, far too little to hide a kernel's launch, argument fetch, first
-// load latency and tail; here the eight steps of a layer run in one launch:
+// load latency and tail; here the eight steps of every layer run in one
+// launch, layer after layer:
 //
 //   0 QKV    u = LN(x)(1 + scale_sa) + shift_sa;  qkv = u Wqkv^T + b
 //   1 SAATT  per head: ao = softmax(q k^T / sqrt(d)) v     (no mask)
@@ -18,23 +19,29 @@
 //
 // Work units: 16 output columns x D input columns of one GEMM (32 columns
 // for UP; DOWN is split into mlp / 2D slices of 2D columns, summed in a fixed
-// order by the last slice of each tile), or one attention head. Unit u of phase p belongs to
-// workgroup (u + base_p) mod G, so a workgroup knows its units in advance and
-// streams their weights into registers before it waits for the previous
-// phase: the HBM latency of the next weights overlaps the current phase.
+// order by the tile's first slice), or one attention head. Unit u of phase p
+// of layer l belongs to workgroup (u + base(l, p)) mod G, where the bases
+// count every unit before it in the launch, so a workgroup knows its units
+// in advance and streams their weights into registers before it waits for
+// the previous phase: the HBM latency of the next weights overlaps the
+// current phase. The next layer's QKV weights are requested by their owners
+// while the current layer's DOWN runs.
 // The outputs of QKV and CAQ, which only the attention phases' few
 // workgroups read, travel as flagged words (below): the attention polls the
 // words of its head, and the load that sees them there is the load that
 // brings them. Every other phase hands on by counters: it writes with
 // device-coherent (sc1) stores, waits for them, then counts, and the next
-// phase polls the counter. Every buffer written inside the launch (the fp32
-// residual stream has one buffer per sublayer) is written once before
-// anything reads it, so once its phase is counted it is read with ordinary
-// cached loads: no XCD's private L2 can hold an older copy.
-// Every wait is bounded: on time-out the workgroup records an error,
-// poisons its outputs with NaN and leaves, so a fault can never hang the
-// device. The workgroup that completes the last DOWN tile resets the
-// counters for the next launch.
+// phase polls the counter (counts accumulate over the launch's layers).
+// Every other buffer written inside the launch (the fp32 residual stream,
+// the attention outputs, the MLP activations) has one copy per layer and
+// sublayer and is written once before anything reads it, so once its phase
+// is counted it is read with ordinary cached loads: no XCD's private L2 can
+// hold an older copy.
+// Every wait is bounded and also gives up once another workgroup has
+// recorded a time-out: the workgroup then poisons the launch's output with
+// NaN and leaves, so a fault can never hang the device. The workgroup that
+// completes the last layer's last DOWN tile resets the counters for the next
+// launch.
 //
 // Each LayerNorm is computed by every workgroup that needs it, from the fp32
 // residual stream held in registers (two-pass mean / variance), so no
@@ -56,45 +63,84 @@ constexpr int DS_WSLOTS = DS_MAXU * DS_KSW;
 constexpr int DS_DP = 96;         // head dim padded for the attention MFMAs
 constexpr int DS_KB = 32;         // keys per attention block
 constexpr unsigned DS_SPIN = 1u << 17;   // polls before a wait gives up (a healthy wait is microseconds)
-// Phase counters: phases before DOWN count into DS_NC slots 256 bytes apart
-// (workgroup w adds to slot w % DS_NC), so arrivals do not serialise on one
-// address; DOWN (few arrivals) uses one counter, whose last arrival resets
-// all of them.
+// Phase counters: every phase counts into DS_NC slots 256 bytes apart
+// (workgroup w adds to slot w % DS_NC), so arrivals and the next phase's
+// polls do not serialise on one address. On the launch's last layer DOWN
+// also counts into one more word, whose last arrival resets them all.
 constexpr int DS_NC = 16, DS_CSTRIDE = 64;
-__host__ __device__ constexpr int ds_counter_words(int) { return DP_N * DS_NC * DS_CSTRIDE; }
+constexpr int DS_LAST = DP_N * DS_NC * DS_CSTRIDE;   // the last layer's DOWN tiles
+__host__ __device__ constexpr int ds_counter_words(int) { return DS_LAST + DS_CSTRIDE; }
 // flagged words of the DOWN slice partials: slices 1 .. of every tile
 __host__ __device__ constexpr int ds_dpart_words(int D, int mlp) { return (mlp / (2 * D) - 1) * (D / 16) * 256; }
+
+// One layer's weights, as the layer table in device memory holds them.
+// The thread index, re-read for every layer: values derived from it are
+// recomputed where a phase uses them instead of being hoisted out of the
+// layer loop, where they would hold registers across every phase (measured:
+// without it the bf16 kernel spills 340 bytes per lane).
+__device__ __forceinline__ int ds_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+// the wave index, known uniform across the wave (a scalar register)
+__device__ __forceinline__ int ds_wave() { return __builtin_amdgcn_readfirstlane(ds_tid() >> 6); }
+
+struct DitLayerPtrs {
+  const void* w[6];               // qkv, o, cq, co, up, down: [N, K] row-major
+  const float* s[6];              // per-row 8-bit weight scales (NULL for bf16)
+  const float* b[6];              // biases
+};
 
 struct DitLayerArgs {
   int n, D, H, hd, mlp, C;        // action rows (<= 16), width, heads, head dim, MLP width, context tokens
   float eps, scale_log2;          // LayerNorm epsilon; log2(e) / sqrt(hd)
-  // [n, D] residual stream (fp32), one buffer per sublayer: x1 = x_in + the
-  // self-attention branch, x2 = x1 + the cross-attention branch, x_out = x2 +
-  // the MLP branch. Each is written once per launch before anything reads
-  // it, so no L2 can hold a stale copy and readers use ordinary cached loads.
+  int l0, l1;                     // the layers this launch runs
+  const DitLayerPtrs* tab;        // [layers] weight table
+  const float* mod;               // [layers][9][D] modulation of this Euler step
+  const uint16_t* ckv;            // context keys: layer l's at ckv + l 2D, row pitch ldc
+  const uint16_t* vt;             // context values transposed: layer l's [D][ldvt] at vt + l D ldvt, zero beyond C keys
+  int ldc, ldvt;                  // ldvt: a multiple of 32, >= C
+  // per-layer buffers, each written once per launch before anything reads it:
+  // xs[l] [n, D] is layer l's input (xs[l + 1] its output), x1 = xs[l] + the
+  // self-attention branch, x2 = x1 + the cross-attention branch (fp32)
+  float* xs;                      // [layers + 1][n][D]
+  float* x1;                      // [layers][n][D]
+  float* x2;
+  uint16_t* aos;                  // [layers][n][D] self-attention output
+  uint16_t* aoc;                  // [layers][n][D] cross-attention output
+  uint16_t* h;                    // [layers][n][mlp] GELU output
+  // flagged words (two bf16 of adjacent columns + flag): [n, 3D / 2], [n, D / 2]
+  uint2* qkv;
+  uint2* q;                       // cross-attention query
+  uint2* dpart;                   // DOWN partials of slices 1..: flagged words [slices - 1][D/16][256]
+  const void* wq_next;            // the next launch's first QKV weights (NULL: none), read ahead into the memory-side cache
+  unsigned* cnt;                  // ds_counter_words(D) counters (zero between launches)
+  int* err;                       // set to 1 when a wait times out
+  unsigned spin;                  // polls before a wait gives up (DS_SPIN unless the host asks for fewer)
+  unsigned flag0;                 // word flag of layer l0 (layer l: flag0 + l - l0): nonzero, and above every
+                                  // flag written since the words were cleared
+};
+
+// Layer l of a launch, resolved from the table (uniform across the workgroup).
+struct DsLayer {
+  const void* w[6];
+  const float* s[6];
+  const float* b[6];
+  const float* mod;
+  const uint16_t* ck;
+  const uint16_t* cv;
   const float* x_in;
   float* x1;
   float* x2;
   float* x_out;
-  // flagged words (two bf16 of adjacent columns + flag): [n, 3D / 2], [n, D / 2]
-  uint2* qkv;
-  uint2* q;                       // cross-attention query
-  uint16_t* aos;                  // [n, D] self-attention output
-  uint16_t* aoc;                  // [n, D] cross-attention output
-  uint16_t* h;                    // [n, mlp] GELU output
-  const uint16_t* ck;             // this layer's context keys [C][D], row pitch ldc
-  const uint16_t* cv;             // this layer's context values transposed: [D][ldvt], zero beyond C keys
-  int ldc, ldvt;                  // ldvt: a multiple of 32, >= C
-  const float* mod;               // [9][D] modulation of this layer and step
-  const void* w[6];               // qkv, o, cq, co, up, down: [N, K] row-major
-  const void* wq_next;            // the next launch's QKV weights (NULL: none), read ahead into the memory-side cache
-  const float* s[6];              // per-row fp8 scales (NULL for bf16)
-  const float* b[6];              // biases
-  uint2* dpart;                   // DOWN partials of slices 1..: flagged words [slices - 1][D/16][256]
-  unsigned* cnt;                  // ds_counter_words(D) counters (zero between launches)
-  int* err;                       // set to 1 when a wait times out
-  unsigned spin;                  // polls before a wait gives up (DS_SPIN unless the host asks for fewer)
-  unsigned flag;                  // this launch's word flag: nonzero, and above every flag written since the words were cleared
+  uint16_t* aos;
+  uint16_t* aoc;
+  uint16_t* h;
+  const void* wq_next;            // the next layer's QKV weights (NULL on the launch's last layer)
+  unsigned flag;
+  int l, li;                      // layer, and its index within the launch
+  bool last;                      // the launch's last layer
 };
 
 __device__ __forceinline__ void st_sc1_f32(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -118,7 +164,7 @@ __device__ __forceinline__ void st_fw(brsrc r, uint32_t word, uint32_t data, uin
 // phases' few workgroups, with a head's rows each (a few KB). False after
 // DS_SPIN rounds.
 template <int NCH, typename WordF, typename PutF>
-__device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, unsigned spin, WordF word, PutF put) {
+__device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, unsigned spin, const int* err, WordF word, PutF put) {
   static_assert(NCH <= 64, "one pending bit per chunk");
   uint4 v[NCH];
   uint64_t pend = 0;
@@ -138,6 +184,8 @@ __device__ __forceinline__ bool ds_poll(brsrc r, uint32_t flag, unsigned spin, W
       }
     if (!pend) return true;
     if (spins >= spin) return false;
+    // another workgroup timed out: give up too
+    if ((spins & 31) == 31 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int i = 0; i < NCH; i++)
@@ -157,10 +205,19 @@ __device__ __forceinline__ int ds_units(const DitLayerArgs& a, int ph) {
 }
 // value of the phase counter once the phase is complete
 __device__ __forceinline__ int ds_target(const DitLayerArgs& a, int ph) { return ph == DP_DOWN ? a.D / 16 : ds_units(a, ph); }
-__device__ __forceinline__ int ds_base(const DitLayerArgs& a, int ph) {
-  int b = 0;
-  for (int q = 0; q < ph; q++) b += ds_units(a, q);
-  return b;
+// units before phase ph of layer l in the launch, modulo the grid
+__device__ __forceinline__ int ds_base(const DitLayerArgs& a, int l, int ph) {
+  int per = 0, b = 0;
+  for (int q = 0; q < DP_N; q++) {
+    if (q == ph) b = per;
+    per += ds_units(a, q);
+  }
+  return (int)(((long long)(l - a.l0) * per + b) % gridDim.x);
+}
+// this workgroup's first unit of phase ph of layer l (>= the phase's units: none)
+__device__ __forceinline__ int ds_first(const DitLayerArgs& a, int l, int ph) {
+  const int G = gridDim.x;
+  return ((int)blockIdx.x - ds_base(a, l, ph) + G) % G;
 }
 
 // Wait until the DS_NC slots of a phase counter sum to target (wave 0
@@ -168,19 +225,25 @@ __device__ __forceinline__ int ds_base(const DitLayerArgs& a, int ph) {
 // polls. One read is in flight at a time: the barrier that follows waits
 // for every outstanding read, so reads issued ahead only delay the exit
 // (measured: 3.5 us per layer with four in flight).
-__device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, unsigned spin, int* sflag) {
-  if (threadIdx.x < 64) {
+// Lane 16 reads the error word with the same load: a time-out elsewhere
+// ends the wait at once.
+__device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, unsigned spin, const int* err, int* sflag) {
+  if (ds_wave() == 0) {
     static_assert(DS_NC == 16, "the phase counter slots are one DPP row");
-    const int lane = threadIdx.x;
+    const int lane = ds_tid();
+    const unsigned* p = lane < DS_NC ? slots + lane * DS_CSTRIDE : reinterpret_cast<const unsigned*>(err);
     unsigned spins = 0;
     bool ok = true;
     while (true) {
-      unsigned v = lane < DS_NC ? __hip_atomic_load(slots + lane * DS_CSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-      // exact: counts stay far below 2^24
-      const unsigned tot = (unsigned)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum((float)v)), 0));
-      if (tot >= target) break;                    // uniform: read from lane 0
-      if (++spins >= spin) { ok = false; break; }
-      __builtin_amdgcn_s_sleep(2);
+      unsigned v = lane <= DS_NC ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      // exact: counts stay far below 2^24; uniform (read from lanes 0 and 16)
+      const unsigned tot = (unsigned)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum((float)(lane < DS_NC ? v : 0u))), 0));
+      if (tot >= target) break;
+      if (++spins >= spin || __builtin_amdgcn_readlane((int)v, DS_NC)) { ok = false; break; }
+      // far from the target, poll less often (fewer reads competing with the
+      // phase being waited for)
+      if (tot + 8 < target) __builtin_amdgcn_s_sleep(16);
+      else __builtin_amdgcn_s_sleep(2);
     }
     if (lane == 0) sflag[0] = ok;
   }
@@ -191,13 +254,13 @@ __device__ __forceinline__ bool ds_wait(const unsigned* slots, unsigned target, 
 // Read bytes [i, i + 1) / n of the next launch's QKV weights and drop them
 // (the memory-side cache keeps them for that launch's first phase).
 template <typename WT, int D>
-__device__ __forceinline__ void ds_prefetch_qkv_share(const DitLayerArgs& a, int i, int n) {
+__device__ __forceinline__ void ds_prefetch_qkv_share(const DitLayerArgs& a, const void* wq, int i, int n) {
   const size_t total = (size_t)3 * D * D * sizeof(WT);
   const size_t share = (total / n + 4095) & ~(size_t)4095;
   const size_t b0 = (size_t)i * share, b1 = b0 + share < total ? b0 + share : total;
-  const brsrc nr = make_brsrc(a.wq_next);
+  const brsrc nr = make_brsrc(wq);
   uint32_t acc = 0;
-  for (size_t off = b0 + (size_t)threadIdx.x * 16; off < b1; off += (size_t)DS_THREADS * 16 * 8) {
+  for (size_t off = b0 + (size_t)ds_tid() * 16; off < b1; off += (size_t)DS_THREADS * 16 * 8) {
     uint4 v[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) {
@@ -263,10 +326,10 @@ __device__ __forceinline__ DsUnit ds_unit(const DitLayerArgs& a, int ph, int u) 
 // The wave's k-steps of a unit: steps s = wave + 4 i (i < NS) of KST for each
 // of the NB column blocks, into register slots OFF + b NS + i.
 template <typename WT, int OFF, int NB, int NS, int KST>
-__device__ __forceinline__ void ds_load_unit(const DitLayerArgs& a, const DsUnit& d, typename DsW<WT>::raw (&r)[DS_WSLOTS]) {
+__device__ __forceinline__ void ds_load_unit(const void* w, const DsUnit& d, typename DsW<WT>::raw (&r)[DS_WSLOTS]) {
   static_assert(OFF + NB * NS <= DS_WSLOTS, "unit exceeds the weight registers");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const brsrc wr = make_brsrc(a.w[d.wi]);
+  const int lane = ds_tid() & 63, wave = ds_wave();
+  const brsrc wr = make_brsrc(w);
 #pragma unroll
   for (int b = 0; b < NB; b++) {
     const int col = d.n0 + b * 16 + (lane & 15);
@@ -280,11 +343,18 @@ __device__ __forceinline__ void ds_load_unit(const DitLayerArgs& a, const DsUnit
   }
 }
 
+// Zero register slots OFF .. OFF + N - 1.
+template <typename WT, int OFF, int N>
+__device__ __forceinline__ void ds_zero_slots(typename DsW<WT>::raw (&r)[DS_WSLOTS]) {
+#pragma unroll
+  for (int i = OFF; i < OFF + N && i < DS_WSLOTS; i++) r[i] = typename DsW<WT>::raw{};
+}
+
 // NB 16 x 16 tiles of one unit: A [16][KW] bf16 in LDS (pitch apitch),
 // weights in register slots OFF ..; the wave's partial sums over its k-steps.
 template <typename WT, int OFF, int NB, int NS, int KST>
 __device__ __forceinline__ void ds_mma(const char* rA, int apitch, const typename DsW<WT>::raw (&w)[DS_WSLOTS], f32x4 (&acc)[NB]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = ds_tid() & 63, wave = ds_wave();
 #pragma unroll
   for (int b = 0; b < NB; b++) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -326,7 +396,7 @@ struct DsAttFr {
 
 __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nblk, int nk, int ldk, int ldvt, int hd,
                                              DsAttFr& f) {
-  const int lane = threadIdx.x & 63, qn = lane & 15, grp = lane >> 4;
+  const int lane = ds_tid() & 63, qn = lane & 15, grp = lane >> 4;
   const int kb = blk * DS_KB;
   const bool live = blk < nblk;
 #pragma unroll
@@ -353,7 +423,7 @@ __device__ __forceinline__ void ds_att_frags(brsrc kr, brsrc vr, int blk, int nb
 __device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp, const uint16_t* Vt, int ldk, int ldvt,
                                              uint16_t* O, int ldo, int oc, int nq, int nk, int hd, float scale_log2,
                                              char* lds_o, DsAttFr& f, bool have0) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = ds_tid(), lane = tid & 63, wave = ds_wave();
   const int qn = lane & 15, grp = lane >> 4;
   const brsrc kr = make_brsrc(Kp), vr = make_brsrc(Vt), orr = make_brsrc(O);
   const int nblk = (nk + DS_KB - 1) / DS_KB;
@@ -482,8 +552,8 @@ __device__ __forceinline__ void ds_attention(const char* qs, const uint16_t* Kp,
 // one 32-key block whose keys 16..31 are absent (their P is zero), with the
 // arithmetic of the cross-attention's single-block case.
 __device__ __forceinline__ void ds_self_att(const char* st, uint16_t* O, int ldo, int oc, int n, int hd, float scale_log2) {
-  if ((threadIdx.x >> 6) != 0) return;
-  const int lane = threadIdx.x & 63, qn = lane & 15, grp = lane >> 4;
+  if (ds_wave() != 0) return;
+  const int lane = ds_tid() & 63, qn = lane & 15, grp = lane >> 4;
   const char* qs = st;
   const char* ks = st + 16 * DS_DP * 2;
   const char* vt = st + 2 * 16 * DS_DP * 2;
@@ -555,18 +625,47 @@ __host__ __device__ constexpr int ds_region_a(int D) {
 }
 __host__ __device__ constexpr int ds_smem_bytes(int D) { return ds_region_a(D) + 2 * 4 * 256 * 4 + 64; }
 
-// One phase of the layer for this workgroup, specialised per phase so that
+// Layer l of the launch from the weight table and the per-layer buffers.
+template <int D>
+__device__ __forceinline__ DsLayer ds_layer(const DitLayerArgs& a, int l) {
+  DsLayer y;
+  const DitLayerPtrs* t = a.tab + l;
+#pragma unroll
+  for (int i = 0; i < 6; i++) { y.w[i] = t->w[i]; y.s[i] = t->s[i]; y.b[i] = t->b[i]; }
+  const size_t nd = (size_t)a.n * D;
+  y.mod = a.mod + (size_t)l * 9 * D;
+  y.ck = a.ckv + (size_t)l * 2 * D;
+  y.cv = a.vt + (size_t)l * D * a.ldvt;
+  y.x_in = a.xs + (size_t)l * nd;
+  y.x_out = a.xs + (size_t)(l + 1) * nd;
+  y.x1 = a.x1 + (size_t)l * nd;
+  y.x2 = a.x2 + (size_t)l * nd;
+  y.aos = a.aos + (size_t)l * nd;
+  y.aoc = a.aoc + (size_t)l * nd;
+  y.h = a.h + (size_t)l * a.n * a.mlp;
+  y.last = l + 1 == a.l1;
+  y.wq_next = y.last ? nullptr : a.tab[l + 1].w[0];
+  y.flag = a.flag0 + (unsigned)(l - a.l0);
+  y.l = l;
+  y.li = l - a.l0;
+  return y;
+}
+
+// One phase of a layer for this workgroup, specialised per phase so that
 // each phase's registers are allocated for that phase alone. False when the
 // workgroup must leave the kernel (a wait timed out). `wdown` holds the
 // workgroup's DOWN unit: a workgroup that also has an UP unit requests it
 // together with the UP weights (it is idle long before UP starts), so its
 // DOWN phase does not begin with a weight fetch queued ahead of its wait.
+// `wqkv` holds its QKV units: those of the next layer are requested during
+// this layer's DOWN, before its wait.
 template <typename WT, int D, int PH>
-__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, char* rA, float* red, int* sflag,
-                                         int& finished_tiles, typename DsW<WT>::raw (&wdown)[DS_WSLOTS], bool& have_down) {
+__device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, const DsLayer& y, int prev_err, char* rA, float* red,
+                                         int* sflag, int& finished_tiles, typename DsW<WT>::raw (&wdown)[DS_WSLOTS],
+                                         bool& have_down, typename DsW<WT>::raw (&wqkv)[DS_WSLOTS], bool& have_qkv) {
   using WR = typename DsW<WT>::raw;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wg = blockIdx.x, G = gridDim.x;
+  const int tid = ds_tid(), lane = tid & 63, wave = ds_wave();
+  const int G = gridDim.x;
   const int n = a.n;
   constexpr int APITCH = D * 2 + 16;
   constexpr int ntile = D / 16;
@@ -578,12 +677,32 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
   constexpr int NSW = (KST + 3) / 4;                 // of them per wave
   constexpr int MAXU = 2 * NB * NSW <= DS_WSLOTS ? 2 : 1;
   const int U = ds_units(a, PH);
-  const int first = ((wg - ds_base(a, PH)) % G + G) % G;
+  const int first = ds_first(a, y.l, PH);
+  // the next layer's QKV units of this workgroup, into wqkv, requested when
+  // UP starts: early enough to arrive long before the next QKV, and not
+  // queued ahead of the DOWN epilogue's loads (loads complete in order).
+  // Every slot is written on every path (zeros where there is no unit), so
+  // the registers are free between a layer's QKV and its UP.
+  auto preload_qkv = [&]() {
+    constexpr int KSTQ = D / 32, NSWQ = (KSTQ + 3) / 4;
+    const int fq = y.last ? 0 : ds_first(a, y.l + 1, DP_QKV), uq = ds_units(a, DP_QKV);
+    const bool one = !y.last && fq < uq, two = one && fq + G < uq;
+    if (one) ds_load_unit<WT, 0, 1, NSWQ, KSTQ>(y.wq_next, ds_unit(a, DP_QKV, fq), wqkv);
+    else ds_zero_slots<WT, 0, NSWQ>(wqkv);
+    if (two) ds_load_unit<WT, NSWQ, 1, NSWQ, KSTQ>(y.wq_next, ds_unit(a, DP_QKV, fq + G), wqkv);
+    else ds_zero_slots<WT, NSWQ, DS_WSLOTS - NSWQ>(wqkv);
+    have_qkv = one;
+  };
   if (first >= U) {                                  // no work in this phase
     if constexpr (PH == DP_UP) {
-      // nor in DOWN: read a share of the next launch's QKV weights
-      const int fd = ((wg - ds_base(a, DP_DOWN)) % G + G) % G, ud = ds_units(a, DP_DOWN);
-      if (fd >= ud && a.wq_next) ds_prefetch_qkv_share<WT, D>(a, fd - ud, G - ud);
+      // nor in DOWN, on the launch's last layer: read a share of the next
+      // launch's first QKV weights into the memory-side cache
+      const int fd = ds_first(a, y.l, DP_DOWN), ud = ds_units(a, DP_DOWN);
+      if (y.last && fd >= ud && a.wq_next) ds_prefetch_qkv_share<WT, D>(a, a.wq_next, fd - ud, G - ud);
+      // wdown is written on every path through UP (its DOWN unit loads it)
+      ds_zero_slots<WT, 0, DS_WSLOTS>(wdown);
+      have_down = false;
+      preload_qkv();
     }
     return true;
   }
@@ -598,14 +717,19 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
   // a wait timed out: record it, poison this workgroup's outputs
   auto fail = [&]() -> bool {
     if (tid == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(a.x_out + e, __builtin_nanf(""));
+    float* xo = a.xs + (size_t)a.l1 * n * D;
+    for (int e = tid; e < n * D; e += DS_THREADS) st_sc1_f32(xo + e, __builtin_nanf(""));
     return false;
   };
-  // every phase but QKV and the attentions waits for the previous phase's
-  // counter; after a failed earlier launch of the run, the first wait leaves
+  // every phase but the attentions waits for the previous phase's counter
+  // (QKV: the previous layer's DOWN; none on the launch's first layer).
+  // Counts accumulate over the launch's layers. After a failed earlier
+  // launch of the run, the first wait leaves.
   auto wait_prev = [&]() -> bool {
-    if (PH == 0) return true;
-    if (!prev_err && ds_wait(a.cnt + (PH - 1) * DS_NC * DS_CSTRIDE, (unsigned)ds_target(a, PH - 1), a.spin, sflag)) return true;
+    if (PH == DP_QKV && y.li == 0) return true;
+    const int pp = PH == DP_QKV ? DP_DOWN : PH - 1;
+    const unsigned target = (unsigned)((PH == DP_QKV ? y.li : y.li + 1) * ds_target(a, pp));
+    if (!prev_err && ds_wait(a.cnt + pp * DS_NC * DS_CSTRIDE, target, a.spin, a.err, sflag)) return true;
     return fail();
   };
   // LayerNorm geometry: wave w normalises rows 4w .. 4w + 3; lane l holds
@@ -616,7 +740,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
     DsAttFr f;
     constexpr bool cross = PH == DP_CAATT;
     if (cross)
-      ds_att_frags(make_brsrc(a.ck + first * a.hd), make_brsrc(a.cv + (size_t)first * a.hd * a.ldvt), wave,
+      ds_att_frags(make_brsrc(y.ck + first * a.hd), make_brsrc(y.cv + (size_t)first * a.hd * a.ldvt), wave,
                    (a.C + DS_KB - 1) / DS_KB, a.C, a.ldc, a.ldvt, a.hd, f);
     // the head's rows are staged after the partials: Q [16][DS_DP], and for
     // the self-attention K [16][DS_DP] and V^T [DS_DP][16], zero beyond n
@@ -641,7 +765,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       if constexpr (cross) {
         constexpr int NCH = (16 * DS_DP / 4 + DS_THREADS - 1) / DS_THREADS;
         ok = ds_poll<NCH>(
-            make_brsrc(a.q), a.flag, a.spin,
+            make_brsrc(a.q), y.flag, a.spin, a.err,
             [&](int i) -> int {
               const int e = tid + i * DS_THREADS;
               if (e >= 16 * hq) return -1;
@@ -655,7 +779,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       } else {
         constexpr int NCH = (3 * 16 * DS_DP / 4 + DS_THREADS - 1) / DS_THREADS;
         ok = ds_poll<NCH>(
-            make_brsrc(a.qkv), a.flag, a.spin,
+            make_brsrc(a.qkv), y.flag, a.spin, a.err,
             [&](int i) -> int {
               const int e = tid + i * DS_THREADS;
               if (e >= 3 * 16 * hq) return -1;
@@ -678,17 +802,17 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       }
       if (!ds_all(ok, sflag)) return fail();
       if constexpr (cross)
-        ds_attention(st, a.ck + hh * hd, a.cv + (size_t)hh * hd * a.ldvt, a.ldc, a.ldvt, a.aoc, D, hh * hd, n, a.C, hd,
+        ds_attention(st, y.ck + hh * hd, y.cv + (size_t)hh * hd * a.ldvt, a.ldc, a.ldvt, y.aoc, D, hh * hd, n, a.C, hd,
                      a.scale_log2, rA, f, j == 0);
       else
-        ds_self_att(st, a.aos, D, hh * hd, n, hd, a.scale_log2);
+        ds_self_att(st, y.aos, D, hh * hd, n, hd, a.scale_log2);
     }
   } else {
     const int mi = PH == DP_QKV ? 0 : PH == DP_CAQ ? 3 : 6;   // shift, scale at mod[mi], mod[mi + 1]
     // shift and 1 + scale of the lane's column groups (requested before the wait)
     float4 shv[norm ? KG : 1], gv[norm ? KG : 1];
     if constexpr (norm) {
-      const brsrc mr = make_brsrc(a.mod + (size_t)mi * D);
+      const brsrc mr = make_brsrc(y.mod + (size_t)mi * D);
 #pragma unroll
       for (int k = 0; k < KG; k++) {
         const int cg = lane + 64 * k;
@@ -701,9 +825,9 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
     float pb[MAXU][NB], ps[MAXU][NB], pg[MAXU][NB];
     {
       const int wi = ds_unit(a, PH, first).wi;
-      const bool scaled = a.s[wi] != nullptr;
-      const brsrc br = make_brsrc(a.b[wi]), sr = make_brsrc(a.s[wi]);
-      const brsrc gr = make_brsrc(a.mod + (size_t)(PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8) * D);
+      const bool scaled = y.s[wi] != nullptr;
+      const brsrc br = make_brsrc(y.b[wi]), sr = make_brsrc(y.s[wi]);
+      const brsrc gr = make_brsrc(y.mod + (size_t)(PH == DP_SAO ? 2 : PH == DP_CAO ? 5 : 8) * D);
 #pragma unroll
       for (int j = 0; j < MAXU; j++) {
         const DsUnit d = ds_unit(a, PH, first + j * G);
@@ -718,12 +842,13 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       }
     }
     // LayerNorm input rows: wave w holds rows 4w .. 4w + 3, lane l the float4
-    // column groups l + 64 k. QKV's input is final at launch, so its rows are
-    // requested ahead of its weights (loads complete in order); the other
-    // LayerNorms read theirs after the wait.
+    // column groups l + 64 k. The first layer's QKV input is final at launch,
+    // so its rows are requested ahead of its weights (loads complete in
+    // order); the other LayerNorms read theirs after the wait.
     float4 xv[norm ? 4 : 1][norm ? KG : 1];
+    const bool x_early = PH == DP_QKV && y.li == 0;
     auto load_x = [&]() {
-      const brsrc xr = make_brsrc(PH == DP_QKV ? a.x_in : PH == DP_CAQ ? a.x1 : a.x2);
+      const brsrc xr = make_brsrc(PH == DP_QKV ? y.x_in : PH == DP_CAQ ? y.x1 : y.x2);
 #pragma unroll
       for (int rr = 0; rr < 4; rr++)
 #pragma unroll
@@ -732,30 +857,39 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
           xv[rr][k] = as_f4(bload16(xr, (cg < D / 4 && r < n) ? ((uint32_t)r * D + 4 * cg) * 4u : BUF_OOB));
         }
     };
-    if constexpr (PH == DP_QKV) load_x();
+    if (x_early) load_x();
     WR wreg[DS_WSLOTS];
     auto& wuse = [&]() -> WR (&)[DS_WSLOTS] {
       if constexpr (PH == DP_DOWN) return wdown;
+      else if constexpr (PH == DP_QKV) return wqkv;
       else return wreg;
     }();
-    if (!(PH == DP_DOWN && have_down)) {
-      ds_load_unit<WT, 0, NB, NSW, KST>(a, ds_unit(a, PH, first), wuse);
+    const bool preloaded = (PH == DP_DOWN && have_down) || (PH == DP_QKV && have_qkv);
+    if (!preloaded) {
+      ds_load_unit<WT, 0, NB, NSW, KST>(y.w[ds_unit(a, PH, first).wi], ds_unit(a, PH, first), wuse);
       if constexpr (MAXU > 1)
-        if (nu > 1) ds_load_unit<WT, NB * NSW, NB, NSW, KST>(a, ds_unit(a, PH, first + G), wuse);
+        if (nu > 1) ds_load_unit<WT, NB * NSW, NB, NSW, KST>(y.w[ds_unit(a, PH, first).wi], ds_unit(a, PH, first + G), wuse);
     }
+    if constexpr (PH == DP_DOWN) have_down = false;
+    if constexpr (PH == DP_QKV) have_qkv = false;
     if constexpr (PH == DP_UP) {
-      const int fd = ((wg - ds_base(a, DP_DOWN)) % G + G) % G, ud = ds_units(a, DP_DOWN);
-      if (fd < ud) {
-        constexpr int KSTD = 2 * D / 32, NSWD = (KSTD + 3) / 4;
-        ds_load_unit<WT, 0, 1, NSWD, KSTD>(a, ds_unit(a, DP_DOWN, fd), wdown);
-        have_down = true;
-      } else if (a.wq_next) {
+      // every slot of wdown is written here (zeros without a DOWN unit), so
+      // the registers are free between a layer's DOWN and the next UP
+      const int fd = ds_first(a, y.l, DP_DOWN), ud = ds_units(a, DP_DOWN);
+      constexpr int KSTD = 2 * D / 32, NSWD = (KSTD + 3) / 4;
+      static_assert(NSWD <= DS_WSLOTS, "a DOWN unit exceeds the weight registers");
+      if (fd < ud) ds_load_unit<WT, 0, 1, NSWD, KSTD>(y.w[5], ds_unit(a, DP_DOWN, fd), wdown);
+      else ds_zero_slots<WT, 0, DS_WSLOTS>(wdown);
+      have_down = fd < ud;
+      preload_qkv();
+      if (fd >= ud && y.last && a.wq_next) {
         // a workgroup with UP but no DOWN work is idle from here to UP's
-        // wait: it reads its share of the next launch's QKV weights, so that
-        // launch's first phase finds them in the memory-side cache (HBM is
-        // quiet here; the UP weights were requested earlier and, needed only
-        // after the cross-attention, have time to arrive)
-        ds_prefetch_qkv_share<WT, D>(a, fd - ud, G - ud);
+        // wait: on the launch's last layer it reads its share of the next
+        // launch's first QKV weights, so that launch's first phase finds
+        // them in the memory-side cache (HBM is quiet here; the UP weights
+        // were requested earlier and, needed only after the
+        // cross-attention, have time to arrive)
+        ds_prefetch_qkv_share<WT, D>(a, a.wq_next, fd - ud, G - ud);
       }
     }
     if (!wait_prev()) return false;
@@ -765,7 +899,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       // SAO, CAO: the attention output; DOWN: the unit's slice of h (a
       // workgroup's units share their k range). Rows beyond n are zeros.
       const DsUnit d0 = ds_unit(a, PH, first);
-      const uint16_t* src = PH == DP_DOWN ? a.h : PH == DP_SAO ? a.aos : a.aoc;
+      const uint16_t* src = PH == DP_DOWN ? y.h : PH == DP_SAO ? y.aos : y.aoc;
       const int lds = PH == DP_DOWN ? a.mlp : D;
       const brsrc sr = make_brsrc(src);
       constexpr int apitch = KW * 2 + 16;
@@ -778,7 +912,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       }
       // the residual input at this thread's epilogue element of each unit,
       // requested with the A operand rather than after the product
-      const brsrc xr = make_brsrc(PH == DP_SAO ? a.x_in : PH == DP_CAO ? a.x1 : a.x2);
+      const brsrc xr = make_brsrc(PH == DP_SAO ? y.x_in : PH == DP_CAO ? y.x1 : y.x2);
 #pragma unroll
       for (int j = 0; j < MAXU; j++) {
         const int r = tid >> 4, col = ds_unit(a, PH, first + j * G).n0 + (tid & 15);
@@ -794,7 +928,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
       // two-pass mean / variance of each of the wave's 4 rows (wave-wide
       // sums), then u = LN(x)(1 + scale) + shift in bf16 into LDS. Rows
       // beyond n read zeros and give finite values that no output uses.
-      if constexpr (PH != DP_QKV) load_x();
+      if (!x_early) load_x();
       float mean[4], rstd[4];
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
@@ -861,21 +995,25 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
         const int col = d.n0 + b * 16 + cc;
         float v = red[(0 * NB + b) * 256 + tid] + red[(1 * NB + b) * 256 + tid] + red[(2 * NB + b) * 256 + tid] +
                   red[(3 * NB + b) * 256 + tid];
-        if (a.s[d.wi]) v *= ps[j][b];
+        if (y.s[d.wi]) v *= ps[j][b];
         if (PH == DP_DOWN) {
           // slices 1.. publish their partial as flagged words and are done;
           // the tile's slice-0 unit adds them to its own in slice order
           const int tile = d.n0 / 16, slice = d.k0 / KW, nsl = a.mlp / KW;
           const brsrc pr = make_brsrc(a.dpart);
           if (slice > 0) {
-            st_fw(pr, (uint32_t)((slice - 1) * ntile + tile) * 256u + tid, __float_as_uint(v), a.flag);
+            st_fw(pr, (uint32_t)((slice - 1) * ntile + tile) * 256u + tid, __float_as_uint(v), y.flag);
             return;
           }
           for (int q = 1; q < nsl; q++) {
             const uint32_t off = ((uint32_t)((q - 1) * ntile + tile) * 256u + tid) * 8u;
             uint2 w = bload8<CP_SC1>(pr, off);
-            for (unsigned spins = 0; w.y != a.flag; spins++) {
-              if (spins >= a.spin) { timed_out = true; break; }
+            for (unsigned spins = 0; w.y != y.flag; spins++) {
+              if (spins >= a.spin ||
+                  ((spins & 31) == 31 && __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                timed_out = true;
+                break;
+              }
               __builtin_amdgcn_s_sleep(1);
               w = bload8<CP_SC1>(pr, off);
             }
@@ -889,7 +1027,7 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
           const uint32_t bits = f2bf(v);
           if constexpr (PH == DP_UP) {
             if (r < n && col < d.N)
-              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bits, make_brsrc(a.h), (uint32_t)(r * a.mlp + col) * 2u, 0, CP_SC1);
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bits, make_brsrc(y.h), (uint32_t)(r * a.mlp + col) * 2u, 0, CP_SC1);
           } else {
             // even columns store the flagged word of their pair (the odd
             // column is the next lane, same row)
@@ -897,12 +1035,12 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
             const int ldo = PH == DP_QKV ? 3 * D : D;
             const uint32_t odd = (uint32_t)__shfl_xor((int)bits, 1, WAVE);
             if (!(cc & 1) && r < n && col < d.N)
-              st_fw(make_brsrc(out), (uint32_t)(r * ldo + col) / 2u, bits | (odd << 16), a.flag);
+              st_fw(make_brsrc(out), (uint32_t)(r * ldo + col) / 2u, bits | (odd << 16), y.flag);
           }
         } else {
           // gated residual: x += gate * v
           if (r < n) {
-            float* xd = PH == DP_SAO ? a.x1 : PH == DP_CAO ? a.x2 : a.x_out;
+            float* xd = PH == DP_SAO ? y.x1 : PH == DP_CAO ? y.x2 : y.x_out;
             st_sc1_f32(xd + (size_t)r * D + col, xpre[j] + pg[j][b] * v);
           }
         }
@@ -926,45 +1064,58 @@ __device__ __forceinline__ bool ds_phase(const DitLayerArgs& a, int prev_err, ch
     sflag[1] = 0;
     unsigned add = PH == DP_DOWN ? (unsigned)finished_tiles : (unsigned)nu;
     if (add) {
-      unsigned* slot = a.cnt + PH * DS_NC * DS_CSTRIDE + (PH == DP_DOWN ? 0 : (wg % DS_NC) * DS_CSTRIDE);
-      unsigned old = __hip_atomic_fetch_add(slot, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // the last DOWN tile: every unit of every phase is done and no
-      // workgroup polls any more, so the counters can be cleared
-      sflag[1] = PH == DP_DOWN && old + add == (unsigned)ds_target(a, DP_DOWN);
+      unsigned* slot = a.cnt + PH * DS_NC * DS_CSTRIDE + ((int)blockIdx.x % DS_NC) * DS_CSTRIDE;
+      __hip_atomic_fetch_add(slot, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the last layer's last DOWN tile: every unit of every phase is done
+      // and no workgroup polls any more, so the counters can be cleared
+      // (release: this workgroup's slot count lands before its reset count)
+      if (PH == DP_DOWN && y.last) {
+        const unsigned old = __hip_atomic_fetch_add(a.cnt + DS_LAST, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        sflag[1] = old + add == (unsigned)ds_target(a, DP_DOWN);
+      }
     }
   }
   __syncthreads();
-  if (sflag[1] && tid < DP_N * DS_NC)
+  if (sflag[1] && tid <= DP_N * DS_NC)
     __hip_atomic_store(a.cnt + tid * DS_CSTRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
+// The weight table of the launches: up to DS_TAB_CHUNK layers per fill.
+constexpr int DS_TAB_CHUNK = 12;
+struct DitTableArgs {
+  DitLayerPtrs p[DS_TAB_CHUNK];
+  int n;
+  DitLayerPtrs* out;
+};
+
 template <typename WT, int D>
-__global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layer(DitLayerArgs a) {
+__global__ __launch_bounds__(DS_THREADS, 1) void k_dit_layers(DitLayerArgs a) {
   extern __shared__ __align__(16) char smem[];
   char* rA = smem;
   float* red = reinterpret_cast<float*>(rA + ds_region_a(D));
   int* sflag = reinterpret_cast<int*>(red + 2 * 4 * 256);
-  const int tid = threadIdx.x;
-  const int wg = blockIdx.x, G = gridDim.x;
-  int finished_tiles = 0;        // DOWN tiles this workgroup completed
-  typename DsW<WT>::raw wdown[DS_WSLOTS];
-  bool have_down = false;
+  typename DsW<WT>::raw wdown[DS_WSLOTS], wqkv[DS_WSLOTS];
+  bool have_down = false, have_qkv = false;
 
   // A failed earlier launch of this run: its flag is requested now and
   // acted on at this launch's first wait, where the workgroup poisons the
-  // stream and leaves (QKV waits for nothing, so it needs no check).
-  if (tid == 0) sflag[2] = 0;
+  // stream and leaves (the first QKV waits for nothing, so it needs no check).
+  if (ds_tid() == 0) sflag[2] = 0;
   __syncthreads();
   const int prev_err = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!ds_phase<WT, D, DP_QKV>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_SAATT>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_SAO>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_CAQ>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_CAATT>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_CAO>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  if (!ds_phase<WT, D, DP_UP>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down)) return;
-  ds_phase<WT, D, DP_DOWN>(a, prev_err, rA, red, sflag, finished_tiles, wdown, have_down);
+  for (int l = a.l0; l < a.l1; l++) {
+    const DsLayer y = ds_layer<D>(a, l);
+    int ft = 0;   // DOWN tiles of this layer this workgroup completed
+    if (!ds_phase<WT, D, DP_QKV>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_SAATT>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_SAO>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_CAQ>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_CAATT>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_CAO>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_UP>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+    if (!ds_phase<WT, D, DP_DOWN>(a, y, prev_err, rA, red, sflag, ft, wdown, have_down, wqkv, have_qkv)) return;
+  }
 }
 
 }  // namespace vla

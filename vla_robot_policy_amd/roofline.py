@@ -151,11 +151,11 @@ def dit_ops(cfg) -> List[Op]:
 def fused_ops(cfg) -> Dict[str, Op]:
     """Operators of kernels that fuse several of the ops above, per launch.
 
-    ``dit.layer`` is one DiT layer for one Euler step in a single launch: its
-    algorithmic bytes are what must cross HBM once per launch (the layer's
-    weights and biases, its context K/V, the residual stream in and out and
-    the layer's modulation vectors); intermediate activations stay on chip.
-    Its FLOPs are those of the layer's GEMMs and attention.
+    ``dit.layers`` is every DiT layer of one Euler step in a single launch:
+    its algorithmic bytes are what must cross HBM once per launch (each
+    layer's weights and biases, its context K/V, the residual stream in and
+    out and its modulation vectors); intermediate activations stay on chip.
+    Its FLOPs are those of the layers' GEMMs and attention.
     """
     out: Dict[str, Op] = {}
     if cfg.kind in ("dit", "step") and cfg.dit is not None:
@@ -166,7 +166,7 @@ def fused_ops(cfg) -> Dict[str, Op]:
         weights = (_wbytes(w, 3 * D, D) + 3 * _wbytes(w, D, D) + _wbytes(w, d.mlp, D) + _wbytes(w, D, d.mlp)
                    + 4.0 * (3 * D + 3 * D + d.mlp + D))
         nbytes = weights + ACT * C * 2 * D + 4.0 * n * D * 2 + 4.0 * 9 * D
-        out["dit.layer"] = Op("dit.layer", "dit_step", flops, nbytes, d.layers * cfg.steps, _compute(w))
+        out["dit.layers"] = Op("dit.layers", "dit_step", d.layers * flops, d.layers * nbytes, cfg.steps, _compute(w))
     return out
 
 
