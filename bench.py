@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ms per VLA step at batch 1 (36L backbone + K-step DiT) + % of MFMA/HBM roofline"
 WORKLOADS = {
+    1: "one pre-norm decoder block, seq 64, fp32 (hidden 256, GQA 4/2 x 64, SwiGLU 688)",
     2: "36-layer backbone prefill, seq 256, bf16 (hidden 2560, GQA 32/8 x 128, SwiGLU 9728), final RMSNorm",
     3: "DiT flow-matching sampler, bf16: 36 layers x 4 Euler steps, chunk 16x7, 256 context tokens",
     4: ("full single-camera VLA step, bf16: ViT 24L (224x224, 14-px patches) -> 2x2 merger -> 36L backbone "
@@ -259,9 +260,10 @@ def phase_fractions(kernels, bound):
 
 
 def component_bench(cfg, steps, warmup):
-    """Backbone prefill alone (vla_backbone_prefill) or the flow sampler
-    alone (vla_flow_euler_sample), launched eagerly back to back on one
-    stream; returns (ms per call, p50, p90)."""
+    """One block (vla_block_forward), the backbone prefill alone
+    (vla_backbone_prefill) or the flow sampler alone (vla_flow_euler_sample),
+    launched eagerly back to back on one stream; returns (ms per call, p50,
+    p90)."""
     import numpy as np
     import torch
     from synth import make_inputs, make_weights
@@ -270,10 +272,21 @@ def component_bench(cfg, steps, warmup):
 
     t0 = time.time()
     W, I = make_weights(cfg), make_inputs(cfg)
-    dw = DeviceWeights(cfg, W, keep_host=False, threads=16, packed=PACKED and cfg.kind == "backbone" and not cfg.block.a8)
+    dw = DeviceWeights(cfg, W, keep_host=False, threads=16,
+                       packed=PACKED and cfg.kind in ("block", "backbone") and cfg.wdtype != "f32" and not cfg.block.a8)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
-    if cfg.kind == "backbone":
+    if cfg.kind == "block":
+        bb = dw.build_backbone()
+        x = upload_input(I["x"])
+        out = torch.empty((cfg.seq, cfg.block.hidden), dtype=torch.float32 if cfg.wdtype == "f32" else torch.int16,
+                          device=dev)
+        need = lib.vla_block_workspace_bytes(dw.block_cfg, cfg.seq)
+        ws = workspace(need)
+
+        def call():
+            lib.check(lib.vla_block_forward(dw.block_cfg, bb.layers[0], x, out, cfg.seq, ws, need, stream))
+    elif cfg.kind == "backbone":
         bb = dw.build_backbone()
         x = upload_input(I["x"])
         out = torch.empty((cfg.seq, cfg.block.hidden), dtype=torch.int16, device=dev)
@@ -513,25 +526,25 @@ def main():
             raise SystemExit("--euler-steps must be in [1, 64]")
         cfg = cfg.replace(steps=a.euler_steps)
         variant += f"; sampler run for {a.euler_steps} Euler step{'s' if a.euler_steps > 1 else ''} instead of the workload's"
-    if cfg.kind in ("backbone", "dit"):
+    if cfg.kind in ("block", "backbone", "dit"):
         if a.only_label or a.fused is not None or a.shape_cache:
             raise SystemExit("--only-label, --fused and --shape-cache need a policy step (--config 4 or 5)")
         ms, p50, p90 = component_bench(cfg, a.steps, a.warmup)
         b = roofline.bound(cfg)
-        what = "36-layer backbone prefill" if cfg.kind == "backbone" else "flow-matching action sampler"
+        what = {"block": "decoder block", "backbone": "36-layer backbone prefill", "dit": "flow-matching action sampler"}[cfg.kind]
         print(json.dumps({
             "metric": f"ms per {what} at batch 1 + % of MFMA/HBM roofline", "value": round(ms, 4), "unit": "ms",
             "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False,
-            "scaling": "weak", "vs_baseline": None, "dtype": cfg.wdtype if cfg.wdtype in ("fp8", "int8") else "bf16",
+            "scaling": "weak", "vs_baseline": None, "dtype": cfg.wdtype if cfg.wdtype in ("fp8", "int8", "f32") else "bf16",
             "data": "synthetic",
-            "config": {"workload": WORKLOADS[a.config] + variant, "global_batch": 1, "seq_len": cfg.seq if cfg.kind == "backbone" else None,
+            "config": {"workload": WORKLOADS[a.config] + variant, "global_batch": 1, "seq_len": cfg.seq if cfg.kind != "dit" else None,
                        "euler_steps": cfg.steps if cfg.kind == "dit" else None, "parallelism": "single GPU"},
             "p50_ms": round(p50, 4), "p90_ms": round(p90, 4),
             "roofline_bound_ms": round(b.seconds * 1e3, 4), "roofline_frac": round(b.seconds * 1e3 / ms, 4),
             "launch": "eager (one entry-point call per step, kernels queued back to back)"}), flush=True)
         return
     if cfg.kind != "step":
-        raise SystemExit("bench.py times policy steps (--config 4 or 5), the backbone (2) or the sampler (3)")
+        raise SystemExit("bench.py times policy steps (--config 4 or 5), a block (1), the backbone (2) or the sampler (3)")
     if a.fused is not None:
         fused_bench(cfg, a.fused, a.steps, a.warmup)
         return
