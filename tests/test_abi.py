@@ -26,9 +26,11 @@ def llm_cfg(**kw):
 
 
 def test_workspace_sizes_scale_with_shape():
-    a = lib.vla_block_workspace_bytes(llm_cfg(), 104)
+    # (not monotonic in between: split-K partials depend on the tiles picked
+    # for each row count)
+    a = lib.vla_block_workspace_bytes(llm_cfg(), 16)
     b = lib.vla_block_workspace_bytes(llm_cfg(), 256)
-    assert 0 < a < b
+    assert 0 < a < b < lib.vla_block_workspace_bytes(llm_cfg(), 1024)
     bb = lib.Backbone(cfg=llm_cfg(), n_layers=36, layers=None, final_norm=None)
     assert lib.vla_backbone_workspace_bytes(bb, 256) >= b
     assert lib.vla_block_workspace_bytes(llm_cfg(head_dim=96), 64) == 0       # unsupported -> 0
@@ -76,6 +78,16 @@ def test_dit_and_step_validation():
     d = lib.Dit(cfg=dc, layers=None)
     assert lib.vla_dit_workspace_bytes(d, 256, 16, 7, 4) > 0
     assert lib.vla_dit_workspace_bytes(d, 256, 65, 7, 4) == 0                  # chunk > 64
+    # above 16 rows (no layer kernel): widths must be multiples of 128
+    d8 = lib.Dit(cfg=lib.DitCfg(hidden=160, heads=2, head_dim=80, mlp=640, layers=2, tdim=256, ctx_dim=160, eps=1e-6,
+                                time_scale=1000.0, freq_base=10000.0, wdtype=lib.VLA_FP8_E4M3, flags=0), layers=None)
+    assert lib.vla_dit_workspace_bytes(d8, 70, 16, 7, 4) > 0                  # the layer kernel
+    assert lib.vla_dit_workspace_bytes(d8, 70, 37, 7, 4) == 0
+    assert "multiples of 128" in lib.vla_last_error()
+    d8.cfg.wdtype = lib.VLA_BF16
+    assert lib.vla_dit_workspace_bytes(d8, 70, 37, 7, 4) == 0
+    d8.cfg.hidden, d8.cfg.heads, d8.cfg.mlp, d8.cfg.ctx_dim = 1280, 16, 5120, 1280
+    assert lib.vla_dit_workspace_bytes(d8, 560, 50, 32, 10) > 0
     assert lib.vla_flow_euler_sample(d, 16, 256, 16, 16, 7, 4, 16, None, 256, 1 << 30) == lib.VLA_ERR_INVALID_ARG
     d.cfg.head_dim = 96
     assert lib.vla_flow_euler_sample(d, 16, 256, 16, 16, 7, 4, 16, None, 256, 1 << 30) == lib.VLA_ERR_SHAPE

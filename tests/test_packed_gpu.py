@@ -67,7 +67,7 @@ def _pair(gu, cfg, W):
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "int8"])
-@pytest.mark.parametrize("seq", [1, 37, 130, 400])
+@pytest.mark.parametrize("seq", [1, 37, 104, 130, 200, 400])
 def test_block_packed(gu, wdtype, seq):
     cfg = small_config("block", wdtype, seq=seq)
     W, I = make_weights(cfg), make_inputs(cfg)

@@ -208,6 +208,24 @@ void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb,
     if (em == E_ROPE && !ac) { u = 2; aq = 4; }
     else if (em == E_RESID && !ac) { wn = 2; wk = 2; nbw = 1; u = 2; split_hint = 0; target_wgs = 0; }
     else if (em == E_RESID && ac) { u = 1; aq = 4; }
+    // compensated gate/up: 256 weight rows per tile over three k-splits, so
+    // 228 workgroups each stage a third of the A rows (47.0 -> 44.7 us at
+    // 104 rows, packed weights)
+    else if (em == E_SWIGLU && ac && wdtype == VLA_BF16) { wn = 8; wk = 1; nbw = 2; u = 2; }
+  }
+  // 193..256 rows of bf16 weights: 128-row tiles for the MLP and the long-K
+  // residual GEMMs (at 256 rows, packed weights: gate/up 105 -> 90 us, down
+  // 76 -> 61 us, O projection 26.4 -> 23.9 us)
+  if (M > 192 && M <= 256 && am == A_BF16 && wdtype == VLA_BF16) {
+    if (ac && em == E_SWIGLU) { mb = 8; wn = 8; wk = 1; nbw = 2; u = 2; }
+    else if (ac && em == E_RESID) { mb = 8; wn = 2; wk = 2; nbw = 2; u = 1; split_hint = 3; target_wgs = 0; }
+    else if (!ac && em == E_RESID && N >= 2048 && K > 1024) { mb = 8; wn = 4; wk = 1; nbw = 1; u = 4; split_hint = 0; target_wgs = 0; }
+  }
+  // fp8 weights over more than 256 rows: two column blocks per wave, so each
+  // A fragment read from LDS feeds two MFMAs (gate/up at 560 rows 121 -> 103
+  // us, QKV 43 -> 41 us)
+  if (mb == 8 && am == A_BF16 && wdtype == VLA_FP8_E4M3 && !ac && (em == E_SWIGLU || em == E_ROPE)) {
+    wn = 4; wk = 1; nbw = 2; u = 2; split_hint = 1;
   }
 }
 
@@ -767,6 +785,13 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.G = cu_count();
   s.stack = dit_stack_ok(cf, n, s.G);
   s.spin = dit_spin_limit();
+  // The launch-per-operation path is validated at widths that are multiples
+  // of 128 (1280 / 5120 / 1280 context). At width 160 with more than 64
+  // context tokens it gave wrong results (bf16 and fp8) and once a device
+  // memory fault, whose cause is not known: such widths are refused there.
+  if (!s.stack && (D % 128 || cf.mlp % 128 || cf.ctx_dim % 128))
+    return fail(VLA_ERR_UNSUPPORTED, "dit: chunks the layer kernel does not take need hidden %d, mlp %d and context "
+                "width %d to be multiples of 128", D, cf.mlp, cf.ctx_dim);
   if (s.stack) {
     const size_t nd = (size_t)n * D;
     s.lx = c.take<float>((size_t)(L + 1) * nd);

@@ -32,6 +32,14 @@ bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_PACKED_ROWS(uint16_t, 7)
   VLA_GEMM_PACKED_ROWS(uint16_t, 8)
   VLA_GEMM_PACKED_RESID(uint16_t)
+  // compensated gate/up of 256 weight rows per tile at 65..112 and 193..256
+  // rows, compensated down of 128 x 64 tiles at 193..256 rows
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 7, 8, 1, 2, 2, 1, 2, 0)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 7, 8, 1, 2, 2, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 8, 8, 1, 2, 2, 1, 2, 0)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 8, 8, 1, 2, 2, 1, 2, 1)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 8, 2, 2, 2, 1, 1, 2, 0)
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 8, 2, 2, 2, 1, 1, 2, 1)
   return false;
 }
 }  // namespace vla

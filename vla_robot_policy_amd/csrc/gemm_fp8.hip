@@ -28,6 +28,11 @@ bool gemm_lookup_fp8(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_PACKED_ROWS(uint8_t, 7)
   VLA_GEMM_PACKED_ROWS(uint8_t, 8)
   VLA_GEMM_PACKED_RESID(uint8_t)
+  // more than 256 rows: two 16-column blocks per wave for gate/up and QKV
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_SWIGLU, 8, 4, 1, 2, 2, 0, 2, 0)
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_SWIGLU, 8, 4, 1, 2, 2, 0, 2, 1)
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_ROPE, 8, 4, 1, 2, 2, 0, 2, 0)
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_ROPE, 8, 4, 1, 2, 2, 0, 2, 1)
   return false;
 }
 }  // namespace vla
