@@ -95,10 +95,15 @@ struct Ctx {
   const char* label = "";  // name of the operation being launched
   std::vector<LaunchRec>* recs = nullptr;
 
+  // A planning pass hands out addresses in a reserved range that is never
+  // dereferenced, not null: code that tests a buffer's presence then takes
+  // the same branch when planning as when running, so the plan sizes the
+  // scratch for the launches that really run.
+  static constexpr uintptr_t PLAN_BASE = (uintptr_t)1 << 44;
   template <typename T>
   T* take(size_t n) {
     off = align_up(off, 256);
-    T* p = plan ? nullptr : reinterpret_cast<T*>(base + off);
+    T* p = reinterpret_cast<T*>(plan ? (char*)PLAN_BASE + off : base + off);
     off += n * sizeof(T);
     return p;
   }
@@ -756,6 +761,10 @@ struct DitState {
   uint2* fw = nullptr; size_t fw_words = 0;
   uint2* fqkv = nullptr; uint2* fq = nullptr; uint2* fdp = nullptr;
   uint16_t* u = nullptr;   // modulated LayerNorm rows of the launch-per-operation path (bf16)
+  // the launch-per-operation path normalises into u (8-bit / bf16 weights)
+  // rather than in the GEMM prologue (fp32 weights); decided from the
+  // configuration, never from u itself, which a planning pass leaves null
+  bool urows = false;
   bool stack = false;
   int G = 0;
   unsigned spin = DS_SPIN;   // poll limit of the layer kernel's bounded waits
@@ -785,13 +794,6 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
   s.G = cu_count();
   s.stack = dit_stack_ok(cf, n, s.G);
   s.spin = dit_spin_limit();
-  // The launch-per-operation path is validated at widths that are multiples
-  // of 128 (1280 / 5120 / 1280 context). At width 160 with more than 64
-  // context tokens it gave wrong results (bf16 and fp8) and once a device
-  // memory fault, whose cause is not known: such widths are refused there.
-  if (!s.stack && (D % 128 || cf.mlp % 128 || cf.ctx_dim % 128))
-    return fail(VLA_ERR_UNSUPPORTED, "dit: chunks the layer kernel does not take need hidden %d, mlp %d and context "
-                "width %d to be multiples of 128", D, cf.mlp, cf.ctx_dim);
   if (s.stack) {
     const size_t nd = (size_t)n * D;
     s.lx = c.take<float>((size_t)(L + 1) * nd);
@@ -813,7 +815,8 @@ vla_status dit_begin(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s) {
     s.h = c.take<uint16_t>((size_t)n * cf.mlp);
   }
   s.derr = c.status;      // word 0 of the workspace's status block
-  s.u = !s.stack && cf.wdtype != VLA_F32 ? c.take<uint16_t>((size_t)n * D) : nullptr;
+  s.urows = !s.stack && cf.wdtype != VLA_F32;
+  s.u = s.urows ? c.take<uint16_t>((size_t)n * D) : nullptr;
   if (s.stack) {
     // phase counters of the layer kernel live in the shared counter array
     // (every kernel leaves its counters at zero)
@@ -902,7 +905,7 @@ size_t dit_vt_elems(const vla_dit_cfg& cf, int C) { return (size_t)cf.layers * c
 
 // Cross-attention K/V of every layer from a context (one launch), and for
 // the layer kernel (vt not null) the values transposed.
-vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16_t* ckv, uint16_t* vt) {
+vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16_t* ckv, uint16_t* vt, bool transpose) {
   const vla_dit_cfg& cf = d.cfg;
   const int D = cf.hidden, L = cf.layers;
   c.label = "dit.cross_kv";
@@ -912,7 +915,7 @@ vla_status dit_cross_kv(Ctx& c, const vla_dit& d, const void* ctx, int C, uint16
   a.w = d.w_ckv; a.ldw = cf.ctx_dim; a.wscale = d.s_ckv; a.bias = d.b_ckv;
   a.c = ckv; a.ldc = L * 2 * D;
   VLA_TRY(gemm(c, a, {cf.wdtype, A_BF16, E_STORE}));
-  if (!vt) return VLA_OK;
+  if (!transpose) return VLA_OK;
   c.label = "dit.cross_vt";
   const int Cp = dit_vt_pitch(C);
   const size_t nt = (size_t)L * (Cp / 8) * D;
@@ -977,7 +980,7 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
       // the GEMM's workgroups would otherwise normalise every row again);
       // fp32 weights normalise in the GEMM's prologue.
       auto modln = [&](GemmArgs& a, int sh, int sc, const char* label) -> vla_status {
-        if (s.u) {
+        if (s.urows) {
           c.label = label;
           VLA_TRY(norm_rows(c, x, D, n, D, xs.rs, 0, cf.eps, mv(sc), 1, mv(sh), s.u, nullptr, D));
           a.a = s.u; a.lda = D;
@@ -986,7 +989,7 @@ vla_status dit_steps(Ctx& c, const vla_dit& d, const DitIO& io, DitState& s, con
         }
         return VLA_OK;
       };
-      const int am_norm = s.u ? A_BF16 : A_NORM;
+      const int am_norm = s.urows ? A_BF16 : A_NORM;
       {  // adaLN(LN) -> self-attn QKV
         GemmArgs a = gargs();
         VLA_TRY(modln(a, 0, 1, "dit.sa_norm"));
@@ -1086,7 +1089,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
   uint16_t* ckv = c.take<uint16_t>((size_t)io.ctx_len * d.cfg.layers * 2 * d.cfg.hidden);
   uint16_t* vt = s.stack ? c.take<uint16_t>(dit_vt_elems(d.cfg, io.ctx_len)) : nullptr;
   VLA_TRY(dit_conditioning(c, d, io, s));
-  VLA_TRY(dit_cross_kv(c, d, io.ctx, io.ctx_len, ckv, vt));
+  VLA_TRY(dit_cross_kv(c, d, io.ctx, io.ctx_len, ckv, vt, s.stack));
   VLA_TRY(dit_in_proj(c, d, io, s));
   return dit_steps(c, d, io, s, ckv, vt, 0, io.K);
 }
@@ -1542,7 +1545,7 @@ vla_status step_sched(Ctx& c, const vla_step_plan& P, const vla_step_shape& sh) 
   uint16_t* ckv = c.take<uint16_t>((size_t)io.ctx_len * P.dit.cfg.layers * 2 * P.dit.cfg.hidden);
   uint16_t* vt = ds.stack ? c.take<uint16_t>(dit_vt_elems(P.dit.cfg, io.ctx_len)) : nullptr;
   VLA_TRY(dit_conditioning(c, P.dit, io, ds));
-  VLA_TRY(dit_cross_kv(c, P.dit, io.ctx, io.ctx_len, ckv, vt));
+  VLA_TRY(dit_cross_kv(c, P.dit, io.ctx, io.ctx_len, ckv, vt, ds.stack));
   VLA_TRY(dit_in_proj(c, P.dit, io, ds));
   return dit_steps(c, P.dit, io, ds, ckv, vt, 0, io.K);
 }
@@ -1593,7 +1596,7 @@ vla_status fused_sched(Ctx& cv, Ctx& ca, const vla_step_plan& P, const vla_step_
   uint16_t* ctx = nullptr;
   int S = 0;
   VLA_TRY(vlm_sched(cv, P, sh, ctx, S));
-  VLA_TRY(dit_cross_kv(cv, P.dit, ctx, S, cur, cur_vt));
+  VLA_TRY(dit_cross_kv(cv, P.dit, ctx, S, cur, cur_vt, vt_elems > 0));
   if (live) {
     VLA_HIP(hipEventRecord(ev->ctx_ready, cv.st));
     VLA_HIP(hipStreamWaitEvent(ca.st, ev->ctx_ready, 0));
