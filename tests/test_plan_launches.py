@@ -57,6 +57,24 @@ if a["kind"] == "dit":
     out["need"] = need
     out["status"] = lib.vla_flow_euler_sample(d, buf(C * cd * 2), C, buf(n * A * 4), n, A, K, buf(n * A * 4),
                                               buf(K * n * A * 4), buf(need), need) if need else -99
+elif a["kind"] == "vit":
+    img, pt, D, mlp, L, od = a["image"], 14, 128, 512, 2, 256
+    cfg = lib.VitCfg(image=img, patch=pt, channels=3, hidden=D, heads=2, head_dim=64, mlp=mlp, layers=L, merge=2,
+                     out_dim=od, eps=1e-6, wdtype=lib.VLA_BF16, flags=0)
+    layers = (lib.VitLayer * L)()
+    for ly in layers:
+        ly.ln1_g = buf(D * 4); ly.ln1_b = buf(D * 4); ly.ln2_g = buf(D * 4); ly.ln2_b = buf(D * 4)
+        ly.w_qkv = buf(3 * D * D * 2); ly.b_qkv = buf(3 * D * 4); ly.w_o = buf(D * D * 2); ly.b_o = buf(D * 4)
+        ly.w_up = buf(mlp * D * 2); ly.b_up = buf(mlp * 4); ly.w_down = buf(D * mlp * 2); ly.b_down = buf(D * 4)
+    g = img // pt
+    v = lib.Vit(cfg=cfg, layers=layers, w_pe=buf(D * 3 * pt * pt * 2), b_pe=buf(D * 4), pos=buf(g * g * D * 4),
+                mln_g=buf(D * 4), mln_b=buf(D * 4), w_m1=buf(16 * D * D * 2), b_m1=buf(4 * D * 4), w_m2=buf(od * 4 * D * 2),
+                b_m2=buf(od * 4))
+    n = a["n_images"]
+    need = lib.vla_vit_workspace_bytes(v, n)
+    out["need"] = need
+    out["status"] = lib.vla_vit_encode(v, buf(n * 3 * img * img * 2), n, buf(n * (g * g // 4) * od * 4), None, buf(need),
+                                       need) if need else -99
 else:
     Hd, I, S = 256, 688, a["seq"]
     cfg = lib.BlockCfg(hidden=Hd, n_q_heads=4, n_kv_heads=2, head_dim=64, intermediate=I, rope_base=1e4, eps=1e-6,
@@ -114,6 +132,15 @@ def test_dit_plan_covers_launches(shim, chunk, ctx, w):
 @pytest.mark.parametrize("seq,w", [(37, "bf16"), (104, "bf16"), (200, "bf16"), (400, "fp8"), (130, "int8")])
 def test_backbone_plan_covers_launches(shim, seq, w):
     res, n, over = run_child(shim, kind="backbone", seq=seq, w=w)
+    assert res["status"] == 0 and res["need"] > 0, res
+    assert n > 10
+    assert not over, over
+
+
+# the vision encoder and merger: one and two images of 8 x 8 and 16 x 16 patches
+@pytest.mark.parametrize("image,n_images", [(112, 1), (224, 1), (224, 2)])
+def test_vit_plan_covers_launches(shim, image, n_images):
+    res, n, over = run_child(shim, kind="vit", image=image, n_images=n_images, w="bf16")
     assert res["status"] == 0 and res["need"] > 0, res
     assert n > 10
     assert not over, over

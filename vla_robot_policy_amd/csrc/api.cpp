@@ -228,10 +228,24 @@ void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb,
   }
   // fp8 weights over more than 256 rows: two column blocks per wave, so each
   // A fragment read from LDS feeds two MFMAs (gate/up at 560 rows 121 -> 103
-  // us, QKV 43 -> 41 us)
+  // us, QKV 43 -> 41 us; the cross K/V GEMM at 560 rows, 256 columns per
+  // tile, 394 -> 268 us)
   if (mb == 8 && am == A_BF16 && wdtype == VLA_FP8_E4M3 && !ac && (em == E_SWIGLU || em == E_ROPE)) {
     wn = 4; wk = 1; nbw = 2; u = 2; split_hint = 1;
   }
+  if (mb == 8 && am == A_BF16 && wdtype == VLA_FP8_E4M3 && !ac && em == E_STORE && N >= 16 * 1024) {
+    wn = 8; wk = 1; nbw = 2; u = 2; split_hint = 1;
+  }
+  // 65..112 rows, plain stores: the wide cross K/V GEMM takes two column
+  // blocks per wave (82 -> 67 us at 104 rows), narrow ones more workgroups
+  // (the 2560 -> 1280 projector 17.6 -> 13.8 us with five k-splits)
+  if (mb == 7 && em == E_STORE && am == A_BF16 && !ac && (wdtype == VLA_BF16 || wdtype == VLA_FP8_E4M3)) {
+    if (N >= 64 * 1024) { wn = 4; wk = 1; nbw = 2; u = 2; }
+    else target_wgs = 100;
+  }
+  // 17..64 rows, plain stores over K of 4096 or more (the merger's two
+  // Linears at 64 rows): four k-splits (16.3 -> 12.4 us, 16.7 -> 13.5 us)
+  if (mid_rows && em == E_STORE && K >= 4096) split_hint = 4;
 }
 
 // Launch one GEMM. For a residual epilogue, *produced receives the column
@@ -411,11 +425,15 @@ vla_status stage_stream(Ctx& c, Stream& st, int M, int N, const void* src, int s
 
 // Normalise M rows of x once, into bf16 (and the remainder plane when out_lo).
 vla_status norm_rows(Ctx& c, const float* x, int ldx, int M, int K, RowStats rs, int rms, float eps, const float* g,
-                     int g_plus_one, const float* bsh, uint16_t* out, uint16_t* out_lo, int ldo) {
+                     int g_plus_one, const float* bsh, uint16_t* out, uint16_t* out_lo, int ldo, int merge = 0,
+                     int vgrid = 0, int n_patches = 0) {
   if (K % 4 != 0 || ldx % 4 != 0 || ldo % 4 != 0) return fail(VLA_ERR_SHAPE, "norm: row length %d must be a multiple of 4", K);
+  if (merge && (vgrid % merge || n_patches != vgrid * vgrid || M % n_patches || ldo != merge * merge * K))
+    return fail(VLA_ERR_SHAPE, "norm: merge %d of a %d-patch grid does not tile", merge, vgrid);
   NormArgs a{};
   a.x = x; a.ldx = ldx; a.M = M; a.K = K; a.rs = rs; a.rms = rms; a.eps = eps;
   a.g = g; a.g_plus_one = g_plus_one; a.bsh = bsh; a.out = out; a.out_lo = out_lo; a.ldo = ldo;
+  a.merge = merge; a.vgrid = vgrid; a.n_patches = n_patches;
   return launch(c, k_norm_rows_ref(), dim3(M), dim3(256), 0, {arg(a)});
 }
 
@@ -1127,6 +1145,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
   uint16_t* ao = c.take<uint16_t>((size_t)S * D);
   uint16_t* h = c.take<uint16_t>((size_t)S * cf.mlp);
   uint16_t* m1 = c.take<uint16_t>((size_t)Mm * MD);
+  uint16_t* mz = c.take<uint16_t>((size_t)Mm * MD);   // LayerNormed patches, 2x2 groups concatenated
   uint16_t* zn = c.take<uint16_t>((size_t)S * D);      // LayerNorm-ed rows (bf16)
   {  // patchify -> Linear + bias + position table (+ row statistics)
     c.label = "vit.patch_embed";
@@ -1201,15 +1220,18 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
     }
   }
   if (vit_out) { c.label = "vit.out"; VLA_TRY(convert_rows(c, z, D, S, D, vit_out, D, 1)); }
-  {  // LN -> 2x2 concat -> Linear -> GELU
+  {  // LN of every patch, written straight into its 2x2 group of the merged rows
+    c.label = "mrg.ln";
+    VLA_TRY(norm_rows(c, z, D, S, D, zst.rs, 0, cf.eps, v.mln_g, 0, v.mln_b, mz, nullptr, MD, cf.merge, grid, np));
+  }
+  {  // Linear -> GELU
     c.label = "mrg.fc1";
     GemmArgs a = gargs();
     a.M = Mm; a.N = MD; a.K = MD;
-    a.a = z; a.lda = D; a.rs = zst.rs; a.norm_rms = 0; a.eps = cf.eps; a.g = v.mln_g; a.bsh = v.mln_b;
-    a.vgrid = grid; a.n_patches = np; a.merge = cf.merge; a.n_merged = nm;
+    a.a = mz; a.lda = MD;
     a.w = v.w_m1; a.ldw = MD; a.bias = v.b_m1; a.act = ACT_GELU;
     a.c = m1; a.ldc = MD;
-    VLA_TRY(gemm(c, a, {VLA_BF16, A_MERGE, E_STORE}));
+    VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE}));
   }
   {  // Linear -> visual tokens (fp32)
     c.label = "mrg.fc2";

@@ -1,5 +1,5 @@
 // Weight-streaming GEMM for small M (16..600 rows), y = prologue(A) . W^T,
-// with fused prologues (row norms, patch gather, merge gather) and fused
+// with fused prologues (row norms, patch gather) and fused
 // epilogues (bias, GELU/SiLU, RoPE, SwiGLU,
 // residual / gated residual with per-tile row moments for the next norm).
 //
@@ -32,7 +32,7 @@
 
 namespace vla {
 
-enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_MERGE = 4, A_FP8 = 6, A_I8 = 7 };
+enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_FP8 = 6, A_I8 = 7 };
 // 8-bit activation codes with a per-row scale (W8A8)
 constexpr bool a_codes(int am) { return am == A_FP8 || am == A_I8; }
 enum EMode { E_STORE = 0, E_ROPE = 1, E_SWIGLU = 2, E_RESID = 3 };
@@ -41,20 +41,19 @@ enum ActKind { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 struct GemmArgs {
   int M, N, K;
   // ---- A source
-  const void* a;         // BF16/F32/NORM/MERGE: matrix [rows, lda]; PATCH: bf16 images
+  const void* a;         // BF16/F32/NORM: matrix [rows, lda]; PATCH: bf16 images
   const void* a_lo;      // BF16 with compensation: remainder plane, same layout as a
   const float* a_scale;  // FP8 / I8: E4M3FN or int8 codes [rows, lda] in a, one float32 scale per row here
                          // (W8A8: the codes are staged as bytes and widened to bf16 at fragment
                          // load, which is exact, so the bf16 MFMA forms exact products)
   int lda;
-  RowStats rs;           // NORM/MERGE: per-tile row moments of the source rows
+  RowStats rs;           // NORM: per-tile row moments of the source rows
   int norm_rms;          // 1: RMSNorm (no mean subtraction), 0: LayerNorm
   float eps;
   const float* g;        // per-k gain (NULL = 1)
   int g_plus_one;        // gain is 1 + g[k] (adaLN scale)
   const float* bsh;      // per-k shift (NULL = 0)
-  int img, patch, chans, vgrid, n_patches;   // PATCH / MERGE geometry
-  int merge, n_merged;                       // MERGE
+  int img, patch, chans, vgrid, n_patches;   // PATCH geometry
   // ---- W
   const void* w;
   int ldw;
@@ -204,7 +203,7 @@ struct GemmTile {
                 "weight chunk rows must split evenly into 16-byte groups over the workgroup");
   static constexpr int SMEM_A = 2 * ABUF + 2 * WBUF;
   static constexpr int SMEM_T = WK * BM * TPITCH * 4;   // one fp32 tile slice per k-wave
-  static constexpr int NROWST = (AM == A_MERGE) ? 4 * BM : BM;   // normaliser entries
+  static constexpr int NROWST = BM;   // normaliser entries
   static constexpr int SMEM = (SMEM_A > SMEM_T ? SMEM_A : SMEM_T) + NROWST * 8 + 64;
   static_assert(SMEM <= 160 * 1024, "tile exceeds the 160 KiB of LDS of a compute unit");
   // threads serving one normalised row: a power of two, at most 64
@@ -376,13 +375,13 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     if constexpr (WLDS) store_w(buf, r);
   };
 
-  // ---- per-row normaliser (NORM / MERGE): (value to subtract, 1/std) of
+  // ---- per-row normaliser (NORM): (value to subtract, 1/std) of
   // every source row of the tile. TPR consecutive threads serve a row; the
   // first LB of each thread's tile partials are requested here, before the
   // first A and W loads, and merged after them (shifted sums, then a fixed
   // butterfly), so they share one memory latency with the weights.
   constexpr int NR = T::NROWST, TPR = T::TPR, LB = 8;
-  constexpr bool NORMED = AM == A_NORM || AM == A_MERGE;
+  constexpr bool NORMED = AM == A_NORM;
   constexpr int NPASS = NORMED ? (NR + NT / TPR - 1) / (NT / TPR) : 1;   // row passes
   float2 rsv[NPASS][NORMED ? LB : 1];
   int rsrc[NPASS];
@@ -402,20 +401,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       const int r = ps * (NT / TPR) + rr;
       int src = -1;
       if (r < NR) {
-        if (AM == A_NORM) {
-          int m = m0 + r;
-          src = m < p.M ? m : -1;
-        } else {
-          int mr = r >> 2, sub = r & 3;         // merged row, 2x2 member
-          int m = m0 + mr;
-          if (m < p.M && sub < p.merge * p.merge) {
-            int per = p.n_merged, im = m / per, mm = m % per;
-            int gq = p.vgrid / p.merge;
-            int R = mm / gq, C = mm % gq;
-            int dy = sub / p.merge, dx = sub % p.merge;
-            src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
-          }
-        }
+        const int m = m0 + r;
+        src = m < p.M ? m : -1;
       }
       rsrc[ps] = src;
       load_parts(rsv[ps], src, 0);
@@ -485,15 +472,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
           t4[e] = bf2f(bload2(ars, (r < BM && m < p.M && kk < p.K) ? off : BUF_OOB));
         }
         ar[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
-      } else if constexpr (AM == A_MERGE) {
-        int D = p.lda;
-        int per = p.n_merged, im = m / per, mm = m % per;
-        int gq = p.vgrid / p.merge;
-        int R = mm / gq, C = mm % gq;
-        int sub = k / D, d = k % D;
-        int dy = sub / p.merge, dx = sub % p.merge;
-        int src = im * p.n_patches + (R * p.merge + dy) * p.vgrid + C * p.merge + dx;
-        ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)src * D + d) * 4u : BUF_OOB));
       }
     }
   };
@@ -502,14 +480,11 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     char* base = sA + buf * T::ABUF;
     const int k = kc + ac4;
     float4 ag = make_float4(1.f, 1.f, 1.f, 1.f), ab = make_float4(0.f, 0.f, 0.f, 0.f);
-    int sub = 0;
-    if constexpr (AM == A_NORM || AM == A_MERGE) {
-      int kk = (AM == A_MERGE) ? (k % p.lda) : k;
-      if (AM == A_MERGE) sub = k / p.lda;
+    if constexpr (AM == A_NORM) {
       if (k < p.K) {
-        if (p.g) ag = *reinterpret_cast<const float4*>(p.g + kk);
+        if (p.g) ag = *reinterpret_cast<const float4*>(p.g + k);
         if (p.g_plus_one) { ag.x += 1.f; ag.y += 1.f; ag.z += 1.f; ag.w += 1.f; }
-        if (p.bsh) ab = *reinterpret_cast<const float4*>(p.bsh + kk);
+        if (p.bsh) ab = *reinterpret_cast<const float4*>(p.bsh + k);
       }
     }
 #pragma unroll
@@ -528,9 +503,9 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         // raw copy of 8 bf16 or 16 fp8 codes (CT is the source type; zeros beyond the edge)
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
         continue;
-      } else if constexpr (AM == A_NORM || AM == A_MERGE) {
+      } else if constexpr (AM == A_NORM) {
         v = ar[i];
-        float2 rs = sRow[AM == A_MERGE ? r * 4 + sub : r];
+        float2 rs = sRow[r];
         v.x = ok ? (v.x - rs.x) * rs.y * ag.x + ab.x : 0.f;
         v.y = ok ? (v.y - rs.x) * rs.y * ag.y + ab.y : 0.f;
         v.z = ok ? (v.z - rs.x) * rs.y * ag.z + ab.z : 0.f;

@@ -14,7 +14,6 @@ bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_WIDE_AC(uint16_t, __bf16, A_BF16, E_SWIGLU)
   VLA_GEMM_NARROW_AC(uint16_t, __bf16, A_BF16, E_RESID)
   VLA_GEMM_NARROW(uint16_t, __bf16, A_PATCH, E_RESID)
-  VLA_GEMM_NARROW(uint16_t, __bf16, A_MERGE, E_STORE)
   // compensated MLP tiles: down at 65-112 rows with one k-step per wave and
   // four activation chunks in flight; the packed gate/up and down tiles
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 7, 4, 2, 1, 1, 1, 4, 0)
@@ -40,6 +39,8 @@ bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_SWIGLU, 8, 8, 1, 2, 2, 1, 2, 1)
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 8, 2, 2, 2, 1, 1, 2, 0)
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 8, 2, 2, 2, 1, 1, 2, 1)
+  // wide plain stores at 65..112 rows: two column blocks per wave
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_STORE, 7, 4, 1, 2, 2, 0, 2, 0)
   return false;
 }
 }  // namespace vla

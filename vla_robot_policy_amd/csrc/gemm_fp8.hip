@@ -33,6 +33,10 @@ bool gemm_lookup_fp8(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_SWIGLU, 8, 4, 1, 2, 2, 0, 2, 1)
   VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_ROPE, 8, 4, 1, 2, 2, 0, 2, 0)
   VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_ROPE, 8, 4, 1, 2, 2, 0, 2, 1)
+  // wide plain stores: 256 columns per tile beyond 256 rows, two column
+  // blocks per wave at 65..112 rows
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_STORE, 8, 8, 1, 2, 2, 0, 2, 0)
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_STORE, 7, 4, 1, 2, 2, 0, 2, 0)
   return false;
 }
 }  // namespace vla

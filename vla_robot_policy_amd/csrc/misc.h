@@ -280,7 +280,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* x, int x_f32, in
 
 // RMSNorm (x * rstd * g) or LayerNorm ((x - mean) * rstd * g + b, g given as
 // 1 + g when g_plus_one), the row moments merged from the writer's tiles.
-// With out_lo, also the remainder lo = bf16(v - hi) of each value.
+// With out_lo, also the remainder lo = bf16(v - hi) of each value. With a
+// merge geometry, each row (a patch) lands in its segment of a merged row.
 __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
   __shared__ float2 snc;
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -331,18 +332,27 @@ __global__ __launch_bounds__(256) void k_norm_rows(NormArgs p) {
     if (tid == 0) p.oscale[r] = __fdiv_rn(am, qmax);
     return;
   }
+  // destination of the row: its own row, or its segment of a merged row
+  size_t obase = (size_t)r * p.ldo;
+  if (p.merge) {
+    const int im = r / p.n_patches, pi = r % p.n_patches, pr = pi / p.vgrid, pc = pi % p.vgrid;
+    const int gq = p.vgrid / p.merge;
+    const int mrow = im * (p.n_patches / (p.merge * p.merge)) + (pr / p.merge) * gq + pc / p.merge;
+    const int seg = (pr % p.merge) * p.merge + pc % p.merge;
+    obase = (size_t)mrow * p.ldo + (size_t)seg * p.K;
+  }
   auto put = [&](int k, float4 x, float4 gg, float4 bb) {
     const float4 uu = norm4(x, gg, bb);
     const float u0 = uu.x, u1 = uu.y, u2 = uu.z, u3 = uu.w;
     uint2 h;
     h.x = pack_bf2(u0, u1);
     h.y = pack_bf2(u2, u3);
-    *reinterpret_cast<uint2*>(p.out + (size_t)r * p.ldo + k) = h;
+    *reinterpret_cast<uint2*>(p.out + obase + k) = h;
     if (p.out_lo) {
       uint2 l;
       l.x = pack_bf2(u0 - bf2f(f2bf(u0)), u1 - bf2f(f2bf(u1)));
       l.y = pack_bf2(u2 - bf2f(f2bf(u2)), u3 - bf2f(f2bf(u3)));
-      *reinterpret_cast<uint2*>(p.out_lo + (size_t)r * p.ldo + k) = l;
+      *reinterpret_cast<uint2*>(p.out_lo + obase + k) = l;
     }
   };
 #pragma unroll

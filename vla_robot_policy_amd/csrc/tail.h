@@ -29,6 +29,11 @@ struct NormArgs {
   uint16_t* out; uint16_t* out_lo; int ldo;            // bf16 result, optional remainder plane
   uint8_t* out8; float* oscale;                        // instead: 8-bit codes [M, ldo] and row scales (K <= 4096)
   int out8_int8;                                       //   int8 codes (else E4M3FN)
+  // merge > 0: the rows are patches of images of vgrid x vgrid patches
+  // (n_patches each, raster order); patch row r is written as segment
+  // (dy * merge + dx) of merged row (image, R, C), where (merge R + dy,
+  // merge C + dx) is its grid position (segments K wide, ldo = merge^2 K)
+  int merge, vgrid, n_patches;
 };
 
 }  // namespace vla
