@@ -2,7 +2,8 @@
 
 Each source compiles to an object in parallel, then hipcc links the shared
 library. Flags: -O3, AOT for gfx950 only, and packed fp32 instructions
-disabled in device code.
+disabled in device code; the attention kernels also keep MFMA accumulators
+in ordinary vector registers.
 """
 
 from __future__ import annotations
@@ -17,7 +18,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvla.so")
-SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_int8.hip", "gemm_f32.hip", "kernels_misc.hip", "dit_stack.hip"]
+SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_fp8.hip", "gemm_int8.hip", "gemm_f32.hip", "kernels_misc.hip", "attention.hip",
+           "dit_stack.hip"]
+# per-source additions: the attention kernels keep MFMA accumulators in
+# ordinary vector registers (their softmax reads every score tile)
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -26,7 +31,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, [])
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

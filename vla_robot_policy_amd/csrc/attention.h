@@ -4,7 +4,10 @@
 // blocks of 32 staged in LDS (K row-major, V transposed), several blocks per
 // stage: a stage's K and V are requested at once (one memory latency for
 // all of them) and the next stage is requested before the current one is
-// computed. The scores are
+// computed. A stage's scores are computed for all its blocks at once
+// (independent MFMA chains), followed by one online-softmax update and the
+// O MFMAs, so the serial max / exp / rescale chain runs once per stage
+// rather than once per 32 keys. The scores are
 // computed transposed, S^T = K Q^T, so a lane holds 8 keys of a single query:
 // the running max / sum of that query live in the lane (plus a 4-way
 // exchange across lane groups), and the exponentiated scores are already in
@@ -12,6 +15,8 @@
 // With grouped KV heads one workgroup serves up to 4 query heads that share
 // one KV head, so each K/V block is fetched once for all of them.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace vla {
@@ -49,6 +54,11 @@ template <> struct ATraits<__bf16> {
     F f; f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>((const uint16_t*)base + off)); return f;
   }
   __device__ static F lfrag(const char* p) { F f; f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); return f; }
+  // the fragment's load has completed past this point
+  __device__ static void ready(const F& f) {
+    const uint4 u = __builtin_bit_cast(uint4, f.v);
+    asm volatile("" ::"v"(u.x), "v"(u.y), "v"(u.z), "v"(u.w));
+  }
   // V^T fragment: keys {4g..4g+3} at p0 and {16+4g..} at p1 (4 elements each)
   __device__ static F lfrag2(const char* p0, const char* p1) {
     uint2 a = *reinterpret_cast<const uint2*>(p0), b = *reinterpret_cast<const uint2*>(p1);
@@ -82,6 +92,10 @@ template <> struct ATraits<float> {
     const float4* p = reinterpret_cast<const float4*>((const float*)base + off);
     float4 a = p[0], b = p[1];
     F f; f.lo = (f32x4){a.x, a.y, a.z, a.w}; f.hi = (f32x4){b.x, b.y, b.z, b.w}; return f;
+  }
+  __device__ static void ready(const F& f) {
+    asm volatile("" ::"v"(f.lo[0]), "v"(f.lo[1]), "v"(f.lo[2]), "v"(f.lo[3]), "v"(f.hi[0]), "v"(f.hi[1]), "v"(f.hi[2]),
+                 "v"(f.hi[3]));
   }
   __device__ static F lfrag(const char* p) {
     float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
@@ -146,6 +160,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   const int kvis = p.causal ? min(p.Sk, wg_row_end) : p.Sk;
   const int kbeg = sp * p.kchunk;
   const int kend = min(kvis, kbeg + p.kchunk);
+  const int klim = p.causal ? min(kend, qrow + 1) : kend;   // this lane's visible keys end
+  const int kfull = p.causal ? min(kend, row0 + 1) : kend;   // keys every query of the wave sees
 
   // K / V of one stage (NBUF blocks from key kb0) into registers: thread
   // group e = tid + i * 256 of a block is key e % 32, dims (e / 32) * 8, so
@@ -177,9 +193,11 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
         for (int t = 0; t < 8; t++) TR::rput(vd + (d8 + t) * VPITCH, rv[b][i], t);
       }
   };
-  load_stage(kbeg);
-
-  // Q^T fragments (B operand): query qn, dims ds*32 + grp*8 .. +8
+  // Q^T fragments (B operand): query qn, dims ds*32 + grp*8 .. +8. They are
+  // requested before the first K / V stage and made ready before the key
+  // loop: a load still pending at the loop's entry makes the compiler wait
+  // for every outstanding load before the first MFMA of each stage, which
+  // would include the next stage's prefetch.
   F qf[DP / 32];
 #pragma unroll
   for (int ds = 0; ds < DP / 32; ds++) {
@@ -187,68 +205,112 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
     if (qrow < p.Sq && d < p.D) qf[ds] = TR::gload(p.q, (size_t)qrow * p.ldq + (size_t)head * p.D + d);
     else qf[ds] = zero_frag(F{});
   }
+  load_stage(kbeg);
+#pragma unroll
+  for (int ds = 0; ds < DP / 32; ds++) TR::ready(qf[ds]);
 
   f32x4 oacc[DP / 16];
 #pragma unroll
   for (int i = 0; i < DP / 16; i++) oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY, lrun = 0.f;
+  float mref = -INFINITY, lrun = 0.f;   // exponent base (raw score units) and this lane's share of l
 
   for (int kb0 = kbeg; kb0 < kend; kb0 += NBUF * KB) {
     __syncthreads();                          // the previous stage's readers are done
     store_stage();
     __syncthreads();
     if (kb0 + NBUF * KB < kend) load_stage(kb0 + NBUF * KB);   // next stage in flight
+    // a stage with at most two live blocks (short key ranges: a chunk's
+    // self-attention, one split of a long context) runs a two-block body
+    // (the choice is uniform across the workgroup); at head dim 128 the
+    // second body would cost registers (one wave per SIMD instead of two)
+    auto stage = [&](auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
+      // scores of every live block of the stage first: S^T for keys kb0 +
+      // 32 b + 16 hb + 4 grp + i of query qn, independent MFMA chains. The
+      // last block may run past the last key: those keys are staged as
+      // zeros and masked below, so the stage is straight-line code.
+      f32x4 s[NB][2];
 #pragma unroll
-    for (int b = 0; b < NBUF; b++) {
-      const int kb = kb0 + b * KB;
-      if (kb >= kend) break;
-      const char* bK = sK + b * ST::KBYTES;
-      const char* bV = sV + b * ST::VBYTES;
-      // S^T for keys kb + hb*16 + 4*grp + i, query qn
-      f32x4 s[2];
+      for (int b = 0; b < NB; b++)
 #pragma unroll
-      for (int hb = 0; hb < 2; hb++) {
-        s[hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int hb = 0; hb < 2; hb++) {
+          s[b][hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          const char* bK = sK + b * ST::KBYTES;
 #pragma unroll
-        for (int ds = 0; ds < DP / 32; ds++) {
-          F kf = TR::lfrag(bK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * ESZ);
-          mma32(s[hb], kf, qf[ds]);
+          for (int ds = 0; ds < DP / 32; ds++) {
+            F kf = TR::lfrag(bK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * ESZ);
+            mma32(s[b][hb], kf, qf[ds]);
+          }
         }
-      }
+      // one online-softmax update for the whole stage, on raw scores; key j is
+      // visible to this lane's query iff j < klim. A stage that every query
+      // of the wave sees whole skips the mask (a wave-uniform test).
       float bmax = -INFINITY;
+      if (kb0 + NB * KB <= kfull) {
 #pragma unroll
-      for (int hb = 0; hb < 2; hb++)
+        for (int b = 0; b < NB; b++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          int j = kb + hb * 16 + grp * 4 + i;
-          bool ok = j < kend && (!p.causal || j <= qrow);
-          float v = ok ? s[hb][i] * p.scale_log2 : -INFINITY;
-          s[hb][i] = v;
-          bmax = fmaxf(bmax, v);
-        }
+          for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) bmax = fmaxf(bmax, s[b][hb][i]);
+      } else {
+        const int kl0 = klim - kb0 - grp * 4;
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+#pragma unroll
+          for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const float v = b * KB + hb * 16 + i < kl0 ? s[b][hb][i] : -INFINITY;
+              s[b][hb][i] = v;
+              bmax = fmaxf(bmax, v);
+            }
+      }
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16, WAVE));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32, WAVE));
-      float mnew = fmaxf(mrun, bmax);
-      float corr = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
-      float pv[8];
+      // The exponent base mref moves only when the running max outgrows it by
+      // more than 2^8 (so P stays within 256), and only then are O and l
+      // rescaled; both share the base, so O / l is unchanged. Most stages
+      // after the first rescale nothing.
+      const float mnew = fmaxf(mref, bmax);
+      const bool grow = mnew != -INFINITY && (mref == -INFINITY || (mnew - mref) * p.scale_log2 > 8.f);
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float corr = grow ? __builtin_amdgcn_exp2f((mref - mnew) * p.scale_log2) : 1.f;
+#pragma unroll
+        for (int db = 0; db < DP / 16; db++) oacc[db] = oacc[db] * corr;
+        lrun *= corr;
+        if (grow) mref = mnew;
+      }
+      const float base = mref == -INFINITY ? 0.f : mref * p.scale_log2;
+      F pf[NB];
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        pv[i] = (mnew == -INFINITY) ? 0.f : exp2f(s[0][i] - mnew);
-        pv[4 + i] = (mnew == -INFINITY) ? 0.f : exp2f(s[1][i] - mnew);
-        psum += pv[i] + pv[4 + i];
+      for (int b = 0; b < NB; b++) {
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          pv[i] = __builtin_amdgcn_exp2f(fmaf(s[b][0][i], p.scale_log2, -base));
+          pv[4 + i] = __builtin_amdgcn_exp2f(fmaf(s[b][1][i], p.scale_log2, -base));
+          psum += pv[i] + pv[4 + i];
+        }
+        frag_from_floats(pf[b], pv);
       }
-      lrun = lrun * corr + psum;
-      mrun = mnew;
-      F pf;
-      frag_from_floats(pf, pv);
+      lrun += psum;
 #pragma unroll
       for (int db = 0; db < DP / 16; db++) {
-        oacc[db] = oacc[db] * corr;
-        const char* vrow = bV + (db * 16 + qn) * VPITCH;
-        F vf = TR::lfrag2(vrow + (grp * 4) * ESZ, vrow + (16 + grp * 4) * ESZ);
-        mma32(oacc[db], vf, pf);
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+          const char* vrow = sV + b * ST::VBYTES + (db * 16 + qn) * VPITCH;
+          F vf = TR::lfrag2(vrow + (grp * 4) * ESZ, vrow + (16 + grp * 4) * ESZ);
+          mma32(oacc[db], vf, pf[b]);
+        }
       }
+    };
+    if constexpr (NBUF > 2 && DP < 128) {
+      if (kend - kb0 <= 2 * KB) stage(std::integral_constant<int, 2>{});
+      else stage(std::integral_constant<int, NBUF>{});
+    } else {
+      stage(std::integral_constant<int, NBUF>{});
     }
   }
   float lsum = lrun;
@@ -264,7 +326,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
       const int d = db * 16 + grp * 4;
       *reinterpret_cast<float4*>(pt + qn * DP + d) = make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
     }
-    if (grp == 0) { pt[16 * DP + qn] = mrun; pt[16 * DP + 16 + qn] = lsum; }
+    if (grp == 0) { pt[16 * DP + qn] = mref == -INFINITY ? -INFINITY : mref * p.scale_log2; pt[16 * DP + 16 + qn] = lsum; }
     return;
   }
   float inv = lsum > 0.f ? 1.f / lsum : 0.f;

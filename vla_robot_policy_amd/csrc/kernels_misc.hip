@@ -1,5 +1,4 @@
-// Attention, staging, norm, conversion and Euler-tail kernel instantiations.
-#include "attention.h"
+// Staging, norm, conversion and Euler-tail kernel instantiations.
 #include "kernels.h"
 #include "misc.h"
 
@@ -18,22 +17,6 @@ __global__ __launch_bounds__(256) void k_convert_rows(const float* x, int ldx, i
   }
 }
 
-#define VLA_ATTN_CASE(CT, F32V, DPV, HPWV)          \
-  if (f32 == F32V && dp == DPV && hpw == HPWV) {    \
-    out->fn = (const void*)&k_attention<CT, DPV, HPWV>; \
-    out->smem = AttnStage<CT, DPV>::SMEM; out->threads = 256; \
-    if (merge) { merge->fn = (const void*)&k_attn_merge<CT, DPV, HPWV>; merge->smem = 0; merge->threads = 256; } \
-    return true;                                    \
-  }
-
-bool attn_lookup(int f32, int dp, int hpw, KernelRef* out, KernelRef* merge) {
-  VLA_ATTN_CASE(__bf16, 0, 64, 1) VLA_ATTN_CASE(__bf16, 0, 64, 2) VLA_ATTN_CASE(__bf16, 0, 64, 4)
-  VLA_ATTN_CASE(__bf16, 0, 96, 1) VLA_ATTN_CASE(__bf16, 0, 96, 2) VLA_ATTN_CASE(__bf16, 0, 96, 4)
-  VLA_ATTN_CASE(__bf16, 0, 128, 1) VLA_ATTN_CASE(__bf16, 0, 128, 2) VLA_ATTN_CASE(__bf16, 0, 128, 4)
-  VLA_ATTN_CASE(float, 1, 64, 1) VLA_ATTN_CASE(float, 1, 64, 2) VLA_ATTN_CASE(float, 1, 64, 4)
-  VLA_ATTN_CASE(float, 1, 128, 1) VLA_ATTN_CASE(float, 1, 128, 2) VLA_ATTN_CASE(float, 1, 128, 4)
-  return false;
-}
 
 const void* k_fill_ref() { return (const void*)&k_fill_u32; }
 const void* k_stage_rows_ref() { return (const void*)&k_stage_rows; }
