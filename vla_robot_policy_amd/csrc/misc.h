@@ -376,9 +376,41 @@ template <> __device__ __forceinline__ float wget<int8_t>(const void* w, size_t 
 
 
 
+// Eight consecutive weights from element i (a multiple of 8) as floats,
+// in one vector load (the matrices are 16-byte aligned, rows a multiple of 8).
+template <typename WT> __device__ __forceinline__ void wload8(const void* w, size_t i, float (&f)[8]);
+template <> __device__ __forceinline__ void wload8<uint16_t>(const void* w, size_t i, float (&f)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>((const uint16_t*)w + i);
+  const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; k++) { f[2 * k] = __uint_as_float(h[k] << 16); f[2 * k + 1] = __uint_as_float(h[k] & 0xFFFF0000u); }
+}
+template <> __device__ __forceinline__ void wload8<float>(const void* w, size_t i, float (&f)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>((const float*)w + i), b = *reinterpret_cast<const float4*>((const float*)w + i + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+template <> __device__ __forceinline__ void wload8<uint8_t>(const void* w, size_t i, float (&f)[8]) {
+  const uint2 u = *reinterpret_cast<const uint2*>((const uint8_t*)w + i);
+  const uint32_t h[2] = {u.x, u.y};
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[k], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)h[k], true);
+    f[4 * k] = lo[0]; f[4 * k + 1] = lo[1]; f[4 * k + 2] = hi[0]; f[4 * k + 3] = hi[1];
+  }
+}
+template <> __device__ __forceinline__ void wload8<int8_t>(const void* w, size_t i, float (&f)[8]) {
+  const uint2 u = *reinterpret_cast<const uint2*>((const int8_t*)w + i);
+#pragma unroll
+  for (int k = 0; k < 8; k++) f[k] = (float)(int8_t)((k < 4 ? u.x : u.y) >> (8 * (k & 3)));
+}
+
 // One workgroup per action row m:
 //   v = (LN(x_m)(1 + scale) + shift) W_out^T + b_out;  a_m <- a_m + v / K
 //   x_m <- a_m W_in^T + b_in, with its (mean, var) for the next LayerNorm.
+// The row is read once into LDS. In the velocity head wave w takes actions
+// w, w + 4, ... of each group of 32 and every lane accumulates all of them
+// over its 8-wide column groups, so the weight loads of all the wave's
+// actions are in flight together (D is a multiple of 8).
 template <typename WT>
 __global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
   extern __shared__ __align__(16) float sh[];
@@ -386,66 +418,97 @@ __global__ __launch_bounds__(256) void k_euler_tail(TailArgs p) {
   float* sa = sh + p.D;           // [A]
   __shared__ float red[8];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* arow = p.a_in + (size_t)m * p.A;
+  const int D = p.D, A = p.A;
+  const float* arow = p.a_in + (size_t)m * A;
   if (p.w_out) {
-    // LayerNorm of x_m: two-pass mean / variance over the row (this
-    // workgroup reads the whole row anyway)
-    const float* xr = p.x + (size_t)m * p.D;
+    // LayerNorm of x_m: the row into LDS with its sum, then the variance
+    // from LDS (two-pass)
+    const float4* xr4 = reinterpret_cast<const float4*>(p.x + (size_t)m * D);
     float s1 = 0.f;
-    for (int d = tid; d < p.D; d += 256) s1 += xr[d];
+    for (int d4 = tid; d4 < D / 4; d4 += 256) {
+      const float4 v = xr4[d4];
+      reinterpret_cast<float4*>(su)[d4] = v;
+      s1 += (v.x + v.y) + (v.z + v.w);
+    }
     s1 = wave_sum(s1);
     if (lane == 0) red[wave] = s1;
     __syncthreads();
-    const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)p.D;
+    const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)D;
     float s2 = 0.f;
-    for (int d = tid; d < p.D; d += 256) { float dd = xr[d] - mean; s2 += dd * dd; }
+    for (int d = tid; d < D; d += 256) { const float dd = su[d] - mean; s2 += dd * dd; }
     s2 = wave_sum(s2);
     if (lane == 0) red[4 + wave] = s2;
     __syncthreads();
-    const float rstd = rsqrtf((red[4] + red[5] + red[6] + red[7]) / (float)p.D + p.eps);
-    __syncthreads();   // red is reused below
-    for (int d = tid; d < p.D; d += 256)
-      su[d] = (xr[d] - mean) * rstd * (1.f + p.scale[d]) + p.shift[d];
+    const float rstd = rsqrtf((red[4] + red[5] + red[6] + red[7]) / (float)D + p.eps);
+    for (int d = tid; d < D; d += 256) su[d] = (su[d] - mean) * rstd * (1.f + p.scale[d]) + p.shift[d];
     __syncthreads();
-    for (int a = wave; a < p.A; a += 4) {
-      float acc = 0.f;
-      for (int d = lane; d < p.D; d += 64) acc += su[d] * wget<WT>(p.w_out, (size_t)a * p.D + d);
-      acc = wave_sum(acc);
-      if (lane == 0) {
-        float v = acc * (p.s_out ? p.s_out[a] : 1.f) + p.b_out[a];
-        if (p.v_out) p.v_out[(size_t)m * p.A + a] = v;
-        float an = arow[a] + v / (float)p.K;
-        sa[a] = an;
+    for (int a0 = 0; a0 < A; a0 += 32) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[i] = 0.f;
+#pragma unroll 2
+      for (int g = lane; g < D / 8; g += 64) {
+        const float4 u0 = reinterpret_cast<const float4*>(su)[2 * g], u1 = reinterpret_cast<const float4*>(su)[2 * g + 1];
+        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const int a = a0 + wave + 4 * i;
+          if (a < A) {
+            float wv[8];
+            wload8<WT>(p.w_out, (size_t)a * D + 8 * g, wv);
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[i] = fmaf(u[e], wv[e], acc[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int a = a0 + wave + 4 * i;
+        const float dot = wave_sum(acc[i]);
+        if (lane == 0 && a < A) {
+          const float v = dot * (p.s_out ? p.s_out[a] : 1.f) + p.b_out[a];
+          if (p.v_out) p.v_out[(size_t)m * A + a] = v;
+          sa[a] = arow[a] + v / (float)p.K;
+        }
       }
     }
     __syncthreads();
-    for (int a = tid; a < p.A; a += 256) p.a_out[(size_t)m * p.A + a] = sa[a];
+    for (int a = tid; a < A; a += 256) p.a_out[(size_t)m * A + a] = sa[a];
   } else {
-    for (int a = tid; a < p.A; a += 256) {
+    for (int a = tid; a < A; a += 256) {
       sa[a] = arow[a];
-      if (p.a_out != p.a_in) p.a_out[(size_t)m * p.A + a] = arow[a];
+      if (p.a_out != p.a_in) p.a_out[(size_t)m * A + a] = arow[a];
     }
   }
   __syncthreads();
   if (!p.w_in) return;
+  // input projection: rows of W_in are A long; 8-wide loads when A allows
+  const bool vec = A % 8 == 0;
   float s = 0.f;
-  for (int d = tid; d < p.D; d += 256) {
-    float acc = p.b_in[d];
-    float sc = p.s_in ? p.s_in[d] : 1.f;
+  for (int d = tid; d < D; d += 256) {
     float dot = 0.f;
-    for (int a = 0; a < p.A; a++) dot += sa[a] * wget<WT>(p.w_in, (size_t)d * p.A + a);
-    acc += dot * sc;
-    p.x_out[(size_t)m * p.D + d] = acc;
+    if (vec) {
+      for (int a8 = 0; a8 < A; a8 += 8) {
+        float wv[8];
+        wload8<WT>(p.w_in, (size_t)d * A + a8, wv);
+#pragma unroll
+        for (int e = 0; e < 8; e++) dot = fmaf(sa[a8 + e], wv[e], dot);
+      }
+    } else {
+      for (int a = 0; a < A; a++) dot = fmaf(sa[a], wget<WT>(p.w_in, (size_t)d * A + a), dot);
+    }
+    const float acc = p.b_in[d] + dot * (p.s_in ? p.s_in[d] : 1.f);
+    p.x_out[(size_t)m * D + d] = acc;
     su[d] = acc;
     s += acc;
   }
   s = wave_sum(s);
   if (lane == 0) red[wave] = s;
   __syncthreads();
-  float mean = (red[0] + red[1] + red[2] + red[3]) / (float)p.D;
+  float mean = (red[0] + red[1] + red[2] + red[3]) / (float)D;
   __syncthreads();
   float q = 0.f;
-  for (int d = tid; d < p.D; d += 256) { float dd = su[d] - mean; q += dd * dd; }
+  for (int d = tid; d < D; d += 256) { float dd = su[d] - mean; q += dd * dd; }
   q = wave_sum(q);
   if (lane == 0) red[4 + wave] = q;
   __syncthreads();
