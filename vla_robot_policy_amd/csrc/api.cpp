@@ -225,6 +225,10 @@ void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb,
     if (ac && em == E_SWIGLU) { mb = 8; wn = 8; wk = 1; nbw = 2; u = 2; }
     else if (ac && em == E_RESID) { mb = 8; wn = 2; wk = 2; nbw = 2; u = 1; split_hint = 3; target_wgs = 0; }
     else if (!ac && em == E_RESID && N >= 2048 && K > 1024) { mb = 8; wn = 4; wk = 1; nbw = 1; u = 4; split_hint = 0; target_wgs = 0; }
+    // narrow long-K residual (the vision MLP's down projection, 1024 wide
+    // over K 4096): 64 x 64 tiles of two k-waves over four k-splits
+    // (15.9 -> 14.4 us)
+    else if (!ac && em == E_RESID && N < 2048 && K > 1024) { mb = 4; wn = 4; wk = 2; nbw = 1; u = 2; split_hint = 4; target_wgs = 0; }
   }
   // fp8 weights over more than 256 rows: two column blocks per wave, so each
   // A fragment read from LDS feeds two MFMAs (gate/up at 560 rows 121 -> 103
