@@ -356,8 +356,6 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
     return fail(VLA_ERR_SHAPE, "attention: row pitches %d/%d/%d/%d not multiples of 8/8/8/4", a.ldq, a.ldk, a.ldv, a.ldo);
   int group = a.Hq / a.Hkv;
   int hpw = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-  KernelRef k{}, km{};
-  if (!attn_lookup(f32 ? 1 : 0, dp, hpw, &k, &km)) return fail(VLA_ERR_UNSUPPORTED, "attention: no kernel for D %d", a.D);
   int rb = 4 / hpw;
   int nrb = (a.Sq + 16 * rb - 1) / (16 * rb);
   int tiles = a.Hkv * (group / hpw) * nrb;
@@ -369,6 +367,21 @@ vla_status attention(Ctx& c, AttnArgs a, bool f32) {
   const int kblocks = (a.Sk + 31) / 32;
   int nsplit = 1;
   if (kblocks >= 12 && tiles <= 64) nsplit = std::min({kblocks / 2, 192 / tiles, ATTN_SPLIT_MAX});
+  // Otherwise, with fewer tiles than about three quarters of the compute
+  // units and at least two key blocks (the batch-1 prefills: 56 tiles for
+  // 104 rows of 32/8 heads, 64 for the encoder's 256 rows of 16 heads), the
+  // key-split form: 16 rows of one head per workgroup, the four waves on
+  // different key blocks, merged in LDS.
+  int ks = 0;
+  if (nsplit == 1 && !f32 && (dp == 64 || dp == 128) && kblocks >= 2 && tiles < 192) {
+    ks = 1;
+    hpw = 1;
+    rb = 1;
+    nrb = (a.Sq + 15) / 16;
+    tiles = a.Hq * nrb;
+  }
+  KernelRef k{}, km{};
+  if (!attn_lookup(f32 ? 1 : 0, dp, hpw, ks, &k, &km)) return fail(VLA_ERR_UNSUPPORTED, "attention: no kernel for D %d", a.D);
   a.kchunk = ((kblocks + nsplit - 1) / nsplit) * 32;
   a.nsplit = nsplit = (a.Sk + a.kchunk - 1) / a.kchunk;
   if (nsplit > 1) {

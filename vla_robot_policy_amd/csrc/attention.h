@@ -14,6 +14,12 @@
 // the B-operand layout of O^T = V^T P^T. No LDS round trip for P.
 // With grouped KV heads one workgroup serves up to 4 query heads that share
 // one KV head, so each K/V block is fetched once for all of them.
+// When that leaves too few workgroups to fill the chip (batch-1 prefills of
+// 100-256 rows), the key-split form (KS) gives each workgroup 16 query rows
+// of one head and lets its four waves take one 32-key block of every stage
+// each; the four partial results (unnormalised O, running max and sum) are
+// combined in LDS in wave order at the end, so the serial chain per wave is
+// a quarter as long and four times as many workgroups share the work.
 #pragma once
 #include <type_traits>
 
@@ -127,14 +133,17 @@ struct AttnStage {
 
 // DP: head dim padded to a multiple of 32 (64, 96, 128). HPW: query heads per
 // workgroup (1, 2 or 4); the 4 waves cover HPW heads x (4 / HPW) row blocks.
-template <typename CT, int DP, int HPW>
+// KS: the key-split form (one head, 16 rows, wave w takes block w of each
+// stage); bf16 only, HPW 1, head dim 64 or 128, no split across workgroups.
+template <typename CT, int DP, int HPW, bool KS = false>
 __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   using TR = ATraits<CT>;
   using F = typename TR::F;
   using ST = AttnStage<CT, DP>;
   using RAW = typename TR::raw;
   constexpr int ESZ = TR::ESZ;
-  constexpr int RB = 4 / HPW;                // 16-row blocks per workgroup
+  static_assert(!KS || (HPW == 1 && ST::NBUF == 4 && DP % 64 == 0), "key-split form: 4 blocks per stage, one head");
+  constexpr int RB = KS ? 1 : 4 / HPW;       // 16-row blocks per workgroup
   constexpr int KB = ST::KB, NBUF = ST::NBUF, GPB = ST::GPB;
   constexpr int KPITCH = ST::KPITCH, VPITCH = ST::VPITCH;
   extern __shared__ __align__(16) char smem[];
@@ -151,8 +160,8 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   const int rb = bid % nrb;  bid /= nrb;
   const int hs = bid % hsets; bid /= hsets;
   const int g = bid;                          // kv head
-  const int head = g * group + hs * HPW + (wave % HPW);
-  const int row0 = (rb * RB + wave / HPW) * 16;     // this wave's first query row
+  const int head = g * group + hs * HPW + (KS ? 0 : wave % HPW);
+  const int row0 = (rb * RB + (KS ? 0 : wave / HPW)) * 16;     // this wave's first query row
   const int wg_row_end = min(p.Sq, (rb + 1) * RB * 16);
   const int qn = lane & 15, grp = lane >> 4;
   const int qrow = row0 + qn;
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
     // second body would cost registers (one wave per SIMD instead of two)
     auto stage = [&](auto nb_c) {
       constexpr int NB = decltype(nb_c)::value;
+      const int bo = KS ? wave : 0;           // the wave's first block of the stage
       // scores of every live block of the stage first: S^T for keys kb0 +
       // 32 b + 16 hb + 4 grp + i of query qn, independent MFMA chains. The
       // last block may run past the last key: those keys are staged as
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
 #pragma unroll
         for (int hb = 0; hb < 2; hb++) {
           s[b][hb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-          const char* bK = sK + b * ST::KBYTES;
+          const char* bK = sK + (bo + b) * ST::KBYTES;
 #pragma unroll
           for (int ds = 0; ds < DP / 32; ds++) {
             F kf = TR::lfrag(bK + (hb * 16 + qn) * KPITCH + (ds * 32 + grp * 8) * ESZ);
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
       // visible to this lane's query iff j < klim. A stage that every query
       // of the wave sees whole skips the mask (a wave-uniform test).
       float bmax = -INFINITY;
-      if (kb0 + NB * KB <= kfull) {
+      if (kb0 + (bo + NB) * KB <= kfull) {
 #pragma unroll
         for (int b = 0; b < NB; b++)
 #pragma unroll
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; i++) bmax = fmaxf(bmax, s[b][hb][i]);
       } else {
-        const int kl0 = klim - kb0 - grp * 4;
+        const int kl0 = klim - kb0 - bo * KB - grp * 4;
 #pragma unroll
         for (int b = 0; b < NB; b++)
 #pragma unroll
@@ -300,13 +310,17 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
       for (int db = 0; db < DP / 16; db++) {
 #pragma unroll
         for (int b = 0; b < NB; b++) {
-          const char* vrow = sV + b * ST::VBYTES + (db * 16 + qn) * VPITCH;
+          const char* vrow = sV + (bo + b) * ST::VBYTES + (db * 16 + qn) * VPITCH;
           F vf = TR::lfrag2(vrow + (grp * 4) * ESZ, vrow + (16 + grp * 4) * ESZ);
           mma32(oacc[db], vf, pf[b]);
         }
       }
     };
-    if constexpr (NBUF > 2 && DP < 128) {
+    if constexpr (KS) {
+      // a block that no query of the wave sees adds nothing: skip it
+      const int kwave = p.causal ? min(kend, row0 + 16) : kend;
+      if (kb0 + wave * KB < kwave) stage(std::integral_constant<int, 1>{});
+    } else if constexpr (NBUF > 2 && DP < 128) {
       if (kend - kb0 <= 2 * KB) stage(std::integral_constant<int, 2>{});
       else stage(std::integral_constant<int, NBUF>{});
     } else {
@@ -316,6 +330,52 @@ __global__ __launch_bounds__(256) void k_attention(AttnArgs p) {
   float lsum = lrun;
   lsum += __shfl_xor(lsum, 16, WAVE);
   lsum += __shfl_xor(lsum, 32, WAVE);
+  if constexpr (KS) {
+    // the four waves' partials of the same 16 queries, combined in LDS: each
+    // wave's O^T tile goes in as [query][dim] rows with its (max, sum), then
+    // thread t produces dims (t % 16) * DP / 16 .. of query t / 16
+    constexpr int OP = DP + 4;                           // row pitch (floats)
+    float* mo = reinterpret_cast<float*>(smem);          // [4][16][OP]
+    float* ml = mo + 4 * 16 * OP;                        // [4][16][2]
+    static_assert((4 * 16 * OP + 4 * 16 * 2) * 4 <= ST::SMEM, "merge tile fits the stage buffers");
+    __syncthreads();                                     // every wave is done with the staged K / V
+#pragma unroll
+    for (int db = 0; db < DP / 16; db++)
+      *reinterpret_cast<float4*>(mo + (wave * 16 + qn) * OP + db * 16 + grp * 4) =
+          make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+    if (grp == 0) {
+      ml[(wave * 16 + qn) * 2] = mref == -INFINITY ? -INFINITY : mref * p.scale_log2;
+      ml[(wave * 16 + qn) * 2 + 1] = lsum;
+    }
+    __syncthreads();
+    const int q = tid >> 4, c0 = (tid & 15) * (DP / 16);
+    float mw[4], fw[4], M = -INFINITY, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) { mw[w] = ml[(w * 16 + q) * 2]; M = fmaxf(M, mw[w]); }
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      fw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - M);   // a wave that saw no key adds nothing
+      L += fw[w] * ml[(w * 16 + q) * 2 + 1];
+    }
+    const float linv = L > 0.f ? 1.f / L : 0.f;
+    const int row = row0 + q;
+    if (row < p.Sq) {
+#pragma unroll
+      for (int i = 0; i < DP / 16; i += 4) {
+        const int d = c0 + i;
+        if (d >= p.D) continue;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const float4 v = *reinterpret_cast<const float4*>(mo + (w * 16 + q) * OP + d);
+          acc.x += fw[w] * v.x; acc.y += fw[w] * v.y; acc.z += fw[w] * v.z; acc.w += fw[w] * v.w;
+        }
+        TR::store4(p.o, (size_t)row * p.ldo + (size_t)head * p.D + d, acc.x * linv, acc.y * linv, acc.z * linv,
+                   acc.w * linv);
+      }
+    }
+    return;
+  }
   if (p.nsplit > 1) {
     // partial of this split: [wave][query][DP] unnormalised O, then the
     // running max and sum of each query

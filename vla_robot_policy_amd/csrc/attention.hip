@@ -16,7 +16,14 @@ namespace vla {
     return true;                                    \
   }
 
-bool attn_lookup(int f32, int dp, int hpw, KernelRef* out, KernelRef* merge) {
+bool attn_lookup(int f32, int dp, int hpw, int ks, KernelRef* out, KernelRef* merge) {
+  if (ks) {   // key-split form: bf16, one head per workgroup, no merge launch
+    if (f32 || hpw != 1 || (dp != 64 && dp != 128)) return false;
+    out->fn = dp == 64 ? (const void*)&k_attention<__bf16, 64, 1, true> : (const void*)&k_attention<__bf16, 128, 1, true>;
+    out->smem = dp == 64 ? AttnStage<__bf16, 64>::SMEM : AttnStage<__bf16, 128>::SMEM;
+    out->threads = 256;
+    return true;
+  }
   VLA_ATTN_CASE(__bf16, 0, 64, 1) VLA_ATTN_CASE(__bf16, 0, 64, 2) VLA_ATTN_CASE(__bf16, 0, 64, 4)
   VLA_ATTN_CASE(__bf16, 0, 96, 1) VLA_ATTN_CASE(__bf16, 0, 96, 2) VLA_ATTN_CASE(__bf16, 0, 96, 4)
   VLA_ATTN_CASE(__bf16, 0, 128, 1) VLA_ATTN_CASE(__bf16, 0, 128, 2) VLA_ATTN_CASE(__bf16, 0, 128, 4)

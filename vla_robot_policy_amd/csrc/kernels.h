@@ -23,7 +23,7 @@ bool gemm_lookup_int8(const GemmPick& g, KernelRef* out);
 
 // Attention: f32 (1) or bf16 (0) elements, padded head dim, heads per workgroup.
 // the attention kernel and the merge of its key-split partials
-bool attn_lookup(int f32, int dp, int hpw, KernelRef* out, KernelRef* merge);
+bool attn_lookup(int f32, int dp, int hpw, int ks, KernelRef* out, KernelRef* merge);
 
 // Misc kernels.
 const void* k_fill_ref();
