@@ -182,6 +182,7 @@ struct GemmOp {
 // same tiles (and give the same bits).
 void pick_tile(int M, int N, int K, int am, int em, int ac, int wdtype, int& mb, int& wn, int& wk, int& nbw,
                int& u, int& aq, int& split_hint, int& target_wgs) {
+  if (am == A_BF16R) am = A_BF16;   // the same staging; the row scale is an epilogue step
   bool wide = em == E_ROPE || em == E_SWIGLU;
   mb = M <= 16 ? 1 : M <= 64 ? 4 : M <= 112 ? 7 : (M <= 256 || (ac && !wide)) ? 4 : 8;
   u = ac ? 2 : 4;
@@ -290,16 +291,18 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (a.ldw % 8 != 0 || a.ldw < a.K) return fail(VLA_ERR_SHAPE, "gemm: weight pitch %d must be >= K=%d and a multiple of 8", a.ldw, a.K);
   if ((op.wdtype == VLA_FP8_E4M3 || op.wdtype == VLA_INT8) && (a.K % 16 != 0 || a.ldw % 16 != 0))
     return fail(VLA_ERR_SHAPE, "gemm: 8-bit weights need K %d and pitch %d to be multiples of 16", a.K, a.ldw);
-  const int ag = op.am == A_BF16 ? 8 : a_codes(op.am) ? 16 : 4;   // activation elements per 16-byte load
+  const int ag = a_bf16(op.am) ? 8 : a_codes(op.am) ? 16 : 4;   // activation elements per 16-byte load
   if (a_codes(op.am) && !a.a_scale && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: 8-bit activations without row scales");
-  if ((op.am == A_BF16 || op.am == A_F32 || op.am == A_NORM || a_codes(op.am)) && (a.lda % ag != 0 || a.K % ag != 0))
+  if (op.am == A_BF16R && !a.rstd && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: deferred RMSNorm rows without their 1 / rms");
+  if ((a_bf16(op.am) || op.am == A_F32 || op.am == A_NORM || a_codes(op.am)) && (a.lda % ag != 0 || a.K % ag != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
   // the epilogues store 4 consecutive columns at once and read the
   // per-column vectors as float4
   if (a.N % 4 != 0 || (op.em == E_RESID ? a.ldx % 4 != 0 : a.ldc % 4 != 0))
     return fail(VLA_ERR_SHAPE, "gemm: N %d and the output pitch must be multiples of 4", a.N);
   for (const void* v : {(const void*)a.bias, (const void*)a.wscale, (const void*)a.gate, (const void*)a.c, (const void*)a.x,
-                        (const void*)a.rope_cos, (const void*)a.rope_sin, (const void*)a.addrow})
+                        (const void*)a.rope_cos, (const void*)a.rope_sin, (const void*)a.addrow, (const void*)a.xg,
+                        (const void*)a.xg_lo, (const void*)a.xg_gain})
     if (reinterpret_cast<uintptr_t>(v) & 15) return fail(VLA_ERR_INVALID_ARG, "gemm: output or epilogue vector not 16-byte aligned");
   // buffer-load offsets are 32-bit: operands up to 2 GiB
   const double wrows = op.em == E_SWIGLU ? (double)a.n_half + a.N : (double)a.N;
@@ -311,9 +314,11 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
     return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
   if ((op.em == E_RESID ? (double)a.M * a.ldx * 4.0 : (double)a.M * a.ldc * (a.c_f32 ? 4.0 : 2.0)) >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: output matrix beyond 2 GiB");
-  if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32 && op.am != A_BF16)))
+  if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32 && !a_bf16(op.am))))
     return fail(VLA_ERR_UNSUPPORTED, "gemm: compensated activations need bf16 weights");
-  if (op.ac && op.am == A_BF16 && !a.a_lo && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: compensated bf16 source without its remainder plane");
+  if ((a.xg || a.rstd_out) && op.em != E_RESID)
+    return fail(VLA_ERR_INVALID_ARG, "gemm: gained bf16 rows and row scales come from a residual epilogue");
+  if (op.ac && a_bf16(op.am) && !a.a_lo && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: compensated bf16 source without its remainder plane");
   if (op.em == E_RESID) {
     if (!a.rs_out && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: residual epilogue without a row-moment output");
     if (a.n_tiles_n > (a.N + 15) / 16) return fail(VLA_ERR_SHAPE, "gemm: residual tiling finer than 16 columns");
@@ -321,7 +326,9 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   }
   size_t part_f = split > 1 ? (size_t)split * tiles * BM * BN : 0;
   c.need_part = std::max(c.need_part, part_f);
-  c.need_tiles = std::max(c.need_tiles, (size_t)tiles);
+  // a residual epilogue that finalises the rows' 1 / rms counts its tiles in
+  // the counter after the split-K ones
+  c.need_tiles = std::max(c.need_tiles, (size_t)tiles + (a.rstd_out ? 1 : 0));
   KernelRef k{};
   bool found = false;
   const GemmPick g{op.am, op.em, mb, wn, wk, nbw, u, op.ac, aq, op.pk};
@@ -337,6 +344,19 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   a.cnt_tile = c.cnt_tile;
   if (k.smem > 64 * 1024) VLA_TRY(allow_smem(k));
   return launch(c, k.fn, dim3(tiles * split), dim3(k.threads), (size_t)k.smem, {arg(a)});
+}
+
+// Whether a GEMM of this shape and kind has an instantiated tile (the
+// deferred-norm forms exist for the backbone's tiles only).
+bool gemm_has(int M, int N, int K, GemmOp op) {
+  int mb, wn, wk, nbw, u, aq, split_hint, target_wgs;
+  pick_tile(M, N, K, op.am, op.em, op.ac, op.wdtype, mb, wn, wk, nbw, u, aq, split_hint, target_wgs);
+  KernelRef k{};
+  const GemmPick g{op.am, op.em, mb, wn, wk, nbw, u, op.ac, aq, op.pk};
+  if (op.wdtype == VLA_BF16) return gemm_lookup_bf16(g, &k);
+  if (op.wdtype == VLA_FP8_E4M3) return gemm_lookup_fp8(g, &k);
+  if (op.wdtype == VLA_INT8) return gemm_lookup_int8(g, &k);
+  return false;
 }
 
 GemmArgs gargs() {
@@ -545,6 +565,7 @@ struct BackboneBufs {
   void* act;       // [S, I]
   uint16_t* xn;    // [S, H] normalised rows (bf16 activations)
   uint16_t* xn_lo; // [S, H] their remainder plane (compensated MLP)
+  float* rstd;     // [S] 1 / rms of the stream's rows (deferred RMSNorm)
   uint16_t* act_lo;// [S, I] remainder plane of the SwiGLU output (compensated MLP)
   uint8_t* q8;     // [S, max(H, q_dim, I)] E4M3FN codes of the next Linear's input (fp8 activations)
   float* q8s;      // [S] their row scales
@@ -574,7 +595,11 @@ BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   b.q8 = nullptr; b.q8s = nullptr;
   b.rope_cos = c.take<float>((size_t)S * (cfg.head_dim / 2));
   b.rope_sin = c.take<float>((size_t)S * (cfg.head_dim / 2));
-  if (cfg.adtype != VLA_F32) b.xn = c.take<uint16_t>((size_t)S * cfg.hidden);
+  b.rstd = nullptr;
+  if (cfg.adtype != VLA_F32) {
+    b.xn = c.take<uint16_t>((size_t)S * cfg.hidden);
+    b.rstd = c.take<float>((size_t)S);
+  }
   if (cfg.flags & VLA_BLOCK_A8) {
     const int w = std::max({cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.intermediate});
     b.q8 = c.take<uint8_t>((size_t)S * w);
@@ -601,6 +626,17 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   const bool a8 = (cfg.flags & VLA_BLOCK_A8) != 0;
   const int i8 = wt == VLA_INT8 ? 1 : 0;              // the activation codes follow the weights' format
   const int am_bf = a8 ? (i8 ? A_I8 : A_FP8) : A_BF16;
+  // Deferred RMSNorm (bf16 activations): each residual epilogue also writes
+  // bf16(x g) with the gain of the norm that reads the stream next (and its
+  // remainder plane for the compensated gate/up) and, from its last tile,
+  // every row's 1 / rms; the QKV and gate/up GEMMs scale their output rows
+  // by it. Only layer 0's attention norm, whose stream comes from the
+  // staging pass, runs as a pass of its own. Up to 112 rows (one row tile):
+  // the last tile merges every row's moments alone, which at 256 rows and
+  // more costs the residual GEMMs more than the norm passes (measured: 560
+  // rows, O projection 51 -> 65 us, down 100 -> 118 us).
+  const bool defer = !f32 && !a8 && S <= 112 && gemm_has(S, nqkv, H, {wt, A_BF16R, E_ROPE, 0, pk}) &&
+                     gemm_has(S, I, H, {wt, A_BF16R, E_SWIGLU, comp, pk});
   {  // cos / sin of every position's RoPE angles, once for the pass
     c.label = "llm.rope_table";
     const int ne = S * (D / 2);
@@ -613,21 +649,23 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       if (a8) {
         c.label = "llm.attn_norm";
         VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, b.q8, b.q8s, H, i8));
-      } else if (!f32) {
+      } else if (!f32 && (!defer || l == 0)) {
         c.label = "llm.attn_norm";
         VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.attn_norm, 0, nullptr, b.xn, nullptr, H));
       }
     c.label = "llm.qkv";
       GemmArgs a = gargs();
       a.M = S; a.N = nqkv; a.K = H;
+      const bool rq = defer && l > 0;   // b.xn holds bf16(x g) from the previous layer's down projection
       if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm; }
       else if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = H; }
       else { a.a = b.xn; a.lda = H; }
+      if (rq) a.rstd = b.rstd;
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
       a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32 || a8;
       a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_cos = b.rope_cos; a.rope_sin = b.rope_sin;
       if (cfg.flags & VLA_BLOCK_QK_NORM) { a.qk_norm = 1; a.qk_eps = cfg.eps; a.qn_g = w.q_norm; a.kn_g = w.k_norm; }
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_ROPE, 0, pk}));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : rq ? A_BF16R : am_bf, E_ROPE, 0, pk}));
     }
     {  // causal GQA attention
     c.label = "llm.attn";
@@ -652,13 +690,14 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.ao; a.lda = qd; }
       a.w = w.w_o; a.ldw = qd; a.wscale = w.s_o;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
+      if (defer) { a.xg = b.xn; a.xg_lo = comp ? b.xn_lo : nullptr; a.xg_gain = w.mlp_norm; a.rstd_out = b.rstd; a.eps = cfg.eps; }
       VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, 0, pk}, &b.xs.rs));
     }
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
       if (a8) {
         c.label = "llm.mlp_norm";
         VLA_TRY(norm_rows8(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, b.q8, b.q8s, H, i8));
-      } else if (!f32) {
+      } else if (!f32 && !defer) {
         c.label = "llm.mlp_norm";
         VLA_TRY(norm_rows(c, b.xs.x, H, S, H, b.xs.rs, 1, cfg.eps, w.mlp_norm, 0, nullptr, b.xn, b.xn_lo, H));
       }
@@ -668,9 +707,10 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm; }
       else if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = H; }
       else { a.a = b.xn; a.a_lo = b.xn_lo; a.lda = H; }
+      if (defer) a.rstd = b.rstd;
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
       a.c = b.act; a.c_lo = b.act_lo; a.ldc = I; a.c_f32 = f32 || a8;
-      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : am_bf, E_SWIGLU, comp, pk}));
+      VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : defer ? A_BF16R : am_bf, E_SWIGLU, comp, pk}));
     }
     {  // down + residual (+ row statistics)
       if (a8) {
@@ -684,6 +724,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.act; a.a_lo = b.act_lo; a.lda = I; }
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
+      if (defer && l + 1 < n_layers) { a.xg = b.xn; a.xg_gain = layers[l + 1].attn_norm; a.rstd_out = b.rstd; a.eps = cfg.eps; }
       VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, comp, pk}, &b.xs.rs));
     }
   }

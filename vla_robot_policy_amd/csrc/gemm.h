@@ -32,9 +32,17 @@
 
 namespace vla {
 
-enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_FP8 = 6, A_I8 = 7 };
+// A_BF16R: bf16 rows that still lack their RMSNorm scale. The producer of
+// the residual stream (a RESID epilogue) wrote them as bf16(x g), g being
+// the norm's gain, and the row's 1 / rms (its last tile merges every tile's
+// row moments), and the output row is scaled in the epilogue:
+// (x g / rms) W^T = (x g) W^T / rms. The norm then costs no pass of its own
+// and the GEMM stages bf16 rows, half the bytes of fp32.
+enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_FP8 = 6, A_I8 = 7, A_BF16R = 8 };
 // 8-bit activation codes with a per-row scale (W8A8)
 constexpr bool a_codes(int am) { return am == A_FP8 || am == A_I8; }
+// bf16 rows staged as they are (with or without the deferred row scale)
+constexpr bool a_bf16(int am) { return am == A_BF16 || am == A_BF16R; }
 enum EMode { E_STORE = 0, E_ROPE = 1, E_SWIGLU = 2, E_RESID = 3 };
 enum ActKind { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 
@@ -75,6 +83,10 @@ struct GemmArgs {
   const float* addrow; int addrow_rows;                   // RESID: + table[m % rows][n]
   const float* gate;                                      // RESID: per-n gate (NULL = 1)
   float2* rs_out;                                         // RESID: [n_tiles_n][M] tile moments of the new stream
+  uint16_t* xg; uint16_t* xg_lo;                          // RESID: also bf16(x * xg_gain) (and its remainder
+  const float* xg_gain;                                   //   plane), pitch ldx: an A_BF16R reader's rows
+  float* rstd_out;                                        // RESID: [M] 1 / rms of the new rows (eps: eps)
+  const float* rstd;                                      // BF16R: [M] 1 / rms of the source rows
   // ---- tiling / split-K (filled by the launcher)
   int split, ksplit;
   float* part;
@@ -186,7 +198,7 @@ struct GemmTile {
   static constexpr int PLANES = AC ? 2 : 1;      // compensated A: hi and lo planes
   static constexpr int APLANE = BM * LROW;
   static constexpr int ABUF = PLANES * APLANE;
-  static constexpr int AG = (AM == A_BF16) ? 8 : a_codes(AM) ? 16 : 4;  // A elements per loader group
+  static constexpr int AG = a_bf16(AM) ? 8 : a_codes(AM) ? 16 : 4;  // A elements per loader group
   static constexpr int AGROUPS = BM * BK / AG;   // A groups per chunk
   static constexpr int GPT = (AGROUPS + THREADS - 1) / THREADS;  // A groups per thread per chunk
   static constexpr int TPITCH = BN + 4;          // fp32 tile pitch (elements)
@@ -210,7 +222,7 @@ struct GemmTile {
   static constexpr int TPR0 = THREADS / NROWST;
   static constexpr int TPR = TPR0 >= 64 ? 64 : TPR0 >= 32 ? 32 : TPR0 >= 16 ? 16 : TPR0 >= 8 ? 8 : TPR0 >= 4 ? 4 : TPR0 >= 2 ? 2 : 1;
   static_assert(THREADS % (BK / AG) == 0, "a thread's A columns must not change between its row groups");
-  static_assert(!AC || (sizeof(CT) == 2 && (AM == A_NORM || AM == A_F32 || AM == A_BF16)), "compensated A needs bf16 MFMA");
+  static_assert(!AC || (sizeof(CT) == 2 && (AM == A_NORM || AM == A_F32 || a_bf16(AM))), "compensated A needs bf16 MFMA");
 };
 
 // Raw A registers: bf16 sources keep 8 bf16 (copied to LDS as is; with
@@ -219,6 +231,8 @@ struct U4x2 { uint4 h, l; };
 template <int AM, int AC> struct ARaw { using type = float4; };
 template <> struct ARaw<A_BF16, 0> { using type = uint4; };
 template <> struct ARaw<A_BF16, 1> { using type = U4x2; };
+template <> struct ARaw<A_BF16R, 0> { using type = uint4; };
+template <> struct ARaw<A_BF16R, 1> { using type = U4x2; };
 template <> struct ARaw<A_FP8, 0> { using type = uint4; };
 template <> struct ARaw<A_I8, 0> { using type = uint4; };
 
@@ -284,6 +298,19 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const float4 e_sc2 = (EM == E_ROPE || EM == E_SWIGLU) ? vec4(p.wscale, ecol2, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
   const float4 e_bi = (EM == E_STORE || EM == E_RESID) ? vec4(p.bias, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
   const float4 e_ga = EM == E_RESID ? vec4(p.gate, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 e_xg = EM == E_RESID ? vec4(p.xg_gain, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
+  // A_BF16R: the 1 / rms of the thread's epilogue rows (written by an
+  // earlier kernel: requested now, used after the main loop)
+  constexpr int NRQ = AM == A_BF16R ? EXP : 1;
+  float rq[NRQ];
+  if constexpr (AM == A_BF16R) {
+    const brsrc qr = make_brsrc(p.rstd);
+#pragma unroll
+    for (int i = 0; i < EXP; i++) {
+      const int m = m0 + er0 + i * ERS;
+      rq[i] = bloadf(qr, (er0 + i * ERS < BM && m < p.M) ? (uint32_t)m * 4u : BUF_OOB);
+    }
+  }
   // QK-norm gains of the columns and of their RoPE partners (a tile lies
   // within the query columns or within the key / value columns, so the gain
   // vector is the same for the whole workgroup)
@@ -449,11 +476,11 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       int r = ar0 + i * RS;
       int m = m0 + r;
       bool ok = r < BM && m < p.M && k < p.K;
-      if constexpr (AM == A_BF16 && AC) {
+      if constexpr (a_bf16(AM) && AC) {
         const uint32_t off = ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB;
         ar[i].h = bload16(ars, off);
         ar[i].l = bload16(make_brsrc(p.a_lo), off);
-      } else if constexpr (AM == A_BF16) {
+      } else if constexpr (a_bf16(AM)) {
         ar[i] = bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 2u : BUF_OOB);
       } else if constexpr (a_codes(AM)) {
         ar[i] = bload16(ars, ok ? (uint32_t)m * p.lda + k : BUF_OOB);
@@ -494,12 +521,12 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       int m = m0 + r;
       bool ok = m < p.M && k < p.K;
       float4 v;
-      if constexpr (AM == A_BF16 && AC) {
+      if constexpr (a_bf16(AM) && AC) {
         // raw copy of both planes
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i].h;
         *reinterpret_cast<uint4*>(base + T::APLANE + r * LROW + ac4 * T::ESZ) = ar[i].l;
         continue;
-      } else if constexpr (AM == A_BF16 || a_codes(AM)) {
+      } else if constexpr (a_bf16(AM) || a_codes(AM)) {
         // raw copy of 8 bf16 or 16 fp8 codes (CT is the source type; zeros beyond the edge)
         *reinterpret_cast<uint4*>(base + r * LROW + ac4 * T::ESZ) = ar[i];
         continue;
@@ -823,14 +850,18 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f), zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
   // W8A8: the per-row scale of the activation codes, applied to the tile in
   // place (RoPE partners and QK-norm statistics read other threads' columns;
-  // the weights' per-column scales are applied below)
-  if constexpr (a_codes(AM)) {
+  // the weights' per-column scales are applied below); A_BF16R with
+  // QK-norm: the row's deferred 1 / rms in the same way (the per-head
+  // statistics must see the scaled rows), else it is applied to the
+  // thread's values below
+  if (a_codes(AM) || (AM == A_BF16R && p.qk_norm)) {
     const brsrc sr = make_brsrc(p.a_scale);
     float rsc[EXP];
 #pragma unroll
     for (int i = 0; i < EXP; i++) {
       const int r = er0 + i * ERS, m = m0 + r;
-      rsc[i] = bloadf(sr, (r < BM && m < p.M) ? (uint32_t)m * 4u : BUF_OOB);
+      if constexpr (AM == A_BF16R) rsc[i] = rq[i];
+      else rsc[i] = bloadf(sr, (r < BM && m < p.M) ? (uint32_t)m * 4u : BUF_OOB);
     }
 #pragma unroll
     for (int i = 0; i < EXP; i++) {
@@ -851,6 +882,17 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     const int r = er0 + i * ERS;
 #pragma unroll
     for (int g = 0; g < NG; g++) y[g][i] = r < BM ? ld4(r, etc + g * EW) : zero4;
+  }
+  // A_BF16R without QK-norm: each row's 1 / rms on the thread's values (and
+  // on the RoPE partners below)
+  const bool rfold = AM == A_BF16R && !p.qk_norm;
+  if constexpr (AM == A_BF16R) {
+    if (rfold) {
+#pragma unroll
+      for (int i = 0; i < EXP; i++)
+#pragma unroll
+        for (int g = 0; g < NG; g++) y[g][i] = mul4(y[g][i], make_float4(rq[i], rq[i], rq[i], rq[i]));
+    }
   }
   // outputs through buffer stores (32-bit element offsets): 4 values as one
   // 16-byte float32 store or one 8-byte bf16 store (ldc and the columns are
@@ -892,6 +934,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     for (int i = 0; i < EXP; i++) {
       const int r = er0 + i * ERS;
       y2[i] = (rot && r < BM) ? ld4(r, ptc) : zero4;
+      if constexpr (AM == A_BF16R)
+        if (rfold) y2[i] = mul4(y2[i], make_float4(rq[i], rq[i], rq[i], rq[i]));
     }
     // QK-norm: the inverse RMS of every (row, head) of the tile over the
     // head's D columns, from the scaled values; four threads per pair, then
@@ -972,6 +1016,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     const float4 sc = p.wscale ? e_sc : one4;
     const float4 ga = p.gate ? e_ga : one4;
     const brsrc xw = make_brsrc(p.x);
+    const brsrc xgw = make_brsrc(p.xg), xglw = make_brsrc(p.xg_lo);
     const brsrc ar = make_brsrc(p.addrow);
     float4 add[EXP];
 #pragma unroll
@@ -989,6 +1034,18 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       if (!row_ok(i)) continue;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, xn), xw, ((uint32_t)m * p.ldx + ecol) * 4u, 0, 0);
       st4(r, etc, xn);
+      if (p.xg) {
+        // the next RMSNorm's input without its row scale: bf16(x g), and
+        // with a remainder plane the pair hi + lo = x g to ~16 bits
+        const float4 t = mul4(xn, e_xg);
+        const uint2 hi = make_uint2(pack_bf2(t.x, t.y), pack_bf2(t.z, t.w));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, hi), xgw, ((uint32_t)m * p.ldx + ecol) * 2u, 0, 0);
+        if (p.xg_lo) {
+          auto lo = [](float v) { return v - bf2f(f2bf(v)); };
+          const uint2 lw = make_uint2(pack_bf2(lo(t.x), lo(t.y)), pack_bf2(lo(t.z), lo(t.w)));
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, lw), xglw, ((uint32_t)m * p.ldx + ecol) * 2u, 0, 0);
+        }
+      }
     }
     // moments of this tile's columns per row (mean, sum of squared
     // deviations), merged by the stream's next reader: TPRM consecutive
@@ -1028,7 +1085,49 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       }
 #pragma unroll
       for (int o = 1; o < TPRM; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
-      if (jq == 0 && m < p.M) p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, sq);
+      if (jq == 0 && m < p.M) {
+        const uint2 mv = make_uint2(__float_as_uint(mean), __float_as_uint(sq));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, mv), make_brsrc(p.rs_out),
+                                              (uint32_t)((size_t)nt * p.M + m) * 8u, 0, CP_SC1);
+      }
+    }
+    // rstd_out: the tile that completes last merges every tile's moments of
+    // every row into the row's 1 / rms (RMSNorm) for an A_BF16R reader; TG
+    // threads per row, each requesting up to RB of its partials at once with
+    // device-coherent loads (the other tiles' sc1 stores)
+    if (p.rstd_out) {
+      const int ntiles = p.n_tiles_m * p.n_tiles_n;
+      if (tile_arrive(p.cnt_tile + ntiles, ntiles, sFlag)) return;
+      const RowStats rs{p.rs_out, p.n_tiles_n, BN, p.N, p.M};
+      const brsrc pr = make_brsrc(p.rs_out);
+      const int tg0 = NT / max(p.M, 1);
+      const int TG = tg0 >= 64 ? 64 : tg0 >= 32 ? 32 : tg0 >= 16 ? 16 : tg0 >= 8 ? 8 : tg0 >= 4 ? 4 : tg0 >= 2 ? 2 : 1;
+      const int jg = tid % TG;
+      constexpr int RB = 20;
+      // every thread runs the same number of row passes (uniform shuffles)
+      const int npass = (p.M + NT / TG - 1) / (NT / TG);
+      for (int ps = 0; ps < npass; ps++) {
+        const int m = ps * (NT / TG) + tid / TG;
+        ShiftSum sa;
+        for (int t0 = 0; t0 < rs.T; t0 += RB * TG) {
+          uint2 v[RB];
+#pragma unroll
+          for (int u = 0; u < RB; u++) {
+            const int t = t0 + jg + u * TG;
+            v[u] = bload8<CP_SC1>(pr, (m < p.M && t < rs.T) ? (uint32_t)((size_t)t * p.M + m) * 8u : BUF_OOB);
+          }
+#pragma unroll
+          for (int u = 0; u < RB; u++) {
+            const int t = t0 + jg + u * TG;
+            if (m < p.M && t < rs.T) sa.add(tile_count(rs, t), make_float2(__uint_as_float(v[u].x), __uint_as_float(v[u].y)));
+          }
+        }
+        float n, mean, m2;
+        sa.moments(n, mean, m2);
+        group_merge(n, mean, m2, TG);
+        if (jg == 0 && m < p.M) p.rstd_out[m] = norm_coeffs(make_float2(mean, n > 0.f ? m2 / n : 0.f), 1, p.eps).y;
+      }
+      if (tid == 0) p.cnt_tile[ntiles] = 0u;
     }
   }
 }

@@ -37,6 +37,8 @@ bool gemm_lookup_fp8(const GemmPick& g, KernelRef* out) {
   // blocks per wave at 65..112 rows
   VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_STORE, 8, 8, 1, 2, 2, 0, 2, 0)
   VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16, E_STORE, 7, 4, 1, 2, 2, 0, 2, 0)
+  VLA_GEMM_BF16R_FP8(0)
+  VLA_GEMM_BF16R_FP8(1)
   return false;
 }
 }  // namespace vla
