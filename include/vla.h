@@ -81,8 +81,10 @@ typedef enum { VLA_F32 = 0, VLA_BF16 = 1, VLA_FP8_E4M3 = 2, VLA_INT8 = 3 } vla_d
  * codes in the weights' format with one scale per row: E4M3FN with s =
  * max|row| / 448 (nearest value, ties to the even code), or int8 with s =
  * max|row| / 127 (nearest integer, halves to even), decided from float32.
- * y = (codes . W codes^T) * s_row * s_channel, with exact code products and
- * float32 accumulation; q, k, v, the attention and the SwiGLU product stay
+ * y = (codes . W codes^T) * s_row * s_channel, with exact code products
+ * (int8: exact int32 sums on the int8 MFMA; E4M3FN: the fp8 MFMA's float32
+ * accumulation, within about 1e-4 relative of exact sums at K = 1024); q,
+ * k, v, the attention and the SwiGLU product stay
  * float32 until quantised. Needs FP8_E4M3 or INT8 weights, BF16 activations,
  * hidden <= 4096, and the Linear inputs (hidden, n_q_heads * head_dim,
  * intermediate) multiples of 16 and at most 16384 wide;

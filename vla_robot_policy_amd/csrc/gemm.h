@@ -564,12 +564,37 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
       for (int j = 0; j < NBW; j++) acci[mb][j] = (i32x4){0, 0, 0, 0};
   }
 
+  // W8A8 fp8: E4M3FN codes of both operands meet in the fp8 MFMA
+  // (16x16x32, fp32 accumulation), with the fragment layout of the bf16 one:
+  // a lane's 8 codes of a 32-wide k-step are one 64-bit operand, so nothing
+  // is widened.
+  constexpr bool F8MMA = AM == A_FP8 && std::is_same_v<WT, uint8_t>;
+
   // One k-step: every A and B fragment of the step is requested from LDS
   // before the first MFMA, so the reads overlap instead of each MFMA waiting
   // for its own read.
   auto compute = [&](int buf, const RR& br) {
     const char* base = sA + buf * T::ABUF;
     const char* wbase = sW + buf * T::WBUF;
+    if constexpr (F8MMA) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int klocal = (u * WK + wk) * 32 + kl;
+        long bi[NBW], ai[MB];
+#pragma unroll
+        for (int j = 0; j < NBW; j++) {
+          if constexpr (WLDS) bi[j] = *reinterpret_cast<const long*>(wbase + ((wn * NBW + j) * 16 + (lane & 15)) * WROW + klocal);
+          else bi[j] = __builtin_bit_cast(long, br[u][j]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) ai[mb] = *reinterpret_cast<const long*>(base + (mb * 16 + (lane & 15)) * LROW + klocal);
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+          for (int j = 0; j < NBW; j++) acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ai[mb], bi[j], acc[mb][j], 0, 0, 0);
+      }
+      return;
+    }
     if constexpr (I8MMA) {
       auto pair = [](const char* p0, const char* p1) {
         const uint2 lo = *reinterpret_cast<const uint2*>(p0), hi = *reinterpret_cast<const uint2*>(p1);
