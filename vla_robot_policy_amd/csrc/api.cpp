@@ -293,7 +293,8 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
     return fail(VLA_ERR_SHAPE, "gemm: 8-bit weights need K %d and pitch %d to be multiples of 16", a.K, a.ldw);
   const int ag = a_bf16(op.am) ? 8 : a_codes(op.am) ? 16 : 4;   // activation elements per 16-byte load
   if (a_codes(op.am) && !a.a_scale && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: 8-bit activations without row scales");
-  if (op.am == A_BF16R && !a.rstd && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: deferred RMSNorm rows without their 1 / rms");
+  if (op.am == A_BF16R && ((!a.rsq && !c.plan) || a.rsq_t < 1 || a.rsq_t > a.rsq_ld || a.rsq_ld % 4))
+    return fail(VLA_ERR_INVALID_ARG, "gemm: deferred RMSNorm rows without their per-tile sums of squares");
   if ((a_bf16(op.am) || op.am == A_F32 || op.am == A_NORM || a_codes(op.am)) && (a.lda % ag != 0 || a.K % ag != 0))
     return fail(VLA_ERR_SHAPE, "gemm: activation pitch %d and K %d must be multiples of %d", a.lda, a.K, ag);
   // the epilogues store 4 consecutive columns at once and read the
@@ -316,7 +317,7 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
     return fail(VLA_ERR_SHAPE, "gemm: output matrix beyond 2 GiB");
   if (op.ac && (op.wdtype != VLA_BF16 || (op.am != A_NORM && op.am != A_F32 && !a_bf16(op.am))))
     return fail(VLA_ERR_UNSUPPORTED, "gemm: compensated activations need bf16 weights");
-  if ((a.xg || a.rstd_out) && op.em != E_RESID)
+  if ((a.xg || a.rsq_out) && op.em != E_RESID)
     return fail(VLA_ERR_INVALID_ARG, "gemm: gained bf16 rows and row scales come from a residual epilogue");
   if (op.ac && a_bf16(op.am) && !a.a_lo && !c.plan) return fail(VLA_ERR_INVALID_ARG, "gemm: compensated bf16 source without its remainder plane");
   if (op.em == E_RESID) {
@@ -326,9 +327,9 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   }
   size_t part_f = split > 1 ? (size_t)split * tiles * BM * BN : 0;
   c.need_part = std::max(c.need_part, part_f);
-  // a residual epilogue that finalises the rows' 1 / rms counts its tiles in
-  // the counter after the split-K ones
-  c.need_tiles = std::max(c.need_tiles, (size_t)tiles + (a.rstd_out ? 1 : 0));
+  if (a.rsq_out && (a.n_tiles_n > a.rsq_ld || a.rsq_ld % 4))
+    return fail(VLA_ERR_SHAPE, "gemm: %d column tiles of sums of squares in rows of %d", a.n_tiles_n, a.rsq_ld);
+  c.need_tiles = std::max(c.need_tiles, (size_t)tiles);
   KernelRef k{};
   bool found = false;
   const GemmPick g{op.am, op.em, mb, wn, wk, nbw, u, op.ac, aq, op.pk};
@@ -565,7 +566,8 @@ struct BackboneBufs {
   void* act;       // [S, I]
   uint16_t* xn;    // [S, H] normalised rows (bf16 activations)
   uint16_t* xn_lo; // [S, H] their remainder plane (compensated MLP)
-  float* rstd;     // [S] 1 / rms of the stream's rows (deferred RMSNorm)
+  float* rsq;      // [S][rsq_ld] per-column-tile sums of squares of the stream's rows (deferred RMSNorm)
+  int rsq_ld;
   uint16_t* act_lo;// [S, I] remainder plane of the SwiGLU output (compensated MLP)
   uint8_t* q8;     // [S, max(H, q_dim, I)] E4M3FN codes of the next Linear's input (fp8 activations)
   float* q8s;      // [S] their row scales
@@ -595,10 +597,11 @@ BackboneBufs take_backbone_bufs(Ctx& c, const vla_block_cfg& cfg, int S) {
   b.q8 = nullptr; b.q8s = nullptr;
   b.rope_cos = c.take<float>((size_t)S * (cfg.head_dim / 2));
   b.rope_sin = c.take<float>((size_t)S * (cfg.head_dim / 2));
-  b.rstd = nullptr;
+  b.rsq = nullptr;
+  b.rsq_ld = (((cfg.hidden + 15) / 16) + 3) / 4 * 4;   // the finest residual tiling: 16 columns
   if (cfg.adtype != VLA_F32) {
     b.xn = c.take<uint16_t>((size_t)S * cfg.hidden);
-    b.rstd = c.take<float>((size_t)S);
+    b.rsq = c.take<float>((size_t)S * b.rsq_ld);
   }
   if (cfg.flags & VLA_BLOCK_A8) {
     const int w = std::max({cfg.hidden, cfg.n_q_heads * cfg.head_dim, cfg.intermediate});
@@ -628,13 +631,11 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   const int am_bf = a8 ? (i8 ? A_I8 : A_FP8) : A_BF16;
   // Deferred RMSNorm (bf16 activations): each residual epilogue also writes
   // bf16(x g) with the gain of the norm that reads the stream next (and its
-  // remainder plane for the compensated gate/up) and, from its last tile,
-  // every row's 1 / rms; the QKV and gate/up GEMMs scale their output rows
-  // by it. Only layer 0's attention norm, whose stream comes from the
-  // staging pass, runs as a pass of its own. Up to 112 rows (one row tile):
-  // the last tile merges every row's moments alone, which at 256 rows and
-  // more costs the residual GEMMs more than the norm passes (measured: 560
-  // rows, O projection 51 -> 65 us, down 100 -> 118 us).
+  // remainder plane for the compensated gate/up) and each column tile's sum
+  // of squares of every row; the QKV and gate/up GEMMs sum a row's tiles
+  // and scale their output rows by its 1 / rms. Only layer 0's attention
+  // norm, whose stream comes from the staging pass, runs as a pass of its
+  // own. Up to 112 rows (one row tile), the prefill it was measured on.
   const bool defer = !f32 && !a8 && S <= 112 && gemm_has(S, nqkv, H, {wt, A_BF16R, E_ROPE, 0, pk}) &&
                      gemm_has(S, I, H, {wt, A_BF16R, E_SWIGLU, comp, pk});
   {  // cos / sin of every position's RoPE angles, once for the pass
@@ -660,7 +661,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.attn_norm; }
       else if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = H; }
       else { a.a = b.xn; a.lda = H; }
-      if (rq) a.rstd = b.rstd;
+      if (rq) { a.rsq = b.rsq; a.rsq_ld = b.rsq_ld; a.rsq_t = b.xs.rs.T; a.eps = cfg.eps; }
       a.w = w.w_qkv; a.ldw = H; a.wscale = w.s_qkv;
       a.c = b.qkv; a.ldc = nqkv; a.c_f32 = f32 || a8;
       a.q_cols = qd; a.k_cols = kd; a.head_dim = D; a.pos0 = 0; a.rope_cos = b.rope_cos; a.rope_sin = b.rope_sin;
@@ -690,7 +691,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.ao; a.lda = qd; }
       a.w = w.w_o; a.ldw = qd; a.wscale = w.s_o;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      if (defer) { a.xg = b.xn; a.xg_lo = comp ? b.xn_lo : nullptr; a.xg_gain = w.mlp_norm; a.rstd_out = b.rstd; a.eps = cfg.eps; }
+      if (defer) { a.xg = b.xn; a.xg_lo = comp ? b.xn_lo : nullptr; a.xg_gain = w.mlp_norm; a.rsq_out = b.rsq; a.rsq_ld = b.rsq_ld; }
       VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, 0, pk}, &b.xs.rs));
     }
     {  // RMSNorm -> gate/up -> SiLU(gate) * up
@@ -707,7 +708,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       if (f32) { a.a = b.xs.x; a.lda = H; a.rs = b.xs.rs; a.norm_rms = 1; a.eps = cfg.eps; a.g = w.mlp_norm; }
       else if (a8) { a.a = b.q8; a.a_scale = b.q8s; a.lda = H; }
       else { a.a = b.xn; a.a_lo = b.xn_lo; a.lda = H; }
-      if (defer) a.rstd = b.rstd;
+      if (defer) { a.rsq = b.rsq; a.rsq_ld = b.rsq_ld; a.rsq_t = b.xs.rs.T; a.eps = cfg.eps; }
       a.w = w.w_gate_up; a.ldw = H; a.wscale = w.s_gate_up; a.n_half = I;
       a.c = b.act; a.c_lo = b.act_lo; a.ldc = I; a.c_f32 = f32 || a8;
       VLA_TRY(gemm(c, a, {wt, f32 ? A_NORM : defer ? A_BF16R : am_bf, E_SWIGLU, comp, pk}));
@@ -724,7 +725,7 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
       else { a.a = b.act; a.a_lo = b.act_lo; a.lda = I; }
       a.w = w.w_down; a.ldw = I; a.wscale = w.s_down;
       a.x = b.xs.x; a.ldx = H; a.rs_out = b.xs.part;
-      if (defer && l + 1 < n_layers) { a.xg = b.xn; a.xg_gain = layers[l + 1].attn_norm; a.rstd_out = b.rstd; a.eps = cfg.eps; }
+      if (defer && l + 1 < n_layers) { a.xg = b.xn; a.xg_gain = layers[l + 1].attn_norm; a.rsq_out = b.rsq; a.rsq_ld = b.rsq_ld; }
       VLA_TRY(gemm(c, a, {wt, f32 ? A_F32 : am_bf, E_RESID, comp, pk}, &b.xs.rs));
     }
   }

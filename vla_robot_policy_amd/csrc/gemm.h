@@ -34,10 +34,10 @@ namespace vla {
 
 // A_BF16R: bf16 rows that still lack their RMSNorm scale. The producer of
 // the residual stream (a RESID epilogue) wrote them as bf16(x g), g being
-// the norm's gain, and the row's 1 / rms (its last tile merges every tile's
-// row moments), and the output row is scaled in the epilogue:
-// (x g / rms) W^T = (x g) W^T / rms. The norm then costs no pass of its own
-// and the GEMM stages bf16 rows, half the bytes of fp32.
+// the norm's gain, and each column tile's sum of squares of every row; the
+// epilogue sums a row's tiles (eps and the width K give 1 / rms) and scales
+// the output row: (x g / rms) W^T = (x g) W^T / rms. The norm then costs no
+// pass of its own and the GEMM stages bf16 rows, half the bytes of fp32.
 enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_FP8 = 6, A_I8 = 7, A_BF16R = 8 };
 // 8-bit activation codes with a per-row scale (W8A8)
 constexpr bool a_codes(int am) { return am == A_FP8 || am == A_I8; }
@@ -85,8 +85,10 @@ struct GemmArgs {
   float2* rs_out;                                         // RESID: [n_tiles_n][M] tile moments of the new stream
   uint16_t* xg; uint16_t* xg_lo;                          // RESID: also bf16(x * xg_gain) (and its remainder
   const float* xg_gain;                                   //   plane), pitch ldx: an A_BF16R reader's rows
-  float* rstd_out;                                        // RESID: [M] 1 / rms of the new rows (eps: eps)
-  const float* rstd;                                      // BF16R: [M] 1 / rms of the source rows
+  float* rsq_out;                                         // RESID: [M][rsq_ld] each column tile's sum of squares
+                                                          //   of the new rows
+  const float* rsq;                                       // BF16R: [M][rsq_ld] the source rows' per-tile sums of
+  int rsq_ld, rsq_t;                                      //   squares, pitch (multiple of 4) and tile count
   // ---- tiling / split-K (filled by the launcher)
   int split, ksplit;
   float* part;
@@ -299,18 +301,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
   const float4 e_bi = (EM == E_STORE || EM == E_RESID) ? vec4(p.bias, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
   const float4 e_ga = EM == E_RESID ? vec4(p.gate, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
   const float4 e_xg = EM == E_RESID ? vec4(p.xg_gain, ecol, ecok) : make_float4(0.f, 0.f, 0.f, 0.f);
-  // A_BF16R: the 1 / rms of the thread's epilogue rows (written by an
-  // earlier kernel: requested now, used after the main loop)
-  constexpr int NRQ = AM == A_BF16R ? EXP : 1;
-  float rq[NRQ];
-  if constexpr (AM == A_BF16R) {
-    const brsrc qr = make_brsrc(p.rstd);
-#pragma unroll
-    for (int i = 0; i < EXP; i++) {
-      const int m = m0 + er0 + i * ERS;
-      rq[i] = bloadf(qr, (er0 + i * ERS < BM && m < p.M) ? (uint32_t)m * 4u : BUF_OOB);
-    }
-  }
+
   // QK-norm gains of the columns and of their RoPE partners (a tile lies
   // within the query columns or within the key / value columns, so the gain
   // vector is the same for the whole workgroup)
@@ -868,6 +859,41 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
     __syncthreads();
   }
 
+  // A_BF16R: the tile rows' 1 / rms from the stream's per-tile sums of
+  // squares (written by an earlier kernel), requested by the workgroup that
+  // runs the epilogue: TPR threads per row, RQ float4 each per round, then a
+  // butterfly over the TPR lanes (every lane ends with the same sum, the
+  // same on every run); into sRow, then into the registers of the thread's
+  // epilogue rows
+  constexpr int NRQ = AM == A_BF16R ? EXP : 1;
+  float rq[NRQ];
+  if constexpr (AM == A_BF16R) {
+    constexpr int RQ = 8;
+    const brsrc qr = make_brsrc(p.rsq);
+    const int m = m0 + rr;
+    const bool rok = rr < BM && m < p.M;
+    float sum = 0.f;
+    for (int t0 = 0; t0 < p.rsq_t; t0 += 4 * RQ * TPR) {   // uniform
+      float4 v[RQ];
+#pragma unroll
+      for (int u = 0; u < RQ; u++) {
+        const int t = t0 + 4 * (jj + u * TPR);
+        v[u] = as_f4(bload16(qr, (rok && t < p.rsq_t) ? ((uint32_t)m * p.rsq_ld + t) * 4u : BUF_OOB));
+      }
+#pragma unroll
+      for (int u = 0; u < RQ; u++) {
+        const int t = t0 + 4 * (jj + u * TPR);   // tiles past rsq_t read as 0 or are masked
+        sum += (v[u].x + (t + 1 < p.rsq_t ? v[u].y : 0.f)) + ((t + 2 < p.rsq_t ? v[u].z : 0.f) + (t + 3 < p.rsq_t ? v[u].w : 0.f));
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) sum += __shfl_xor(sum, o, WAVE);
+    if (jj == 0 && rr < BM) sRow[rr] = make_float2(0.f, rok ? rsqrtf(sum / (float)p.K + p.eps) : 0.f);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EXP; i++) rq[i] = er0 + i * ERS < BM ? sRow[er0 + i * ERS].y : 0.f;
+    __syncthreads();   // sRow is reused below (QK-norm statistics)
+  }
   auto mul4 = [](float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); };
   auto fma4 = [](float4 a, float4 b, float4 c) {
     return make_float4(a.x * b.x + c.x, a.y * b.y + c.y, a.z * b.z + c.z, a.w * b.w + c.w);
@@ -1111,48 +1137,9 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
 #pragma unroll
       for (int o = 1; o < TPRM; o <<= 1) sq += __shfl_xor(sq, o, WAVE);
       if (jq == 0 && m < p.M) {
-        const uint2 mv = make_uint2(__float_as_uint(mean), __float_as_uint(sq));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, mv), make_brsrc(p.rs_out),
-                                              (uint32_t)((size_t)nt * p.M + m) * 8u, 0, CP_SC1);
+        p.rs_out[(size_t)nt * p.M + m] = make_float2(mean, sq);
+        if (p.rsq_out) p.rsq_out[(size_t)m * p.rsq_ld + nt] = sq + (float)ncols * mean * mean;
       }
-    }
-    // rstd_out: the tile that completes last merges every tile's moments of
-    // every row into the row's 1 / rms (RMSNorm) for an A_BF16R reader; TG
-    // threads per row, each requesting up to RB of its partials at once with
-    // device-coherent loads (the other tiles' sc1 stores)
-    if (p.rstd_out) {
-      const int ntiles = p.n_tiles_m * p.n_tiles_n;
-      if (tile_arrive(p.cnt_tile + ntiles, ntiles, sFlag)) return;
-      const RowStats rs{p.rs_out, p.n_tiles_n, BN, p.N, p.M};
-      const brsrc pr = make_brsrc(p.rs_out);
-      const int tg0 = NT / max(p.M, 1);
-      const int TG = tg0 >= 64 ? 64 : tg0 >= 32 ? 32 : tg0 >= 16 ? 16 : tg0 >= 8 ? 8 : tg0 >= 4 ? 4 : tg0 >= 2 ? 2 : 1;
-      const int jg = tid % TG;
-      constexpr int RB = 20;
-      // every thread runs the same number of row passes (uniform shuffles)
-      const int npass = (p.M + NT / TG - 1) / (NT / TG);
-      for (int ps = 0; ps < npass; ps++) {
-        const int m = ps * (NT / TG) + tid / TG;
-        ShiftSum sa;
-        for (int t0 = 0; t0 < rs.T; t0 += RB * TG) {
-          uint2 v[RB];
-#pragma unroll
-          for (int u = 0; u < RB; u++) {
-            const int t = t0 + jg + u * TG;
-            v[u] = bload8<CP_SC1>(pr, (m < p.M && t < rs.T) ? (uint32_t)((size_t)t * p.M + m) * 8u : BUF_OOB);
-          }
-#pragma unroll
-          for (int u = 0; u < RB; u++) {
-            const int t = t0 + jg + u * TG;
-            if (m < p.M && t < rs.T) sa.add(tile_count(rs, t), make_float2(__uint_as_float(v[u].x), __uint_as_float(v[u].y)));
-          }
-        }
-        float n, mean, m2;
-        sa.moments(n, mean, m2);
-        group_merge(n, mean, m2, TG);
-        if (jg == 0 && m < p.M) p.rstd_out[m] = norm_coeffs(make_float2(mean, n > 0.f ? m2 / n : 0.f), 1, p.eps).y;
-      }
-      if (tid == 0) p.cnt_tile[ntiles] = 0u;
     }
   }
 }
