@@ -635,8 +635,8 @@ vla_status sched_layers(Ctx& c, const vla_block_cfg& cfg, const vla_block_weight
   // of squares of every row; the QKV and gate/up GEMMs sum a row's tiles
   // and scale their output rows by its 1 / rms. Only layer 0's attention
   // norm, whose stream comes from the staging pass, runs as a pass of its
-  // own. Up to 112 rows (one row tile), the prefill it was measured on.
-  const bool defer = !f32 && !a8 && S <= 112 && gemm_has(S, nqkv, H, {wt, A_BF16R, E_ROPE, 0, pk}) &&
+  // own.
+  const bool defer = !f32 && !a8 && gemm_has(S, nqkv, H, {wt, A_BF16R, E_ROPE, 0, pk}) &&
                      gemm_has(S, I, H, {wt, A_BF16R, E_SWIGLU, comp, pk});
   {  // cos / sin of every position's RoPE angles, once for the pass
     c.label = "llm.rope_table";

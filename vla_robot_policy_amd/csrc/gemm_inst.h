@@ -59,17 +59,26 @@
   VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 4, 2, 2, 1, 2, 0, 2, 1)
 
 // Deferred-RMSNorm (A_BF16R) counterparts of the backbone's QKV and gate/up
-// tiles up to 112 rows (one row tile), row-major (PKV 0) and packed (PKV 1):
-// 1-16, 17-64 and 65-112 rows; the compensated gate/up of bf16 weights with
-// its 256-weight-row tile at 65-112 rows
+// tiles, row-major (PKV 0) and packed (PKV 1): 1-16, 17-64 and 113-256
+// (64-row tiles), 65-112 and beyond 256 rows; the compensated gate/up of
+// bf16 weights with its 256-weight-row tiles at 65-112 and 193-256 rows
 #define VLA_GEMM_BF16R_BF16(PKV)                                                        \
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_ROPE, 1, 8, 1, 1, 4, 0, 2, PKV)         \
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_ROPE, 4, 8, 1, 1, 4, 0, 2, PKV)         \
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_ROPE, 7, 8, 1, 1, 2, 0, 4, PKV)         \
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_ROPE, 8, 8, 1, 1, 4, 0, 2, PKV)         \
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_SWIGLU, 1, 4, 2, 2, 1, 1, 2, PKV)       \
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_SWIGLU, 4, 4, 2, 2, 1, 1, 2, PKV)       \
-  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_SWIGLU, 7, 8, 1, 2, 2, 1, 2, PKV)
-// fp8 weights (plain bf16 activations) at 65-112 rows
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_SWIGLU, 7, 8, 1, 2, 2, 1, 2, PKV)       \
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_SWIGLU, 8, 8, 1, 2, 2, 1, 2, PKV)       \
+  VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16R, E_SWIGLU, 8, 4, 2, 2, 1, 1, 2, PKV)
+// fp8 weights (plain bf16 activations): the same row classes
 #define VLA_GEMM_BF16R_FP8(PKV)                                                         \
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_ROPE, 1, 8, 1, 1, 4, 0, 2, PKV)          \
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_ROPE, 4, 8, 1, 1, 4, 0, 2, PKV)          \
   VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_ROPE, 7, 8, 1, 1, 2, 0, 4, PKV)          \
-  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_SWIGLU, 7, 8, 1, 1, 4, 0, 2, PKV)
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_ROPE, 8, 4, 1, 2, 2, 0, 2, PKV)          \
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_SWIGLU, 1, 8, 1, 1, 4, 0, 2, PKV)        \
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_SWIGLU, 4, 8, 1, 1, 4, 0, 2, PKV)        \
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_SWIGLU, 7, 8, 1, 1, 4, 0, 2, PKV)        \
+  VLA_GEMM_CASE_F(uint8_t, __bf16, A_BF16R, E_SWIGLU, 8, 4, 1, 2, 2, 0, 2, PKV)
