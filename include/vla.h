@@ -253,12 +253,16 @@ size_t vla_dit_workspace_bytes(const vla_dit* dit, int32_t ctx_len, int32_t chun
  * out = GELU(u W_m1^T + b_m1) W_m2^T + b_m2.
  * w_pe rows have a pitch of round_up(channels*patch^2, 8) elements; the pad
  * columns must be zero.
+ * With flags & VLA_BLOCK_PACKED, every layer's w_qkv, w_o, w_up and w_down
+ * are the packed copies vla_pack_weights (BF16) writes of the row-major
+ * matrices below; the results are the same bits. Other flags:
+ * VLA_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t image, patch, channels, hidden, heads, head_dim, mlp, layers, merge, out_dim;
   float eps;
   int32_t wdtype; /* BF16 */
-  int32_t flags;  /* must be 0 */
+  int32_t flags;  /* 0 or VLA_BLOCK_PACKED */
 } vla_vit_cfg;
 
 typedef struct {

@@ -100,3 +100,30 @@ def test_backbone_packed(gu, wdtype):
     e = gu.upload_input(I["x"])
     got = gu.run_backbone(cfg, packed, e, cfg.seq)
     np.testing.assert_array_equal(got, gu.run_backbone(cfg, plain, e, cfg.seq))
+
+
+def test_vit_packed(gu):
+    """The vision encoder with its layers' four Linears packed: the same bits
+    as with row-major weights, and within the bf16 bar of the oracle."""
+    import torch
+    from oracle import vit as ovit
+    from vla_robot_policy_amd import lib
+    cfg = small_config("step", "bf16")
+    v = cfg.vit
+    W, I = make_weights(cfg), make_inputs(cfg)
+    outs = []
+    for dw in _pair(gu, cfg, W):
+        V = dw.build_vit()
+        toks = torch.empty((v.n_merged, v.out_dim), dtype=torch.float32, device=gu.DEV)
+        z = torch.empty((v.n_patches, v.hidden), dtype=torch.float32, device=gu.DEV)
+        need = lib.vla_vit_workspace_bytes(V, 1)
+        ws = gu.workspace(need)
+        lib.check(lib.vla_vit_encode(V, gu.upload_input(I["image"]), 1, toks, z, ws, need))
+        torch.cuda.synchronize()
+        outs.append((z.cpu().numpy(), toks.cpu().numpy()))
+    (z0, t0), (z1, t1) = outs
+    zr = ovit.vit(to_f64(I["image"])[0], Weights(W), v)
+    gu.relerr(z1, zr, gu.TOL["bf16"], "packed vit encoder")
+    gu.relerr(t1, ovit.merger(zr, Weights(W), v), gu.TOL["bf16"], "packed vit merged")
+    np.testing.assert_array_equal(z1, z0)
+    np.testing.assert_array_equal(t1, t0)

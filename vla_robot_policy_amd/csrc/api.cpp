@@ -1175,7 +1175,7 @@ vla_status sched_dit(Ctx& c, const vla_dit& d, const DitIO& io) {
 vla_status check_vit(const vla_vit* v) {
   if (!v) return fail(VLA_ERR_INVALID_ARG, "null vit");
   const vla_vit_cfg& c = v->cfg;
-  if (c.flags != 0) return fail(VLA_ERR_UNSUPPORTED, "vit cfg flags must be 0");
+  if (c.flags & ~VLA_BLOCK_PACKED) return fail(VLA_ERR_UNSUPPORTED, "vit cfg flags: only VLA_BLOCK_PACKED");
   if (c.wdtype != VLA_BF16) return fail(VLA_ERR_UNSUPPORTED, "vit: weights must be bf16");
   if (c.patch <= 0 || c.image % c.patch || c.merge <= 0 || (c.image / c.patch) % c.merge)
     return fail(VLA_ERR_SHAPE, "vit: image %d / patch %d / merge %d do not tile", c.image, c.patch, c.merge);
@@ -1198,6 +1198,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
   const int grid = cf.image / cf.patch, np = grid * grid, S = n_img * np, D = cf.hidden;
   const int pdim = cf.channels * cf.patch * cf.patch, pitch = (int)align_up(pdim, 8);
   const int nm = np / (cf.merge * cf.merge), Mm = n_img * nm, MD = D * cf.merge * cf.merge;
+  const int pk = (cf.flags & VLA_BLOCK_PACKED) ? 1 : 0;   // the layers' four Linears packed by vla_pack_weights
   Stream zst = take_stream(c, S, D);
   float* z = zst.x;
   uint16_t* qkv = c.take<uint16_t>((size_t)S * 3 * D);
@@ -1226,7 +1227,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
       a.a = zn; a.lda = D;
       a.w = w.w_qkv; a.ldw = D; a.bias = w.b_qkv;
       a.c = qkv; a.ldc = 3 * D;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE}));
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE, 0, pk}));
     }
     {
       c.label = "vit.attn";
@@ -1255,7 +1256,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
       a.a = ao; a.lda = D;
       a.w = w.w_o; a.ldw = D; a.bias = w.b_o;
       a.x = z; a.ldx = D; a.rs_out = zst.part;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}, &zst.rs));
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID, 0, pk}, &zst.rs));
     }
     {
       c.label = "vit.ln2";
@@ -1266,7 +1267,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
       a.a = zn; a.lda = D;
       a.w = w.w_up; a.ldw = D; a.bias = w.b_up; a.act = ACT_GELU;
       a.c = h; a.ldc = cf.mlp;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE}));
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_STORE, 0, pk}));
     }
     {
       c.label = "vit.down";
@@ -1275,7 +1276,7 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
       a.a = h; a.lda = cf.mlp;
       a.w = w.w_down; a.ldw = cf.mlp; a.bias = w.b_down;
       a.x = z; a.ldx = D; a.rs_out = zst.part;
-      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}, &zst.rs));
+      VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID, 0, pk}, &zst.rs));
     }
   }
   if (vit_out) { c.label = "vit.out"; VLA_TRY(convert_rows(c, z, D, S, D, vit_out, D, 1)); }

@@ -43,6 +43,7 @@ bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_STORE, 7, 4, 1, 2, 2, 0, 2, 0)
   // narrow long-K residual at 193..256 rows: two k-waves of 64 columns
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 4, 4, 2, 1, 2, 0, 2, 0)
+  VLA_GEMM_PACKED_STORE(uint16_t)
   VLA_GEMM_BF16R_BF16(0)
   VLA_GEMM_BF16R_BF16(1)
   return false;

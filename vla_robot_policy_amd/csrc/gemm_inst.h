@@ -58,6 +58,15 @@
   VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 1, 1, 4, 1, 4, 0, 2, 1)         \
   VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 4, 2, 2, 1, 2, 0, 2, 1)
 
+// Packed-weight plain-store tiles (the vision encoder's QKV and MLP
+// up-projection with packed weights), for every row class, and the packed
+// narrow long-K residual tile of 193-256 rows (its MLP down-projection)
+#define VLA_GEMM_PACKED_STORE(WT)                                                \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_STORE, 1, 1, 4, 1, 4, 0, 2, 1)         \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_STORE, 4, 4, 1, 1, 4, 0, 2, 1)         \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_STORE, 7, 4, 1, 1, 4, 0, 2, 1)         \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_STORE, 8, 4, 1, 1, 4, 0, 2, 1)         \
+  VLA_GEMM_CASE_F(WT, __bf16, A_BF16, E_RESID, 4, 4, 2, 1, 2, 0, 2, 1)
 // Deferred-RMSNorm (A_BF16R) counterparts of the backbone's QKV and gate/up
 // tiles, row-major (PKV 0) and packed (PKV 1): 1-16, 17-64 and 113-256
 // (64-row tiles), 65-112 and beyond 256 rows; the compensated gate/up of

@@ -64,14 +64,15 @@ class DeviceWeights:
             s = self.up_array(np.concatenate([t.scale for t in ts])).data_ptr()
         return w, s
 
-    def up_rows_packed(self, names: Sequence[str]):
+    def up_rows_packed(self, names: Sequence[str], code: int = None):
         """up_rows, then the matrix repacked on the device by vla_pack_weights
-        (the row-major upload is dropped once the packing kernel has run)."""
+        (the row-major upload is dropped once the packing kernel has run);
+        code: the weights' dtype (default: the model's)."""
         w, s = self.up_rows(names)
         src = next(t for t in reversed(self.keep) if t.data_ptr() == w)
         n = sum(self.t[x].data.shape[0] for x in names)
         k = self.t[names[0]].data.shape[1]
-        code = lib.DTYPE_CODE[self.cfg.wdtype]
+        code = lib.DTYPE_CODE[self.cfg.wdtype] if code is None else code
         out = torch.empty(lib.vla_packed_bytes(code, n, k), dtype=torch.uint8, device=self.device)
         lib.check(lib.vla_pack_weights(code, src, n, k, k, out, torch.cuda.current_stream(self.device).cuda_stream))
         torch.cuda.synchronize(self.device)
@@ -174,19 +175,21 @@ class DeviceWeights:
         v = cfg.vit
         vc = lib.VitCfg(image=v.image, patch=v.patch, channels=v.channels, hidden=v.hidden, heads=v.heads,
                         head_dim=v.head_dim, mlp=v.mlp, layers=v.layers, merge=v.merge, out_dim=v.out_dim, eps=v.eps,
-                        wdtype=lib.VLA_BF16, flags=0)
+                        wdtype=lib.VLA_BF16, flags=lib.VLA_BLOCK_PACKED if self.packed else 0)
+        # the encoder's weights are bf16 whatever the backbone's
+        rows = (lambda names: self.up_rows_packed(names, lib.VLA_BF16)) if self.packed else self.up_rows
         layers = (lib.VitLayer * v.layers)()
         for l in range(v.layers):
             p = f"vit.{l}."
             self.prefetch([n for n in self.t.names() if n.startswith(p)])
             L = layers[l]
             L.ln1_g, L.ln1_b = self.up(p + "ln1_g"), self.up(p + "ln1_b")
-            L.w_qkv, _ = self.up_rows([p + "wq", p + "wk", p + "wv"])
+            L.w_qkv, _ = rows([p + "wq", p + "wk", p + "wv"])
             L.b_qkv = self.up_vec([p + "bq", p + "bk", p + "bv"])
-            L.w_o, _ = self.up_rows([p + "wo"]); L.b_o = self.up_vec([p + "bo"])
+            L.w_o, _ = rows([p + "wo"]); L.b_o = self.up_vec([p + "bo"])
             L.ln2_g, L.ln2_b = self.up(p + "ln2_g"), self.up(p + "ln2_b")
-            L.w_up, _ = self.up_rows([p + "w1"]); L.b_up = self.up_vec([p + "b1"])
-            L.w_down, _ = self.up_rows([p + "w2"]); L.b_down = self.up_vec([p + "b2"])
+            L.w_up, _ = rows([p + "w1"]); L.b_up = self.up_vec([p + "b1"])
+            L.w_down, _ = rows([p + "w2"]); L.b_down = self.up_vec([p + "b2"])
         V = lib.Vit(cfg=vc, layers=layers)
         pad = (-v.patch_dim) % 8
         V.w_pe, _ = self.up_rows(["vit.pe_w"], pad_cols=pad)
