@@ -311,7 +311,7 @@ vla_status gemm(Ctx& c, GemmArgs a, GemmOp op, RowStats* produced = nullptr) {
   if (op.pk && (std::ceil(wrows / 16.0) * std::ceil(a.K / 32.0) * 512.0 * wbytes >= (double)BUF_LIMIT ||
                 (op.em == E_SWIGLU && a.n_half % 16)))
     return fail(VLA_ERR_SHAPE, "gemm: packed weight matrix beyond 2 GiB, or gate/up halves not on 16-row blocks");
-  if (op.am != A_PATCH && (double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
+  if ((double)a.M * a.lda * 4.0 >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: activation matrix beyond 2 GiB");
   if ((op.em == E_RESID ? (double)a.M * a.ldx * 4.0 : (double)a.M * a.ldc * (a.c_f32 ? 4.0 : 2.0)) >= (double)BUF_LIMIT)
     return fail(VLA_ERR_SHAPE, "gemm: output matrix beyond 2 GiB");
@@ -1207,14 +1207,22 @@ vla_status sched_vit(Ctx& c, const vla_vit& v, const void* images, int n_img, fl
   uint16_t* m1 = c.take<uint16_t>((size_t)Mm * MD);
   uint16_t* mz = c.take<uint16_t>((size_t)Mm * MD);   // LayerNormed patches, 2x2 groups concatenated
   uint16_t* zn = c.take<uint16_t>((size_t)S * D);      // LayerNorm-ed rows (bf16)
+  uint16_t* prow = c.take<uint16_t>((size_t)S * pitch);   // patch rows, zero-padded to the weights' pitch
   {  // patchify -> Linear + bias + position table (+ row statistics)
+    c.label = "vit.patch_rows";
+    const size_t ne = (size_t)S * (pitch / 8);
+    VLA_TRY(launch(c, k_patch_rows_ref(), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0,
+                   {arg((const uint16_t*)images), arg(n_img), arg(cf.channels), arg(cf.image), arg(cf.patch), arg(grid),
+                    arg(pitch), arg(prow)}));
     c.label = "vit.patch_embed";
     GemmArgs a = gargs();
-    a.M = S; a.N = D; a.K = pdim;
-    a.a = images; a.img = cf.image; a.patch = cf.patch; a.chans = cf.channels; a.vgrid = grid; a.n_patches = np;
+    // K runs over the pitch: the pad columns are zero in the patch rows and
+    // in w_pe alike
+    a.M = S; a.N = D; a.K = pitch;
+    a.a = prow; a.lda = pitch;
     a.w = v.w_pe; a.ldw = pitch; a.bias = v.b_pe;
     a.x = z; a.ldx = D; a.x_init = 1; a.addrow = v.pos; a.addrow_rows = np; a.rs_out = zst.part;
-    VLA_TRY(gemm(c, a, {VLA_BF16, A_PATCH, E_RESID}, &zst.rs));
+    VLA_TRY(gemm(c, a, {VLA_BF16, A_BF16, E_RESID}, &zst.rs));
   }
   for (int l = 0; l < cf.layers; l++) {
     const vla_vit_layer& w = v.layers[l];

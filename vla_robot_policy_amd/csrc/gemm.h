@@ -1,5 +1,5 @@
 // Weight-streaming GEMM for small M (16..600 rows), y = prologue(A) . W^T,
-// with fused prologues (row norms, patch gather) and fused
+// with fused prologues (row norms) and fused
 // epilogues (bias, GELU/SiLU, RoPE, SwiGLU,
 // residual / gated residual with per-tile row moments for the next norm).
 //
@@ -38,7 +38,7 @@ namespace vla {
 // epilogue sums a row's tiles (eps and the width K give 1 / rms) and scales
 // the output row: (x g / rms) W^T = (x g) W^T / rms. The norm then costs no
 // pass of its own and the GEMM stages bf16 rows, half the bytes of fp32.
-enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_PATCH = 3, A_FP8 = 6, A_I8 = 7, A_BF16R = 8 };
+enum AMode { A_BF16 = 0, A_F32 = 1, A_NORM = 2, A_FP8 = 6, A_I8 = 7, A_BF16R = 8 };
 // 8-bit activation codes with a per-row scale (W8A8)
 constexpr bool a_codes(int am) { return am == A_FP8 || am == A_I8; }
 // bf16 rows staged as they are (with or without the deferred row scale)
@@ -49,7 +49,7 @@ enum ActKind { ACT_NONE = 0, ACT_GELU = 1, ACT_SILU = 2 };
 struct GemmArgs {
   int M, N, K;
   // ---- A source
-  const void* a;         // BF16/F32/NORM: matrix [rows, lda]; PATCH: bf16 images
+  const void* a;         // BF16/F32/NORM: matrix [rows, lda]
   const void* a_lo;      // BF16 with compensation: remainder plane, same layout as a
   const float* a_scale;  // FP8 / I8: E4M3FN or int8 codes [rows, lda] in a, one float32 scale per row here
                          // (W8A8: the codes are staged as bytes and widened to bf16 at fragment
@@ -61,7 +61,6 @@ struct GemmArgs {
   const float* g;        // per-k gain (NULL = 1)
   int g_plus_one;        // gain is 1 + g[k] (adaLN scale)
   const float* bsh;      // per-k shift (NULL = 0)
-  int img, patch, chans, vgrid, n_patches;   // PATCH geometry
   // ---- W
   const void* w;
   int ldw;
@@ -477,19 +476,6 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm(GemmArgs p) {
         ar[i] = bload16(ars, ok ? (uint32_t)m * p.lda + k : BUF_OOB);
       } else if constexpr (AM == A_F32 || AM == A_NORM) {
         ar[i] = as_f4(bload16(ars, ok ? ((uint32_t)m * p.lda + k) * 4u : BUF_OOB));
-      } else if constexpr (AM == A_PATCH) {
-        int im = m / p.n_patches, pi = m % p.n_patches;
-        int pr = pi / p.vgrid, pc = pi % p.vgrid;
-        int P2 = p.patch * p.patch;
-        float t4[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          int kk = k + e;
-          int c = kk / P2, rem = kk % P2, ky = rem / p.patch, kx = rem % p.patch;
-          uint32_t off = ((((uint32_t)im * p.chans + c) * p.img + pr * p.patch + ky) * p.img + pc * p.patch + kx) * 2u;
-          t4[e] = bf2f(bload2(ars, (r < BM && m < p.M && kk < p.K) ? off : BUF_OOB));
-        }
-        ar[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
       }
     }
   };

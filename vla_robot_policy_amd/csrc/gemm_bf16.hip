@@ -13,7 +13,6 @@ bool gemm_lookup_bf16(const GemmPick& g, KernelRef* out) {
   VLA_GEMM_WIDE(uint16_t, __bf16, A_BF16, E_SWIGLU)
   VLA_GEMM_WIDE_AC(uint16_t, __bf16, A_BF16, E_SWIGLU)
   VLA_GEMM_NARROW_AC(uint16_t, __bf16, A_BF16, E_RESID)
-  VLA_GEMM_NARROW(uint16_t, __bf16, A_PATCH, E_RESID)
   // compensated MLP tiles: down at 65-112 rows with one k-step per wave and
   // four activation chunks in flight; the packed gate/up and down tiles
   VLA_GEMM_CASE_F(uint16_t, __bf16, A_BF16, E_RESID, 7, 4, 2, 1, 1, 1, 4, 0)

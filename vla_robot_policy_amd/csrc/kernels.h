@@ -33,6 +33,7 @@ const void* k_time_embed_ref();
 const void* k_rope_table_ref();
 const void* k_pack_weights_ref();
 const void* k_ctx_vt_ref();
+const void* k_patch_rows_ref();
 const void* k_dit_table_ref();
 const void* k_norm_rows_ref();
 const void* k_quant_rows_ref();

@@ -25,6 +25,7 @@ const void* k_time_embed_ref() { return (const void*)&k_time_embed; }
 const void* k_rope_table_ref() { return (const void*)&k_rope_table; }
 const void* k_pack_weights_ref() { return (const void*)&k_pack_weights; }
 const void* k_ctx_vt_ref() { return (const void*)&k_ctx_vt; }
+const void* k_patch_rows_ref() { return (const void*)&k_patch_rows; }
 const void* k_norm_rows_ref() { return (const void*)&k_norm_rows; }
 const void* k_quant_rows_ref() { return (const void*)&k_quant_rows; }
 const void* k_convert_rows_ref() { return (const void*)&k_convert_rows; }

@@ -164,6 +164,37 @@ __global__ __launch_bounds__(256) void k_ctx_vt(const uint16_t* kv, int C, int L
   *reinterpret_cast<uint4*>(vt + ((size_t)l * D + d) * Cp + c0) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Patch rows of a batch of images (bf16 [n_img][chans][img][img]): row m =
+// patch (pr, pc) of image m / n_patches with features in (channel, row,
+// column) order, zero from k = chans * patch^2 up to the row pitch; one
+// thread per 8 features (one 16-byte store).
+__global__ __launch_bounds__(256) void k_patch_rows(const uint16_t* img, int n_img, int chans, int size, int patch,
+                                                    int grid, int pitch, uint16_t* out) {
+  const int n8 = pitch / 8;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int np = grid * grid;
+  if (e >= (size_t)n_img * np * n8) return;
+  const int m = (int)(e / n8), k0 = (int)(e % n8) * 8;
+  const int im = m / np, pi = m % np, pr = pi / grid, pc = pi % grid;
+  const int P2 = patch * patch, K = chans * P2;
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    uint32_t h[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int k = k0 + 2 * j + q;
+      h[q] = 0u;
+      if (k < K) {
+        const int c = k / P2, r = k % P2, ky = r / patch, kx = r % patch;
+        h[q] = img[(((size_t)im * chans + c) * size + pr * patch + ky) * size + pc * patch + kx];
+      }
+    }
+    w[j] = h[0] | (h[1] << 16);
+  }
+  *reinterpret_cast<uint4*>(out + (size_t)m * pitch + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // RoPE tables of a pass: cs[pos][i] = cos(pos theta_i), sn[pos][i] =
 // sin(pos theta_i), theta_i = base^(-2i / D), i < D / 2, pos < S (half-split
 // rotation of the pairs (i, i + D/2)). The frequency and the angle are formed
